@@ -1,0 +1,355 @@
+"""fp64 CPU oracle for relation-aware self-attention and T5 bucketed bias.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this module.  The product path
+(the HIP library and its Python binding) never calls it, and this module shares
+no code with that path: it imports nothing from the package.
+
+Everything here is the plain definition of the method, written for a reader to
+check against the pages by eye.  Inputs may be any real dtype (fp32, bf16 as
+torch or numpy arrays); they are upcast exactly to float64 and all arithmetic
+runs in float64.
+
+Sources (page titles, then section / equation):
+
+* "Self-Attention with Relative Position Representations" (paper summary page),
+  §3.4 "Standard Self-Attention" (Eq. 1, Eq. 2 and the softmax), "Relation-Aware
+  Self-Attention" (Eq. 3, Eq. 4), "Relative Position Representations: From
+  Arbitrary Edges to Sequences" (the clip function and the 2k+1 tables),
+  "Efficient Implementation" (Eq. 5, the split of the logit and of the output).
+* "Shaw et al. Relative Position Representations" (tutorial page): the same
+  equations in q, k, v notation with offset r = j - i.
+* "Relative position embeddings" (survey page), section "T5": the scalar bias
+  A_ij = q_i.k_j + b^(h)_beta(j-i), the bucket function beta, no 1/sqrt(d).
+
+Readings where the pages are silent or garbled (each is listed in the design doc):
+
+* offset sign is j - i, table row 0 holds offset -k;
+* tables are [Ht, 2k+1, d] with Ht in {1, H} (Ht == 1: shared by all heads);
+* the 1/sqrt(d) scale multiplies both terms of the logit (Eq. 5); a^V is unscaled;
+* masks: causal hides keys j > i; key padding hides keys j >= len_b; masked
+  keys contribute neither v_j nor a^V_ij; a row with no visible key outputs 0;
+* T5 bidirectional: half of the buckets per sign, B_exact = half/2, the
+  logarithmic part spans (half - B_exact) buckets and is capped at half - 1,
+  keys after the query (delta > 0) use the upper half; unidirectional uses all
+  B buckets for delta <= 0 and maps delta > 0 to bucket 0;
+* the floor in beta is taken of the exact real number (rational comparison),
+  not of a rounded floating-point logarithm.
+"""
+from __future__ import annotations
+
+from fractions import Fraction
+
+import numpy as np
+
+__all__ = [
+    "clip",
+    "relative_labels",
+    "visible",
+    "t5_bucket",
+    "t5_bucket_matrix",
+    "shaw_logits",
+    "relattn_bruteforce",
+    "relattn_factored",
+    "relattn_rows",
+    "t5_attention",
+    "t5_rows",
+    "to_f64",
+]
+
+
+# ---------------------------------------------------------------------------
+# helpers
+# ---------------------------------------------------------------------------
+
+def to_f64(x):
+    """Exact upcast of a numpy array or torch tensor (any real dtype) to float64."""
+    if x is None:
+        return None
+    if hasattr(x, "detach"):  # torch tensor; bf16 -> fp64 is exact
+        import torch
+        return x.detach().to(device="cpu", dtype=torch.float64).numpy()
+    return np.asarray(x, dtype=np.float64)
+
+
+def _table_for_head(table, h):
+    """Per-head slice of a [Ht, 2k+1, d] table; Ht == 1 means shared by all heads."""
+    if table is None:
+        return None
+    return table[0] if table.shape[0] == 1 else table[h]
+
+
+def _key_lengths(key_lens, batch, n):
+    if key_lens is None:
+        return [n] * batch
+    lens = [int(x) for x in np.asarray(key_lens).reshape(-1)]
+    return [max(0, min(n, x)) for x in lens]
+
+
+# ---------------------------------------------------------------------------
+# relative position labels (paper summary page, "Relative Position
+# Representations: From Arbitrary Edges to Sequences")
+# ---------------------------------------------------------------------------
+
+def clip(x: int, k: int) -> int:
+    """clip(x, k) = max(-k, min(k, x))."""
+    return max(-k, min(k, x))
+
+
+def relative_labels(n: int, k: int) -> np.ndarray:
+    """R[i, j] = clip(j - i, k) for query i and key j (int64, n x n)."""
+    by_delta = np.array([clip(x, k) for x in range(-(n - 1), n)], dtype=np.int64)
+    delta = np.arange(n)[None, :] - np.arange(n)[:, None]  # j - i
+    return by_delta[delta + (n - 1)]
+
+
+def visible(n: int, causal: bool, key_len: int) -> np.ndarray:
+    """Boolean n x n matrix: key j is visible to query i."""
+    i = np.arange(n)[:, None]
+    j = np.arange(n)[None, :]
+    ok = j < key_len
+    if causal:
+        ok = ok & (j <= i)
+    return np.broadcast_to(ok, (n, n)).copy()
+
+
+# ---------------------------------------------------------------------------
+# T5 bucketing (survey page "Relative position embeddings", section "T5")
+# ---------------------------------------------------------------------------
+
+def t5_bucket(delta: int, num_buckets: int = 32, max_distance: int = 128,
+              bidirectional: bool = True) -> int:
+    """Bucket beta(delta) for offset delta = j - i.
+
+    For a distance a below B_exact the bucket is a itself.  Otherwise it is
+    B_exact + floor((nb) * ln(a / B_exact) / ln(D_max / B_exact)), clamped to the
+    last bucket of its half, with nb the number of logarithmic buckets.  The
+    floor is evaluated exactly: floor(x) >= t  <=>  (a/B_exact)^nb >=
+    (D_max/B_exact)^t, a comparison of rationals.
+    """
+    if bidirectional:
+        half = num_buckets // 2
+        base = half if delta > 0 else 0
+        a = abs(delta)
+    else:
+        half = num_buckets
+        base = 0
+        a = max(-delta, 0)
+    exact = half // 2
+    if a < exact:
+        return base + a
+    nb = half - exact
+    lhs = Fraction(a, exact) ** nb
+    step = Fraction(max_distance, exact)
+    t = 0
+    # largest t with (a/exact)^nb >= (D/exact)^t, stopping at the cap half-1
+    while exact + t < half - 1 and lhs >= step ** (t + 1):
+        t += 1
+    return base + exact + t
+
+
+def t5_bucket_matrix(n: int, num_buckets: int = 32, max_distance: int = 128,
+                     bidirectional: bool = True) -> np.ndarray:
+    """Bmat[i, j] = beta(j - i) (int64, n x n)."""
+    by_delta = np.array([t5_bucket(x, num_buckets, max_distance, bidirectional)
+                         for x in range(-(n - 1), n)], dtype=np.int64)
+    delta = np.arange(n)[None, :] - np.arange(n)[:, None]  # j - i
+    return by_delta[delta + (n - 1)]
+
+
+# ---------------------------------------------------------------------------
+# softmax over visible keys (paper summary page, §3.4 softmax under Eq. 2)
+# ---------------------------------------------------------------------------
+
+def _masked_softmax_rows(e: np.ndarray, ok: np.ndarray) -> np.ndarray:
+    """alpha[i, j] = exp(e_ij) / sum_{visible j'} exp(e_ij'); 0 where hidden.
+
+    A row with no visible key gets all-zero weights.
+    """
+    e_vis = np.where(ok, e, -np.inf)
+    row_max = e_vis.max(axis=1, keepdims=True)
+    row_max = np.where(np.isfinite(row_max), row_max, 0.0)  # rows with no key
+    w = np.where(ok, np.exp(e_vis - row_max), 0.0)
+    total = w.sum(axis=1, keepdims=True)
+    return np.divide(w, total, out=np.zeros_like(w), where=total > 0)
+
+
+# ---------------------------------------------------------------------------
+# Shaw et al., brute force: materialise a^K_ij and a^V_ij (Eq. 3, Eq. 4)
+# ---------------------------------------------------------------------------
+
+def _default_scale(d: int, scale):
+    return 1.0 / np.sqrt(d) if (scale is None or scale <= 0) else float(scale)
+
+
+def shaw_logits(q, k, aK, clip_k: int, scale=None) -> np.ndarray:
+    """e[i, j] = scale * q_i . (k_j + a^K_ij) for ONE head (q, k: [n, d]).
+
+    a^K_ij = w^K_clip(j-i, k) (Eq. 4); no mask applied.
+    """
+    q = to_f64(q)
+    k = to_f64(k)
+    n, d = q.shape
+    s = _default_scale(d, scale)
+    R = relative_labels(n, clip_k)
+    if aK is None:
+        AK = np.zeros((n, n, d))
+    else:
+        AK = to_f64(aK)[R + clip_k]  # [n, n, d], row (i, j) = w^K_{clip(j-i)}
+    keys = k[None, :, :] + AK  # relation-augmented key of j as seen from i
+    return s * np.einsum("id,ijd->ij", q, keys)
+
+
+def relattn_bruteforce(q, k, v, aK=None, aV=None, clip_k: int = 0, scale=None,
+                       causal: bool = False, key_lens=None, return_alpha=False):
+    """Relation-aware self-attention by its definition, all heads.
+
+    q, k, v: [B, H, n, d]; aK, aV: [Ht, 2k+1, d] or None (None counts as zero).
+    Materialises the n x n x d edge tensors per head (Eq. 3 and Eq. 4), then
+    masked softmax, then z_i = sum_j alpha_ij (v_j + a^V_ij).
+    """
+    q, k, v = to_f64(q), to_f64(k), to_f64(v)
+    aK, aV = to_f64(aK), to_f64(aV)
+    B, H, n, d = q.shape
+    lens = _key_lengths(key_lens, B, n)
+    R = relative_labels(n, clip_k)
+    z = np.zeros((B, H, n, v.shape[-1]))
+    alphas = np.zeros((B, H, n, n)) if return_alpha else None
+    for b in range(B):
+        ok = visible(n, causal, lens[b])
+        for h in range(H):
+            e = shaw_logits(q[b, h], k[b, h], _table_for_head(aK, h), clip_k, scale)
+            alpha = _masked_softmax_rows(e, ok)
+            if aV is None:
+                AV = np.zeros((n, n, v.shape[-1]))
+            else:
+                AV = _table_for_head(aV, h)[R + clip_k]  # [n, n, d]
+            vals = v[b, h][None, :, :] + AV  # value of j as seen from i
+            z[b, h] = np.einsum("ij,ijd->id", alpha, vals)
+            if return_alpha:
+                alphas[b, h] = alpha
+    return (z, alphas) if return_alpha else z
+
+
+# ---------------------------------------------------------------------------
+# Shaw et al., factored (Eq. 5 and the split of Eq. 3)
+# ---------------------------------------------------------------------------
+
+def relattn_factored(q, k, v, aK=None, aV=None, clip_k: int = 0, scale=None,
+                     causal: bool = False, key_lens=None, return_bucket_sums=False):
+    """Same result as ``relattn_bruteforce`` through the split of Eq. 5.
+
+    e = scale * Q K^T + L[i, clip(j-i)+k] with L = scale * Q (w^K)^T, and
+    z = alpha V + S W^V with S[i, r] = sum of alpha_ij over keys j whose label
+    is r.  Nothing of size n x n x d is formed.
+    """
+    q, k, v = to_f64(q), to_f64(k), to_f64(v)
+    aK, aV = to_f64(aK), to_f64(aV)
+    B, H, n, d = q.shape
+    s = _default_scale(d, scale)
+    lens = _key_lengths(key_lens, B, n)
+    R = relative_labels(n, clip_k)
+    nlab = 2 * clip_k + 1
+    z = np.zeros((B, H, n, v.shape[-1]))
+    S_all = np.zeros((B, H, n, nlab)) if return_bucket_sums else None
+    for b in range(B):
+        ok = visible(n, causal, lens[b])
+        for h in range(H):
+            e = s * (q[b, h] @ k[b, h].T)  # content term (Eq. 2 form)
+            if aK is not None:
+                L = s * (q[b, h] @ _table_for_head(aK, h).T)  # [n, 2k+1]
+                e = e + np.take_along_axis(L, R + clip_k, axis=1)
+            alpha = _masked_softmax_rows(e, ok)
+            out = alpha @ v[b, h]
+            # S[i, r] = sum of alpha_ij over the keys j whose label row is r
+            S = np.stack([np.bincount(R[i] + clip_k, weights=alpha[i], minlength=nlab)
+                          for i in range(n)])
+            if aV is not None:
+                out = out + S @ _table_for_head(aV, h)
+            z[b, h] = out
+            if return_bucket_sums:
+                S_all[b, h] = S
+    return (z, S_all) if return_bucket_sums else z
+
+
+def relattn_rows(q, k, v, aK=None, aV=None, clip_k: int = 0, scale=None,
+                 causal: bool = False, key_lens=None, rows=()):
+    """Brute-force output rows z[b, h, i] for a list of (b, h, i).
+
+    For each row the n x d slab k_j + a^K_ij and v_j + a^V_ij is materialised
+    (Eq. 4 and Eq. 3 for one query), so large shapes can be sampled row by row.
+    Returns an array [len(rows), d].
+    """
+    q, k, v = to_f64(q), to_f64(k), to_f64(v)
+    aK, aV = to_f64(aK), to_f64(aV)
+    B, H, n, d = q.shape
+    s = _default_scale(d, scale)
+    lens = _key_lengths(key_lens, B, n)
+    out = np.zeros((len(rows), v.shape[-1]))
+    labels = np.array([clip(j, clip_k) for j in range(-(n - 1), n)]) + clip_k
+    for t, (b, h, i) in enumerate(rows):
+        idx = labels[np.arange(n) - i + (n - 1)]  # label row of (i, j) for all j
+        tk = _table_for_head(aK, h)
+        tv = _table_for_head(aV, h)
+        keys = k[b, h] + (tk[idx] if tk is not None else 0.0)
+        vals = v[b, h] + (tv[idx] if tv is not None else 0.0)
+        e = s * (keys @ q[b, h, i])
+        ok = np.arange(n) < lens[b]
+        if causal:
+            ok &= np.arange(n) <= i
+        if not ok.any():
+            continue
+        w = np.exp(e[ok] - e[ok].max())
+        out[t] = (w / w.sum()) @ vals[ok]
+    return out
+
+
+# ---------------------------------------------------------------------------
+# T5 scalar bias (survey page "Relative position embeddings", section "T5")
+# ---------------------------------------------------------------------------
+
+def t5_attention(q, k, v, bias, num_buckets: int = 32, max_distance: int = 128,
+                 bidirectional: bool = True, scale=None, causal: bool = False,
+                 key_lens=None):
+    """A_ij = scale * q_i.k_j + bias[beta(j-i), h], softmax, z_i = sum alpha_ij v_j.
+
+    bias: [num_buckets, H]; T5 uses no 1/sqrt(d) scaling, so scale defaults to 1.
+    """
+    q, k, v = to_f64(q), to_f64(k), to_f64(v)
+    bias = to_f64(bias)
+    B, H, n, d = q.shape
+    s = 1.0 if (scale is None or scale <= 0) else float(scale)
+    lens = _key_lengths(key_lens, B, n)
+    Bm = t5_bucket_matrix(n, num_buckets, max_distance, bidirectional)
+    z = np.zeros((B, H, n, v.shape[-1]))
+    for b in range(B):
+        ok = visible(n, causal, lens[b])
+        for h in range(H):
+            e = s * (q[b, h] @ k[b, h].T) + bias[Bm, h]
+            z[b, h] = _masked_softmax_rows(e, ok) @ v[b, h]
+    return z
+
+
+def t5_rows(q, k, v, bias, num_buckets: int = 32, max_distance: int = 128,
+            bidirectional: bool = True, scale=None, causal: bool = False,
+            key_lens=None, rows=()):
+    """T5 output rows z[b, h, i] for a list of (b, h, i)."""
+    q, k, v = to_f64(q), to_f64(k), to_f64(v)
+    bias = to_f64(bias)
+    B, H, n, d = q.shape
+    s = 1.0 if (scale is None or scale <= 0) else float(scale)
+    lens = _key_lengths(key_lens, B, n)
+    by_delta = np.array([t5_bucket(x, num_buckets, max_distance, bidirectional)
+                         for x in range(-(n - 1), n)])
+    out = np.zeros((len(rows), v.shape[-1]))
+    for t, (b, h, i) in enumerate(rows):
+        bk = by_delta[np.arange(n) - i + (n - 1)]
+        e = s * (k[b, h] @ q[b, h, i]) + bias[bk, h]
+        ok = np.arange(n) < lens[b]
+        if causal:
+            ok &= np.arange(n) <= i
+        if not ok.any():
+            continue
+        w = np.exp(e[ok] - e[ok].max())
+        out[t] = (w / w.sum()) @ v[b, h][ok]
+    return out

@@ -1,0 +1,416 @@
+"""Pins of the fp64 oracle against what the pages and the mathematics fix.
+
+No GPU.  Each test names the passage (page title, section / equation) it
+checks.  Sources of stored values are the JSON files in tests/golden/, each with
+its citation; none was produced by the HIP path.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import relattn_oracle as orc
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def rnd(shape, seed, std=1.0):
+    return np.random.default_rng(seed).standard_normal(shape) * std
+
+
+def sdpa(q, k, v, ok, scale):
+    """Textbook attention (Eq. 1-2) by a library routine, fp64 on the CPU."""
+    t = lambda x: torch.from_numpy(np.ascontiguousarray(x))
+    return torch.nn.functional.scaled_dot_product_attention(
+        t(q), t(k), t(v), attn_mask=torch.from_numpy(ok), scale=scale).numpy()
+
+
+# ---------------------------------------------------------------------------
+# labels: paper summary page, "Relative Position Representations: From
+# Arbitrary Edges to Sequences"
+# ---------------------------------------------------------------------------
+
+def test_clip_worked_values():
+    g = golden("clip_worked_values.json")
+    for x, want in g["clip_k4"]:
+        assert oracle.clip(x, 4) == want
+    d = g["direction"]
+    R = oracle.relative_labels(8, 4)
+    assert R[d["i"], d["j"]] == d["forward"]
+    assert R[d["j"], d["i"]] == d["reverse"]
+
+
+def test_label_counts():
+    g = golden("clip_worked_values.json")
+    for k, count in g["label_count"]:
+        R = oracle.relative_labels(2 * k + 5, k)
+        assert len(np.unique(R)) == count
+    assert sorted(np.unique(oracle.relative_labels(12, 4)).tolist()) == g["labels_k4"]
+
+
+def test_k0_single_label():
+    # k = 0: every pair gets the same label (Table 2 discussion of k = 0).
+    assert np.all(oracle.relative_labels(9, 0) == 0)
+
+
+# ---------------------------------------------------------------------------
+# T5 buckets: survey page "Relative position embeddings", section "T5"
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("case", ["default_bidirectional", "small_bidirectional",
+                                  "small_unidirectional"])
+def test_t5_bucket_hand_table(case):
+    g = golden("t5_buckets.json")[case]
+    for delta, want in g["delta_to_bucket"]:
+        got = oracle.t5_bucket(delta, g["num_buckets"], g["max_distance"],
+                               g["bidirectional"])
+        assert got == want, (delta, got, want)
+
+
+def test_t5_first_distance_per_bucket():
+    g = golden("t5_buckets.json")["default_bidirectional"]
+    for bucket, first in g["first_distance_of_bucket"]:
+        assert oracle.t5_bucket(-first) == bucket
+        assert oracle.t5_bucket(-(first - 1)) == bucket - 1
+
+
+def test_t5_bucket_matches_real_formula_away_from_ties():
+    """Exact floor equals the floating-point evaluation of the printed formula
+    wherever the real value is not within 1e-9 of an integer."""
+    for (B, D, bidir) in [(32, 128, True), (32, 128, False), (16, 64, True),
+                          (64, 256, True), (8, 8, False)]:
+        half = B // 2 if bidir else B
+        ex = half // 2
+        for a in range(ex, 3000):
+            x = math.log(a / ex) / math.log(D / ex) * (half - ex)
+            if abs(x - round(x)) < 1e-9:
+                continue
+            want = min(half - 1, ex + math.floor(x))
+            assert oracle.t5_bucket(-a, B, D, bidir) == want, (B, D, a)
+
+
+def test_t5_bucket_ties_are_exact():
+    # a = 16, 32, 64 make 2*log2(a/8) exactly 2, 4, 6 (B=32, D=128).
+    for a, want in [(16, 10), (32, 12), (64, 14)]:
+        assert oracle.t5_bucket(-a) == want
+        assert oracle.t5_bucket(a) == want + 16
+
+
+def test_t5_param_count():
+    # 32 buckets x 12 heads = 384 numbers (T5 section); the bias table of the
+    # T5 workload is [num_buckets, H].
+    import workloads
+    t = workloads.make_inputs("t5", batch=1, n=8)["t5_bias"]
+    assert t.shape == (32, 12) and t.numel() == 384
+
+
+def test_edge_table_param_counts():
+    # Per-head tables of the big model with k = 8: 16*17*64*2 = 34,816 numbers;
+    # shared across heads: 17*64*2 = 2,176 ("Key Design Choices", per-head
+    # versus shared edge representations).
+    assert 16 * (2 * 8 + 1) * 64 * 2 == 34816
+    assert (2 * 8 + 1) * 64 * 2 == 2176
+
+
+# ---------------------------------------------------------------------------
+# hand-worked examples (Eq. 3, Eq. 4; T5 logit)
+# ---------------------------------------------------------------------------
+
+def _softmax(x):
+    x = np.asarray(x, dtype=np.float64)
+    w = np.exp(x - x.max())
+    return w / w.sum()
+
+
+def test_shaw_worked_example():
+    g = golden("shaw_worked_example.json")
+    q, k, v = (np.array(g[x], dtype=np.float64) for x in "qkv")
+    wK, wV = np.array(g["wK"], float), np.array(g["wV"], float)
+    c = g["clip"]
+    assert oracle.relative_labels(3, c).tolist() == g["labels"]
+    e = oracle.shaw_logits(q, k, wK, c)
+    np.testing.assert_allclose(e, g["logits"], rtol=0, atol=1e-15)
+    u = np.array(g["value_plus_edge"], float)
+    want = np.stack([_softmax(g["logits"][i]) @ u[i] for i in range(3)])
+    Q, K, V = (x[None, None] for x in (q, k, v))
+    for fn in (oracle.relattn_bruteforce, oracle.relattn_factored):
+        z = fn(Q, K, V, wK[None], wV[None], c)[0, 0]
+        np.testing.assert_allclose(z, want, rtol=0, atol=1e-15)
+        np.testing.assert_allclose(z[1], g["z_row1_uniform"], rtol=0, atol=1e-15)
+        zc = fn(Q, K, V, wK[None], wV[None], c, causal=True)[0, 0]
+        np.testing.assert_allclose(zc[0], g["causal_z"]["row0"], atol=1e-15)
+        np.testing.assert_allclose(zc[1], g["causal_z"]["row1"], atol=1e-15)
+        np.testing.assert_allclose(zc[2], want[2], atol=1e-15)
+
+
+def test_t5_worked_example():
+    g = golden("t5_worked_example.json")
+    q, k, v = (np.array(g[x], dtype=np.float64)[None, None] for x in "qkv")
+    bias = np.array(g["bias"], float)[:, None]
+    Bm = oracle.t5_bucket_matrix(3, g["num_buckets"], g["max_distance"],
+                                 g["bidirectional"])
+    assert Bm.tolist() == g["buckets"]
+    want = np.stack([_softmax(g["logits"][i]) @ v[0, 0] for i in range(3)])
+    z = oracle.t5_attention(q, k, v, bias, g["num_buckets"], g["max_distance"],
+                            g["bidirectional"])[0, 0]
+    np.testing.assert_allclose(z, want, rtol=0, atol=1e-15)
+
+
+# ---------------------------------------------------------------------------
+# special cases that reduce to textbook attention (Eq. 1, Eq. 2)
+# ---------------------------------------------------------------------------
+
+MASKS = [(False, None), (True, None), (False, [5, 11]), (True, [7, 11])]
+
+
+@pytest.mark.parametrize("causal,lens", MASKS)
+def test_zero_tables_equal_textbook_attention(causal, lens):
+    B, H, n, d, c = 2, 3, 11, 8, 3
+    q, k, v = rnd((B, H, n, d), 1), rnd((B, H, n, d), 2), rnd((B, H, n, d), 3)
+    zeros = np.zeros((H, 2 * c + 1, d))
+    for b in range(B):
+        ok = oracle.visible(n, causal, n if lens is None else lens[b])
+        ref = sdpa(q[b], k[b], v[b], ok, 1 / math.sqrt(d))
+        for fn in (oracle.relattn_bruteforce, oracle.relattn_factored):
+            for tables in ((zeros, zeros), (None, None)):
+                z = fn(q, k, v, *tables, c, causal=causal, key_lens=lens)
+                np.testing.assert_allclose(z[b], ref, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("causal,lens", MASKS)
+def test_t5_zero_bias_equals_unscaled_attention(causal, lens):
+    B, H, n, d = 2, 3, 13, 8
+    q, k, v = rnd((B, H, n, d), 4), rnd((B, H, n, d), 5), rnd((B, H, n, d), 6)
+    z = oracle.t5_attention(q, k, v, np.zeros((32, H)), causal=causal, key_lens=lens)
+    for b in range(B):
+        ok = oracle.visible(n, causal, n if lens is None else lens[b])
+        np.testing.assert_allclose(z[b], sdpa(q[b], k[b], v[b], ok, 1.0),
+                                   rtol=1e-12, atol=1e-12)
+
+
+def test_k0_closed_form():
+    """k = 0: q_i.w^K_0 is constant per row, so alpha is vanilla attention and,
+    since every row of alpha sums to 1, z = vanilla + w^V_0."""
+    B, H, n, d = 1, 2, 10, 8
+    q, k, v = rnd((B, H, n, d), 7), rnd((B, H, n, d), 8), rnd((B, H, n, d), 9)
+    wK, wV = rnd((H, 1, d), 10), rnd((H, 1, d), 11)
+    for causal in (False, True):
+        ok = oracle.visible(n, causal, n)
+        for fn in (oracle.relattn_bruteforce, oracle.relattn_factored):
+            z = fn(q, k, v, wK, wV, 0, causal=causal)
+            for h in range(H):
+                want = sdpa(q[0, h], k[0, h], v[0, h], ok, 1 / math.sqrt(d)) + wV[h, 0]
+                np.testing.assert_allclose(z[0, h], want, rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# invariants of alpha and of the bucket sums (softmax under Eq. 2; Eq. 5 split)
+# ---------------------------------------------------------------------------
+
+def test_alpha_rows_and_bucket_sums():
+    B, H, n, d, c = 2, 2, 14, 8, 3
+    q, k, v = rnd((B, H, n, d), 12), rnd((B, H, n, d), 13), rnd((B, H, n, d), 14)
+    wK, wV = rnd((H, 2 * c + 1, d), 15), rnd((H, 2 * c + 1, d), 16)
+    lens = [9, 0]
+    _, alpha = oracle.relattn_bruteforce(q, k, v, wK, wV, c, causal=True,
+                                         key_lens=lens, return_alpha=True)
+    _, S = oracle.relattn_factored(q, k, v, wK, wV, c, causal=True, key_lens=lens,
+                                   return_bucket_sums=True)
+    np.testing.assert_allclose(alpha[0].sum(-1), 1.0, atol=1e-14)
+    assert np.all(alpha[1] == 0)              # len 0: no visible key
+    np.testing.assert_allclose(S[0].sum(-1), 1.0, atol=1e-14)
+    assert np.all(alpha[0][..., :, 9:] == 0)  # padded keys get no weight
+    for h in range(H):
+        for i in range(n):
+            for r in range(1, 2 * c):          # interior label: one key only
+                j = i + r - c
+                if 0 <= j < n:
+                    assert S[0, h, i, r] == pytest.approx(alpha[0, h, i, j], abs=1e-15)
+
+
+# ---------------------------------------------------------------------------
+# Eq. 5: the factored form equals the definition
+# ---------------------------------------------------------------------------
+
+def _cases():
+    rng = np.random.default_rng(2026)
+    for t in range(40):
+        n = int(rng.integers(1, 25))
+        c = int(rng.integers(0, n + 3))
+        d = int(rng.choice([2, 4, 8]))
+        H = int(rng.integers(1, 4))
+        B = int(rng.integers(1, 3))
+        causal = bool(rng.integers(0, 2))
+        lens = None if rng.integers(0, 2) else [int(x) for x in rng.integers(0, n + 1, B)]
+        shared = bool(rng.integers(0, 2))
+        which = int(rng.integers(0, 4))  # 0 K+V, 1 K only, 2 V only, 3 none
+        yield t, n, c, d, H, B, causal, lens, shared, which
+
+
+@pytest.mark.parametrize("case", list(_cases()), ids=lambda c: f"case{c[0]}")
+def test_factored_matches_bruteforce(case):
+    t, n, c, d, H, B, causal, lens, shared, which = case
+    q, k, v = (rnd((B, H, n, d), 100 * t + s) for s in range(3))
+    Ht = 1 if shared else H
+    wK = rnd((Ht, 2 * c + 1, d), 100 * t + 3) if which in (0, 1) else None
+    wV = rnd((Ht, 2 * c + 1, d), 100 * t + 4) if which in (0, 2) else None
+    scale = None if t % 3 else 0.37
+    zb = oracle.relattn_bruteforce(q, k, v, wK, wV, c, scale, causal, lens)
+    zf = oracle.relattn_factored(q, k, v, wK, wV, c, scale, causal, lens)
+    np.testing.assert_allclose(zf, zb, rtol=0, atol=1e-12)
+    rows = [(b, h, i) for b in range(B) for h in range(H) for i in range(n)]
+    zr = oracle.relattn_rows(q, k, v, wK, wV, c, scale, causal, lens, rows=rows)
+    np.testing.assert_allclose(zr, zb.reshape(-1, zb.shape[-1]), rtol=0, atol=1e-12)
+
+
+def test_t5_rows_match_full():
+    B, H, n, d = 2, 3, 40, 8
+    q, k, v = rnd((B, H, n, d), 20), rnd((B, H, n, d), 21), rnd((B, H, n, d), 22)
+    bias = rnd((32, H), 23)
+    lens = [25, 40]
+    for bidir in (True, False):
+        z = oracle.t5_attention(q, k, v, bias, 32, 16, bidir, key_lens=lens)
+        rows = [(b, h, i) for b in range(B) for h in range(H) for i in range(n)]
+        zr = oracle.t5_rows(q, k, v, bias, 32, 16, bidir, key_lens=lens, rows=rows)
+        np.testing.assert_allclose(zr, z.reshape(-1, d), rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# clipping (section "Relative Position Representations: From Arbitrary Edges to
+# Sequences"): offsets range over -(n-1)..n-1, so k >= n-1 clips nothing
+# ---------------------------------------------------------------------------
+
+def _per_offset_attention(q, k, v, tK, tV):
+    """Unclipped relative attention with one vector per offset j-i, written
+    directly from Eq. 3 and Eq. 4 with a^X_ij = t[j - i + n - 1] (no clip)."""
+    n, d = q.shape
+    out = np.zeros_like(v)
+    for i in range(n):
+        e = np.array([q[i] @ (k[j] + tK[j - i + n - 1]) for j in range(n)]) / math.sqrt(d)
+        a = _softmax(e)
+        out[i] = sum(a[j] * (v[j] + tV[j - i + n - 1]) for j in range(n))
+    return out
+
+
+def test_no_clipping_when_k_at_least_n_minus_1():
+    n, d = 7, 4
+    q, k, v = rnd((1, 1, n, d), 30), rnd((1, 1, n, d), 31), rnd((1, 1, n, d), 32)
+    tK, tV = rnd((2 * n - 1, d), 33), rnd((2 * n - 1, d), 34)
+    want = _per_offset_attention(q[0, 0], k[0, 0], v[0, 0], tK, tV)
+    for c in (n - 1, n, n + 3):
+        pad = c - (n - 1)  # table rows for |offset| > n-1 are never reachable
+        wK = np.concatenate([rnd((pad, d), 35), tK, rnd((pad, d), 36)])[None]
+        wV = np.concatenate([rnd((pad, d), 37), tV, rnd((pad, d), 38)])[None]
+        for fn in (oracle.relattn_bruteforce, oracle.relattn_factored):
+            np.testing.assert_allclose(fn(q, k, v, wK, wV, c)[0, 0], want, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# causal masking (decoder self-attention): only offsets <= 0 are visible
+# ---------------------------------------------------------------------------
+
+def test_causal_ignores_positive_offset_rows():
+    B, H, n, d, c = 1, 2, 12, 8, 4
+    q, k, v = rnd((B, H, n, d), 40), rnd((B, H, n, d), 41), rnd((B, H, n, d), 42)
+    wK, wV = rnd((H, 2 * c + 1, d), 43), rnd((H, 2 * c + 1, d), 44)
+    wK2, wV2 = wK.copy(), wV.copy()
+    wK2[:, c + 1:] += 5.0  # rows of offsets 1..k
+    wV2[:, c + 1:] -= 3.0
+    for fn in (oracle.relattn_bruteforce, oracle.relattn_factored):
+        z1 = fn(q, k, v, wK, wV, c, causal=True)
+        z2 = fn(q, k, v, wK2, wV2, c, causal=True)
+        assert np.array_equal(z1, z2)
+
+
+def test_causal_prefix_property():
+    B, H, n, d, c = 1, 2, 15, 8, 3
+    q, k, v = rnd((B, H, n, d), 50), rnd((B, H, n, d), 51), rnd((B, H, n, d), 52)
+    wK, wV = rnd((H, 2 * c + 1, d), 53), rnd((H, 2 * c + 1, d), 54)
+    full = oracle.relattn_factored(q, k, v, wK, wV, c, causal=True)
+    m = 9
+    pre = oracle.relattn_bruteforce(q[..., :m, :], k[..., :m, :], v[..., :m, :],
+                                    wK, wV, c, causal=True)
+    np.testing.assert_allclose(pre, full[..., :m, :], atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# tables shared across heads ("Efficient Implementation", edge sharing)
+# ---------------------------------------------------------------------------
+
+def test_shared_tables_equal_replicated():
+    B, H, n, d, c = 2, 3, 10, 4, 2
+    q, k, v = rnd((B, H, n, d), 60), rnd((B, H, n, d), 61), rnd((B, H, n, d), 62)
+    wK, wV = rnd((1, 2 * c + 1, d), 63), rnd((1, 2 * c + 1, d), 64)
+    for fn in (oracle.relattn_bruteforce, oracle.relattn_factored):
+        z1 = fn(q, k, v, wK, wV, c)
+        z2 = fn(q, k, v, np.repeat(wK, H, 0), np.repeat(wV, H, 0), c)
+        assert np.array_equal(z1, z2)
+
+
+# ---------------------------------------------------------------------------
+# one-hot probe of the offset sign (a^K_ij = w^K_clip(j-i))
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("offset", [-3, -1, 0, 2])
+def test_one_hot_probe_offset_sign(offset):
+    """Only the key-table row of ``offset`` is non-zero and q is parallel to it:
+    each query attends (almost) entirely to key j = i + offset.  With value
+    rows v_j = e_j the output row is that one-hot vector."""
+    n, c = 10, 4
+    d = n + 1
+    q = np.zeros((1, 1, n, d)); q[..., n] = 1.0
+    k = np.zeros((1, 1, n, d))
+    v = np.eye(n, d)[None, None]
+    wK = np.zeros((1, 2 * c + 1, d)); wK[0, offset + c, n] = 60.0
+    z = oracle.relattn_factored(q, k, v, wK, None, c)[0, 0]
+    zb = oracle.relattn_bruteforce(q, k, v, wK, None, c)[0, 0]
+    for i in range(n):
+        j = i + offset
+        if 0 <= j < n:
+            assert np.argmax(z[i]) == j and z[i, j] > 0.999
+            assert np.argmax(zb[i]) == j
+
+
+# ---------------------------------------------------------------------------
+# the pins bite: plant a mistake in the oracle and watch a pin fail
+# ---------------------------------------------------------------------------
+
+def test_planted_sign_flip_is_caught(monkeypatch):
+    monkeypatch.setattr(orc, "clip", lambda x, k: max(-k, min(k, -x)))
+    with pytest.raises(AssertionError):
+        test_shaw_worked_example()
+    with pytest.raises(AssertionError):
+        test_one_hot_probe_offset_sign(2)
+
+
+def test_planted_unscaled_key_term_is_caught(monkeypatch):
+    real = orc.shaw_logits
+
+    def wrong(q, k, aK, clip_k, scale=None):  # scale only on the content term
+        e = real(q, k, None, clip_k, scale)
+        if aK is None:
+            return e
+        R = orc.relative_labels(len(q), clip_k)
+        return e + np.einsum("id,ijd->ij", orc.to_f64(q), orc.to_f64(aK)[R + clip_k])
+
+    monkeypatch.setattr(orc, "shaw_logits", wrong)
+    with pytest.raises(AssertionError):
+        test_shaw_worked_example()
+
+
+def test_planted_dropped_value_term_is_caught(monkeypatch):
+    real = orc.relattn_bruteforce
+    wrong = lambda q, k, v, aK=None, aV=None, *a, **kw: real(q, k, v, aK, None, *a, **kw)
+    monkeypatch.setattr(orc, "relattn_bruteforce", wrong)
+    monkeypatch.setattr(oracle, "relattn_bruteforce", wrong)
+    with pytest.raises(AssertionError):
+        test_k0_closed_form()

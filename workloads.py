@@ -1,0 +1,144 @@
+"""Seeded synthetic workloads for relation-aware attention (inputs only).
+
+This module holds shapes, value distributions and seeds, and nothing of the
+method's arithmetic.  Tests, the benchmark and the smoke check draw their inputs
+from here, so the fp64 oracle and the HIP path see bit-identical operands.
+
+Inputs are drawn in fp32 on the CPU with ``torch.Generator().manual_seed(seed)``
+in the fixed order q, k, v, key table, value table (or the T5 bias table), key
+lengths, and are then cast once to the workload's dtype.
+
+The shapes are those of the Transformer base and big models of "Self-Attention
+with Relative Position Representations" (§5, Evaluation Methodology: d_z = 64,
+8 or 16 heads), a long-sequence stress shape, and the T5 default bucketing
+(B = 32, max_distance = 128) of "Relative position embeddings", section "T5".
+The pages train on WMT14 translation data; these synthetic tensors of the same
+attention shapes stand in for it (no data or trained weights are needed to time
+or check the forward operator).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import torch
+
+SEED_BASE = 20260000
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    config_id: int
+    description: str
+    batch: int
+    heads: int
+    n: int
+    d: int
+    clip: int = 0
+    dtype: torch.dtype = torch.bfloat16
+    qkv_std: float = 1.0
+    table_std: float = 0.02
+    use_key_table: bool = True
+    use_value_table: bool = True
+    causal: bool = False
+    len_range: tuple | None = None          # inclusive [lo, hi] key lengths
+    t5: dict | None = None                  # num_buckets, max_distance, bidirectional
+    extra: dict = field(default_factory=dict)
+
+    @property
+    def seed(self) -> int:
+        return SEED_BASE + self.config_id
+
+
+WORKLOADS = {
+    "tiny": Workload(
+        name="tiny", config_id=1,
+        description="tiny fp32 check: B1 H2 n32 d16 clip 4, key+value tables",
+        batch=1, heads=2, n=32, d=16, clip=4, dtype=torch.float32,
+        qkv_std=1.0, table_std=0.1),
+    "base": Workload(
+        name="base", config_id=2,
+        description="Transformer-base encoder self-attention: B32 H8 n128 d64 "
+                    "clip 16, key padding lengths U[64,128], key+value tables",
+        batch=32, heads=8, n=128, d=64, clip=16, len_range=(64, 128)),
+    "big_causal_k": Workload(
+        name="big_causal_k", config_id=3,
+        description="Transformer-big decoder causal self-attention: B16 H16 "
+                    "n256 d64 clip 16, key table only",
+        batch=16, heads=16, n=256, d=64, clip=16, causal=True,
+        use_value_table=False),
+    "big_causal_kv": Workload(
+        name="big_causal_kv", config_id=3,
+        description="Transformer-big decoder causal self-attention: B16 H16 "
+                    "n256 d64 clip 16, key+value tables",
+        batch=16, heads=16, n=256, d=64, clip=16, causal=True),
+    "long": Workload(
+        name="long", config_id=4,
+        description="long-sequence causal stress: B2 H16 n4096 d128 clip 64, "
+                    "key+value tables",
+        batch=2, heads=16, n=4096, d=128, clip=64, causal=True),
+    "t5": Workload(
+        name="t5", config_id=5,
+        description="T5 bucketed scalar bias: B8 H12 n1024 d64, bidirectional, "
+                    "32 buckets, max_distance 128, no 1/sqrt(d), key padding "
+                    "lengths U[512,1024]",
+        batch=8, heads=12, n=1024, d=64, qkv_std=1.0 / 8.0, table_std=1.0,
+        use_key_table=False, use_value_table=False, len_range=(512, 1024),
+        t5={"num_buckets": 32, "max_distance": 128, "bidirectional": True}),
+}
+
+
+def make_inputs(w: Workload | str, *, batch=None, n=None, heads=None,
+                seed=None) -> dict:
+    """CPU tensors for workload ``w`` (optionally with a smaller batch/n/heads).
+
+    Returns a dict with q, k, v ([B, H, n, d], workload dtype), key_table and
+    value_table ([H, 2c+1, d] or None), t5_bias ([num_buckets, H] fp32 or None)
+    and key_lens (int32 [B] or None).  Every tensor is drawn even when the
+    workload drops it, so the draw order (and thus the bits of what is kept)
+    does not depend on the variant.
+    """
+    if isinstance(w, str):
+        w = WORKLOADS[w]
+    B = batch or w.batch
+    H = heads or w.heads
+    N = n or w.n
+    g = torch.Generator().manual_seed(w.seed if seed is None else seed)
+
+    def normal(shape, std):
+        return torch.randn(shape, generator=g, dtype=torch.float32) * std
+
+    q = normal((B, H, N, w.d), w.qkv_std)
+    k = normal((B, H, N, w.d), w.qkv_std)
+    v = normal((B, H, N, w.d), w.qkv_std)
+    out = {"q": q.to(w.dtype), "k": k.to(w.dtype), "v": v.to(w.dtype),
+           "key_table": None, "value_table": None, "t5_bias": None,
+           "key_lens": None}
+    if w.t5 is None:
+        rows = 2 * w.clip + 1
+        kt = normal((H, rows, w.d), w.table_std)
+        vt = normal((H, rows, w.d), w.table_std)
+        if w.use_key_table:
+            out["key_table"] = kt.to(w.dtype)
+        if w.use_value_table:
+            out["value_table"] = vt.to(w.dtype)
+    else:
+        out["t5_bias"] = normal((w.t5["num_buckets"], H), w.table_std)
+    if w.len_range is not None:
+        lo, hi = w.len_range
+        lo, hi = min(lo, N), min(hi, N)
+        out["key_lens"] = torch.randint(lo, hi + 1, (B,), generator=g,
+                                        dtype=torch.int32)
+    return out
+
+
+def attention_kwargs(w: Workload | str) -> dict:
+    """Non-tensor operator arguments of a workload."""
+    if isinstance(w, str):
+        w = WORKLOADS[w]
+    kw = {"causal": w.causal}
+    if w.t5 is None:
+        kw["clip"] = w.clip
+    else:
+        kw.update(w.t5)
+    return kw
