@@ -1,0 +1,142 @@
+/*
+ * librelattn: fused forward of relation-aware self-attention on AMD MI355X
+ * (gfx950), plus the T5 bucketed scalar-bias variant.
+ *
+ * What is computed (one head; q_i, k_j, v_j are rows of q, k, v):
+ *
+ *   Shaw et al. ("Self-Attention with Relative Position Representations",
+ *   section 3.4, Eq. 3 and Eq. 4, with the tables of section "Relative Position
+ *   Representations: From Arbitrary Edges to Sequences"):
+ *       r(i, j) = clip(j - i, k) = max(-k, min(k, j - i))
+ *       e_ij    = scale * q_i . (k_j + wK[r(i, j) + k])
+ *       alpha   = softmax over the visible keys j of e_i.
+ *       z_i     = sum_j alpha_ij * (v_j + wV[r(i, j) + k])
+ *     A missing table (NULL) counts as all zeros.  scale <= 0 selects
+ *     1/sqrt(d).  The scale multiplies both terms of e (Eq. 5); wV is unscaled.
+ *
+ *   T5 ("Relative position embeddings", section "T5"):
+ *       e_ij = scale * q_i . k_j + bias[beta(j - i), h],  scale <= 0 selects 1
+ *     where beta is the bucket function of that section.  Bidirectional: half
+ *     = num_buckets/2 buckets per sign, keys after the query (j > i) use the
+ *     upper half; unidirectional: all buckets for j <= i, bucket 0 for j > i.
+ *     B_exact = half/2; the floor in beta is taken of the exact real value.
+ *
+ *   Masks (no page defines them): causal hides keys j > i; key_lens[b] hides
+ *   keys j >= key_lens[b] (clamped to [0, n]) of batch b.  A hidden key adds
+ *   neither v_j nor wV.  A query row with no visible key outputs zeros.
+ *
+ * Conventions for every entry point:
+ *   - All tensor data pointers are DEVICE pointers owned by the caller.  The
+ *     library allocates nothing and keeps no state between calls; it is
+ *     thread-safe.  Equal inputs give bit-identical outputs.
+ *   - relattn_fwd only enqueues work on `stream` (a hipStream_t, NULL = the
+ *     default stream) and returns.  Buffers must stay alive until the stream
+ *     has passed that point.  Faults during execution surface at the caller's
+ *     next synchronisation.
+ *   - Return value: RELATTN_OK (0) or a negative relattn_status.  A message
+ *     with the detail is kept per thread (relattn_last_error).  No exception or
+ *     abort crosses this interface.
+ */
+#ifndef RELATTN_H
+#define RELATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RELATTN_VERSION 1
+
+typedef enum {
+  RELATTN_OK = 0,
+  RELATTN_ERR_INVALID_ARGUMENT = -1, /* null/shape/stride/parameter error     */
+  RELATTN_ERR_UNSUPPORTED = -2,      /* valid, but outside what is built      */
+  RELATTN_ERR_NO_DEVICE = -3,        /* no usable HIP device                  */
+  RELATTN_ERR_LAUNCH_FAILED = -4     /* HIP reported an error at launch        */
+} relattn_status;
+
+typedef enum { RELATTN_F32 = 0, RELATTN_BF16 = 1 } relattn_dtype;
+
+/* A strided tensor view.  `stride` counts ELEMENTS, not bytes.  The last
+ * dimension must be contiguous (stride 1).  Dimensions past `ndim` are ignored. */
+typedef struct {
+  void* data;          /* device pointer (may be NULL only if the view is empty) */
+  int32_t dtype;       /* relattn_dtype */
+  int32_t ndim;
+  int64_t shape[4];
+  int64_t stride[4];
+} relattn_tensor;
+
+typedef struct {
+  int32_t causal;            /* nonzero: hide keys j > i                    */
+  const int32_t* key_lens;   /* device int32[B] or NULL (all n keys visible) */
+} relattn_mask;
+
+typedef struct {
+  int32_t num_buckets;       /* B of the T5 section; even when bidirectional */
+  int32_t max_distance;      /* D_max; must exceed B_exact                   */
+  int32_t bidirectional;     /* nonzero: split buckets by sign of j - i      */
+} relattn_t5_params;
+
+/*
+ * relattn_fwd: enqueue the forward pass.
+ *
+ *   q, k, v, out : [B, H, n, d], one dtype (F32 or BF16), d in {16,32,64,128}.
+ *                  Rows must start 16-byte aligned (data pointer and the
+ *                  strides of dims 0..2 in bytes are multiples of 16).
+ *   wK, wV       : Shaw tables [Ht, 2*clip_k + 1, d] of the same dtype, with
+ *                  Ht = H (one table per head) or Ht = 1 (shared by all
+ *                  heads).  Row r holds offset r - clip_k.  Either may be NULL.
+ *   t5_bias, t5  : T5 bias table [num_buckets, H] (F32) and its parameters.
+ *                  Given together or not at all; excludes wK and wV.
+ *   clip_k       : k >= 0 of clip(j - i, k) (ignored for T5).
+ *   scale        : logit scale; <= 0 picks 1/sqrt(d) (Shaw) or 1 (T5).
+ *   mask         : NULL = no mask.
+ *   stream       : hipStream_t to enqueue on (NULL = default stream).
+ *
+ * Errors: INVALID_ARGUMENT for inconsistent shapes, dtypes, strides or
+ * parameters; UNSUPPORTED for a head size outside {16,32,64,128}, misaligned
+ * rows, or a label window (2*clip_k+1, or 2n-1 when clip_k >= n) or T5 bias
+ * window too large for on-chip memory; NO_DEVICE; LAUNCH_FAILED.  Empty
+ * problems (B, H or n equal to 0) return RELATTN_OK and launch nothing.
+ */
+int relattn_fwd(const relattn_tensor* q, const relattn_tensor* k,
+                const relattn_tensor* v, const relattn_tensor* wK,
+                const relattn_tensor* wV, const relattn_tensor* t5_bias,
+                const relattn_t5_params* t5, int32_t clip_k, float scale,
+                const relattn_mask* mask, relattn_tensor* out, void* stream);
+
+/* relattn_validate: the argument checks of relattn_fwd, run on the host only.
+ * Makes no HIP call and touches no device memory, so it works without a GPU.
+ * Returns the status relattn_fwd would return before launching. */
+int relattn_validate(const relattn_tensor* q, const relattn_tensor* k,
+                     const relattn_tensor* v, const relattn_tensor* wK,
+                     const relattn_tensor* wV, const relattn_tensor* t5_bias,
+                     const relattn_t5_params* t5, int32_t clip_k, float scale,
+                     const relattn_mask* mask, const relattn_tensor* out);
+
+/* relattn_debug_indices: write, for every offset delta = j - i in
+ * [-(n-1), n-1], the integer index the kernels use for that offset into
+ * out_dev[delta + n - 1] (device int32[2n-1]):
+ *   t5 == NULL : the table row clip(delta, clip_k) + clip_k   (clip section)
+ *   t5 != NULL : the bucket beta(delta)                       (T5 section)
+ * computed on the device by the same functions the attention kernels use.
+ * Enqueued on `stream`; same error codes as relattn_fwd. */
+int relattn_debug_indices(int32_t n, int32_t clip_k, const relattn_t5_params* t5,
+                          int32_t* out_dev, void* stream);
+
+/* Static text for a status code. */
+const char* relattn_strerror(int status);
+
+/* Detail of the last error raised on the calling thread ("" if none). */
+const char* relattn_last_error(void);
+
+/* RELATTN_VERSION of the built library. */
+int relattn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RELATTN_H */

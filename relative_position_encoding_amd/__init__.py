@@ -1,0 +1,186 @@
+"""Python binding of librelattn (relation-aware self-attention on MI355X).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of librelattn.so, reached through its C ABI (include/relattn.h).
+PyTorch supplies device memory and the current stream.  There is no fallback:
+if the library is missing, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = ["fwd", "validate", "debug_indices", "RelattnError", "library_path",
+           "OK", "INVALID_ARGUMENT", "UNSUPPORTED", "NO_DEVICE", "LAUNCH_FAILED"]
+
+OK, INVALID_ARGUMENT, UNSUPPORTED, NO_DEVICE, LAUNCH_FAILED = 0, -1, -2, -3, -4
+_F32, _BF16 = 0, 1
+
+library_path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "librelattn.so")
+
+
+class RelattnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+class _Tensor(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int32),
+                ("ndim", ctypes.c_int32), ("shape", ctypes.c_int64 * 4),
+                ("stride", ctypes.c_int64 * 4)]
+
+
+class _Mask(ctypes.Structure):
+    _fields_ = [("causal", ctypes.c_int32), ("key_lens", ctypes.c_void_p)]
+
+
+class _T5(ctypes.Structure):
+    _fields_ = [("num_buckets", ctypes.c_int32), ("max_distance", ctypes.c_int32),
+                ("bidirectional", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(library_path):
+        raise RuntimeError(
+            f"{library_path} is not built; run `python -m relative_position_encoding_amd.build`")
+    lib = ctypes.CDLL(library_path)
+    P = ctypes.POINTER
+    args = [P(_Tensor), P(_Tensor), P(_Tensor), P(_Tensor), P(_Tensor), P(_Tensor),
+            P(_T5), ctypes.c_int32, ctypes.c_float, P(_Mask), P(_Tensor)]
+    lib.relattn_fwd.argtypes = args + [ctypes.c_void_p]
+    lib.relattn_fwd.restype = ctypes.c_int
+    lib.relattn_validate.argtypes = args
+    lib.relattn_validate.restype = ctypes.c_int
+    lib.relattn_debug_indices.argtypes = [ctypes.c_int32, ctypes.c_int32, P(_T5),
+                                          ctypes.c_void_p, ctypes.c_void_p]
+    lib.relattn_debug_indices.restype = ctypes.c_int
+    lib.relattn_strerror.argtypes = [ctypes.c_int]
+    lib.relattn_strerror.restype = ctypes.c_char_p
+    lib.relattn_last_error.argtypes = []
+    lib.relattn_last_error.restype = ctypes.c_char_p
+    lib.relattn_version.argtypes = []
+    lib.relattn_version.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.float32:
+        return _F32
+    if t.dtype == torch.bfloat16:
+        return _BF16
+    return 99  # rejected by the library
+
+
+def _view(t):
+    if t is None:
+        return None
+    v = _Tensor()
+    v.data = t.data_ptr() or None
+    v.dtype = _dtype_code(t)
+    v.ndim = t.dim()
+    for i in range(min(t.dim(), 4)):
+        v.shape[i] = t.shape[i]
+        v.stride[i] = t.stride(i)
+    return v
+
+
+def _ref(x):
+    return ctypes.byref(x) if x is not None else None
+
+
+def _args(q, k, v, wK, wV, t5_bias, clip, causal, key_lens, num_buckets,
+          max_distance, bidirectional, scale, out):
+    keep = []  # keep ctypes objects alive through the call
+    views = [_view(x) for x in (q, k, v, wK, wV, t5_bias)]
+    keep += views
+    t5 = None
+    if t5_bias is not None:
+        t5 = _T5(int(num_buckets), int(max_distance), 1 if bidirectional else 0)
+    mask = None
+    if causal or key_lens is not None:
+        mask = _Mask(1 if causal else 0, key_lens.data_ptr() if key_lens is not None else None)
+    outv = _view(out)
+    keep += [t5, mask, outv]
+    args = [_ref(x) for x in views] + [_ref(t5), int(clip),
+                                        float(0.0 if scale is None else scale),
+                                        _ref(mask), _ref(outv)]
+    return args, keep
+
+
+def _raise(lib, status):
+    msg = lib.relattn_last_error().decode() or lib.relattn_strerror(status).decode()
+    raise RelattnError(status, f"relattn: {lib.relattn_strerror(status).decode()}: {msg}")
+
+
+def fwd(q, k, v, wK=None, wV=None, *, clip=0, causal=False, key_lens=None,
+        t5_bias=None, num_buckets=32, max_distance=128, bidirectional=True,
+        scale=None, out=None, stream=None):
+    """Relation-aware self-attention forward (or T5 bias when t5_bias is given).
+
+    q, k, v: [B, H, n, d] CUDA(HIP) tensors (float32 or bfloat16);
+    wK, wV: [H or 1, 2*clip+1, d] tables of the same dtype (None = absent);
+    key_lens: int32 [B] device tensor; t5_bias: float32 [num_buckets, H].
+    Enqueued on ``stream`` (default: torch's current stream); returns ``out``.
+    """
+    import torch
+    lib = _load()
+    if key_lens is not None and key_lens.dtype != torch.int32:
+        raise RelattnError(INVALID_ARGUMENT, "relattn: key_lens must be int32")
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    elif hasattr(stream, "cuda_stream"):
+        stream = stream.cuda_stream
+    args, keep = _args(q, k, v, wK, wV, t5_bias, clip, causal, key_lens, num_buckets,
+                       max_distance, bidirectional, scale, out)
+    st = lib.relattn_fwd(*args, ctypes.c_void_p(stream))
+    del keep
+    if st != OK:
+        _raise(lib, st)
+    return out
+
+
+def validate(q, k, v, wK=None, wV=None, *, clip=0, causal=False, key_lens=None,
+             t5_bias=None, num_buckets=32, max_distance=128, bidirectional=True,
+             scale=None, out=None):
+    """Host-only argument check of ``fwd``; returns the library status code."""
+    lib = _load()
+    if out is None:
+        out = q
+    args, keep = _args(q, k, v, wK, wV, t5_bias, clip, causal, key_lens, num_buckets,
+                       max_distance, bidirectional, scale, out)
+    st = lib.relattn_validate(*args)
+    del keep
+    return st
+
+
+def last_error() -> str:
+    return _load().relattn_last_error().decode()
+
+
+def debug_indices(n, clip=0, *, t5=False, num_buckets=32, max_distance=128,
+                  bidirectional=True, device="cuda", stream=None):
+    """Per-offset integer indices computed on the GPU by the kernels' own index
+    functions: entry delta + n - 1 holds clip(delta, clip) + clip, or the T5
+    bucket of delta when ``t5`` is true."""
+    import torch
+    lib = _load()
+    out = torch.empty(2 * n - 1, dtype=torch.int32, device=device)
+    if stream is None:
+        stream = torch.cuda.current_stream(out.device).cuda_stream
+    t5p = _T5(int(num_buckets), int(max_distance), 1 if bidirectional else 0) if t5 else None
+    st = lib.relattn_debug_indices(int(n), int(clip), _ref(t5p), ctypes.c_void_p(out.data_ptr()),
+                                   ctypes.c_void_p(stream))
+    if st != OK:
+        _raise(lib, st)
+    return out

@@ -1,0 +1,430 @@
+// C-ABI entry points of librelattn: argument validation (host only), plan
+// selection and launch.  The operation is defined in include/relattn.h.
+#include "relattn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <atomic>
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <string>
+#include <vector>
+
+#include "relattn_internal.h"
+
+namespace {
+
+using relattn::FwdParams;
+using relattn::LaunchCfg;
+using relattn::RelMode;
+using relattn::T5Buckets;
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+constexpr size_t kMaxLdsBytes = 160 * 1024;  // LDS per workgroup on gfx950
+constexpr int64_t kMaxSeq = int64_t(1) << 30;
+
+size_t elem_size(int dtype) { return dtype == RELATTN_BF16 ? 2 : 4; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int64_t numel(const relattn_tensor* t) {
+  int64_t n = 1;
+  for (int i = 0; i < t->ndim; ++i) n *= t->shape[i];
+  return n;
+}
+
+// Shape-independent checks of a strided view with `ndim` dims, innermost
+// contiguous; `vec_rows`: rows are read with 16-byte vector loads.
+int check_view(const relattn_tensor* t, const char* name, int ndim, bool vec_rows) {
+  if (!t) return fail(RELATTN_ERR_INVALID_ARGUMENT, "%s is NULL", name);
+  if (t->ndim != ndim)
+    return fail(RELATTN_ERR_INVALID_ARGUMENT, "%s must have %d dims, got %d", name, ndim,
+                t->ndim);
+  if (t->dtype != RELATTN_F32 && t->dtype != RELATTN_BF16)
+    return fail(RELATTN_ERR_INVALID_ARGUMENT, "%s has unknown dtype %d", name, t->dtype);
+  for (int i = 0; i < ndim; ++i) {
+    if (t->shape[i] < 0)
+      return fail(RELATTN_ERR_INVALID_ARGUMENT, "%s shape[%d] < 0", name, i);
+    if (t->stride[i] < 0)
+      return fail(RELATTN_ERR_INVALID_ARGUMENT, "%s stride[%d] < 0", name, i);
+  }
+  if (numel(t) == 0) return RELATTN_OK;
+  if (!t->data) return fail(RELATTN_ERR_INVALID_ARGUMENT, "%s data is NULL", name);
+  if (t->stride[ndim - 1] != 1)
+    return fail(RELATTN_ERR_UNSUPPORTED, "%s: innermost dimension must be contiguous", name);
+  if (vec_rows) {
+    const size_t es = elem_size(t->dtype);
+    if (!aligned16(t->data))
+      return fail(RELATTN_ERR_UNSUPPORTED, "%s: data pointer is not 16-byte aligned", name);
+    for (int i = 0; i + 1 < ndim; ++i)
+      if ((t->stride[i] * es) % 16 != 0)
+        return fail(RELATTN_ERR_UNSUPPORTED, "%s: stride[%d] is not a multiple of 16 bytes",
+                    name, i);
+  }
+  return RELATTN_OK;
+}
+
+// ---- T5 bucket thresholds, exact ------------------------------------------
+// floor(nlog * ln(a/ex) / ln(D/ex)) >= t  <=>  a^nlog * ex^t >= D^t * ex^nlog,
+// evaluated with arbitrary-precision unsigned integers.
+struct Big {
+  std::vector<uint32_t> w{1u};
+  void mul(uint32_t m) {
+    uint64_t carry = 0;
+    for (auto& d : w) {
+      const uint64_t t = uint64_t(d) * m + carry;
+      d = uint32_t(t);
+      carry = t >> 32;
+    }
+    if (carry) w.push_back(uint32_t(carry));
+  }
+};
+
+int cmp_big(const Big& x, const Big& y) {
+  size_t nx = x.w.size(), ny = y.w.size();
+  while (nx > 1 && x.w[nx - 1] == 0) --nx;
+  while (ny > 1 && y.w[ny - 1] == 0) --ny;
+  if (nx != ny) return nx < ny ? -1 : 1;
+  for (size_t i = nx; i-- > 0;)
+    if (x.w[i] != y.w[i]) return x.w[i] < y.w[i] ? -1 : 1;
+  return 0;
+}
+
+bool log_bucket_at_least(uint32_t a, uint32_t ex, uint32_t D, int nlog, int t) {
+  Big lhs, rhs;
+  for (int i = 0; i < nlog; ++i) lhs.mul(a);
+  for (int i = 0; i < t; ++i) lhs.mul(ex);
+  for (int i = 0; i < t; ++i) rhs.mul(D);
+  for (int i = 0; i < nlog; ++i) rhs.mul(ex);
+  return cmp_big(lhs, rhs) >= 0;
+}
+
+int check_t5(const relattn_t5_params* t5, T5Buckets* out) {
+  const int nb = t5->num_buckets;
+  const bool bidir = t5->bidirectional != 0;
+  if (nb < 2) return fail(RELATTN_ERR_INVALID_ARGUMENT, "num_buckets must be >= 2");
+  if (bidir && (nb % 2 != 0 || nb < 4))
+    return fail(RELATTN_ERR_INVALID_ARGUMENT,
+                "bidirectional bucketing needs an even num_buckets >= 4");
+  const int half = bidir ? nb / 2 : nb;
+  const int exact = half / 2;
+  const int nlog = half - exact;
+  if (t5->max_distance <= exact)
+    return fail(RELATTN_ERR_INVALID_ARGUMENT, "max_distance (%d) must exceed B_exact (%d)",
+                t5->max_distance, exact);
+  if (nlog - 1 > relattn::kMaxT5Thresholds)
+    return fail(RELATTN_ERR_UNSUPPORTED, "num_buckets too large (at most %d log buckets)",
+                relattn::kMaxT5Thresholds + 1);
+  if (!out) return RELATTN_OK;
+  // Memoised per thread: the thresholds depend only on (nb, D, bidir).
+  thread_local int c_nb = -1, c_d = -1, c_bi = -1;
+  thread_local T5Buckets c_tb;
+  if (c_nb == nb && c_d == t5->max_distance && c_bi == (int)bidir) {
+    *out = c_tb;
+    return RELATTN_OK;
+  }
+  T5Buckets tb = {};
+  tb.half = half;
+  tb.exact = exact;
+  tb.nlog = nlog;
+  tb.bidir = bidir ? 1 : 0;
+  const uint32_t D = (uint32_t)t5->max_distance, ex = (uint32_t)exact;
+  for (int t = 1; t < nlog; ++t) {
+    uint32_t lo = ex, hi = D;  // the condition holds at a = D
+    while (lo < hi) {
+      const uint32_t mid = lo + (hi - lo) / 2;
+      if (log_bucket_at_least(mid, ex, D, nlog, t)) hi = mid;
+      else lo = mid + 1;
+    }
+    tb.thr[t - 1] = (int32_t)lo;
+  }
+  c_nb = nb;
+  c_d = t5->max_distance;
+  c_bi = (int)bidir;
+  c_tb = tb;
+  *out = tb;
+  return RELATTN_OK;
+}
+
+struct Plan {
+  bool empty = false;
+  bool bf16 = false;
+  int d = 0;
+  LaunchCfg cfg{2, 64};
+  RelMode mode = relattn::kRelNone;
+  bool has_wk = false, has_wv = false;
+  FwdParams p{};
+};
+
+int check_table(const relattn_tensor* t, const char* name, const relattn_tensor* q,
+                int clip_k) {
+  int st = check_view(t, name, 3, true);
+  if (st) return st;
+  if (t->dtype != q->dtype)
+    return fail(RELATTN_ERR_INVALID_ARGUMENT, "%s dtype differs from q", name);
+  const int64_t H = q->shape[1], d = q->shape[3];
+  if (!(t->shape[0] == H || t->shape[0] == 1))
+    return fail(RELATTN_ERR_INVALID_ARGUMENT, "%s: shape[0] must be H (%lld) or 1", name,
+                (long long)H);
+  if (t->shape[1] != 2 * (int64_t)clip_k + 1)
+    return fail(RELATTN_ERR_INVALID_ARGUMENT, "%s: shape[1] must be 2*clip_k+1 = %lld", name,
+                (long long)(2 * (int64_t)clip_k + 1));
+  if (t->shape[2] != d)
+    return fail(RELATTN_ERR_INVALID_ARGUMENT, "%s: shape[2] must equal d = %lld", name,
+                (long long)d);
+  return RELATTN_OK;
+}
+
+int make_plan(const relattn_tensor* q, const relattn_tensor* k, const relattn_tensor* v,
+              const relattn_tensor* wK, const relattn_tensor* wV,
+              const relattn_tensor* t5_bias, const relattn_t5_params* t5, int32_t clip_k,
+              float scale, const relattn_mask* mask, const relattn_tensor* out, Plan* plan,
+              bool want_t5_table) {
+  int st;
+  if ((st = check_view(q, "q", 4, true))) return st;
+  if ((st = check_view(k, "k", 4, true))) return st;
+  if ((st = check_view(v, "v", 4, true))) return st;
+  if ((st = check_view(out, "out", 4, true))) return st;
+  const relattn_tensor* others[3] = {k, v, out};
+  const char* names[3] = {"k", "v", "out"};
+  for (int t = 0; t < 3; ++t) {
+    if (others[t]->dtype != q->dtype)
+      return fail(RELATTN_ERR_INVALID_ARGUMENT, "%s dtype differs from q", names[t]);
+    for (int i = 0; i < 4; ++i)
+      if (others[t]->shape[i] != q->shape[i])
+        return fail(RELATTN_ERR_INVALID_ARGUMENT, "%s shape differs from q in dim %d",
+                    names[t], i);
+  }
+  const int64_t B = q->shape[0], H = q->shape[1], n = q->shape[2], d = q->shape[3];
+  if (!(d == 16 || d == 32 || d == 64 || d == 128))
+    return fail(RELATTN_ERR_UNSUPPORTED, "head size d = %lld is not one of 16, 32, 64, 128",
+                (long long)d);
+  if (n > kMaxSeq)
+    return fail(RELATTN_ERR_UNSUPPORTED, "sequence length %lld exceeds 2^30", (long long)n);
+  if (std::isnan(scale) || std::isinf(scale))
+    return fail(RELATTN_ERR_INVALID_ARGUMENT, "scale must be finite");
+
+  const bool is_t5 = t5_bias != nullptr || t5 != nullptr;
+  if ((t5_bias == nullptr) != (t5 == nullptr))
+    return fail(RELATTN_ERR_INVALID_ARGUMENT, "t5_bias and t5 params must be given together");
+  if (is_t5 && (wK || wV))
+    return fail(RELATTN_ERR_INVALID_ARGUMENT, "T5 bias excludes the wK/wV tables");
+  if (!is_t5 && clip_k < 0)
+    return fail(RELATTN_ERR_INVALID_ARGUMENT, "clip_k must be >= 0");
+  if (!is_t5 && (int64_t)clip_k > kMaxSeq)
+    return fail(RELATTN_ERR_UNSUPPORTED, "clip_k exceeds 2^30");
+  if (wK && (st = check_table(wK, "wK", q, clip_k))) return st;
+  if (wV && (st = check_table(wV, "wV", q, clip_k))) return st;
+  T5Buckets tb = {};
+  if (is_t5) {
+    if ((st = check_view(t5_bias, "t5_bias", 2, false))) return st;
+    if (t5_bias->dtype != RELATTN_F32)
+      return fail(RELATTN_ERR_INVALID_ARGUMENT, "t5_bias must be F32");
+    if (t5_bias->shape[0] != t5->num_buckets || t5_bias->shape[1] != H)
+      return fail(RELATTN_ERR_INVALID_ARGUMENT, "t5_bias must be [num_buckets, H]");
+    if ((st = check_t5(t5, want_t5_table ? &tb : nullptr))) return st;
+  }
+  if (mask && mask->key_lens && (reinterpret_cast<uintptr_t>(mask->key_lens) & 3u))
+    return fail(RELATTN_ERR_INVALID_ARGUMENT, "key_lens is not 4-byte aligned");
+
+  Plan& P = *plan;
+  P.bf16 = q->dtype == RELATTN_BF16;
+  P.d = (int)d;
+  P.mode = is_t5 ? relattn::kRelT5 : ((wK || wV) ? relattn::kRelShaw : relattn::kRelNone);
+  P.has_wk = wK != nullptr;
+  P.has_wv = wV != nullptr;
+  P.empty = (B == 0 || H == 0 || n == 0);
+  if (P.empty) return RELATTN_OK;
+
+  FwdParams& p = P.p;
+  p.B = (int32_t)B;
+  p.H = (int32_t)H;
+  p.n = (int32_t)n;
+  p.causal = (mask && mask->causal) ? 1 : 0;
+  p.key_lens = mask ? mask->key_lens : nullptr;
+  p.clip = is_t5 ? 0 : clip_k;
+  const bool causal = p.causal != 0;
+  // Label rows any query can reach: offsets j - i lie in [-(n-1), n-1], or in
+  // [-(n-1), 0] under the causal mask.
+  if (P.mode == relattn::kRelShaw) {
+    const int64_t c = clip_k;
+    const int64_t r_lo = std::max<int64_t>(0, c - (n - 1));
+    const int64_t r_hi = causal ? c : std::min<int64_t>(2 * c, c + n - 1);
+    p.r_lo = (int32_t)r_lo;
+    p.nr = (int32_t)(r_hi - r_lo + 1);
+  } else {
+    p.r_lo = 0;
+    p.nr = 1;
+  }
+  p.t5_dist = is_t5 ? (int32_t)std::min<int64_t>(t5->max_distance, n - 1) : 0;
+  p.t5 = tb;
+  const float s = scale > 0.f ? scale
+                              : (is_t5 ? 1.f : 1.f / std::sqrt((float)d));
+  p.scale_log2 = s * 1.4426950408889634f;
+
+  // Workgroup shape: 32 query rows per wave; prefer 4 waves when that still
+  // gives at least two workgroups per compute unit (256 CUs).
+  auto lds_ok = [&](const LaunchCfg& c) {
+    return relattn::lds_bytes(P.bf16, P.d, c, P.mode, P.has_wv, p.nr, p.t5_dist) <=
+           kMaxLdsBytes;
+  };
+  std::vector<LaunchCfg> order;
+  if (P.bf16) {
+    const int64_t wgs4 = B * H * ((n + 127) / 128);
+    if (wgs4 >= 512) order = {{4, 64}, {2, 64}};
+    else order = {{2, 64}, {4, 64}};
+  } else {
+    if (n <= 32) order = {{1, 32}, {2, 32}};
+    else order = {{2, 32}, {1, 32}};
+  }
+  bool found = false;
+  for (const auto& c : order)
+    if (lds_ok(c)) {
+      P.cfg = c;
+      found = true;
+      break;
+    }
+  if (!found) {
+    if (P.mode == relattn::kRelT5)
+      return fail(RELATTN_ERR_UNSUPPORTED,
+                  "T5 offset window 2*min(max_distance, n-1)+1 = %d does not fit on chip",
+                  2 * p.t5_dist + 1);
+    return fail(RELATTN_ERR_UNSUPPORTED,
+                "label window of %d rows (2*clip_k+1 clipped to 2n-1) does not fit on chip",
+                p.nr);
+  }
+  const int br = 32 * P.cfg.waves;
+  p.n_qtiles = (int32_t)((n + br - 1) / br);
+  if (B * H * (int64_t)p.n_qtiles > INT32_MAX)
+    return fail(RELATTN_ERR_UNSUPPORTED, "too many workgroups (B*H*ceil(n/%d))", br);
+
+  p.q = q->data;
+  p.k = k->data;
+  p.v = v->data;
+  p.o = out->data;
+  p.q_sb = q->stride[0]; p.q_sh = q->stride[1]; p.q_sn = q->stride[2];
+  p.k_sb = k->stride[0]; p.k_sh = k->stride[1]; p.k_sn = k->stride[2];
+  p.v_sb = v->stride[0]; p.v_sh = v->stride[1]; p.v_sn = v->stride[2];
+  p.o_sb = out->stride[0]; p.o_sh = out->stride[1]; p.o_sn = out->stride[2];
+  if (wK) {
+    p.wk = wK->data;
+    p.wk_sh = wK->shape[0] == 1 ? 0 : wK->stride[0];
+    p.wk_sr = wK->stride[1];
+  }
+  if (wV) {
+    p.wv = wV->data;
+    p.wv_sh = wV->shape[0] == 1 ? 0 : wV->stride[0];
+    p.wv_sr = wV->stride[1];
+  }
+  if (is_t5) {
+    p.t5_bias = static_cast<const float*>(t5_bias->data);
+    p.tb_sb = t5_bias->stride[0];
+    p.tb_sh = t5_bias->stride[1];
+  }
+  return RELATTN_OK;
+}
+
+// The device the calling thread has selected must be a gfx950.
+int check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    (void)hipGetLastError();
+    return fail(RELATTN_ERR_NO_DEVICE, "no HIP device available");
+  }
+  static std::atomic<int> known[64];  // 0 unknown, 1 gfx950, 2 other
+  const int slot = dev < 64 ? dev : -1;
+  int state = slot >= 0 ? known[slot].load(std::memory_order_relaxed) : 0;
+  if (state == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+      (void)hipGetLastError();
+      return fail(RELATTN_ERR_NO_DEVICE, "cannot query HIP device %d", dev);
+    }
+    state = std::string(prop.gcnArchName).rfind("gfx950", 0) == 0 ? 1 : 2;
+    if (slot >= 0) known[slot].store(state, std::memory_order_relaxed);
+  }
+  if (state != 1) return fail(RELATTN_ERR_UNSUPPORTED, "device %d is not a gfx950", dev);
+  return RELATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int relattn_validate(const relattn_tensor* q, const relattn_tensor* k, const relattn_tensor* v,
+                     const relattn_tensor* wK, const relattn_tensor* wV,
+                     const relattn_tensor* t5_bias, const relattn_t5_params* t5,
+                     int32_t clip_k, float scale, const relattn_mask* mask,
+                     const relattn_tensor* out) {
+  g_last_error.clear();
+  Plan plan;
+  return make_plan(q, k, v, wK, wV, t5_bias, t5, clip_k, scale, mask, out, &plan, false);
+}
+
+int relattn_fwd(const relattn_tensor* q, const relattn_tensor* k, const relattn_tensor* v,
+                const relattn_tensor* wK, const relattn_tensor* wV,
+                const relattn_tensor* t5_bias, const relattn_t5_params* t5, int32_t clip_k,
+                float scale, const relattn_mask* mask, relattn_tensor* out, void* stream) {
+  g_last_error.clear();
+  Plan plan;
+  int st = make_plan(q, k, v, wK, wV, t5_bias, t5, clip_k, scale, mask, out, &plan, true);
+  if (st) return st;
+  if ((st = check_device())) return st;
+  if (plan.empty) return RELATTN_OK;
+  const int e = relattn::launch_fwd(plan.bf16, plan.d, plan.cfg, plan.mode, plan.has_wk,
+                                    plan.has_wv, plan.p, stream);
+  if (e != (int)hipSuccess)
+    return fail(RELATTN_ERR_LAUNCH_FAILED, "launch failed: %s",
+                hipGetErrorString((hipError_t)e));
+  return RELATTN_OK;
+}
+
+int relattn_debug_indices(int32_t n, int32_t clip_k, const relattn_t5_params* t5,
+                          int32_t* out_dev, void* stream) {
+  g_last_error.clear();
+  if (n < 1 || n > kMaxSeq) return fail(RELATTN_ERR_INVALID_ARGUMENT, "n must be in [1, 2^30]");
+  if (!out_dev) return fail(RELATTN_ERR_INVALID_ARGUMENT, "out_dev is NULL");
+  if (reinterpret_cast<uintptr_t>(out_dev) & 3u)
+    return fail(RELATTN_ERR_INVALID_ARGUMENT, "out_dev is not 4-byte aligned");
+  if (!t5 && clip_k < 0) return fail(RELATTN_ERR_INVALID_ARGUMENT, "clip_k must be >= 0");
+  T5Buckets tb = {};
+  int st;
+  if (t5 && (st = check_t5(t5, &tb))) return st;
+  if ((st = check_device())) return st;
+  const int e = relattn::launch_debug_indices(n, clip_k, t5 ? &tb : nullptr, out_dev, stream);
+  if (e != (int)hipSuccess)
+    return fail(RELATTN_ERR_LAUNCH_FAILED, "launch failed: %s",
+                hipGetErrorString((hipError_t)e));
+  return RELATTN_OK;
+}
+
+const char* relattn_strerror(int status) {
+  switch (status) {
+    case RELATTN_OK: return "ok";
+    case RELATTN_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case RELATTN_ERR_UNSUPPORTED: return "unsupported";
+    case RELATTN_ERR_NO_DEVICE: return "no device";
+    case RELATTN_ERR_LAUNCH_FAILED: return "launch failed";
+  }
+  return "unknown status";
+}
+
+const char* relattn_last_error(void) { return g_last_error.c_str(); }
+
+int relattn_version(void) { return RELATTN_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,71 @@
+// Internal interface between the C-ABI host code (relattn_api.cpp) and the
+// gfx950 kernels (relattn_kernels.hip).  Not installed, not part of the ABI.
+#pragma once
+
+#include <stdint.h>
+
+namespace relattn {
+
+constexpr int kMaxT5Thresholds = 64;
+
+// Bucket function of the T5 section, in the form the kernels evaluate it.
+// thr[t] is the smallest distance a whose logarithmic bucket index
+// floor(nlog * ln(a / exact) / ln(D_max / exact)) is at least t + 1; the host
+// derives it with exact integer arithmetic.
+struct T5Buckets {
+  int32_t half;     // buckets per sign (bidirectional) or all buckets
+  int32_t exact;    // B_exact = half / 2
+  int32_t nlog;     // half - exact logarithmic buckets
+  int32_t bidir;
+  int32_t thr[kMaxT5Thresholds];
+};
+
+// Everything a forward launch needs.  Strides count elements.
+struct FwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  const void* wk;          // [Ht, 2c+1, d] or null
+  const void* wv;          // [Ht, 2c+1, d] or null
+  const float* t5_bias;    // [NB, H] or null
+  const int32_t* key_lens; // [B] or null
+
+  int64_t q_sb, q_sh, q_sn;
+  int64_t k_sb, k_sh, k_sn;
+  int64_t v_sb, v_sh, v_sn;
+  int64_t o_sb, o_sh, o_sn;
+  int64_t wk_sh, wk_sr;    // head stride 0 = shared table
+  int64_t wv_sh, wv_sr;
+  int64_t tb_sb, tb_sh;    // T5 bias strides: bucket, head
+
+  int32_t B, H, n;
+  int32_t clip;            // c of clip(j - i, c)
+  int32_t r_lo, nr;        // label rows reachable: [r_lo, r_lo + nr)
+  int32_t causal;
+  float scale_log2;        // logit scale times log2(e)
+  int32_t t5_dist;         // offsets are clamped to [-t5_dist, t5_dist]
+  int32_t n_qtiles;        // query tiles per (b, h)
+  T5Buckets t5;
+};
+
+enum RelMode { kRelNone = 0, kRelShaw = 1, kRelT5 = 2 };
+
+// Kernel configuration picked by the host for one call.
+struct LaunchCfg {
+  int waves;   // 32 query rows per wave
+  int kblock;  // keys per tile
+};
+
+// Host-side helpers shared with the launcher.
+int label_row_stride(int nr);
+size_t lds_bytes(bool bf16, int d, const LaunchCfg& cfg, RelMode mode,
+                 bool has_wv, int nr, int t5_dist);
+
+// Launchers (relattn_kernels.hip).  Return a hipError_t value.
+int launch_fwd(bool bf16, int d, const LaunchCfg& cfg, RelMode mode, bool has_wk,
+               bool has_wv, const FwdParams& p, void* stream);
+int launch_debug_indices(int n, int clip, const T5Buckets* t5, int32_t* out,
+                         void* stream);
+
+}  // namespace relattn

@@ -1,0 +1,152 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry point
+declared in include/relattn.h, and its host-only validation rejects bad
+arguments with the documented status codes."""
+import os
+import re
+import subprocess
+import sys
+
+import pytest
+import torch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def ra():
+    import relative_position_encoding_amd as ra
+    if not os.path.exists(ra.library_path):
+        from relative_position_encoding_amd import build
+        build.build()
+    return ra
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "relattn.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(relattn_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol(ra):
+    import ctypes
+    lib = ctypes.CDLL(ra.library_path)
+    names = declared_functions()
+    assert {"relattn_fwd", "relattn_validate", "relattn_debug_indices"} <= set(names)
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_version_and_strerror(ra):
+    lib = ra._load()
+    assert lib.relattn_version() == 1
+    for st in (ra.OK, ra.INVALID_ARGUMENT, ra.UNSUPPORTED, ra.NO_DEVICE, ra.LAUNCH_FAILED):
+        assert lib.relattn_strerror(st)
+    assert lib.relattn_strerror(12345) == b"unknown status"
+
+
+def T(*shape, dtype=torch.bfloat16):
+    return torch.zeros(*shape, dtype=dtype)
+
+
+def qkv(B=2, H=3, n=40, d=64, dtype=torch.bfloat16):
+    return T(B, H, n, d, dtype=dtype), T(B, H, n, d, dtype=dtype), T(B, H, n, d, dtype=dtype)
+
+
+def test_valid_arguments(ra):
+    q, k, v = qkv()
+    assert ra.validate(q, k, v) == ra.OK
+    assert ra.validate(q, k, v, T(3, 9, 64), T(3, 9, 64), clip=4, causal=True) == ra.OK
+    assert ra.validate(q, k, v, T(1, 9, 64), None, clip=4) == ra.OK   # shared table
+    assert ra.validate(q, k, v, None, T(3, 9, 64), clip=4) == ra.OK   # value table only
+    assert ra.validate(q, k, v, t5_bias=T(32, 3, dtype=torch.float32)) == ra.OK
+    qf, kf, vf = qkv(dtype=torch.float32, d=16)
+    assert ra.validate(qf, kf, vf, T(3, 1, 16, dtype=torch.float32), clip=0) == ra.OK
+
+
+@pytest.mark.parametrize("case", [
+    "dtype_mix", "shape_mix", "table_rows", "table_heads", "table_dtype", "neg_clip",
+    "t5_and_tables", "t5_odd_buckets", "t5_small_distance", "t5_bias_shape",
+    "t5_bias_dtype", "ndim", "nan_scale"])
+def test_invalid_arguments(ra, case):
+    q, k, v = qkv()
+    kw = {}
+    args = [q, k, v]
+    if case == "dtype_mix":
+        args[1] = k.float()
+    elif case == "shape_mix":
+        args[2] = T(2, 3, 41, 64)
+    elif case == "table_rows":
+        args += [T(3, 8, 64)]; kw["clip"] = 4
+    elif case == "table_heads":
+        args += [T(2, 9, 64)]; kw["clip"] = 4
+    elif case == "table_dtype":
+        args += [T(3, 9, 64, dtype=torch.float32)]; kw["clip"] = 4
+    elif case == "neg_clip":
+        args += [T(3, 1, 64)]; kw["clip"] = -1
+    elif case == "t5_and_tables":
+        args += [T(3, 9, 64)]; kw.update(clip=4, t5_bias=T(32, 3, dtype=torch.float32))
+    elif case == "t5_odd_buckets":
+        kw.update(t5_bias=T(31, 3, dtype=torch.float32), num_buckets=31)
+    elif case == "t5_small_distance":
+        kw.update(t5_bias=T(32, 3, dtype=torch.float32), max_distance=8)
+    elif case == "t5_bias_shape":
+        kw.update(t5_bias=T(32, 4, dtype=torch.float32))
+    elif case == "t5_bias_dtype":
+        kw.update(t5_bias=T(32, 3))
+    elif case == "ndim":
+        args = [T(3, 40, 64)] * 3
+    elif case == "nan_scale":
+        kw["scale"] = float("nan")
+    assert ra.validate(*args, **kw) == ra.INVALID_ARGUMENT, ra.last_error()
+    assert ra.last_error()
+
+
+@pytest.mark.parametrize("case", ["head_size", "noncontig_d", "misaligned_stride",
+                                  "huge_label_window", "fp16"])
+def test_unsupported_arguments(ra, case):
+    q, k, v = qkv()
+    args, kw = [q, k, v], {}
+    if case == "head_size":
+        args = list(qkv(d=48))
+    elif case == "noncontig_d":
+        args = [T(2, 3, 40, 128)[..., ::2]] * 3
+    elif case == "misaligned_stride":
+        x = T(2, 3, 40, 68)[..., :64]  # row stride 136 bytes
+        args = [x, x, x]
+    elif case == "huge_label_window":
+        q, k, v = qkv(n=5000, B=1, H=1)
+        c = 4000
+        args = [q, k, v, T(1, 2 * c + 1, 64)]
+        kw["clip"] = c
+    elif case == "fp16":
+        args = list(qkv(dtype=torch.float16))
+    st = ra.validate(*args, **kw)
+    expected = ra.INVALID_ARGUMENT if case == "fp16" else ra.UNSUPPORTED
+    assert st == expected, ra.last_error()
+
+
+def test_empty_problem_validates(ra):
+    for shape in [(0, 2, 8, 64), (2, 0, 8, 64), (2, 2, 0, 64)]:
+        x = T(*shape)
+        assert ra.validate(x, x, x, clip=2) == ra.OK
+
+
+def test_no_device_status():
+    """relattn_fwd reports NO_DEVICE when HIP sees no device (forced from the
+    host by hiding every device from the child process)."""
+    code = r"""
+import sys, torch
+sys.path.insert(0, %r)
+import relative_position_encoding_amd as ra
+q = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
+lib = ra._load()
+args, keep = ra._args(q, q, q, None, None, None, 0, False, None, 32, 128, True, None, q)
+st = lib.relattn_fwd(*args, None)
+print(st)
+""" % ROOT
+    env = dict(os.environ, HIP_VISIBLE_DEVICES="-1", ROCR_VISIBLE_DEVICES="-1",
+               CUDA_VISIBLE_DEVICES="-1")
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True,
+                       env=env, timeout=300)
+    assert r.returncode == 0, r.stderr
+    assert int(r.stdout.strip().splitlines()[-1]) == -3
