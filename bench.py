@@ -1,0 +1,289 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused relation-aware attention forward on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--gpus 1]
+
+One step is one call of relattn_fwd over one batch of the workload (every step
+of the method runs inside that call).  The timed region is K back-to-back
+steps on one HIP stream, bracketed by HIP events, after W untimed steps.  The
+steps cycle through several copies of the inputs whose total size exceeds the
+256 MB last-level cache, so each step reads its operands from HBM as a
+stream of fresh batches would.
+
+Prints ONE JSON line: TFLOP/s of the headline workload (Transformer-big
+decoder causal self-attention with key and value tables), its fraction of the
+bf16 MFMA peak, the HBM roofline of the kernel, the fp64 oracle timed on the
+host cores, and the same figures for the other Transformer shapes.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "rel-attention fwd TFLOP/s at 1 GPU (+% MFMA peak, HBM GB/s), base/big shapes"
+HEADLINE = "big_causal_kv"
+OTHER = ["base", "big_causal_k", "long", "t5"]
+PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # dense MFMA, MI355X
+PEAK_HBM_GBS = 8000.0
+LLC_BYTES = 256 << 20
+KERNEL_SRC = os.path.join(ROOT, "relative_position_encoding_amd", "csrc", "relattn_kernels.hip")
+
+
+# ---------------------------------------------------------------------------
+# algorithmic work per call
+# ---------------------------------------------------------------------------
+
+def work(w, key_lens):
+    """(flops, bytes, dense_flops) the method must do for one call.
+
+    flops: 4*d per visible (query, key) pair (content logits and P.V) plus
+    2*d*n*R per relative table (the Q.(w^K)^T product and the bucketed
+    alpha.w^V product), R = reachable clipped offsets.  bytes: q and out once,
+    k and v rows up to the key length once, plus the tables.
+    """
+    import numpy as np
+    B, H, n, d = w.batch, w.heads, w.n, w.d
+    esz = w.dtype.itemsize
+    lens = [n] * B if key_lens is None else [int(x) for x in key_lens]
+    pairs = 0
+    for L in lens:
+        i = np.arange(n)
+        vis = np.minimum(i + 1, L) if w.causal else np.full(n, L)
+        pairs += int(vis.sum())
+    flops = 4.0 * d * pairs * H
+    tables = 0
+    if w.t5 is None:
+        R = min(w.clip + 1, n) if w.causal else min(2 * w.clip + 1, 2 * n - 1)
+        ntab = int(w.use_key_table) + int(w.use_value_table)
+        flops += 2.0 * d * n * R * ntab * B * H
+        tables = ntab * H * (2 * w.clip + 1) * d * esz
+    else:
+        tables = w.t5["num_buckets"] * H * 4
+    kv_rows = sum(lens)
+    nbytes = H * (2 * B * n * d + 2 * kv_rows * d) * esz + tables
+    dense = 4.0 * B * H * n * n * d
+    return flops, float(nbytes), dense
+
+
+# ---------------------------------------------------------------------------
+# GPU timing
+# ---------------------------------------------------------------------------
+
+def _prepare(ra, w, copies, stream_ptr):
+    """Device copies of the inputs and pre-marshalled ctypes arguments."""
+    import torch
+    import workloads
+    x = workloads.make_inputs(w)
+    calls = []
+    keep = []
+    for _ in range(copies):
+        g = {k: (t.to("cuda").clone() if t is not None else None) for k, t in x.items()}
+        out = torch.empty_like(g["q"])
+        if w.t5 is None:
+            args, kp = ra._args(g["q"], g["k"], g["v"], g["key_table"], g["value_table"], None,
+                                w.clip, w.causal, g["key_lens"], 32, 128, True, None, out)
+        else:
+            args, kp = ra._args(g["q"], g["k"], g["v"], None, None, g["t5_bias"], 0, w.causal,
+                                g["key_lens"], w.t5["num_buckets"], w.t5["max_distance"],
+                                w.t5["bidirectional"], None, out)
+        calls.append(args + [ctypes.c_void_p(stream_ptr)])
+        keep += [g, out, kp]
+    return x, calls, keep
+
+
+def time_gpu(ra, w, steps, warmup):
+    import torch
+    lib = ra._load()
+    stream = torch.cuda.Stream()  # default priority
+    flops, nbytes, dense = work(w, None)
+    copies = max(1, min(16, int(2 * LLC_BYTES // max(nbytes, 1)) + 1))
+    x, calls, keep = _prepare(ra, w, copies, stream.cuda_stream)
+    flops, nbytes, dense = work(w, x["key_lens"])
+    fwd = lib.relattn_fwd
+    with torch.cuda.stream(stream):
+        for s in range(warmup):
+            st = fwd(*calls[s % copies])
+            if st != 0:
+                raise RuntimeError(ra.last_error())
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        wall0 = time.perf_counter()
+        t0.record(stream)
+        for s in range(steps):
+            fwd(*calls[s % copies])
+        t1.record(stream)
+        wall_submit = time.perf_counter() - wall0
+        torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    del keep
+    sec = ms * 1e-3
+    dt = "bf16" if w.dtype.itemsize == 2 else "f32"
+    res = {
+        "ms_per_step": ms,
+        "tflops": flops / sec / 1e12,
+        "mfma_peak_frac": flops / sec / 1e12 / PEAK_TFLOPS[dt],
+        "dense_equiv_tflops": dense / sec / 1e12,
+        "hbm_gbs": nbytes / sec / 1e9,
+        "alg_gflop": flops / 1e9,
+        "alg_mbytes": nbytes / 1e6,
+        "input_copies": copies,
+        "host_submit_us_per_step": wall_submit / steps * 1e6,
+        "dtype": dt,
+    }
+    return res
+
+
+def bound_of(flops, nbytes, dt):
+    ridge = PEAK_TFLOPS[dt] * 1e12 / (PEAK_HBM_GBS * 1e9)
+    return "hbm" if flops / nbytes < ridge else "mfma"
+
+
+# ---------------------------------------------------------------------------
+# HBM traffic from committed rocprofv3 counter summaries
+# ---------------------------------------------------------------------------
+
+def kernel_sha():
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def traffic_per_launch(name):
+    """Measured HBM bytes per launch, or None when the counters are missing or
+    were taken on a different kernel source."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{name}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_sha256") != kernel_sha():
+        return None
+    return t["fetch_kib"] * 1024 * t["fetch_scale"] + t["write_kib"] * 1024 * t["write_scale"]
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the fp64 oracle as it stands, on the host cores
+# ---------------------------------------------------------------------------
+
+def cpu_baseline(w, min_seconds=5.0):
+    import oracle
+    import workloads
+    from threadpoolctl import threadpool_info
+    x = workloads.make_inputs(w)
+    flops, _, _ = work(w, x["key_lens"])
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        if w.t5 is None:
+            oracle.relattn_factored(x["q"], x["k"], x["v"], x["key_table"], x["value_table"],
+                                    w.clip, causal=w.causal, key_lens=x["key_lens"])
+        else:
+            oracle.t5_attention(x["q"], x["k"], x["v"], x["t5_bias"], causal=w.causal,
+                                key_lens=x["key_lens"], **w.t5)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds:
+            break
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {"value": flops * reps / el / 1e12, "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"whole {w.name} workload, fp64 factored oracle (Eq. 5 form), "
+                      f"{reps} run(s) in {el:.1f} s, {len(os.sched_getaffinity(0))} host "
+                      f"cores visible"}
+
+
+def copy_calibration(mib=512, reps=5):
+    """A plain device copy of known size, for scaling the HBM byte counters."""
+    import torch
+    a = torch.empty(mib << 20, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_each_way": mib << 20, "reps": reps}))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[1])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", default=HEADLINE)
+    ap.add_argument("--only", action="store_true", help="time the headline workload only")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    a = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if a.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              f"(asked for --gpus {a.gpus}, WORLD_SIZE {world})", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import relative_position_encoding_amd as ra
+    import workloads
+    if not os.path.exists(ra.library_path):
+        from relative_position_encoding_amd import build
+        build.build()
+    if a.copy_calibration:
+        copy_calibration()
+        return
+
+    w = workloads.WORKLOADS[a.workload]
+    head = time_gpu(ra, w, a.steps, a.warmup)
+    flops = head["alg_gflop"] * 1e9
+    nbytes = head["alg_mbytes"] * 1e6
+    bound = bound_of(flops, nbytes, head["dtype"])
+    sec = head["ms_per_step"] * 1e-3
+    if bound == "hbm":
+        ach, peak, unit = nbytes / sec / 1e9, PEAK_HBM_GBS, "GB/s"
+    else:
+        ach, peak, unit = flops / sec / 1e12, PEAK_TFLOPS[head["dtype"]], "TFLOP/s"
+    traffic = traffic_per_launch(w.name)
+    mask = ("causal" if w.causal else "") + ("+key_padding" if w.len_range else "")
+    tables = ("t5_bias" if w.t5 else
+              "+".join([x for x, u in (("key", w.use_key_table), ("value", w.use_value_table))
+                        if u]) or "none")
+    line = {
+        "metric": METRIC, "value": round(head["tflops"], 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(head["ms_per_step"], 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": head["dtype"], "data": "synthetic",
+        "config": {"workload": w.description, "name": w.name, "batch": w.batch,
+                   "heads": w.heads, "seq_len": w.n, "head_dim": w.d, "clip": w.clip,
+                   "mask": mask or "none", "tables": tables,
+                   "input_copies": head["input_copies"]},
+        "mfma_peak_frac": round(head["mfma_peak_frac"], 4),
+        "hbm_gbs": round(head["hbm_gbs"], 1),
+        "dense_equiv_tflops": round(head["dense_equiv_tflops"], 3),
+        "roofline": {"bound": bound, "achieved": round(ach, 2), "peak": peak, "unit": unit,
+                     "frac": round(ach / peak, 4),
+                     "traffic": None if traffic is None else round(traffic)},
+        "alg_gflop_per_step": round(head["alg_gflop"], 4),
+        "alg_mbytes_per_step": round(head["alg_mbytes"], 3),
+        "host_submit_us_per_step": round(head["host_submit_us_per_step"], 2),
+    }
+    if not a.only:
+        others = {}
+        for name in OTHER:
+            if name == w.name:
+                continue
+            r = time_gpu(ra, workloads.WORKLOADS[name], max(50, a.steps // 5), 10)
+            others[name] = {k: round(r[k], 4) for k in
+                            ("ms_per_step", "tflops", "mfma_peak_frac", "hbm_gbs",
+                             "dense_equiv_tflops")}
+        line["workloads"] = others
+    if not a.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

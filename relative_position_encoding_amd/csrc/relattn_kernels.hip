@@ -41,8 +41,17 @@ namespace relattn {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+// Native vectors (HIP's uint4/uint2 are structs; copying those through memory
+// keeps them out of registers).
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
+
+// 2^x with the hardware exponential (about 1 ulp; results below 2^-126,
+// which cannot change a softmax sum at fp32 precision, flush to zero).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 constexpr float kNegInf = -__builtin_inff();
 
 // ---------------------------------------------------------------------------
@@ -71,11 +80,21 @@ __device__ __forceinline__ int t5_bucket(int delta, const T5Buckets& t) {
   return base + t.exact + s;
 }
 
+// Relative-logit rows in LDS hold the nr reachable labels between kRelPad
+// copies of the first and of the last label on each side, plus one dummy slot.
+// With the padding, a group of 8 consecutive logits reads 8 consecutive
+// entries from one clamped base index, whether the group lies in the band,
+// in a tail or across an edge; no per-element clamp is needed.
+constexpr int kRelPad = 16;
+
 __host__ __device__ inline int label_row_stride_impl(int nr) {
-  // Even stride: consecutive query rows then hit distinct LDS banks when the
-  // lanes of a wave gather along a diagonal j - i.
-  return (nr & 1) ? nr + 1 : nr;
+  // even stride: consecutive query rows hit distinct LDS banks when the lanes
+  // of a wave gather along a diagonal j - i
+  return (nr + 2 * kRelPad + 1 + 1) & ~1;
 }
+
+// Label rows of the value table staged in LDS, padded to whole MFMA steps.
+__host__ __device__ inline int value_rows_padded(int nr) { return (nr + 15) & ~15; }
 
 int label_row_stride(int nr) { return label_row_stride_impl(nr); }
 
@@ -143,15 +162,9 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(const FwdParams p) {
   using T = typename G::T;
   using Op = std::conditional_t<BF16, bf16x8, float>;
   constexpr int BR = G::BR, NT = G::NT, NKB = G::NKB, DVB = G::DVB;
-  constexpr int KSTEP = G::KSTEP, NKS = G::NKS, KS = G::KS, VS = G::VS;
+  constexpr int NKS = G::NKS, KS = G::KS, VS = G::VS;
   constexpr bool SHAW = (MODE == kRelShaw);
   constexpr bool T5 = (MODE == kRelT5);
-
-  extern __shared__ __align__(16) unsigned char smem[];
-  T* Ks = reinterpret_cast<T*>(smem);
-  T* Vs = Ks + G::K_ELEMS;
-  float* LE = reinterpret_cast<float*>(smem + G::TILE_BYTES);  // Shaw: L rows
-  float* TB = LE;                                              // T5: bias by offset
 
   // ---- which tile
   const int lid = xcd_remap(blockIdx.x, gridDim.x);
@@ -169,141 +182,101 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(const FwdParams p) {
   int kv_len = p.n;
   if (p.key_lens) kv_len = min(max(p.key_lens[b], 0), p.n);
   const int kv_end = p.causal ? min(kv_len, i0 + BR) : kv_len;
+  const int kv_last = max(kv_len - 1, 0);
   const int c = p.clip;
   const int r_hi = p.r_lo + p.nr - 1;
+  const int RS = label_row_stride_impl(p.nr);
+  const int NRP = value_rows_padded(p.nr);
+
+  // ---- LDS carve: K/V tile | L rows (Shaw) or bias-by-offset (T5) | w^V
+  extern __shared__ __align__(16) unsigned char smem[];
+  T* Ks = reinterpret_cast<T*>(smem);
+  T* Vs = Ks + G::K_ELEMS;
+  float* LE = reinterpret_cast<float*>(smem + G::TILE_BYTES);
+  float* TB = LE;
+  T* WV = reinterpret_cast<T*>(LE + BR * RS);
+  float* myLE = LE + qrow * RS;
 
   const T* qg = reinterpret_cast<const T*>(p.q) + b * p.q_sb + h * p.q_sh;
   const T* kg = reinterpret_cast<const T*>(p.k) + b * p.k_sb + h * p.k_sh;
   const T* vg = reinterpret_cast<const T*>(p.v) + b * p.v_sb + h * p.v_sh;
   T* og = reinterpret_cast<T*>(p.o) + b * p.o_sb + h * p.o_sh;
 
-  // ---- Q as the B operand of S^T = K Q^T, resident for the whole kernel
+  // ---- Q as the B operand of S^T = K Q^T, resident for the whole kernel.
+  // Rows past n load row n-1 (never stored); loads are unconditional so they
+  // are all in flight together.
   Op qop[NKS];
   {
-    const T* qrow_ptr = qg + (int64_t)qi * p.q_sn;
+    const T* qrow_ptr = qg + (int64_t)min(qi, p.n - 1) * p.q_sn;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
       if constexpr (BF16) {
-        qop[ks] = q_ok ? *reinterpret_cast<const bf16x8*>(qrow_ptr + ks * 16 + 8 * hh)
-                       : bf16x8{};
+        qop[ks] = *reinterpret_cast<const bf16x8*>(qrow_ptr + ks * 16 + 8 * hh);
       } else {
-        qop[ks] = q_ok ? qrow_ptr[ks * 2 + hh] : 0.f;
+        qop[ks] = qrow_ptr[ks * 2 + hh];
       }
     }
   }
 
-  // ---- relative key logits L (Shaw) or bias-by-offset vector (T5), in LDS
-  const int RS = label_row_stride_impl(p.nr);
-  float* myLE = LE + qrow * RS;
-  if constexpr (SHAW) {
-    if constexpr (HAS_WK) {
-      const T* wkh = reinterpret_cast<const T*>(p.wk) + h * p.wk_sh;
-      const int nlb = (p.nr + 31) / 32;
-      for (int lb = 0; lb < nlb; ++lb) {
-        const int arow = lb * 32 + ql;  // MFMA row m = ql <-> label row r_lo + arow
-        const bool a_ok = arow < p.nr;
-        const T* wrow = wkh + (int64_t)(p.r_lo + (a_ok ? arow : 0)) * p.wk_sr;
-        f32x16 acc = {};
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-          Op a;
-          if constexpr (BF16) {
-            a = a_ok ? *reinterpret_cast<const bf16x8*>(wrow + ks * 16 + 8 * hh) : bf16x8{};
-          } else {
-            a = a_ok ? wrow[ks * 2 + hh] : 0.f;
-          }
-          acc = mfma(a, qop[ks], acc);
-        }
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int idx = lb * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
-          if (idx < p.nr) myLE[idx] = acc[i] * p.scale_log2;
-        }
-      }
-    } else {
-      for (int idx = hh; idx < p.nr; idx += 2) myLE[idx] = 0.f;
-    }
-  }
-  if constexpr (T5) {
-    const int nb = 2 * p.t5_dist + 1;
-    for (int x = tid; x < nb; x += NT) {
-      const int bucket = t5_bucket(x - p.t5_dist, p.t5);
-      TB[x] = kLog2e * p.t5_bias[bucket * p.tb_sb + h * p.tb_sh];
-    }
-  }
-  __syncthreads();
-  float Llo = 0.f, Lhi = 0.f;  // L at labels -c and +c (clamped into the window)
-  if constexpr (SHAW && HAS_WK) {
-    Llo = myLE[min(max(0, p.r_lo), r_hi) - p.r_lo];
-    Lhi = myLE[min(max(2 * c, p.r_lo), r_hi) - p.r_lo];
-  }
-
-  // ---- K/V tile staging: global -> registers (prefetch) -> LDS
+  // ---- K/V tile staging: global -> registers (prefetch) -> LDS.  Key rows
+  // past the key length are clamped to the last visible row: their logits are
+  // masked, so the values only need to be finite.
   constexpr int EPC = BF16 ? 8 : 4;  // elements per 16-byte chunk
   constexpr int K_CPR = D / EPC;
   constexpr int K_CHUNKS = BC * K_CPR;
   constexpr int K_PER_T = (K_CHUNKS + NT - 1) / NT;
   constexpr int V_UNITS = BF16 ? (BC / 4) * (D / 4) : K_CHUNKS;
   constexpr int V_PER_T = (V_UNITS + NT - 1) / NT;
-  uint4 kreg[K_PER_T];
-  uint2 vreg_b[BF16 ? V_PER_T : 1][4];
-  uint4 vreg_f[BF16 ? 1 : V_PER_T];
+  u32x4 kreg[K_PER_T];
+  u32x2 vreg_b[BF16 ? V_PER_T : 1][4];
+  u32x4 vreg_f[BF16 ? 1 : V_PER_T];
 
-  auto load_tile = [&](int j0) {
+  auto load_tile = [&](int j0) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < K_PER_T; ++u) {
-      const int ch = tid + u * NT;
+      const int ch = min(tid + u * NT, K_CHUNKS - 1);
       const int row = ch / K_CPR, col = ch - row * K_CPR;
-      const int j = j0 + row;
-      uint4 val = {0u, 0u, 0u, 0u};
-      if (ch < K_CHUNKS && j < kv_len)
-        val = *reinterpret_cast<const uint4*>(kg + (int64_t)j * p.k_sn + col * EPC);
-      kreg[u] = val;
+      const int j = min(j0 + row, kv_last);
+      kreg[u] = *reinterpret_cast<const u32x4*>(kg + (int64_t)j * p.k_sn + col * EPC);
     }
     if constexpr (BF16) {
 #pragma unroll
       for (int u = 0; u < V_PER_T; ++u) {
-        const int un = tid + u * NT;
+        const int un = min(tid + u * NT, V_UNITS - 1);
         const int du = un % (D / 4), ku = un / (D / 4);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int j = j0 + 4 * ku + r;
-          uint2 val = {0u, 0u};
-          if (un < V_UNITS && j < kv_len)
-            val = *reinterpret_cast<const uint2*>(vg + (int64_t)j * p.v_sn + 4 * du);
-          vreg_b[u][r] = val;
+          const int j = min(j0 + 4 * ku + r, kv_last);
+          vreg_b[u][r] = *reinterpret_cast<const u32x2*>(vg + (int64_t)j * p.v_sn + 4 * du);
         }
       }
     } else {
 #pragma unroll
       for (int u = 0; u < V_PER_T; ++u) {
-        const int ch = tid + u * NT;
+        const int ch = min(tid + u * NT, K_CHUNKS - 1);
         const int row = ch / K_CPR, col = ch - row * K_CPR;
-        const int j = j0 + row;
-        uint4 val = {0u, 0u, 0u, 0u};
-        if (ch < K_CHUNKS && j < kv_len)
-          val = *reinterpret_cast<const uint4*>(vg + (int64_t)j * p.v_sn + col * EPC);
-        vreg_f[u] = val;
+        const int j = min(j0 + row, kv_last);
+        vreg_f[u] = *reinterpret_cast<const u32x4*>(vg + (int64_t)j * p.v_sn + col * EPC);
       }
     }
   };
 
-  auto store_tile = [&]() {
+  auto store_tile = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < K_PER_T; ++u) {
       const int ch = tid + u * NT;
       const int row = ch / K_CPR, col = ch - row * K_CPR;
-      if (ch < K_CHUNKS) *reinterpret_cast<uint4*>(Ks + row * KS + col * EPC) = kreg[u];
+      if (K_CHUNKS % NT == 0 || ch < K_CHUNKS)
+        *reinterpret_cast<u32x4*>(Ks + row * KS + col * EPC) = kreg[u];
     }
     if constexpr (BF16) {
 #pragma unroll
       for (int u = 0; u < V_PER_T; ++u) {
         const int un = tid + u * NT;
-        if (un >= V_UNITS) continue;
         const int du = un % (D / 4), ku = un / (D / 4);
-        const uint2* r = vreg_b[u];
+        const u32x2* r = vreg_b[u];
         // 4x4 transpose of 16-bit values: column e of the 4 rows -> Vt row 4du+e
-        uint2 col[4];
+        u32x2 col[4];
         col[0].x = (r[0].x & 0xffffu) | (r[1].x << 16);
         col[0].y = (r[2].x & 0xffffu) | (r[3].x << 16);
         col[1].x = (r[0].x >> 16) | (r[1].x & 0xffff0000u);
@@ -312,30 +285,125 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(const FwdParams p) {
         col[2].y = (r[2].y & 0xffffu) | (r[3].y << 16);
         col[3].x = (r[0].y >> 16) | (r[1].y & 0xffff0000u);
         col[3].y = (r[2].y >> 16) | (r[3].y & 0xffff0000u);
+        if (V_UNITS % NT == 0 || un < V_UNITS) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          *reinterpret_cast<uint2*>(Vs + (4 * du + e) * VS + 4 * ku) = col[e];
+          for (int e = 0; e < 4; ++e)
+            *reinterpret_cast<u32x2*>(Vs + (4 * du + e) * VS + 4 * ku) = col[e];
+        }
       }
     } else {
 #pragma unroll
       for (int u = 0; u < V_PER_T; ++u) {
         const int ch = tid + u * NT;
         const int row = ch / K_CPR, col = ch - row * K_CPR;
-        if (ch < K_CHUNKS) *reinterpret_cast<uint4*>(Vs + row * VS + col * EPC) = vreg_f[u];
+        if (K_CHUNKS % NT == 0 || ch < K_CHUNKS)
+          *reinterpret_cast<u32x4*>(Vs + row * VS + col * EPC) = vreg_f[u];
       }
     }
   };
+
+  const int ntiles = (kv_end + BC - 1) / BC;
+  if (ntiles > 0) load_tile(0);  // in flight while the tables are prepared
+
+  // ---- relative logits in LDS.  Shaw: row qrow holds scale*log2e*q.w^K_r for
+  // the reachable label rows r_lo..r_hi at entries kRelPad + (r - r_lo).  T5:
+  // one shared vector holds log2e*bias[beta(delta), h] for delta in
+  // [-dist, dist] at entries kRelPad + dist + delta.  Both are padded.
+  if constexpr (SHAW) {
+    if constexpr (HAS_WK) {
+      const T* wkh = reinterpret_cast<const T*>(p.wk) + h * p.wk_sh;
+      const int nlb = (p.nr + 31) / 32;
+      for (int lb = 0; lb < nlb; ++lb) {
+        // MFMA row m = ql <-> label row r_lo + lb*32 + ql (clamped; rows past
+        // the window produce values that are never stored)
+        const T* wrow = wkh + (int64_t)min(p.r_lo + lb * 32 + ql, r_hi) * p.wk_sr;
+        Op a[NKS];
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+          if constexpr (BF16) {
+            a[ks] = *reinterpret_cast<const bf16x8*>(wrow + ks * 16 + 8 * hh);
+          } else {
+            a[ks] = wrow[ks * 2 + hh];
+          }
+        }
+        f32x16 acc = {};
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) acc = mfma(a[ks], qop[ks], acc);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int idx = lb * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
+          if (idx < p.nr) myLE[kRelPad + idx] = acc[i] * p.scale_log2;
+        }
+      }
+    } else {
+      for (int idx = hh; idx < p.nr + 2 * kRelPad; idx += 2) myLE[idx] = 0.f;
+    }
+    if constexpr (HAS_WV) {
+      // value table rows r_lo .. r_hi (zero past nr): bf16 transposed to
+      // WV[d][label] so a lane reads 8 labels of one d with one 16-byte load;
+      // fp32 kept as WV[label][d].
+      const T* wvh = reinterpret_cast<const T*>(p.wv) + h * p.wv_sh;
+      constexpr int CPR = D / EPC;
+      const int nch = NRP * CPR;
+      for (int u = tid; u < nch; u += NT) {
+        const int idx = u / CPR, ch = u - idx * CPR;
+        const T* src = wvh + (int64_t)(p.r_lo + min(idx, p.nr - 1)) * p.wv_sr + ch * EPC;
+        u32x4 val = *reinterpret_cast<const u32x4*>(src);
+        if (idx >= p.nr) val = u32x4{0u, 0u, 0u, 0u};
+        if constexpr (BF16) {
+          const int WS = NRP + 8;
+          const unsigned w32[4] = {val.x, val.y, val.z, val.w};
+          unsigned short* dst = reinterpret_cast<unsigned short*>(WV);
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            dst[(ch * 8 + e) * WS + idx] = (unsigned short)(w32[e >> 1] >> (16 * (e & 1)));
+        } else {
+          *reinterpret_cast<u32x4*>(WV + idx * (D + 4) + ch * 4) = val;
+        }
+      }
+    }
+  }
+  if constexpr (T5) {
+    const int nb = 2 * p.t5_dist + 1 + 2 * kRelPad;
+    for (int x = tid; x < nb; x += NT) {
+      const int delta = min(max(x - kRelPad - p.t5_dist, -p.t5_dist), p.t5_dist);
+      TB[x] = kLog2e * p.t5_bias[t5_bucket(delta, p.t5) * p.tb_sb + h * p.tb_sh];
+    }
+  }
+  __syncthreads();
+  if constexpr (SHAW && HAS_WK) {
+    // replicate the first / last label into the padding of this row
+    const float edge = myLE[hh ? kRelPad + p.nr - 1 : kRelPad];
+    float* pad = myLE + (hh ? kRelPad + p.nr : 0);
+#pragma unroll
+    for (int x = 0; x < kRelPad; ++x) pad[x] = edge;
+  }
+  __syncthreads();
+
+  // window of offsets delta = j - i covered by the relative row, and the
+  // relative logit of the two ends (used for tiles entirely outside the band)
+  const int dlo = T5 ? -p.t5_dist : p.r_lo - c;           // delta of entry kRelPad
+  const int nwin = T5 ? 2 * p.t5_dist + 1 : p.nr;
+  const float* relrow = T5 ? TB : myLE;
+  float Llo = 0.f, Lhi = 0.f;
+  if constexpr (SHAW || T5) {
+    Llo = relrow[kRelPad];
+    Lhi = relrow[kRelPad + nwin - 1];
+  }
+  const int band = T5 ? p.t5_dist : c;  // |j - i| >= band: one end value for the tile
 
   // ---- running state (per lane: one query, half of each tile's keys)
   f32x16 oacc[DVB];
 #pragma unroll
   for (int mb = 0; mb < DVB; ++mb) oacc[mb] = f32x16{};
   float m_run = kNegInf;
-  float l_part = 0.f, tlo = 0.f, thi = 0.f;
+  float l_part = 0.f, thi = 0.f;
   const int hi_from = max(c, 1 - c);  // offsets >= hi_from fall in the +c bucket
+  constexpr int KSTR = BF16 ? 1 : 2;  // key step between consecutive registers
+  constexpr int SPAN = 7 * KSTR + 1;  // keys spanned by a group of 8 registers
+  const int hoff = BF16 ? 8 * hh : hh;  // key offset of this lane half
+  const int dummy = p.nr + 2 * kRelPad;
 
-  const int ntiles = (kv_end + BC - 1) / BC;
-  if (ntiles > 0) load_tile(0);
   for (int t = 0; t < ntiles; ++t) {
     const int j0 = t * BC;
     __syncthreads();  // every wave is done with the previous tile
@@ -350,54 +418,86 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(const FwdParams p) {
     f32x16 s[NKB];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
-      s[kb] = f32x16{};
+      // all K fragments of the block first, then the MFMA chain
       const int krow = 32 * kb + k_row_of_mfma_row<BF16>(ql);
+      Op a[NKS];
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
-        Op a;
         if constexpr (BF16) {
-          a = *reinterpret_cast<const bf16x8*>(Ks + krow * KS + ks * 16 + 8 * hh);
+          a[ks] = *reinterpret_cast<const bf16x8*>(Ks + krow * KS + ks * 16 + 8 * hh);
         } else {
-          a = Ks[krow * KS + ks * 2 + hh];
+          a[ks] = Ks[krow * KS + ks * 2 + hh];
         }
-        s[kb] = mfma(a, qop[ks], s[kb]);
       }
+      s[kb] = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) s[kb] = mfma(a[ks], qop[ks], s[kb]);
     }
 
-    // logits in log2 units, relative term, masks
+    // Register (kb, 8g + e) holds key j0 + hoff + 32kb + 16g + KSTR*e, i.e.
+    // offset delta = kofs + 32kb + 16g + KSTR*e from this lane's query.
+    const int kofs = j0 + hoff - qi;
     const bool need_mask = (j0 + BC > kv_len) || (p.causal && j0 + BC - 1 > wq0);
+    // visible iff its key offset within the lane's keys is <= lim
+    const int lim = min(kv_len - 1 - j0 - hoff, p.causal ? -kofs : 0x3fffffff);
     const int dmin = j0 - (wq0 + 31), dmax = j0 + BC - 1 - wq0;
-    const bool all_lo = dmax <= -c, all_hi = dmin >= c;
-    const bool tail_lo = all_lo, tail_hi = dmin >= hi_from;  // whole tile in one tail
+    const bool all_lo = dmax <= -band, all_hi = dmin >= band;  // wave-uniform
+    const bool off_band = (SHAW || T5) && (all_lo || all_hi);
     float tmax = kNegInf;
+    if (!(SHAW || T5) || off_band) {
+      // no relative term, or one end value for the whole tile
+      const float rel = (SHAW || T5) ? (all_lo ? Llo : Lhi) : 0.f;
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
+      for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int j = j0 + 32 * kb + key_of_reg<BF16>(i, hh);
-        const int delta = j - qi;
-        float x = s[kb][i] * p.scale_log2;
-        bool vis = true;
-        if (need_mask) vis = (j < kv_len) && (!p.causal || j <= qi);
-        if constexpr (SHAW) {
-          if (all_lo) {
-            x += Llo;
-          } else if (all_hi) {
-            x += Lhi;
-          } else {
-            const int slot = min(max(clip_label(delta, c), p.r_lo), r_hi) - p.r_lo;
-            if constexpr (HAS_WK) x += myLE[slot];
-            if constexpr (HAS_WV) {
-              if (vis && q_ok && delta > -c && delta < c) myLE[slot] = x;
-            }
+        for (int i = 0; i < 16; ++i) {
+          const int ko = 32 * kb + 16 * (i >> 3) + KSTR * (i & 7);
+          float x = fmaf(s[kb][i], p.scale_log2, rel);
+          if (need_mask) x = (ko <= lim) ? x : kNegInf;
+          s[kb][i] = x;
+          tmax = fmaxf(tmax, x);
+        }
+    } else {
+      // band: gather every relative logit of the tile first (8 consecutive
+      // entries per group from one clamped base, see kRelPad), then combine
+      float rv[NKB][16];
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+          const int d0 = kofs + 32 * kb + 16 * g;  // offset of the group's first key
+          const int bidx = min(max(d0 - dlo + kRelPad, 0), nwin + 2 * kRelPad - SPAN);
+          const float* grp = relrow + bidx;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) rv[kb][8 * g + e] = grp[KSTR * e];
+        }
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int ko = 32 * kb + 16 * (i >> 3) + KSTR * (i & 7);
+          float x = fmaf(s[kb][i], p.scale_log2, rv[kb][i]);
+          if (need_mask) x = (ko <= lim) ? x : kNegInf;
+          rv[kb][i] = x;  // unmasked logits of visible keys are kept for write-back
+          s[kb][i] = x;
+          tmax = fmaxf(tmax, x);
+        }
+      if constexpr (SHAW && HAS_WV) {
+        // in-band logits go to their own label slot (the value term needs
+        // them once the row max is final); everything else to the dummy slot.
+        // interior: 1 - c <= delta <= c - 1, visible, live query.
+        const int lo_ko = 1 - c - kofs;
+        const int hi_ko = q_ok ? min(c - 1 - kofs, lim) : lo_ko - 1;
+        const unsigned width = (unsigned)(hi_ko - lo_ko);
+        const int sbase = kofs - dlo + kRelPad;  // slot of key offset 0
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int ko = 32 * kb + 16 * (i >> 3) + KSTR * (i & 7);
+            const bool interior = hi_ko >= lo_ko && (unsigned)(ko - lo_ko) <= width;
+            myLE[interior ? sbase + ko : dummy] = rv[kb][i];
           }
-        }
-        if constexpr (T5) {
-          x += TB[min(max(delta, -p.t5_dist), p.t5_dist) + p.t5_dist];
-        }
-        x = vis ? x : kNegInf;
-        s[kb][i] = x;
-        tmax = fmaxf(tmax, x);
       }
     }
 
@@ -405,64 +505,74 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(const FwdParams p) {
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
     const float m_new = fmaxf(m_run, tmax);
     const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-    const float alpha = exp2f(m_run - m_use);
+    const float alpha = fast_exp2(m_run - m_use);
     m_run = m_new;
     l_part *= alpha;
-    tlo *= alpha;
-    thi *= alpha;
+    if constexpr (SHAW && HAS_WV) thi *= alpha;
+    if (__any(alpha != 1.f)) {  // wave-uniform: skip the rescale when no row max moved
 #pragma unroll
-    for (int mb = 0; mb < DVB; ++mb) oacc[mb] *= alpha;
+      for (int mb = 0; mb < DVB; ++mb) oacc[mb] *= alpha;
+    }
 
-    float psum = 0.f, plo = 0.f, phi = 0.f;
+    float psum = 0.f;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float pv = exp2f(s[kb][i] - m_use);
+        const float pv = fast_exp2(s[kb][i] - m_use);
         s[kb][i] = pv;
         psum += pv;
-        if constexpr (SHAW && HAS_WV) {
-          if (!tail_lo && !tail_hi) {
-            const int delta = j0 + 32 * kb + key_of_reg<BF16>(i, hh) - qi;
-            if (delta <= -c) plo += pv;
-            else if (delta >= hi_from) phi += pv;
-          }
-        }
       }
     }
     l_part += psum;
     if constexpr (SHAW && HAS_WV) {
-      if (tail_lo) plo = psum;
-      else if (tail_hi) phi = psum;
-      tlo += plo;
-      thi += phi;
+      // +c bucket (keys at offset >= c); empty under the causal mask
+      if (!p.causal && !all_lo) {
+        if (all_hi) {
+          thi += psum;
+        } else {
+          const int hi_ko = hi_from - kofs;  // first key offset in the +c bucket
+          float phi = 0.f;
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const int ko = 32 * kb + 16 * (i >> 3) + KSTR * (i & 7);
+              phi += (ko >= hi_ko) ? s[kb][i] : 0.f;
+            }
+          thi += phi;
+        }
+      }
     }
 
     // O^T += V^T P^T
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
       if constexpr (BF16) {
+        bf16x8 va[2][DVB];
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+          for (int mb = 0; mb < DVB; ++mb) {
+            const int dv = min(32 * mb + ql, D - 1);  // rows past D are never stored
+            va[t2][mb] =
+                *reinterpret_cast<const bf16x8*>(Vs + dv * VS + 32 * kb + 16 * t2 + 8 * hh);
+          }
 #pragma unroll
         for (int t2 = 0; t2 < 2; ++t2) {
           bf16x8 pb;
 #pragma unroll
           for (int e = 0; e < 8; ++e) pb[e] = (__bf16)s[kb][8 * t2 + e];
 #pragma unroll
-          for (int mb = 0; mb < DVB; ++mb) {
-            const int dv = 32 * mb + ql;
-            const bf16x8 a = (dv < D)
-                ? *reinterpret_cast<const bf16x8*>(Vs + dv * VS + 32 * kb + 16 * t2 + 8 * hh)
-                : bf16x8{};
-            oacc[mb] = mfma(a, pb, oacc[mb]);
-          }
+          for (int mb = 0; mb < DVB; ++mb) oacc[mb] = mfma(va[t2][mb], pb, oacc[mb]);
         }
       } else {
 #pragma unroll
         for (int s2 = 0; s2 < 16; ++s2) {
 #pragma unroll
           for (int mb = 0; mb < DVB; ++mb) {
-            const int dv = 32 * mb + ql;
-            const float a = (dv < D) ? Vs[(32 * kb + 2 * s2 + hh) * VS + dv] : 0.f;
+            const int dv = min(32 * mb + ql, D - 1);
+            const float a = Vs[(32 * kb + 2 * s2 + hh) * VS + dv];
             oacc[mb] = mfma(a, s[kb][s2], oacc[mb]);
           }
         }
@@ -475,41 +585,39 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(const FwdParams p) {
   const float l = l_part + __shfl_xor(l_part, 32);
   const float inv_l = l > 0.f ? 1.f / l : 0.f;
   if constexpr (SHAW && HAS_WV) {
-    const float tlo_all = tlo + __shfl_xor(tlo, 32);
     const float thi_all = thi + __shfl_xor(thi, 32);
     const float m_fin = (m_run == kNegInf) ? 0.f : m_run;
-    const T* wvh = reinterpret_cast<const T*>(p.wv) + h * p.wv_sh;
-    // weight of label row (r_lo + idx) for this lane's query
-    auto bucket_weight = [&](int idx) -> float {
-      if (idx >= p.nr || !q_ok) return 0.f;
+    // weight of an in-band label row (r_lo + idx): the single key it holds
+    auto interior_weight = [&](int idx) __attribute__((always_inline)) -> float {
       const int r = p.r_lo + idx;
-      float w = 0.f;
-      if (r == 0) w += tlo_all;
-      if (r == 2 * c) w += thi_all;
-      if (r > 0 && r < 2 * c) {
-        const int j = qi + r - c;
-        const bool vis = j >= 0 && j < kv_len && (!p.causal || j <= qi);
-        if (vis) w = exp2f(myLE[idx] - m_fin);
-      }
-      return w;
+      const int j = qi + r - c;
+      const bool ok = idx < p.nr && q_ok && r > 0 && r < 2 * c && j >= 0 && j < kv_len &&
+                      (!p.causal || j <= qi);
+      const float e = myLE[kRelPad + min(idx, p.nr - 1)];
+      return ok ? fast_exp2(e - m_fin) : 0.f;
+    };
+    // the -c bucket holds what the row sum leaves after the band and the +c bucket
+    float isum = 0.f;
+    for (int idx = hh; idx < p.nr; idx += 2) isum += interior_weight(idx);
+    isum += __shfl_xor(isum, 32);
+    const float tlo_all = fmaxf(l - isum - thi_all, 0.f);
+    auto bucket_weight = [&](int idx) __attribute__((always_inline)) -> float {
+      const int r = p.r_lo + idx;
+      const float w = (r == 0 ? tlo_all : 0.f) + (r == 2 * c ? thi_all : 0.f);
+      return (idx < p.nr && q_ok) ? w + interior_weight(idx) : 0.f;
     };
     constexpr int LSTEP = BF16 ? 16 : 2;
-    const int nls = (p.nr + LSTEP - 1) / LSTEP;
+    const int nls = NRP / LSTEP;
     for (int ls = 0; ls < nls; ++ls) {
       if constexpr (BF16) {
         bf16x8 bw;
 #pragma unroll
         for (int e = 0; e < 8; ++e) bw[e] = (__bf16)bucket_weight(ls * 16 + 8 * hh + e);
+        const int WS = NRP + 8;
 #pragma unroll
         for (int mb = 0; mb < DVB; ++mb) {
-          const int dv = 32 * mb + ql;
-          bf16x8 a;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int idx = ls * 16 + 8 * hh + e;
-            a[e] = (idx < p.nr && dv < D) ? wvh[(int64_t)(p.r_lo + idx) * p.wv_sr + dv]
-                                          : (__bf16)0.f;
-          }
+          const int dv = min(32 * mb + ql, D - 1);
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(WV + dv * WS + ls * 16 + 8 * hh);
           oacc[mb] = mfma(a, bw, oacc[mb]);
         }
       } else {
@@ -517,10 +625,8 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(const FwdParams p) {
         const float bw = bucket_weight(idx);
 #pragma unroll
         for (int mb = 0; mb < DVB; ++mb) {
-          const int dv = 32 * mb + ql;
-          const float a = (idx < p.nr && dv < D) ? wvh[(int64_t)(p.r_lo + idx) * p.wv_sr + dv]
-                                                 : 0.f;
-          oacc[mb] = mfma(a, bw, oacc[mb]);
+          const int dv = min(32 * mb + ql, D - 1);
+          oacc[mb] = mfma(WV[idx * (D + 4) + dv], bw, oacc[mb]);
         }
       }
     }
@@ -535,17 +641,16 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(const FwdParams p) {
         const int dv0 = 32 * mb + 8 * g + 4 * hh;
         if (dv0 < D) {
           if constexpr (BF16) {
-            __bf16 o4[4];
+            typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+            bf16x4 o4;
 #pragma unroll
             for (int e = 0; e < 4; ++e) o4[e] = (__bf16)(oacc[mb][4 * g + e] * inv_l);
-            *reinterpret_cast<uint2*>(orow + dv0) = *reinterpret_cast<const uint2*>(o4);
+            *reinterpret_cast<bf16x4*>(orow + dv0) = o4;
           } else {
-            float4 o4;
-            o4.x = oacc[mb][4 * g + 0] * inv_l;
-            o4.y = oacc[mb][4 * g + 1] * inv_l;
-            o4.z = oacc[mb][4 * g + 2] * inv_l;
-            o4.w = oacc[mb][4 * g + 3] * inv_l;
-            *reinterpret_cast<float4*>(orow + dv0) = o4;
+            f32x4 o4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o4[e] = oacc[mb][4 * g + e] * inv_l;
+            *reinterpret_cast<f32x4*>(orow + dv0) = o4;
           }
         }
       }
@@ -566,11 +671,17 @@ __global__ void debug_indices_kernel(int n, int clip, T5Buckets t5, int use_t5,
 // ---------------------------------------------------------------------------
 
 template <bool BF16, int D, int NW, int BC>
-static size_t lds_bytes_t(RelMode mode, int nr, int t5_dist) {
+static size_t lds_bytes_t(RelMode mode, bool has_wv, int nr, int t5_dist) {
   using G = Geo<BF16, D, NW, BC>;
   size_t extra = 0;
-  if (mode == kRelShaw) extra = (size_t)G::BR * label_row_stride_impl(nr) * sizeof(float);
-  if (mode == kRelT5) extra = (size_t)(2 * t5_dist + 1) * sizeof(float);
+  if (mode == kRelShaw) {
+    extra = (size_t)G::BR * label_row_stride_impl(nr) * sizeof(float);
+    if (has_wv) {
+      const size_t nrp = value_rows_padded(nr);
+      extra += BF16 ? (size_t)D * (nrp + 8) * 2 : nrp * (D + 4) * 4;
+    }
+  }
+  if (mode == kRelT5) extra = (size_t)(2 * t5_dist + 1 + 2 * kRelPad) * sizeof(float);
   return G::TILE_BYTES + extra;
 }
 
@@ -579,10 +690,9 @@ constexpr int kBlockKeysF32 = 32;
 
 size_t lds_bytes(bool bf16, int d, const LaunchCfg& cfg, RelMode mode, bool has_wv,
                  int nr, int t5_dist) {
-  (void)has_wv;
 #define RELATTN_LDS(BF, DD, NWW, BCC) \
   if (bf16 == BF && d == DD && cfg.waves == NWW && cfg.kblock == BCC) \
-    return lds_bytes_t<BF, DD, NWW, BCC>(mode, nr, t5_dist);
+    return lds_bytes_t<BF, DD, NWW, BCC>(mode, has_wv, nr, t5_dist);
 #define RELATTN_LDS_D(BF, NWW, BCC) \
   RELATTN_LDS(BF, 16, NWW, BCC) RELATTN_LDS(BF, 32, NWW, BCC) \
   RELATTN_LDS(BF, 64, NWW, BCC) RELATTN_LDS(BF, 128, NWW, BCC)
@@ -598,7 +708,7 @@ size_t lds_bytes(bool bf16, int d, const LaunchCfg& cfg, RelMode mode, bool has_
 template <int D, int NW, int BC, bool BF16, int MODE, bool HAS_WK, bool HAS_WV>
 static int launch_t(const FwdParams& p, void* stream) {
   auto kern = fwd_kernel<D, NW, BC, BF16, MODE, HAS_WK, HAS_WV>;
-  const size_t lds = lds_bytes_t<BF16, D, NW, BC>((RelMode)MODE, p.nr, p.t5_dist);
+  const size_t lds = lds_bytes_t<BF16, D, NW, BC>((RelMode)MODE, HAS_WV, p.nr, p.t5_dist);
   if (lds > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
