@@ -285,8 +285,8 @@ int make_plan(const relattn_tensor* q, const relattn_tensor* k, const relattn_te
   std::vector<LaunchCfg> order;
   if (P.bf16) {
     const int64_t wgs4 = B * H * ((n + 127) / 128);
-    if (wgs4 >= 512) order = {{4, 64}, {2, 64}};
-    else order = {{2, 64}, {4, 64}};
+    if (wgs4 >= 512) order = {{4, 64}, {2, 64}, {1, 64}};
+    else order = {{2, 64}, {4, 64}, {1, 64}};
   } else {
     if (n <= 32) order = {{1, 32}, {2, 32}};
     else order = {{2, 32}, {1, 32}};

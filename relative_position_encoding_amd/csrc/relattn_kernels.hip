@@ -81,7 +81,7 @@ __device__ __forceinline__ int t5_bucket(int delta, const T5Buckets& t) {
 }
 
 // Relative-logit rows in LDS hold the nr reachable labels between kRelPad
-// copies of the first and of the last label on each side, plus one dummy slot.
+// copies of the first and of the last label on each side.
 // With the padding, a group of 8 consecutive logits reads 8 consecutive
 // entries from one clamped base index, whether the group lies in the band,
 // in a tail or across an edge; no per-element clamp is needed.
@@ -90,8 +90,20 @@ constexpr int kRelPad = 16;
 __host__ __device__ inline int label_row_stride_impl(int nr) {
   // even stride: consecutive query rows hit distinct LDS banks when the lanes
   // of a wave gather along a diagonal j - i
-  return (nr + 2 * kRelPad + 1 + 1) & ~1;
+  return (nr + 2 * kRelPad + 1) & ~1;
 }
+
+// In-band logits are written back to a second row per query, indexed by
+// label + 1 and clamped to [0, nr + 1]: entries 0 and nr + 1 take every logit
+// outside the label window, and the tail labels take every logit of their
+// tail; the epilogue reads only the in-band labels, so no per-element test
+// is needed.  Even stride for the same bank argument as above.
+__host__ __device__ inline int logit_row_stride_impl(int nr) { return (nr + 2 + 1) & ~1; }
+
+// A row max may run ahead of the max used for the exponentials by this much
+// (log2 units) before the running sums are rescaled: p <= 2^8 stays exact in
+// fp32 sums and in bf16 operands, and most tiles then skip the rescale.
+constexpr float kRescaleSlack = 8.f;
 
 // Label rows of the value table staged in LDS, padded to whole MFMA steps.
 __host__ __device__ inline int value_rows_padded(int nr) { return (nr + 15) & ~15; }
@@ -194,8 +206,11 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(const FwdParams p) {
   T* Vs = Ks + G::K_ELEMS;
   float* LE = reinterpret_cast<float*>(smem + G::TILE_BYTES);
   float* TB = LE;
-  T* WV = reinterpret_cast<T*>(LE + BR * RS);
+  float* EB = LE + BR * RS;  // in-band logits (value term)
+  const int ERS = logit_row_stride_impl(p.nr);
+  T* WV = reinterpret_cast<T*>(EB + (HAS_WV ? BR * ERS : 0));
   float* myLE = LE + qrow * RS;
+  float* myEB = EB + qrow * ERS;
 
   const T* qg = reinterpret_cast<const T*>(p.q) + b * p.q_sb + h * p.q_sh;
   const T* kg = reinterpret_cast<const T*>(p.k) + b * p.k_sb + h * p.k_sh;
@@ -402,7 +417,6 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(const FwdParams p) {
   constexpr int KSTR = BF16 ? 1 : 2;  // key step between consecutive registers
   constexpr int SPAN = 7 * KSTR + 1;  // keys spanned by a group of 8 registers
   const int hoff = BF16 ? 8 * hh : hh;  // key offset of this lane half
-  const int dummy = p.nr + 2 * kRelPad;
 
   for (int t = 0; t < ntiles; ++t) {
     const int j0 = t * BC;
@@ -483,36 +497,33 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(const FwdParams p) {
           tmax = fmaxf(tmax, x);
         }
       if constexpr (SHAW && HAS_WV) {
-        // in-band logits go to their own label slot (the value term needs
-        // them once the row max is final); everything else to the dummy slot.
-        // interior: 1 - c <= delta <= c - 1, visible, live query.
-        const int lo_ko = 1 - c - kofs;
-        const int hi_ko = q_ok ? min(c - 1 - kofs, lim) : lo_ko - 1;
-        const unsigned width = (unsigned)(hi_ko - lo_ko);
-        const int sbase = kofs - dlo + kRelPad;  // slot of key offset 0
+        // logits to their label slot of the write-back row (see
+        // logit_row_stride_impl); masked keys are harmless there because the
+        // epilogue re-checks visibility
+        const int wbase = kofs + c - p.r_lo + 1;  // entry of key offset 0
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int ko = 32 * kb + 16 * (i >> 3) + KSTR * (i & 7);
-            const bool interior = hi_ko >= lo_ko && (unsigned)(ko - lo_ko) <= width;
-            myLE[interior ? sbase + ko : dummy] = rv[kb][i];
+            myEB[min(max(wbase + ko, 0), p.nr + 1)] = rv[kb][i];
           }
       }
     }
 
     // online softmax: one cross-lane max per tile, everything else per lane
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    const float m_new = fmaxf(m_run, tmax);
-    const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-    const float alpha = fast_exp2(m_run - m_use);
-    m_run = m_new;
-    l_part *= alpha;
-    if constexpr (SHAW && HAS_WV) thi *= alpha;
-    if (__any(alpha != 1.f)) {  // wave-uniform: skip the rescale when no row max moved
+    const bool grow = tmax > m_run + kRescaleSlack;  // -inf + slack is -inf
+    if (__any(grow)) {  // wave-uniform
+      const float m_next = grow ? tmax : m_run;
+      const float alpha = fast_exp2(m_run - m_next);  // 0 when m_run is -inf
+      m_run = m_next;
+      l_part *= alpha;
+      if constexpr (SHAW && HAS_WV) thi *= alpha;
 #pragma unroll
       for (int mb = 0; mb < DVB; ++mb) oacc[mb] *= alpha;
     }
+    const float m_use = (m_run == kNegInf) ? 0.f : m_run;
 
     float psum = 0.f;
 #pragma unroll
@@ -593,7 +604,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(const FwdParams p) {
       const int j = qi + r - c;
       const bool ok = idx < p.nr && q_ok && r > 0 && r < 2 * c && j >= 0 && j < kv_len &&
                       (!p.causal || j <= qi);
-      const float e = myLE[kRelPad + min(idx, p.nr - 1)];
+      const float e = myEB[1 + min(idx, p.nr - 1)];
       return ok ? fast_exp2(e - m_fin) : 0.f;
     };
     // the -c bucket holds what the row sum leaves after the band and the +c bucket
@@ -677,6 +688,7 @@ static size_t lds_bytes_t(RelMode mode, bool has_wv, int nr, int t5_dist) {
   if (mode == kRelShaw) {
     extra = (size_t)G::BR * label_row_stride_impl(nr) * sizeof(float);
     if (has_wv) {
+      extra += (size_t)G::BR * logit_row_stride_impl(nr) * sizeof(float);
       const size_t nrp = value_rows_padded(nr);
       extra += BF16 ? (size_t)D * (nrp + 8) * 2 : nrp * (D + 4) * 4;
     }
@@ -696,6 +708,7 @@ size_t lds_bytes(bool bf16, int d, const LaunchCfg& cfg, RelMode mode, bool has_
 #define RELATTN_LDS_D(BF, NWW, BCC) \
   RELATTN_LDS(BF, 16, NWW, BCC) RELATTN_LDS(BF, 32, NWW, BCC) \
   RELATTN_LDS(BF, 64, NWW, BCC) RELATTN_LDS(BF, 128, NWW, BCC)
+  RELATTN_LDS_D(true, 1, kBlockKeys)
   RELATTN_LDS_D(true, 2, kBlockKeys)
   RELATTN_LDS_D(true, 4, kBlockKeys)
   RELATTN_LDS_D(false, 1, kBlockKeysF32)
@@ -749,6 +762,7 @@ int launch_fwd(bool bf16, int d, const LaunchCfg& cfg, RelMode mode, bool has_wk
                bool has_wv, const FwdParams& p, void* stream) {
   if (bf16) {
     if (cfg.kblock != kBlockKeys) return (int)hipErrorInvalidValue;
+    if (cfg.waves == 1) return launch_d<1, kBlockKeys, true>(d, mode, has_wk, has_wv, p, stream);
     if (cfg.waves == 2) return launch_d<2, kBlockKeys, true>(d, mode, has_wk, has_wv, p, stream);
     if (cfg.waves == 4) return launch_d<4, kBlockKeys, true>(d, mode, has_wk, has_wv, p, stream);
   } else {
