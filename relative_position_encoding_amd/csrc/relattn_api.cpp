@@ -138,6 +138,7 @@ int check_t5(const relattn_t5_params* t5, T5Buckets* out) {
     return RELATTN_OK;
   }
   T5Buckets tb = {};
+  tb.nb = nb;
   tb.half = half;
   tb.exact = exact;
   tb.nlog = nlog;
@@ -164,7 +165,7 @@ struct Plan {
   bool empty = false;
   bool bf16 = false;
   int d = 0;
-  LaunchCfg cfg{2, 64};
+  LaunchCfg cfg{2, 64, 2, true};
   RelMode mode = relattn::kRelNone;
   bool has_wk = false, has_wv = false;
   FwdParams p{};
@@ -277,20 +278,29 @@ int make_plan(const relattn_tensor* q, const relattn_tensor* k, const relattn_te
   p.scale_log2 = s * 1.4426950408889634f;
 
   // Workgroup shape: 32 query rows per wave; prefer 4 waves when that still
-  // gives at least two workgroups per compute unit (256 CUs).
+  // gives at least two workgroups per compute unit (256 CUs), and a 3-tile
+  // K/V ring when it fits next to the relative tables.
+  const int nb = is_t5 ? t5->num_buckets : 0;
   auto lds_ok = [&](const LaunchCfg& c) {
-    return relattn::lds_bytes(P.bf16, P.d, c, P.mode, P.has_wv, p.nr, p.t5_dist) <=
-           kMaxLdsBytes;
+    return relattn::lds_bytes(P.bf16, P.d, c, P.mode, P.has_wk, P.has_wv, p.nr, p.t5_dist,
+                              nb) <= kMaxLdsBytes;
   };
-  std::vector<LaunchCfg> order;
+  std::vector<int> waves;
+  int kblock;
   if (P.bf16) {
+    kblock = 64;
     const int64_t wgs4 = B * H * ((n + 127) / 128);
-    if (wgs4 >= 512) order = {{4, 64}, {2, 64}, {1, 64}};
-    else order = {{2, 64}, {4, 64}, {1, 64}};
+    if (wgs4 >= 512) waves = {4, 2, 1};
+    else waves = {2, 4, 1};
   } else {
-    if (n <= 32) order = {{1, 32}, {2, 32}};
-    else order = {{2, 32}, {1, 32}};
+    kblock = 32;
+    if (n <= 32) waves = {1, 2};
+    else waves = {2, 1};
   }
+  std::vector<LaunchCfg> order;
+  for (bool res : {true, false})
+    for (int w : waves)
+      for (int st : {3, 2}) order.push_back({w, kblock, st, res});
   bool found = false;
   for (const auto& c : order)
     if (lds_ok(c)) {
@@ -309,6 +319,8 @@ int make_plan(const relattn_tensor* q, const relattn_tensor* k, const relattn_te
   }
   const int br = 32 * P.cfg.waves;
   p.n_qtiles = (int32_t)((n + br - 1) / br);
+  p.nstage = P.cfg.nstage;
+  p.wv_resident = P.cfg.wv_resident ? 1 : 0;
   if (B * H * (int64_t)p.n_qtiles > INT32_MAX)
     return fail(RELATTN_ERR_UNSUPPORTED, "too many workgroups (B*H*ceil(n/%d))", br);
 

@@ -13,6 +13,7 @@ constexpr int kMaxT5Thresholds = 64;
 // floor(nlog * ln(a / exact) / ln(D_max / exact)) is at least t + 1; the host
 // derives it with exact integer arithmetic.
 struct T5Buckets {
+  int32_t nb;       // number of buckets (rows of the bias table)
   int32_t half;     // buckets per sign (bidirectional) or all buckets
   int32_t exact;    // B_exact = half / 2
   int32_t nlog;     // half - exact logarithmic buckets
@@ -46,6 +47,8 @@ struct FwdParams {
   float scale_log2;        // logit scale times log2(e)
   int32_t t5_dist;         // offsets are clamped to [-t5_dist, t5_dist]
   int32_t n_qtiles;        // query tiles per (b, h)
+  int32_t nstage;          // K/V tiles in the LDS ring (2 or 3)
+  int32_t wv_resident;     // w^V tile loaded up front (else staged after the loop)
   T5Buckets t5;
 };
 
@@ -55,12 +58,13 @@ enum RelMode { kRelNone = 0, kRelShaw = 1, kRelT5 = 2 };
 struct LaunchCfg {
   int waves;   // 32 query rows per wave
   int kblock;  // keys per tile
+  int nstage;  // K/V tiles in the LDS ring
+  bool wv_resident;  // w^V tile has its own LDS region
 };
 
-// Host-side helpers shared with the launcher.
-int label_row_stride(int nr);
-size_t lds_bytes(bool bf16, int d, const LaunchCfg& cfg, RelMode mode,
-                 bool has_wv, int nr, int t5_dist);
+// Dynamic LDS bytes of one workgroup (same layout function as the kernel).
+size_t lds_bytes(bool bf16, int d, const LaunchCfg& cfg, RelMode mode, bool has_wk,
+                 bool has_wv, int nr, int t5_dist, int t5_nb);
 
 // Launchers (relattn_kernels.hip).  Return a hipError_t value.
 int launch_fwd(bool bf16, int d, const LaunchCfg& cfg, RelMode mode, bool has_wk,
