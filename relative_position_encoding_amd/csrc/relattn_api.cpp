@@ -35,6 +35,9 @@ int fail(int code, const char* fmt, ...) {
 }
 
 constexpr size_t kMaxLdsBytes = 160 * 1024;  // LDS per workgroup on gfx950
+// compute units of an MI355X; only the launch-shape heuristic uses it (the
+// plan is made on the host, without a device)
+constexpr int64_t kNumCUs = 256;
 constexpr int64_t kMaxSeq = int64_t(1) << 30;
 
 size_t elem_size(int dtype) { return dtype == RELATTN_BF16 ? 2 : 4; }
@@ -165,7 +168,7 @@ struct Plan {
   bool empty = false;
   bool bf16 = false;
   int d = 0;
-  LaunchCfg cfg{2, 64, 2, true};
+  LaunchCfg cfg{2, 64, 2, relattn::kWvResident};
   RelMode mode = relattn::kRelNone;
   bool has_wk = false, has_wv = false;
   FwdParams p{};
@@ -277,13 +280,14 @@ int make_plan(const relattn_tensor* q, const relattn_tensor* k, const relattn_te
                               : (is_t5 ? 1.f : 1.f / std::sqrt((float)d));
   p.scale_log2 = s * 1.4426950408889634f;
 
-  // Workgroup shape: 32 query rows per wave; prefer 4 waves when that still
-  // gives at least two workgroups per compute unit (256 CUs), and a 3-tile
-  // K/V ring when it fits next to the relative tables.
+  // Workgroup shape: 32 query rows per wave, 64-key (bf16) or 32-key (fp32)
+  // tiles, a 3- or 2-tile K/V ring and one of three places for the w^V rows.
+  // Among the shapes whose LDS fits, take the one that keeps the most waves
+  // of this grid resident per compute unit (two per SIMD for d <= 64, one
+  // for d = 128, as the kernels are compiled); ties go to the earlier one.
   const int nb = is_t5 ? t5->num_buckets : 0;
-  auto lds_ok = [&](const LaunchCfg& c) {
-    return relattn::lds_bytes(P.bf16, P.d, c, P.mode, P.has_wk, P.has_wv, p.nr, p.t5_dist,
-                              nb) <= kMaxLdsBytes;
+  auto lds_of = [&](const LaunchCfg& c) {
+    return relattn::lds_bytes(P.bf16, P.d, c, P.mode, P.has_wk, P.has_wv, p.nr, p.t5_dist, nb);
   };
   std::vector<int> waves;
   int kblock;
@@ -297,17 +301,28 @@ int make_plan(const relattn_tensor* q, const relattn_tensor* k, const relattn_te
     if (n <= 32) waves = {1, 2};
     else waves = {2, 1};
   }
+  const int vgpr_waves_per_cu = d <= 64 ? 8 : 4;
   std::vector<LaunchCfg> order;
-  for (bool res : {true, false})
-    for (int w : waves)
-      for (int st : {3, 2}) order.push_back({w, kblock, st, res});
+  for (int w : waves)
+    for (int st : {3, 2})
+      for (int wm : {relattn::kWvResident, relattn::kWvRing, relattn::kWvChunked})
+        order.push_back({w, kblock, st, wm});
   bool found = false;
-  for (const auto& c : order)
-    if (lds_ok(c)) {
+  int64_t best = -1;
+  for (const auto& c : order) {
+    const size_t lds = lds_of(c);
+    if (lds > kMaxLdsBytes) continue;
+    const int64_t wgs = B * H * ((n + 32 * c.waves - 1) / (32 * c.waves));
+    const int64_t fit = std::min<int64_t>(vgpr_waves_per_cu / c.waves,
+                                          lds ? (int64_t)(kMaxLdsBytes / lds) : 64);
+    const int64_t need = (wgs + kNumCUs - 1) / kNumCUs;  // workgroups per CU in one round
+    const int64_t resident = std::min(fit, need) * c.waves;
+    if (resident > best) {
+      best = resident;
       P.cfg = c;
       found = true;
-      break;
     }
+  }
   if (!found) {
     if (P.mode == relattn::kRelT5)
       return fail(RELATTN_ERR_UNSUPPORTED,
@@ -320,7 +335,15 @@ int make_plan(const relattn_tensor* q, const relattn_tensor* k, const relattn_te
   const int br = 32 * P.cfg.waves;
   p.n_qtiles = (int32_t)((n + br - 1) / br);
   p.nstage = P.cfg.nstage;
-  p.wv_resident = P.cfg.wv_resident ? 1 : 0;
+  p.wv_mode = P.cfg.wv_mode;
+  {
+    // stage loads address a tile's rows by 32-bit byte offsets from its first
+    // row when that range fits
+    const int64_t esz = P.bf16 ? 2 : 4;
+    const int64_t span_k = (int64_t)P.cfg.kblock * k->stride[2] * esz;
+    const int64_t span_v = (int64_t)P.cfg.kblock * v->stride[2] * esz;
+    p.dma32 = (span_k < (int64_t)1 << 31 && span_v < (int64_t)1 << 31) ? 1 : 0;
+  }
   if (B * H * (int64_t)p.n_qtiles > INT32_MAX)
     return fail(RELATTN_ERR_UNSUPPORTED, "too many workgroups (B*H*ceil(n/%d))", br);
 

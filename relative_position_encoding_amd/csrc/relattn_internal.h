@@ -48,21 +48,28 @@ struct FwdParams {
   int32_t t5_dist;         // offsets are clamped to [-t5_dist, t5_dist]
   int32_t n_qtiles;        // query tiles per (b, h)
   int32_t nstage;          // K/V tiles in the LDS ring (2 or 3)
-  int32_t wv_resident;     // w^V tile loaded up front (else staged after the loop)
+  int32_t wv_mode;         // WvMode: where the w^V tile is staged
+  int32_t dma32;           // K/V tile rows fit 32-bit byte offsets (fast stage loads)
   T5Buckets t5;
 };
 
 enum RelMode { kRelNone = 0, kRelShaw = 1, kRelT5 = 2 };
+
+// Where the w^V rows wait for the epilogue: their own LDS region (loaded in
+// the prologue), the first K/V ring stage the loop frees, or the free ring
+// after the loop in chunks.
+enum WvMode { kWvResident = 0, kWvRing = 1, kWvChunked = 2 };
 
 // Kernel configuration picked by the host for one call.
 struct LaunchCfg {
   int waves;   // 32 query rows per wave
   int kblock;  // keys per tile
   int nstage;  // K/V tiles in the LDS ring
-  bool wv_resident;  // w^V tile has its own LDS region
+  int wv_mode;  // WvMode
 };
 
-// Dynamic LDS bytes of one workgroup (same layout function as the kernel).
+// Dynamic LDS bytes of one workgroup (same layout function as the kernel);
+// SIZE_MAX when the configuration cannot hold the tables.
 size_t lds_bytes(bool bf16, int d, const LaunchCfg& cfg, RelMode mode, bool has_wk,
                  bool has_wv, int nr, int t5_dist, int t5_nb);
 

@@ -212,16 +212,47 @@ __device__ __forceinline__ void dma_stage(unsigned char RELATTN_LDS* st, const T
   }
 }
 
+// The same stage with a uniform base pointer per tensor and per-lane 32-bit
+// byte offsets computed once (stage_offsets): no clamp and no 64-bit address
+// arithmetic per tile, so the loads take the scalar-base + vector-offset
+// form.  For tiles that lie entirely below the last valid row.
+template <int ROWB, int NW, int BC, typename T>
+__device__ __forceinline__ void stage_offsets(uint32_t (&off)[2 * BC * ROWB / 1024 / NW],
+                                              int64_t k_stride, int64_t v_stride, int wave,
+                                              int lane) {
+  constexpr int CPR = ROWB / 16;
+  constexpr int NI_TILE = BC * ROWB / 1024;
+  constexpr int NI = 2 * NI_TILE;
+#pragma unroll
+  for (int u = 0; u < NI / NW; ++u) {
+    const int I = wave + u * NW;
+    const bool is_v = I >= NI_TILE;
+    const int o = (is_v ? I - NI_TILE : I) * 1024 + lane * 16;
+    const int r = o / ROWB;
+    const int c = ((o % ROWB) >> 4) ^ chunk_swizzle<CPR>(r);
+    off[u] = (uint32_t)((int64_t)r * (is_v ? v_stride : k_stride) * (int64_t)sizeof(T) + c * 16);
+  }
+}
+template <int ROWB, int NW, int BC, typename T>
+__device__ __forceinline__ void dma_stage_fast(unsigned char RELATTN_LDS* st, const T* kbase,
+                                               const T* vbase,
+                                               const uint32_t (&off)[2 * BC * ROWB / 1024 / NW],
+                                               int wave) {
+  constexpr int NI_TILE = BC * ROWB / 1024;
+  constexpr int NI = 2 * NI_TILE;
+#pragma unroll
+  for (int u = 0; u < NI / NW; ++u) {
+    const int I = wave + u * NW;
+    const bool is_v = I >= NI_TILE;  // wave-uniform
+    const unsigned char* b = reinterpret_cast<const unsigned char*>(is_v ? vbase : kbase);
+    __builtin_amdgcn_global_load_lds((const RELATTN_GLOBAL void*)(b + off[u]),
+                                     (RELATTN_LDS void*)(st + I * 1024), 16, 0, 0);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Geometry and LDS budget, identical on host and device.
 // ---------------------------------------------------------------------------
-
-// Relative-logit rows hold the nr reachable labels between rel_pad copies of
-// the first and of the last label on each side: a group of 8 logits (keys
-// KSTR apart) then reads 8 entries from one clamped base, whether the group
-// lies in the band, in a tail or across an edge.
-template <bool BF16>
-__host__ __device__ constexpr int rel_pad() { return BF16 ? 8 : 16; }
 
 template <bool BF16, int D, int NW, int BC>
 struct Geo {
@@ -237,23 +268,36 @@ struct Geo {
   static constexpr int TILEB = BC * ROWB;         // one K or V tile
   static constexpr int STAGEB = 2 * TILEB;        // K then V
   static constexpr int LPW = STAGEB / 1024 / NW;  // DMA instructions per wave per stage
-  static constexpr int PAD = rel_pad<BF16>();
+  // A lane's logits come in groups of 8 keys KSTR apart, spanning SPAN
+  // offsets.  Relative-logit rows hold the reachable labels with PADL copies
+  // of the first label below and PADU copies of the last above: a group then
+  // reads its 8 entries from one base clamped to [0, labels + PADL + PADU -
+  // SPAN], whether it lies in the band, in a tail or across an edge, and the
+  // top SPAN entries stay clear of the band-logit stores (which reach at most
+  // SPAN - 1 entries past the last label).
+  static constexpr int KSTR = BF16 ? 1 : 2;
+  static constexpr int SPAN = 7 * KSTR + 1;
+  static constexpr int PADL = SPAN - 1;
+  static constexpr int PADU = 2 * SPAN - 1;
   static_assert(STAGEB % (1024 * NW) == 0, "stage must split into whole 1 KB instructions");
+  static_assert(BR * ROWB <= STAGEB, "the Q tile must fit one ring stage");
+  static_assert(BR * ROWB % 1024 == 0, "the Q tile must split into whole 1 KB instructions");
 };
 
 struct Layout {
-  int wk, wv, le, tbc, tb, total;  // byte offsets / total bytes
+  int wk, wv, le, tbc, tb, qs, total;  // byte offsets / total bytes
   int wk_rows, wv_rows, lrs;       // tile rows, relative-row stride (floats)
   int wk_chunk;                    // w^K rows staged at a time (multiple of 32)
   int wv_chunk;                    // w^V rows staged at a time (multiple of 16)
 };
 
-// wv_resident: the w^V tile gets its own region, loaded in the prologue;
-// otherwise it is staged in chunks through the free ring after the loop.
+// w^V staging (wv_mode): kWvResident gives the tile its own region, loaded
+// in the prologue; kWvRing loads it into the first ring stage the loop no
+// longer needs (it must fit one stage); kWvChunked stages it in chunks
+// through the free ring after the loop.
 template <bool BF16, int D, int NW, int BC>
 __host__ __device__ inline Layout make_layout(int mode, bool has_wk, bool has_wv, int nr,
-                                              int nstage, int t5_dist, int t5_nb,
-                                              bool wv_resident) {
+                                              int nstage, int t5_dist, int t5_nb, int wv_mode) {
   using G = Geo<BF16, D, NW, BC>;
   Layout L{};
   int off = nstage * G::STAGEB;
@@ -265,24 +309,41 @@ __host__ __device__ inline Layout make_layout(int mode, bool has_wk, bool has_wv
   const bool shaw = mode == kRelShaw, t5 = mode == kRelT5;
   L.wk_rows = dma_rows((nr + 31) & ~31, G::ROWB);
   L.wv_rows = dma_rows((nr + 15) & ~15, G::ROWB);
-  // relative row: padding, nr labels, padding, one dummy slot; even stride so
-  // that the rows of one wave hit distinct banks along a diagonal j - i
-  L.lrs = (nr + 2 * G::PAD + 1 + 1) & ~1;
+  // relative row: padding, nr labels, padding.  Dword LDS accesses are
+  // served 32 lanes at a time by 32 banks; the lanes of a wave hold 32
+  // consecutive queries and read their rows along a diagonal j - i (or, once
+  // clamped, down a column).  A stride of 2 mod 4 keeps both patterns, and
+  // the two dwords of each ds_read2/ds_write2, nearly free of bank conflicts
+  // (measured: a stride of 0 mod 8 costs about five times as many).
+  {
+    const int m = nr + G::PADL + G::PADU;
+    L.lrs = m + ((2 - m) & 3);
+  }
   // the w^K tile is read once, before the loop, in label blocks of 32: it is
   // staged in the last ring stage, which receives its first K/V tile only
   // inside the loop (in several chunks if it does not fit)
   L.wk = (nstage - 1) * G::STAGEB;
   L.wk_chunk = min(L.wk_rows, (G::STAGEB / G::ROWB) / 32 * 32);
-  if (shaw && has_wv && wv_resident) {
+  L.wv = 0;
+  L.wv_chunk = L.wv_rows;
+  if (shaw && has_wv && wv_mode == kWvResident) {
     L.wv = take(L.wv_rows * G::ROWB);
-    L.wv_chunk = L.wv_rows;
-  } else {
-    L.wv = 0;  // ring stages, free after the loop
+  } else if (shaw && has_wv && wv_mode == kWvChunked) {
     L.wv_chunk = min(L.wv_rows, (nstage * G::STAGEB / G::ROWB) / 16 * 16);
   }
-  L.le = (shaw && (has_wk || has_wv)) ? take(G::BR * L.lrs * 4) : off;
+  // The Q tile of the workgroup arrives by LDS-DMA and is read into registers
+  // in the prologue: it borrows the relative rows (written only afterwards),
+  // or else the last ring stage, which the loop fills first.
+  const int q_bytes = G::BR * G::ROWB;
+  if (shaw && (has_wk || has_wv)) {
+    L.le = take(max(G::BR * L.lrs * 4, q_bytes));
+    L.qs = L.le;
+  } else {
+    L.le = off;
+    L.qs = (nstage - 1) * G::STAGEB;
+  }
   L.tbc = t5 ? take(((t5_nb + 63) & ~63) * 4) : off;
-  L.tb = t5 ? take((2 * t5_dist + 1 + 2 * G::PAD) * 4) : off;
+  L.tb = t5 ? take((2 * t5_dist + 1 + G::PADL + G::PADU) * 4) : off;
   L.total = off;
   return L;
 }
@@ -326,6 +387,34 @@ __device__ __forceinline__ float elem_f32(const unsigned char* tile, int row, in
 // apart from the K/V stages still streaming into other ring slots by LDS-DMA
 // and would otherwise wait for all of those first.  frag_col_wait() completes
 // them; its register operands order every use after the wait.
+// Lane part of the two transpose reads for columns dv0.. of a block of rows
+// starting at a multiple of 16 (the swizzle depends on row bits 1-3 only, so
+// rows 16 apart differ by a constant offset).
+template <int ROWB, int D>
+__device__ __forceinline__ void frag_col_base(int dv0, int lane, uint32_t& lo, uint32_t& hi) {
+  int col = dv0 + (lane & 16) + 4 * (lane & 3);
+  if constexpr (D < 32) col = min(col, D - 4);  // columns past D feed rows never stored
+  const int row = 8 * (lane >> 5) + ((lane & 15) >> 2);
+  lo = (uint32_t)tile_offset<ROWB>(row, col * 2);
+  hi = (uint32_t)tile_offset<ROWB>(row + 4, col * 2);
+}
+// Transpose reads at precomputed lane bases plus a constant row offset.
+template <int OFS>
+__device__ __forceinline__ void frag_col_issue_at(uint32_t base_lo, uint32_t base_hi,
+                                                  bf16x4& lo, bf16x4& hi) {
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(lo) : "v"(base_lo), "n"(OFS));
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(hi) : "v"(base_hi), "n"(OFS));
+}
+template <int ROWB>
+__device__ __forceinline__ void frag_col_issue_blk(int blk16, uint32_t base_lo, uint32_t base_hi,
+                                                   bf16x4& lo, bf16x4& hi) {
+  switch (blk16) {  // resolved at compile time once the caller's loops unroll
+    case 0: frag_col_issue_at<0>(base_lo, base_hi, lo, hi); break;
+    case 1: frag_col_issue_at<16 * ROWB>(base_lo, base_hi, lo, hi); break;
+    case 2: frag_col_issue_at<32 * ROWB>(base_lo, base_hi, lo, hi); break;
+    default: frag_col_issue_at<48 * ROWB>(base_lo, base_hi, lo, hi); break;
+  }
+}
 template <int ROWB, int D>
 __device__ __forceinline__ void frag_col_issue(uint32_t tile_lds, int row0, int dv0, int lane,
                                                bf16x4& lo, bf16x4& hi) {
@@ -356,6 +445,19 @@ __device__ __forceinline__ int xcd_remap(int bid, int G) {
                      : rem * (per + 1) + (xcd - rem) * per + loc;
 }
 
+// Sum and max of a value over the two lane halves (lanes l and l ^ 32, which
+// hold the two key halves of the same query): one v_permlane32_swap.
+__device__ __forceinline__ float halves_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float halves_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // Two waves per SIMD for d <= 64 (they hide each other's softmax and memory
 // latency); d = 128 needs the whole register file for one.
 template <int D, int NW, int BC, bool BF16, int MODE, bool HAS_WK, bool HAS_WV>
@@ -365,12 +467,11 @@ __attribute__((amdgpu_waves_per_eu(D <= 64 ? 2 : 1))) void fwd_kernel(const FwdP
   using T = typename G::T;
   using Op = std::conditional_t<BF16, bf16x8, float>;
   constexpr int NT = G::NT, NKB = G::NKB, DVB = G::DVB;
-  constexpr int NKS = G::NKS, ROWB = G::ROWB, PAD = G::PAD, LPW = G::LPW;
+  constexpr int NKS = G::NKS, ROWB = G::ROWB, LPW = G::LPW;
+  constexpr int KSTR = G::KSTR, SPAN = G::SPAN, PADL = G::PADL, PADU = G::PADU;
   constexpr bool SHAW = (MODE == kRelShaw);
   constexpr bool T5 = (MODE == kRelT5);
   constexpr bool GATHER = (SHAW && HAS_WK) || T5;  // a gathered relative logit
-  constexpr int KSTR = BF16 ? 1 : 2;  // key step between consecutive registers
-  constexpr int SPAN = 7 * KSTR + 1;  // keys spanned by a group of 8 registers
 
   // ---- which tile
   const int lid = xcd_remap(blockIdx.x, gridDim.x);
@@ -379,7 +480,8 @@ __attribute__((amdgpu_waves_per_eu(D <= 64 ? 2 : 1))) void fwd_kernel(const FwdP
   if (p.causal) qt = p.n_qtiles - 1 - qt;  // longest causal rows first
   const int b = bh / p.H, h = bh - b * p.H;
   const int i0 = qt * (32 * NW);
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar loops
   const int ql = lane & 31, hh = lane >> 5;
   const int qrow = wave * 32 + ql;
   const int qi = i0 + qrow;
@@ -393,9 +495,10 @@ __attribute__((amdgpu_waves_per_eu(D <= 64 ? 2 : 1))) void fwd_kernel(const FwdP
   const int r_hi = p.r_lo + p.nr - 1;
   const int ntiles = (kv_end + BC - 1) / BC;
   const int nstage = p.nstage;
+  const bool wv_ring = SHAW && HAS_WV && p.wv_mode == kWvRing;
 
   const Layout lay = make_layout<BF16, D, NW, BC>(MODE, HAS_WK, HAS_WV, p.nr, nstage, p.t5_dist,
-                                                  p.t5.nb, p.wv_resident != 0);
+                                                  p.t5.nb, p.wv_mode);
   extern __shared__ __align__(16) unsigned char smem[];
   unsigned char RELATTN_LDS* smem_lds = (unsigned char RELATTN_LDS*)smem;
   const uint32_t smem_addr = (uint32_t)(uintptr_t)smem_lds;  // LDS byte address of smem
@@ -409,33 +512,25 @@ __attribute__((amdgpu_waves_per_eu(D <= 64 ? 2 : 1))) void fwd_kernel(const FwdP
   const T* vg = reinterpret_cast<const T*>(p.v) + b * p.v_sb + h * p.v_sh;
   T* og = reinterpret_cast<T*>(p.o) + b * p.o_sb + h * p.o_sh;
 
-  // ---- Q as the B operand of S^T = K Q^T, resident for the whole kernel.
-  // Rows past n load row n-1 (never stored).
-  Op qop[NKS];
-  {
-    const T* qrow_ptr = qg + (int64_t)min(qi, p.n - 1) * p.q_sn;
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      if constexpr (BF16) {
-        qop[ks] = *reinterpret_cast<const bf16x8*>(qrow_ptr + ks * 16 + 8 * hh);
-      } else {
-        qop[ks] = qrow_ptr[ks * 2 + hh];
-      }
-    }
-  }
-
-  // ---- LDS-DMA, oldest first: relative tables, then the first K/V stages.
-  // Key rows past the key length read the last visible row (finite, masked).
+  // ---- LDS-DMA, oldest first: the Q tile, the relative tables, then the
+  // first K/V stages.  (Q goes through LDS too: the compiler cannot count the
+  // DMA instructions issued after a register load and would wait for all of
+  // them before the first use of Q.)  Query rows past n and key rows past the
+  // key length read the last valid row (finite, never stored or masked).
+  compiler_fence();
+  dma_tile<ROWB, NW>(smem_lds + lay.qs, qg, p.q_sn, i0, p.n - 1, G::BR, wave, lane);
   compiler_fence();
   const T* wkh = reinterpret_cast<const T*>(p.wk) + h * p.wk_sh;
   const T* wvh = reinterpret_cast<const T*>(p.wv) + h * p.wv_sh;
+  int n_after_q = 0;  // this wave's DMA instructions issued after the Q tile
   if constexpr (SHAW && HAS_WK) {
-    dma_tile<ROWB, NW>(smem_lds + lay.wk, wkh, p.wk_sr, p.r_lo, r_hi, lay.wk_chunk, wave, lane);
+    n_after_q += dma_tile<ROWB, NW>(smem_lds + lay.wk, wkh, p.wk_sr, p.r_lo, r_hi, lay.wk_chunk,
+                                    wave, lane);
   }
   compiler_fence();
   int n_after_wk = 0;  // this wave's DMA instructions issued after the w^K chunk
   if constexpr (SHAW && HAS_WV) {
-    if (p.wv_resident)
+    if (p.wv_mode == kWvResident)
       n_after_wk += dma_tile<ROWB, NW>(smem_lds + lay.wv, wvh, p.wv_sr, p.r_lo, r_hi,
                                        lay.wv_rows, wave, lane);
   }
@@ -451,23 +546,42 @@ __attribute__((amdgpu_waves_per_eu(D <= 64 ? 2 : 1))) void fwd_kernel(const FwdP
     }
   }
   compiler_fence();
-  auto issue_stage = [&](int tile) __attribute__((always_inline)) {
-    dma_stage<ROWB, NW, BC>(smem_lds + (tile % nstage) * G::STAGEB, kg, p.k_sn, vg, p.v_sn,
-                            tile * BC, kv_last, wave, lane);
+  uint32_t soff[LPW];  // per-lane offsets of this wave's stage loads (fast path)
+  if (p.dma32) stage_offsets<ROWB, NW, BC, T>(soff, p.k_sn, p.v_sn, wave, lane);
+  auto issue_stage = [&](int tile, int stage) __attribute__((always_inline)) {
+    if (p.dma32 && tile * BC + BC - 1 <= kv_last) {
+      dma_stage_fast<ROWB, NW, BC>(smem_lds + stage * G::STAGEB, kg + (int64_t)tile * BC * p.k_sn,
+                                   vg + (int64_t)tile * BC * p.v_sn, soff, wave);
+    } else {
+      dma_stage<ROWB, NW, BC>(smem_lds + stage * G::STAGEB, kg, p.k_sn, vg, p.v_sn, tile * BC,
+                              kv_last, wave, lane);
+    }
     compiler_fence();
   };
   const int n_pre = min(nstage - 1, ntiles);
-  for (int s = 0; s < n_pre; ++s) issue_stage(s);
+  for (int s = 0; s < n_pre; ++s) issue_stage(s, s);
   n_after_wk += n_pre * LPW;
+  n_after_q += n_after_wk;
+
+  // ---- Q as the B operand of S^T = K Q^T, in registers for the whole kernel
+  wait_vm_dyn(SHAW && HAS_WK ? n_after_wk : (T5 ? n_pre * LPW : n_after_q));
+  block_sync();  // every wave's share of the Q tile (and of the tables) landed
+  Op qop[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) {
+    if constexpr (BF16) {
+      qop[ks] = frag_row<ROWB>(smem + lay.qs, qrow, 2 * ks + hh);
+    } else {
+      qop[ks] = elem_f32<ROWB>(smem + lay.qs, qrow, 2 * ks + hh);
+    }
+  }
+  if constexpr (SHAW && (HAS_WK || HAS_WV)) block_sync();  // Q sits in the relative rows
 
   // ---- relative logits in LDS.  Shaw: row qrow holds scale*log2e*q.w^K_r for
-  // the reachable label rows r_lo..r_hi at entries PAD + (r - r_lo), padded.
+  // the reachable label rows r_lo..r_hi at entries PADL + (r - r_lo), with
+  // PADL copies of the first label below and PADU copies of the last above.
   // T5: one shared vector holds log2e*bias[beta(delta), h] for delta in
-  // [-dist, dist] at entries PAD + dist + delta, padded.
-  if constexpr (GATHER) {
-    wait_vm_dyn(T5 ? n_pre * LPW : n_after_wk);  // the tables are older than the stages
-    block_sync();
-  }
+  // [-dist, dist] at entries PADL + dist + delta, padded the same way.
   if constexpr (SHAW && HAS_WK) {
     const unsigned char* wkt = smem + lay.wk;
     const int nlb = (p.nr + 31) / 32;
@@ -496,36 +610,46 @@ __attribute__((amdgpu_waves_per_eu(D <= 64 ? 2 : 1))) void fwd_kernel(const FwdP
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int idx = lb * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
-        if (idx < p.nr) myLE[PAD + idx] = acc[i] * p.scale_log2;
+        if (idx < p.nr) myLE[PADL + idx] = acc[i] * p.scale_log2;
       }
     }
     compiler_fence();  // the row was written by both halves of this wave
-    const float edge = myLE[hh ? PAD + p.nr - 1 : PAD];
-    float* pad = myLE + (hh ? PAD + p.nr : 0);
+    // Under the causal mask no offset above 0 is visible: the upper padding
+    // holds -inf, so every logit gathered for a future key comes out masked.
+    const float edge = hh ? (p.causal ? kNegInf : myLE[PADL + p.nr - 1]) : myLE[PADL];
+    float* pad = myLE + (hh ? PADL + p.nr : 0);
+    const int npad = hh ? PADU : PADL;
 #pragma unroll
-    for (int x = 0; x < PAD; ++x) pad[x] = edge;
+    for (int x = 0; x < PADU; ++x)
+      if (x < npad) pad[x] = edge;
     compiler_fence();
   }
   if constexpr (T5) {
-    const int nb = 2 * p.t5_dist + 1 + 2 * PAD;
+    const int nb = 2 * p.t5_dist + 1 + PADL + PADU;
     for (int x = tid; x < nb; x += NT) {
-      const int delta = min(max(x - PAD - p.t5_dist, -p.t5_dist), p.t5_dist);
-      TB[x] = kLog2e * TBC[t5_bucket(delta, p.t5)];
+      const int delta = min(max(x - PADL - p.t5_dist, -p.t5_dist), p.t5_dist);
+      // as for the Shaw rows: future offsets carry the causal mask
+      TB[x] = (p.causal && x - PADL - p.t5_dist > 0) ? kNegInf
+                                                     : kLog2e * TBC[t5_bucket(delta, p.t5)];
     }
     block_sync();
   }
 
   // window of offsets delta = j - i covered by the relative row, and the
   // relative logit of its two ends (used for tiles entirely outside the band)
-  const int dlo = T5 ? -p.t5_dist : p.r_lo - c;  // delta of entry PAD
+  const int dlo = T5 ? -p.t5_dist : p.r_lo - c;  // delta of entry PADL
   const int nwin = T5 ? 2 * p.t5_dist + 1 : p.nr;
+  const int gtop = nwin + PADL + PADU - SPAN;     // highest gather base
   const float* relrow = T5 ? TB : myLE;
   float Llo = 0.f, Lhi = 0.f;
   if constexpr (GATHER) {
-    Llo = relrow[PAD];
-    Lhi = relrow[PAD + nwin - 1];
+    Llo = relrow[PADL];
+    Lhi = relrow[PADL + nwin - 1];
   }
   const int band = T5 ? p.t5_dist : c;  // |j - i| >= band: one end value for the tile
+  // offsets whose label holds a single key (1 <= r <= 2c - 1, reachable):
+  // their logits are kept for the value term
+  const int wb_lo = max(1, p.r_lo) - c, wb_hi = min(2 * c - 1, r_hi) - c;
 
   // ---- running state (per lane: one query, half of each tile's keys)
   f32x16 oacc[DVB];
@@ -533,24 +657,35 @@ __attribute__((amdgpu_waves_per_eu(D <= 64 ? 2 : 1))) void fwd_kernel(const FwdP
   for (int mb = 0; mb < DVB; ++mb) oacc[mb] = f32x16{};
   float m_run = kNegInf;
   float l_part = 0.f, thi = 0.f;
+  // transpose-read lane bases of the V tile (columns 32 mb ..)
+  uint32_t trb_lo[DVB], trb_hi[DVB];
+#pragma unroll
+  for (int mb = 0; mb < DVB; ++mb) frag_col_base<ROWB, D>(32 * mb, lane, trb_lo[mb], trb_hi[mb]);
   const int hi_from = max(c, 1 - c);    // offsets >= hi_from fall in the +c bucket
   const int hoff = BF16 ? 8 * hh : hh;  // key offset of this lane half
+  int wv_stage = -1, wv_cnt = 0;        // ring stage and DMA count of the w^V tile
 
-  for (int t = 0; t < ntiles; ++t) {
+  int st_cur = 0, st_next = nstage - 1;  // ring stages of tiles t and t + nstage - 1
+  for (int t = 0; t < ntiles; ++t, st_cur = (st_cur + 1 == nstage) ? 0 : st_cur + 1,
+           st_next = (st_next + 1 == nstage) ? 0 : st_next + 1) {
     const int j0 = t * BC;
-    // tile t landed for this wave (the next stage may still be in flight) ...
-    if (nstage > 2 && t + 1 < ntiles) {
-      wait_vm<LPW>();
-    } else {
-      wait_vm<0>();
-    }
+    // tile t landed for this wave (later stages and w^V may still be in flight) ...
+    wait_vm_dyn(min(nstage - 2, ntiles - 1 - t) * LPW + wv_cnt);
     block_sync();  // ... and for every wave; stage (t - 1) % nstage is free
-    if (t + nstage - 1 < ntiles) issue_stage(t + nstage - 1);
+    if (t + nstage - 1 < ntiles) {
+      issue_stage(t + nstage - 1, st_next);
+    } else if (wv_ring && wv_stage < 0) {
+      // no K/V tile left to prefetch: the free stage takes the w^V rows
+      wv_stage = st_next;
+      wv_cnt = dma_tile<ROWB, NW>(smem_lds + wv_stage * G::STAGEB, wvh, p.wv_sr, p.r_lo, r_hi,
+                                  lay.wv_rows, wave, lane);
+      compiler_fence();
+    }
 
     if (wq0 >= p.n) continue;                  // no live query in this wave
     if (p.causal && j0 > wq0 + 31) continue;   // tile entirely in the future
 
-    const unsigned char* Kt = smem + (t % nstage) * G::STAGEB;
+    const unsigned char* Kt = smem + st_cur * G::STAGEB;
     const unsigned char* Vt = Kt + G::TILEB;
 
     // S^T block kb: rows = keys j0 + 32kb + .., columns = this wave's queries
@@ -575,82 +710,86 @@ __attribute__((amdgpu_waves_per_eu(D <= 64 ? 2 : 1))) void fwd_kernel(const FwdP
     // Register (kb, 8g + e) holds key j0 + hoff + 32kb + 16g + KSTR*e, i.e.
     // offset delta = kofs + 32kb + 16g + KSTR*e from this lane's query.
     const int kofs = j0 + hoff - qi;
-    const bool need_mask = (j0 + BC > kv_len) || (p.causal && j0 + BC - 1 > wq0);
-    // visible iff its key offset within the lane's keys is <= lim
-    const int lim = min(kv_len - 1 - j0 - hoff, p.causal ? -kofs : 0x3fffffff);
     const int dmin = j0 - (wq0 + 31), dmax = j0 + BC - 1 - wq0;
     const bool all_lo = dmax <= -band, all_hi = dmin >= band;  // wave-uniform
     const bool off_band = (SHAW || T5) && (all_lo || all_hi);
-    // in-band logits go to their own label entry of the relative row (the
-    // value term needs them once the row max is final): each such entry is
-    // gathered only for its own key, before this write; everything else goes
-    // to the dummy entry.  In band: 1 - c <= delta <= c - 1, visible, live row.
-    const int sbase = kofs - dlo + PAD;  // entry of key offset 0
-    const int lo_ko = 1 - c - kofs;
-    const int hi_ko = q_ok ? min(c - 1 - kofs, lim) : lo_ko - 1;
-    const unsigned in_width = (unsigned)(hi_ko - lo_ko);
-    const bool any_in = hi_ko >= lo_ko;
-    const int dummy = p.nr + 2 * PAD;
+    // Per-element masking: key-length cuts, and causal cuts unless the
+    // gathered relative logits already carry them (-inf past offset 0).
+    const bool causal_cut = p.causal && j0 + BC - 1 > wq0;
+    const bool need_mask = (j0 + BC > kv_len) || (causal_cut && !(GATHER && !off_band));
+    // visible iff its key offset within the lane's keys is <= lim
+    const int lim = min(kv_len - 1 - j0 - hoff, p.causal ? -kofs : 0x3fffffff);
+
+    // logits (log2 units) of the tile, masked to -inf where invisible
     float tmax = kNegInf;
-    if (!GATHER || off_band) {
-      // no gathered term here: nothing relative, the tile's end value, or no
-      // key table (then only the value term needs the band logits)
-      const float rel = GATHER ? (all_lo ? Llo : Lhi) : 0.f;
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int ko = 32 * kb + 16 * (i >> 3) + KSTR * (i & 7);
-          float x = fmaf(s[kb][i], p.scale_log2, rel);
-          if constexpr (SHAW && HAS_WV && !HAS_WK) {
-            if (!off_band) {
-              const bool in = any_in && (unsigned)(ko - lo_ko) <= in_width;
-              myLE[in ? sbase + ko : dummy] = x;
-            }
-          }
-          if (need_mask) x = (ko <= lim) ? x : kNegInf;
-          s[kb][i] = x;
-          tmax = fmaxf(tmax, x);
-        }
-    } else {
-      // band: gather every relative logit of the tile first (8 entries per
-      // group from one clamped base, see rel_pad), then combine
-      float rv[NKB][16];
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int g = 0; g < 2; ++g) {
-          const int d0 = kofs + 32 * kb + 16 * g;  // offset of the group's first key
-          const int bidx = min(max(d0 - dlo + PAD, 0), nwin + 2 * PAD - SPAN);
-          const float* grp = relrow + bidx;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) rv[kb][8 * g + e] = grp[KSTR * e];
-        }
+    auto finish = [&](float (&rv)[NKB][16], auto mask_tag) __attribute__((always_inline)) {
+      constexpr bool MASK = decltype(mask_tag)::value;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int ko = 32 * kb + 16 * (i >> 3) + KSTR * (i & 7);
           float x = fmaf(s[kb][i], p.scale_log2, rv[kb][i]);
-          rv[kb][i] = x;  // unmasked logits of the band, for the value term
-          if (need_mask) x = (ko <= lim) ? x : kNegInf;
+          if constexpr (MASK) x = (ko <= lim) ? x : kNegInf;
           s[kb][i] = x;
           tmax = fmaxf(tmax, x);
         }
-      if constexpr (SHAW && HAS_WV) {
+    };
+    {
+      float rv[NKB][16];
+      if (!GATHER || off_band) {
+        // no gathered term: nothing relative, or the tile's end value
+        const float rel = GATHER ? (all_lo ? Llo : Lhi) : 0.f;
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int ko = 32 * kb + 16 * (i >> 3) + KSTR * (i & 7);
-            const bool in = any_in && (unsigned)(ko - lo_ko) <= in_width;
-            myLE[in ? sbase + ko : dummy] = rv[kb][i];
+          for (int i = 0; i < 16; ++i) rv[kb][i] = rel;
+      } else {
+        // band: every relative logit of the tile, 8 entries per group read
+        // from one clamped base (the row padding makes the clamp exact)
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int g = 0; g < 2; ++g) {
+            const int d0 = kofs + 32 * kb + 16 * g;  // offset of the group's first key
+            const int bidx = min(max(d0 - dlo + PADL, 0), gtop);
+            const float* grp = relrow + bidx;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) rv[kb][8 * g + e] = grp[KSTR * e];
+          }
+      }
+      if (need_mask) {
+        finish(rv, std::true_type{});
+      } else {
+        finish(rv, std::false_type{});
+      }
+    }
+    if constexpr (SHAW && HAS_WV) {
+      // The value term needs the final logit of every key whose label holds
+      // that key alone.  Each group of 8 that touches such an offset is stored
+      // whole at its own label entries (PADL + delta - dlo onwards).  A lane's
+      // offsets grow from tile to tile and all gathers of a tile precede these
+      // stores, so the entries overwritten here are never gathered again: the
+      // entries a later group reads lie above every offset stored so far, or
+      // (fully past the band) in the top SPAN entries of the upper padding,
+      // which no store reaches.
+      if (!off_band) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int g = 0; g < 2; ++g) {
+            const int d0 = kofs + 32 * kb + 16 * g;
+            if (q_ok && d0 + (SPAN - 1) >= wb_lo && d0 <= wb_hi) {
+              float* dst = myLE + (d0 - dlo + PADL);
+#pragma unroll
+              for (int e = 0; e < 8; ++e) dst[KSTR * e] = s[kb][8 * g + e];
+            }
           }
       }
     }
 
     // online softmax: one cross-lane max per tile, everything else per lane
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    tmax = halves_max(tmax);
     const bool grow = tmax > m_run + kRescaleSlack;  // -inf + slack is -inf
     if (__any(grow)) {  // wave-uniform
       const float m_next = grow ? tmax : m_run;
@@ -704,8 +843,8 @@ __attribute__((amdgpu_waves_per_eu(D <= 64 ? 2 : 1))) void fwd_kernel(const FwdP
         for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
           for (int mb = 0; mb < DVB; ++mb)
-            frag_col_issue<ROWB, D>(vt_lds, 32 * kb + 16 * t2, 32 * mb, lane, vlo[t2 * DVB + mb],
-                                    vhi[t2 * DVB + mb]);
+            frag_col_issue_blk<ROWB>(2 * kb + t2, vt_lds + trb_lo[mb], vt_lds + trb_hi[mb],
+                                     vlo[t2 * DVB + mb], vhi[t2 * DVB + mb]);
         bf16x8 pb[2];
 #pragma unroll
         for (int t2 = 0; t2 < 2; ++t2)
@@ -729,53 +868,87 @@ __attribute__((amdgpu_waves_per_eu(D <= 64 ? 2 : 1))) void fwd_kernel(const FwdP
       }
     }
   }
-  wait_vm<0>();  // the value table has landed even when no tile ran
+  if (wv_ring && wv_stage < 0) {
+    // no tile ran: any stage is free
+    wv_stage = 0;
+    dma_tile<ROWB, NW>(smem_lds, wvh, p.wv_sr, p.r_lo, r_hi, lay.wv_rows, wave, lane);
+  }
+  wait_vm<0>();  // the value table has landed
   block_sync();
 
   // ---- epilogue
-  const float l = l_part + __shfl_xor(l_part, 32);
+  const float l = halves_sum(l_part);
   const float inv_l = l > 0.f ? 1.f / l : 0.f;
   if constexpr (SHAW && HAS_WV) {
-    const float thi_all = thi + __shfl_xor(thi, 32);
+    const float thi_all = halves_sum(thi);
     const float m_fin = (m_run == kNegInf) ? 0.f : m_run;
-    // weight of an in-band label row (r_lo + idx): the single key it holds
-    auto interior_weight = [&](int idx) __attribute__((always_inline)) -> float {
-      const int r = p.r_lo + idx;
-      const int j = qi + r - c;
-      const bool ok = idx < p.nr && q_ok && r > 0 && r < 2 * c && j >= 0 && j < kv_len &&
-                      (!p.causal || j <= qi);
-      const float e = myLE[PAD + min(idx, p.nr - 1)];
-      return ok ? fast_exp2(e - m_fin) : 0.f;
-    };
-    // the -c bucket holds what the row sum leaves after the band and the +c bucket
-    float isum = 0.f;
-    for (int idx = hh; idx < p.nr; idx += 2) isum += interior_weight(idx);
-    isum += __shfl_xor(isum, 32);
-    const float tlo_all = fmaxf(l - isum - thi_all, 0.f);
-    auto bucket_weight = [&](int idx) __attribute__((always_inline)) -> float {
-      const int r = p.r_lo + idx;
-      const float w = (r == 0 ? tlo_all : 0.f) + (r == 2 * c ? thi_all : 0.f);
-      return (idx < p.nr && q_ok) ? w + interior_weight(idx) : 0.f;
+    // label indices (r - r_lo) whose key is visible and holds the label
+    // alone: r in [1, 2c-1], key j = qi + r - c in [0, kv_len), j <= qi if causal
+    int r_in_hi = min(2 * c - 1, c - qi + kv_len - 1);
+    if (p.causal) r_in_hi = min(r_in_hi, c);
+    const int i_in_lo = max(1, c - qi) - p.r_lo;
+    const int i_in_hi = q_ok ? r_in_hi - p.r_lo : i_in_lo - 1;
+    const bool any_in = i_in_hi >= i_in_lo;
+    const unsigned i_in_w = (unsigned)(i_in_hi - i_in_lo);
+    const int i_thi = 2 * c - p.r_lo;  // label +c (index past nr when unreachable)
+    // label index of this lane's e-th weight in 16-label step ls
+    auto label_of = [&](int ls, int e) __attribute__((always_inline)) {
+      return BF16 ? ls * 16 + 8 * hh + e : ls * 16 + 2 * e + hh;
     };
     const int nls = (p.nr + 15) / 16;
     const int ls_chunk = lay.wv_chunk / 16;
-    for (int ls = 0; ls < nls; ++ls) {
-      if (!p.wv_resident && ls % ls_chunk == 0) {
-        // stage the next chunk of w^V rows in the (now free) ring
-        block_sync();
-        dma_tile<ROWB, NW>(smem_lds, wvh, p.wv_sr, p.r_lo + ls * 16, r_hi, lay.wv_chunk, wave,
-                           lane);
-        wait_vm<0>();
-        block_sync();
+    int loaded = 0;  // chunk of w^V rows in LDS (chunked staging)
+    float isum = 0.f, tlo_all = 0.f;
+    // label -c, whose weight is what the row sum leaves after all others, sits
+    // in step 0: do that step last
+    for (int it = 0; it < nls; ++it) {
+      const int ls = (it + 1 < nls) ? it + 1 : 0;
+      int lsr = ls;  // step within the staged rows
+      int wv_off = lay.wv;
+      if (p.wv_mode == kWvChunked) {
+        const int ch = ls / ls_chunk;
+        if (it == 0 || ch != loaded) {
+          block_sync();
+          dma_tile<ROWB, NW>(smem_lds, wvh, p.wv_sr, p.r_lo + ch * lay.wv_chunk, r_hi,
+                             lay.wv_chunk, wave, lane);
+          wait_vm<0>();
+          block_sync();
+          loaded = ch;
+        }
+        lsr = ls - ch * ls_chunk;
+        wv_off = 0;
+      } else if (p.wv_mode == kWvRing) {
+        wv_off = wv_stage * G::STAGEB;
       }
-      const int lsr = ls % ls_chunk;  // label step within the staged chunk
-      const unsigned char* wvt = smem + lay.wv;
+      float w[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int idx = label_of(ls, e);
+        const float x = myLE[PADL + idx];  // inside the row for every step
+        const bool ok = any_in && (unsigned)(idx - i_in_lo) <= i_in_w;
+        w[e] = ok ? fast_exp2(x - m_fin) : 0.f;
+        isum += w[e];
+      }
+      if (it + 1 == nls) {
+        // every single-key weight is in isum now
+        tlo_all = fmaxf(l - halves_sum(isum) - thi_all, 0.f);
+        if (p.r_lo == 0 && hh == 0) w[0] += tlo_all;  // label index 0 is -c
+      }
+      if (!p.causal) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) w[e] += (label_of(ls, e) == i_thi) ? thi_all : 0.f;
+      }
+      if (!q_ok) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) w[e] = 0.f;
+      }
+      const unsigned char* wvt = smem + wv_off;
       if constexpr (BF16) {
         bf16x8 bw;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) bw[e] = (__bf16)bucket_weight(ls * 16 + 8 * hh + e);
+        for (int e = 0; e < 8; ++e) bw[e] = (__bf16)w[e];
         bf16x4 wlo[DVB], whi[DVB];
-        const uint32_t wv_lds = smem_addr + (uint32_t)lay.wv;
+        const uint32_t wv_lds = smem_addr + (uint32_t)wv_off;
 #pragma unroll
         for (int mb = 0; mb < DVB; ++mb)
           frag_col_issue<ROWB, D>(wv_lds, lsr * 16, 32 * mb, lane, wlo[mb], whi[mb]);
@@ -784,13 +957,11 @@ __attribute__((amdgpu_waves_per_eu(D <= 64 ? 2 : 1))) void fwd_kernel(const FwdP
         for (int mb = 0; mb < DVB; ++mb) oacc[mb] = mfma(frag_join(wlo[mb], whi[mb]), bw, oacc[mb]);
       } else {
 #pragma unroll
-        for (int s2 = 0; s2 < 8; ++s2) {
-          const int idx = ls * 16 + 2 * s2 + hh;
-          const float bw = bucket_weight(idx);
+        for (int e = 0; e < 8; ++e) {
 #pragma unroll
           for (int mb = 0; mb < DVB; ++mb) {
             const int dv = min(32 * mb + ql, D - 1);
-            oacc[mb] = mfma(elem_f32<ROWB>(wvt, lsr * 16 + 2 * s2 + hh, dv), bw, oacc[mb]);
+            oacc[mb] = mfma(elem_f32<ROWB>(wvt, lsr * 16 + 2 * e + hh, dv), w[e], oacc[mb]);
           }
         }
       }
@@ -839,37 +1010,39 @@ constexpr int kBlockKeysF32 = 32;
 
 template <bool BF16, int D, int NW, int BC>
 static size_t lds_bytes_t(RelMode mode, bool has_wk, bool has_wv, int nr, int nstage,
-                          int t5_dist, int t5_nb, bool wv_resident) {
-  return (size_t)make_layout<BF16, D, NW, BC>(mode, has_wk, has_wv, nr, nstage, t5_dist, t5_nb,
-                                              wv_resident)
-      .total;
+                          int t5_dist, int t5_nb, int wv_mode) {
+  using G = Geo<BF16, D, NW, BC>;
+  const Layout L = make_layout<BF16, D, NW, BC>(mode, has_wk, has_wv, nr, nstage, t5_dist, t5_nb,
+                                                wv_mode);
+  if (mode == kRelShaw && has_wv && wv_mode == kWvRing && L.wv_rows * G::ROWB > G::STAGEB)
+    return ~(size_t)0;  // the w^V tile does not fit one ring stage
+  return (size_t)L.total;
 }
 
 size_t lds_bytes(bool bf16, int d, const LaunchCfg& cfg, RelMode mode, bool has_wk,
                  bool has_wv, int nr, int t5_dist, int t5_nb) {
-#define RELATTN_LDS(BF, DD, NWW, BCC)                                                 \
+#define RELATTN_LDS_CASE(BF, DD, NWW, BCC)                                                 \
   if (bf16 == BF && d == DD && cfg.waves == NWW && cfg.kblock == BCC)                \
     return lds_bytes_t<BF, DD, NWW, BCC>(mode, has_wk, has_wv, nr, cfg.nstage, t5_dist, \
-                                         t5_nb, cfg.wv_resident);
+                                         t5_nb, cfg.wv_mode);
 #define RELATTN_LDS_D(BF, NWW, BCC) \
-  RELATTN_LDS(BF, 16, NWW, BCC) RELATTN_LDS(BF, 32, NWW, BCC) \
-  RELATTN_LDS(BF, 64, NWW, BCC) RELATTN_LDS(BF, 128, NWW, BCC)
+  RELATTN_LDS_CASE(BF, 16, NWW, BCC) RELATTN_LDS_CASE(BF, 32, NWW, BCC) \
+  RELATTN_LDS_CASE(BF, 64, NWW, BCC) RELATTN_LDS_CASE(BF, 128, NWW, BCC)
   RELATTN_LDS_D(true, 1, kBlockKeys)
   RELATTN_LDS_D(true, 2, kBlockKeys)
   RELATTN_LDS_D(true, 4, kBlockKeys)
   RELATTN_LDS_D(false, 1, kBlockKeysF32)
   RELATTN_LDS_D(false, 2, kBlockKeysF32)
 #undef RELATTN_LDS_D
-#undef RELATTN_LDS
-  return 0;
+#undef RELATTN_LDS_CASE
+  return ~(size_t)0;  // no such kernel
 }
 
 template <int D, int NW, int BC, bool BF16, int MODE, bool HAS_WK, bool HAS_WV>
 static int launch_t(const FwdParams& p, void* stream) {
   auto kern = fwd_kernel<D, NW, BC, BF16, MODE, HAS_WK, HAS_WV>;
   const size_t lds = lds_bytes_t<BF16, D, NW, BC>((RelMode)MODE, HAS_WK, HAS_WV, p.nr,
-                                                  p.nstage, p.t5_dist, p.t5.nb,
-                                                  p.wv_resident != 0);
+                                                  p.nstage, p.t5_dist, p.t5.nb, p.wv_mode);
   if (lds > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
