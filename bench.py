@@ -173,7 +173,7 @@ def traffic_per_launch(name):
 # CPU baseline: the fp64 oracle as it stands, on the host cores
 # ---------------------------------------------------------------------------
 
-def cpu_baseline(w, min_seconds=5.0):
+def cpu_baseline(w, min_seconds=12.0):
     import oracle
     import workloads
     from threadpoolctl import threadpool_info
