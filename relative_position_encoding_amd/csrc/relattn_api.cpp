@@ -302,7 +302,9 @@ int make_plan(const relattn_tensor* q, const relattn_tensor* k, const relattn_te
     if (n <= 32) waves = {1, 2};
     else waves = {2, 1};
   }
-  const int vgpr_waves_per_cu = d <= 64 ? 8 : 4;
+  // waves per CU the kernels' register budget allows (4 SIMDs; see the kernel)
+  const int vgpr_waves_per_cu =
+      4 * (d > 64 ? 1 : ((P.bf16 && P.mode != relattn::kRelShaw) ? 3 : 2));
   std::vector<LaunchCfg> order;
   for (int w : waves)
     for (int st : {3, 2})

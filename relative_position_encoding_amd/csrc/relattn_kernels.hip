@@ -458,11 +458,18 @@ __device__ __forceinline__ float halves_max(float x) {
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
-// Two waves per SIMD for d <= 64 (they hide each other's softmax and memory
-// latency); d = 128 needs the whole register file for one.
+// Waves per SIMD the register budget is sized for (the host plan uses the
+// same rule): d = 128 needs the whole register file for one; for d <= 64,
+// three for bf16 without the Shaw tables (168 registers; lets the T5 grid run
+// in one round) and two otherwise (the Shaw state and fp32 operands spill).
+template <int D, int MODE, bool BF16>
+__host__ __device__ constexpr int waves_per_simd() {
+  return D > 64 ? 1 : ((BF16 && MODE != kRelShaw) ? 3 : 2);
+}
 template <int D, int NW, int BC, bool BF16, int MODE, bool HAS_WK, bool HAS_WV>
 __global__ __launch_bounds__(64 * NW)
-__attribute__((amdgpu_waves_per_eu(D <= 64 ? 2 : 1))) void fwd_kernel(const FwdParams p) {
+__attribute__((amdgpu_waves_per_eu(waves_per_simd<D, MODE, BF16>()))) void fwd_kernel(
+    const FwdParams p) {
   using G = Geo<BF16, D, NW, BC>;
   using T = typename G::T;
   using Op = std::conditional_t<BF16, bf16x8, float>;
