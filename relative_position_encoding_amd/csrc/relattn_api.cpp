@@ -290,33 +290,38 @@ int make_plan(const relattn_tensor* q, const relattn_tensor* k, const relattn_te
     return relattn::lds_bytes(P.bf16, P.d, c, P.mode, P.has_wk, P.has_wv, p.nr, p.t5_dist, nb);
   };
   std::vector<int> waves;
-  int kblock;
+  std::vector<int> kblocks;
   if (P.bf16) {
-    kblock = 64;
     // four waves first: a workgroup then shares each K/V tile among 128
     // query rows (measured faster than two waves even when that leaves one
     // workgroup per compute unit, e.g. B32 H8 n128)
     waves = {4, 2, 1};
+    kblocks = {64};
+    if (d == 128) kblocks.push_back(32);  // two waves per SIMD at d = 128
   } else {
-    kblock = 32;
+    kblocks = {32};
     if (n <= 32) waves = {1, 2};
     else waves = {2, 1};
   }
-  // waves per CU the kernels' register budget allows (4 SIMDs; see the kernel)
-  const int vgpr_waves_per_cu =
-      4 * (d > 64 ? 1 : ((P.bf16 && P.mode != relattn::kRelShaw) ? 3 : 2));
+  // waves per CU the kernels' register budget allows (4 SIMDs; the same rule
+  // as the kernels')
+  auto vgpr_waves_per_cu = [&](int kblock) {
+    if (d > 64) return 4 * ((P.bf16 && kblock == 32) ? 2 : 1);
+    return 4 * ((P.bf16 && P.mode != relattn::kRelShaw) ? 3 : 2);
+  };
   std::vector<LaunchCfg> order;
-  for (int w : waves)
-    for (int st : {3, 2})
-      for (int wm : {relattn::kWvResident, relattn::kWvRing, relattn::kWvChunked})
-        order.push_back({w, kblock, st, wm});
+  for (int kb : kblocks)
+    for (int w : waves)
+      for (int st : {3, 2})
+        for (int wm : {relattn::kWvResident, relattn::kWvRing, relattn::kWvChunked})
+          order.push_back({w, kb, st, wm});
   bool found = false;
   int64_t best = -1;
   for (const auto& c : order) {
     const size_t lds = lds_of(c);
     if (lds > kMaxLdsBytes) continue;
     const int64_t wgs = B * H * ((n + 32 * c.waves - 1) / (32 * c.waves));
-    const int64_t fit = std::min<int64_t>(vgpr_waves_per_cu / c.waves,
+    const int64_t fit = std::min<int64_t>(vgpr_waves_per_cu(c.kblock) / c.waves,
                                           lds ? (int64_t)(kMaxLdsBytes / lds) : 64);
     const int64_t need = (wgs + kNumCUs - 1) / kNumCUs;  // workgroups per CU in one round
     const int64_t resident = std::min(fit, need) * c.waves;

@@ -280,7 +280,6 @@ struct Geo {
   static constexpr int PADL = SPAN - 1;
   static constexpr int PADU = 2 * SPAN - 1;
   static_assert(STAGEB % (1024 * NW) == 0, "stage must split into whole 1 KB instructions");
-  static_assert(BR * ROWB <= STAGEB, "the Q tile must fit one ring stage");
   static_assert(BR * ROWB % 1024 == 0, "the Q tile must split into whole 1 KB instructions");
 };
 
@@ -333,14 +332,15 @@ __host__ __device__ inline Layout make_layout(int mode, bool has_wk, bool has_wv
   }
   // The Q tile of the workgroup arrives by LDS-DMA and is read into registers
   // in the prologue: it borrows the relative rows (written only afterwards),
-  // or else the last ring stage, which the loop fills first.
+  // or else the last ring stage, which the loop fills first, or else (too
+  // big for a stage) a region of its own.
   const int q_bytes = G::BR * G::ROWB;
   if (shaw && (has_wk || has_wv)) {
     L.le = take(max(G::BR * L.lrs * 4, q_bytes));
     L.qs = L.le;
   } else {
     L.le = off;
-    L.qs = (nstage - 1) * G::STAGEB;
+    L.qs = q_bytes <= G::STAGEB ? (nstage - 1) * G::STAGEB : take(q_bytes);
   }
   L.tbc = t5 ? take(((t5_nb + 63) & ~63) * 4) : off;
   L.tb = t5 ? take((2 * t5_dist + 1 + G::PADL + G::PADU) * 4) : off;
@@ -459,16 +459,17 @@ __device__ __forceinline__ float halves_max(float x) {
 }
 
 // Waves per SIMD the register budget is sized for (the host plan uses the
-// same rule): d = 128 needs the whole register file for one; for d <= 64,
-// three for bf16 without the Shaw tables (168 registers; lets the T5 grid run
-// in one round) and two otherwise (the Shaw state and fp32 operands spill).
-template <int D, int MODE, bool BF16>
+// same rule): d = 128 with 64-key tiles needs the whole register file for one,
+// with 32-key tiles (bf16) two fit; for d <= 64, three for bf16 without the
+// Shaw tables (168 registers; lets the T5 grid run in one round) and two
+// otherwise (the Shaw state and fp32 operands spill).
+template <int D, int MODE, bool BF16, int BC>
 __host__ __device__ constexpr int waves_per_simd() {
-  return D > 64 ? 1 : ((BF16 && MODE != kRelShaw) ? 3 : 2);
+  return D > 64 ? ((BF16 && BC == 32) ? 2 : 1) : ((BF16 && MODE != kRelShaw) ? 3 : 2);
 }
 template <int D, int NW, int BC, bool BF16, int MODE, bool HAS_WK, bool HAS_WV>
 __global__ __launch_bounds__(64 * NW)
-__attribute__((amdgpu_waves_per_eu(waves_per_simd<D, MODE, BF16>()))) void fwd_kernel(
+__attribute__((amdgpu_waves_per_eu(waves_per_simd<D, MODE, BF16, BC>()))) void fwd_kernel(
     const FwdParams p) {
   using G = Geo<BF16, D, NW, BC>;
   using T = typename G::T;
@@ -1013,6 +1014,7 @@ __global__ void debug_indices_kernel(int n, int clip, T5Buckets t5, int use_t5,
 // ---------------------------------------------------------------------------
 
 constexpr int kBlockKeys = 64;  // keys per tile, bf16
+constexpr int kBlockKeysD128 = 32;  // bf16 d = 128 with two waves per SIMD
 constexpr int kBlockKeysF32 = 32;
 
 template <bool BF16, int D, int NW, int BC>
@@ -1038,6 +1040,14 @@ size_t lds_bytes(bool bf16, int d, const LaunchCfg& cfg, RelMode mode, bool has_
   RELATTN_LDS_D(true, 1, kBlockKeys)
   RELATTN_LDS_D(true, 2, kBlockKeys)
   RELATTN_LDS_D(true, 4, kBlockKeys)
+  if (bf16 && d == 128 && cfg.kblock == kBlockKeysD128) {
+    if (cfg.waves == 2)
+      return lds_bytes_t<true, 128, 2, kBlockKeysD128>(mode, has_wk, has_wv, nr, cfg.nstage,
+                                                       t5_dist, t5_nb, cfg.wv_mode);
+    if (cfg.waves == 4)
+      return lds_bytes_t<true, 128, 4, kBlockKeysD128>(mode, has_wk, has_wv, nr, cfg.nstage,
+                                                       t5_dist, t5_nb, cfg.wv_mode);
+  }
   RELATTN_LDS_D(false, 1, kBlockKeysF32)
   RELATTN_LDS_D(false, 2, kBlockKeysF32)
 #undef RELATTN_LDS_D
@@ -1089,6 +1099,13 @@ static int launch_d(int d, RelMode mode, bool has_wk, bool has_wv, const FwdPara
 int launch_fwd(bool bf16, int d, const LaunchCfg& cfg, RelMode mode, bool has_wk,
                bool has_wv, const FwdParams& p, void* stream) {
   if (bf16) {
+    if (cfg.kblock == kBlockKeysD128 && d == 128) {
+      if (cfg.waves == 2)
+        return launch_mode<128, 2, kBlockKeysD128, true>(mode, has_wk, has_wv, p, stream);
+      if (cfg.waves == 4)
+        return launch_mode<128, 4, kBlockKeysD128, true>(mode, has_wk, has_wv, p, stream);
+      return (int)hipErrorInvalidValue;
+    }
     if (cfg.kblock != kBlockKeys) return (int)hipErrorInvalidValue;
     if (cfg.waves == 1) return launch_d<1, kBlockKeys, true>(d, mode, has_wk, has_wv, p, stream);
     if (cfg.waves == 2) return launch_d<2, kBlockKeys, true>(d, mode, has_wk, has_wv, p, stream);
