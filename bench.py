@@ -99,15 +99,24 @@ def _prepare(ra, w, copies, stream_ptr):
     return x, calls, keep
 
 
-def time_gpu(ra, w, steps, warmup):
+def time_gpu(ra, w, steps, warmup, hot=False, reps=1):
+    """Time ``steps`` back-to-back calls on one stream, ``reps`` times.
+
+    Cold (default): the calls cycle through enough input copies to exceed twice
+    the last-level cache, so operands come from HBM.  Hot: one set of inputs
+    for every call, so they stay cache-resident.  ms_per_step is the median
+    over the repetitions (the single timed region when reps == 1).
+    """
+    import statistics
     import torch
     lib = ra._load()
     stream = torch.cuda.Stream()  # default priority
     flops, nbytes, dense = work(w, None)
-    copies = max(1, min(16, int(2 * LLC_BYTES // max(nbytes, 1)) + 1))
+    copies = 1 if hot else max(1, min(16, int(2 * LLC_BYTES // max(nbytes, 1)) + 1))
     x, calls, keep = _prepare(ra, w, copies, stream.cuda_stream)
     flops, nbytes, dense = work(w, x["key_lens"])
     fwd = lib.relattn_fwd
+    times = []
     with torch.cuda.stream(stream):
         for s in range(warmup):
             st = fwd(*calls[s % copies])
@@ -116,14 +125,16 @@ def time_gpu(ra, w, steps, warmup):
         torch.cuda.synchronize()
         t0 = torch.cuda.Event(enable_timing=True)
         t1 = torch.cuda.Event(enable_timing=True)
-        wall0 = time.perf_counter()
-        t0.record(stream)
-        for s in range(steps):
-            fwd(*calls[s % copies])
-        t1.record(stream)
-        wall_submit = time.perf_counter() - wall0
-        torch.cuda.synchronize()
-    ms = t0.elapsed_time(t1) / steps
+        for r in range(reps):
+            wall0 = time.perf_counter()
+            t0.record(stream)
+            for s in range(steps):
+                fwd(*calls[s % copies])
+            t1.record(stream)
+            wall_submit = time.perf_counter() - wall0
+            torch.cuda.synchronize()
+            times.append(t0.elapsed_time(t1) / steps)
+    ms = statistics.median(times)
     del keep
     sec = ms * 1e-3
     dt = "bf16" if w.dtype.itemsize == 2 else "f32"
@@ -138,8 +149,15 @@ def time_gpu(ra, w, steps, warmup):
         "input_copies": copies,
         "host_submit_us_per_step": wall_submit / steps * 1e6,
         "dtype": dt,
+        "roofline_frac": flops / sec / 1e12 / ceiling_tflops(flops, nbytes, dt),
+        "ms_reps": times,
     }
     return res
+
+
+def ceiling_tflops(flops, nbytes, dt):
+    """Roofline ceiling min(MFMA peak, arithmetic intensity x HBM peak), TFLOP/s."""
+    return min(PEAK_TFLOPS[dt], flops / nbytes * PEAK_HBM_GBS / 1e3)
 
 
 def bound_of(flops, nbytes, dt):
@@ -199,6 +217,105 @@ def cpu_baseline(w, min_seconds=12.0):
                       f"cores visible"}
 
 
+def oracle_report(per_workload_s=2.0):
+    """Wall time of the fp64 oracle per workload on the host cores.
+
+    Factored oracle (Eq. 5 form; T5: its definition) on whole workloads where a
+    call is short, else on a few (b, h) heads, scaled to the whole workload;
+    brute force (materialised n x n x d edge tensors) on the tiny and base
+    workloads; row-sampled brute force elsewhere, as time per output row.
+    """
+    import numpy as np
+    import oracle
+    import workloads
+    rng = np.random.default_rng(0)
+    rep = {}
+    for name in ["tiny", "base", "big_causal_k", "big_causal_kv", "long", "t5"]:
+        w = workloads.WORKLOADS[name]
+        x = workloads.make_inputs(w)
+        B, H = w.batch, w.heads
+        lens = x["key_lens"]
+        kw = dict(causal=w.causal)
+
+        def head_slice(bs, hs):
+            y = {k: x[k] for k in ("q", "k", "v")}
+            y = {k: t[bs, hs] for k, t in y.items()}
+            kl = None if lens is None else lens[bs]
+            return y, kl
+
+        def factored(bs, hs):
+            y, kl = head_slice(bs, hs)
+            if w.t5 is None:
+                kt = None if x["key_table"] is None else x["key_table"][hs]
+                vt = None if x["value_table"] is None else x["value_table"][hs]
+                oracle.relattn_factored(y["q"], y["k"], y["v"], kt, vt, w.clip,
+                                        key_lens=kl, **kw)
+            else:
+                oracle.t5_attention(y["q"], y["k"], y["v"], x["t5_bias"][:, hs],
+                                    key_lens=kl, **kw, **w.t5)
+
+        # factored: grow the sample of heads until it takes about per_workload_s
+        nb, nh, el = 1, 1, 0.0
+        while True:
+            t0 = time.perf_counter()
+            factored(slice(0, nb), slice(0, nh))
+            el = time.perf_counter() - t0
+            if el >= per_workload_s / 4 or (nb == B and nh == H):
+                break
+            if nh < H:
+                nh = min(H, nh * 2)
+            else:
+                nb = min(B, nb * 2)
+        entry = {"factored_s_per_call": el * (B * H) / (nb * nh),
+                 "factored_sample_heads": nb * nh}
+        if name in ("tiny", "base"):
+            t0 = time.perf_counter()
+            oracle.relattn_bruteforce(x["q"], x["k"], x["v"], x["key_table"],
+                                      x["value_table"], w.clip, key_lens=lens, **kw)
+            entry["bruteforce_s_per_call"] = time.perf_counter() - t0
+        else:
+            nrows = 16
+            rows = [(int(rng.integers(B)), int(rng.integers(H)), int(rng.integers(w.n)))
+                    for _ in range(nrows)]
+            t0 = time.perf_counter()
+            if w.t5 is None:
+                oracle.relattn_rows(x["q"], x["k"], x["v"], x["key_table"], x["value_table"],
+                                    w.clip, key_lens=lens, rows=rows, **kw)
+            else:
+                oracle.t5_rows(x["q"], x["k"], x["v"], x["t5_bias"], key_lens=lens,
+                               rows=rows, **kw, **w.t5)
+            entry["bruteforce_s_per_row"] = (time.perf_counter() - t0) / nrows
+            entry["bruteforce_rows"] = nrows
+        rep[name] = {k: (round(v, 6) if isinstance(v, float) else v) for k, v in entry.items()}
+    return rep
+
+
+def gpu_identity():
+    """Marketing name, ISA and peak engine clock of the first GPU agent (rocminfo)."""
+    import subprocess
+    try:
+        txt = subprocess.run(["rocminfo"], capture_output=True, text=True, timeout=60).stdout
+    except (OSError, subprocess.SubprocessError):
+        return None
+    for agent in txt.split("Agent ")[1:]:
+        if "Device Type:             GPU" not in agent:
+            continue
+        info = {}
+        for line in agent.splitlines():
+            key, _, val = line.strip().partition(":")
+            val = val.strip()
+            if key == "Marketing Name" and "name" not in info:
+                info["name"] = val
+            elif key == "Name" and val.startswith("gfx") and "isa" not in info:
+                info["isa"] = val
+            elif key == "Max Clock Freq. (MHz)" and "max_clock_mhz" not in info:
+                info["max_clock_mhz"] = int(val.split()[0])
+            elif key == "Compute Unit" and "compute_units" not in info:
+                info["compute_units"] = int(val.split()[0])
+        return info
+    return None
+
+
 def copy_calibration(mib=512, reps=5):
     """A plain device copy of known size, for scaling the HBM byte counters."""
     import torch
@@ -216,7 +333,8 @@ def main():
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default=HEADLINE)
-    ap.add_argument("--only", action="store_true", help="time the headline workload only")
+    ap.add_argument("--only", action="store_true",
+                    help="time the headline workload only (no per-workload table, no oracle report)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     a = ap.parse_args()
@@ -226,6 +344,7 @@ def main():
               f"(asked for --gpus {a.gpus}, WORLD_SIZE {world})", file=sys.stderr)
         sys.exit(2)
 
+    gpu = None if a.copy_calibration else gpu_identity()  # before this process uses the GPU
     import torch
     import relative_position_encoding_amd as ra
     import workloads
@@ -236,6 +355,8 @@ def main():
         copy_calibration()
         return
 
+    if gpu is not None and not gpu.get("name"):
+        gpu["name"] = torch.cuda.get_device_name(0)
     w = workloads.WORKLOADS[a.workload]
     head = time_gpu(ra, w, a.steps, a.warmup)
     flops = head["alg_gflop"] * 1e9
@@ -269,19 +390,31 @@ def main():
         "alg_gflop_per_step": round(head["alg_gflop"], 4),
         "alg_mbytes_per_step": round(head["alg_mbytes"], 3),
         "host_submit_us_per_step": round(head["host_submit_us_per_step"], 2),
+        "gpu": gpu,
     }
     if not a.only:
-        others = {}
-        for name in OTHER:
-            if name == w.name:
-                continue
-            r = time_gpu(ra, workloads.WORKLOADS[name], max(50, a.steps // 5), 10)
-            others[name] = {k: round(r[k], 4) for k in
-                            ("ms_per_step", "tflops", "mfma_peak_frac", "hbm_gbs",
-                             "dense_equiv_tflops")}
-        line["workloads"] = others
+        # every workload, the headline included: median of 5 timed regions with
+        # inputs streamed from HBM (cold) and with one cache-resident input set (hot)
+        per = {}
+        for name in [w.name] + [x for x in OTHER if x != w.name]:
+            wl = workloads.WORKLOADS[name]
+            k = max(50, a.steps // 5)
+            cold = time_gpu(ra, wl, k, 10, reps=5)
+            hot = time_gpu(ra, wl, k, 10, hot=True, reps=5)
+            e = {key: round(cold[key], 4) for key in
+                 ("ms_per_step", "tflops", "mfma_peak_frac", "hbm_gbs", "dense_equiv_tflops",
+                  "roofline_frac")}
+            e["bound"] = bound_of(cold["alg_gflop"] * 1e9, cold["alg_mbytes"] * 1e6,
+                                  cold["dtype"])
+            e["hot_ms_per_step"] = round(hot["ms_per_step"], 5)
+            e["hot_tflops"] = round(hot["tflops"], 4)
+            e["steps_per_rep"] = k
+            per[name] = e
+        line["workloads"] = per
     if not a.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w)
+        if not a.only:
+            line["oracle_timing"] = oracle_report()
     print(json.dumps(line))
 
 
