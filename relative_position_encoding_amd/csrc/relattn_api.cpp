@@ -305,9 +305,9 @@ int make_plan(const relattn_tensor* q, const relattn_tensor* k, const relattn_te
   }
   // waves per CU the kernels' register budget allows (4 SIMDs; the same rule
   // as the kernels')
-  auto vgpr_waves_per_cu = [&](int kblock) {
+  auto vgpr_waves_per_cu = [&](int kblock, int waves) {
     if (d > 64) return 4 * ((P.bf16 && kblock == 32) ? 2 : 1);
-    return 4 * ((P.bf16 && P.mode != relattn::kRelShaw) ? 3 : 2);
+    return 4 * ((P.bf16 && P.mode != relattn::kRelShaw && (d <= 32 || waves == 4)) ? 3 : 2);
   };
   std::vector<LaunchCfg> order;
   for (int kb : kblocks)
@@ -321,7 +321,7 @@ int make_plan(const relattn_tensor* q, const relattn_tensor* k, const relattn_te
     const size_t lds = lds_of(c);
     if (lds > kMaxLdsBytes) continue;
     const int64_t wgs = B * H * ((n + 32 * c.waves - 1) / (32 * c.waves));
-    const int64_t fit = std::min<int64_t>(vgpr_waves_per_cu(c.kblock) / c.waves,
+    const int64_t fit = std::min<int64_t>(vgpr_waves_per_cu(c.kblock, c.waves) / c.waves,
                                           lds ? (int64_t)(kMaxLdsBytes / lds) : 64);
     const int64_t need = (wgs + kNumCUs - 1) / kNumCUs;  // workgroups per CU in one round
     const int64_t resident = std::min(fit, need) * c.waves;

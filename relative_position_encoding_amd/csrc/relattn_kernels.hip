@@ -197,6 +197,11 @@ __device__ __forceinline__ void dma_stage(unsigned char RELATTN_LDS* st, const T
   constexpr int NI_TILE = BC * ROWB / 1024;
   constexpr int NI = 2 * NI_TILE;
   static_assert(NI % NW == 0, "stage must split evenly over the waves");
+  // The lane index passes through an opaque register move so that the address
+  // arithmetic below stays at the (rare) call site: hoisted out of the tile
+  // loop it would hold eight 64-bit addresses live across the loop, which
+  // spills to scratch under tight register budgets.
+  asm volatile("" : "+v"(lane));
 #pragma unroll
   for (int u = 0; u < NI / NW; ++u) {
     const int I = wave + u * NW;     // instruction within the stage
@@ -461,15 +466,17 @@ __device__ __forceinline__ float halves_max(float x) {
 // Waves per SIMD the register budget is sized for (the host plan uses the
 // same rule): d = 128 with 64-key tiles needs the whole register file for one,
 // with 32-key tiles (bf16) two fit; for d <= 64, three for bf16 without the
-// Shaw tables (168 registers; lets the T5 grid run in one round) and two
-// otherwise (the Shaw state and fp32 operands spill).
-template <int D, int MODE, bool BF16, int BC>
+// Shaw tables (168 registers; lets the T5 grid run in one round) when that
+// compiles without spilling (d <= 32, or four-wave workgroups, whose
+// per-wave share of the stage loads is smallest), and two otherwise.
+template <int D, int NW, int MODE, bool BF16, int BC>
 __host__ __device__ constexpr int waves_per_simd() {
-  return D > 64 ? ((BF16 && BC == 32) ? 2 : 1) : ((BF16 && MODE != kRelShaw) ? 3 : 2);
+  return D > 64 ? ((BF16 && BC == 32) ? 2 : 1)
+                : ((BF16 && MODE != kRelShaw && (D <= 32 || NW == 4)) ? 3 : 2);
 }
 template <int D, int NW, int BC, bool BF16, int MODE, bool HAS_WK, bool HAS_WV>
 __global__ __launch_bounds__(64 * NW)
-__attribute__((amdgpu_waves_per_eu(waves_per_simd<D, MODE, BF16, BC>()))) void fwd_kernel(
+__attribute__((amdgpu_waves_per_eu(waves_per_simd<D, NW, MODE, BF16, BC>()))) void fwd_kernel(
     const FwdParams p) {
   using G = Geo<BF16, D, NW, BC>;
   using T = typename G::T;
