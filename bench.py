@@ -406,6 +406,8 @@ def main():
                   "roofline_frac")}
             e["bound"] = bound_of(cold["alg_gflop"] * 1e9, cold["alg_mbytes"] * 1e6,
                                   cold["dtype"])
+            tr = traffic_per_launch(name)
+            e["traffic"] = None if tr is None else round(tr)
             e["hot_ms_per_step"] = round(hot["ms_per_step"], 5)
             e["hot_tflops"] = round(hot["tflops"], 4)
             e["steps_per_rep"] = k
