@@ -600,6 +600,7 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<D, NW, MODE, BF16, BC>()))) vo
   if constexpr (SHAW && HAS_WK) {
     const unsigned char* wkt = smem + lay.wk;
     const int nlb = (p.nr + 31) / 32;
+    float edge_lo = 0.f;
     const int lb_chunk = lay.wk_chunk / 32;
     for (int lb = 0; lb < nlb; ++lb) {
       if (lb > 0 && lb % lb_chunk == 0) {
@@ -611,27 +612,37 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<D, NW, MODE, BF16, BC>()))) vo
         block_sync();
       }
       const int row = (lb % lb_chunk) * 32 + ql;  // MFMA row m = ql <-> label r_lo + lb*32 + ql
-      f32x16 acc = {};
+      Op a[NKS];
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
-        Op a;
         if constexpr (BF16) {
-          a = frag_row<ROWB>(wkt, row, 2 * ks + hh);
+          a[ks] = frag_row<ROWB>(wkt, row, 2 * ks + hh);
         } else {
-          a = elem_f32<ROWB>(wkt, row, 2 * ks + hh);
+          a[ks] = elem_f32<ROWB>(wkt, row, 2 * ks + hh);
         }
-        acc = mfma(a, qop[ks], acc);
       }
+      f32x16 acc = {};
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int idx = lb * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
-        if (idx < p.nr) myLE[PADL + idx] = acc[i] * p.scale_log2;
+      for (int ks = 0; ks < NKS; ++ks) acc = mfma(a[ks], qop[ks], acc);
+      if (PADL + nlb * 32 <= lay.lrs) {
+        // the whole 32-label block fits the row: entries past the last label
+        // land in the padding, which is written below
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          myLE[PADL + lb * 32 + 8 * (i >> 2) + 4 * hh + (i & 3)] = acc[i] * p.scale_log2;
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int idx = lb * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
+          if (idx < p.nr) myLE[PADL + idx] = acc[i] * p.scale_log2;
+        }
       }
+      if (lb == 0) edge_lo = acc[0] * p.scale_log2;  // label 0 of this lane's query (hh = 0)
     }
     compiler_fence();  // the row was written by both halves of this wave
     // Under the causal mask no offset above 0 is visible: the upper padding
     // holds -inf, so every logit gathered for a future key comes out masked.
-    const float edge = hh ? (p.causal ? kNegInf : myLE[PADL + p.nr - 1]) : myLE[PADL];
+    const float edge = hh ? (p.causal ? kNegInf : myLE[PADL + p.nr - 1]) : edge_lo;
     float* pad = myLE + (hh ? PADL + p.nr : 0);
     const int npad = hh ? PADU : PADL;
 #pragma unroll
@@ -685,7 +696,14 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<D, NW, MODE, BF16, BC>()))) vo
            st_next = (st_next + 1 == nstage) ? 0 : st_next + 1) {
     const int j0 = t * BC;
     // tile t landed for this wave (later stages and w^V may still be in flight) ...
-    wait_vm_dyn(min(nstage - 2, ntiles - 1 - t) * LPW + wv_cnt);
+    {
+      // the steady state (one stage still in flight) and the drained state
+      // take one compare each instead of the general switch's branch tree
+      const int pending = min(nstage - 2, ntiles - 1 - t) * LPW + wv_cnt;
+      if (pending == LPW) wait_vm<LPW>();
+      else if (pending == 0) wait_vm<0>();
+      else wait_vm_dyn(pending);
+    }
     block_sync();  // ... and for every wave; stage (t - 1) % nstage is free
     if (t + nstage - 1 < ntiles) {
       issue_stage(t + nstage - 1, st_next);
