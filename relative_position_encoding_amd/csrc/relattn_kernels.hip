@@ -54,6 +54,7 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
 #define RELATTN_LDS __attribute__((address_space(3)))
 #define RELATTN_GLOBAL __attribute__((address_space(1)))
+#define RELATTN_CONST __attribute__((address_space(4)))
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegInf = -__builtin_inff();
@@ -443,7 +444,9 @@ __device__ __forceinline__ void frag_col_wait(bf16x4 (&lo)[N], bf16x4 (&hi)[N]) 
 
 // Workgroup id -> logical tile id.  Workgroups are dealt to the 8 XCDs round
 // robin; this makes consecutive logical ids (tiles of the same batch and head,
-// which share K and V) run on the same XCD and hence share its L2.
+// which share K and V) run on the same XCD and hence share its L2.  (Causal
+// grids whose heads divide evenly over the XCDs use the heaviest-first dealing
+// in the kernel instead.)
 __device__ __forceinline__ int xcd_remap(int bid, int G) {
   const int per = G / 8, rem = G % 8, xcd = bid % 8, loc = bid / 8;
   return (xcd < rem) ? xcd * (per + 1) + loc
@@ -488,11 +491,28 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<D, NW, MODE, BF16, BC>()))) vo
   constexpr bool T5 = (MODE == kRelT5);
   constexpr bool GATHER = (SHAW && HAS_WK) || T5;  // a gathered relative logit
 
+  // One field of each 64-byte line of the parameter block (and the grid size),
+  // so that all of them are requested together behind one wait instead of
+  // one scalar-cache miss after another as the prologue first needs them.
+  asm volatile("" ::"s"(p.q), "s"(p.q_sb), "s"(p.v_sn), "s"(p.tb_sb), "s"(p.dma32), "s"(gridDim.x));
   // ---- which tile
-  const int lid = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = lid / p.n_qtiles;
-  int qt = lid - bh * p.n_qtiles;
-  if (p.causal) qt = p.n_qtiles - 1 - qt;  // longest causal rows first
+  int bh, qt;
+  if (p.causal && (gridDim.x & 7) == 0 && (gridDim.x >> 3) % p.n_qtiles == 0) {
+    // Causal tiles differ in work.  Each XCD holds whole heads; it is dealt the
+    // heaviest tile of each of its heads first, then the next heaviest, and so
+    // on, so that the workgroups that share a CU in one round differ in work
+    // and later rounds start with the longest remaining tiles.
+    const int x = blockIdx.x & 7, loc = blockIdx.x >> 3;
+    const int hpx = (gridDim.x >> 3) / p.n_qtiles;  // heads per XCD
+    const int rank = loc / hpx;
+    bh = x * hpx + (loc - rank * hpx);
+    qt = p.n_qtiles - 1 - rank;
+  } else {
+    const int lid = xcd_remap(blockIdx.x, gridDim.x);
+    bh = lid / p.n_qtiles;
+    qt = lid - bh * p.n_qtiles;
+    if (p.causal) qt = p.n_qtiles - 1 - qt;  // longest causal rows first
+  }
   const int b = bh / p.H, h = bh - b * p.H;
   const int i0 = qt * (32 * NW);
   const int tid = threadIdx.x, lane = tid & 63;
@@ -502,13 +522,8 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<D, NW, MODE, BF16, BC>()))) vo
   const int qi = i0 + qrow;
   const bool q_ok = qi < p.n;
   const int wq0 = i0 + wave * 32;
-  int kv_len = p.n;
-  if (p.key_lens) kv_len = min(max(p.key_lens[b], 0), p.n);
-  const int kv_end = p.causal ? min(kv_len, i0 + 32 * NW) : kv_len;
-  const int kv_last = max(kv_len - 1, 0);
   const int c = p.clip;
   const int r_hi = p.r_lo + p.nr - 1;
-  const int ntiles = (kv_end + BC - 1) / BC;
   const int nstage = p.nstage;
   const bool wv_ring = SHAW && HAS_WV && p.wv_mode == kWvRing;
 
@@ -561,6 +576,21 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<D, NW, MODE, BF16, BC>()))) vo
     }
   }
   compiler_fence();
+  // Key range of this workgroup.  The key length is read only now, after the
+  // Q and table requests have left, as a scalar load through the constant
+  // address space: a vector load would be counted with the DMA loads, and any
+  // earlier scalar load would be waited for together with the kernel arguments
+  // that the first requests need.  The opaque move keeps the compiler from
+  // hoisting the load.
+  int kv_len = p.n;
+  if (p.key_lens) {
+    const int32_t* klp = p.key_lens + b;
+    asm volatile("" : "+s"(klp));
+    kv_len = min(max(*(const RELATTN_CONST int32_t*)klp, 0), p.n);
+  }
+  const int kv_end = p.causal ? min(kv_len, i0 + 32 * NW) : kv_len;
+  const int kv_last = max(kv_len - 1, 0);
+  const int ntiles = (kv_end + BC - 1) / BC;
   uint32_t soff[LPW];  // per-lane offsets of this wave's stage loads (fast path)
   if (p.dma32) stage_offsets<ROWB, NW, BC, T>(soff, p.k_sn, p.v_sn, wave, lane);
   auto issue_stage = [&](int tile, int stage) __attribute__((always_inline)) {
