@@ -54,6 +54,8 @@ __all__ = [
     "relattn_rows",
     "t5_attention",
     "t5_rows",
+    "relattn_decode",
+    "t5_decode",
     "to_f64",
 ]
 
@@ -353,3 +355,75 @@ def t5_rows(q, k, v, bias, num_buckets: int = 32, max_distance: int = 128,
         w = np.exp(e[ok] - e[ok].max())
         out[t] = (w / w.sum()) @ v[b, h][ok]
     return out
+
+
+# ---------------------------------------------------------------------------
+# Incremental decoding over a key/value cache
+# ---------------------------------------------------------------------------
+
+def _decode_positions(Tq, L, cache_lens, B):
+    """Position of query t of batch b: len_b - Tq + t, with len_b clamped to [0, L]."""
+    lens = [L] * B if cache_lens is None else [min(max(int(x), 0), L) for x in cache_lens]
+    return [[lens[b] - Tq + t for t in range(Tq)] for b in range(B)]
+
+
+def relattn_decode(q, k, v, aK=None, aV=None, clip_k: int = 0, scale=None, cache_lens=None):
+    """The newest Tq positions of each sequence attending over its cache.
+
+    q: [B, H, Tq, d]; k, v: [B, H, L, d] (the cache); aK, aV: [Ht, 2k+1, d] or
+    None; cache_lens: [B] valid cache rows per batch (None = L), the new
+    positions included.  Query t of batch b sits at position i = len_b - Tq + t
+    and sees the keys j <= i (the causal mask of a decoder).  Each output row
+    is Eq. 3 with the logits of Eq. 4 (paper-summary page, section 3.4, with
+    r = clip(j - i, k)), computed here key by key; a query with no visible key
+    (i < 0) outputs zeros.
+    """
+    q, k, v = to_f64(q), to_f64(k), to_f64(v)
+    aK, aV = to_f64(aK), to_f64(aV)
+    B, H, Tq, d = q.shape
+    L = k.shape[2]
+    s = _default_scale(d, scale)
+    pos = _decode_positions(Tq, L, cache_lens, B)
+    z = np.zeros((B, H, Tq, v.shape[-1]))
+    for b in range(B):
+        for h in range(H):
+            tk, tv = _table_for_head(aK, h), _table_for_head(aV, h)
+            for t in range(Tq):
+                i = pos[b][t]
+                if i < 0:
+                    continue
+                e = np.empty(i + 1)
+                vals = np.empty((i + 1, v.shape[-1]))
+                for j in range(i + 1):
+                    r = clip(j - i, clip_k) + clip_k
+                    key = k[b, h, j] + (tk[r] if tk is not None else 0.0)
+                    e[j] = s * float(q[b, h, t] @ key)
+                    vals[j] = v[b, h, j] + (tv[r] if tv is not None else 0.0)
+                w = np.exp(e - e.max())
+                z[b, h, t] = (w / w.sum()) @ vals
+    return z
+
+
+def t5_decode(q, k, v, bias, num_buckets: int = 32, max_distance: int = 128,
+              bidirectional: bool = True, scale=None, cache_lens=None):
+    """T5 bias (survey page, section "T5") for the newest Tq positions over a
+    cache; positions and visibility as in ``relattn_decode``."""
+    q, k, v = to_f64(q), to_f64(k), to_f64(v)
+    bias = to_f64(bias)
+    B, H, Tq, d = q.shape
+    L = k.shape[2]
+    s = 1.0 if (scale is None or scale <= 0) else float(scale)
+    pos = _decode_positions(Tq, L, cache_lens, B)
+    z = np.zeros((B, H, Tq, v.shape[-1]))
+    for b in range(B):
+        for h in range(H):
+            for t in range(Tq):
+                i = pos[b][t]
+                if i < 0:
+                    continue
+                e = np.array([s * float(q[b, h, t] @ k[b, h, j]) +
+                              bias[t5_bucket(j - i, num_buckets, max_distance, bidirectional), h]
+                              for j in range(i + 1)])
+                w = np.exp(e - e.max())
+                z[b, h, t] = (w / w.sum()) @ v[b, h, :i + 1]
+    return z

@@ -414,3 +414,90 @@ def test_planted_dropped_value_term_is_caught(monkeypatch):
     monkeypatch.setattr(oracle, "relattn_bruteforce", wrong)
     with pytest.raises(AssertionError):
         test_k0_closed_form()
+
+
+# ---------------------------------------------------------------------------
+# incremental decoding: each new position's row is the causal forward's row at
+# that position (paper-summary page §3.4, Eq. 3 and Eq. 4; the causal reading
+# of the mask); the decode oracle is pinned to the forward oracle's rows and to
+# closed forms
+# ---------------------------------------------------------------------------
+
+def _decode_case(seed, B=3, H=2, L=23, d=8, Tq=2):
+    q_full = rnd((B, H, L, d), seed)
+    k, v = rnd((B, H, L, d), seed + 1), rnd((B, H, L, d), seed + 2)
+    lens = [L, 11, 1][:B]
+    return q_full, k, v, lens, Tq
+
+
+@pytest.mark.parametrize("c", [0, 3, 30])
+@pytest.mark.parametrize("tables", ["kv", "k", "v", "none", "shared"])
+def test_decode_matches_forward_rows(c, tables):
+    q_full, k, v, lens, Tq = _decode_case(40 + c)
+    B, H, L, d = q_full.shape
+    Ht = 1 if tables == "shared" else H
+    wK = rnd((Ht, 2 * c + 1, d), 50, 0.3) if tables in ("kv", "k", "shared") else None
+    wV = rnd((Ht, 2 * c + 1, d), 51, 0.3) if tables in ("kv", "v", "shared") else None
+    # the decode queries are the full sequence's rows at positions len - Tq + t
+    q = np.zeros((B, H, Tq, d))
+    rows, where = [], []
+    for b in range(B):
+        for t in range(Tq):
+            i = lens[b] - Tq + t
+            if i >= 0:
+                q[b, :, t] = q_full[b, :, i]
+                for h in range(H):
+                    rows.append((b, h, i))
+                    where.append((b, h, t))
+    z = oracle.relattn_decode(q, k, v, wK, wV, c, cache_lens=lens)
+    zr = oracle.relattn_rows(q_full, k, v, wK, wV, c, causal=True, key_lens=lens, rows=rows)
+    for (b, h, t), row in zip(where, zr):
+        np.testing.assert_allclose(z[b, h, t], row, rtol=0, atol=1e-12)
+    # a query with no visible key (position < 0) outputs zeros
+    assert np.all(z[2, :, 0] == 0.0) and lens[2] - Tq + 0 < 0
+
+
+@pytest.mark.parametrize("bidir", [True, False])
+def test_t5_decode_matches_forward_rows(bidir):
+    q_full, k, v, lens, Tq = _decode_case(60, L=40)
+    B, H, L, d = q_full.shape
+    bias = rnd((32, H), 61)
+    q = np.zeros((B, H, Tq, d))
+    rows, where = [], []
+    for b in range(B):
+        for t in range(Tq):
+            i = lens[b] - Tq + t
+            if i >= 0:
+                q[b, :, t] = q_full[b, :, i]
+                for h in range(H):
+                    rows.append((b, h, i))
+                    where.append((b, h, t))
+    z = oracle.t5_decode(q, k, v, bias, 32, 16, bidir, cache_lens=lens)
+    zr = oracle.t5_rows(q_full, k, v, bias, 32, 16, bidir, causal=True, key_lens=lens, rows=rows)
+    for (b, h, t), row in zip(where, zr):
+        np.testing.assert_allclose(z[b, h, t], row, rtol=0, atol=1e-12)
+
+
+def test_decode_first_position_closed_form():
+    """One cached key at offset 0 (label row k): alpha = 1, so the output is
+    v_0 + a^V_0 (Eq. 3) whatever the logits are."""
+    B, H, L, d, c = 1, 2, 5, 4, 2
+    q, k, v = rnd((B, H, 1, d), 70), rnd((B, H, L, d), 71), rnd((B, H, L, d), 72)
+    wK, wV = rnd((H, 2 * c + 1, d), 73), rnd((H, 2 * c + 1, d), 74)
+    z = oracle.relattn_decode(q, k, v, wK, wV, c, cache_lens=[1])
+    for h in range(H):
+        np.testing.assert_allclose(z[0, h, 0], v[0, h, 0] + wV[h, c], rtol=0, atol=1e-14)
+
+
+def test_decode_two_keys_closed_form():
+    """Two cached keys at offsets -1 and 0 with clip 1: labels 0 and 1, so
+    alpha_0 = 1 / (1 + exp(e_1 - e_0)) with e_j = q.(k_j + a^K) / sqrt(d)."""
+    d, c = 4, 1
+    q, k, v = rnd((1, 1, 1, d), 80), rnd((1, 1, 2, d), 81), rnd((1, 1, 2, d), 82)
+    wK, wV = rnd((1, 3, d), 83), rnd((1, 3, d), 84)
+    e0 = q[0, 0, 0] @ (k[0, 0, 0] + wK[0, 0]) / math.sqrt(d)
+    e1 = q[0, 0, 0] @ (k[0, 0, 1] + wK[0, 1]) / math.sqrt(d)
+    a0 = 1.0 / (1.0 + math.exp(e1 - e0))
+    want = a0 * (v[0, 0, 0] + wV[0, 0]) + (1 - a0) * (v[0, 0, 1] + wV[0, 1])
+    z = oracle.relattn_decode(q, k, v, wK, wV, c, cache_lens=[2])
+    np.testing.assert_allclose(z[0, 0, 0], want, rtol=0, atol=1e-14)
