@@ -29,9 +29,9 @@
  *   - All tensor data pointers are DEVICE pointers owned by the caller.  The
  *     library allocates nothing and keeps no state between calls; it is
  *     thread-safe.  Equal inputs give bit-identical outputs.
- *   - relattn_fwd only enqueues work on `stream` (a hipStream_t, NULL = the
- *     default stream) and returns.  Buffers must stay alive until the stream
- *     has passed that point.  Faults during execution surface at the caller's
+ *   - relattn_fwd and relattn_decode only enqueue work on `stream` (a
+ *     hipStream_t, NULL = the default stream) and return.  Buffers must stay
+ *     alive until the stream has passed that point.  Faults during execution surface at the caller's
  *     next synchronisation.
  *   - Return value: RELATTN_OK (0) or a negative relattn_status.  A message
  *     with the detail is kept per thread (relattn_last_error).  No exception or
@@ -40,6 +40,7 @@
 #ifndef RELATTN_H
 #define RELATTN_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -125,6 +126,52 @@ int relattn_validate(const relattn_tensor* q, const relattn_tensor* k,
  * Enqueued on `stream`; same error codes as relattn_fwd. */
 int relattn_debug_indices(int32_t n, int32_t clip_k, const relattn_t5_params* t5,
                           int32_t* out_dev, void* stream);
+
+/*
+ * relattn_decode: incremental decoding.  The newest Tq positions of each
+ * sequence attend over its key/value cache with the causal mask; each output
+ * row is the row relattn_fwd would compute for that position with causal = 1
+ * (same formulas, tables and T5 bias as above).
+ *
+ *   q, out       : [B, H, Tq, d].  Query t of batch b sits at position
+ *                  i = cache_lens[b] - Tq + t and sees the keys j <= i.
+ *   k, v         : [B, H, L, d] caches, L >= 1 rows; rows j < cache_lens[b]
+ *                  must hold the keys and values of positions 0..j (the new
+ *                  positions included); later rows are never read.
+ *   wK, wV, t5_bias, t5, clip_k, scale: as for relattn_fwd.
+ *   cache_lens   : device int32[B] (4-byte aligned), clamped to [0, L]; NULL
+ *                  means L for every batch.  A query whose position is
+ *                  negative (cache_lens[b] < Tq - t) sees no key and outputs
+ *                  zeros.
+ *   workspace    : device buffer of at least workspace_bytes, 16-byte
+ *                  aligned, owned by the caller; its contents on entry do not
+ *                  matter and are overwritten.  Its size comes from
+ *                  relattn_decode_workspace_size (0 for empty problems, where
+ *                  NULL is accepted).  Calls that share a workspace must be
+ *                  ordered (same stream).
+ *   stream       : hipStream_t to enqueue on (NULL = default stream).
+ *
+ * Dtypes, head sizes, alignment and error codes as for relattn_fwd; the
+ * cache may be longer than 65535 * 32768 / (d * element bytes) rows only
+ * with UNSUPPORTED.  Enqueues two kernels and returns.
+ */
+int relattn_decode(const relattn_tensor* q, const relattn_tensor* k,
+                   const relattn_tensor* v, const relattn_tensor* wK,
+                   const relattn_tensor* wV, const relattn_tensor* t5_bias,
+                   const relattn_t5_params* t5, int32_t clip_k, float scale,
+                   const int32_t* cache_lens, relattn_tensor* out,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* relattn_decode_workspace_size: the argument checks of relattn_decode (host
+ * only: no HIP call, works without a GPU) and the workspace it needs, written
+ * to *bytes.  The size depends only on the shapes, dtype and tables. */
+int relattn_decode_workspace_size(const relattn_tensor* q, const relattn_tensor* k,
+                                  const relattn_tensor* v, const relattn_tensor* wK,
+                                  const relattn_tensor* wV,
+                                  const relattn_tensor* t5_bias,
+                                  const relattn_t5_params* t5, int32_t clip_k,
+                                  float scale, const relattn_tensor* out,
+                                  size_t* bytes);
 
 /* Static text for a status code. */
 const char* relattn_strerror(int status);

@@ -10,7 +10,8 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["fwd", "validate", "debug_indices", "RelattnError", "library_path",
+__all__ = ["fwd", "validate", "decode", "decode_workspace_size", "debug_indices",
+           "RelattnError", "library_path",
            "OK", "INVALID_ARGUMENT", "UNSUPPORTED", "NO_DEVICE", "LAUNCH_FAILED"]
 
 OK, INVALID_ARGUMENT, UNSUPPORTED, NO_DEVICE, LAUNCH_FAILED = 0, -1, -2, -3, -4
@@ -58,6 +59,13 @@ def _load():
     lib.relattn_fwd.restype = ctypes.c_int
     lib.relattn_validate.argtypes = args
     lib.relattn_validate.restype = ctypes.c_int
+    dec = [P(_Tensor), P(_Tensor), P(_Tensor), P(_Tensor), P(_Tensor), P(_Tensor),
+           P(_T5), ctypes.c_int32, ctypes.c_float]
+    lib.relattn_decode.argtypes = dec + [ctypes.c_void_p, P(_Tensor), ctypes.c_void_p,
+                                         ctypes.c_size_t, ctypes.c_void_p]
+    lib.relattn_decode.restype = ctypes.c_int
+    lib.relattn_decode_workspace_size.argtypes = dec + [P(_Tensor), P(ctypes.c_size_t)]
+    lib.relattn_decode_workspace_size.restype = ctypes.c_int
     lib.relattn_debug_indices.argtypes = [ctypes.c_int32, ctypes.c_int32, P(_T5),
                                           ctypes.c_void_p, ctypes.c_void_p]
     lib.relattn_debug_indices.restype = ctypes.c_int
@@ -181,6 +189,75 @@ def debug_indices(n, clip=0, *, t5=False, num_buckets=32, max_distance=128,
     t5p = _T5(int(num_buckets), int(max_distance), 1 if bidirectional else 0) if t5 else None
     st = lib.relattn_debug_indices(int(n), int(clip), _ref(t5p), ctypes.c_void_p(out.data_ptr()),
                                    ctypes.c_void_p(stream))
+    if st != OK:
+        _raise(lib, st)
+    return out
+
+
+def _dec_args(q, k, v, wK, wV, t5_bias, clip, num_buckets, max_distance, bidirectional,
+              scale):
+    keep = []
+    views = [_view(x) for x in (q, k, v, wK, wV, t5_bias)]
+    t5 = None
+    if t5_bias is not None:
+        t5 = _T5(int(num_buckets), int(max_distance), 1 if bidirectional else 0)
+    keep += views + [t5]
+    args = [_ref(x) for x in views] + [_ref(t5), int(clip),
+                                        float(0.0 if scale is None else scale)]
+    return args, keep
+
+
+def decode_workspace_size(q, k, v, wK=None, wV=None, *, clip=0, t5_bias=None,
+                          num_buckets=32, max_distance=128, bidirectional=True, scale=None,
+                          out=None):
+    """Workspace bytes ``decode`` needs (host-only check of its arguments);
+    raises RelattnError on invalid arguments."""
+    lib = _load()
+    args, keep = _dec_args(q, k, v, wK, wV, t5_bias, clip, num_buckets, max_distance,
+                           bidirectional, scale)
+    outv = _view(q if out is None else out)
+    nbytes = ctypes.c_size_t(0)
+    st = lib.relattn_decode_workspace_size(*args, ctypes.byref(outv), ctypes.byref(nbytes))
+    del keep
+    if st != OK:
+        _raise(lib, st)
+    return int(nbytes.value)
+
+
+def decode(q, k, v, wK=None, wV=None, *, clip=0, cache_lens=None, t5_bias=None,
+           num_buckets=32, max_distance=128, bidirectional=True, scale=None, out=None,
+           workspace=None, stream=None):
+    """Incremental decoding: q [B, H, Tq, d] holds the newest Tq positions of
+    each sequence, k and v [B, H, L, d] its cache; query t of batch b sits at
+    position cache_lens[b] - Tq + t (cache_lens: int32 [B] device tensor, None
+    = L) and sees the keys up to it.  Tables and T5 arguments as for ``fwd``.
+    ``workspace`` (a device tensor of at least ``decode_workspace_size`` bytes)
+    is allocated through torch when not given.  Returns ``out``."""
+    import torch
+    lib = _load()
+    if cache_lens is not None and cache_lens.dtype != torch.int32:
+        raise RelattnError(INVALID_ARGUMENT, "relattn: cache_lens must be int32")
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    need = decode_workspace_size(q, k, v, wK, wV, clip=clip, t5_bias=t5_bias,
+                                 num_buckets=num_buckets, max_distance=max_distance,
+                                 bidirectional=bidirectional, scale=scale, out=out)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    elif hasattr(stream, "cuda_stream"):
+        stream = stream.cuda_stream
+    args, keep = _dec_args(q, k, v, wK, wV, t5_bias, clip, num_buckets, max_distance,
+                           bidirectional, scale)
+    outv = _view(out)
+    st = lib.relattn_decode(*args,
+                            ctypes.c_void_p(cache_lens.data_ptr() if cache_lens is not None
+                                            else None),
+                            ctypes.byref(outv), ctypes.c_void_p(workspace.data_ptr()),
+                            ctypes.c_size_t(workspace.numel() * workspace.element_size()),
+                            ctypes.c_void_p(stream))
+    del keep
     if st != OK:
         _raise(lib, st)
     return out

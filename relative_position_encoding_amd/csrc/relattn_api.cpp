@@ -381,6 +381,133 @@ int make_plan(const relattn_tensor* q, const relattn_tensor* k, const relattn_te
   return RELATTN_OK;
 }
 
+// ---- incremental decoding --------------------------------------------------
+
+struct DecPlan {
+  bool empty = false;
+  bool bf16 = false;
+  int d = 0;
+  RelMode mode = relattn::kRelNone;
+  bool has_wk = false, has_wv = false;
+  size_t ws_bytes = 0;
+  size_t ws_o_off = 0, ws_band_off = 0;  // byte offsets in the workspace
+  relattn::DecParams p{};
+};
+
+size_t align16(size_t x) { return (x + 15) & ~size_t(15); }
+
+int make_dec_plan(const relattn_tensor* q, const relattn_tensor* k, const relattn_tensor* v,
+                  const relattn_tensor* wK, const relattn_tensor* wV,
+                  const relattn_tensor* t5_bias, const relattn_t5_params* t5, int32_t clip_k,
+                  float scale, const relattn_tensor* out, DecPlan* plan, bool want_t5_table) {
+  int st;
+  if ((st = check_view(q, "q", 4, true))) return st;
+  if ((st = check_view(k, "k", 4, true))) return st;
+  if ((st = check_view(v, "v", 4, true))) return st;
+  if ((st = check_view(out, "out", 4, true))) return st;
+  const relattn_tensor* others[3] = {k, v, out};
+  const char* names[3] = {"k", "v", "out"};
+  for (int t = 0; t < 3; ++t)
+    if (others[t]->dtype != q->dtype)
+      return fail(RELATTN_ERR_INVALID_ARGUMENT, "%s dtype differs from q", names[t]);
+  for (int i = 0; i < 4; ++i)
+    if (out->shape[i] != q->shape[i])
+      return fail(RELATTN_ERR_INVALID_ARGUMENT, "out shape differs from q in dim %d", i);
+  for (int t = 0; t < 2; ++t)
+    for (int i : {0, 1, 3})
+      if (others[t]->shape[i] != q->shape[i])
+        return fail(RELATTN_ERR_INVALID_ARGUMENT, "%s shape differs from q in dim %d",
+                    names[t], i);
+  if (v->shape[2] != k->shape[2])
+    return fail(RELATTN_ERR_INVALID_ARGUMENT, "k and v caches differ in length");
+  const int64_t B = q->shape[0], H = q->shape[1], Tq = q->shape[2], d = q->shape[3];
+  const int64_t L = k->shape[2];
+  if (!(d == 16 || d == 32 || d == 64 || d == 128))
+    return fail(RELATTN_ERR_UNSUPPORTED, "head size d = %lld is not one of 16, 32, 64, 128",
+                (long long)d);
+  if (L > kMaxSeq || Tq > kMaxSeq)
+    return fail(RELATTN_ERR_UNSUPPORTED, "cache or query length exceeds 2^30");
+  if (std::isnan(scale) || std::isinf(scale))
+    return fail(RELATTN_ERR_INVALID_ARGUMENT, "scale must be finite");
+  const bool is_t5 = t5_bias != nullptr || t5 != nullptr;
+  if ((t5_bias == nullptr) != (t5 == nullptr))
+    return fail(RELATTN_ERR_INVALID_ARGUMENT, "t5_bias and t5 params must be given together");
+  if (is_t5 && (wK || wV))
+    return fail(RELATTN_ERR_INVALID_ARGUMENT, "T5 bias excludes the wK/wV tables");
+  if (!is_t5 && clip_k < 0) return fail(RELATTN_ERR_INVALID_ARGUMENT, "clip_k must be >= 0");
+  if (!is_t5 && (int64_t)clip_k > kMaxSeq)
+    return fail(RELATTN_ERR_UNSUPPORTED, "clip_k exceeds 2^30");
+  if (wK && (st = check_table(wK, "wK", q, clip_k))) return st;
+  if (wV && (st = check_table(wV, "wV", q, clip_k))) return st;
+  T5Buckets tb = {};
+  if (is_t5) {
+    if ((st = check_view(t5_bias, "t5_bias", 2, false))) return st;
+    if (t5_bias->dtype != RELATTN_F32)
+      return fail(RELATTN_ERR_INVALID_ARGUMENT, "t5_bias must be F32");
+    if (t5_bias->shape[0] != t5->num_buckets || t5_bias->shape[1] != H)
+      return fail(RELATTN_ERR_INVALID_ARGUMENT, "t5_bias must be [num_buckets, H]");
+    if ((st = check_t5(t5, want_t5_table ? &tb : nullptr))) return st;
+  }
+
+  DecPlan& P = *plan;
+  P.bf16 = q->dtype == RELATTN_BF16;
+  P.d = (int)d;
+  P.mode = is_t5 ? relattn::kRelT5 : ((wK || wV) ? relattn::kRelShaw : relattn::kRelNone);
+  P.has_wk = wK != nullptr;
+  P.has_wv = wV != nullptr;
+  P.empty = (B == 0 || H == 0 || Tq == 0);
+  if (P.empty) return RELATTN_OK;
+  const int64_t rows = B * H * Tq;
+  if (rows > INT32_MAX) return fail(RELATTN_ERR_UNSUPPORTED, "too many query rows (B*H*Tq)");
+  const int ch = relattn::dec_chunk(P.bf16 ? 2 : 4, P.d);
+  const int64_t nch = std::max<int64_t>(1, (L + ch - 1) / ch);
+  if (nch > 65535)
+    return fail(RELATTN_ERR_UNSUPPORTED, "cache of %lld rows exceeds %lld", (long long)L,
+                (long long)65535 * ch);
+  const int64_t nband = (P.mode == relattn::kRelShaw && P.has_wv)
+                            ? std::min<int64_t>(clip_k, std::max<int64_t>(L, 1))
+                            : 0;
+  P.ws_o_off = align16((size_t)rows * nch * 2 * sizeof(float));
+  P.ws_band_off = P.ws_o_off + (size_t)rows * nch * d * sizeof(float);
+  P.ws_bytes = align16(P.ws_band_off + (size_t)rows * nband * sizeof(float));
+
+  relattn::DecParams& p = P.p;
+  p.B = (int32_t)B;
+  p.H = (int32_t)H;
+  p.Tq = (int32_t)Tq;
+  p.L = (int32_t)L;
+  p.clip = is_t5 ? 0 : clip_k;
+  p.nband = (int32_t)nband;
+  p.nch = (int32_t)nch;
+  p.t5 = tb;
+  const float s = scale > 0.f ? scale : (is_t5 ? 1.f : 1.f / std::sqrt((float)d));
+  p.scale_log2 = s * 1.4426950408889634f;
+  p.q = q->data;
+  p.k = k->data;
+  p.v = v->data;
+  p.o = out->data;
+  p.q_sb = q->stride[0]; p.q_sh = q->stride[1]; p.q_st = q->stride[2];
+  p.k_sb = k->stride[0]; p.k_sh = k->stride[1]; p.k_sn = k->stride[2];
+  p.v_sb = v->stride[0]; p.v_sh = v->stride[1]; p.v_sn = v->stride[2];
+  p.o_sb = out->stride[0]; p.o_sh = out->stride[1]; p.o_st = out->stride[2];
+  if (wK) {
+    p.wk = wK->data;
+    p.wk_sh = wK->shape[0] == 1 ? 0 : wK->stride[0];
+    p.wk_sr = wK->stride[1];
+  }
+  if (wV) {
+    p.wv = wV->data;
+    p.wv_sh = wV->shape[0] == 1 ? 0 : wV->stride[0];
+    p.wv_sr = wV->stride[1];
+  }
+  if (is_t5) {
+    p.t5_bias = static_cast<const float*>(t5_bias->data);
+    p.tb_sb = t5_bias->stride[0];
+    p.tb_sh = t5_bias->stride[1];
+  }
+  return RELATTN_OK;
+}
+
 // The device the calling thread has selected must be a gfx950.
 int check_device() {
   int dev = -1;
@@ -449,6 +576,53 @@ int relattn_debug_indices(int32_t n, int32_t clip_k, const relattn_t5_params* t5
   if (t5 && (st = check_t5(t5, &tb))) return st;
   if ((st = check_device())) return st;
   const int e = relattn::launch_debug_indices(n, clip_k, t5 ? &tb : nullptr, out_dev, stream);
+  if (e != (int)hipSuccess)
+    return fail(RELATTN_ERR_LAUNCH_FAILED, "launch failed: %s",
+                hipGetErrorString((hipError_t)e));
+  return RELATTN_OK;
+}
+
+int relattn_decode_workspace_size(const relattn_tensor* q, const relattn_tensor* k,
+                                  const relattn_tensor* v, const relattn_tensor* wK,
+                                  const relattn_tensor* wV, const relattn_tensor* t5_bias,
+                                  const relattn_t5_params* t5, int32_t clip_k, float scale,
+                                  const relattn_tensor* out, size_t* bytes) {
+  g_last_error.clear();
+  if (!bytes) return fail(RELATTN_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  DecPlan plan;
+  const int st = make_dec_plan(q, k, v, wK, wV, t5_bias, t5, clip_k, scale, out, &plan, false);
+  if (st) return st;
+  *bytes = plan.empty ? 0 : plan.ws_bytes;
+  return RELATTN_OK;
+}
+
+int relattn_decode(const relattn_tensor* q, const relattn_tensor* k, const relattn_tensor* v,
+                   const relattn_tensor* wK, const relattn_tensor* wV,
+                   const relattn_tensor* t5_bias, const relattn_t5_params* t5, int32_t clip_k,
+                   float scale, const int32_t* cache_lens, relattn_tensor* out, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  DecPlan plan;
+  int st = make_dec_plan(q, k, v, wK, wV, t5_bias, t5, clip_k, scale, out, &plan, true);
+  if (st) return st;
+  if (cache_lens && (reinterpret_cast<uintptr_t>(cache_lens) & 3u))
+    return fail(RELATTN_ERR_INVALID_ARGUMENT, "cache_lens is not 4-byte aligned");
+  if (!plan.empty) {
+    if (workspace_bytes < plan.ws_bytes)
+      return fail(RELATTN_ERR_INVALID_ARGUMENT, "workspace of %zu bytes, %zu needed",
+                  workspace_bytes, plan.ws_bytes);
+    if (!workspace || !aligned16(workspace))
+      return fail(RELATTN_ERR_INVALID_ARGUMENT, "workspace is NULL or not 16-byte aligned");
+  }
+  if ((st = check_device())) return st;
+  if (plan.empty) return RELATTN_OK;
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  plan.p.cache_lens = cache_lens;
+  plan.p.ws_ml = reinterpret_cast<float*>(ws);
+  plan.p.ws_o = reinterpret_cast<float*>(ws + plan.ws_o_off);
+  plan.p.ws_band = reinterpret_cast<float*>(ws + plan.ws_band_off);
+  const int e = relattn::launch_decode(plan.bf16, plan.d, plan.mode, plan.has_wk, plan.has_wv,
+                                       plan.p, stream);
   if (e != (int)hipSuccess)
     return fail(RELATTN_ERR_LAUNCH_FAILED, "launch failed: %s",
                 hipGetErrorString((hipError_t)e));

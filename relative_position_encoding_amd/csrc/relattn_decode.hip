@@ -1,0 +1,309 @@
+// Incremental decoding for gfx950: the newest Tq positions of each sequence
+// attend over its key/value cache ("Self-Attention with Relative Position
+// Representations", section 3.4, Eq. 3 and Eq. 4 with r = clip(j - i, k);
+// T5 section of "Relative position embeddings" for the bias variant).  Query
+// t of batch b sits at position i = len_b - Tq + t and sees keys j <= i.
+//
+// One decoding step reads the whole cache once and does little arithmetic per
+// byte, so the work is split into chunks of the cache that stream from HBM in
+// parallel:
+//   decode_partial_kernel  one workgroup per (query row, chunk of keys): the
+//       chunk's logits e_j = scale * q . (k_j + a^K_ij) in log2 units (T5: the
+//       bucketed bias instead of a^K), its max m_c, the sum l_c of 2^(e_j - m_c)
+//       and the partial output O_c = sum_j 2^(e_j - m_c) v_j.  Each K and V row
+//       is read by LPR lanes with 16-byte loads (coalesced rows, every load of
+//       a lane issued before the first use); a dot product is summed over the
+//       LPR lanes of its row.  The raw logits of keys whose label holds them
+//       alone (offsets -k < j - i <= 0) are kept for the value term.
+//   decode_combine_kernel  one workgroup per query row, one thread per output
+//       column: m = max m_c, l = sum l_c 2^(m_c - m), O = sum O_c 2^(m_c - m);
+//       the value term adds 2^(e_j - m) a^V for each single-key label and the
+//       remaining weight l - sum of those for label -k; z = O / l.
+#include <hip/hip_runtime.h>
+
+#include <type_traits>
+
+#include "relattn_device.h"
+#include "relattn_internal.h"
+
+namespace relattn {
+namespace {
+
+constexpr int kDecThreads = 256;
+
+template <bool BF16>
+struct Frag;  // 16 bytes of a row
+template <>
+struct Frag<true> {
+  using V = bf16x8;
+  static constexpr int N = 8;
+};
+template <>
+struct Frag<false> {
+  using V = f32x4;
+  static constexpr int N = 4;
+};
+
+template <bool BF16>
+__device__ __forceinline__ typename Frag<BF16>::V load_frag(const void* base, int64_t elem) {
+  using V = typename Frag<BF16>::V;
+  return *reinterpret_cast<const V*>(static_cast<const char*>(base) + elem * (BF16 ? 2 : 4));
+}
+
+// Sum over the W consecutive lanes that share a row (W a power of two <= 64).
+template <int W>
+__device__ __forceinline__ float group_sum(float x) {
+#pragma unroll
+  for (int o = W / 2; o > 0; o /= 2) x += __shfl_xor(x, o);
+  return x;
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o /= 2) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o /= 2) x += __shfl_xor(x, o);
+  return x;
+}
+
+// Position of query row `row` = (b * H + h) * Tq + t, and its batch and head.
+struct RowPos {
+  int b, h, t, i;
+};
+__device__ __forceinline__ RowPos row_pos(const DecParams& p, int row) {
+  RowPos r;
+  r.t = row % p.Tq;
+  const int bh = row / p.Tq;
+  r.b = bh / p.H;
+  r.h = bh - r.b * p.H;
+  const int len = p.cache_lens ? min(max(p.cache_lens[r.b], 0), p.L) : p.L;
+  r.i = len - p.Tq + r.t;
+  return r;
+}
+
+template <int D, bool BF16, int MODE, bool HAS_WK, bool HAS_WV>
+__global__ __launch_bounds__(kDecThreads) void decode_partial_kernel(const DecParams p) {
+  using V = typename Frag<BF16>::V;
+  constexpr int EPL = Frag<BF16>::N;           // elements per 16-byte load
+  constexpr int LPR = D / EPL;                 // lanes per row
+  constexpr int RPP = kDecThreads / LPR;       // rows per pass
+  constexpr int CH = dec_chunk(BF16 ? 2 : 4, D);
+  constexpr int NP = CH / RPP;                 // passes (8)
+  static_assert(LPR >= 1 && LPR <= 64 && NP * RPP == CH, "chunk geometry");
+  constexpr bool SHAW = MODE == kRelShaw;
+  constexpr bool T5 = MODE == kRelT5;
+  __shared__ float s_e[CH];
+  __shared__ float s_red[8];
+  __shared__ float s_acc[RPP * D];
+
+  const int row = blockIdx.x, chunk = blockIdx.y;
+  const RowPos rp = row_pos(p, row);
+  const int i = rp.i, b = rp.b, h = rp.h;
+  const int j0 = chunk * CH;
+  if (i < 0 || j0 > i) return;  // no visible key in this chunk (whole workgroup)
+  const int j1 = min(j0 + CH, i + 1);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int part = tid % LPR, rs = tid / LPR;
+  const int c0 = part * EPL;  // first column of this lane's fragment
+
+  float qf[EPL];
+  {
+    const V x = load_frag<BF16>(p.q, b * p.q_sb + h * p.q_sh + rp.t * p.q_st + c0);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) qf[e] = (float)x[e];
+  }
+  const int64_t kb = b * p.k_sb + h * p.k_sh, vb = b * p.v_sb + h * p.v_sh;
+
+  // every K and V fragment of this lane, requested before the first use; rows
+  // past the last visible key read that key again (finite, weighted 0)
+  V kf[NP], vf[NP];
+#pragma unroll
+  for (int it = 0; it < NP; ++it) {
+    const int j = min(j0 + rs + it * RPP, j1 - 1);
+    kf[it] = load_frag<BF16>(p.k, kb + j * p.k_sn + c0);
+  }
+#pragma unroll
+  for (int it = 0; it < NP; ++it) {
+    const int j = min(j0 + rs + it * RPP, j1 - 1);
+    vf[it] = load_frag<BF16>(p.v, vb + j * p.v_sn + c0);
+  }
+
+  // relative logit of every key at offset <= -k (label row 0)
+  float far = 0.f;
+  if constexpr (SHAW && HAS_WK) {
+    const V w = load_frag<BF16>(p.wk, h * p.wk_sh + c0);
+    float d0 = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) d0 = fmaf(qf[e], (float)w[e], d0);
+    far = group_sum<LPR>(d0) * p.scale_log2;
+  }
+
+  // logits, log2 units
+#pragma unroll
+  for (int it = 0; it < NP; ++it) {
+    const int r = rs + it * RPP;
+    const bool valid = j0 + r < j1;
+    const int j = min(j0 + r, j1 - 1);
+    const int delta = j - i;  // <= 0
+    float x[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) x[e] = (float)kf[it][e];
+    float rel = 0.f;
+    if constexpr (SHAW && HAS_WK) {
+      if (delta > -p.clip) {
+        // inside the window: a^K of this key's own label joins k_j (Eq. 4)
+        const V w = load_frag<BF16>(p.wk, h * p.wk_sh + (delta + p.clip) * p.wk_sr + c0);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) x[e] += (float)w[e];
+      } else {
+        rel = far;
+      }
+    }
+    if constexpr (T5) rel = kLog2e * p.t5_bias[t5_bucket(delta, p.t5) * p.tb_sb + h * p.tb_sh];
+    float dot = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) dot = fmaf(qf[e], x[e], dot);
+    dot = group_sum<LPR>(dot);
+    const float lg = valid ? fmaf(dot, p.scale_log2, rel) : kNegInf;
+    if (part == 0) {
+      s_e[r] = lg;
+      if constexpr (SHAW && HAS_WV) {
+        if (valid && delta > -p.clip) p.ws_band[(int64_t)row * p.nband + delta + p.nband - 1] = lg;
+      }
+    }
+  }
+  __syncthreads();
+
+  // chunk max and sum of 2^(e - m)
+  float m = kNegInf;
+  for (int x = tid; x < CH; x += kDecThreads) m = fmaxf(m, s_e[x]);
+  m = wave_max(m);
+  if (lane == 0) s_red[wave] = m;
+  __syncthreads();
+  m = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+  float l = 0.f;
+  for (int x = tid; x < CH; x += kDecThreads) {
+    const float pv = fast_exp2(s_e[x] - m);  // 0 for the rows past the last key
+    s_e[x] = pv;
+    l += pv;
+  }
+  l = wave_sum(l);
+  if (lane == 0) s_red[4 + wave] = l;
+  __syncthreads();
+  l = (s_red[4] + s_red[5]) + (s_red[6] + s_red[7]);
+
+  // partial output: each lane sums its columns over its rows, then the row
+  // groups are summed through LDS
+  float acc[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
+#pragma unroll
+  for (int it = 0; it < NP; ++it) {
+    const float pv = s_e[rs + it * RPP];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[e] = fmaf(pv, (float)vf[it][e], acc[e]);
+  }
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) s_acc[rs * D + c0 + e] = acc[e];
+  __syncthreads();
+  const int64_t slot = (int64_t)row * p.nch + chunk;
+  for (int dim = tid; dim < D; dim += kDecThreads) {
+    float o = 0.f;
+    for (int g = 0; g < RPP; ++g) o += s_acc[g * D + dim];
+    p.ws_o[slot * D + dim] = o;
+  }
+  if (tid == 0) {
+    p.ws_ml[2 * slot] = m;
+    p.ws_ml[2 * slot + 1] = l;
+  }
+}
+
+template <int D, bool BF16, int MODE, bool HAS_WV>
+__global__ __launch_bounds__(128) void decode_combine_kernel(const DecParams p) {
+  using T = std::conditional_t<BF16, __bf16, float>;
+  constexpr int CH = dec_chunk(BF16 ? 2 : 4, D);
+  const int row = blockIdx.x, dim = threadIdx.x;
+  if (dim >= D) return;
+  const RowPos rp = row_pos(p, row);
+  T* orow = reinterpret_cast<T*>(p.o) + rp.b * p.o_sb + rp.h * p.o_sh + rp.t * p.o_st;
+  if (rp.i < 0) {  // no visible key: zeros
+    orow[dim] = (T)0.f;
+    return;
+  }
+  const int nchr = rp.i / CH + 1;  // chunks holding keys 0..i
+  const float* ml = p.ws_ml + (int64_t)row * p.nch * 2;
+  const float* po = p.ws_o + (int64_t)row * p.nch * D;
+  float m = kNegInf;
+  for (int c = 0; c < nchr; ++c) m = fmaxf(m, ml[2 * c]);
+  float l = 0.f, o = 0.f;
+  for (int c = 0; c < nchr; ++c) {
+    const float f = fast_exp2(ml[2 * c] - m);
+    l = fmaf(ml[2 * c + 1], f, l);
+    o = fmaf(po[c * D + dim], f, o);
+  }
+  if constexpr (MODE == kRelShaw && HAS_WV) {
+    // labels -k+1 .. 0 hold one key each (when it exists); label -k (row 0)
+    // holds every key at offset <= -k: what the row sum leaves
+    const T* wv = reinterpret_cast<const T*>(p.wv) + rp.h * p.wv_sh;
+    const float* band = p.ws_band + (int64_t)row * p.nband;
+    float sb = 0.f;
+    for (int delta = max(1 - p.nband, -rp.i); delta <= 0; ++delta) {
+      const float w = fast_exp2(band[delta + p.nband - 1] - m);
+      sb += w;
+      o = fmaf(w, (float)wv[(delta + p.clip) * p.wv_sr + dim], o);
+    }
+    const float tail = fmaxf(l - sb, 0.f);
+    o = fmaf(tail, (float)wv[dim], o);
+  }
+  orow[dim] = (T)(o / l);
+}
+
+template <int D, bool BF16, int MODE, bool HAS_WK, bool HAS_WV>
+int launch_dec_t(const DecParams& p, hipStream_t s) {
+  const int rows = p.B * p.H * p.Tq;
+  hipLaunchKernelGGL((decode_partial_kernel<D, BF16, MODE, HAS_WK, HAS_WV>), dim3(rows, p.nch),
+                     dim3(kDecThreads), 0, s, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return (int)e;
+  hipLaunchKernelGGL((decode_combine_kernel<D, BF16, MODE, HAS_WV>), dim3(rows), dim3(128), 0,
+                     s, p);
+  return (int)hipGetLastError();
+}
+
+template <int D, bool BF16>
+int launch_dec_mode(RelMode mode, bool has_wk, bool has_wv, const DecParams& p, hipStream_t s) {
+  if (mode == kRelT5) return launch_dec_t<D, BF16, kRelT5, false, false>(p, s);
+  if (mode == kRelShaw) {
+    if (has_wk && has_wv) return launch_dec_t<D, BF16, kRelShaw, true, true>(p, s);
+    if (has_wk) return launch_dec_t<D, BF16, kRelShaw, true, false>(p, s);
+    return launch_dec_t<D, BF16, kRelShaw, false, true>(p, s);
+  }
+  return launch_dec_t<D, BF16, kRelNone, false, false>(p, s);
+}
+
+template <bool BF16>
+int launch_dec_d(int d, RelMode mode, bool has_wk, bool has_wv, const DecParams& p,
+                 hipStream_t s) {
+  switch (d) {
+    case 16: return launch_dec_mode<16, BF16>(mode, has_wk, has_wv, p, s);
+    case 32: return launch_dec_mode<32, BF16>(mode, has_wk, has_wv, p, s);
+    case 64: return launch_dec_mode<64, BF16>(mode, has_wk, has_wv, p, s);
+    case 128: return launch_dec_mode<128, BF16>(mode, has_wk, has_wv, p, s);
+  }
+  return (int)hipErrorInvalidValue;
+}
+
+}  // namespace
+
+int launch_decode(bool bf16, int d, RelMode mode, bool has_wk, bool has_wv, const DecParams& p,
+                  void* stream) {
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  return bf16 ? launch_dec_d<true>(d, mode, has_wk, has_wv, p, s)
+              : launch_dec_d<false>(d, mode, has_wk, has_wv, p, s);
+}
+
+}  // namespace relattn

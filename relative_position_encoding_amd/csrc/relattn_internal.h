@@ -79,4 +79,48 @@ int launch_fwd(bool bf16, int d, const LaunchCfg& cfg, RelMode mode, bool has_wk
 int launch_debug_indices(int n, int clip, const T5Buckets* t5, int32_t* out,
                          void* stream);
 
+// ---- incremental decoding (relattn_decode.hip) ----------------------------
+
+// Keys of the cache one decode workgroup covers: 32 KB of K rows, i.e. eight
+// 16-byte loads of K (and of V) per lane of a 256-thread workgroup.
+constexpr int dec_chunk(int elem_bytes, int d) { return 32768 / (elem_bytes * d); }
+
+// Everything a decode launch needs.  Query t of batch b sits at position
+// cache_lens[b] - Tq + t of its sequence.  Strides count elements.  The
+// workspace holds, per query row (b, h, t) and chunk, the partial max and sum
+// (ws_ml, 2 floats) and the partial output (ws_o, d floats), and per row the
+// raw logits of the keys whose label holds them alone (ws_band, nband floats).
+struct DecParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  const void* wk;
+  const void* wv;
+  const float* t5_bias;
+  const int32_t* cache_lens;  // [B] or null (every row of the cache is valid)
+  float* ws_ml;
+  float* ws_o;
+  float* ws_band;
+
+  int64_t q_sb, q_sh, q_st;
+  int64_t k_sb, k_sh, k_sn;
+  int64_t v_sb, v_sh, v_sn;
+  int64_t o_sb, o_sh, o_st;
+  int64_t wk_sh, wk_sr;
+  int64_t wv_sh, wv_sr;
+  int64_t tb_sb, tb_sh;
+
+  int32_t B, H, Tq, L;  // L = rows of the cache
+  int32_t clip;
+  int32_t nband;        // min(clip, L) with a value table, else 0
+  int32_t nch;          // chunks per query row: ceil(L / kDecChunk)
+  float scale_log2;
+  T5Buckets t5;
+};
+
+// Launch the partial and combine kernels.  Returns a hipError_t value.
+int launch_decode(bool bf16, int d, RelMode mode, bool has_wk, bool has_wv,
+                  const DecParams& p, void* stream);
+
 }  // namespace relattn

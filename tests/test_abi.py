@@ -150,3 +150,49 @@ print(st)
                        env=env, timeout=300)
     assert r.returncode == 0, r.stderr
     assert int(r.stdout.strip().splitlines()[-1]) == -3
+
+
+# ---------------------------------------------------------------------------
+# relattn_decode: host-only checks through relattn_decode_workspace_size
+# ---------------------------------------------------------------------------
+
+def test_decode_workspace_size(ra):
+    B, H, Tq, L, d, c = 2, 3, 1, 1000, 64, 16
+    q, k, v = T(B, H, Tq, d), T(B, H, L, d), T(B, H, L, d)
+    ch = 32768 // (2 * d)                       # keys per decode workgroup (bf16)
+    nch = -(-L // ch)
+    rows = B * H * Tq
+    base = -(-(rows * nch * 2 * 4) // 16) * 16 + rows * nch * d * 4
+    # value table: one raw logit per single-key label (min(c, L) of them) per row
+    want = -(-(base + rows * c * 4) // 16) * 16
+    assert ra.decode_workspace_size(q, k, v, T(H, 2 * c + 1, d), T(H, 2 * c + 1, d),
+                                    clip=c) == want
+    assert ra.decode_workspace_size(q, k, v, T(H, 2 * c + 1, d), clip=c) == -(-base // 16) * 16
+    assert ra.decode_workspace_size(q, k, v, t5_bias=T(32, H, dtype=torch.float32)) > 0
+    e = T(0, H, Tq, d)
+    assert ra.decode_workspace_size(e, T(0, H, L, d), T(0, H, L, d)) == 0
+
+
+@pytest.mark.parametrize("case", ["cache_mismatch", "head_mismatch", "dtype_mix",
+                                  "table_rows", "t5_and_tables", "head_size"])
+def test_decode_rejects(ra, case):
+    H, d, c = 3, 64, 4
+    q, k, v = T(2, H, 1, d), T(2, H, 50, d), T(2, H, 50, d)
+    args, kw = [q, k, v], {}
+    code = ra.INVALID_ARGUMENT
+    if case == "cache_mismatch":
+        args[2] = T(2, H, 49, d)
+    elif case == "head_mismatch":
+        args[1] = T(2, H + 1, 50, d)
+    elif case == "dtype_mix":
+        args[2] = T(2, H, 50, d, dtype=torch.float32)
+    elif case == "table_rows":
+        args += [T(H, 2 * c, d)]; kw["clip"] = c
+    elif case == "t5_and_tables":
+        args += [T(H, 2 * c + 1, d)]; kw.update(clip=c, t5_bias=T(32, H, dtype=torch.float32))
+    elif case == "head_size":
+        args = [T(2, H, 1, 48), T(2, H, 50, 48), T(2, H, 50, 48)]
+        code = ra.UNSUPPORTED
+    with pytest.raises(ra.RelattnError) as ei:
+        ra.decode_workspace_size(*args, **kw)
+    assert ei.value.status == code

@@ -1,0 +1,201 @@
+"""GPU parity of incremental decoding (relattn_decode, through the C ABI)
+against the fp64 decode oracle.  Bars as for the forward: max-abs 1e-5 for
+fp32 and 2e-2 for bf16 inputs with fp32 accumulation."""
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+TOL = {torch.float32: 1e-5, torch.bfloat16: 2e-2}
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module")
+def ra():
+    import relative_position_encoding_amd as ra
+    if not os.path.exists(ra.library_path):
+        from relative_position_encoding_amd import build
+        build.build()
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return ra
+
+
+@pytest.fixture(autouse=True)
+def _announce(request):
+    sys.stderr.write(f"\n[gpu-case] {request.node.nodeid}\n")
+    sys.stderr.flush()
+    yield
+
+
+def chunk(dtype, d):
+    """Keys per decode workgroup (32 KB of K rows)."""
+    return 32768 // ((2 if dtype == torch.bfloat16 else 4) * d)
+
+
+def gen(B, H, Tq, L, d, dtype, seed, c, shared=False, tstd=0.1):
+    g = torch.Generator().manual_seed(seed)
+    r = lambda *s: torch.randn(*s, generator=g)
+    q, k, v = r(B, H, Tq, d), r(B, H, L, d), r(B, H, L, d)
+    Ht = 1 if shared else H
+    wK, wV = r(Ht, 2 * c + 1, d) * tstd, r(Ht, 2 * c + 1, d) * tstd
+    return [x.to(dtype) for x in (q, k, v, wK, wV)]
+
+
+def dev(x):
+    return None if x is None else x.to(DEV)
+
+
+def run(ra, q, k, v, wK, wV, c, lens, **kw):
+    lens_d = None if lens is None else torch.tensor(lens, dtype=torch.int32, device=DEV)
+    out = ra.decode(dev(q), dev(k), dev(v), dev(wK), dev(wV), clip=c, cache_lens=lens_d, **kw)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy()
+
+
+def maxerr(a, b):
+    return float(np.max(np.abs(np.asarray(a, np.float64) - b))) if np.size(b) else 0.0
+
+
+def lens_for(L, B, Tq):
+    """Full cache, a ragged length inside a chunk, one key, fewer keys than
+    new positions (some queries see nothing), and an empty cache."""
+    return [L, max(1, L - 37), 1, max(0, Tq - 1), 0][:B]
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=str)
+@pytest.mark.parametrize("d", [16, 32, 64, 128])
+@pytest.mark.parametrize("tables", ["kv", "k", "v", "none"])
+def test_decode_parity(ra, dtype, d, tables):
+    c, Tq, B, H = 5, 2, 5, 2
+    L = 2 * chunk(dtype, d) + 29           # several chunks and a ragged tail
+    L = min(L, 700)
+    q, k, v, wK, wV = gen(B, H, Tq, L, d, dtype, 100 + d, c)
+    wK = wK if tables in ("kv", "k") else None
+    wV = wV if tables in ("kv", "v") else None
+    lens = lens_for(L, B, Tq)
+    got = run(ra, q, k, v, wK, wV, c, lens)
+    want = oracle.relattn_decode(q, k, v, wK, wV, c, cache_lens=lens)
+    assert maxerr(got, want) <= TOL[dtype], maxerr(got, want)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=str)
+@pytest.mark.parametrize("c,L", [(0, 40), (1, 3), (64, 300), (300, 280), (16, 1)])
+def test_decode_clip_extremes(ra, dtype, c, L):
+    """No clipping (k >= L: every label holds one key), k = 0 (one label),
+    and a one-row cache."""
+    q, k, v, wK, wV = gen(3, 2, 1, L, 64, dtype, 200 + c, c)
+    lens = [L, max(1, L // 2), 1]
+    got = run(ra, q, k, v, wK, wV, c, lens)
+    want = oracle.relattn_decode(q, k, v, wK, wV, c, cache_lens=lens)
+    assert maxerr(got, want) <= TOL[dtype], maxerr(got, want)
+
+
+def test_decode_shared_tables_and_no_lens(ra):
+    q, k, v, wK, wV = gen(2, 3, 3, 300, 64, torch.bfloat16, 300, 8, shared=True)
+    got = run(ra, q, k, v, wK, wV, 8, None)
+    want = oracle.relattn_decode(q, k, v, wK, wV, 8, cache_lens=None)
+    assert maxerr(got, want) <= 2e-2
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=str)
+@pytest.mark.parametrize("bidir", [True, False])
+def test_decode_t5_parity(ra, dtype, bidir):
+    B, H, Tq, L, d = 4, 3, 2, 600, 64
+    g = torch.Generator().manual_seed(400)
+    q = (torch.randn(B, H, Tq, d, generator=g) / 8).to(dtype)
+    k = (torch.randn(B, H, L, d, generator=g) / 8).to(dtype)
+    v = torch.randn(B, H, L, d, generator=g).to(dtype)
+    bias = torch.randn(32, H, generator=g)
+    lens = [L, 333, 1, 0]
+    lens_d = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    out = ra.decode(dev(q), dev(k), dev(v), t5_bias=dev(bias), num_buckets=32,
+                    max_distance=128, bidirectional=bidir, cache_lens=lens_d)
+    torch.cuda.synchronize()
+    want = oracle.t5_decode(q, k, v, bias, 32, 128, bidir, cache_lens=lens)
+    assert maxerr(out.float().cpu().numpy(), want) <= TOL[dtype]
+
+
+def test_decode_matches_forward_rows(ra):
+    """The decode output of the newest position equals the causal forward's row
+    at that position (two HIP paths, same inputs)."""
+    B, H, L, d, c = 2, 4, 300, 64, 16
+    q_full, k, v, wK, wV = gen(B, H, L, L, d, torch.float32, 500, c)
+    lens = [L, 211]
+    lens_d = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    fwd = ra.fwd(dev(q_full), dev(k), dev(v), dev(wK), dev(wV), clip=c, causal=True)
+    q = torch.stack([q_full[b, :, lens[b] - 1] for b in range(B)])[:, :, None]
+    dec = ra.decode(dev(q), dev(k), dev(v), dev(wK), dev(wV), clip=c, cache_lens=lens_d)
+    torch.cuda.synchronize()
+    for b in range(B):
+        np.testing.assert_allclose(dec[b, :, 0].cpu().numpy(), fwd[b, :, lens[b] - 1].cpu().numpy(),
+                                   rtol=0, atol=1e-5)
+
+
+def test_decode_strided_cache(ra):
+    """Caches allocated for more rows and heads than used (strided views)."""
+    big_k = torch.randn(2, 5, 900, 64).to(torch.bfloat16)
+    big_v = torch.randn(2, 5, 900, 64).to(torch.bfloat16)
+    k, v = big_k[:, 1:4, :520], big_v[:, 1:4, :520]
+    q, _, _, wK, wV = gen(2, 3, 1, 1, 64, torch.bfloat16, 600, 4)
+    lens = [520, 300]
+    got = run(ra, q, k, v, wK, wV, 4, lens)
+    want = oracle.relattn_decode(q, k, v, wK, wV, 4, cache_lens=lens)
+    assert maxerr(got, want) <= 2e-2
+
+
+def test_decode_workspace_reuse(ra):
+    """Two calls in a row on one workspace, the second smaller."""
+    q1, k1, v1, wK, wV = gen(3, 2, 1, 900, 64, torch.bfloat16, 700, 16)
+    q2, k2, v2, _, _ = gen(2, 2, 1, 300, 64, torch.bfloat16, 701, 16)
+    need = ra.decode_workspace_size(dev(q1), dev(k1), dev(v1), dev(wK), dev(wV), clip=16)
+    ws = torch.empty(need, dtype=torch.uint8, device=DEV)
+    for (q, k, v, lens) in ((q1, k1, v1, [900, 450, 2]), (q2, k2, v2, [300, 17])):
+        lens_d = torch.tensor(lens, dtype=torch.int32, device=DEV)
+        out = ra.decode(dev(q), dev(k), dev(v), dev(wK), dev(wV), clip=16, cache_lens=lens_d,
+                        workspace=ws)
+        torch.cuda.synchronize()
+        want = oracle.relattn_decode(q, k, v, wK, wV, 16, cache_lens=lens)
+        assert maxerr(out.float().cpu().numpy(), want) <= 2e-2
+
+
+def test_decode_small_workspace_rejected(ra):
+    q, k, v, wK, wV = gen(2, 2, 1, 300, 64, torch.bfloat16, 800, 4)
+    ws = torch.empty(64, dtype=torch.uint8, device=DEV)
+    with pytest.raises(ra.RelattnError) as ei:
+        ra.decode(dev(q), dev(k), dev(v), dev(wK), dev(wV), clip=4, workspace=ws)
+    assert ei.value.status == ra.INVALID_ARGUMENT
+
+
+def test_decode_deterministic(ra):
+    q, k, v, wK, wV = gen(2, 2, 2, 700, 64, torch.bfloat16, 900, 16)
+    a = run(ra, q, k, v, wK, wV, 16, [700, 401])
+    b = run(ra, q, k, v, wK, wV, 16, [700, 401])
+    assert np.array_equal(a, b)
+
+
+def test_decode_workload_sampled_rows(ra):
+    """The decode workload at full size (as the benchmark times it): every
+    row against the fp64 oracle on a sample of 24 (batch, head) pairs."""
+    w = workloads.DECODE_WORKLOADS["decode"]
+    x = workloads.make_decode_inputs(w)
+    lens = x["cache_lens"].tolist()
+    out = ra.decode(dev(x["q"]), dev(x["k"]), dev(x["v"]), dev(x["key_table"]),
+                    dev(x["value_table"]), clip=w.clip, cache_lens=dev(x["cache_lens"]))
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy()
+    rng = np.random.default_rng(0)
+    pairs = [(int(rng.integers(w.batch)), int(rng.integers(w.heads))) for _ in range(24)]
+    for b, h in pairs:
+        sl = lambda t: t[b:b + 1, h:h + 1]
+        want = oracle.relattn_decode(sl(x["q"]), sl(x["k"]), sl(x["v"]),
+                                     x["key_table"][h:h + 1], x["value_table"][h:h + 1],
+                                     w.clip, cache_lens=[lens[b]])
+        assert maxerr(got[b, h], want[0, 0]) <= 2e-2, (b, h)

@@ -142,3 +142,66 @@ def attention_kwargs(w: Workload | str) -> dict:
     else:
         kw.update(w.t5)
     return kw
+
+
+# ---------------------------------------------------------------------------
+# Incremental decoding: the newest position(s) of each sequence over its
+# key/value cache.  Beam search with the Transformer big model is the pages'
+# inference setting ("Self-Attention with Relative Position Representations",
+# §5); 16 sentences x 4 beams give 64 sequences.
+# ---------------------------------------------------------------------------
+
+@dataclass(frozen=True)
+class DecodeWorkload:
+    name: str
+    config_id: int
+    description: str
+    batch: int
+    heads: int
+    cache: int               # rows of the cache (L)
+    d: int
+    tq: int = 1              # new positions per sequence
+    clip: int = 16
+    dtype: torch.dtype = torch.bfloat16
+    qkv_std: float = 1.0
+    table_std: float = 0.02
+    len_range: tuple = (512, 1024)
+
+    @property
+    def seed(self) -> int:
+        return SEED_BASE + self.config_id
+
+
+DECODE_WORKLOADS = {
+    "decode": DecodeWorkload(
+        name="decode", config_id=6,
+        description="Transformer-big beam-search decoding step: B64 (16 sentences x 4 "
+                    "beams) H16 d64 clip 16, key+value tables, cache of 1024 positions "
+                    "with lengths U[512,1024], one new position per sequence",
+        batch=64, heads=16, cache=1024, d=64),
+}
+
+
+def make_decode_inputs(w: DecodeWorkload | str, *, batch=None, heads=None, cache=None,
+                       tq=None, seed=None) -> dict:
+    """CPU tensors for a decode workload: q [B, H, Tq, d], the caches k and v
+    [B, H, L, d], key_table and value_table [H, 2c+1, d] and cache_lens int32
+    [B] (drawn in that order, fp32 then cast once to the workload dtype)."""
+    if isinstance(w, str):
+        w = DECODE_WORKLOADS[w]
+    B, H = batch or w.batch, heads or w.heads
+    L, Tq = cache or w.cache, tq or w.tq
+    g = torch.Generator().manual_seed(w.seed if seed is None else seed)
+
+    def normal(shape, std):
+        return torch.randn(shape, generator=g, dtype=torch.float32) * std
+
+    q = normal((B, H, Tq, w.d), w.qkv_std)
+    k = normal((B, H, L, w.d), w.qkv_std)
+    v = normal((B, H, L, w.d), w.qkv_std)
+    kt = normal((H, 2 * w.clip + 1, w.d), w.table_std)
+    vt = normal((H, 2 * w.clip + 1, w.d), w.table_std)
+    lo, hi = min(w.len_range[0], L), min(w.len_range[1], L)
+    lens = torch.randint(lo, hi + 1, (B,), generator=g, dtype=torch.int32)
+    return {"q": q.to(w.dtype), "k": k.to(w.dtype), "v": v.to(w.dtype),
+            "key_table": kt.to(w.dtype), "value_table": vt.to(w.dtype), "cache_lens": lens}
