@@ -35,6 +35,7 @@ PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # dense MFMA, MI355X
 PEAK_HBM_GBS = 8000.0
 LLC_BYTES = 256 << 20
 KERNEL_SRC = os.path.join(ROOT, "relative_position_encoding_amd", "csrc", "relattn_kernels.hip")
+DECODE_SRC = os.path.join(ROOT, "relative_position_encoding_amd", "csrc", "relattn_decode.hip")
 
 
 # ---------------------------------------------------------------------------
@@ -160,6 +161,95 @@ def ceiling_tflops(flops, nbytes, dt):
     return min(PEAK_TFLOPS[dt], flops / nbytes * PEAK_HBM_GBS / 1e3)
 
 
+# ---------------------------------------------------------------------------
+# incremental decoding (the newest position of each sequence over its cache)
+# ---------------------------------------------------------------------------
+
+def decode_work(w, cache_lens):
+    """(flops, bytes) one decoding step must do: q.k and p.v for every visible
+    key (4*d per key), the relative key term for the labels (2*d*(k+1)) and
+    the value term (2*d*(k+1)) per query; bytes: every visible cache row of k
+    and v once, q and out once, the tables once."""
+    esz = w.dtype.itemsize
+    keys = sum(int(x) for x in cache_lens) * w.heads * w.tq
+    rows = w.batch * w.heads * w.tq
+    flops = 4.0 * w.d * keys + 2 * 2.0 * w.d * (w.clip + 1) * rows
+    cache_bytes = 2.0 * sum(int(x) for x in cache_lens) * w.heads * w.d * esz
+    nbytes = cache_bytes + 2.0 * rows * w.d * esz + 2 * w.heads * (2 * w.clip + 1) * w.d * esz
+    return flops, nbytes
+
+
+def time_decode(ra, w, steps, warmup, hot=False, reps=1):
+    """Time ``steps`` back-to-back decoding steps (median of ``reps`` timed
+    regions).  Cold: the steps cycle through enough cache copies to exceed
+    twice the last-level cache; hot: one cache, reused by every step."""
+    import statistics
+    import torch
+    import workloads
+    lib = ra._load()
+    stream = torch.cuda.Stream()  # default priority
+    x = workloads.make_decode_inputs(w)
+    flops, nbytes = decode_work(w, x["cache_lens"].tolist())
+    copies = 1 if hot else max(1, min(16, int(2 * LLC_BYTES // nbytes) + 1))
+    calls, keep = [], []
+    for _ in range(copies):
+        g = {k: v.to("cuda").clone() for k, v in x.items()}
+        out = torch.empty_like(g["q"])
+        need = ra.decode_workspace_size(g["q"], g["k"], g["v"], g["key_table"], g["value_table"],
+                                        clip=w.clip, out=out)
+        ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+        args, kp = ra._dec_args(g["q"], g["k"], g["v"], g["key_table"], g["value_table"], None,
+                                w.clip, 32, 128, True, None)
+        outv = ra._view(out)
+        calls.append(args + [ctypes.c_void_p(g["cache_lens"].data_ptr()), ctypes.byref(outv),
+                             ctypes.c_void_p(ws.data_ptr()), ctypes.c_size_t(need),
+                             ctypes.c_void_p(stream.cuda_stream)])
+        keep += [g, out, ws, kp, outv]
+    fn = lib.relattn_decode
+    times = []
+    with torch.cuda.stream(stream):
+        for s_ in range(warmup):
+            if fn(*calls[s_ % copies]) != 0:
+                raise RuntimeError(ra.last_error())
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        for _ in range(reps):
+            t0.record(stream)
+            for s_ in range(steps):
+                fn(*calls[s_ % copies])
+            t1.record(stream)
+            torch.cuda.synchronize()
+            times.append(t0.elapsed_time(t1) / steps)
+    del keep
+    ms = statistics.median(times)
+    return {"ms_per_step": ms, "gbs": nbytes / (ms * 1e-3) / 1e9,
+            "tflops": flops / (ms * 1e-3) / 1e12, "alg_mbytes": nbytes / 1e6,
+            "alg_gflop": flops / 1e9, "input_copies": copies,
+            "tokens_per_s": w.batch * w.tq / (ms * 1e-3)}
+
+
+def decode_report(ra, steps):
+    """The decode workload's figures for the JSON line (not the headline)."""
+    import workloads
+    w = workloads.DECODE_WORKLOADS["decode"]
+    cold = time_decode(ra, w, steps, 20, reps=5)
+    hot = time_decode(ra, w, steps, 20, hot=True, reps=5)
+    tr = traffic_per_launch("decode")
+    sec = cold["ms_per_step"] * 1e-3
+    return {
+        "workload": w.description, "ms_per_step": round(cold["ms_per_step"], 5),
+        "tokens_per_s": round(cold["tokens_per_s"], 1),
+        "roofline": {"bound": "hbm", "achieved": round(cold["gbs"], 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(cold["gbs"] / PEAK_HBM_GBS, 4),
+                     "traffic": None if tr is None else round(tr)},
+        "tflops": round(cold["tflops"], 3), "alg_mbytes_per_step": round(cold["alg_mbytes"], 3),
+        "hot_ms_per_step": round(hot["ms_per_step"], 5), "input_copies": cold["input_copies"],
+        "steps_per_rep": steps,
+        "kernels": "decode_partial_kernel (streams the cache) + decode_combine_kernel",
+    }
+
+
 def bound_of(flops, nbytes, dt):
     ridge = PEAK_TFLOPS[dt] * 1e12 / (PEAK_HBM_GBS * 1e9)
     return "hbm" if flops / nbytes < ridge else "mfma"
@@ -169,8 +259,8 @@ def bound_of(flops, nbytes, dt):
 # HBM traffic from committed rocprofv3 counter summaries
 # ---------------------------------------------------------------------------
 
-def kernel_sha():
-    with open(KERNEL_SRC, "rb") as f:
+def kernel_sha(path=KERNEL_SRC):
+    with open(path, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()
 
 
@@ -182,7 +272,7 @@ def traffic_per_launch(name):
         return None
     with open(path) as f:
         t = json.load(f)
-    if t.get("kernel_sha256") != kernel_sha():
+    if t.get("kernel_sha256") != kernel_sha(DECODE_SRC if name == "decode" else KERNEL_SRC):
         return None
     return t["fetch_kib"] * 1024 * t["fetch_scale"] + t["write_kib"] * 1024 * t["write_scale"]
 
@@ -287,6 +377,19 @@ def oracle_report(per_workload_s=2.0):
             entry["bruteforce_s_per_row"] = (time.perf_counter() - t0) / nrows
             entry["bruteforce_rows"] = nrows
         rep[name] = {k: (round(v, 6) if isinstance(v, float) else v) for k, v in entry.items()}
+    # decode: per-row brute force (Eq. 3 and Eq. 4 key by key) on 8 rows
+    wd = workloads.DECODE_WORKLOADS["decode"]
+    xd = workloads.make_decode_inputs(wd)
+    lens = xd["cache_lens"].tolist()
+    t0 = time.perf_counter()
+    for r in range(8):
+        b, h = int(rng.integers(wd.batch)), int(rng.integers(wd.heads))
+        sl = lambda t: t[b:b + 1, h:h + 1]
+        oracle.relattn_decode(sl(xd["q"]), sl(xd["k"]), sl(xd["v"]), xd["key_table"][h:h + 1],
+                              xd["value_table"][h:h + 1], wd.clip, cache_lens=[lens[b]])
+    el = (time.perf_counter() - t0) / 8
+    rep["decode"] = {"bruteforce_s_per_row": round(el, 6), "bruteforce_rows": 8,
+                     "bruteforce_s_per_step": round(el * wd.batch * wd.heads * wd.tq, 3)}
     return rep
 
 
@@ -337,6 +440,8 @@ def main():
                     help="time the headline workload only (no per-workload table, no oracle report)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="time the decode workload only and print its figures")
     a = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if a.gpus != 1 or world != 1:
@@ -353,6 +458,9 @@ def main():
         build.build()
     if a.copy_calibration:
         copy_calibration()
+        return
+    if a.decode_only:
+        print(json.dumps({"decode": decode_report(ra, max(50, a.steps // 5))}))
         return
 
     if gpu is not None and not gpu.get("name"):
@@ -413,6 +521,7 @@ def main():
             e["steps_per_rep"] = k
             per[name] = e
         line["workloads"] = per
+        line["decode"] = decode_report(ra, max(50, a.steps // 5))
     if not a.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w)
         if not a.only:

@@ -15,10 +15,15 @@
 //       a lane issued before the first use); a dot product is summed over the
 //       LPR lanes of its row.  The raw logits of keys whose label holds them
 //       alone (offsets -k < j - i <= 0) are kept for the value term.
-//   decode_combine_kernel  one workgroup per query row, one thread per output
-//       column: m = max m_c, l = sum l_c 2^(m_c - m), O = sum O_c 2^(m_c - m);
-//       the value term adds 2^(e_j - m) a^V for each single-key label and the
-//       remaining weight l - sum of those for label -k; z = O / l.
+//   decode_combine_kernel  one workgroup per query row: m = max m_c,
+//       l = sum l_c 2^(m_c - m), O = sum O_c 2^(m_c - m); the value term adds
+//       2^(e_j - m) a^V for each single-key label and the remaining weight
+//       l - sum of those for label -k; z = O / l.  Chunk factors and label
+//       weights are computed in parallel and staged in LDS; the column sums
+//       are split over groups of threads so that their loads are independent.
+//       (A separate kernel: handing partial results from one workgroup to
+//       another inside one launch needs device-scope fences, which write back
+//       and invalidate the XCDs' L2 caches and cost far more than a launch.)
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
@@ -222,44 +227,91 @@ __global__ __launch_bounds__(kDecThreads) void decode_partial_kernel(const DecPa
   }
 }
 
+// Sum (or max) over the 256 threads of the workgroup; `slot` picks a private
+// group of LDS words so that consecutive reductions need no extra barrier.
+__device__ __forceinline__ float block_sum(float x, float* red, int slot) {
+  x = wave_sum(x);
+  if ((threadIdx.x & 63) == 0) red[4 * slot + (threadIdx.x >> 6)] = x;
+  __syncthreads();
+  return (red[4 * slot] + red[4 * slot + 1]) + (red[4 * slot + 2] + red[4 * slot + 3]);
+}
+__device__ __forceinline__ float block_max(float x, float* red, int slot) {
+  x = wave_max(x);
+  if ((threadIdx.x & 63) == 0) red[4 * slot + (threadIdx.x >> 6)] = x;
+  __syncthreads();
+  return fmaxf(fmaxf(red[4 * slot], red[4 * slot + 1]), fmaxf(red[4 * slot + 2], red[4 * slot + 3]));
+}
+
 template <int D, bool BF16, int MODE, bool HAS_WV>
-__global__ __launch_bounds__(128) void decode_combine_kernel(const DecParams p) {
+__global__ __launch_bounds__(kDecThreads) void decode_combine_kernel(const DecParams p) {
   using T = std::conditional_t<BF16, __bf16, float>;
   constexpr int CH = dec_chunk(BF16 ? 2 : 4, D);
-  const int row = blockIdx.x, dim = threadIdx.x;
-  if (dim >= D) return;
+  constexpr int NG = kDecThreads / D;  // column groups
+  constexpr int TILE = 1024;           // chunk factors / label weights staged at a time
+  __shared__ float s_f[TILE];
+  __shared__ float s_red[12];
+  __shared__ float s_o[kDecThreads];
+  const int row = blockIdx.x, tid = threadIdx.x;
+  const int dim = tid % D, grp = tid / D;
   const RowPos rp = row_pos(p, row);
   T* orow = reinterpret_cast<T*>(p.o) + rp.b * p.o_sb + rp.h * p.o_sh + rp.t * p.o_st;
-  if (rp.i < 0) {  // no visible key: zeros
-    orow[dim] = (T)0.f;
+  if (rp.i < 0) {  // no visible key: zeros (whole workgroup)
+    if (tid < D) orow[tid] = (T)0.f;
     return;
   }
   const int nchr = rp.i / CH + 1;  // chunks holding keys 0..i
   const float* ml = p.ws_ml + (int64_t)row * p.nch * 2;
   const float* po = p.ws_o + (int64_t)row * p.nch * D;
   float m = kNegInf;
-  for (int c = 0; c < nchr; ++c) m = fmaxf(m, ml[2 * c]);
+  for (int c = tid; c < nchr; c += kDecThreads) m = fmaxf(m, ml[2 * c]);
+  m = block_max(m, s_red, 0);
+  // l = sum l_c 2^(m_c - m); column `dim` of O summed over this group's chunks
   float l = 0.f, o = 0.f;
-  for (int c = 0; c < nchr; ++c) {
-    const float f = fast_exp2(ml[2 * c] - m);
-    l = fmaf(ml[2 * c + 1], f, l);
-    o = fmaf(po[c * D + dim], f, o);
+  for (int c0 = 0; c0 < nchr; c0 += TILE) {
+    const int nt = min(TILE, nchr - c0);
+    for (int x = tid; x < nt; x += kDecThreads) {
+      const float f = fast_exp2(ml[2 * (c0 + x)] - m);
+      s_f[x] = f;
+      l = fmaf(ml[2 * (c0 + x) + 1], f, l);
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int x = grp; x < nt; x += NG) o = fmaf(po[(int64_t)(c0 + x) * D + dim], s_f[x], o);
+    __syncthreads();
   }
+  l = block_sum(l, s_red, 1);
   if constexpr (MODE == kRelShaw && HAS_WV) {
     // labels -k+1 .. 0 hold one key each (when it exists); label -k (row 0)
     // holds every key at offset <= -k: what the row sum leaves
     const T* wv = reinterpret_cast<const T*>(p.wv) + rp.h * p.wv_sh;
     const float* band = p.ws_band + (int64_t)row * p.nband;
+    const int lo = max(1 - p.nband, -rp.i);  // lowest offset with a key
+    const int cnt = 1 - lo;
     float sb = 0.f;
-    for (int delta = max(1 - p.nband, -rp.i); delta <= 0; ++delta) {
-      const float w = fast_exp2(band[delta + p.nband - 1] - m);
-      sb += w;
-      o = fmaf(w, (float)wv[(delta + p.clip) * p.wv_sr + dim], o);
+    for (int t0 = 0; t0 < cnt; t0 += TILE) {
+      const int nt = min(TILE, cnt - t0);
+      for (int x = tid; x < nt; x += kDecThreads) {
+        const float w = fast_exp2(band[lo + t0 + x + p.nband - 1] - m);
+        s_f[x] = w;
+        sb += w;
+      }
+      __syncthreads();
+#pragma unroll 4
+      for (int x = grp; x < nt; x += NG)
+        o = fmaf(s_f[x], (float)wv[(int64_t)(lo + t0 + x + p.clip) * p.wv_sr + dim], o);
+      __syncthreads();
     }
-    const float tail = fmaxf(l - sb, 0.f);
-    o = fmaf(tail, (float)wv[dim], o);
+    sb = block_sum(sb, s_red, 2);
+    if (grp == 0) o = fmaf(fmaxf(l - sb, 0.f), (float)wv[dim], o);
   }
-  orow[dim] = (T)(o / l);
+  s_o[tid] = o;
+  __syncthreads();
+  if (tid < D) {
+    float z = 0.f;
+#pragma unroll
+    for (int g = 0; g < NG; ++g) z += s_o[g * D + tid];
+    orow[tid] = (T)(z / l);
+  }
 }
 
 template <int D, bool BF16, int MODE, bool HAS_WK, bool HAS_WV>
@@ -269,8 +321,8 @@ int launch_dec_t(const DecParams& p, hipStream_t s) {
                      dim3(kDecThreads), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return (int)e;
-  hipLaunchKernelGGL((decode_combine_kernel<D, BF16, MODE, HAS_WV>), dim3(rows), dim3(128), 0,
-                     s, p);
+  hipLaunchKernelGGL((decode_combine_kernel<D, BF16, MODE, HAS_WV>), dim3(rows),
+                     dim3(kDecThreads), 0, s, p);
   return (int)hipGetLastError();
 }
 
