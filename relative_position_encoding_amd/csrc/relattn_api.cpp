@@ -467,9 +467,18 @@ int make_dec_plan(const relattn_tensor* q, const relattn_tensor* k, const relatt
   const int64_t nband = (P.mode == relattn::kRelShaw && P.has_wv)
                             ? std::min<int64_t>(clip_k, std::max<int64_t>(L, 1))
                             : 0;
-  P.ws_o_off = align16((size_t)rows * nch * 2 * sizeof(float));
-  P.ws_band_off = P.ws_o_off + (size_t)rows * nch * d * sizeof(float);
-  P.ws_bytes = align16(P.ws_band_off + (size_t)rows * nband * sizeof(float));
+  // Split each row's cache over just enough workgroups to give the launch
+  // about kDecTargetWgs of them; a row held by one workgroup needs no
+  // partial results (and no workspace) when its single-key labels fit in LDS.
+  int64_t nsp = std::min<int64_t>(nch, (relattn::kDecTargetWgs + rows - 1) / rows);
+  const int64_t cps = (nch + nsp - 1) / nsp;
+  nsp = (nch + cps - 1) / cps;
+  const bool direct = nsp == 1 && nband <= relattn::kDirectBand;
+  if (!direct) {
+    P.ws_o_off = align16((size_t)rows * nsp * 2 * sizeof(float));
+    P.ws_band_off = P.ws_o_off + (size_t)rows * nsp * d * sizeof(float);
+    P.ws_bytes = align16(P.ws_band_off + (size_t)rows * nband * sizeof(float));
+  }
 
   relattn::DecParams& p = P.p;
   p.B = (int32_t)B;
@@ -479,6 +488,9 @@ int make_dec_plan(const relattn_tensor* q, const relattn_tensor* k, const relatt
   p.clip = is_t5 ? 0 : clip_k;
   p.nband = (int32_t)nband;
   p.nch = (int32_t)nch;
+  p.cps = (int32_t)cps;
+  p.nsp = (int32_t)nsp;
+  p.direct = direct ? 1 : 0;
   p.t5 = tb;
   const float s = scale > 0.f ? scale : (is_t5 ? 1.f : 1.f / std::sqrt((float)d));
   p.scale_log2 = s * 1.4426950408889634f;
@@ -607,7 +619,7 @@ int relattn_decode(const relattn_tensor* q, const relattn_tensor* k, const relat
   if (st) return st;
   if (cache_lens && (reinterpret_cast<uintptr_t>(cache_lens) & 3u))
     return fail(RELATTN_ERR_INVALID_ARGUMENT, "cache_lens is not 4-byte aligned");
-  if (!plan.empty) {
+  if (!plan.empty && plan.ws_bytes > 0) {
     if (workspace_bytes < plan.ws_bytes)
       return fail(RELATTN_ERR_INVALID_ARGUMENT, "workspace of %zu bytes, %zu needed",
                   workspace_bytes, plan.ws_bytes);

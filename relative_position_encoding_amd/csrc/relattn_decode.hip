@@ -35,6 +35,10 @@ namespace relattn {
 namespace {
 
 constexpr int kDecThreads = 256;
+// rows with at most this many splits and single-key labels take the combine
+// path that issues every load at once
+constexpr int kFastChunks = 8;
+constexpr int kFastLabels = 64;
 
 template <bool BF16>
 struct Frag;  // 16 bytes of a row
@@ -90,28 +94,38 @@ __device__ __forceinline__ RowPos row_pos(const DecParams& p, int row) {
   return r;
 }
 
-template <int D, bool BF16, int MODE, bool HAS_WK, bool HAS_WV>
-__global__ __launch_bounds__(kDecThreads) void decode_partial_kernel(const DecParams p) {
+template <int D, bool BF16, int MODE, bool HAS_WK, bool HAS_WV, bool DIRECT>
+__global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(4))) void decode_kernel(
+    const DecParams p) {
   using V = typename Frag<BF16>::V;
+  using T = std::conditional_t<BF16, __bf16, float>;
   constexpr int EPL = Frag<BF16>::N;           // elements per 16-byte load
   constexpr int LPR = D / EPL;                 // lanes per row
   constexpr int RPP = kDecThreads / LPR;       // rows per pass
   constexpr int CH = dec_chunk(BF16 ? 2 : 4, D);
   constexpr int NP = CH / RPP;                 // passes (8)
+  constexpr int NG = kDecThreads / D;          // column groups of the value term
   static_assert(LPR >= 1 && LPR <= 64 && NP * RPP == CH, "chunk geometry");
   constexpr bool SHAW = MODE == kRelShaw;
   constexpr bool T5 = MODE == kRelT5;
+  constexpr bool VT = SHAW && HAS_WV;
   __shared__ float s_e[CH];
   __shared__ float s_red[8];
   __shared__ float s_acc[RPP * D];
+  __shared__ float s_band[DIRECT && VT ? kDirectBand : 1];
 
-  const int row = blockIdx.x, chunk = blockIdx.y;
+  const int row = blockIdx.x, split = blockIdx.y;
   const RowPos rp = row_pos(p, row);
   const int i = rp.i, b = rp.b, h = rp.h;
-  const int j0 = chunk * CH;
-  if (i < 0 || j0 > i) return;  // no visible key in this chunk (whole workgroup)
-  const int j1 = min(j0 + CH, i + 1);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (i < 0) {  // no visible key: zeros (written here when this workgroup owns the row)
+    if (DIRECT && tid < D)
+      reinterpret_cast<T*>(p.o)[b * p.o_sb + h * p.o_sh + rp.t * p.o_st + tid] = (T)0.f;
+    return;
+  }
+  // this workgroup's chunks of the row (the same for the whole workgroup)
+  const int cb = split * p.cps, ce = min(cb + p.cps, i / CH + 1);
+  if (cb >= ce) return;
   const int part = tid % LPR, rs = tid / LPR;
   const int c0 = part * EPL;  // first column of this lane's fragment
 
@@ -123,20 +137,6 @@ __global__ __launch_bounds__(kDecThreads) void decode_partial_kernel(const DecPa
   }
   const int64_t kb = b * p.k_sb + h * p.k_sh, vb = b * p.v_sb + h * p.v_sh;
 
-  // every K and V fragment of this lane, requested before the first use; rows
-  // past the last visible key read that key again (finite, weighted 0)
-  V kf[NP], vf[NP];
-#pragma unroll
-  for (int it = 0; it < NP; ++it) {
-    const int j = min(j0 + rs + it * RPP, j1 - 1);
-    kf[it] = load_frag<BF16>(p.k, kb + j * p.k_sn + c0);
-  }
-#pragma unroll
-  for (int it = 0; it < NP; ++it) {
-    const int j = min(j0 + rs + it * RPP, j1 - 1);
-    vf[it] = load_frag<BF16>(p.v, vb + j * p.v_sn + c0);
-  }
-
   // relative logit of every key at offset <= -k (label row 0)
   float far = 0.f;
   if constexpr (SHAW && HAS_WK) {
@@ -147,83 +147,144 @@ __global__ __launch_bounds__(kDecThreads) void decode_partial_kernel(const DecPa
     far = group_sum<LPR>(d0) * p.scale_log2;
   }
 
-  // logits, log2 units
-#pragma unroll
-  for (int it = 0; it < NP; ++it) {
-    const int r = rs + it * RPP;
-    const bool valid = j0 + r < j1;
-    const int j = min(j0 + r, j1 - 1);
-    const int delta = j - i;  // <= 0
-    float x[EPL];
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) x[e] = (float)kf[it][e];
-    float rel = 0.f;
-    if constexpr (SHAW && HAS_WK) {
-      if (delta > -p.clip) {
-        // inside the window: a^K of this key's own label joins k_j (Eq. 4)
-        const V w = load_frag<BF16>(p.wk, h * p.wk_sh + (delta + p.clip) * p.wk_sr + c0);
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) x[e] += (float)w[e];
-      } else {
-        rel = far;
-      }
-    }
-    if constexpr (T5) rel = kLog2e * p.t5_bias[t5_bucket(delta, p.t5) * p.tb_sb + h * p.tb_sh];
-    float dot = 0.f;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) dot = fmaf(qf[e], x[e], dot);
-    dot = group_sum<LPR>(dot);
-    const float lg = valid ? fmaf(dot, p.scale_log2, rel) : kNegInf;
-    if (part == 0) {
-      s_e[r] = lg;
-      if constexpr (SHAW && HAS_WV) {
-        if (valid && delta > -p.clip) p.ws_band[(int64_t)row * p.nband + delta + p.nband - 1] = lg;
-      }
-    }
-  }
-  __syncthreads();
-
-  // chunk max and sum of 2^(e - m)
-  float m = kNegInf;
-  for (int x = tid; x < CH; x += kDecThreads) m = fmaxf(m, s_e[x]);
-  m = wave_max(m);
-  if (lane == 0) s_red[wave] = m;
-  __syncthreads();
-  m = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
-  float l = 0.f;
-  for (int x = tid; x < CH; x += kDecThreads) {
-    const float pv = fast_exp2(s_e[x] - m);  // 0 for the rows past the last key
-    s_e[x] = pv;
-    l += pv;
-  }
-  l = wave_sum(l);
-  if (lane == 0) s_red[4 + wave] = l;
-  __syncthreads();
-  l = (s_red[4] + s_red[5]) + (s_red[6] + s_red[7]);
-
-  // partial output: each lane sums its columns over its rows, then the row
-  // groups are summed through LDS
+  // online softmax over the chunks: running max and sum, this lane's columns
+  float m_run = kNegInf, l_run = 0.f;
   float acc[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
+  for (int c = cb; c < ce; ++c) {
+    const int j0 = c * CH, j1 = min(j0 + CH, i + 1);
+    // every K and V fragment of this lane for the chunk, requested before the
+    // first use; rows past the last visible key read that key again (finite,
+    // weighted 0)
+    V kf[NP], vf[NP];
 #pragma unroll
-  for (int it = 0; it < NP; ++it) {
-    const float pv = s_e[rs + it * RPP];
+    for (int it = 0; it < NP; ++it) {
+      const int j = min(j0 + rs + it * RPP, j1 - 1);
+      kf[it] = load_frag<BF16>(p.k, kb + j * p.k_sn + c0);
+    }
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[e] = fmaf(pv, (float)vf[it][e], acc[e]);
+    for (int it = 0; it < NP; ++it) {
+      const int j = min(j0 + rs + it * RPP, j1 - 1);
+      vf[it] = load_frag<BF16>(p.v, vb + j * p.v_sn + c0);
+    }
+    // logits, log2 units
+#pragma unroll
+    for (int it = 0; it < NP; ++it) {
+      const int r = rs + it * RPP;
+      const bool valid = j0 + r < j1;
+      const int j = min(j0 + r, j1 - 1);
+      const int delta = j - i;  // <= 0
+      float x[EPL];
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) x[e] = (float)kf[it][e];
+      float rel = 0.f;
+      if constexpr (SHAW && HAS_WK) {
+        if (delta > -p.clip) {
+          // inside the window: a^K of this key's own label joins k_j (Eq. 4)
+          const V w = load_frag<BF16>(p.wk, h * p.wk_sh + (delta + p.clip) * p.wk_sr + c0);
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) x[e] += (float)w[e];
+        } else {
+          rel = far;
+        }
+      }
+      if constexpr (T5) rel = kLog2e * p.t5_bias[t5_bucket(delta, p.t5) * p.tb_sb + h * p.tb_sh];
+      float dot = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) dot = fmaf(qf[e], x[e], dot);
+      dot = group_sum<LPR>(dot);
+      const float lg = valid ? fmaf(dot, p.scale_log2, rel) : kNegInf;
+      if (part == 0) {
+        s_e[r] = lg;
+        if constexpr (VT) {
+          if (valid && delta > -p.clip) {
+            if constexpr (DIRECT) s_band[delta + p.nband - 1] = lg;
+            else p.ws_band[(int64_t)row * p.nband + delta + p.nband - 1] = lg;
+          }
+        }
+      }
+    }
+    __syncthreads();
+    // chunk max; the running state then moves to the new max
+    float mc = kNegInf;
+    for (int x = tid; x < CH; x += kDecThreads) mc = fmaxf(mc, s_e[x]);
+    mc = wave_max(mc);
+    if (lane == 0) s_red[wave] = mc;
+    __syncthreads();
+    const float m_new = fmaxf(m_run, fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3])));
+    const float sc = fast_exp2(m_run - m_new);  // 0 before the first chunk
+    float lc = 0.f;
+    for (int x = tid; x < CH; x += kDecThreads) {
+      const float pv = fast_exp2(s_e[x] - m_new);  // 0 for the rows past the last key
+      s_e[x] = pv;
+      lc += pv;
+    }
+    lc = wave_sum(lc);
+    if (lane == 0) s_red[4 + wave] = lc;
+    __syncthreads();
+    l_run = fmaf(l_run, sc, (s_red[4] + s_red[5]) + (s_red[6] + s_red[7]));
+    m_run = m_new;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[e] *= sc;
+#pragma unroll
+    for (int it = 0; it < NP; ++it) {
+      const float pv = s_e[rs + it * RPP];
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[e] = fmaf(pv, (float)vf[it][e], acc[e]);
+    }
+    __syncthreads();  // s_e and s_red are rewritten by the next chunk
   }
+
+  // this workgroup's output columns: the lanes' sums over their rows, summed
+  // over the row groups through LDS
 #pragma unroll
   for (int e = 0; e < EPL; ++e) s_acc[rs * D + c0 + e] = acc[e];
   __syncthreads();
-  const int64_t slot = (int64_t)row * p.nch + chunk;
-  for (int dim = tid; dim < D; dim += kDecThreads) {
+  if constexpr (!DIRECT) {
+    const int64_t slot = (int64_t)row * p.nsp + split;
+    for (int dim = tid; dim < D; dim += kDecThreads) {
+      float o = 0.f;
+      for (int g = 0; g < RPP; ++g) o += s_acc[g * D + dim];
+      p.ws_o[slot * D + dim] = o;
+    }
+    if (tid == 0) {
+      p.ws_ml[2 * slot] = m_run;
+      p.ws_ml[2 * slot + 1] = l_run;
+    }
+  } else {
+    // The workgroup holds the whole row: value term and output here.  Thread
+    // (dim, grp) sums column dim over the row groups grp, grp + NG, ... and
+    // over the single-key labels grp, grp + NG, ...
+    const int dim = tid % D, grp = tid / D;
     float o = 0.f;
-    for (int g = 0; g < RPP; ++g) o += s_acc[g * D + dim];
-    p.ws_o[slot * D + dim] = o;
-  }
-  if (tid == 0) {
-    p.ws_ml[2 * slot] = m;
-    p.ws_ml[2 * slot + 1] = l;
+    for (int g = grp; g < RPP; g += NG) o += s_acc[g * D + dim];
+    float sbp = 0.f;  // this group's share of the single-key weights
+    float w0 = 0.f;
+    if constexpr (VT) {
+      const T* wvh = reinterpret_cast<const T*>(p.wv) + h * p.wv_sh;
+      const int lo = max(1 - p.nband, -i);  // lowest offset with a key
+      for (int x = grp; x < 1 - lo; x += NG) {
+        const float w = fast_exp2(s_band[lo + x + p.nband - 1] - m_run);
+        sbp += w;
+        o = fmaf(w, (float)wvh[(lo + x + p.clip) * p.wv_sr + dim], o);
+      }
+      w0 = (float)wvh[dim];  // label -k
+    }
+    __syncthreads();  // s_acc and s_e are reused for the group sums
+    s_acc[tid] = o;
+    if (dim == 0) s_e[grp] = sbp;
+    __syncthreads();
+    if (tid < D) {
+      float z = 0.f, sb = 0.f;
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        z += s_acc[g * D + tid];
+        sb += s_e[g];
+      }
+      if constexpr (VT) z = fmaf(fmaxf(l_run - sb, 0.f), w0, z);
+      reinterpret_cast<T*>(p.o)[b * p.o_sb + h * p.o_sh + rp.t * p.o_st + tid] = (T)(z / l_run);
+    }
   }
 }
 
@@ -248,20 +309,110 @@ __global__ __launch_bounds__(kDecThreads) void decode_combine_kernel(const DecPa
   constexpr int CH = dec_chunk(BF16 ? 2 : 4, D);
   constexpr int NG = kDecThreads / D;  // column groups
   constexpr int TILE = 1024;           // chunk factors / label weights staged at a time
+  constexpr bool VT = MODE == kRelShaw && HAS_WV;
   __shared__ float s_f[TILE];
   __shared__ float s_red[12];
   __shared__ float s_o[kDecThreads];
   const int row = blockIdx.x, tid = threadIdx.x;
   const int dim = tid % D, grp = tid / D;
+  const float* ml = p.ws_ml + (int64_t)row * p.nsp * 2;
+  const float* po = p.ws_o + (int64_t)row * p.nsp * D;
+  const T* wv = reinterpret_cast<const T*>(p.wv);
+  const float* band = p.ws_band + (int64_t)row * p.nband;
+
+  if (p.nsp <= kFastChunks && p.nband <= kFastLabels) {
+    // Few chunks and labels (the usual decoding step).  Every address below
+    // depends on the launch parameters only, so all loads, the key length's
+    // included, are in flight together: the row costs one memory round trip.
+    // Slots past the row's position are masked afterwards.  Each thread
+    // derives the row max and sum from all chunk scalars itself; the column
+    // sums and the single-key weights are summed over the thread groups
+    // (group g takes chunks and labels g, g + NG, ...).
+    constexpr int UC = (kFastChunks + NG - 1) / NG, UL = (kFastLabels + NG - 1) / NG;
+    const int t = row % p.Tq, bh = row / p.Tq;
+    const int b = bh / p.H, h = bh - b * p.H;
+    const int len_raw = p.cache_lens ? p.cache_lens[b] : p.L;
+    float mlv[2 * kFastChunks], pov[UC], pmv[UC], blv[UL], wvv[UL];
+    float w0 = 0.f;
+#pragma unroll
+    for (int c = 0; c < kFastChunks; ++c) {
+      mlv[2 * c] = c < p.nsp ? ml[2 * c] : kNegInf;
+      mlv[2 * c + 1] = c < p.nsp ? ml[2 * c + 1] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < UC; ++u) {
+      const int c = grp + u * NG;
+      pov[u] = c < p.nsp ? po[c * D + dim] : 0.f;
+      pmv[u] = c < p.nsp ? ml[2 * c] : kNegInf;  // (indexing mlv by grp would spill)
+    }
+    if constexpr (VT) {
+      // label slot x holds offset x + 1 - nband (labels -k+1 .. 0)
+      const T* wvh = wv + h * p.wv_sh;
+#pragma unroll
+      for (int u = 0; u < UL; ++u) {
+        const int x = grp + u * NG;
+        blv[u] = x < p.nband ? band[x] : kNegInf;
+        wvv[u] = x < p.nband ? (float)wvh[(x + 1 - p.nband + p.clip) * p.wv_sr + dim] : 0.f;
+      }
+      w0 = (float)wvh[dim];  // label -k
+    }
+    T* orow = reinterpret_cast<T*>(p.o) + b * p.o_sb + h * p.o_sh + t * p.o_st;
+    const int i = min(max(len_raw, 0), p.L) - p.Tq + t;  // this query's position
+    if (i < 0) {  // no visible key: zeros (whole workgroup)
+      if (tid < D) orow[tid] = (T)0.f;
+      return;
+    }
+    const int nchr = i / CH / p.cps + 1;  // splits holding keys 0..i
+    float m = kNegInf;
+#pragma unroll
+    for (int c = 0; c < kFastChunks; ++c)
+      if (c < nchr) m = fmaxf(m, mlv[2 * c]);
+    float l = 0.f, o = 0.f;
+#pragma unroll
+    for (int c = 0; c < kFastChunks; ++c)
+      if (c < nchr) l = fmaf(mlv[2 * c + 1], fast_exp2(mlv[2 * c] - m), l);
+#pragma unroll
+    for (int u = 0; u < UC; ++u) {
+      const int c = grp + u * NG;
+      if (c < nchr) o = fmaf(pov[u], fast_exp2(pmv[u] - m), o);
+    }
+    float sbp = 0.f;  // this group's share of the single-key weights
+    if constexpr (VT) {
+#pragma unroll
+      for (int u = 0; u < UL; ++u) {
+        const int x = grp + u * NG;
+        if (x < p.nband && x + 1 - p.nband >= -i) {  // the key at that offset exists
+          const float w = fast_exp2(blv[u] - m);
+          sbp += w;
+          o = fmaf(w, wvv[u], o);
+        }
+      }
+    }
+    s_o[tid] = o;
+    if (dim == 0) s_f[grp] = sbp;
+    __syncthreads();
+    if (tid < D) {
+      float z = 0.f, sb = 0.f;
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        z += s_o[g * D + tid];
+        sb += s_f[g];
+      }
+      if constexpr (VT) z = fmaf(fmaxf(l - sb, 0.f), w0, z);
+      orow[tid] = (T)(z / l);
+    }
+    return;
+  }
+
   const RowPos rp = row_pos(p, row);
   T* orow = reinterpret_cast<T*>(p.o) + rp.b * p.o_sb + rp.h * p.o_sh + rp.t * p.o_st;
   if (rp.i < 0) {  // no visible key: zeros (whole workgroup)
     if (tid < D) orow[tid] = (T)0.f;
     return;
   }
-  const int nchr = rp.i / CH + 1;  // chunks holding keys 0..i
-  const float* ml = p.ws_ml + (int64_t)row * p.nch * 2;
-  const float* po = p.ws_o + (int64_t)row * p.nch * D;
+  const int nchr = rp.i / CH / p.cps + 1;  // splits holding keys 0..i
+  const int lo = VT ? max(1 - p.nband, -rp.i) : 1;  // lowest offset with a single-key label
+  const int cnt = 1 - lo;                             // single-key labels with a key
   float m = kNegInf;
   for (int c = tid; c < nchr; c += kDecThreads) m = fmaxf(m, ml[2 * c]);
   m = block_max(m, s_red, 0);
@@ -283,10 +434,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_combine_kernel(const DecPa
   if constexpr (MODE == kRelShaw && HAS_WV) {
     // labels -k+1 .. 0 hold one key each (when it exists); label -k (row 0)
     // holds every key at offset <= -k: what the row sum leaves
-    const T* wv = reinterpret_cast<const T*>(p.wv) + rp.h * p.wv_sh;
-    const float* band = p.ws_band + (int64_t)row * p.nband;
-    const int lo = max(1 - p.nband, -rp.i);  // lowest offset with a key
-    const int cnt = 1 - lo;
+    const T* wvh = wv + rp.h * p.wv_sh;
     float sb = 0.f;
     for (int t0 = 0; t0 < cnt; t0 += TILE) {
       const int nt = min(TILE, cnt - t0);
@@ -298,11 +446,11 @@ __global__ __launch_bounds__(kDecThreads) void decode_combine_kernel(const DecPa
       __syncthreads();
 #pragma unroll 4
       for (int x = grp; x < nt; x += NG)
-        o = fmaf(s_f[x], (float)wv[(int64_t)(lo + t0 + x + p.clip) * p.wv_sr + dim], o);
+        o = fmaf(s_f[x], (float)wvh[(int64_t)(lo + t0 + x + p.clip) * p.wv_sr + dim], o);
       __syncthreads();
     }
     sb = block_sum(sb, s_red, 2);
-    if (grp == 0) o = fmaf(fmaxf(l - sb, 0.f), (float)wv[dim], o);
+    if (grp == 0) o = fmaf(fmaxf(l - sb, 0.f), (float)wvh[dim], o);
   }
   s_o[tid] = o;
   __syncthreads();
@@ -317,7 +465,12 @@ __global__ __launch_bounds__(kDecThreads) void decode_combine_kernel(const DecPa
 template <int D, bool BF16, int MODE, bool HAS_WK, bool HAS_WV>
 int launch_dec_t(const DecParams& p, hipStream_t s) {
   const int rows = p.B * p.H * p.Tq;
-  hipLaunchKernelGGL((decode_partial_kernel<D, BF16, MODE, HAS_WK, HAS_WV>), dim3(rows, p.nch),
+  if (p.direct) {
+    hipLaunchKernelGGL((decode_kernel<D, BF16, MODE, HAS_WK, HAS_WV, true>), dim3(rows, 1),
+                       dim3(kDecThreads), 0, s, p);
+    return (int)hipGetLastError();
+  }
+  hipLaunchKernelGGL((decode_kernel<D, BF16, MODE, HAS_WK, HAS_WV, false>), dim3(rows, p.nsp),
                      dim3(kDecThreads), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return (int)e;

@@ -81,9 +81,14 @@ int launch_debug_indices(int n, int clip, const T5Buckets* t5, int32_t* out,
 
 // ---- incremental decoding (relattn_decode.hip) ----------------------------
 
-// Keys of the cache one decode workgroup covers: 32 KB of K rows, i.e. eight
-// 16-byte loads of K (and of V) per lane of a 256-thread workgroup.
+// Keys of the cache one decode workgroup streams per step of its loop: 32 KB
+// of K rows, i.e. eight 16-byte loads of K (and of V) per lane of a
+// 256-thread workgroup.
 constexpr int dec_chunk(int elem_bytes, int d) { return 32768 / (elem_bytes * d); }
+// Workgroups a decode launch aims for (four per compute unit), and the most
+// single-key labels a workgroup that owns a whole row keeps in LDS.
+constexpr int kDecTargetWgs = 1024;
+constexpr int kDirectBand = 1024;
 
 // Everything a decode launch needs.  Query t of batch b sits at position
 // cache_lens[b] - Tq + t of its sequence.  Strides count elements.  The
@@ -114,7 +119,11 @@ struct DecParams {
   int32_t B, H, Tq, L;  // L = rows of the cache
   int32_t clip;
   int32_t nband;        // min(clip, L) with a value table, else 0
-  int32_t nch;          // chunks per query row: ceil(L / kDecChunk)
+  int32_t nch;          // chunks per query row: ceil(L / dec_chunk)
+  int32_t cps;          // chunks per split: one workgroup streams a split
+  int32_t nsp;          // splits per query row: ceil(nch / cps)
+  int32_t direct;       // nsp == 1 and the row's single-key labels fit in LDS:
+                        // one workgroup per row writes the output itself
   float scale_log2;
   T5Buckets t5;
 };

@@ -199,3 +199,42 @@ def test_decode_workload_sampled_rows(ra):
                                      x["key_table"][h:h + 1], x["value_table"][h:h + 1],
                                      w.clip, cache_lens=[lens[b]])
         assert maxerr(got[b, h], want[0, 0]) <= 2e-2, (b, h)
+
+
+@pytest.mark.parametrize("dtype,d,tables", [(torch.bfloat16, 64, "kv"), (torch.bfloat16, 128, "kv"),
+                                             (torch.float32, 32, "k"), (torch.bfloat16, 16, "v")])
+def test_decode_rows_own_workgroup(ra, dtype, d, tables):
+    """At least 1024 query rows: each row's whole cache is streamed by one
+    workgroup, which writes the output itself (no partial results); sampled
+    rows against the oracle, including empty and one-key caches."""
+    B, H, Tq, L, c = 32, 16, 2, 3 * chunk(dtype, d) // 2 + 5, 9
+    q, k, v, wK, wV = gen(B, H, Tq, L, d, dtype, 1000 + d, c)
+    wK = wK if tables in ("kv", "k") else None
+    wV = wV if tables in ("kv", "v") else None
+    lens = [L - (7 * b) % L for b in range(B)]
+    lens[3], lens[5], lens[6] = 0, 1, 2
+    assert ra.decode_workspace_size(dev(q), dev(k), dev(v), dev(wK), dev(wV), clip=c) == 0
+    got = run(ra, q, k, v, wK, wV, c, lens)
+    for b in [0, 3, 5, 6, 17, 31]:
+        for h in [0, 15]:
+            sl = lambda t: t[b:b + 1, h:h + 1]
+            want = oracle.relattn_decode(sl(q), sl(k), sl(v),
+                                         None if wK is None else wK[h:h + 1],
+                                         None if wV is None else wV[h:h + 1], c,
+                                         cache_lens=[lens[b]])
+            assert maxerr(got[b, h], want[0, 0]) <= TOL[dtype], (b, h)
+
+
+def test_decode_splits_of_several_chunks(ra):
+    """256 query rows over a long cache: each workgroup streams a split of two
+    chunks with the online softmax across them before the combine."""
+    B, H, L, d, c = 16, 16, 2048 + 40, 64, 16
+    q, k, v, wK, wV = gen(B, H, 1, L, d, torch.bfloat16, 1100, c)
+    lens = [L - 97 * b for b in range(B)]
+    got = run(ra, q, k, v, wK, wV, c, lens)
+    for b in [0, 7, 15]:
+        for h in [0, 9]:
+            sl = lambda t: t[b:b + 1, h:h + 1]
+            want = oracle.relattn_decode(sl(q), sl(k), sl(v), wK[h:h + 1], wV[h:h + 1], c,
+                                         cache_lens=[lens[b]])
+            assert maxerr(got[b, h], want[0, 0]) <= 2e-2, (b, h)
