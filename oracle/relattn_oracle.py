@@ -56,6 +56,7 @@ __all__ = [
     "t5_rows",
     "relattn_decode",
     "t5_decode",
+    "offset_bias_attention",
     "to_f64",
 ]
 
@@ -426,4 +427,36 @@ def t5_decode(q, k, v, bias, num_buckets: int = 32, max_distance: int = 128,
                               for j in range(i + 1)])
                 w = np.exp(e - e.max())
                 z[b, h, t] = (w / w.sum()) @ v[b, h, :i + 1]
+    return z
+
+
+# ---------------------------------------------------------------------------
+# Scalar bias by clipped offset (survey page "Relative position embeddings",
+# section "Placement in the taxonomy": the T5 bias with its bucket table
+# replaced by a function of the offset, -m_h |delta| giving ALiBi)
+# ---------------------------------------------------------------------------
+
+def offset_bias_attention(q, k, v, bias, window: int, scale=None, causal: bool = False,
+                          key_lens=None):
+    """A_ij = scale * q_i.k_j + bias[h', clip(j - i, window) + window], softmax,
+    z_i = sum_j alpha_ij v_j.
+
+    bias: [Hb, 2*window + 1] with Hb in {1, H} (Hb == 1: one row for every
+    head); entry window + delta holds offset delta; offsets beyond +-window
+    take the end entries (the clip of the tables of Shaw et al.).  scale
+    defaults to 1/sqrt(d), the attention this bias is added to.
+    """
+    q, k, v = to_f64(q), to_f64(k), to_f64(v)
+    bias = to_f64(bias)
+    B, H, n, d = q.shape
+    s = _default_scale(d, scale)
+    lens = _key_lengths(key_lens, B, n)
+    R = relative_labels(n, window) + window  # n x n entry index
+    z = np.zeros((B, H, n, v.shape[-1]))
+    for b in range(B):
+        ok = visible(n, causal, lens[b])
+        for h in range(H):
+            row = bias[0 if bias.shape[0] == 1 else h]
+            e = s * (q[b, h] @ k[b, h].T) + row[R]
+            z[b, h] = _masked_softmax_rows(e, ok) @ v[b, h]
     return z

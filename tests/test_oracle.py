@@ -501,3 +501,63 @@ def test_decode_two_keys_closed_form():
     want = a0 * (v[0, 0, 0] + wV[0, 0]) + (1 - a0) * (v[0, 0, 1] + wV[0, 1])
     z = oracle.relattn_decode(q, k, v, wK, wV, c, cache_lens=[2])
     np.testing.assert_allclose(z[0, 0, 0], want, rtol=0, atol=1e-14)
+
+
+# ---------------------------------------------------------------------------
+# scalar bias by clipped offset (survey page "Relative position embeddings",
+# section "Placement in the taxonomy")
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("bidir", [True, False])
+@pytest.mark.parametrize("causal,lens", [(False, None), (True, None), (False, [9, 30])])
+def test_offset_bias_from_t5_buckets_equals_t5(bidir, causal, lens):
+    """A table filled with the T5 bias of each offset's bucket (window large
+    enough to cover every offset) gives the T5 attention, scale 1."""
+    B, H, n, d = 2, 3, 30, 8
+    q, k, v = rnd((B, H, n, d), 90), rnd((B, H, n, d), 91), rnd((B, H, n, d), 92)
+    t5b = rnd((32, H), 93)
+    W = n - 1
+    table = np.array([[t5b[oracle.t5_bucket(x, 32, 16, bidir), h] for x in range(-W, W + 1)]
+                      for h in range(H)])
+    z = oracle.offset_bias_attention(q, k, v, table, W, scale=1.0, causal=causal, key_lens=lens)
+    want = oracle.t5_attention(q, k, v, t5b, 32, 16, bidir, causal=causal, key_lens=lens)
+    np.testing.assert_allclose(z, want, rtol=0, atol=1e-12)
+
+
+def test_offset_bias_constant_is_textbook():
+    """A bias equal for every offset cancels in the softmax: textbook scaled
+    attention (library routine)."""
+    B, H, n, d = 1, 2, 12, 8
+    q, k, v = rnd((B, H, n, d), 94), rnd((B, H, n, d), 95), rnd((B, H, n, d), 96)
+    table = np.full((1, 9), 3.7)
+    z = oracle.offset_bias_attention(q, k, v, table, 4)
+    ok = np.ones((n, n), dtype=bool)
+    np.testing.assert_allclose(z, sdpa(q, k, v, ok, 1 / math.sqrt(d)), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("offset", [-3, 0, 2])
+def test_offset_bias_one_hot_probe(offset):
+    """A large bias at one offset makes each query attend to the key at that
+    offset (j = i + offset) when it exists: the sign and centring of the
+    table index."""
+    n, d, W = 8, 4, 5
+    q, k, v = rnd((1, 1, n, d), 97, 0.01), rnd((1, 1, n, d), 98, 0.01), rnd((1, 1, n, d), 99)
+    table = np.zeros((1, 2 * W + 1))
+    table[0, W + offset] = 60.0
+    z = oracle.offset_bias_attention(q, k, v, table, W)
+    for i in range(n):
+        if 0 <= i + offset < n:
+            np.testing.assert_allclose(z[0, 0, i], v[0, 0, i + offset], atol=1e-9)
+
+
+def test_alibi_window_clips_to_end_entries():
+    """ALiBi (-m |delta|) with window w: offsets beyond w take the bias of w,
+    which equals ALiBi with the distance capped at w."""
+    B, H, n, d, w = 1, 2, 16, 8, 5
+    q, k, v = rnd((B, H, n, d), 100), rnd((B, H, n, d), 101), rnd((B, H, n, d), 102)
+    slopes = [0.5, 0.125]
+    table = np.array([[-m * abs(x) for x in range(-w, w + 1)] for m in slopes])
+    big = np.array([[-m * min(abs(x), w) for x in range(-(n - 1), n)] for m in slopes])
+    z = oracle.offset_bias_attention(q, k, v, table, w, causal=True)
+    z2 = oracle.offset_bias_attention(q, k, v, big, n - 1, causal=True)
+    np.testing.assert_allclose(z, z2, rtol=0, atol=1e-12)
