@@ -128,6 +128,36 @@ int relattn_debug_indices(int32_t n, int32_t clip_k, const relattn_t5_params* t5
                           int32_t* out_dev, void* stream);
 
 /*
+ * relattn_fwd_offset_bias: attention with a scalar bias by clipped offset, the
+ * T5 bias with its bucket table replaced by a function of the offset (survey
+ * page "Relative position embeddings", section "Placement in the taxonomy";
+ * ALiBi is bias[h, window + delta] = -m_h * |delta|):
+ *
+ *       e_ij = scale * q_i . k_j + bias[h', clip(j - i, window) + window]
+ *
+ *   q, k, v, out : as for relattn_fwd.
+ *   bias         : [Hb, 2*window + 1] F32, Hb = H (one row per head) or 1
+ *                  (shared); entry window + delta holds offset delta, and
+ *                  offsets beyond +-window take the end entries.
+ *   window       : >= 0.
+ *   scale        : logit scale; <= 0 picks 1/sqrt(d).
+ *   mask, stream : as for relattn_fwd.
+ * Errors as for relattn_fwd; UNSUPPORTED when the window clipped to n - 1 does
+ * not fit on chip (2*min(window, n-1)+1 entries).  No value term.
+ */
+int relattn_fwd_offset_bias(const relattn_tensor* q, const relattn_tensor* k,
+                            const relattn_tensor* v, const relattn_tensor* bias,
+                            int32_t window, float scale, const relattn_mask* mask,
+                            relattn_tensor* out, void* stream);
+
+/* relattn_validate_offset_bias: the argument checks of relattn_fwd_offset_bias,
+ * host only (no HIP call). */
+int relattn_validate_offset_bias(const relattn_tensor* q, const relattn_tensor* k,
+                                 const relattn_tensor* v, const relattn_tensor* bias,
+                                 int32_t window, float scale, const relattn_mask* mask,
+                                 const relattn_tensor* out);
+
+/*
  * relattn_decode: incremental decoding.  The newest Tq positions of each
  * sequence attend over its key/value cache with the causal mask; each output
  * row is the row relattn_fwd would compute for that position with causal = 1

@@ -10,7 +10,8 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["fwd", "validate", "decode", "decode_workspace_size", "debug_indices",
+__all__ = ["fwd", "validate", "fwd_offset_bias", "validate_offset_bias", "decode",
+           "decode_workspace_size", "debug_indices",
            "RelattnError", "library_path",
            "OK", "INVALID_ARGUMENT", "UNSUPPORTED", "NO_DEVICE", "LAUNCH_FAILED"]
 
@@ -66,6 +67,12 @@ def _load():
     lib.relattn_decode.restype = ctypes.c_int
     lib.relattn_decode_workspace_size.argtypes = dec + [P(_Tensor), P(ctypes.c_size_t)]
     lib.relattn_decode_workspace_size.restype = ctypes.c_int
+    ob = [P(_Tensor), P(_Tensor), P(_Tensor), P(_Tensor), ctypes.c_int32, ctypes.c_float,
+          P(_Mask), P(_Tensor)]
+    lib.relattn_fwd_offset_bias.argtypes = ob + [ctypes.c_void_p]
+    lib.relattn_fwd_offset_bias.restype = ctypes.c_int
+    lib.relattn_validate_offset_bias.argtypes = ob
+    lib.relattn_validate_offset_bias.restype = ctypes.c_int
     lib.relattn_debug_indices.argtypes = [ctypes.c_int32, ctypes.c_int32, P(_T5),
                                           ctypes.c_void_p, ctypes.c_void_p]
     lib.relattn_debug_indices.restype = ctypes.c_int
@@ -261,3 +268,47 @@ def decode(q, k, v, wK=None, wV=None, *, clip=0, cache_lens=None, t5_bias=None,
     if st != OK:
         _raise(lib, st)
     return out
+
+
+def _ob_args(q, k, v, bias, window, causal, key_lens, scale, out):
+    views = [_view(x) for x in (q, k, v, bias)]
+    mask = None
+    if causal or key_lens is not None:
+        mask = _Mask(1 if causal else 0, key_lens.data_ptr() if key_lens is not None else None)
+    outv = _view(out)
+    args = [_ref(x) for x in views] + [int(window), float(0.0 if scale is None else scale),
+                                        _ref(mask), _ref(outv)]
+    return args, views + [mask, outv]
+
+
+def fwd_offset_bias(q, k, v, bias, window, *, causal=False, key_lens=None, scale=None,
+                    out=None, stream=None):
+    """Attention with a scalar bias by clipped offset: bias [H or 1, 2*window+1]
+    float32, entry window + delta for offset delta = j - i (ALiBi:
+    -m_h * |delta|).  Other arguments as for ``fwd``; returns ``out``."""
+    import torch
+    lib = _load()
+    if key_lens is not None and key_lens.dtype != torch.int32:
+        raise RelattnError(INVALID_ARGUMENT, "relattn: key_lens must be int32")
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    elif hasattr(stream, "cuda_stream"):
+        stream = stream.cuda_stream
+    args, keep = _ob_args(q, k, v, bias, window, causal, key_lens, scale, out)
+    st = lib.relattn_fwd_offset_bias(*args, ctypes.c_void_p(stream))
+    del keep
+    if st != OK:
+        _raise(lib, st)
+    return out
+
+
+def validate_offset_bias(q, k, v, bias, window, *, causal=False, key_lens=None, scale=None,
+                         out=None):
+    """Host-only argument check of ``fwd_offset_bias``; returns the status code."""
+    lib = _load()
+    args, keep = _ob_args(q, k, v, bias, window, causal, key_lens, scale, q if out is None else out)
+    st = lib.relattn_validate_offset_bias(*args)
+    del keep
+    return st

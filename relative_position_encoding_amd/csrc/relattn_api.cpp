@@ -197,7 +197,7 @@ int make_plan(const relattn_tensor* q, const relattn_tensor* k, const relattn_te
               const relattn_tensor* wK, const relattn_tensor* wV,
               const relattn_tensor* t5_bias, const relattn_t5_params* t5, int32_t clip_k,
               float scale, const relattn_mask* mask, const relattn_tensor* out, Plan* plan,
-              bool want_t5_table) {
+              bool want_t5_table, const relattn_tensor* ob = nullptr, int32_t ob_window = 0) {
   int st;
   if ((st = check_view(q, "q", 4, true))) return st;
   if ((st = check_view(k, "k", 4, true))) return st;
@@ -223,14 +223,29 @@ int make_plan(const relattn_tensor* q, const relattn_tensor* k, const relattn_te
     return fail(RELATTN_ERR_INVALID_ARGUMENT, "scale must be finite");
 
   const bool is_t5 = t5_bias != nullptr || t5 != nullptr;
+  const bool is_ob = ob != nullptr;  // scalar bias by clipped offset
   if ((t5_bias == nullptr) != (t5 == nullptr))
     return fail(RELATTN_ERR_INVALID_ARGUMENT, "t5_bias and t5 params must be given together");
   if (is_t5 && (wK || wV))
     return fail(RELATTN_ERR_INVALID_ARGUMENT, "T5 bias excludes the wK/wV tables");
-  if (!is_t5 && clip_k < 0)
+  if (is_ob && (wK || wV || is_t5))
+    return fail(RELATTN_ERR_INVALID_ARGUMENT, "an offset bias excludes the other tables");
+  if (!is_t5 && !is_ob && clip_k < 0)
     return fail(RELATTN_ERR_INVALID_ARGUMENT, "clip_k must be >= 0");
-  if (!is_t5 && (int64_t)clip_k > kMaxSeq)
+  if (!is_t5 && !is_ob && (int64_t)clip_k > kMaxSeq)
     return fail(RELATTN_ERR_UNSUPPORTED, "clip_k exceeds 2^30");
+  if (is_ob) {
+    if ((st = check_view(ob, "bias", 2, false))) return st;
+    if (ob->dtype != RELATTN_F32) return fail(RELATTN_ERR_INVALID_ARGUMENT, "bias must be F32");
+    if (ob_window < 0) return fail(RELATTN_ERR_INVALID_ARGUMENT, "window must be >= 0");
+    if ((int64_t)ob_window > kMaxSeq) return fail(RELATTN_ERR_UNSUPPORTED, "window exceeds 2^30");
+    if (!(ob->shape[0] == q->shape[1] || ob->shape[0] == 1))
+      return fail(RELATTN_ERR_INVALID_ARGUMENT, "bias: shape[0] must be H (%lld) or 1",
+                  (long long)q->shape[1]);
+    if (ob->shape[1] != 2 * (int64_t)ob_window + 1)
+      return fail(RELATTN_ERR_INVALID_ARGUMENT, "bias: shape[1] must be 2*window+1 = %lld",
+                  (long long)(2 * (int64_t)ob_window + 1));
+  }
   if (wK && (st = check_table(wK, "wK", q, clip_k))) return st;
   if (wV && (st = check_table(wV, "wV", q, clip_k))) return st;
   T5Buckets tb = {};
@@ -248,7 +263,8 @@ int make_plan(const relattn_tensor* q, const relattn_tensor* k, const relattn_te
   Plan& P = *plan;
   P.bf16 = q->dtype == RELATTN_BF16;
   P.d = (int)d;
-  P.mode = is_t5 ? relattn::kRelT5 : ((wK || wV) ? relattn::kRelShaw : relattn::kRelNone);
+  P.mode = (is_t5 || is_ob) ? relattn::kRelT5
+                             : ((wK || wV) ? relattn::kRelShaw : relattn::kRelNone);
   P.has_wk = wK != nullptr;
   P.has_wv = wV != nullptr;
   P.empty = (B == 0 || H == 0 || n == 0);
@@ -260,7 +276,7 @@ int make_plan(const relattn_tensor* q, const relattn_tensor* k, const relattn_te
   p.n = (int32_t)n;
   p.causal = (mask && mask->causal) ? 1 : 0;
   p.key_lens = mask ? mask->key_lens : nullptr;
-  p.clip = is_t5 ? 0 : clip_k;
+  p.clip = (is_t5 || is_ob) ? 0 : clip_k;
   const bool causal = p.causal != 0;
   // Label rows any query can reach: offsets j - i lie in [-(n-1), n-1], or in
   // [-(n-1), 0] under the causal mask.
@@ -274,7 +290,15 @@ int make_plan(const relattn_tensor* q, const relattn_tensor* k, const relattn_te
     p.r_lo = 0;
     p.nr = 1;
   }
-  p.t5_dist = is_t5 ? (int32_t)std::min<int64_t>(t5->max_distance, n - 1) : 0;
+  p.t5_dist = is_t5 ? (int32_t)std::min<int64_t>(t5->max_distance, n - 1)
+                    : (is_ob ? (int32_t)std::min<int64_t>(ob_window, n - 1) : 0);
+  if (is_ob) {
+    // the table's entries for offsets -t5_dist .. t5_dist stand in for the
+    // bucket column; offsets beyond them take the end entries, as buckets do
+    tb.nb = 2 * p.t5_dist + 1;
+    p.ob = 1;
+    p.ob_lo = ob_window - p.t5_dist;
+  }
   p.t5 = tb;
   const float s = scale > 0.f ? scale
                               : (is_t5 ? 1.f : 1.f / std::sqrt((float)d));
@@ -285,7 +309,7 @@ int make_plan(const relattn_tensor* q, const relattn_tensor* k, const relattn_te
   // Among the shapes whose LDS fits, take the one that keeps the most waves
   // of this grid resident per compute unit (two per SIMD for d <= 64, one
   // for d = 128, as the kernels are compiled); ties go to the earlier one.
-  const int nb = is_t5 ? t5->num_buckets : 0;
+  const int nb = is_t5 ? t5->num_buckets : (is_ob ? p.t5.nb : 0);
   auto lds_of = [&](const LaunchCfg& c) {
     return relattn::lds_bytes(P.bf16, P.d, c, P.mode, P.has_wk, P.has_wv, p.nr, p.t5_dist, nb);
   };
@@ -334,7 +358,8 @@ int make_plan(const relattn_tensor* q, const relattn_tensor* k, const relattn_te
   if (!found) {
     if (P.mode == relattn::kRelT5)
       return fail(RELATTN_ERR_UNSUPPORTED,
-                  "T5 offset window 2*min(max_distance, n-1)+1 = %d does not fit on chip",
+                  "scalar-bias offset window 2*min(max_distance or window, n-1)+1 = %d "
+                  "does not fit on chip",
                   2 * p.t5_dist + 1);
     return fail(RELATTN_ERR_UNSUPPORTED,
                 "label window of %d rows (2*clip_k+1 clipped to 2n-1) does not fit on chip",
@@ -377,6 +402,11 @@ int make_plan(const relattn_tensor* q, const relattn_tensor* k, const relattn_te
     p.t5_bias = static_cast<const float*>(t5_bias->data);
     p.tb_sb = t5_bias->stride[0];
     p.tb_sh = t5_bias->stride[1];
+  }
+  if (is_ob) {
+    p.t5_bias = static_cast<const float*>(ob->data);
+    p.tb_sb = ob->stride[1];
+    p.tb_sh = ob->shape[0] == 1 ? 0 : ob->stride[0];
   }
   return RELATTN_OK;
 }
@@ -564,6 +594,37 @@ int relattn_fwd(const relattn_tensor* q, const relattn_tensor* k, const relattn_
   g_last_error.clear();
   Plan plan;
   int st = make_plan(q, k, v, wK, wV, t5_bias, t5, clip_k, scale, mask, out, &plan, true);
+  if (st) return st;
+  if ((st = check_device())) return st;
+  if (plan.empty) return RELATTN_OK;
+  const int e = relattn::launch_fwd(plan.bf16, plan.d, plan.cfg, plan.mode, plan.has_wk,
+                                    plan.has_wv, plan.p, stream);
+  if (e != (int)hipSuccess)
+    return fail(RELATTN_ERR_LAUNCH_FAILED, "launch failed: %s",
+                hipGetErrorString((hipError_t)e));
+  return RELATTN_OK;
+}
+
+int relattn_validate_offset_bias(const relattn_tensor* q, const relattn_tensor* k,
+                                 const relattn_tensor* v, const relattn_tensor* bias,
+                                 int32_t window, float scale, const relattn_mask* mask,
+                                 const relattn_tensor* out) {
+  g_last_error.clear();
+  if (!bias) return fail(RELATTN_ERR_INVALID_ARGUMENT, "bias is NULL");
+  Plan plan;
+  return make_plan(q, k, v, nullptr, nullptr, nullptr, nullptr, 0, scale, mask, out, &plan, false,
+                   bias, window);
+}
+
+int relattn_fwd_offset_bias(const relattn_tensor* q, const relattn_tensor* k,
+                            const relattn_tensor* v, const relattn_tensor* bias, int32_t window,
+                            float scale, const relattn_mask* mask, relattn_tensor* out,
+                            void* stream) {
+  g_last_error.clear();
+  if (!bias) return fail(RELATTN_ERR_INVALID_ARGUMENT, "bias is NULL");
+  Plan plan;
+  int st = make_plan(q, k, v, nullptr, nullptr, nullptr, nullptr, 0, scale, mask, out, &plan, true,
+                     bias, window);
   if (st) return st;
   if ((st = check_device())) return st;
   if (plan.empty) return RELATTN_OK;

@@ -50,6 +50,12 @@ struct FwdParams {
   int32_t nstage;          // K/V tiles in the LDS ring (2 or 3)
   int32_t wv_mode;         // WvMode: where the w^V tile is staged
   int32_t dma32;           // K/V tile rows fit 32-bit byte offsets (fast stage loads)
+  // The scalar-bias arm takes either T5 buckets (ob = 0: t5_bias is [NB, H])
+  // or a table by clipped offset (ob = 1: t5_bias points at the head's row of
+  // a [Hb, 2W + 1] table; t5.nb = 2 * t5_dist + 1 entries starting at ob_lo
+  // = W - t5_dist are loaded).
+  int32_t ob;
+  int32_t ob_lo;
   T5Buckets t5;
 };
 

@@ -524,10 +524,11 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<D, NW, MODE, BF16, BC>()))) vo
                                        lay.wv_rows, wave, lane);
   }
   if constexpr (T5) {
-    // bias column of this head, 4 bytes per lane, issued by wave 0
+    // bias column of this head (or the window of its row of a table by
+    // offset), 4 bytes per lane, issued by wave 0
     if (wave == 0) {
       for (int I = 0; I * 64 < p.t5.nb; ++I) {
-        const int bucket = min(I * 64 + lane, p.t5.nb - 1);
+        const int bucket = min(I * 64 + lane, p.t5.nb - 1) + p.ob_lo;
         __builtin_amdgcn_global_load_lds(
             (const RELATTN_GLOBAL void*)(p.t5_bias + bucket * p.tb_sb + h * p.tb_sh),
             (RELATTN_LDS void*)(smem_lds + lay.tbc + I * 256), 4, 0, 0);
@@ -644,8 +645,8 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<D, NW, MODE, BF16, BC>()))) vo
     for (int x = tid; x < nb; x += NT) {
       const int delta = min(max(x - PADL - p.t5_dist, -p.t5_dist), p.t5_dist);
       // as for the Shaw rows: future offsets carry the causal mask
-      TB[x] = (p.causal && x - PADL - p.t5_dist > 0) ? kNegInf
-                                                     : kLog2e * TBC[t5_bucket(delta, p.t5)];
+      const int entry = p.ob ? delta + p.t5_dist : t5_bucket(delta, p.t5);
+      TB[x] = (p.causal && x - PADL - p.t5_dist > 0) ? kNegInf : kLog2e * TBC[entry];
     }
     block_sync();
   }

@@ -196,3 +196,22 @@ def test_decode_rejects(ra, case):
     with pytest.raises(ra.RelattnError) as ei:
         ra.decode_workspace_size(*args, **kw)
     assert ei.value.status == code
+
+
+# ---------------------------------------------------------------------------
+# relattn_fwd_offset_bias: host-only checks
+# ---------------------------------------------------------------------------
+
+def test_offset_bias_validation(ra):
+    q, k, v = qkv()
+    F = lambda *s: T(*s, dtype=torch.float32)
+    assert ra.validate_offset_bias(q, k, v, F(3, 9), 4) == ra.OK
+    assert ra.validate_offset_bias(q, k, v, F(1, 9), 4, causal=True) == ra.OK
+    assert ra.validate_offset_bias(q, k, v, F(3, 1), 0) == ra.OK
+    assert ra.validate_offset_bias(q, k, v, F(3, 8), 4) == ra.INVALID_ARGUMENT      # 2w+1
+    assert ra.validate_offset_bias(q, k, v, F(2, 9), 4) == ra.INVALID_ARGUMENT      # heads
+    assert ra.validate_offset_bias(q, k, v, T(3, 9), 4) == ra.INVALID_ARGUMENT      # dtype
+    assert ra.validate_offset_bias(q, k, v, F(3, 1), -1) == ra.INVALID_ARGUMENT     # window
+    big = 40000
+    qb, kb, vb = qkv(B=1, H=1, n=50000)
+    assert ra.validate_offset_bias(qb, kb, vb, F(1, 2 * big + 1), big) == ra.UNSUPPORTED
