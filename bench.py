@@ -250,6 +250,83 @@ def decode_report(ra, steps):
     }
 
 
+# ---------------------------------------------------------------------------
+# scalar bias by clipped offset: causal ALiBi on the T5 shape
+# ---------------------------------------------------------------------------
+
+ALIBI = {"name": "alibi", "batch": 8, "heads": 12, "n": 1024, "d": 64, "seed": 20260007,
+         "description": "causal ALiBi (-m_h |j - i|, slopes 2^(-8(h+1)/H), window n-1) as a "
+                        "table by offset: B8 H12 n1024 d64, bf16"}
+
+
+def alibi_inputs():
+    import torch
+    a = ALIBI
+    g = torch.Generator().manual_seed(a["seed"])
+    q, k, v = (torch.randn(a["batch"], a["heads"], a["n"], a["d"], generator=g).to(torch.bfloat16)
+               for _ in range(3))
+    W, H = a["n"] - 1, a["heads"]
+    slopes = [2.0 ** (-8.0 * (h + 1) / H) for h in range(H)]
+    bias = torch.tensor([[-m * abs(x) for x in range(-W, W + 1)] for m in slopes],
+                        dtype=torch.float32)
+    return q, k, v, bias, W
+
+
+def time_alibi(ra, steps, warmup, hot=False, reps=5):
+    import statistics
+    import torch
+    lib = ra._load()
+    stream = torch.cuda.Stream()
+    q, k, v, bias, W = alibi_inputs()
+    a = ALIBI
+    B, H, n, d = a["batch"], a["heads"], a["n"], a["d"]
+    pairs = B * H * n * (n + 1) // 2
+    flops = 4.0 * d * pairs
+    nbytes = 4.0 * B * H * n * d * 2 + bias.numel() * 4
+    copies = 1 if hot else max(1, min(16, int(2 * LLC_BYTES // nbytes) + 1))
+    calls, keep = [], []
+    for _ in range(copies):
+        g = [x.to("cuda").clone() for x in (q, k, v, bias)]
+        out = torch.empty_like(g[0])
+        args, kp = ra._ob_args(g[0], g[1], g[2], g[3], W, True, None, None, out)
+        calls.append(args + [ctypes.c_void_p(stream.cuda_stream)])
+        keep += [g, out, kp]
+    fn = lib.relattn_fwd_offset_bias
+    times = []
+    with torch.cuda.stream(stream):
+        for s_ in range(warmup):
+            if fn(*calls[s_ % copies]) != 0:
+                raise RuntimeError(ra.last_error())
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        for _ in range(reps):
+            t0.record(stream)
+            for s_ in range(steps):
+                fn(*calls[s_ % copies])
+            t1.record(stream)
+            torch.cuda.synchronize()
+            times.append(t0.elapsed_time(t1) / steps)
+    del keep
+    ms = statistics.median(times)
+    sec = ms * 1e-3
+    return {"ms_per_step": ms, "tflops": flops / sec / 1e12, "hbm_gbs": nbytes / sec / 1e9,
+            "alg_gflop": flops / 1e9, "alg_mbytes": nbytes / 1e6, "input_copies": copies}
+
+
+def alibi_report(ra, steps):
+    cold = time_alibi(ra, steps, 10)
+    hot = time_alibi(ra, steps, 10, hot=True)
+    ceil = ceiling_tflops(cold["alg_gflop"] * 1e9, cold["alg_mbytes"] * 1e6, "bf16")
+    return {"workload": ALIBI["description"], "ms_per_step": round(cold["ms_per_step"], 5),
+            "tflops": round(cold["tflops"], 3),
+            "mfma_peak_frac": round(cold["tflops"] / PEAK_TFLOPS["bf16"], 4),
+            "roofline_frac": round(cold["tflops"] / ceil, 4),
+            "bound": bound_of(cold["alg_gflop"] * 1e9, cold["alg_mbytes"] * 1e6, "bf16"),
+            "hbm_gbs": round(cold["hbm_gbs"], 1), "hot_ms_per_step": round(hot["ms_per_step"], 5),
+            "alg_gflop_per_step": round(cold["alg_gflop"], 4), "steps_per_rep": steps}
+
+
 def bound_of(flops, nbytes, dt):
     ridge = PEAK_TFLOPS[dt] * 1e12 / (PEAK_HBM_GBS * 1e9)
     return "hbm" if flops / nbytes < ridge else "mfma"
@@ -442,6 +519,8 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--decode-only", action="store_true",
                     help="time the decode workload only and print its figures")
+    ap.add_argument("--alibi-only", action="store_true",
+                    help="time the offset-bias (ALiBi) workload only and print its figures")
     a = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if a.gpus != 1 or world != 1:
@@ -461,6 +540,9 @@ def main():
         return
     if a.decode_only:
         print(json.dumps({"decode": decode_report(ra, max(50, a.steps // 5))}))
+        return
+    if a.alibi_only:
+        print(json.dumps({"offset_bias": alibi_report(ra, max(50, a.steps // 5))}))
         return
 
     if gpu is not None and not gpu.get("name"):
@@ -522,6 +604,7 @@ def main():
             per[name] = e
         line["workloads"] = per
         line["decode"] = decode_report(ra, max(50, a.steps // 5))
+        line["offset_bias"] = alibi_report(ra, max(50, a.steps // 5))
     if not a.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w)
         if not a.only:
