@@ -34,7 +34,12 @@ Readings where the pages are silent or garbled (each is listed in the design doc):
   keys after the query (delta > 0) use the upper half; unidirectional uses all
   B buckets for delta <= 0 and maps delta > 0 to bucket 0;
 * the floor in beta is taken of the exact real number (rational comparison),
-  not of a rounded floating-point logarithm.
+  not of a rounded floating-point logarithm;
+* backward (no page prints it): the gradients of a scalar loss sum(dz * z) by
+  the chain rule through the forward above; a table shared by all heads takes
+  the sum over heads, and hidden pairs give no gradient.  Pinned by central
+  finite differences of the forward, by library autograd where the tables
+  vanish, and by the row-sum identities of the softmax.
 """
 from __future__ import annotations
 
@@ -57,6 +62,8 @@ __all__ = [
     "relattn_decode",
     "t5_decode",
     "offset_bias_attention",
+    "relattn_backward",
+    "t5_backward",
     "to_f64",
 ]
 
@@ -460,3 +467,86 @@ def offset_bias_attention(q, k, v, bias, window: int, scale=None, causal: bool =
             e = s * (q[b, h] @ k[b, h].T) + row[R]
             z[b, h] = _masked_softmax_rows(e, ok) @ v[b, h]
     return z
+
+
+# ---------------------------------------------------------------------------
+# Backward: gradients of a loss through the forward of Eq. 3 and Eq. 4 (and of
+# the T5 bias), by the chain rule written out term by term.  dz is the
+# gradient of the loss with respect to the output z.
+# ---------------------------------------------------------------------------
+
+def relattn_backward(q, k, v, aK=None, aV=None, clip_k: int = 0, dz=None, scale=None,
+                     causal: bool = False, key_lens=None):
+    """Gradients (dq, dk, dv, daK, daV) of sum(dz * z), z = relattn_bruteforce(...).
+
+    For one head, with alpha the masked softmax of e_ij = s q_i.(k_j + a^K_ij)
+    and z_i = sum_j alpha_ij (v_j + a^V_ij):
+      dalpha_ij = dz_i . (v_j + a^V_ij)
+      de_ij     = alpha_ij (dalpha_ij - sum_j' alpha_ij' dalpha_ij')   (softmax)
+      dq_i      = s sum_j de_ij (k_j + a^K_ij)
+      dk_j      = s sum_i de_ij q_i            dv_j = sum_i alpha_ij dz_i
+      da^K_r    = s sum_{(i,j): label r} de_ij q_i
+      da^V_r    = sum_{(i,j): label r} alpha_ij dz_i
+    Tables shared by all heads (Ht == 1) collect the sums of every head.
+    Returns None for an absent table.
+    """
+    q, k, v, dz = to_f64(q), to_f64(k), to_f64(v), to_f64(dz)
+    aK, aV = to_f64(aK), to_f64(aV)
+    B, H, n, d = q.shape
+    s = _default_scale(d, scale)
+    lens = _key_lengths(key_lens, B, n)
+    R = relative_labels(n, clip_k) + clip_k
+    nlab = 2 * clip_k + 1
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    daK = None if aK is None else np.zeros_like(aK)
+    daV = None if aV is None else np.zeros_like(aV)
+    for b in range(B):
+        ok = visible(n, causal, lens[b])
+        for h in range(H):
+            tk, tv = _table_for_head(aK, h), _table_for_head(aV, h)
+            keys = k[b, h][None, :, :] + (tk[R] if tk is not None else 0.0)   # [n, n, d]
+            vals = v[b, h][None, :, :] + (tv[R] if tv is not None else 0.0)
+            e = s * np.einsum("id,ijd->ij", q[b, h], keys)
+            alpha = _masked_softmax_rows(e, ok)
+            dalpha = np.einsum("id,ijd->ij", dz[b, h], vals)
+            de = alpha * (dalpha - (alpha * dalpha).sum(axis=1, keepdims=True))
+            dq[b, h] = s * np.einsum("ij,ijd->id", de, keys)
+            dk[b, h] = s * de.T @ q[b, h]
+            dv[b, h] = alpha.T @ dz[b, h]
+            hk = 0 if (aK is not None and aK.shape[0] == 1) else h
+            hv = 0 if (aV is not None and aV.shape[0] == 1) else h
+            for r in range(nlab):
+                sel = R == r
+                if daK is not None:
+                    daK[hk, r] += s * (de * sel).sum(axis=1) @ q[b, h]
+                if daV is not None:
+                    daV[hv, r] += (alpha * sel).sum(axis=1) @ dz[b, h]
+    return dq, dk, dv, daK, daV
+
+
+def t5_backward(q, k, v, bias, num_buckets: int = 32, max_distance: int = 128,
+                bidirectional: bool = True, dz=None, scale=None, causal: bool = False,
+                key_lens=None):
+    """Gradients (dq, dk, dv, dbias) of sum(dz * z) for the T5 bias attention:
+    de as in ``relattn_backward`` with dalpha_ij = dz_i . v_j, and
+    dbias[beta, h] = sum over the pairs of bucket beta of de_ij."""
+    q, k, v, dz = to_f64(q), to_f64(k), to_f64(v), to_f64(dz)
+    bias = to_f64(bias)
+    B, H, n, d = q.shape
+    s = 1.0 if (scale is None or scale <= 0) else float(scale)
+    lens = _key_lengths(key_lens, B, n)
+    Bm = t5_bucket_matrix(n, num_buckets, max_distance, bidirectional)
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    db = np.zeros_like(bias)
+    for b in range(B):
+        ok = visible(n, causal, lens[b])
+        for h in range(H):
+            e = s * (q[b, h] @ k[b, h].T) + bias[Bm, h]
+            alpha = _masked_softmax_rows(e, ok)
+            dalpha = dz[b, h] @ v[b, h].T
+            de = alpha * (dalpha - (alpha * dalpha).sum(axis=1, keepdims=True))
+            dq[b, h] = s * de @ k[b, h]
+            dk[b, h] = s * de.T @ q[b, h]
+            dv[b, h] = alpha.T @ dz[b, h]
+            db[:, h] += np.bincount(Bm.ravel(), weights=de.ravel(), minlength=num_buckets)
+    return dq, dk, dv, db

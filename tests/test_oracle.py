@@ -561,3 +561,104 @@ def test_alibi_window_clips_to_end_entries():
     z = oracle.offset_bias_attention(q, k, v, table, w, causal=True)
     z2 = oracle.offset_bias_attention(q, k, v, big, n - 1, causal=True)
     np.testing.assert_allclose(z, z2, rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# backward: the chain rule through Eq. 3 and Eq. 4, pinned by central finite
+# differences of the (independently pinned) forward oracle, by library
+# autograd when the tables vanish, and by closed-form sums
+# ---------------------------------------------------------------------------
+
+def _fd_check(f, x, grad, idx_list, eps=1e-6, tol=1e-6):
+    for idx in idx_list:
+        x0 = x[idx]
+        x[idx] = x0 + eps
+        fp = f()
+        x[idx] = x0 - eps
+        fm = f()
+        x[idx] = x0
+        fd = (fp - fm) / (2 * eps)
+        assert abs(fd - grad[idx]) <= tol * max(1.0, abs(fd)), (idx, fd, grad[idx])
+
+
+@pytest.mark.parametrize("causal,lens,shared", [(False, None, False), (True, None, False),
+                                               (False, [5, 7], True)])
+def test_backward_matches_finite_differences(causal, lens, shared):
+    B, H, n, d, c = 2, 2, 7, 4, 2
+    q, k, v = rnd((B, H, n, d), 110), rnd((B, H, n, d), 111), rnd((B, H, n, d), 112)
+    Ht = 1 if shared else H
+    aK, aV = rnd((Ht, 2 * c + 1, d), 113, 0.5), rnd((Ht, 2 * c + 1, d), 114, 0.5)
+    dz = rnd((B, H, n, d), 115)
+    grads = oracle.relattn_backward(q, k, v, aK, aV, c, dz, causal=causal, key_lens=lens)
+    loss = lambda: float((dz * oracle.relattn_bruteforce(q, k, v, aK, aV, c, causal=causal,
+                                                         key_lens=lens)).sum())
+    rng = np.random.default_rng(116)
+    for x, g in zip((q, k, v, aK, aV), grads):
+        idx = [tuple(int(rng.integers(s)) for s in x.shape) for _ in range(6)]
+        _fd_check(loss, x, g, idx)
+
+
+@pytest.mark.parametrize("bidir", [True, False])
+def test_t5_backward_matches_finite_differences(bidir):
+    B, H, n, d = 1, 2, 20, 4
+    q, k, v = rnd((B, H, n, d), 120), rnd((B, H, n, d), 121), rnd((B, H, n, d), 122)
+    bias, dz = rnd((8, H), 123), rnd((B, H, n, d), 124)
+    grads = oracle.t5_backward(q, k, v, bias, 8, 12, bidir, dz, causal=True)
+    loss = lambda: float((dz * oracle.t5_attention(q, k, v, bias, 8, 12, bidir,
+                                                   causal=True)).sum())
+    rng = np.random.default_rng(125)
+    for x, g in zip((q, k, v, bias), grads):
+        idx = [tuple(int(rng.integers(s)) for s in x.shape) for _ in range(6)]
+        _fd_check(loss, x, g, idx)
+
+
+def test_backward_zero_tables_equals_library_autograd():
+    """Zero tables: the gradients of textbook attention, by torch autograd of
+    the library routine in fp64."""
+    B, H, n, d = 2, 2, 9, 8
+    q, k, v, dz = (rnd((B, H, n, d), 130 + i) for i in range(4))
+    c = 3
+    z0 = np.zeros((H, 2 * c + 1, d))
+    dq, dk, dv, daK, daV = oracle.relattn_backward(q, k, v, z0, z0, c, dz, causal=True)
+    t = [torch.tensor(x, requires_grad=True) for x in (q, k, v)]
+    out = torch.nn.functional.scaled_dot_product_attention(*t, is_causal=True)
+    out.backward(torch.tensor(dz))
+    for mine, theirs in zip((dq, dk, dv), t):
+        np.testing.assert_allclose(mine, theirs.grad.numpy(), rtol=0, atol=1e-12)
+
+
+def test_backward_closed_form_sums():
+    """Every row's weights sum to 1: the value gradients summed over keys (and
+    over labels) equal the output gradients summed over queries, and the
+    logit gradients of a row sum to 0, so the key-table gradient summed over
+    labels is s * sum_i (sum_j de_ij) q_i = 0."""
+    B, H, n, d, c = 1, 2, 10, 4, 3
+    q, k, v = rnd((B, H, n, d), 140), rnd((B, H, n, d), 141), rnd((B, H, n, d), 142)
+    aK, aV = rnd((H, 2 * c + 1, d), 143), rnd((H, 2 * c + 1, d), 144)
+    dz = rnd((B, H, n, d), 145)
+    dq, dk, dv, daK, daV = oracle.relattn_backward(q, k, v, aK, aV, c, dz)
+    for h in range(H):
+        np.testing.assert_allclose(dv[0, h].sum(axis=0), dz[0, h].sum(axis=0), atol=1e-12)
+        np.testing.assert_allclose(daV[h].sum(axis=0), dz[0, h].sum(axis=0), atol=1e-12)
+        np.testing.assert_allclose(daK[h].sum(axis=0), 0.0, atol=1e-12)
+        np.testing.assert_allclose(dk[0, h].sum(axis=0), 0.0, atol=1e-12)
+
+
+def test_t5_backward_bias_gradient_sums_to_zero():
+    """sum over buckets of dbias[:, h] = sum_ij de_ij = 0; and a bias constant
+    across buckets shifts every row by one value, which the softmax ignores, so
+    q, k, v get the textbook gradients (torch autograd of the library routine)."""
+    B, H, n, d = 1, 2, 12, 4
+    q, k, v, dz = (rnd((B, H, n, d), 150 + i) for i in range(4))
+    bias = rnd((16, H), 154)
+    db = oracle.t5_backward(q, k, v, bias, 16, 40, True, dz, key_lens=[9])[3]
+    np.testing.assert_allclose(db.sum(axis=0), 0.0, atol=1e-12)
+    flat = np.repeat(rnd((1, H), 155), 8, axis=0)
+    dq, dk, dv, db1 = oracle.t5_backward(q, k, v, flat, 8, 20, False, dz, scale=0.5,
+                                         causal=True)
+    t = [torch.tensor(x, requires_grad=True) for x in (q, k, v)]
+    torch.nn.functional.scaled_dot_product_attention(*t, is_causal=True, scale=0.5).backward(
+        torch.tensor(dz))
+    for mine, theirs in zip((dq, dk, dv), t):
+        np.testing.assert_allclose(mine, theirs.grad.numpy(), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(db1.sum(axis=0), 0.0, atol=1e-12)
