@@ -29,7 +29,7 @@
  *   - All tensor data pointers are DEVICE pointers owned by the caller.  The
  *     library allocates nothing and keeps no state between calls; it is
  *     thread-safe.  Equal inputs give bit-identical outputs.
- *   - relattn_fwd and relattn_decode only enqueue work on `stream` (a
+ *   - Entry points that launch kernels only enqueue work on `stream` (a
  *     hipStream_t, NULL = the default stream) and return.  Buffers must stay
  *     alive until the stream has passed that point.  Faults during execution surface at the caller's
  *     next synchronisation.
@@ -202,6 +202,101 @@ int relattn_decode_workspace_size(const relattn_tensor* q, const relattn_tensor*
                                   const relattn_t5_params* t5, int32_t clip_k,
                                   float scale, const relattn_tensor* out,
                                   size_t* bytes);
+
+/*
+ * Training.  The backward pass needs each query row's log-sum-exp of its
+ * logits, lse_i = log sum_{visible j} exp(e_ij) (natural log; -inf for a row
+ * that sees no key), which these forward variants also write:
+ *
+ * relattn_fwd_lse / relattn_fwd_offset_bias_lse: relattn_fwd /
+ *   relattn_fwd_offset_bias plus lse: [B, H, n] F32, innermost dimension
+ *   contiguous, device memory owned by the caller.  Same errors.
+ */
+int relattn_fwd_lse(const relattn_tensor* q, const relattn_tensor* k,
+                    const relattn_tensor* v, const relattn_tensor* wK,
+                    const relattn_tensor* wV, const relattn_tensor* t5_bias,
+                    const relattn_t5_params* t5, int32_t clip_k, float scale,
+                    const relattn_mask* mask, relattn_tensor* out, relattn_tensor* lse,
+                    void* stream);
+int relattn_fwd_offset_bias_lse(const relattn_tensor* q, const relattn_tensor* k,
+                                const relattn_tensor* v, const relattn_tensor* bias,
+                                int32_t window, float scale, const relattn_mask* mask,
+                                relattn_tensor* out, relattn_tensor* lse, void* stream);
+
+/*
+ * relattn_bwd: enqueue the backward pass: the gradients of a scalar loss L
+ * given dout = dL/dz for the attention relattn_fwd_lse computed (Eq. 3 and
+ * Eq. 4 of the Shaw section 3.4, or the T5 bias, differentiated by the chain
+ * rule; the papers train these models end to end).  With P the weights,
+ * dP_ij = dout_i.(v_j + wV[r]), D_i = dout_i.z_i and dS_ij = P_ij (dP_ij - D_i):
+ *     dq_i = s sum_j dS_ij (k_j + wK[r])    dk_j = s sum_i dS_ij q_i
+ *     dv_j = sum_i P_ij dout_i
+ *     dwK[r] = s sum over pairs of label r of dS_ij q_i
+ *     dwV[r] = sum over pairs of label r of P_ij dout_i
+ *     dbias[beta, h] = sum over pairs of bucket beta of dS_ij
+ * Table gradients of a shared table (Ht = 1) sum over the heads.  Pairs that
+ * are hidden by the mask contribute nothing.
+ *
+ *   q .. mask      : exactly the arguments of the forward call.
+ *   out, lse       : that call's output and row log-sum-exp (unchanged).
+ *   dout           : [B, H, n, d], dtype and alignment of q.
+ *   dq, dk, dv     : outputs like q (16-byte aligned rows).
+ *   dwK, dwV       : outputs [Ht, 2*clip_k + 1, d] F32 (innermost contiguous),
+ *                    or NULL to skip; a non-NULL one needs its table.  Rows of
+ *                    labels no pair reaches are set to zero.
+ *   dbias          : output like t5_bias (F32), or NULL to skip.
+ *   workspace      : device buffer of at least the bytes that
+ *                    relattn_bwd_workspace_size reports (16-byte aligned,
+ *                    caller-owned; contents on entry do not matter).  Calls
+ *                    that share a workspace must be ordered (same stream).
+ * All outputs are fully overwritten; the results are bitwise reproducible
+ * (no atomics).  Errors as for relattn_fwd; UNSUPPORTED also when the
+ * per-workgroup state of the label window (or of the T5 buckets) does not
+ * fit on chip.  Enqueues up to three kernels and returns.
+ */
+int relattn_bwd(const relattn_tensor* q, const relattn_tensor* k, const relattn_tensor* v,
+                const relattn_tensor* wK, const relattn_tensor* wV,
+                const relattn_tensor* t5_bias, const relattn_t5_params* t5, int32_t clip_k,
+                float scale, const relattn_mask* mask, const relattn_tensor* out,
+                const relattn_tensor* dout, const relattn_tensor* lse, relattn_tensor* dq,
+                relattn_tensor* dk, relattn_tensor* dv, relattn_tensor* dwK,
+                relattn_tensor* dwV, relattn_tensor* dbias, void* workspace,
+                size_t workspace_bytes, void* stream);
+
+/* relattn_bwd_workspace_size: the argument checks of relattn_bwd (host only:
+ * no HIP call) and the workspace bytes it needs, written to *bytes (0 for
+ * empty problems).  Depends only on shapes, dtype, tables and mask kind. */
+int relattn_bwd_workspace_size(const relattn_tensor* q, const relattn_tensor* k,
+                               const relattn_tensor* v, const relattn_tensor* wK,
+                               const relattn_tensor* wV, const relattn_tensor* t5_bias,
+                               const relattn_t5_params* t5, int32_t clip_k, float scale,
+                               const relattn_mask* mask, const relattn_tensor* out,
+                               const relattn_tensor* dout, const relattn_tensor* lse,
+                               const relattn_tensor* dq, const relattn_tensor* dk,
+                               const relattn_tensor* dv, const relattn_tensor* dwK,
+                               const relattn_tensor* dwV, const relattn_tensor* dbias,
+                               size_t* bytes);
+
+/* relattn_bwd_offset_bias and its workspace size: the same for
+ * relattn_fwd_offset_bias_lse; dbias is [Hb, 2*window + 1] F32 or NULL (e.g.
+ * fixed ALiBi slopes).  A bias gradient needs per-workgroup sums over
+ * 2*min(window, n-1)+1 entries on chip: larger windows give UNSUPPORTED
+ * unless dbias is NULL. */
+int relattn_bwd_offset_bias(const relattn_tensor* q, const relattn_tensor* k,
+                            const relattn_tensor* v, const relattn_tensor* bias,
+                            int32_t window, float scale, const relattn_mask* mask,
+                            const relattn_tensor* out, const relattn_tensor* dout,
+                            const relattn_tensor* lse, relattn_tensor* dq, relattn_tensor* dk,
+                            relattn_tensor* dv, relattn_tensor* dbias, void* workspace,
+                            size_t workspace_bytes, void* stream);
+int relattn_bwd_offset_bias_workspace_size(const relattn_tensor* q, const relattn_tensor* k,
+                                           const relattn_tensor* v, const relattn_tensor* bias,
+                                           int32_t window, float scale,
+                                           const relattn_mask* mask, const relattn_tensor* out,
+                                           const relattn_tensor* dout,
+                                           const relattn_tensor* lse, const relattn_tensor* dq,
+                                           const relattn_tensor* dk, const relattn_tensor* dv,
+                                           const relattn_tensor* dbias, size_t* bytes);
 
 /* Static text for a status code. */
 const char* relattn_strerror(int status);

@@ -11,7 +11,9 @@ import ctypes
 import os
 
 __all__ = ["fwd", "validate", "fwd_offset_bias", "validate_offset_bias", "decode",
-           "decode_workspace_size", "debug_indices",
+           "decode_workspace_size", "debug_indices", "fwd_lse", "fwd_offset_bias_lse",
+           "bwd", "bwd_workspace_size", "bwd_offset_bias", "bwd_offset_bias_workspace_size",
+           "attention", "attention_offset_bias",
            "RelattnError", "library_path",
            "OK", "INVALID_ARGUMENT", "UNSUPPORTED", "NO_DEVICE", "LAUNCH_FAILED"]
 
@@ -73,6 +75,23 @@ def _load():
     lib.relattn_fwd_offset_bias.restype = ctypes.c_int
     lib.relattn_validate_offset_bias.argtypes = ob
     lib.relattn_validate_offset_bias.restype = ctypes.c_int
+    lib.relattn_fwd_lse.argtypes = args + [P(_Tensor), ctypes.c_void_p]
+    lib.relattn_fwd_lse.restype = ctypes.c_int
+    lib.relattn_fwd_offset_bias_lse.argtypes = ob + [P(_Tensor), ctypes.c_void_p]
+    lib.relattn_fwd_offset_bias_lse.restype = ctypes.c_int
+    # q k v wK wV t5_bias t5 clip scale mask out dout lse dq dk dv dwK dwV dbias
+    bw = args + [P(_Tensor)] * 8
+    lib.relattn_bwd.argtypes = bw + [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    lib.relattn_bwd.restype = ctypes.c_int
+    lib.relattn_bwd_workspace_size.argtypes = bw + [P(ctypes.c_size_t)]
+    lib.relattn_bwd_workspace_size.restype = ctypes.c_int
+    # q k v bias window scale mask out dout lse dq dk dv dbias
+    obw = ob + [P(_Tensor)] * 6
+    lib.relattn_bwd_offset_bias.argtypes = obw + [ctypes.c_void_p, ctypes.c_size_t,
+                                                  ctypes.c_void_p]
+    lib.relattn_bwd_offset_bias.restype = ctypes.c_int
+    lib.relattn_bwd_offset_bias_workspace_size.argtypes = obw + [P(ctypes.c_size_t)]
+    lib.relattn_bwd_offset_bias_workspace_size.restype = ctypes.c_int
     lib.relattn_debug_indices.argtypes = [ctypes.c_int32, ctypes.c_int32, P(_T5),
                                           ctypes.c_void_p, ctypes.c_void_p]
     lib.relattn_debug_indices.restype = ctypes.c_int
@@ -312,3 +331,258 @@ def validate_offset_bias(q, k, v, bias, window, *, causal=False, key_lens=None, 
     st = lib.relattn_validate_offset_bias(*args)
     del keep
     return st
+
+
+# ---------------------------------------------------------------------------
+# training: forward with row statistics, backward
+# ---------------------------------------------------------------------------
+
+def _stream_of(q, stream):
+    import torch
+    if stream is None:
+        return torch.cuda.current_stream(q.device).cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+
+
+def _check_lens(key_lens):
+    import torch
+    if key_lens is not None and key_lens.dtype != torch.int32:
+        raise RelattnError(INVALID_ARGUMENT, "relattn: key_lens must be int32")
+
+
+def _new_lse(q):
+    import torch
+    return torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+
+
+def fwd_lse(q, k, v, wK=None, wV=None, *, clip=0, causal=False, key_lens=None,
+            t5_bias=None, num_buckets=32, max_distance=128, bidirectional=True,
+            scale=None, out=None, lse=None, stream=None):
+    """``fwd`` that also writes each row's log-sum-exp of its logits (natural
+    log, float32 [B, H, n]; -inf for a row that sees no key), the statistic
+    ``bwd`` takes.  Returns (out, lse)."""
+    import torch
+    lib = _load()
+    _check_lens(key_lens)
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    if lse is None:
+        lse = _new_lse(q)
+    args, keep = _args(q, k, v, wK, wV, t5_bias, clip, causal, key_lens, num_buckets,
+                       max_distance, bidirectional, scale, out)
+    lv = _view(lse)
+    st = lib.relattn_fwd_lse(*args, _ref(lv), ctypes.c_void_p(_stream_of(q, stream)))
+    del keep, lv
+    if st != OK:
+        _raise(lib, st)
+    return out, lse
+
+
+def fwd_offset_bias_lse(q, k, v, bias, window, *, causal=False, key_lens=None, scale=None,
+                        out=None, lse=None, stream=None):
+    """``fwd_offset_bias`` with the row log-sum-exp; returns (out, lse)."""
+    import torch
+    lib = _load()
+    _check_lens(key_lens)
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    if lse is None:
+        lse = _new_lse(q)
+    args, keep = _ob_args(q, k, v, bias, window, causal, key_lens, scale, out)
+    lv = _view(lse)
+    st = lib.relattn_fwd_offset_bias_lse(*args, _ref(lv), ctypes.c_void_p(_stream_of(q, stream)))
+    del keep, lv
+    if st != OK:
+        _raise(lib, st)
+    return out, lse
+
+
+def _bwd_outputs(q, wK, wV, bias, dq, dk, dv, dwK, dwV, dbias, want_dwk, want_dwv,
+                 want_dbias):
+    import torch
+
+    def new_like_q(x):
+        return x if x is not None else torch.empty_like(q, memory_format=torch.contiguous_format)
+
+    def new_f32(x, ref, want):
+        if x is not None or ref is None or not want:
+            return x
+        return torch.empty(ref.shape, dtype=torch.float32, device=q.device)
+    return (new_like_q(dq), new_like_q(dk), new_like_q(dv), new_f32(dwK, wK, want_dwk),
+            new_f32(dwV, wV, want_dwv), new_f32(dbias, bias, want_dbias))
+
+
+def _bwd_args(q, k, v, wK, wV, t5_bias, clip, causal, key_lens, num_buckets, max_distance,
+              bidirectional, scale, out, dout, lse, grads):
+    args, keep = _args(q, k, v, wK, wV, t5_bias, clip, causal, key_lens, num_buckets,
+                       max_distance, bidirectional, scale, out)
+    extra = [_view(x) for x in (dout, lse) + tuple(grads)]
+    return args + [_ref(x) for x in extra], keep + extra
+
+
+def bwd_workspace_size(q, k, v, wK=None, wV=None, *, out, dout, lse, clip=0, causal=False,
+                       key_lens=None, t5_bias=None, num_buckets=32, max_distance=128,
+                       bidirectional=True, scale=None, dq=None, dk=None, dv=None, dwK=None,
+                       dwV=None, dbias=None, want_dwk=True, want_dwv=True, want_dbias=True):
+    """Workspace bytes ``bwd`` needs for these shapes (host only)."""
+    lib = _load()
+    grads = _bwd_outputs(q, wK, wV, t5_bias, dq if dq is not None else q,
+                         dk if dk is not None else q, dv if dv is not None else q, dwK, dwV,
+                         dbias, want_dwk, want_dwv, want_dbias)
+    args, keep = _bwd_args(q, k, v, wK, wV, t5_bias, clip, causal, key_lens, num_buckets,
+                           max_distance, bidirectional, scale, out, dout, lse, grads)
+    n = ctypes.c_size_t(0)
+    st = lib.relattn_bwd_workspace_size(*args, ctypes.byref(n))
+    del keep
+    if st != OK:
+        _raise(lib, st)
+    return int(n.value)
+
+
+def bwd(q, k, v, wK=None, wV=None, *, out, dout, lse, clip=0, causal=False, key_lens=None,
+        t5_bias=None, num_buckets=32, max_distance=128, bidirectional=True, scale=None,
+        dq=None, dk=None, dv=None, dwK=None, dwV=None, dbias=None, want_dwk=True,
+        want_dwv=True, want_dbias=True, workspace=None, stream=None):
+    """Gradients of sum(dout * out) for the attention ``fwd_lse`` computed.
+
+    out, lse: the forward's output and row log-sum-exp; dout: dL/d out.
+    Returns (dq, dk, dv, dwK, dwV, dbias): dq, dk, dv like q; table gradients
+    float32 like wK / wV (None when the table is absent or not wanted); dbias
+    float32 like t5_bias.  ``workspace``: a uint8 device tensor of at least
+    ``bwd_workspace_size`` bytes (allocated here when None)."""
+    import torch
+    lib = _load()
+    _check_lens(key_lens)
+    grads = _bwd_outputs(q, wK, wV, t5_bias, dq, dk, dv, dwK, dwV, dbias, want_dwk,
+                         want_dwv, want_dbias)
+    args, keep = _bwd_args(q, k, v, wK, wV, t5_bias, clip, causal, key_lens, num_buckets,
+                           max_distance, bidirectional, scale, out, dout, lse, grads)
+    n = ctypes.c_size_t(0)
+    st = lib.relattn_bwd_workspace_size(*args, ctypes.byref(n))
+    if st != OK:
+        _raise(lib, st)
+    if workspace is None:
+        workspace = torch.empty(max(int(n.value), 1), dtype=torch.uint8, device=q.device)
+    st = lib.relattn_bwd(*args, ctypes.c_void_p(workspace.data_ptr()),
+                         ctypes.c_size_t(workspace.numel()),
+                         ctypes.c_void_p(_stream_of(q, stream)))
+    del keep
+    if st != OK:
+        _raise(lib, st)
+    return grads
+
+
+def _bwd_ob_args(q, k, v, bias, window, causal, key_lens, scale, out, dout, lse, grads):
+    args, keep = _ob_args(q, k, v, bias, window, causal, key_lens, scale, out)
+    extra = [_view(x) for x in (dout, lse) + tuple(grads)]
+    return args + [_ref(x) for x in extra], keep + extra
+
+
+def bwd_offset_bias_workspace_size(q, k, v, bias, window, *, out, dout, lse, causal=False,
+                                   key_lens=None, scale=None, want_dbias=True):
+    """Workspace bytes ``bwd_offset_bias`` needs (host only)."""
+    lib = _load()
+    db = _bwd_outputs(q, None, None, bias, q, q, q, None, None, None, False, False,
+                      want_dbias)[5]
+    args, keep = _bwd_ob_args(q, k, v, bias, window, causal, key_lens, scale, out, dout, lse,
+                              (q, q, q, db))
+    n = ctypes.c_size_t(0)
+    st = lib.relattn_bwd_offset_bias_workspace_size(*args, ctypes.byref(n))
+    del keep
+    if st != OK:
+        _raise(lib, st)
+    return int(n.value)
+
+
+def bwd_offset_bias(q, k, v, bias, window, *, out, dout, lse, causal=False, key_lens=None,
+                    scale=None, dq=None, dk=None, dv=None, dbias=None, want_dbias=True,
+                    workspace=None, stream=None):
+    """Gradients for ``fwd_offset_bias_lse``: returns (dq, dk, dv, dbias); dbias
+    float32 like ``bias`` (None when not wanted, e.g. fixed ALiBi slopes)."""
+    import torch
+    lib = _load()
+    _check_lens(key_lens)
+    dq, dk, dv, _, _, db = _bwd_outputs(q, None, None, bias, dq, dk, dv, None, None, dbias,
+                                        False, False, want_dbias)
+    args, keep = _bwd_ob_args(q, k, v, bias, window, causal, key_lens, scale, out, dout, lse,
+                              (dq, dk, dv, db))
+    n = ctypes.c_size_t(0)
+    st = lib.relattn_bwd_offset_bias_workspace_size(*args, ctypes.byref(n))
+    if st != OK:
+        _raise(lib, st)
+    if workspace is None:
+        workspace = torch.empty(max(int(n.value), 1), dtype=torch.uint8, device=q.device)
+    st = lib.relattn_bwd_offset_bias(*args, ctypes.c_void_p(workspace.data_ptr()),
+                                     ctypes.c_size_t(workspace.numel()),
+                                     ctypes.c_void_p(_stream_of(q, stream)))
+    del keep
+    if st != OK:
+        _raise(lib, st)
+    return dq, dk, dv, db
+
+
+def _autograd_fn():
+    import torch
+
+    class _Attention(torch.autograd.Function):
+        @staticmethod
+        def forward(ctx, q, k, v, wK, wV, t5_bias, opts):
+            out, lse = fwd_lse(q, k, v, wK, wV, t5_bias=t5_bias, **opts)
+            ctx.save_for_backward(q, k, v, wK, wV, t5_bias, out, lse)
+            ctx.opts = opts
+            return out
+
+        @staticmethod
+        def backward(ctx, dout):
+            q, k, v, wK, wV, t5_bias, out, lse = ctx.saved_tensors
+            dout = dout.contiguous()
+            g = bwd(q, k, v, wK, wV, t5_bias=t5_bias, out=out, dout=dout, lse=lse,
+                    want_dwk=ctx.needs_input_grad[3], want_dwv=ctx.needs_input_grad[4],
+                    want_dbias=ctx.needs_input_grad[5], **ctx.opts)
+            dq, dk, dv, dwK, dwV, db = g
+            cast = lambda x, ref: None if x is None else x.to(ref.dtype)
+            return dq, dk, dv, cast(dwK, wK), cast(dwV, wV), db, None
+
+    class _AttentionOB(torch.autograd.Function):
+        @staticmethod
+        def forward(ctx, q, k, v, bias, window, opts):
+            out, lse = fwd_offset_bias_lse(q, k, v, bias, window, **opts)
+            ctx.save_for_backward(q, k, v, bias, out, lse)
+            ctx.window, ctx.opts = window, opts
+            return out
+
+        @staticmethod
+        def backward(ctx, dout):
+            q, k, v, bias, out, lse = ctx.saved_tensors
+            dq, dk, dv, db = bwd_offset_bias(q, k, v, bias, ctx.window, out=out,
+                                             dout=dout.contiguous(), lse=lse,
+                                             want_dbias=ctx.needs_input_grad[3], **ctx.opts)
+            return dq, dk, dv, db, None, None
+
+    return _Attention, _AttentionOB
+
+
+_fns = None
+
+
+def attention(q, k, v, wK=None, wV=None, *, clip=0, causal=False, key_lens=None,
+              t5_bias=None, num_buckets=32, max_distance=128, bidirectional=True, scale=None):
+    """Differentiable ``fwd`` (torch.autograd): the forward runs ``fwd_lse``,
+    the backward ``bwd``; gradients flow to q, k, v, the tables and t5_bias."""
+    global _fns
+    if _fns is None:
+        _fns = _autograd_fn()
+    opts = dict(clip=clip, causal=causal, key_lens=key_lens, scale=scale)
+    if t5_bias is not None:
+        opts.update(num_buckets=num_buckets, max_distance=max_distance,
+                    bidirectional=bidirectional)
+    return _fns[0].apply(q, k, v, wK, wV, t5_bias, opts)
+
+
+def attention_offset_bias(q, k, v, bias, window, *, causal=False, key_lens=None, scale=None):
+    """Differentiable ``fwd_offset_bias``."""
+    global _fns
+    if _fns is None:
+        _fns = _autograd_fn()
+    return _fns[1].apply(q, k, v, bias, window,
+                         dict(causal=causal, key_lens=key_lens, scale=scale))

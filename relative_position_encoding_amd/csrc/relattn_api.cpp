@@ -573,9 +573,340 @@ int check_device() {
   return RELATTN_OK;
 }
 
+// ---- backward ---------------------------------------------------------------
+
+int check_like_q(const relattn_tensor* t, const char* name, const relattn_tensor* q) {
+  int st = check_view(t, name, 4, true);
+  if (st) return st;
+  if (t->dtype != q->dtype) return fail(RELATTN_ERR_INVALID_ARGUMENT, "%s dtype differs from q", name);
+  for (int i = 0; i < 4; ++i)
+    if (t->shape[i] != q->shape[i])
+      return fail(RELATTN_ERR_INVALID_ARGUMENT, "%s shape differs from q in dim %d", name, i);
+  return RELATTN_OK;
+}
+
+int check_f32(const relattn_tensor* t, const char* name, int ndim, const int64_t* shape) {
+  int st = check_view(t, name, ndim, false);
+  if (st) return st;
+  if (t->dtype != RELATTN_F32) return fail(RELATTN_ERR_INVALID_ARGUMENT, "%s must be F32", name);
+  for (int i = 0; i < ndim; ++i)
+    if (t->shape[i] != shape[i])
+      return fail(RELATTN_ERR_INVALID_ARGUMENT, "%s: shape[%d] must be %lld, got %lld", name, i,
+                  (long long)shape[i], (long long)t->shape[i]);
+  return RELATTN_OK;
+}
+
+// lse output/input of shape [B, H, n]
+int check_lse(const relattn_tensor* lse, const relattn_tensor* q) {
+  if (!lse) return fail(RELATTN_ERR_INVALID_ARGUMENT, "lse is NULL");
+  const int64_t shp[3] = {q->shape[0], q->shape[1], q->shape[2]};
+  return check_f32(lse, "lse", 3, shp);
+}
+
+struct BwdPlan {
+  Plan fwd;
+  relattn::BwdCfg cfg{};
+  relattn::BwdParams p{};
+  size_t ws_bytes = 0;
+  size_t off_stat = 0, off_rl = 0, off_rv = 0, off_pk = 0, off_pv = 0, off_pb = 0;
+};
+
+int make_bwd_plan(const relattn_tensor* q, const relattn_tensor* k, const relattn_tensor* v,
+                  const relattn_tensor* wK, const relattn_tensor* wV,
+                  const relattn_tensor* t5_bias, const relattn_t5_params* t5, int32_t clip_k,
+                  float scale, const relattn_mask* mask, const relattn_tensor* out,
+                  const relattn_tensor* dout, const relattn_tensor* lse,
+                  const relattn_tensor* dq, const relattn_tensor* dk, const relattn_tensor* dv,
+                  const relattn_tensor* dwK, const relattn_tensor* dwV,
+                  const relattn_tensor* dbias, BwdPlan* plan, bool want_t5_table,
+                  const relattn_tensor* ob = nullptr, int32_t ob_window = 0) {
+  Plan& F = plan->fwd;
+  int st = make_plan(q, k, v, wK, wV, t5_bias, t5, clip_k, scale, mask, out, &F, want_t5_table,
+                     ob, ob_window);
+  if (st) return st;
+  if ((st = check_like_q(dout, "dout", q))) return st;
+  if ((st = check_like_q(dq, "dq", q))) return st;
+  if ((st = check_like_q(dk, "dk", q))) return st;
+  if ((st = check_like_q(dv, "dv", q))) return st;
+  if ((st = check_lse(lse, q))) return st;
+  const int64_t B = q->shape[0], H = q->shape[1], n = q->shape[2], d = q->shape[3];
+  if (dwK) {
+    if (!wK) return fail(RELATTN_ERR_INVALID_ARGUMENT, "dwK given without wK");
+    const int64_t shp[3] = {wK->shape[0], 2 * (int64_t)clip_k + 1, d};
+    if ((st = check_f32(dwK, "dwK", 3, shp))) return st;
+  }
+  if (dwV) {
+    if (!wV) return fail(RELATTN_ERR_INVALID_ARGUMENT, "dwV given without wV");
+    const int64_t shp[3] = {wV->shape[0], 2 * (int64_t)clip_k + 1, d};
+    if ((st = check_f32(dwV, "dwV", 3, shp))) return st;
+  }
+  if (dbias) {
+    if (!t5_bias && !ob)
+      return fail(RELATTN_ERR_INVALID_ARGUMENT, "dbias given without a bias table");
+    const int64_t shp[2] = {t5_bias ? t5_bias->shape[0] : ob->shape[0],
+                            t5_bias ? t5_bias->shape[1] : ob->shape[1]};
+    if ((st = check_f32(dbias, "dbias", 2, shp))) return st;
+  }
+  if (F.empty) return RELATTN_OK;
+
+  const relattn::FwdParams& f = F.p;
+  relattn::BwdParams& p = plan->p;
+  relattn::BwdCfg& cfg = plan->cfg;
+  cfg = relattn::bwd_cfg(F.bf16, F.d, false, false);
+  p.B = f.B;
+  p.H = f.H;
+  p.n = f.n;
+  p.d = (int32_t)d;
+  p.n_pad = (int32_t)((n + 63) / 64 * 64);
+  p.clip = f.clip;
+  p.r_lo = f.r_lo;
+  p.nr = f.nr;
+  p.nrp = (f.nr + 7) / 8 * 8;
+  p.htk = wK ? (int32_t)wK->shape[0] : 0;
+  p.htv = wV ? (int32_t)wV->shape[0] : 0;
+  p.hb = ob ? (int32_t)ob->shape[0] : (int32_t)H;
+  p.causal = f.causal;
+  p.key_lens = f.key_lens;
+  const bool is_t5 = t5_bias != nullptr;
+  p.scale = scale > 0.f ? scale : (is_t5 ? 1.f : 1.f / std::sqrt((float)d));
+  p.scale_log2 = f.scale_log2;
+  p.t5_dist = f.t5_dist;
+  p.ob = f.ob;
+  p.ob_lo = f.ob_lo;
+  p.ob_w = ob ? ob_window : 0;
+  p.t5 = f.t5;
+  p.t5_bias = f.t5_bias;
+  p.tb_sb = f.tb_sb;
+  p.tb_sh = f.tb_sh;
+  p.q = f.q;
+  p.k = f.k;
+  p.v = f.v;
+  p.o = f.o;
+  p.wk = f.wk;
+  p.wv = f.wv;
+  p.wk_sh = f.wk_sh;
+  p.wk_sr = f.wk_sr;
+  p.wv_sh = f.wv_sh;
+  p.wv_sr = f.wv_sr;
+  p.q_sb = f.q_sb; p.q_sh = f.q_sh; p.q_sn = f.q_sn;
+  p.k_sb = f.k_sb; p.k_sh = f.k_sh; p.k_sn = f.k_sn;
+  p.v_sb = f.v_sb; p.v_sh = f.v_sh; p.v_sn = f.v_sn;
+  p.o_sb = f.o_sb; p.o_sh = f.o_sh; p.o_sn = f.o_sn;
+  p.dout = dout->data;
+  p.do_sb = dout->stride[0]; p.do_sh = dout->stride[1]; p.do_sn = dout->stride[2];
+  p.dq = dq->data;
+  p.dq_sb = dq->stride[0]; p.dq_sh = dq->stride[1]; p.dq_sn = dq->stride[2];
+  p.dk = dk->data;
+  p.dk_sb = dk->stride[0]; p.dk_sh = dk->stride[1]; p.dk_sn = dk->stride[2];
+  p.dv = dv->data;
+  p.dv_sb = dv->stride[0]; p.dv_sh = dv->stride[1]; p.dv_sn = dv->stride[2];
+  p.lse = static_cast<const float*>(lse->data);
+  p.lse_sb = lse->stride[0];
+  p.lse_sh = lse->stride[1];
+  if ((lse->stride[2]) != 1)
+    return fail(RELATTN_ERR_UNSUPPORTED, "lse: innermost dimension must be contiguous");
+  if (dwK) {
+    p.dwk = static_cast<float*>(dwK->data);
+    p.dwk_sh = dwK->stride[0];
+    p.dwk_sr = dwK->stride[1];
+  }
+  if (dwV) {
+    p.dwv = static_cast<float*>(dwV->data);
+    p.dwv_sh = dwV->stride[0];
+    p.dwv_sr = dwV->stride[1];
+  }
+  if (dbias) {
+    p.db = static_cast<float*>(dbias->data);
+    p.db_s0 = dbias->stride[0];
+    p.db_s1 = dbias->stride[1];
+  }
+  const bool shaw = F.mode == relattn::kRelShaw, t5m = F.mode == relattn::kRelT5;
+  const bool want_db = t5m && dbias != nullptr;
+  // the wide workgroup shapes unless their LDS does not fit
+  size_t lq = relattn::bwd_lds_q(F.bf16, F.d, cfg, F.mode, F.has_wk, F.has_wv, p.nr, p.t5_dist,
+                                 p.t5.nb, want_db);
+  size_t lkv = relattn::bwd_lds_kv(F.bf16, F.d, cfg, F.mode, F.has_wk, F.has_wv, p.nrp,
+                                   p.t5_dist);
+  if (lq > kMaxLdsBytes || lkv > kMaxLdsBytes) {
+    cfg = relattn::bwd_cfg(F.bf16, F.d, lq > kMaxLdsBytes, lkv > kMaxLdsBytes);
+    lq = relattn::bwd_lds_q(F.bf16, F.d, cfg, F.mode, F.has_wk, F.has_wv, p.nr, p.t5_dist,
+                            p.t5.nb, want_db);
+    lkv = relattn::bwd_lds_kv(F.bf16, F.d, cfg, F.mode, F.has_wk, F.has_wv, p.nrp, p.t5_dist);
+  }
+  const int64_t brq = 32 * cfg.qwaves, brk = 32 * cfg.kwaves;
+  p.n_qtiles = (int32_t)((n + brq - 1) / brq);
+  p.n_ktiles = (int32_t)((n + brk - 1) / brk);
+  if (B * H * (int64_t)std::max(p.n_qtiles, p.n_ktiles) > INT32_MAX)
+    return fail(RELATTN_ERR_UNSUPPORTED, "too many workgroups");
+  if (lq > kMaxLdsBytes || lkv > kMaxLdsBytes)
+    return fail(RELATTN_ERR_UNSUPPORTED,
+                "backward: per-workgroup state of %zu / %zu bytes exceeds on-chip memory "
+                "(label window %d rows, offset window %d)",
+                lq, lkv, p.nr, 2 * p.t5_dist + 1);
+
+  // workspace sections (fp32), 256-byte aligned
+  size_t off = 0;
+  auto take = [&](int64_t floats) {
+    const size_t at = off;
+    off += ((size_t)floats * 4 + 255) / 256 * 256;
+    return at;
+  };
+  const int64_t BH = B * H;
+  plan->off_stat = take(BH * 2 * p.n_pad + 64);
+  plan->off_rl = (shaw && F.has_wk) ? take(BH * p.n_pad * p.nrp) : 0;
+  plan->off_rv = (shaw && F.has_wv) ? take(BH * p.n_pad * p.nrp) : 0;
+  plan->off_pk = (shaw && F.has_wk) ? take(BH * p.n_qtiles * p.nr * d) : 0;
+  plan->off_pv = (shaw && F.has_wv) ? take(BH * p.n_qtiles * p.nr * d) : 0;
+  plan->off_pb = want_db ? take(BH * p.n_qtiles * p.t5.nb) : 0;
+  plan->ws_bytes = off;
+  return RELATTN_OK;
+}
+
+int run_bwd(BwdPlan& plan, const relattn_tensor* wK, const relattn_tensor* wV, bool want_db,
+            void* workspace, size_t workspace_bytes, void* stream) {
+  if (plan.fwd.empty) return RELATTN_OK;
+  if (workspace_bytes < plan.ws_bytes)
+    return fail(RELATTN_ERR_INVALID_ARGUMENT, "workspace of %zu bytes, %zu needed",
+                workspace_bytes, plan.ws_bytes);
+  if (!workspace || !aligned16(workspace))
+    return fail(RELATTN_ERR_INVALID_ARGUMENT, "workspace is NULL or not 16-byte aligned");
+  int st;
+  if ((st = check_device())) return st;
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  relattn::BwdParams& p = plan.p;
+  const bool shaw = plan.fwd.mode == relattn::kRelShaw;
+  p.ws_stat = reinterpret_cast<float*>(ws + plan.off_stat);
+  p.ws_rl = (shaw && wK) ? reinterpret_cast<float*>(ws + plan.off_rl) : nullptr;
+  p.ws_rv = (shaw && wV) ? reinterpret_cast<float*>(ws + plan.off_rv) : nullptr;
+  p.ws_pk = (shaw && wK) ? reinterpret_cast<float*>(ws + plan.off_pk) : nullptr;
+  p.ws_pv = (shaw && wV) ? reinterpret_cast<float*>(ws + plan.off_pv) : nullptr;
+  p.ws_pb = want_db ? reinterpret_cast<float*>(ws + plan.off_pb) : nullptr;
+  const int e = relattn::launch_bwd(plan.fwd.bf16, plan.fwd.d, plan.cfg, plan.fwd.mode,
+                                    plan.fwd.has_wk, plan.fwd.has_wv, p, stream);
+  if (e != (int)hipSuccess)
+    return fail(RELATTN_ERR_LAUNCH_FAILED, "launch failed: %s", hipGetErrorString((hipError_t)e));
+  return RELATTN_OK;
+}
+
+int run_fwd_lse(Plan& plan, const relattn_tensor* lse, void* stream) {
+  if (plan.empty) return RELATTN_OK;
+  if (lse->stride[2] != 1)
+    return fail(RELATTN_ERR_UNSUPPORTED, "lse: innermost dimension must be contiguous");
+  int st;
+  if ((st = check_device())) return st;
+  plan.p.lse = static_cast<float*>(lse->data);
+  plan.p.lse_sb = lse->stride[0];
+  plan.p.lse_sh = lse->stride[1];
+  const int e = relattn::launch_fwd(plan.bf16, plan.d, plan.cfg, plan.mode, plan.has_wk,
+                                    plan.has_wv, plan.p, stream);
+  if (e != (int)hipSuccess)
+    return fail(RELATTN_ERR_LAUNCH_FAILED, "launch failed: %s", hipGetErrorString((hipError_t)e));
+  return RELATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+int relattn_fwd_lse(const relattn_tensor* q, const relattn_tensor* k, const relattn_tensor* v,
+                    const relattn_tensor* wK, const relattn_tensor* wV,
+                    const relattn_tensor* t5_bias, const relattn_t5_params* t5, int32_t clip_k,
+                    float scale, const relattn_mask* mask, relattn_tensor* out,
+                    relattn_tensor* lse, void* stream) {
+  g_last_error.clear();
+  Plan plan;
+  int st = make_plan(q, k, v, wK, wV, t5_bias, t5, clip_k, scale, mask, out, &plan, true);
+  if (st) return st;
+  if ((st = check_lse(lse, q))) return st;
+  return run_fwd_lse(plan, lse, stream);
+}
+
+int relattn_fwd_offset_bias_lse(const relattn_tensor* q, const relattn_tensor* k,
+                                const relattn_tensor* v, const relattn_tensor* bias,
+                                int32_t window, float scale, const relattn_mask* mask,
+                                relattn_tensor* out, relattn_tensor* lse, void* stream) {
+  g_last_error.clear();
+  if (!bias) return fail(RELATTN_ERR_INVALID_ARGUMENT, "bias is NULL");
+  Plan plan;
+  int st = make_plan(q, k, v, nullptr, nullptr, nullptr, nullptr, 0, scale, mask, out, &plan, true,
+                     bias, window);
+  if (st) return st;
+  if ((st = check_lse(lse, q))) return st;
+  return run_fwd_lse(plan, lse, stream);
+}
+
+int relattn_bwd_workspace_size(const relattn_tensor* q, const relattn_tensor* k,
+                               const relattn_tensor* v, const relattn_tensor* wK,
+                               const relattn_tensor* wV, const relattn_tensor* t5_bias,
+                               const relattn_t5_params* t5, int32_t clip_k, float scale,
+                               const relattn_mask* mask, const relattn_tensor* out,
+                               const relattn_tensor* dout, const relattn_tensor* lse,
+                               const relattn_tensor* dq, const relattn_tensor* dk,
+                               const relattn_tensor* dv, const relattn_tensor* dwK,
+                               const relattn_tensor* dwV, const relattn_tensor* dbias,
+                               size_t* bytes) {
+  g_last_error.clear();
+  if (!bytes) return fail(RELATTN_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  BwdPlan plan;
+  const int st = make_bwd_plan(q, k, v, wK, wV, t5_bias, t5, clip_k, scale, mask, out, dout, lse,
+                               dq, dk, dv, dwK, dwV, dbias, &plan, true);
+  if (st) return st;
+  *bytes = plan.fwd.empty ? 0 : plan.ws_bytes;
+  return RELATTN_OK;
+}
+
+int relattn_bwd(const relattn_tensor* q, const relattn_tensor* k, const relattn_tensor* v,
+                const relattn_tensor* wK, const relattn_tensor* wV,
+                const relattn_tensor* t5_bias, const relattn_t5_params* t5, int32_t clip_k,
+                float scale, const relattn_mask* mask, const relattn_tensor* out,
+                const relattn_tensor* dout, const relattn_tensor* lse, relattn_tensor* dq,
+                relattn_tensor* dk, relattn_tensor* dv, relattn_tensor* dwK, relattn_tensor* dwV,
+                relattn_tensor* dbias, void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  BwdPlan plan;
+  const int st = make_bwd_plan(q, k, v, wK, wV, t5_bias, t5, clip_k, scale, mask, out, dout, lse,
+                               dq, dk, dv, dwK, dwV, dbias, &plan, true);
+  if (st) return st;
+  return run_bwd(plan, wK, wV, t5_bias != nullptr && dbias != nullptr, workspace,
+                 workspace_bytes, stream);
+}
+
+int relattn_bwd_offset_bias_workspace_size(const relattn_tensor* q, const relattn_tensor* k,
+                                           const relattn_tensor* v, const relattn_tensor* bias,
+                                           int32_t window, float scale, const relattn_mask* mask,
+                                           const relattn_tensor* out, const relattn_tensor* dout,
+                                           const relattn_tensor* lse, const relattn_tensor* dq,
+                                           const relattn_tensor* dk, const relattn_tensor* dv,
+                                           const relattn_tensor* dbias, size_t* bytes) {
+  g_last_error.clear();
+  if (!bytes) return fail(RELATTN_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  if (!bias) return fail(RELATTN_ERR_INVALID_ARGUMENT, "bias is NULL");
+  BwdPlan plan;
+  const int st = make_bwd_plan(q, k, v, nullptr, nullptr, nullptr, nullptr, 0, scale, mask, out,
+                               dout, lse, dq, dk, dv, nullptr, nullptr, dbias, &plan, true, bias,
+                               window);
+  if (st) return st;
+  *bytes = plan.fwd.empty ? 0 : plan.ws_bytes;
+  return RELATTN_OK;
+}
+
+int relattn_bwd_offset_bias(const relattn_tensor* q, const relattn_tensor* k,
+                            const relattn_tensor* v, const relattn_tensor* bias, int32_t window,
+                            float scale, const relattn_mask* mask, const relattn_tensor* out,
+                            const relattn_tensor* dout, const relattn_tensor* lse,
+                            relattn_tensor* dq, relattn_tensor* dk, relattn_tensor* dv,
+                            relattn_tensor* dbias, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  g_last_error.clear();
+  if (!bias) return fail(RELATTN_ERR_INVALID_ARGUMENT, "bias is NULL");
+  BwdPlan plan;
+  const int st = make_bwd_plan(q, k, v, nullptr, nullptr, nullptr, nullptr, 0, scale, mask, out,
+                               dout, lse, dq, dk, dv, nullptr, nullptr, dbias, &plan, true, bias,
+                               window);
+  if (st) return st;
+  return run_bwd(plan, nullptr, nullptr, dbias != nullptr, workspace, workspace_bytes, stream);
+}
+
 
 int relattn_validate(const relattn_tensor* q, const relattn_tensor* k, const relattn_tensor* v,
                      const relattn_tensor* wK, const relattn_tensor* wV,

@@ -20,6 +20,7 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 #define RELATTN_CONST __attribute__((address_space(4)))
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegInf = -__builtin_inff();
 
 // 2^x with the hardware exponential (about 1 ulp; results below 2^-126,

@@ -56,6 +56,10 @@ struct FwdParams {
   // = W - t5_dist are loaded).
   int32_t ob;
   int32_t ob_lo;
+  // Optional row statistics: lse[b * lse_sb + h * lse_sh + i] receives the
+  // natural-log log-sum-exp of row i's visible logits (-inf for none).
+  float* lse;
+  int64_t lse_sb, lse_sh;
   T5Buckets t5;
 };
 
@@ -84,6 +88,88 @@ int launch_fwd(bool bf16, int d, const LaunchCfg& cfg, RelMode mode, bool has_wk
                bool has_wv, const FwdParams& p, void* stream);
 int launch_debug_indices(int n, int clip, const T5Buckets* t5, int32_t* out,
                          void* stream);
+
+// ---- backward (relattn_backward.hip) --------------------------------------
+
+// Everything the three backward launches need.  Strides count elements.
+// Workspace sections (fp32):
+//   ws_stat [B*H][2][n_pad] + 64 : per query, lse in log2 units and D = dz.z
+//   ws_rl   [B*H][n_pad][nrp]    : relative logits (log2 units) of labels r_lo..
+//   ws_rv   [B*H][n_pad][nrp]    : dz_i . w^V_r
+//   ws_pk   [B*H][n_qtiles][nr][d], ws_pv the same : per query-tile partial
+//                                  table gradients (ws_pk already scaled)
+//   ws_pb   [B*H][n_qtiles][nb]  : per query-tile partial bias gradients
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;            // forward output z
+  const void* dout;         // dz
+  const float* lse;         // [B, H, n] natural log
+  const void* wk;
+  const void* wv;
+  const float* t5_bias;
+  const int32_t* key_lens;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dwk;               // [Htk, 2c+1, d] or null
+  float* dwv;
+  float* db;                // T5: [NB, H]; offset bias: [Hb, 2W+1]; or null
+  float* ws_stat;
+  float* ws_rl;
+  float* ws_rv;
+  float* ws_pk;
+  float* ws_pv;
+  float* ws_pb;
+
+  int64_t q_sb, q_sh, q_sn;
+  int64_t k_sb, k_sh, k_sn;
+  int64_t v_sb, v_sh, v_sn;
+  int64_t o_sb, o_sh, o_sn;
+  int64_t do_sb, do_sh, do_sn;
+  int64_t dq_sb, dq_sh, dq_sn;
+  int64_t dk_sb, dk_sh, dk_sn;
+  int64_t dv_sb, dv_sh, dv_sn;
+  int64_t lse_sb, lse_sh;
+  int64_t wk_sh, wk_sr;
+  int64_t wv_sh, wv_sr;
+  int64_t tb_sb, tb_sh;
+  int64_t dwk_sh, dwk_sr;   // output table gradients
+  int64_t dwv_sh, dwv_sr;
+  int64_t db_s0, db_s1;     // bias gradient strides (dims 0 and 1 of its shape)
+
+  int32_t B, H, n, d;
+  int32_t n_pad;            // n rounded up to 64
+  int32_t clip;
+  int32_t r_lo, nr, nrp;    // reachable labels [r_lo, r_lo + nr); nrp = row stride
+  int32_t htk, htv;         // table heads (H or 1)
+  int32_t hb;               // bias gradient heads (offset bias: H or 1)
+  int32_t causal;
+  float scale;              // logit scale s
+  float scale_log2;         // s * log2(e)
+  int32_t t5_dist;
+  int32_t ob, ob_lo, ob_w;  // offset bias: window W of the table
+  int32_t n_qtiles;         // query tiles per (b, h) of the dq kernel
+  int32_t n_ktiles;         // key tiles per (b, h) of the dk/dv kernel
+  T5Buckets t5;
+};
+
+struct BwdCfg {
+  int qwaves, qkblock;  // dq kernel: waves (32 query rows each), keys per tile
+  int kwaves, kqblock;  // dk/dv kernel: waves (32 key rows each), queries per tile
+};
+
+// Workgroup shapes the backward kernels are built with: the wide ones, or the
+// narrow ones (half the query rows of the dq kernel, or half the queries per
+// tile of the dk/dv kernel) that fit larger label windows on chip.
+BwdCfg bwd_cfg(bool bf16, int d, bool narrow_q, bool narrow_kv);
+size_t bwd_lds_q(bool bf16, int d, const BwdCfg& cfg, RelMode mode, bool has_wk, bool has_wv,
+                 int nr, int t5_dist, int nb, bool want_db);
+size_t bwd_lds_kv(bool bf16, int d, const BwdCfg& cfg, RelMode mode, bool has_wk, bool has_wv,
+                  int nrp, int t5_dist);
+int launch_bwd(bool bf16, int d, const BwdCfg& cfg, RelMode mode, bool has_wk, bool has_wv,
+               const BwdParams& p, void* stream);
 
 // ---- incremental decoding (relattn_decode.hip) ----------------------------
 
