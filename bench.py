@@ -13,7 +13,8 @@ stream of fresh batches would.
 Prints ONE JSON line: TFLOP/s of the headline workload (Transformer-big
 decoder causal self-attention with key and value tables), its fraction of the
 bf16 MFMA peak, the HBM roofline of the kernel, the fp64 oracle timed on the
-host cores, and the same figures for the other Transformer shapes.
+host cores, the same figures for the other Transformer shapes, and those of
+incremental decoding, of the offset-bias (ALiBi) arm and of the backward.
 """
 from __future__ import annotations
 
@@ -327,6 +328,137 @@ def alibi_report(ra, steps):
             "alg_gflop_per_step": round(cold["alg_gflop"], 4), "steps_per_rep": steps}
 
 
+# ---------------------------------------------------------------------------
+# backward (relattn_bwd: dq/dk/dv kernels and the table-gradient reduction)
+# ---------------------------------------------------------------------------
+
+BWD_SRC = os.path.join(ROOT, "relative_position_encoding_amd", "csrc", "relattn_backward.hip")
+
+
+def bwd_work(w, key_lens):
+    """(flops, bytes) one backward call must do.
+
+    flops: 10*d per visible pair (the logits again, dP = dz.v, and the dV,
+    dK and dQ products) plus, per query row and reachable label, 2*d for each
+    of: the relative logit q.w^K (again), dQ's G w^K term and dw^K's q G term
+    (key table); dz.w^V and dw^V's dz W term (value table).  bytes: q, k, v,
+    the output z and dz read once; dq, dk, dv written once; the tables read
+    and their gradients (fp32) written once; the row log-sum-exp read once.
+    """
+    import numpy as np
+    B, H, n, d = w.batch, w.heads, w.n, w.d
+    esz = w.dtype.itemsize
+    lens = [n] * B if key_lens is None else [int(x) for x in key_lens]
+    pairs = 0
+    for L in lens:
+        i = np.arange(n)
+        pairs += int((np.minimum(i + 1, L) if w.causal else np.full(n, L)).sum())
+    flops = 10.0 * d * pairs * H
+    tab_bytes = 0.0
+    if w.t5 is None:
+        R = min(w.clip + 1, n) if w.causal else min(2 * w.clip + 1, 2 * n - 1)
+        per = 3 * int(w.use_key_table) + 2 * int(w.use_value_table)
+        flops += 2.0 * d * n * R * per * B * H
+        ntab = int(w.use_key_table) + int(w.use_value_table)
+        tab_bytes = ntab * H * (2 * w.clip + 1) * d * (esz + 4)
+    else:
+        tab_bytes = 2 * w.t5["num_buckets"] * H * 4
+    nbytes = 8.0 * B * H * n * d * esz + 4.0 * B * H * n + tab_bytes
+    return flops, nbytes
+
+
+def time_bwd(ra, w, steps, warmup, hot=False, reps=5):
+    """Time ``steps`` back-to-back relattn_bwd calls (median of ``reps``
+    timed regions); cold: the calls cycle through enough input copies to
+    exceed twice the last-level cache; hot: one input set."""
+    import statistics
+    import torch
+    import workloads
+    lib = ra._load()
+    stream = torch.cuda.Stream()  # default priority
+    x = workloads.make_inputs(w)
+    flops, nbytes = bwd_work(w, x["key_lens"])
+    copies = 1 if hot else max(1, min(16, int(2 * LLC_BYTES // nbytes) + 1))
+    g0 = torch.Generator().manual_seed(20260009)
+    dz_cpu = torch.randn(x["q"].shape, generator=g0).to(x["q"].dtype)
+    calls, keep = [], []
+    t5 = w.t5 or {}
+    for _ in range(copies):
+        g = {k: (t.to("cuda").clone() if t is not None else None) for k, t in x.items()}
+        dz = dz_cpu.to("cuda")
+        kw = dict(clip=w.clip, causal=w.causal, key_lens=g["key_lens"])
+        if w.t5 is not None:
+            kw.update(t5_bias=g["t5_bias"], **t5)
+        out, lse = ra.fwd_lse(g["q"], g["k"], g["v"], g["key_table"], g["value_table"], **kw)
+        grads = ra._bwd_outputs(g["q"], g["key_table"], g["value_table"], g["t5_bias"], None,
+                                None, None, None, None, None, True, True, True)
+        args, kp = ra._bwd_args(g["q"], g["k"], g["v"], g["key_table"], g["value_table"],
+                                g["t5_bias"], w.clip, w.causal, g["key_lens"],
+                                t5.get("num_buckets", 32), t5.get("max_distance", 128),
+                                t5.get("bidirectional", True), None, out, dz, lse, grads)
+        need = ctypes.c_size_t(0)
+        if lib.relattn_bwd_workspace_size(*args, ctypes.byref(need)) != 0:
+            raise RuntimeError(ra.last_error())
+        ws = torch.empty(max(need.value, 1), dtype=torch.uint8, device="cuda")
+        calls.append(args + [ctypes.c_void_p(ws.data_ptr()), ctypes.c_size_t(need.value),
+                             ctypes.c_void_p(stream.cuda_stream)])
+        keep += [g, dz, out, lse, grads, kp, ws]
+    torch.cuda.synchronize()
+    fn = lib.relattn_bwd
+    times = []
+    with torch.cuda.stream(stream):
+        for s_ in range(warmup):
+            if fn(*calls[s_ % copies]) != 0:
+                raise RuntimeError(ra.last_error())
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        for _ in range(reps):
+            t0.record(stream)
+            for s_ in range(steps):
+                fn(*calls[s_ % copies])
+            t1.record(stream)
+            torch.cuda.synchronize()
+            times.append(t0.elapsed_time(t1) / steps)
+    del keep
+    ms = statistics.median(times)
+    sec = ms * 1e-3
+    return {"ms_per_step": ms, "tflops": flops / sec / 1e12, "hbm_gbs": nbytes / sec / 1e9,
+            "alg_gflop": flops / 1e9, "alg_mbytes": nbytes / 1e6, "input_copies": copies,
+            "workspace_mbytes": need.value / 1e6}
+
+
+def bwd_report(ra, steps, name=HEADLINE):
+    """The backward's figures on a workload (the headline's by default)."""
+    import workloads
+    w = workloads.WORKLOADS[name]
+    cold = time_bwd(ra, w, steps, 10)
+    hot = time_bwd(ra, w, steps, 10, hot=True)
+    flops, nbytes = cold["alg_gflop"] * 1e9, cold["alg_mbytes"] * 1e6
+    bound = bound_of(flops, nbytes, "bf16" if w.dtype.itemsize == 2 else "f32")
+    sec = cold["ms_per_step"] * 1e-3
+    dt = "bf16" if w.dtype.itemsize == 2 else "f32"
+    if bound == "hbm":
+        ach, peak, unit = nbytes / sec / 1e9, PEAK_HBM_GBS, "GB/s"
+    else:
+        ach, peak, unit = flops / sec / 1e12, PEAK_TFLOPS[dt], "TFLOP/s"
+    tr = traffic_per_launch("bwd_" + name)
+    return {"workload": w.description, "ms_per_step": round(cold["ms_per_step"], 5),
+            "tflops": round(cold["tflops"], 3),
+            "mfma_peak_frac": round(cold["tflops"] / PEAK_TFLOPS[dt], 4),
+            "roofline": {"bound": bound, "achieved": round(ach, 2), "peak": peak, "unit": unit,
+                         "frac": round(ach / peak, 4),
+                         "traffic": None if tr is None else round(tr)},
+            "roofline_frac": round(cold["tflops"] / ceiling_tflops(flops, nbytes, dt), 4),
+            "hbm_gbs": round(cold["hbm_gbs"], 1), "hot_ms_per_step": round(hot["ms_per_step"], 5),
+            "alg_gflop_per_step": round(cold["alg_gflop"], 4),
+            "alg_mbytes_per_step": round(cold["alg_mbytes"], 3),
+            "workspace_mbytes": round(cold["workspace_mbytes"], 3),
+            "input_copies": cold["input_copies"], "steps_per_rep": steps,
+            "kernels": "bwd_q_kernel (dq, label sums, table partials) + bwd_kv_kernel (dk, dv) "
+                       "+ bwd_reduce_kernel (table gradients)"}
+
+
 def bound_of(flops, nbytes, dt):
     ridge = PEAK_TFLOPS[dt] * 1e12 / (PEAK_HBM_GBS * 1e9)
     return "hbm" if flops / nbytes < ridge else "mfma"
@@ -349,7 +481,8 @@ def traffic_per_launch(name):
         return None
     with open(path) as f:
         t = json.load(f)
-    if t.get("kernel_sha256") != kernel_sha(DECODE_SRC if name == "decode" else KERNEL_SRC):
+    src = DECODE_SRC if name == "decode" else (BWD_SRC if name.startswith("bwd_") else KERNEL_SRC)
+    if t.get("kernel_sha256") != kernel_sha(src):
         return None
     return t["fetch_kib"] * 1024 * t["fetch_scale"] + t["write_kib"] * 1024 * t["write_scale"]
 
@@ -467,6 +600,18 @@ def oracle_report(per_workload_s=2.0):
     el = (time.perf_counter() - t0) / 8
     rep["decode"] = {"bruteforce_s_per_row": round(el, 6), "bruteforce_rows": 8,
                      "bruteforce_s_per_step": round(el * wd.batch * wd.heads * wd.tq, 3)}
+    # backward: the chain-rule oracle on 4 heads of the headline workload
+    w = workloads.WORKLOADS[HEADLINE]
+    x = workloads.make_inputs(w)
+    dz = x["q"].float()
+    t0 = time.perf_counter()
+    for h in range(4):
+        sl = lambda t: t[0:1, h:h + 1]
+        oracle.relattn_backward(sl(x["q"]), sl(x["k"]), sl(x["v"]), x["key_table"][h:h + 1],
+                                x["value_table"][h:h + 1], w.clip, sl(dz), causal=w.causal)
+    el = (time.perf_counter() - t0) / 4
+    rep["backward_" + HEADLINE] = {"s_per_head": round(el, 6), "sample_heads": 4,
+                                   "s_per_call": round(el * w.batch * w.heads, 3)}
     return rep
 
 
@@ -521,6 +666,8 @@ def main():
                     help="time the decode workload only and print its figures")
     ap.add_argument("--alibi-only", action="store_true",
                     help="time the offset-bias (ALiBi) workload only and print its figures")
+    ap.add_argument("--bwd-only", action="store_true",
+                    help="time the backward on --workload only and print its figures")
     a = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if a.gpus != 1 or world != 1:
@@ -543,6 +690,9 @@ def main():
         return
     if a.alibi_only:
         print(json.dumps({"offset_bias": alibi_report(ra, max(50, a.steps // 5))}))
+        return
+    if a.bwd_only:
+        print(json.dumps({"backward": bwd_report(ra, max(50, a.steps // 5), a.workload)}))
         return
 
     if gpu is not None and not gpu.get("name"):
@@ -605,6 +755,7 @@ def main():
         line["workloads"] = per
         line["decode"] = decode_report(ra, max(50, a.steps // 5))
         line["offset_bias"] = alibi_report(ra, max(50, a.steps // 5))
+        line["backward"] = bwd_report(ra, max(50, a.steps // 5))
     if not a.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w)
         if not a.only:
