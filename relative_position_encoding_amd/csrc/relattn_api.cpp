@@ -608,7 +608,7 @@ struct BwdPlan {
   relattn::BwdCfg cfg{};
   relattn::BwdParams p{};
   size_t ws_bytes = 0;
-  size_t off_stat = 0, off_rl = 0, off_rv = 0, off_pk = 0, off_pv = 0, off_pb = 0;
+  size_t off_stat = 0, off_pk = 0, off_pv = 0, off_pb = 0;
 };
 
 int make_bwd_plan(const relattn_tensor* q, const relattn_tensor* k, const relattn_tensor* v,
@@ -661,7 +661,6 @@ int make_bwd_plan(const relattn_tensor* q, const relattn_tensor* k, const relatt
   p.clip = f.clip;
   p.r_lo = f.r_lo;
   p.nr = f.nr;
-  p.nrp = (f.nr + 7) / 8 * 8;
   p.htk = wK ? (int32_t)wK->shape[0] : 0;
   p.htv = wV ? (int32_t)wV->shape[0] : 0;
   p.hb = ob ? (int32_t)ob->shape[0] : (int32_t)H;
@@ -725,13 +724,13 @@ int make_bwd_plan(const relattn_tensor* q, const relattn_tensor* k, const relatt
   // the wide workgroup shapes unless their LDS does not fit
   size_t lq = relattn::bwd_lds_q(F.bf16, F.d, cfg, F.mode, F.has_wk, F.has_wv, p.nr, p.t5_dist,
                                  p.t5.nb, want_db);
-  size_t lkv = relattn::bwd_lds_kv(F.bf16, F.d, cfg, F.mode, F.has_wk, F.has_wv, p.nrp,
+  size_t lkv = relattn::bwd_lds_kv(F.bf16, F.d, cfg, F.mode, F.has_wk, F.has_wv, p.nr,
                                    p.t5_dist);
   if (lq > kMaxLdsBytes || lkv > kMaxLdsBytes) {
     cfg = relattn::bwd_cfg(F.bf16, F.d, lq > kMaxLdsBytes, lkv > kMaxLdsBytes);
     lq = relattn::bwd_lds_q(F.bf16, F.d, cfg, F.mode, F.has_wk, F.has_wv, p.nr, p.t5_dist,
                             p.t5.nb, want_db);
-    lkv = relattn::bwd_lds_kv(F.bf16, F.d, cfg, F.mode, F.has_wk, F.has_wv, p.nrp, p.t5_dist);
+    lkv = relattn::bwd_lds_kv(F.bf16, F.d, cfg, F.mode, F.has_wk, F.has_wv, p.nr, p.t5_dist);
   }
   const int64_t brq = 32 * cfg.qwaves, brk = 32 * cfg.kwaves;
   p.n_qtiles = (int32_t)((n + brq - 1) / brq);
@@ -753,8 +752,6 @@ int make_bwd_plan(const relattn_tensor* q, const relattn_tensor* k, const relatt
   };
   const int64_t BH = B * H;
   plan->off_stat = take(BH * 2 * p.n_pad + 64);
-  plan->off_rl = (shaw && F.has_wk) ? take(BH * p.n_pad * p.nrp) : 0;
-  plan->off_rv = (shaw && F.has_wv) ? take(BH * p.n_pad * p.nrp) : 0;
   plan->off_pk = (shaw && F.has_wk) ? take(BH * p.n_qtiles * p.nr * d) : 0;
   plan->off_pv = (shaw && F.has_wv) ? take(BH * p.n_qtiles * p.nr * d) : 0;
   plan->off_pb = want_db ? take(BH * p.n_qtiles * p.t5.nb) : 0;
@@ -776,8 +773,6 @@ int run_bwd(BwdPlan& plan, const relattn_tensor* wK, const relattn_tensor* wV, b
   relattn::BwdParams& p = plan.p;
   const bool shaw = plan.fwd.mode == relattn::kRelShaw;
   p.ws_stat = reinterpret_cast<float*>(ws + plan.off_stat);
-  p.ws_rl = (shaw && wK) ? reinterpret_cast<float*>(ws + plan.off_rl) : nullptr;
-  p.ws_rv = (shaw && wV) ? reinterpret_cast<float*>(ws + plan.off_rv) : nullptr;
   p.ws_pk = (shaw && wK) ? reinterpret_cast<float*>(ws + plan.off_pk) : nullptr;
   p.ws_pv = (shaw && wV) ? reinterpret_cast<float*>(ws + plan.off_pv) : nullptr;
   p.ws_pb = want_db ? reinterpret_cast<float*>(ws + plan.off_pb) : nullptr;

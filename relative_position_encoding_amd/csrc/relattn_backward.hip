@@ -14,7 +14,7 @@
 // where G[i, r] and W[i, r] sum dS_ij and P_ij over the keys of label r; the
 // bias gradient sums dS_ij over the pairs of each bucket.
 //
-// Three launches, no atomics (results are bitwise reproducible):
+// Two launches, no atomics (results are bitwise reproducible):
 //  * bwd_q_kernel (one workgroup per 32*NW query rows, like the forward):
 //    recomputes P from the forward's log-sum-exp, forms dS and accumulates dQ
 //    on MFMA (dQ^T += K^T dS^T, K^T by LDS transpose reads).  Each query's
@@ -22,12 +22,14 @@
 //    keys go by: inside the band every label holds exactly one key, the two
 //    end labels are per-lane register sums.  The epilogue adds G W^K to dQ
 //    and writes the tile's partial table gradients Q^T G and dZ^T W.  It also
-//    leaves, per query, lse (log2 units), D and the relative rows for:
+//    leaves, per query, lse (log2 units) and D for:
 //  * bwd_kv_kernel (one workgroup per 32*NW key rows): a lane owns one key;
 //    recomputes S = Q K^T and dP = dZ V^T per query block, and accumulates
-//    dV^T += dZ^T P and dK^T += Q^T dS with MFMA.
-//  * bwd_reduce_kernel: sums the partial table and bias gradients over
-//    batches (and heads, for shared tables) in a fixed order.
+//    dV^T += dZ^T P and dK^T += Q^T dS with MFMA.  The relative rows of each
+//    query tile are recomputed there too (one small MFMA product against the
+//    table rows held in LDS) rather than read back from memory.
+//  * extra workgroups of the dk/dv launch sum the partial table and bias
+//    gradients over batches (and heads, for shared tables) in a fixed order.
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
@@ -55,6 +57,13 @@ struct BGeo {
   static constexpr int ROWB = D * ESZ;
   static constexpr int TILEB = BC * ROWB;
   static constexpr int KSTR = BF16 ? 1 : 2;
+  // A lane's logits come in groups of 8 keys KSTR apart, spanning SPAN
+  // offsets.  The dq kernel's relative rows hold the reachable labels with
+  // PADL entries below and PADU above, so that a group reads and writes its 8
+  // entries from one base (clamped into the row) without a per-key test.
+  static constexpr int SPAN = 7 * KSTR + 1;
+  static constexpr int PADL = SPAN - 1;
+  static constexpr int PADU = SPAN - 1;
 };
 
 // Waves per SIMD the register budget is sized for.
@@ -64,14 +73,14 @@ __host__ __device__ constexpr int bwd_waves_per_simd() {
 }
 
 // ---- dq kernel geometry ------------------------------------------------------
-// LDS: a ring of two K/V stages, then the per-query rows.  The ring also
-// stages, outside the key loop, the Q and dZ tiles and the table rows.
+// LDS: a ring of two K/V stages (in the epilogue it takes the Q and dZ
+// tiles), the table rows of the reachable labels (resident), then the
+// per-query rows (Shaw) or the offset vector and bucket rows (T5).
 struct LayQ {
-  int ring, rg, rv, tb, tbi, gb, total;
+  int ring, tk, tv, rg, rv, tb, tbi, gb, total;
   int lrs;       // relative row stride (floats)
   int gbs;       // bucket row stride (floats)
-  int kv_chunk;  // table rows per prologue chunk (w^K and w^V side by side)
-  int wk_chunk;  // w^K rows per epilogue chunk
+  int tab_rows;  // table rows held (labels rounded up to 32)
 };
 
 template <bool BF16, int D, int NW, int BC>
@@ -88,32 +97,60 @@ __host__ __device__ inline LayQ make_lay_q(int mode, bool has_wk, bool has_wv, i
   };
   // a lane's reads walk a diagonal of the rows (stride lrs - 1 across lanes),
   // the epilogue reads columns (stride lrs): 2 mod 4 keeps both cheap
-  L.lrs = nr + ((2 - nr) & 3);
-  L.rg = L.rv = L.tb = L.tbi = L.gb = off;
+  {
+    const int m = nr + G::PADL + G::PADU;
+    L.lrs = m + ((2 - m) & 3);
+  }
+  L.tab_rows = (nr + 31) / 32 * 32;
+  L.tk = L.tv = L.rg = L.rv = L.tb = L.tbi = L.gb = off;
   L.gbs = nb | 1;
   if (mode == kRelShaw) {
-    if (has_wk) L.rg = take(G::BR * L.lrs * 4);
-    if (has_wv) L.rv = take(G::BR * L.lrs * 4);
+    if (has_wk) {
+      L.tk = take(L.tab_rows * G::ROWB);
+      L.rg = take(G::BR * L.lrs * 4);
+    }
+    if (has_wv) {
+      L.tv = take(L.tab_rows * G::ROWB);
+      L.rv = take(G::BR * L.lrs * 4);
+    }
   } else if (mode == kRelT5) {
     L.tb = take((2 * t5_dist + 1) * 4);
     L.tbi = take((2 * t5_dist + 1) * 4);
     if (want_db) L.gb = take(2 * G::BR * L.gbs * 4);
   }
   L.total = off;
-  L.kv_chunk = (L.ring / (2 * G::ROWB)) / 32 * 32;
-  L.wk_chunk = (L.ring / G::ROWB) / 32 * 32;
   return L;
 }
 
+// Row fragments of one row as the B operand of a 32x32 MFMA (lane half hh
+// holds columns 16 ks + 8 hh + 0..7 for bf16, 2 ks + hh for fp32), read
+// straight from memory.
+template <bool BF16, int D, typename Op, typename T>
+__device__ __forceinline__ void load_row_frags(const T* row, int hh, Op (&op)[BF16 ? D / 16 : D / 2]) {
+#pragma unroll
+  for (int ks = 0; ks < (BF16 ? D / 16 : D / 2); ++ks) {
+    if constexpr (BF16) {
+      op[ks] = *reinterpret_cast<const bf16x8*>(row + 16 * ks + 8 * hh);
+    } else {
+      op[ks] = row[2 * ks + hh];
+    }
+  }
+}
+
 // ---- dk/dv kernel geometry -------------------------------------------------
-// One stage: Q tile, dZ tile (BQ rows each), lse and D of the BQ queries, and
-// their relative rows (nrp floats each; w^K logits, then dz.w^V).
+// A ring of two stages, each: the Q and dZ tiles (BQ rows each) and the lse
+// and D of the BQ queries.  Then, for the Shaw tables: the table rows of the
+// reachable labels (resident), the tile's relative rows (its queries'
+// s*log2(e)*q.w^K_r and dz.w^V_r, computed per tile) and, per query, the two
+// end labels' values less lse and D.
 struct LayKV {
-  int q, z, lse, dd, rl, rv, stage, tb, total;
+  int q, z, lse, dd, stage, rl, rv, tail, tk, tv, tb, total;
+  int lrs;       // relative row stride (floats)
+  int tab_rows;  // table rows held (labels rounded up to 32)
 };
 
 template <bool BF16, int D, int NW, int BQ>
-__host__ __device__ inline LayKV make_lay_kv(int mode, bool has_wk, bool has_wv, int nrp,
+__host__ __device__ inline LayKV make_lay_kv(int mode, bool has_wk, bool has_wv, int nr,
                                              int t5_dist) {
   using G = BGeo<BF16, D, NW, BQ>;
   LayKV L{};
@@ -127,15 +164,23 @@ __host__ __device__ inline LayKV make_lay_kv(int mode, bool has_wk, bool has_wv,
   L.z = take(G::TILEB);
   L.lse = take(256);  // one 4-byte DMA instruction (64 lanes) each
   L.dd = take(256);
-  L.rl = L.rv = off;
-  if (mode == kRelShaw && has_wk) L.rl = take(BQ * nrp * 4);
-  if (mode == kRelShaw && has_wv) L.rv = take(BQ * nrp * 4);
   L.stage = off;
   off = 2 * L.stage;
-  // the prologue stages this workgroup's K and V rows in the ring
-  off = max(off, 2 * G::BR * G::ROWB);
-  L.tb = off;
-  if (mode == kRelT5) take((2 * t5_dist + 1) * 4);
+  L.lrs = nr + ((2 - nr) & 3);
+  L.tab_rows = (nr + 31) / 32 * 32;
+  L.rl = L.rv = L.tail = L.tk = L.tv = L.tb = off;
+  if (mode == kRelShaw && (has_wk || has_wv)) {
+    if (has_wk) {
+      L.tk = take(L.tab_rows * G::ROWB);
+      L.rl = take(BQ * L.lrs * 4);
+    }
+    if (has_wv) {
+      L.tv = take(L.tab_rows * G::ROWB);
+      L.rv = take(BQ * L.lrs * 4);
+    }
+    L.tail = take(4 * BQ * 4);
+  }
+  if (mode == kRelT5) L.tb = take((2 * t5_dist + 1) * 4);
   L.total = off;
   return L;
 }
@@ -178,17 +223,18 @@ __device__ __forceinline__ void dma_flat(unsigned char RELATTN_LDS* lds, const v
 }
 
 // One K/V (or Q/dZ) stage of BC rows each, row index clamped to row_max.
+// Returns the number of DMA instructions this wave issued.
 template <int ROWB, int NW, int BC, typename T>
-__device__ __forceinline__ void stage_pair(unsigned char RELATTN_LDS* st, const T* a,
-                                           int64_t a_stride, const T* b, int64_t b_stride,
-                                           int row0, int row_max, int wave, int lane) {
-  dma_tile<ROWB, NW>(st, a, a_stride, row0, row_max, BC, wave, lane);
-  dma_tile<ROWB, NW>(st + BC * ROWB, b, b_stride, row0, row_max, BC, wave, lane);
+__device__ __forceinline__ int stage_pair(unsigned char RELATTN_LDS* st, const T* a,
+                                          int64_t a_stride, const T* b, int64_t b_stride,
+                                          int row0, int row_max, int wave, int lane) {
+  return dma_tile<ROWB, NW>(st, a, a_stride, row0, row_max, BC, wave, lane) +
+         dma_tile<ROWB, NW>(st + BC * ROWB, b, b_stride, row0, row_max, BC, wave, lane);
 }
 
 template <typename T, int D>
 __device__ __forceinline__ void store_row_block(T* row, const f32x16 (&acc)[(D + 31) / 32],
-                                                float mul, int hh) {
+                                                float mul, int hh, bool zero = false) {
 #pragma unroll
   for (int mb = 0; mb < (D + 31) / 32; ++mb) {
 #pragma unroll
@@ -198,12 +244,12 @@ __device__ __forceinline__ void store_row_block(T* row, const f32x16 (&acc)[(D +
         if constexpr (std::is_same_v<T, __bf16>) {
           bf16x4 o4;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) o4[e] = (__bf16)(acc[mb][4 * g + e] * mul);
+          for (int e = 0; e < 4; ++e) o4[e] = (__bf16)(zero ? 0.f : acc[mb][4 * g + e] * mul);
           *reinterpret_cast<bf16x4*>(row + d0) = o4;
         } else {
           f32x4 o4;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) o4[e] = acc[mb][4 * g + e] * mul;
+          for (int e = 0; e < 4; ++e) o4[e] = zero ? 0.f : acc[mb][4 * g + e] * mul;
           *reinterpret_cast<f32x4*>(row + d0) = o4;
         }
       }
@@ -228,6 +274,7 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd<D>()))) void bwd_q_kernel(
   constexpr bool SHAW = MODE == kRelShaw, T5 = MODE == kRelT5;
   constexpr bool ROWS = SHAW && (HAS_WK || HAS_WV);
   static_assert(2 * BR * ROWB <= 4 * G::TILEB, "Q and dZ tiles must fit the ring");
+  constexpr int SPAN = G::SPAN, PADL = G::PADL;
 
   int bh, qt;
   q_tile_of(p.causal, p.n_qtiles, bh, qt);
@@ -249,8 +296,11 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd<D>()))) void bwd_q_kernel(
   extern __shared__ __align__(16) unsigned char smem[];
   unsigned char RELATTN_LDS* smem_lds = (unsigned char RELATTN_LDS*)smem;
   const uint32_t smem_addr = (uint32_t)(uintptr_t)smem_lds;
-  float* RG = reinterpret_cast<float*>(smem + lay.rg) + qrow * lay.lrs;
-  float* RV = reinterpret_cast<float*>(smem + lay.rv) + qrow * lay.lrs;
+  // this query's rows; entry PADL + x holds label r_lo + x
+  float* RGp = reinterpret_cast<float*>(smem + lay.rg) + qrow * lay.lrs;
+  float* RVp = reinterpret_cast<float*>(smem + lay.rv) + qrow * lay.lrs;
+  float* RG = RGp + PADL;
+  float* RV = RVp + PADL;
   float* TB = reinterpret_cast<float*>(smem + lay.tb);
   int* TBI = reinterpret_cast<int*>(smem + lay.tbi);
   float* GB = reinterpret_cast<float*>(smem + lay.gb) + (2 * qrow + hh) * lay.gbs;
@@ -264,9 +314,22 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd<D>()))) void bwd_q_kernel(
   const T* wkh = reinterpret_cast<const T*>(p.wk) + h * p.wk_sh;
   const T* wvh = reinterpret_cast<const T*>(p.wv) + h * p.wv_sh;
 
-  // ---- Q and dZ tiles through the ring into registers (B operands)
-  dma_tile<ROWB, NW>(smem_lds, qg, p.q_sn, i0, p.n - 1, BR, wave, lane);
-  dma_tile<ROWB, NW>(smem_lds + BR * ROWB, zg, p.do_sn, i0, p.n - 1, BR, wave, lane);
+  // ---- everything the loop needs, requested at once: this lane's q and dz
+  // row (B operands, straight from memory), the lse, z for D, the table rows
+  // (LDS, resident) or the bias window, and the first K/V tile
+  int kv_len = p.n;
+  if (p.key_lens) kv_len = min(max(p.key_lens[b], 0), p.n);
+  const int kv_end = p.causal ? min(kv_len, i0 + BR) : kv_len;
+  const int kv_last = max(kv_len - 1, 0);
+  const int ntiles = (kv_end + BC - 1) / BC;
+  const int qr = min(qi, p.n - 1);
+  Op qop[NKS], zop[NKS];
+  load_row_frags<BF16, D>(qg + (int64_t)qr * p.q_sn, hh, qop);
+  load_row_frags<BF16, D>(zg + (int64_t)qr * p.do_sn, hh, zop);
+  Op oop[NKS];
+  load_row_frags<BF16, D>(og + (int64_t)qr * p.o_sn, hh, oop);
+  float lse2 = kPosInf;  // rows past n: every weight comes out 0
+  if (q_ok) lse2 = p.lse[b * p.lse_sb + h * p.lse_sh + qi] * kLog2e;
   if constexpr (T5) {
     // log2(e) * bias and the bias entry of every offset in [-dist, dist]
     for (int x = tid; x <= 2 * dist; x += NT) {
@@ -279,111 +342,82 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd<D>()))) void bwd_q_kernel(
       for (int x = tid; x < 2 * BR * lay.gbs; x += NT) gb0[x] = 0.f;
     }
   }
-  float lse2 = kPosInf;  // rows past n: every weight comes out 0
-  if (q_ok) lse2 = p.lse[b * p.lse_sb + h * p.lse_sh + qi] * kLog2e;
-  wait_vm<0>();
-  block_sync();
-  Op qop[NKS], zop[NKS];
+  compiler_fence();
+  if constexpr (SHAW && HAS_WK)
+    dma_tile<ROWB, NW>(smem_lds + lay.tk, wkh, p.wk_sr, p.r_lo, r_hi, lay.tab_rows, wave, lane);
+  if constexpr (SHAW && HAS_WV)
+    dma_tile<ROWB, NW>(smem_lds + lay.tv, wvh, p.wv_sr, p.r_lo, r_hi, lay.tab_rows, wave, lane);
+  constexpr int STAGEB = 2 * G::TILEB;
+  if (ntiles > 0)
+    stage_pair<ROWB, NW, BC>(smem_lds, kg, p.k_sn, vg, p.v_sn, 0, kv_last, wave, lane);
+  compiler_fence();
+  // D_i = dz_i . z_i (each lane half holds half of the row)
+  float dd = 0.f;
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks) {
     if constexpr (BF16) {
-      qop[ks] = frag_row<ROWB>(smem, qrow, 2 * ks + hh);
-      zop[ks] = frag_row<ROWB>(smem + BR * ROWB, qrow, 2 * ks + hh);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dd = fmaf((float)oop[ks][e], (float)zop[ks][e], dd);
     } else {
-      qop[ks] = elem_f32<ROWB>(smem, qrow, 2 * ks + hh);
-      zop[ks] = elem_f32<ROWB>(smem + BR * ROWB, qrow, 2 * ks + hh);
+      dd = fmaf(oop[ks], zop[ks], dd);
     }
   }
-  // D_i = dz_i . z_i (each lane half holds half of the row)
-  float dd = 0.f;
-  if (q_ok) {
-    const T* zr = og + (int64_t)qi * p.o_sn;
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      if constexpr (BF16) {
-        const bf16x8 z8 = *reinterpret_cast<const bf16x8*>(zr + 16 * ks + 8 * hh);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) dd = fmaf((float)z8[e], (float)zop[ks][e], dd);
-      } else {
-        dd = fmaf(zr[2 * ks + hh], zop[ks], dd);
-      }
-    }
-  }
-  dd = halves_sum(dd);
+  dd = halves_sum(q_ok ? dd : 0.f);
   if (hh == 0 && qi < p.n_pad) {
     float* st = p.ws_stat + (int64_t)bh * 2 * p.n_pad;
     st[qi] = lse2;
     st[p.n_pad + qi] = dd;
   }
-  block_sync();  // the ring is free
+  wait_vm<0>();
+  block_sync();  // tables, bias window and the first K/V tile landed
 
   // ---- relative rows: Shaw row qrow holds s*log2(e)*q.w^K_r (then dS sums)
-  // and dz.w^V_r (then weight sums) for labels r_lo + x, x < nr; both go to
-  // the workspace for the key-side kernel
+  // and dz.w^V_r (then weight sums) for labels r_lo + x, x < nr
   if constexpr (ROWS) {
-    const int nlb = (p.nr + 31) / 32;
-    const int cb = lay.kv_chunk / 32;
-    for (int lb0 = 0; lb0 < nlb; lb0 += cb) {
-      const int rows = min(cb, nlb - lb0) * 32;
-      if constexpr (HAS_WK)
-        dma_tile<ROWB, NW>(smem_lds, wkh, p.wk_sr, p.r_lo + lb0 * 32, r_hi, rows, wave, lane);
-      if constexpr (HAS_WV)
-        dma_tile<ROWB, NW>(smem_lds + lay.kv_chunk * ROWB, wvh, p.wv_sr, p.r_lo + lb0 * 32, r_hi,
-                           rows, wave, lane);
-      wait_vm<0>();
-      block_sync();
-      for (int lb = lb0; lb < lb0 + rows / 32; ++lb) {
-        const int row = (lb - lb0) * 32 + ql;
+    const int nlb = lay.tab_rows / 32;
+    for (int lb = 0; lb < nlb; ++lb) {
 #pragma unroll
-        for (int which = 0; which < 2; ++which) {
-          if (which == 0 && !HAS_WK) continue;
-          if (which == 1 && !HAS_WV) continue;
-          const unsigned char* tile = smem + (which ? lay.kv_chunk * ROWB : 0);
-          f32x16 acc = {};
+      for (int which = 0; which < 2; ++which) {
+        if (which == 0 && !HAS_WK) continue;
+        if (which == 1 && !HAS_WV) continue;
+        const unsigned char* tile = smem + (which ? lay.tv : lay.tk);
+        f32x16 acc = {};
 #pragma unroll
-          for (int ks = 0; ks < NKS; ++ks) {
-            if constexpr (BF16) {
-              acc = mfma(frag_row<ROWB>(tile, row, 2 * ks + hh), which ? zop[ks] : qop[ks], acc);
-            } else {
-              acc = mfma(elem_f32<ROWB>(tile, row, 2 * ks + hh), which ? zop[ks] : qop[ks], acc);
-            }
-          }
-          const float mul = which ? 1.f : p.scale_log2;
-          float* lrow = which ? RV : RG;
-          float* wrow = (which ? p.ws_rv : p.ws_rl) + ((int64_t)bh * p.n_pad + qi) * p.nrp;
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int x0 = lb * 32 + 8 * g + 4 * hh;  // acc[4g + e]: label x0 + e
-            f32x4 v4;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              v4[e] = acc[4 * g + e] * mul;
-              if (x0 + e < p.nr) lrow[x0 + e] = v4[e];
-            }
-            if (q_ok && x0 < p.nrp) *reinterpret_cast<f32x4*>(wrow + x0) = v4;
+        for (int ks = 0; ks < NKS; ++ks) {
+          if constexpr (BF16) {
+            acc = mfma(frag_row<ROWB>(tile, lb * 32 + ql, 2 * ks + hh), which ? zop[ks] : qop[ks],
+                       acc);
+          } else {
+            acc = mfma(elem_f32<ROWB>(tile, lb * 32 + ql, 2 * ks + hh), which ? zop[ks] : qop[ks],
+                       acc);
           }
         }
+        const float mul = which ? 1.f : p.scale_log2;
+        float* lrow = which ? RV : RG;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int x = lb * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);  // label of acc[i]
+          if (x < p.nr) lrow[x] = acc[i] * mul;
+        }
       }
-      block_sync();  // before the next chunk or the first K/V stage
     }
+    compiler_fence();  // each row is read back by the lanes of its own wave only
   }
 
-  // ---- key loop
-  int kv_len = p.n;
-  if (p.key_lens) kv_len = min(max(p.key_lens[b], 0), p.n);
-  const int kv_end = p.causal ? min(kv_len, i0 + BR) : kv_len;
-  const int kv_last = max(kv_len - 1, 0);
-  const int ntiles = (kv_end + BC - 1) / BC;
-  if (ntiles > 0)
-    stage_pair<ROWB, NW, BC>(smem_lds, kg, p.k_sn, vg, p.v_sn, 0, kv_last, wave, lane);
-
+  // ---- key loop (tile 0 is in stage 0)
   const int band = T5 ? dist : c;          // |delta| >= band: an end label
   const int hi_from = max(band, 1 - band);  // delta >= hi_from: the upper end
   const float rl_lo = (SHAW && HAS_WK) ? RG[0] : (T5 ? TB[0] : 0.f);
   const float rl_hi = (SHAW && HAS_WK) ? RG[p.nr - 1] : (T5 ? TB[2 * dist] : 0.f);
   const float rv_lo = (SHAW && HAS_WV) ? RV[0] : 0.f;
   const float rv_hi = (SHAW && HAS_WV) ? RV[p.nr - 1] : 0.f;
-  float g_lo = 0.f, g_hi = 0.f, w_lo = 0.f, w_hi = 0.f;  // end-label sums of dS and P
+  // running sums of dS and P over every key, and over the keys of the upper
+  // end label (the lower end's sum is what the in-band and upper sums leave)
+  float g_all = 0.f, g_hi = 0.f, w_all = 0.f, w_hi = 0.f;
+  float g_lo = 0.f;  // T5: lower end bucket's sum of dS
+  // in-band offsets whose label is reachable: their group is stored whole
+  const int wb_lo = max(1, p.r_lo) - c, wb_hi = min(2 * c - 1, r_hi) - c;
+  const int dlo = p.r_lo - c;  // offset of label entry 0
   f32x16 dq[DVB];
 #pragma unroll
   for (int mb = 0; mb < DVB; ++mb) dq[mb] = f32x16{};
@@ -394,16 +428,18 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd<D>()))) void bwd_q_kernel(
 
   for (int t = 0; t < ntiles; ++t) {
     const int st = t & 1;
-    wait_vm<0>();
-    block_sync();  // tile t landed everywhere; stage st ^ 1 is free
+    if (t > 0) {
+      wait_vm<0>();
+      block_sync();  // tile t landed everywhere; the other stage is free
+    }
     if (t + 1 < ntiles)
-      stage_pair<ROWB, NW, BC>(smem_lds + (st ^ 1) * 2 * G::TILEB, kg, p.k_sn, vg, p.v_sn,
+      stage_pair<ROWB, NW, BC>(smem_lds + (st ^ 1) * STAGEB, kg, p.k_sn, vg, p.v_sn,
                                (t + 1) * BC, kv_last, wave, lane);
     compiler_fence();
     const int j0 = t * BC;
     if (wq0 >= p.n) continue;
     if (p.causal && j0 > wq0 + 31) continue;
-    const unsigned char* Kt = smem + st * 2 * G::TILEB;
+    const unsigned char* Kt = smem + st * STAGEB;
     const unsigned char* Vt = Kt + G::TILEB;
 
 #pragma unroll
@@ -427,64 +463,130 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd<D>()))) void bwd_q_kernel(
       const int kofs = jb + hoff - qi;
       const int lim = min(kv_len - 1 - jb - hoff, p.causal ? -kofs : 0x3fffffff);
       const int dmin = jb - (wq0 + 31), dmax = jb + 31 - wq0;
-      const bool all_lo = dmax <= -band, all_hi = dmin >= hi_from;  // wave-uniform
+      // wave-uniform: the whole block at one end label (or no relative term)
+      const bool all_lo = dmax <= -band, all_hi = dmin >= hi_from;
+      const bool off_band = MODE == kRelNone || all_lo || all_hi;
+      // some key of the block hidden from some query of the wave
+      const bool need_mask = jb + 31 >= kv_len || (p.causal && jb + 31 > wq0);
       float pw[16], ds[16];
+      if (off_band) {
+        // one relative logit and one value term for every key of the block:
+        // P = 2^(s*log2e*S + (L_end - lse)), dS = P (dP + (V_end - D))
+        const float cl = (all_hi ? rl_hi : rl_lo) - lse2;
+        const float cv = (all_hi ? rv_hi : rv_lo) - dd;
+        auto run = [&](auto mask_tag) __attribute__((always_inline)) {
+          constexpr bool MASK = decltype(mask_tag)::value;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int ko = 16 * (i >> 3) + KSTR * (i & 7);
-        const int delta = kofs + ko;
-        float rl = 0.f, rv = 0.f;
-        if constexpr (SHAW) {
-          const int x = min(max(delta + c - p.r_lo, 0), p.nr - 1);
-          if constexpr (HAS_WK) rl = all_lo ? rl_lo : (all_hi ? rl_hi : RG[x]);
-          if constexpr (HAS_WV) rv = all_lo ? rv_lo : (all_hi ? rv_hi : RV[x]);
-        } else if constexpr (T5) {
-          rl = all_lo ? rl_lo : (all_hi ? rl_hi : TB[min(max(delta, -dist), dist) + dist]);
+          for (int i = 0; i < 16; ++i) {
+            float pv = fast_exp2(fmaf(s[i], p.scale_log2, cl));
+            if constexpr (MASK) pv = (16 * (i >> 3) + KSTR * (i & 7) <= lim) ? pv : 0.f;
+            pw[i] = pv;
+            ds[i] = pv * (dp[i] + cv);
+          }
+        };
+        if (need_mask) {
+          run(std::true_type{});
+        } else {
+          run(std::false_type{});
         }
-        const bool vis = ko <= lim;
-        const float pv = vis ? fast_exp2(fmaf(s[i], p.scale_log2, rl) - lse2) : 0.f;
-        pw[i] = pv;
-        ds[i] = vis ? pv * (dp[i] + rv - dd) : 0.f;
-      }
-      // per-label sums
-      if constexpr (SHAW || T5) {
-        if (all_lo || all_hi) {
+        if constexpr (SHAW || T5) {
           float gs = 0.f, ws = 0.f;
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             gs += ds[i];
             ws += pw[i];
           }
-          if (all_lo) {
-            g_lo += gs;
-            w_lo += ws;
-          } else {
+          if constexpr (SHAW) {
+            g_all += gs;
+            w_all += ws;
+          }
+          if (all_hi) {
             g_hi += gs;
             w_hi += ws;
+          } else if constexpr (T5) {
+            g_lo += gs;
           }
-        } else {
+        }
+      } else if constexpr (SHAW) {
+        // in the band: each group of 8 keys reads its 8 relative logits from
+        // one base (the row padding keeps it in the row; end labels come from
+        // registers)
+        float rlv[16], rvv[16];
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+          const int d0 = kofs + 16 * g;
+          const int bidx = min(max(d0 - dlo, -PADL), lay.lrs - PADL - SPAN);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            rlv[8 * g + e] = HAS_WK ? RG[bidx + KSTR * e] : 0.f;
+            rvv[8 * g + e] = HAS_WV ? RV[bidx + KSTR * e] : 0.f;
+          }
+        }
+        float gs = 0.f, ws = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int ko = 16 * (i >> 3) + KSTR * (i & 7);
+          const int delta = kofs + ko;
+          const bool lo = delta <= -band, hi = delta >= hi_from;
+          const float rl = lo ? rl_lo : (hi ? rl_hi : rlv[i]);
+          const float rv = lo ? rv_lo : (hi ? rv_hi : rvv[i]);
+          const bool vis = ko <= lim;
+          const float pv = vis ? fast_exp2(fmaf(s[i], p.scale_log2, rl) - lse2) : 0.f;
+          pw[i] = pv;
+          ds[i] = vis ? pv * (dp[i] + rv - dd) : 0.f;
+          gs += ds[i];
+          ws += pv;
+        }
+        g_all += gs;
+        w_all += ws;
+        if (!p.causal) {
+          // keys at the upper end label (none is visible under the causal mask)
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            const int ko = 16 * (i >> 3) + KSTR * (i & 7);
-            const int delta = kofs + ko;
+            const bool hi = kofs + 16 * (i >> 3) + KSTR * (i & 7) >= hi_from;
+            g_hi += hi ? ds[i] : 0.f;
+            w_hi += hi ? pw[i] : 0.f;
+          }
+        }
+        // a group that holds a reachable in-band label is stored whole at its
+        // own entries (entries of other labels are rewritten in the epilogue;
+        // the padding absorbs the rest): every such label holds exactly this
+        // one key of the row
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+          const int d0 = kofs + 16 * g;
+          if (q_ok && d0 + (SPAN - 1) >= wb_lo && d0 <= wb_hi) {
+            const int base = d0 - dlo;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              if constexpr (HAS_WK) RG[base + KSTR * e] = ds[8 * g + e];
+              if constexpr (HAS_WV) RV[base + KSTR * e] = pw[8 * g + e];
+            }
+          }
+        }
+      } else {
+        // T5 in the band: the bias of each key's bucket
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int ko = 16 * (i >> 3) + KSTR * (i & 7);
+          const int delta = kofs + ko;
+          float rl = 0.f;
+          if constexpr (T5) rl = TB[min(max(delta, -dist), dist) + dist];
+          const bool vis = ko <= lim;
+          const float pv = vis ? fast_exp2(fmaf(s[i], p.scale_log2, rl) - lse2) : 0.f;
+          pw[i] = pv;
+          ds[i] = vis ? pv * (dp[i] - dd) : 0.f;
+        }
+        if constexpr (T5) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int delta = kofs + 16 * (i >> 3) + KSTR * (i & 7);
             if (delta <= -band) {
               g_lo += ds[i];
-              w_lo += pw[i];
             } else if (delta >= hi_from) {
               g_hi += ds[i];
-              w_hi += pw[i];
-            } else if (q_ok && qi + delta < p.n) {
-              // the only key of its label in this row (labels past the
-              // reachable ones belong to masked future keys)
-              if constexpr (SHAW) {
-                const int x = delta + c - p.r_lo;
-                if ((unsigned)x < (unsigned)p.nr) {
-                  if constexpr (HAS_WK) RG[x] = ds[i];
-                  if constexpr (HAS_WV) RV[x] = pw[i];
-                }
-              } else {
-                if (want_db) GB[TBI[delta + dist]] += ds[i];
-              }
+            } else if (want_db && q_ok && qi + delta < p.n) {
+              GB[TBI[delta + dist]] += ds[i];
             }
           }
         }
@@ -522,69 +624,93 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd<D>()))) void bwd_q_kernel(
     }
   }
   wait_vm<0>();
-  block_sync();
-
-  // ---- epilogue: final label sums of this row
+  block_sync();  // the ring is free
+  // the Q and dZ tiles for the partial table gradients, rebuilt in the ring
+  // from the row fragments each lane holds (same layout as a DMA'd tile)
   if constexpr (ROWS) {
-    const float gl = halves_sum(g_lo), gh = halves_sum(g_hi);
-    const float wl = halves_sum(w_lo), wh = halves_sum(w_hi);
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      if constexpr (BF16) {
+        const int o = tile_offset<ROWB>(qrow, (2 * ks + hh) * 16);
+        if constexpr (HAS_WK) *reinterpret_cast<bf16x8*>(smem + o) = qop[ks];
+        if constexpr (HAS_WV) *reinterpret_cast<bf16x8*>(smem + BR * ROWB + o) = zop[ks];
+      } else {
+        const int o = tile_offset<ROWB>(qrow, (2 * ks + hh) * 4);
+        if constexpr (HAS_WK) *reinterpret_cast<float*>(smem + o) = qop[ks];
+        if constexpr (HAS_WV) *reinterpret_cast<float*>(smem + BR * ROWB + o) = zop[ks];
+      }
+    }
+  }
+
+  // ---- epilogue: final label sums of this row.  In-band labels hold their
+  // key's dS (and P) where the pair is visible, zero elsewhere; the lower end
+  // label takes what the row's total leaves after the in-band and upper sums.
+  if constexpr (ROWS) {
+    const float gall = halves_sum(g_all), wall = halves_sum(w_all);
+    const float gh = halves_sum(g_hi), wh = halves_sum(w_hi);
     const int x_lo = -p.r_lo;         // label -c (present when r_lo == 0)
     const int x_hi = 2 * c - p.r_lo;  // label +c (present when < nr)
+    float gin = 0.f, win = 0.f;
     for (int x = hh; x < p.nr; x += 2) {
+      if (x == x_lo || x == x_hi) continue;
       const int delta = x + p.r_lo - c;
       const int j = qi + delta;
       const bool vis = q_ok && j >= 0 && j < kv_len && (!p.causal || delta <= 0);
-      float gv = 0.f, wv = 0.f;
-      if (x == x_lo || x == x_hi) {
-        gv = (x == x_lo ? gl : 0.f) + (x == x_hi ? gh : 0.f);
-        wv = (x == x_lo ? wl : 0.f) + (x == x_hi ? wh : 0.f);
-      } else if (vis) {
-        if constexpr (HAS_WK) gv = RG[x];
-        if constexpr (HAS_WV) wv = RV[x];
+      if constexpr (HAS_WK) {
+        const float v = vis ? RG[x] : 0.f;
+        RG[x] = v;
+        gin += v;
       }
-      if (!q_ok) gv = wv = 0.f;
-      if constexpr (HAS_WK) RG[x] = gv;
-      if constexpr (HAS_WV) RV[x] = wv;
+      if constexpr (HAS_WV) {
+        const float v = vis ? RV[x] : 0.f;
+        RV[x] = v;
+        win += v;
+      }
+    }
+    gin = halves_sum(gin);
+    win = halves_sum(win);
+    const float gl = gall - gin - gh, wl = wall - win - wh;
+    if (hh == 0) {
+      if (x_lo == 0) {
+        if constexpr (HAS_WK) RG[0] = q_ok ? gl + (x_hi == 0 ? gh : 0.f) : 0.f;
+        if constexpr (HAS_WV) RV[0] = q_ok ? wl + (x_hi == 0 ? wh : 0.f) : 0.f;
+      }
+      if (x_hi != x_lo && x_hi < p.nr) {
+        if constexpr (HAS_WK) RG[x_hi] = q_ok ? gh : 0.f;
+        if constexpr (HAS_WV) RV[x_hi] = q_ok ? wh : 0.f;
+      }
     }
     compiler_fence();  // the other half of this wave wrote the rest of the row
   }
 
-  // ---- dQ^T += (w^K)^T G^T, w^K in label chunks through the ring
+  // ---- dQ^T += (w^K)^T G^T with the resident w^K rows
   if constexpr (SHAW && HAS_WK) {
     const int nls = (p.nr + 15) / 16;
-    for (int l0 = 0; l0 < nls * 16; l0 += lay.wk_chunk) {
-      const int rows = min(lay.wk_chunk, (nls * 16 - l0 + 31) / 32 * 32);
-      block_sync();
-      dma_tile<ROWB, NW>(smem_lds, wkh, p.wk_sr, p.r_lo + l0, r_hi, rows, wave, lane);
-      wait_vm<0>();
-      block_sync();
-      const int ls_end = min(nls, (l0 + rows) / 16);
-      for (int ls = l0 / 16; ls < ls_end; ++ls) {
-        const int lsr = ls - l0 / 16;
-        if constexpr (BF16) {
-          bf16x8 bw;
+    const uint32_t tk_lds = smem_addr + (uint32_t)lay.tk;
+    for (int ls = 0; ls < nls; ++ls) {
+      if constexpr (BF16) {
+        bf16x8 bw;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int x = ls * 16 + 8 * hh + e;
-            bw[e] = (__bf16)(x < p.nr ? RG[x] : 0.f);
-          }
-          bf16x4 wlo[DVB], whi[DVB];
+        for (int e = 0; e < 8; ++e) {
+          const int x = ls * 16 + 8 * hh + e;
+          bw[e] = (__bf16)(x < p.nr ? RG[x] : 0.f);
+        }
+        bf16x4 wlo[DVB], whi[DVB];
 #pragma unroll
-          for (int mb = 0; mb < DVB; ++mb)
-            frag_col_issue<ROWB, D>(smem_addr, lsr * 16, 32 * mb, lane, wlo[mb], whi[mb]);
-          frag_col_wait(wlo, whi);
+        for (int mb = 0; mb < DVB; ++mb)
+          frag_col_issue<ROWB, D>(tk_lds, ls * 16, 32 * mb, lane, wlo[mb], whi[mb]);
+        frag_col_wait(wlo, whi);
 #pragma unroll
-          for (int mb = 0; mb < DVB; ++mb) dq[mb] = mfma(frag_join(wlo[mb], whi[mb]), bw, dq[mb]);
-        } else {
+        for (int mb = 0; mb < DVB; ++mb) dq[mb] = mfma(frag_join(wlo[mb], whi[mb]), bw, dq[mb]);
+      } else {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int x = ls * 16 + 2 * e + hh;
-            const float w = x < p.nr ? RG[x] : 0.f;
+        for (int e = 0; e < 8; ++e) {
+          const int x = ls * 16 + 2 * e + hh;
+          const float w = x < p.nr ? RG[x] : 0.f;
 #pragma unroll
-            for (int mb = 0; mb < DVB; ++mb) {
-              const int dcol = min(32 * mb + ql, D - 1);
-              dq[mb] = mfma(elem_f32<ROWB>(smem, lsr * 16 + 2 * e + hh, dcol), w, dq[mb]);
-            }
+          for (int mb = 0; mb < DVB; ++mb) {
+            const int dcol = min(32 * mb + ql, D - 1);
+            dq[mb] = mfma(elem_f32<ROWB>(smem + lay.tk, ls * 16 + 2 * e + hh, dcol), w, dq[mb]);
           }
         }
       }
@@ -594,12 +720,7 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd<D>()))) void bwd_q_kernel(
 
   // ---- partial table gradients of this tile: (w^K)' = s Q^T G, (w^V)' = dZ^T W
   if constexpr (ROWS) {
-    block_sync();
-    if constexpr (HAS_WK) dma_tile<ROWB, NW>(smem_lds, qg, p.q_sn, i0, p.n - 1, BR, wave, lane);
-    if constexpr (HAS_WV)
-      dma_tile<ROWB, NW>(smem_lds + BR * ROWB, zg, p.do_sn, i0, p.n - 1, BR, wave, lane);
-    wait_vm<0>();
-    block_sync();
+    block_sync();  // the Q and dZ tiles are written; every row is final
     const int nlb = (p.nr + 31) / 32;
     const int per = nlb * DVB;
     constexpr int NWHICH = (HAS_WK ? 1 : 0) + (HAS_WV ? 1 : 0);
@@ -608,7 +729,7 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd<D>()))) void bwd_q_kernel(
       const bool isv = HAS_WK ? tt >= per : true;
       const int r = (HAS_WK && isv) ? tt - per : tt;
       const int lb = r / DVB, mb = r - lb * DVB;
-      const float* Gr = reinterpret_cast<const float*>(smem + (isv ? lay.rv : lay.rg));
+      const float* Gr = reinterpret_cast<const float*>(smem + (isv ? lay.rv : lay.rg)) + PADL;
       const unsigned char* X = smem + (isv ? BR * ROWB : 0);
       const int x = min(lb * 32 + ql, p.nr - 1);
       f32x16 acc = {};
@@ -666,6 +787,108 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd<D>()))) void bwd_q_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Table and bias gradients: sums of the per-tile partials in a fixed order,
+// done by extra workgroups of the dk/dv launch.  Role ids: first one
+// workgroup per (table head, label) of d w^K, then of d w^V, then the bias
+// gradient's workgroups (nt entries each).
+// ---------------------------------------------------------------------------
+__host__ __device__ inline int reduce_tables_rows(const BwdParams& p, int which) {
+  const int ht = which ? (p.dwv ? p.htv : 0) : (p.dwk ? p.htk : 0);
+  return ht * (2 * p.clip + 1);
+}
+__host__ __device__ inline int reduce_role_count(const BwdParams& p, int nt) {
+  int n = reduce_tables_rows(p, 0) + reduce_tables_rows(p, 1);
+  if (p.db) {
+    const int64_t total = p.ob ? (int64_t)p.hb * (2 * p.ob_w + 1) : (int64_t)p.t5.nb * p.H;
+    n += (int)((total + nt - 1) / nt);
+  }
+  return n;
+}
+
+// One (table head, label) row of d w^K or d w^V: the nt threads form nt/d
+// groups of d columns; group g sums terms g, g + G, ... and the groups are
+// added in order.
+__device__ void reduce_table_row(const BwdParams& p, int which, int row, int nt) {
+  float* out = which ? p.dwv : p.dwk;
+  const int ht = which ? p.htv : p.htk;
+  const int nlab = 2 * p.clip + 1;
+  const int hq = row / nlab, r = row - hq * nlab;
+  const int d = p.d, G = nt / d;
+  const int tid = threadIdx.x;
+  const int dd = tid % d, g = tid / d;
+  const int x = r - p.r_lo;
+  float acc = 0.f;
+  if (x >= 0 && x < p.nr) {
+    const float* part = which ? p.ws_pv : p.ws_pk;
+    const int h_lo = ht == 1 ? 0 : hq, hn = ht == 1 ? p.H : 1;
+    const int nq = p.n_qtiles;
+    const int U = p.B * hn * nq;  // term u: (b, head, query tile)
+#pragma unroll 4
+    for (int u = g; u < U; u += G) {
+      const int tq = u % nq, bh2 = u / nq;
+      const int b = bh2 / hn, hh = h_lo + (bh2 - b * hn);
+      acc += part[(((int64_t)(b * p.H + hh) * nq + tq) * p.nr + x) * d + dd];
+    }
+  }
+  extern __shared__ __align__(16) unsigned char smem[];
+  float* red = reinterpret_cast<float*>(smem);
+  red[tid] = acc;
+  __syncthreads();
+  if (g == 0) {
+    float sum = 0.f;
+    for (int k = 0; k < G; ++k) sum += red[k * d + dd];
+    const int64_t sh = which ? p.dwv_sh : p.dwk_sh, sr = which ? p.dwv_sr : p.dwk_sr;
+    out[hq * sh + r * sr + dd] = sum;
+  }
+}
+
+// Bias gradient entries [blk * nt, blk * nt + nt): one thread each.
+__device__ void reduce_bias(const BwdParams& p, int blk, int nt) {
+  const int64_t idx = (int64_t)blk * nt + threadIdx.x;
+  const int nq = p.n_qtiles;
+  const int nbt = p.t5.nb;  // entries per head in the partials
+  if (p.ob) {
+    // offset-bias table [hb, 2W + 1]: entries outside the loaded window
+    // (offsets no pair reaches) get zero
+    const int nw = 2 * p.ob_w + 1;
+    if (idx >= (int64_t)p.hb * nw) return;
+    const int w = (int)(idx % nw), hq = (int)(idx / nw);
+    const int e = w - p.ob_lo;
+    float acc = 0.f;
+    if (e >= 0 && e < nbt) {
+      const int h_lo = p.hb == 1 ? 0 : hq, h_hi = p.hb == 1 ? p.H : hq + 1;
+      for (int b = 0; b < p.B; ++b)
+        for (int hh = h_lo; hh < h_hi; ++hh) {
+          const float* src = p.ws_pb + (int64_t)(b * p.H + hh) * nq * nbt + e;
+          for (int t = 0; t < nq; ++t) acc += src[(int64_t)t * nbt];
+        }
+    }
+    p.db[hq * p.db_s0 + w * p.db_s1] = acc;
+  } else {
+    // T5 table [nb, H]
+    if (idx >= (int64_t)nbt * p.H) return;
+    const int hq = (int)(idx % p.H), e = (int)(idx / p.H);
+    float acc = 0.f;
+    for (int b = 0; b < p.B; ++b) {
+      const float* src = p.ws_pb + (int64_t)(b * p.H + hq) * nq * nbt + e;
+      for (int t = 0; t < nq; ++t) acc += src[(int64_t)t * nbt];
+    }
+    p.db[e * p.db_s0 + hq * p.db_s1] = acc;
+  }
+}
+
+__device__ void reduce_role(const BwdParams& p, int role, int nt) {
+  const int rk = reduce_tables_rows(p, 0), rv = reduce_tables_rows(p, 1);
+  if (role < rk) {
+    reduce_table_row(p, 0, role, nt);
+  } else if (role < rk + rv) {
+    reduce_table_row(p, 1, role - rk, nt);
+  } else {
+    reduce_bias(p, role - rk - rv, nt);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // dk/dv kernel
 // ---------------------------------------------------------------------------
 template <int D, int NW, int BQ, bool BF16, int MODE, bool HAS_WK, bool HAS_WV>
@@ -678,8 +901,16 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd<D>()))) void bwd_kv_kernel
   constexpr int NT = G::NT, NQB = G::NKB, DVB = G::DVB, NKS = G::NKS, ROWB = G::ROWB;
   constexpr int KSTR = G::KSTR, BR = G::BR;
   constexpr bool SHAW = MODE == kRelShaw, T5 = MODE == kRelT5;
+  constexpr bool ROWS = SHAW && (HAS_WK || HAS_WV);
 
-  const int lid = xcd_remap(blockIdx.x, gridDim.x);
+  // workgroups past the key tiles sum the table and bias gradients (the dq
+  // kernel, launched before on the same stream, has written the partials)
+  const int n_kv = p.B * p.H * p.n_ktiles;
+  if ((int)blockIdx.x >= n_kv) {
+    reduce_role(p, (int)blockIdx.x - n_kv, NT);
+    return;
+  }
+  const int lid = xcd_remap(blockIdx.x, n_kv);
   const int bh = lid / p.n_ktiles, kt = lid - bh * p.n_ktiles;
   const int b = bh / p.H, h = bh - b * p.H;
   const int k0 = kt * BR;
@@ -690,12 +921,16 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd<D>()))) void bwd_kv_kernel
   const int kj = wk0 + ql;  // this lane's key
   const int c = p.clip;
   const int dist = p.t5_dist;
+  const int r_hi = p.r_lo + p.nr - 1;
 
-  const LayKV lay = make_lay_kv<BF16, D, NW, BQ>(MODE, HAS_WK, HAS_WV, p.nrp, dist);
+  const LayKV lay = make_lay_kv<BF16, D, NW, BQ>(MODE, HAS_WK, HAS_WV, p.nr, dist);
   extern __shared__ __align__(16) unsigned char smem[];
   unsigned char RELATTN_LDS* smem_lds = (unsigned char RELATTN_LDS*)smem;
   const uint32_t smem_addr = (uint32_t)(uintptr_t)smem_lds;
   float* TB = reinterpret_cast<float*>(smem + lay.tb);
+  float* RLt = reinterpret_cast<float*>(smem + lay.rl);
+  float* RVt = reinterpret_cast<float*>(smem + lay.rv);
+  float* TAIL = reinterpret_cast<float*>(smem + lay.tail);  // [a_lo | a_hi | b_lo | b_hi][BQ]
 
   const T* qg = reinterpret_cast<const T*>(p.q) + b * p.q_sb + h * p.q_sh;
   const T* kg = reinterpret_cast<const T*>(p.k) + b * p.k_sb + h * p.k_sh;
@@ -704,39 +939,32 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd<D>()))) void bwd_kv_kernel
   T* dkg = reinterpret_cast<T*>(p.dk) + b * p.dk_sb + h * p.dk_sh;
   T* dvg = reinterpret_cast<T*>(p.dv) + b * p.dv_sb + h * p.dv_sh;
   const float* stat = p.ws_stat + (int64_t)bh * 2 * p.n_pad;
-  const float* rlg = p.ws_rl + (int64_t)bh * p.n_pad * p.nrp;
-  const float* rvg = p.ws_rv + (int64_t)bh * p.n_pad * p.nrp;
 
-  // ---- this workgroup's K and V rows into registers (B operands)
-  dma_tile<ROWB, NW>(smem_lds, kg, p.k_sn, k0, p.n - 1, BR, wave, lane);
-  dma_tile<ROWB, NW>(smem_lds + BR * ROWB, vg, p.v_sn, k0, p.n - 1, BR, wave, lane);
+  // ---- requested at once: this lane's k and v row (B operands, straight
+  // from memory), the table rows of the reachable labels (LDS, resident) or
+  // the bias window, and the first query tile
+  int kv_len = p.n;
+  if (p.key_lens) kv_len = min(max(p.key_lens[b], 0), p.n);
+  // query tiles that can see a key of this workgroup
+  const int t_lo = p.causal ? k0 / BQ : 0;
+  const int t_end = (k0 < kv_len) ? (p.n + BQ - 1) / BQ : t_lo;
+  const int kr = min(kj, p.n - 1);
+  Op kop[NKS], vop[NKS];
+  load_row_frags<BF16, D>(kg + (int64_t)kr * p.k_sn, hh, kop);
+  load_row_frags<BF16, D>(vg + (int64_t)kr * p.v_sn, hh, vop);
   if constexpr (T5) {
     for (int x = tid; x <= 2 * dist; x += NT) {
       const int entry = p.ob ? x : t5_bucket(x - dist, p.t5);
       TB[x] = kLog2e * p.t5_bias[(entry + p.ob_lo) * p.tb_sb + h * p.tb_sh];
     }
   }
-  wait_vm<0>();
-  block_sync();
-  Op kop[NKS], vop[NKS];
-  const int krow = wave * 32 + ql;
-#pragma unroll
-  for (int ks = 0; ks < NKS; ++ks) {
-    if constexpr (BF16) {
-      kop[ks] = frag_row<ROWB>(smem, krow, 2 * ks + hh);
-      vop[ks] = frag_row<ROWB>(smem + BR * ROWB, krow, 2 * ks + hh);
-    } else {
-      kop[ks] = elem_f32<ROWB>(smem, krow, 2 * ks + hh);
-      vop[ks] = elem_f32<ROWB>(smem + BR * ROWB, krow, 2 * ks + hh);
-    }
-  }
-  block_sync();  // the ring is free
-
-  int kv_len = p.n;
-  if (p.key_lens) kv_len = min(max(p.key_lens[b], 0), p.n);
-  // query tiles that can see a key of this workgroup
-  const int t_lo = p.causal ? k0 / BQ : 0;
-  const int t_end = (k0 < kv_len) ? (p.n + BQ - 1) / BQ : t_lo;
+  compiler_fence();
+  if constexpr (SHAW && HAS_WK)
+    dma_tile<ROWB, NW>(smem_lds + lay.tk, reinterpret_cast<const T*>(p.wk) + h * p.wk_sh,
+                       p.wk_sr, p.r_lo, r_hi, lay.tab_rows, wave, lane);
+  if constexpr (SHAW && HAS_WV)
+    dma_tile<ROWB, NW>(smem_lds + lay.tv, reinterpret_cast<const T*>(p.wv) + h * p.wv_sh,
+                       p.wv_sr, p.r_lo, r_hi, lay.tab_rows, wave, lane);
   auto issue = [&](int t, int stage) __attribute__((always_inline)) {
     unsigned char RELATTN_LDS* st = smem_lds + stage * lay.stage;
     const int q0 = t * BQ;
@@ -745,10 +973,6 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd<D>()))) void bwd_kv_kernel
       dma_flat<1, 4>(st + lay.lse, stat + q0, 256, 0, lane);
       dma_flat<1, 4>(st + lay.dd, stat + p.n_pad + q0, 256, 0, lane);
     }
-    if constexpr (SHAW && HAS_WK)
-      dma_flat<NW, 16>(st + lay.rl, rlg + (int64_t)q0 * p.nrp, BQ * p.nrp * 4, wave, lane);
-    if constexpr (SHAW && HAS_WV)
-      dma_flat<NW, 16>(st + lay.rv, rvg + (int64_t)q0 * p.nrp, BQ * p.nrp * 4, wave, lane);
     compiler_fence();
   };
   if (t_lo < t_end) issue(t_lo, 0);
@@ -761,20 +985,79 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd<D>()))) void bwd_kv_kernel
   for (int mb = 0; mb < DVB; ++mb) frag_col_base<ROWB, D>(32 * mb, lane, trb_lo[mb], trb_hi[mb]);
   const int hoff = BF16 ? 8 * hh : hh;
   const bool k_ok = kj < kv_len;
+  const int band = T5 ? dist : c;          // |delta| >= band: an end label
+  const int hi_from = max(band, 1 - band);  // delta >= hi_from: the upper end
+
+  // 16 per-query values of this lane's registers: vector reads of 4
+  // consecutive queries (bf16 register order), else one by one
+  auto per_query = [&](const float* arr, int qb, float (&out)[16]) __attribute__((always_inline)) {
+    if constexpr (BF16) {
+#pragma unroll
+      for (int g = 0; g < 2; ++g)
+#pragma unroll
+        for (int hv = 0; hv < 2; ++hv) {
+          const f32x4 a = *reinterpret_cast<const f32x4*>(arr + 32 * qb + hoff + 16 * g + 4 * hv);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) out[8 * g + 4 * hv + e] = a[e];
+        }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) out[i] = arr[32 * qb + hoff + 16 * (i >> 3) + KSTR * (i & 7)];
+    }
+  };
 
   for (int t = t_lo; t < t_end; ++t) {
     const int stg = (t - t_lo) & 1;
     wait_vm<0>();
-    block_sync();
+    block_sync();  // tile t (and the tables) landed everywhere; the other stage
+                   // and the rows are free
     if (t + 1 < t_end) issue(t + 1, stg ^ 1);
     const unsigned char* S0 = smem + stg * lay.stage;
     const unsigned char* Qt = S0 + lay.q;
     const unsigned char* Zt = S0 + lay.z;
     const float* LS = reinterpret_cast<const float*>(S0 + lay.lse);
     const float* DD = reinterpret_cast<const float*>(S0 + lay.dd);
-    const float* RLt = reinterpret_cast<const float*>(S0 + lay.rl);
-    const float* RVt = reinterpret_cast<const float*>(S0 + lay.rv);
     const int q0 = t * BQ;
+
+    if constexpr (ROWS) {
+      // relative rows of the tile's queries: C[label, query] = w_r . x_q with
+      // x = q (key table, scaled to log2 units) or dz (value table), and the
+      // two end labels less lse (key table) or D (value table)
+      constexpr int NWHICH = (HAS_WK ? 1 : 0) + (HAS_WV ? 1 : 0);
+      const int nlb = lay.tab_rows / 32;
+      for (int it = wave; it < NQB * nlb * NWHICH; it += NW) {
+        const int which = it % NWHICH, rest = it / NWHICH;
+        const int lb = rest % nlb, qb = rest / nlb;
+        const bool isv = HAS_WK ? which == 1 : true;
+        const unsigned char* tab = smem + (isv ? lay.tv : lay.tk);
+        const unsigned char* X = isv ? Zt : Qt;
+        f32x16 acc = {};
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+          if constexpr (BF16) {
+            acc = mfma(frag_row<ROWB>(tab, lb * 32 + ql, 2 * ks + hh),
+                       frag_row<ROWB>(X, 32 * qb + ql, 2 * ks + hh), acc);
+          } else {
+            acc = mfma(elem_f32<ROWB>(tab, lb * 32 + ql, 2 * ks + hh),
+                       elem_f32<ROWB>(X, 32 * qb + ql, 2 * ks + hh), acc);
+          }
+        }
+        const int lq = 32 * qb + ql;
+        float* row = (isv ? RVt : RLt) + lq * lay.lrs;
+        const float mul = isv ? 1.f : p.scale_log2;
+        const float sub = isv ? DD[lq] : LS[lq];
+        float* tl = TAIL + (isv ? 2 * BQ : 0);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int x = lb * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
+          const float v = acc[i] * mul;
+          if (x < p.nr) row[x] = v;
+          if (x == 0) tl[lq] = v - sub;
+          if (x == p.nr - 1) tl[BQ + lq] = v - sub;
+        }
+      }
+      block_sync();
+    }
     if (wk0 >= p.n || wk0 >= kv_len) continue;  // no live key in this wave
 
 #pragma unroll
@@ -796,47 +1079,74 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd<D>()))) void bwd_kv_kernel
           dp = mfma(elem_f32<ROWB>(Zt, qrowm, 2 * ks + hh), vop[ks], dp);
         }
       }
-      float lsv[16], ddv[16];
-      if constexpr (BF16) {
+      // offsets delta = key - query of the block: all at one end label (or no
+      // relative term)?  Keys past the key length are not masked here: their
+      // columns are independent and are written as zeros.
+      const bool all_lo = (wk0 + 31) - qb0 <= -band;
+      const bool all_hi = wk0 - (qb0 + 31) >= hi_from;
+      const bool off_band = MODE == kRelNone || all_lo || all_hi;
+      // some query of the block past n, or before some key of the wave
+      const bool need_mask = qb0 + 31 >= p.n || (p.causal && wk0 + 31 > qb0);
+      float pw[16], ds[16];
+      if (off_band) {
+        // per query: the end label's relative logit less lse, and its value
+        // term less D
+        float av[16], bv[16];
+        if constexpr (ROWS && HAS_WK) {
+          per_query(TAIL + (all_hi ? BQ : 0), qb, av);
+        } else {
+          per_query(LS, qb, av);
+          const float e = T5 ? (all_hi ? TB[2 * dist] : TB[0]) : 0.f;
 #pragma unroll
-        for (int g = 0; g < 2; ++g)
+          for (int i = 0; i < 16; ++i) av[i] = e - av[i];
+        }
+        if constexpr (ROWS && HAS_WV) {
+          per_query(TAIL + 2 * BQ + (all_hi ? BQ : 0), qb, bv);
+        } else {
+          per_query(DD, qb, bv);
 #pragma unroll
-          for (int hv = 0; hv < 2; ++hv) {
-            const int lq = 32 * qb + hoff + 16 * g + 4 * hv;
-            const f32x4 a = *reinterpret_cast<const f32x4*>(LS + lq);
-            const f32x4 d4 = *reinterpret_cast<const f32x4*>(DD + lq);
+          for (int i = 0; i < 16; ++i) bv[i] = -bv[i];
+        }
+        auto run = [&](auto mask_tag) __attribute__((always_inline)) {
+          constexpr bool MASK = decltype(mask_tag)::value;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              lsv[8 * g + 4 * hv + e] = a[e];
-              ddv[8 * g + 4 * hv + e] = d4[e];
+          for (int i = 0; i < 16; ++i) {
+            float pv = fast_exp2(fmaf(s[i], p.scale_log2, av[i]));
+            if constexpr (MASK) {
+              const int qq = qb0 + hoff + 16 * (i >> 3) + KSTR * (i & 7);
+              pv = (qq < p.n && (!p.causal || kj <= qq)) ? pv : 0.f;
             }
+            pw[i] = pv;
+            ds[i] = pv * (dp[i] + bv[i]);
           }
+        };
+        if (need_mask) {
+          run(std::true_type{});
+        } else {
+          run(std::false_type{});
+        }
       } else {
+        float lsv[16], ddv[16];
+        per_query(LS, qb, lsv);
+        per_query(DD, qb, ddv);
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int lq = 32 * qb + hoff + 16 * (i >> 3) + KSTR * (i & 7);
-          lsv[i] = LS[lq];
-          ddv[i] = DD[lq];
+          const int qq = q0 + lq;
+          const int delta = kj - qq;
+          float rl = 0.f, rv = 0.f;
+          if constexpr (SHAW) {
+            const int x = min(max(delta + c - p.r_lo, 0), p.nr - 1);
+            if constexpr (HAS_WK) rl = RLt[lq * lay.lrs + x];
+            if constexpr (HAS_WV) rv = RVt[lq * lay.lrs + x];
+          } else if constexpr (T5) {
+            rl = TB[min(max(delta, -dist), dist) + dist];
+          }
+          const bool vis = qq < p.n && (!p.causal || delta <= 0);
+          const float pv = vis ? fast_exp2(fmaf(s[i], p.scale_log2, rl) - lsv[i]) : 0.f;
+          pw[i] = pv;
+          ds[i] = vis ? pv * (dp[i] + rv - ddv[i]) : 0.f;
         }
-      }
-      float pw[16], ds[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int lq = 32 * qb + hoff + 16 * (i >> 3) + KSTR * (i & 7);
-        const int qq = q0 + lq;
-        const int delta = kj - qq;
-        float rl = 0.f, rv = 0.f;
-        if constexpr (SHAW) {
-          const int x = min(max(delta + c - p.r_lo, 0), p.nr - 1);
-          if constexpr (HAS_WK) rl = RLt[lq * p.nrp + x];
-          if constexpr (HAS_WV) rv = RVt[lq * p.nrp + x];
-        } else if constexpr (T5) {
-          rl = TB[min(max(delta, -dist), dist) + dist];
-        }
-        const bool vis = k_ok && qq < p.n && (!p.causal || delta <= 0);
-        const float pv = vis ? fast_exp2(fmaf(s[i], p.scale_log2, rl) - lsv[i]) : 0.f;
-        pw[i] = pv;
-        ds[i] = vis ? pv * (dp[i] + rv - ddv[i]) : 0.f;
       }
       // dV^T += dZ^T P and dK^T += Q^T dS
       if constexpr (BF16) {
@@ -883,75 +1193,9 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd<D>()))) void bwd_kv_kernel
   }
   wait_vm<0>();
   if (kj < p.n) {
-    store_row_block<T, D>(dkg + (int64_t)kj * p.dk_sn, dk, p.scale, hh);
-    store_row_block<T, D>(dvg + (int64_t)kj * p.dv_sn, dv, 1.f, hh);
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Table and bias gradients: sums of the per-tile partials in a fixed order.
-// blockIdx.y: 0 = d w^K, 1 = d w^V, 2 = d bias.  One thread per output.
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void bwd_reduce_kernel(const BwdParams p) {
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int which = blockIdx.y;
-  const int nq = p.n_qtiles;
-  if (which < 2) {
-    float* out = which ? p.dwv : p.dwk;
-    const float* part = which ? p.ws_pv : p.ws_pk;
-    if (!out) return;
-    const int ht = which ? p.htv : p.htk;
-    const int nlab = 2 * p.clip + 1;
-    const int64_t total = (int64_t)ht * nlab * p.d;
-    if (idx >= total) return;
-    const int dd = (int)(idx % p.d);
-    const int r = (int)((idx / p.d) % nlab);
-    const int hq = (int)(idx / ((int64_t)p.d * nlab));
-    float acc = 0.f;
-    const int x = r - p.r_lo;
-    if (x >= 0 && x < p.nr) {
-      const int h_lo = ht == 1 ? 0 : hq, h_hi = ht == 1 ? p.H : hq + 1;
-      for (int b = 0; b < p.B; ++b)
-        for (int hh = h_lo; hh < h_hi; ++hh) {
-          const float* src = part + ((int64_t)(b * p.H + hh) * nq * p.nr + x) * p.d + dd;
-          for (int t = 0; t < nq; ++t) acc += src[(int64_t)t * p.nr * p.d];
-        }
-    }
-    const int64_t sh = which ? p.dwv_sh : p.dwk_sh, sr = which ? p.dwv_sr : p.dwk_sr;
-    out[hq * sh + r * sr + dd] = acc;
-  } else {
-    if (!p.db) return;
-    const int nbt = p.t5.nb;  // entries per head in the partials
-    if (p.ob) {
-      // offset-bias table [hb, 2W + 1]: entries outside the loaded window
-      // (offsets no pair reaches) get zero
-      const int nw = 2 * p.ob_w + 1;
-      const int64_t total = (int64_t)p.hb * nw;
-      if (idx >= total) return;
-      const int w = (int)(idx % nw), hq = (int)(idx / nw);
-      const int e = w - p.ob_lo;
-      float acc = 0.f;
-      if (e >= 0 && e < nbt) {
-        const int h_lo = p.hb == 1 ? 0 : hq, h_hi = p.hb == 1 ? p.H : hq + 1;
-        for (int b = 0; b < p.B; ++b)
-          for (int hh = h_lo; hh < h_hi; ++hh) {
-            const float* src = p.ws_pb + (int64_t)(b * p.H + hh) * nq * nbt + e;
-            for (int t = 0; t < nq; ++t) acc += src[(int64_t)t * nbt];
-          }
-      }
-      p.db[hq * p.db_s0 + w * p.db_s1] = acc;
-    } else {
-      // T5 table [nb, H]
-      const int64_t total = (int64_t)nbt * p.H;
-      if (idx >= total) return;
-      const int hq = (int)(idx % p.H), e = (int)(idx / p.H);
-      float acc = 0.f;
-      for (int b = 0; b < p.B; ++b) {
-        const float* src = p.ws_pb + (int64_t)(b * p.H + hq) * nq * nbt + e;
-        for (int t = 0; t < nq; ++t) acc += src[(int64_t)t * nbt];
-      }
-      p.db[e * p.db_s0 + hq * p.db_s1] = acc;
-    }
+    // a key past the key length is seen by no query: its gradients are zero
+    store_row_block<T, D>(dkg + (int64_t)kj * p.dk_sn, dk, p.scale, hh, !k_ok);
+    store_row_block<T, D>(dvg + (int64_t)kj * p.dv_sn, dv, 1.f, hh, !k_ok);
   }
 }
 
@@ -985,13 +1229,13 @@ static size_t lds_q_t(int qwaves, RelMode mode, bool has_wk, bool has_wv, int nr
       .total;
 }
 template <bool BF16, int D>
-static size_t lds_kv_t(int kqblock, RelMode mode, bool has_wk, bool has_wv, int nrp,
+static size_t lds_kv_t(int kqblock, RelMode mode, bool has_wk, bool has_wv, int nr,
                        int t5_dist) {
   using S = BwdShape<BF16, D>;
   if (kqblock == S::KBQ_WIDE)
-    return (size_t)make_lay_kv<BF16, D, S::KW, S::KBQ_WIDE>(mode, has_wk, has_wv, nrp, t5_dist)
+    return (size_t)make_lay_kv<BF16, D, S::KW, S::KBQ_WIDE>(mode, has_wk, has_wv, nr, t5_dist)
         .total;
-  return (size_t)make_lay_kv<BF16, D, S::KW, S::KBQ_NARROW>(mode, has_wk, has_wv, nrp, t5_dist)
+  return (size_t)make_lay_kv<BF16, D, S::KW, S::KBQ_NARROW>(mode, has_wk, has_wv, nr, t5_dist)
       .total;
 }
 
@@ -1021,12 +1265,12 @@ static size_t lds_q_d(int d, int qw, RelMode mode, bool wk, bool wv, int nr, int
   }
 }
 template <bool BF16>
-static size_t lds_kv_d(int d, int bq, RelMode mode, bool wk, bool wv, int nrp, int dist) {
+static size_t lds_kv_d(int d, int bq, RelMode mode, bool wk, bool wv, int nr, int dist) {
   switch (d) {
-    case 16: return lds_kv_t<BF16, 16>(bq, mode, wk, wv, nrp, dist);
-    case 32: return lds_kv_t<BF16, 32>(bq, mode, wk, wv, nrp, dist);
-    case 64: return lds_kv_t<BF16, 64>(bq, mode, wk, wv, nrp, dist);
-    default: return lds_kv_t<BF16, 128>(bq, mode, wk, wv, nrp, dist);
+    case 16: return lds_kv_t<BF16, 16>(bq, mode, wk, wv, nr, dist);
+    case 32: return lds_kv_t<BF16, 32>(bq, mode, wk, wv, nr, dist);
+    case 64: return lds_kv_t<BF16, 64>(bq, mode, wk, wv, nr, dist);
+    default: return lds_kv_t<BF16, 128>(bq, mode, wk, wv, nr, dist);
   }
 }
 
@@ -1036,9 +1280,9 @@ size_t bwd_lds_q(bool bf16, int d, const BwdCfg& cfg, RelMode mode, bool has_wk,
               : lds_q_d<false>(d, cfg.qwaves, mode, has_wk, has_wv, nr, t5_dist, nb, want_db);
 }
 size_t bwd_lds_kv(bool bf16, int d, const BwdCfg& cfg, RelMode mode, bool has_wk, bool has_wv,
-                  int nrp, int t5_dist) {
-  return bf16 ? lds_kv_d<true>(d, cfg.kqblock, mode, has_wk, has_wv, nrp, t5_dist)
-              : lds_kv_d<false>(d, cfg.kqblock, mode, has_wk, has_wv, nrp, t5_dist);
+                  int nr, int t5_dist) {
+  return bf16 ? lds_kv_d<true>(d, cfg.kqblock, mode, has_wk, has_wv, nr, t5_dist)
+              : lds_kv_d<false>(d, cfg.kqblock, mode, has_wk, has_wv, nr, t5_dist);
 }
 
 template <int D, int NW, int BC, bool BF16, int MODE, bool WK, bool WV>
@@ -1059,7 +1303,7 @@ static int launch_q(const BwdParams& p, hipStream_t s) {
 
 template <int D, int NW, int BQ, bool BF16, int MODE, bool WK, bool WV>
 static int launch_kv(const BwdParams& p, hipStream_t s) {
-  const LayKV lay = make_lay_kv<BF16, D, NW, BQ>(MODE, WK, WV, p.nrp, p.t5_dist);
+  const LayKV lay = make_lay_kv<BF16, D, NW, BQ>(MODE, WK, WV, p.nr, p.t5_dist);
   auto kern = bwd_kv_kernel<D, NW, BQ, BF16, MODE, WK, WV>;
   if (lay.total > 64 * 1024) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -1067,8 +1311,8 @@ static int launch_kv(const BwdParams& p, hipStream_t s) {
                                              lay.total);
     if (e != hipSuccess) return (int)e;
   }
-  const dim3 grid((unsigned)((int64_t)p.B * p.H * p.n_ktiles));
-  hipLaunchKernelGGL(kern, grid, dim3(64 * NW), (size_t)lay.total, s, p);
+  const dim3 grid((unsigned)((int64_t)p.B * p.H * p.n_ktiles + reduce_role_count(p, 64 * NW)));
+  hipLaunchKernelGGL(kern, grid, dim3(64 * NW), (size_t)max(lay.total, 64 * NW * 4), s, p);
   return (int)hipGetLastError();
 }
 
@@ -1083,15 +1327,6 @@ static int launch_bwd_t(const BwdCfg& cfg, const BwdParams& p, void* stream) {
   e = cfg.kqblock == S::KBQ_WIDE ? launch_kv<D, S::KW, S::KBQ_WIDE, BF16, MODE, WK, WV>(p, s)
                                  : launch_kv<D, S::KW, S::KBQ_NARROW, BF16, MODE, WK, WV>(p, s);
   if (e != (int)hipSuccess) return e;
-  if (p.dwk || p.dwv || p.db) {
-    int64_t most = 0;
-    if (p.dwk) most = max(most, (int64_t)p.htk * (2 * p.clip + 1) * p.d);
-    if (p.dwv) most = max(most, (int64_t)p.htv * (2 * p.clip + 1) * p.d);
-    if (p.db) most = max(most, p.ob ? (int64_t)p.hb * (2 * p.ob_w + 1) : (int64_t)p.t5.nb * p.H);
-    const dim3 grid((unsigned)((most + 255) / 256), 3);
-    hipLaunchKernelGGL(bwd_reduce_kernel, grid, dim3(256), 0, s, p);
-    e = (int)hipGetLastError();
-  }
   return e;
 }
 

@@ -94,8 +94,6 @@ int launch_debug_indices(int n, int clip, const T5Buckets* t5, int32_t* out,
 // Everything the three backward launches need.  Strides count elements.
 // Workspace sections (fp32):
 //   ws_stat [B*H][2][n_pad] + 64 : per query, lse in log2 units and D = dz.z
-//   ws_rl   [B*H][n_pad][nrp]    : relative logits (log2 units) of labels r_lo..
-//   ws_rv   [B*H][n_pad][nrp]    : dz_i . w^V_r
 //   ws_pk   [B*H][n_qtiles][nr][d], ws_pv the same : per query-tile partial
 //                                  table gradients (ws_pk already scaled)
 //   ws_pb   [B*H][n_qtiles][nb]  : per query-tile partial bias gradients
@@ -117,8 +115,6 @@ struct BwdParams {
   float* dwv;
   float* db;                // T5: [NB, H]; offset bias: [Hb, 2W+1]; or null
   float* ws_stat;
-  float* ws_rl;
-  float* ws_rv;
   float* ws_pk;
   float* ws_pv;
   float* ws_pb;
@@ -142,7 +138,7 @@ struct BwdParams {
   int32_t B, H, n, d;
   int32_t n_pad;            // n rounded up to 64
   int32_t clip;
-  int32_t r_lo, nr, nrp;    // reachable labels [r_lo, r_lo + nr); nrp = row stride
+  int32_t r_lo, nr;         // reachable labels [r_lo, r_lo + nr)
   int32_t htk, htv;         // table heads (H or 1)
   int32_t hb;               // bias gradient heads (offset bias: H or 1)
   int32_t causal;
@@ -167,7 +163,7 @@ BwdCfg bwd_cfg(bool bf16, int d, bool narrow_q, bool narrow_kv);
 size_t bwd_lds_q(bool bf16, int d, const BwdCfg& cfg, RelMode mode, bool has_wk, bool has_wv,
                  int nr, int t5_dist, int nb, bool want_db);
 size_t bwd_lds_kv(bool bf16, int d, const BwdCfg& cfg, RelMode mode, bool has_wk, bool has_wv,
-                  int nrp, int t5_dist);
+                  int nr, int t5_dist);
 int launch_bwd(bool bf16, int d, const BwdCfg& cfg, RelMode mode, bool has_wk, bool has_wv,
                const BwdParams& p, void* stream);
 
