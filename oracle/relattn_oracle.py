@@ -64,6 +64,7 @@ __all__ = [
     "offset_bias_attention",
     "relattn_backward",
     "t5_backward",
+    "offset_bias_backward",
     "to_f64",
 ]
 
@@ -549,4 +550,33 @@ def t5_backward(q, k, v, bias, num_buckets: int = 32, max_distance: int = 128,
             dk[b, h] = s * de.T @ q[b, h]
             dv[b, h] = alpha.T @ dz[b, h]
             db[:, h] += np.bincount(Bm.ravel(), weights=de.ravel(), minlength=num_buckets)
+    return dq, dk, dv, db
+
+
+def offset_bias_backward(q, k, v, bias, window: int, dz=None, scale=None,
+                         causal: bool = False, key_lens=None):
+    """Gradients (dq, dk, dv, dbias) of sum(dz * z) for offset_bias_attention:
+    de as in ``relattn_backward`` with dalpha_ij = dz_i . v_j, and dbias[h', w]
+    = sum over the pairs whose clipped offset has entry w of de_ij (summed over
+    the heads when one row serves every head)."""
+    q, k, v, dz = to_f64(q), to_f64(k), to_f64(v), to_f64(dz)
+    bias = to_f64(bias)
+    B, H, n, d = q.shape
+    s = _default_scale(d, scale)
+    lens = _key_lengths(key_lens, B, n)
+    R = relative_labels(n, window) + window
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    db = np.zeros_like(bias)
+    for b in range(B):
+        ok = visible(n, causal, lens[b])
+        for h in range(H):
+            hb = 0 if bias.shape[0] == 1 else h
+            e = s * (q[b, h] @ k[b, h].T) + bias[hb][R]
+            alpha = _masked_softmax_rows(e, ok)
+            dalpha = dz[b, h] @ v[b, h].T
+            de = alpha * (dalpha - (alpha * dalpha).sum(axis=1, keepdims=True))
+            dq[b, h] = s * de @ k[b, h]
+            dk[b, h] = s * de.T @ q[b, h]
+            dv[b, h] = alpha.T @ dz[b, h]
+            db[hb] += np.bincount(R.ravel(), weights=de.ravel(), minlength=2 * window + 1)
     return dq, dk, dv, db

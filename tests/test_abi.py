@@ -215,3 +215,94 @@ def test_offset_bias_validation(ra):
     big = 40000
     qb, kb, vb = qkv(B=1, H=1, n=50000)
     assert ra.validate_offset_bias(qb, kb, vb, F(1, 2 * big + 1), big) == ra.UNSUPPORTED
+
+
+# ---------------------------------------------------------------------------
+# backward: host-only checks of relattn_bwd_workspace_size (no HIP call)
+# ---------------------------------------------------------------------------
+
+def _ws_expected(B, H, n, d, nr, tables, nb=0, brq=128):
+    """Workspace bytes from the sections the library documents: per query, lse
+    and D (+64 floats of slack); per query tile of the dq kernel, the partial
+    gradient of each table ([nr, d]) and of the bias ([nb]); each section
+    rounded up to 256 bytes."""
+    up = lambda floats: (floats * 4 + 255) // 256 * 256
+    n_pad = (n + 63) // 64 * 64
+    nqt = (n + brq - 1) // brq
+    total = up(B * H * 2 * n_pad + 64)
+    total += tables * up(B * H * nqt * nr * d)
+    if nb:
+        total += up(B * H * nqt * nb)
+    return total
+
+
+def _bwd_ws(ra, q, k, v, wK=None, wV=None, **kw):
+    B, H, n, d = q.shape
+    out = torch.zeros_like(q)
+    lse = T(B, H, n, dtype=torch.float32)
+    return ra.bwd_workspace_size(q, k, v, wK, wV, out=out, dout=torch.zeros_like(q), lse=lse,
+                                 **kw)
+
+
+def test_bwd_workspace_size(ra):
+    q, k, v = qkv(B=2, H=3, n=300, d=64)
+    # causal: labels -4..0 reachable (nr = 5); non-causal: all 9
+    assert _bwd_ws(ra, q, k, v, T(3, 9, 64), T(3, 9, 64), clip=4, causal=True) == \
+        _ws_expected(2, 3, 300, 64, 5, 2)
+    assert _bwd_ws(ra, q, k, v, T(3, 9, 64), None, clip=4) == _ws_expected(2, 3, 300, 64, 9, 1)
+    assert _bwd_ws(ra, q, k, v) == _ws_expected(2, 3, 300, 64, 1, 0)
+    t5 = T(32, 3, dtype=torch.float32)
+    assert _bwd_ws(ra, q, k, v, t5_bias=t5) == _ws_expected(2, 3, 300, 64, 1, 0, nb=32)
+    assert _bwd_ws(ra, q, k, v, t5_bias=t5, want_dbias=False) == _ws_expected(2, 3, 300, 64, 1, 0)
+    q0, k0, v0 = qkv(B=0)
+    assert _bwd_ws(ra, q0, k0, v0) == 0
+
+
+@pytest.mark.parametrize("case", ["dout_shape", "lse_dtype", "lse_shape", "dq_dtype",
+                                  "dwk_without_wk", "dwk_shape", "dwk_dtype",
+                                  "dbias_without_bias"])
+def test_bwd_rejects(ra, case):
+    q, k, v = qkv(n=50)
+    B, H, n, d = q.shape
+    wK = T(3, 9, 64)
+    out, dout = torch.zeros_like(q), torch.zeros_like(q)
+    lse = T(B, H, n, dtype=torch.float32)
+    kw = dict(clip=4)
+    tabs = [wK, None]
+    if case == "dout_shape":
+        dout = T(B, H, n + 1, d)
+    elif case == "lse_dtype":
+        lse = T(B, H, n)
+    elif case == "lse_shape":
+        lse = T(B, H, n - 1, dtype=torch.float32)
+    elif case == "dq_dtype":
+        kw["dq"] = torch.zeros_like(q).float()
+    elif case == "dwk_without_wk":
+        tabs = [None, None]
+        kw["dwK"] = T(3, 9, 64, dtype=torch.float32)
+    elif case == "dwk_shape":
+        kw["dwK"] = T(3, 7, 64, dtype=torch.float32)
+    elif case == "dwk_dtype":
+        kw["dwK"] = T(3, 9, 64)
+    elif case == "dbias_without_bias":
+        kw["dbias"] = T(32, 3, dtype=torch.float32)
+    with pytest.raises(ra.RelattnError) as e:
+        ra.bwd_workspace_size(q, k, v, *tabs, out=out, dout=dout, lse=lse, **kw)
+    assert e.value.status == ra.INVALID_ARGUMENT, case
+
+
+def test_bwd_offset_bias_window_checks(ra):
+    """A bias gradient needs per-workgroup sums over 2*min(W, n-1)+1 offsets on
+    chip: too wide is UNSUPPORTED; without the bias gradient it is accepted."""
+    q, k, v = qkv(B=1, H=2, n=600, d=64)
+    out, dout = torch.zeros_like(q), torch.zeros_like(q)
+    lse = T(1, 2, 600, dtype=torch.float32)
+    bias = T(2, 2 * 599 + 1, dtype=torch.float32)
+    with pytest.raises(ra.RelattnError) as e:
+        ra.bwd_offset_bias_workspace_size(q, k, v, bias, 599, out=out, dout=dout, lse=lse)
+    assert e.value.status == ra.UNSUPPORTED
+    assert ra.bwd_offset_bias_workspace_size(q, k, v, bias, 599, out=out, dout=dout, lse=lse,
+                                             want_dbias=False) > 0
+    small = T(2, 11, dtype=torch.float32)
+    assert ra.bwd_offset_bias_workspace_size(q, k, v, small, 5, out=out, dout=dout,
+                                             lse=lse) > 0

@@ -253,3 +253,67 @@ def test_backward_full_size_sampled(ra, shape):
         else:
             zsum += rows.sum(axis=1)
     assert np.max(np.abs(dwv.sum(axis=1) - zsum)) <= 0.02 * np.abs(zsum).max()
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=str)
+@pytest.mark.parametrize("mask", ["none", "causal", "lens"])
+@pytest.mark.parametrize("window,shared", [(0, False), (5, True), (20, False)])
+def test_offset_bias_backward_parity(ra, dtype, mask, window, shared):
+    """Scalar bias by clipped offset: dq, dk, dv and the table gradient."""
+    B, H, n, d = 2, 3, 150, 64
+    q, k, v, dz = (gen((B, H, n, d), dtype, 1000 + window + i) for i in range(4))
+    bias = gen((1 if shared else H, 2 * window + 1), torch.float32, 1005)
+    causal = mask == "causal"
+    lens = [n, 77] if mask == "lens" else None
+    lens_d = None if lens is None else torch.tensor(lens, dtype=torch.int32, device=DEV)
+    qd, kd, vd, bd, dzd = (dev(x) for x in (q, k, v, bias, dz))
+    out, lse = ra.fwd_offset_bias_lse(qd, kd, vd, bd, window, causal=causal, key_lens=lens_d)
+    got = ra.bwd_offset_bias(qd, kd, vd, bd, window, out=out, dout=dzd, lse=lse, causal=causal,
+                             key_lens=lens_d)
+    torch.cuda.synchronize()
+    want = oracle.offset_bias_backward(q, k, v, bias, window, dz, causal=causal, key_lens=lens)
+    if window == 0 and dtype == torch.bfloat16:
+        # one entry for every pair: a constant per head, which the softmax
+        # ignores, so the true gradient is 0.  What remains is the rounding of
+        # D_i = dz_i.z_i taken with the stored bf16 output: per row
+        # |sum_j dS_ij| = |D_exact - D_used| <= 2^-9 sum_d |dz_id| |z_id|
+        # (2^-8 below covers the sums' own rounding)
+        check(got[:3], want[:3], dtype, names=("dq", "dk", "dv"))
+        z = oracle.offset_bias_attention(q, k, v, bias, window, causal=causal, key_lens=lens)
+        per_head = 2.0 ** -8 * (np.abs(dz.double().numpy()) * np.abs(z)).sum(axis=(0, 2, 3))
+        bound = per_head if bias.shape[0] > 1 else per_head.sum(keepdims=True)
+        err = np.abs(got[3].double().cpu().numpy()[:, 0] - want[3][:, 0])
+        assert np.all(err <= bound), (err, bound)
+    else:
+        check(got, want, dtype, names=("dq", "dk", "dv", "dbias"))
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=str)
+def test_alibi_backward_without_bias_gradient(ra, dtype):
+    """Causal ALiBi over the whole sequence (window n - 1, fixed slopes): the
+    bias gradient is not asked for; dq, dk, dv against the oracle."""
+    B, H, n, d = 2, 4, 200, 64
+    q, k, v, dz = (gen((B, H, n, d), dtype, 1100 + i) for i in range(4))
+    W = n - 1
+    slopes = [2.0 ** (-8.0 * (h + 1) / H) for h in range(H)]
+    bias = torch.tensor([[-m * abs(x) for x in range(-W, W + 1)] for m in slopes])
+    qd, kd, vd, bd, dzd = (dev(x) for x in (q, k, v, bias, dz))
+    out, lse = ra.fwd_offset_bias_lse(qd, kd, vd, bd, W, causal=True)
+    dq, dk, dv, db = ra.bwd_offset_bias(qd, kd, vd, bd, W, out=out, dout=dzd, lse=lse,
+                                        causal=True, want_dbias=False)
+    torch.cuda.synchronize()
+    assert db is None
+    want = oracle.offset_bias_backward(q, k, v, bias, W, dz, causal=True)
+    check((dq, dk, dv), want[:3], dtype, names=("dq", "dk", "dv"))
+
+
+def test_backward_rejects_bias_gradient_too_wide(ra):
+    """A bias gradient over 2n - 1 offsets does not fit on chip: UNSUPPORTED,
+    reported before any launch."""
+    B, H, n, d = 1, 2, 600, 64
+    q, k, v, dz = (gen((B, H, n, d), torch.bfloat16, 1200 + i).to(DEV) for i in range(4))
+    bias = torch.zeros(H, 2 * (n - 1) + 1, device=DEV)
+    out, lse = ra.fwd_offset_bias_lse(q, k, v, bias, n - 1)
+    with pytest.raises(ra.RelattnError) as e:
+        ra.bwd_offset_bias(q, k, v, bias, n - 1, out=out, dout=dz, lse=lse)
+    assert e.value.status == ra.UNSUPPORTED

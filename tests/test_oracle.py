@@ -662,3 +662,39 @@ def test_t5_backward_bias_gradient_sums_to_zero():
     for mine, theirs in zip((dq, dk, dv), t):
         np.testing.assert_allclose(mine, theirs.grad.numpy(), rtol=0, atol=1e-12)
     np.testing.assert_allclose(db1.sum(axis=0), 0.0, atol=1e-12)
+
+
+@pytest.mark.parametrize("shared,causal", [(False, False), (True, True)])
+def test_offset_bias_backward_matches_finite_differences(shared, causal):
+    B, H, n, d, W = 1, 2, 12, 4, 5
+    q, k, v, dz = (rnd((B, H, n, d), 160 + i) for i in range(4))
+    bias = rnd((1 if shared else H, 2 * W + 1), 164)
+    grads = oracle.offset_bias_backward(q, k, v, bias, W, dz, causal=causal, key_lens=[9])
+    loss = lambda: float((dz * oracle.offset_bias_attention(q, k, v, bias, W, causal=causal,
+                                                           key_lens=[9])).sum())
+    rng = np.random.default_rng(165)
+    for x, g in zip((q, k, v, bias), grads):
+        idx = [tuple(int(rng.integers(s)) for s in x.shape) for _ in range(6)]
+        _fd_check(loss, x, g, idx)
+
+
+@pytest.mark.parametrize("bidir", [True, False])
+def test_offset_bias_backward_against_t5_backward(bidir):
+    """A table holding each offset's T5 bucket bias is the T5 forward; its
+    gradient summed over the offsets of each bucket is the T5 bias gradient,
+    and q, k, v get the same gradients."""
+    B, H, n, d, nb, maxd = 1, 2, 40, 8, 8, 12
+    q, k, v, dz = (rnd((B, H, n, d), 170 + i) for i in range(4))
+    tb = rnd((nb, H), 174)
+    W = n - 1
+    beta = np.array([oracle.t5_bucket(w - W, nb, maxd, bidir) for w in range(2 * W + 1)])
+    table = tb[beta].T  # [H, 2W + 1]
+    dq, dk, dv, dob = oracle.offset_bias_backward(q, k, v, table, W, dz, scale=1.0,
+                                                  causal=True)
+    tq, tk, tv, dtb = oracle.t5_backward(q, k, v, tb, nb, maxd, bidir, dz, causal=True)
+    for a, b_ in ((dq, tq), (dk, tk), (dv, tv)):
+        np.testing.assert_allclose(a, b_, rtol=0, atol=1e-12)
+    for h in range(H):
+        folded = np.bincount(beta, weights=dob[h], minlength=nb)
+        np.testing.assert_allclose(folded, dtb[:, h], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dob.sum(axis=1), 0.0, atol=1e-12)
