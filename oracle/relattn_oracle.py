@@ -35,6 +35,12 @@ Readings where the pages are silent or garbled (each is listed in the design doc):
   B buckets for delta <= 0 and maps delta > 0 to bucket 0;
 * the floor in beta is taken of the exact real number (rational comparison),
   not of a rounded floating-point logarithm;
+* Transformer-XL (transformer-xl page, "Relative Position Encoding in
+  Transformer-XL", and the survey page's "Transformer-XL" section): the score is
+  the four terms (a) q.k, (b) q.R_{i-j}, (c) u.k, (d) v.R_{i-j}, with R the
+  projected relative encodings, given as a table over i - j (clipped to +-W like
+  the other tables; W >= n - 1 clips nothing); the attention scale (1/sqrt(d) by
+  default) multiplies the whole score, as it does for the Shaw logit;
 * backward (no page prints it): the gradients of a scalar loss sum(dz * z) by
   the chain rule through the forward above; a table shared by all heads takes
   the sum over heads, and hidden pairs give no gradient.  Pinned by central
@@ -65,6 +71,7 @@ __all__ = [
     "relattn_backward",
     "t5_backward",
     "offset_bias_backward",
+    "xl_attention",
     "to_f64",
 ]
 
@@ -580,3 +587,40 @@ def offset_bias_backward(q, k, v, bias, window: int, dz=None, scale=None,
             dv[b, h] = alpha.T @ dz[b, h]
             db[hb] += np.bincount(R.ravel(), weights=de.ravel(), minlength=2 * window + 1)
     return dq, dk, dv, db
+
+
+def xl_attention(q, k, v, R, u, vb, window: int, scale=None, causal: bool = False,
+                 key_lens=None):
+    """Transformer-XL relative logits (transformer-xl page, the four-term score;
+    survey page, section "Transformer-XL"):
+
+        A_ij = s * [ q_i.k_j  +  q_i.R_{i-j}  +  u.k_j  +  v.R_{i-j} ]
+                      (a)          (b)          (c)        (d)
+
+    R: [Hr, 2*window + 1, d], row window + (i - j) holds distance i - j;
+    distances beyond +-window take the end rows.  u, vb: [Hu, d] (Hr, Hu in
+    {1, H}; 1 = shared by all heads).  Softmax over the visible keys, z = alpha V
+    (no value term).  s defaults to 1/sqrt(d).
+    """
+    q, k, v = to_f64(q), to_f64(k), to_f64(v)
+    R, u, vb = to_f64(R), to_f64(u), to_f64(vb)
+    B, H, n, d = q.shape
+    s = _default_scale(d, scale)
+    lens = _key_lengths(key_lens, B, n)
+    i = np.arange(n)[:, None]
+    j = np.arange(n)[None, :]
+    dist = np.clip(i - j, -window, window) + window  # row of R for each pair
+    z = np.zeros((B, H, n, v.shape[-1]))
+    for b in range(B):
+        ok = visible(n, causal, lens[b])
+        for h in range(H):
+            Rh = R[0 if R.shape[0] == 1 else h][dist]          # [n, n, d]
+            uh = u[0 if u.shape[0] == 1 else h]
+            vh = vb[0 if vb.shape[0] == 1 else h]
+            term_a = q[b, h] @ k[b, h].T
+            term_b = np.einsum("id,ijd->ij", q[b, h], Rh)
+            term_c = (k[b, h] @ uh)[None, :]
+            term_d = np.einsum("d,ijd->ij", vh, Rh)
+            e = s * (term_a + term_b + term_c + term_d)
+            z[b, h] = _masked_softmax_rows(e, ok) @ v[b, h]
+    return z

@@ -698,3 +698,48 @@ def test_offset_bias_backward_against_t5_backward(bidir):
         folded = np.bincount(beta, weights=dob[h], minlength=nb)
         np.testing.assert_allclose(folded, dtb[:, h], rtol=0, atol=1e-12)
     np.testing.assert_allclose(dob.sum(axis=1), 0.0, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# Transformer-XL relative logits
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("causal,window,shared", [(False, 20, False), (True, 20, True),
+                                                  (False, 3, False)])
+def test_xl_without_global_biases_is_shaw_with_reversed_table(causal, window, shared):
+    """u = v = 0 leaves terms (a) and (b): the Shaw key term with the table read
+    by i - j instead of j - i, i.e. w^K[r] = R[2W - r]."""
+    B, H, n, d = 2, 2, 11, 8
+    q, k, v = (rnd((B, H, n, d), 180 + i) for i in range(3))
+    R = rnd((1 if shared else H, 2 * window + 1, d), 183)
+    zero = np.zeros((1, d))
+    got = oracle.xl_attention(q, k, v, R, zero, zero, window, causal=causal, key_lens=[n, 7])
+    want = oracle.relattn_bruteforce(q, k, v, R[:, ::-1].copy(), None, window, causal=causal,
+                                     key_lens=[n, 7])
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-12)
+
+
+def test_xl_without_position_table_is_attention_of_shifted_queries():
+    """R = 0 leaves terms (a) and (c): q_i.k_j + u.k_j = (q_i + u).k_j, i.e.
+    library attention of q + u; term (d) vanishes whatever v is."""
+    B, H, n, d, W = 1, 3, 9, 8, 4
+    q, k, v = (rnd((B, H, n, d), 190 + i) for i in range(3))
+    u, vb = rnd((H, d), 193), rnd((H, d), 194)
+    got = oracle.xl_attention(q, k, v, np.zeros((H, 2 * W + 1, d)), u, vb, W, causal=True)
+    qs = torch.tensor(q + u[None, :, None, :])
+    want = torch.nn.functional.scaled_dot_product_attention(
+        qs, torch.tensor(k), torch.tensor(v), is_causal=True).numpy()
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-12)
+
+
+def test_xl_global_position_bias_is_an_offset_bias():
+    """q = 0 and u = 0 leave term (d) alone: v.R_{i-j} is a scalar
+    by distance, i.e. an offset bias with entry W + (j - i) = v.R[W - (j - i)]."""
+    B, H, n, d, W = 1, 2, 10, 8, 6
+    k, v = rnd((B, H, n, d), 200), rnd((B, H, n, d), 201)
+    q = np.zeros((B, H, n, d))
+    R, vb = rnd((H, 2 * W + 1, d), 202), rnd((H, d), 203)
+    got = oracle.xl_attention(q, k, v, R, np.zeros((H, d)), vb, W, scale=0.5)
+    bias = np.stack([0.5 * (R[h] @ vb[h])[::-1] for h in range(H)])  # entry W + (j - i)
+    want = oracle.offset_bias_attention(q, k, v, bias, W, scale=0.5)
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-12)
