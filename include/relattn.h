@@ -150,6 +150,38 @@ int relattn_fwd_offset_bias(const relattn_tensor* q, const relattn_tensor* k,
                             int32_t window, float scale, const relattn_mask* mask,
                             relattn_tensor* out, void* stream);
 
+/*
+ * relattn_fwd_xl: Transformer-XL relative logits (the transformer-xl page's
+ * four-term score; survey page, section "Transformer-XL"):
+ *
+ *       e_ij = scale * [ q_i.k_j + q_i.R_{i-j} + u.k_j + v.R_{i-j} ]
+ *            = scale * [ (q_i + u).k_j + (q_i + v).R_{i-j} ]
+ *
+ *   q, k, v, out : as for relattn_fwd.  No value term: z_i = sum_j alpha_ij v_j.
+ *   R            : [Hr, 2*window + 1, d] position table (the projected
+ *                  relative encodings W_R r), dtype of q, Hr in {H, 1}; row
+ *                  window + (i - j) holds distance i - j; distances beyond
+ *                  +-window take the end rows (window >= n - 1 clips nothing).
+ *   u, vb        : [Hu, d] global biases (dtype of q, Hu in {H, 1}, rows
+ *                  16-byte aligned): u for the content logit, vb for the
+ *                  relative logit.  q + u and q + vb are rounded once to the
+ *                  input dtype.
+ *   scale        : multiplies the whole score; <= 0 picks 1/sqrt(d).
+ *   mask, stream : as for relattn_fwd.
+ * The segment memory of Transformer-XL (keys longer than the queries) is not
+ * part of this call.  Errors as for relattn_fwd.
+ */
+int relattn_fwd_xl(const relattn_tensor* q, const relattn_tensor* k, const relattn_tensor* v,
+                   const relattn_tensor* R, const relattn_tensor* u, const relattn_tensor* vb,
+                   int32_t window, float scale, const relattn_mask* mask, relattn_tensor* out,
+                   void* stream);
+
+/* relattn_validate_xl: the argument checks of relattn_fwd_xl, host only. */
+int relattn_validate_xl(const relattn_tensor* q, const relattn_tensor* k, const relattn_tensor* v,
+                        const relattn_tensor* R, const relattn_tensor* u, const relattn_tensor* vb,
+                        int32_t window, float scale, const relattn_mask* mask,
+                        const relattn_tensor* out);
+
 /* relattn_validate_offset_bias: the argument checks of relattn_fwd_offset_bias,
  * host only (no HIP call). */
 int relattn_validate_offset_bias(const relattn_tensor* q, const relattn_tensor* k,

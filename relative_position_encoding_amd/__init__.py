@@ -13,7 +13,7 @@ import os
 __all__ = ["fwd", "validate", "fwd_offset_bias", "validate_offset_bias", "decode",
            "decode_workspace_size", "debug_indices", "fwd_lse", "fwd_offset_bias_lse",
            "bwd", "bwd_workspace_size", "bwd_offset_bias", "bwd_offset_bias_workspace_size",
-           "attention", "attention_offset_bias",
+           "attention", "attention_offset_bias", "fwd_xl", "validate_xl",
            "RelattnError", "library_path",
            "OK", "INVALID_ARGUMENT", "UNSUPPORTED", "NO_DEVICE", "LAUNCH_FAILED"]
 
@@ -92,6 +92,11 @@ def _load():
     lib.relattn_bwd_offset_bias.restype = ctypes.c_int
     lib.relattn_bwd_offset_bias_workspace_size.argtypes = obw + [P(ctypes.c_size_t)]
     lib.relattn_bwd_offset_bias_workspace_size.restype = ctypes.c_int
+    xl = [P(_Tensor)] * 6 + [ctypes.c_int32, ctypes.c_float, P(_Mask), P(_Tensor)]
+    lib.relattn_fwd_xl.argtypes = xl + [ctypes.c_void_p]
+    lib.relattn_fwd_xl.restype = ctypes.c_int
+    lib.relattn_validate_xl.argtypes = xl
+    lib.relattn_validate_xl.restype = ctypes.c_int
     lib.relattn_debug_indices.argtypes = [ctypes.c_int32, ctypes.c_int32, P(_T5),
                                           ctypes.c_void_p, ctypes.c_void_p]
     lib.relattn_debug_indices.restype = ctypes.c_int
@@ -586,3 +591,48 @@ def attention_offset_bias(q, k, v, bias, window, *, causal=False, key_lens=None,
         _fns = _autograd_fn()
     return _fns[1].apply(q, k, v, bias, window,
                          dict(causal=causal, key_lens=key_lens, scale=scale))
+
+
+# ---------------------------------------------------------------------------
+# Transformer-XL relative logits
+# ---------------------------------------------------------------------------
+
+def _xl_args(q, k, v, R, u, vb, window, causal, key_lens, scale, out):
+    views = [_view(x) for x in (q, k, v, R, u, vb)]
+    mask = None
+    if causal or key_lens is not None:
+        mask = _Mask(1 if causal else 0, key_lens.data_ptr() if key_lens is not None else None)
+    outv = _view(out)
+    args = [_ref(x) for x in views] + [int(window), float(0.0 if scale is None else scale),
+                                        _ref(mask), _ref(outv)]
+    return args, views + [mask, outv]
+
+
+def fwd_xl(q, k, v, R, u, vb, window, *, causal=False, key_lens=None, scale=None, out=None,
+           stream=None):
+    """Transformer-XL relative logits: e_ij = s[(q_i + u).k_j + (q_i + vb).R_{i-j}].
+
+    R: [H or 1, 2*window+1, d], row window + (i - j) for distance i - j; u, vb:
+    [H or 1, d] global biases; all in the dtype of q.  Returns ``out``."""
+    import torch
+    lib = _load()
+    _check_lens(key_lens)
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    args, keep = _xl_args(q, k, v, R, u, vb, window, causal, key_lens, scale, out)
+    st = lib.relattn_fwd_xl(*args, ctypes.c_void_p(_stream_of(q, stream)))
+    del keep
+    if st != OK:
+        _raise(lib, st)
+    return out
+
+
+def validate_xl(q, k, v, R, u, vb, window, *, causal=False, key_lens=None, scale=None,
+                out=None):
+    """Host-only argument check of ``fwd_xl``; returns the status code."""
+    lib = _load()
+    args, keep = _xl_args(q, k, v, R, u, vb, window, causal, key_lens, scale,
+                          q if out is None else out)
+    st = lib.relattn_validate_xl(*args)
+    del keep
+    return st

@@ -197,7 +197,8 @@ int make_plan(const relattn_tensor* q, const relattn_tensor* k, const relattn_te
               const relattn_tensor* wK, const relattn_tensor* wV,
               const relattn_tensor* t5_bias, const relattn_t5_params* t5, int32_t clip_k,
               float scale, const relattn_mask* mask, const relattn_tensor* out, Plan* plan,
-              bool want_t5_table, const relattn_tensor* ob = nullptr, int32_t ob_window = 0) {
+              bool want_t5_table, const relattn_tensor* ob = nullptr, int32_t ob_window = 0,
+              const relattn_tensor* xl_u = nullptr, const relattn_tensor* xl_v = nullptr) {
   int st;
   if ((st = check_view(q, "q", 4, true))) return st;
   if ((st = check_view(k, "k", 4, true))) return st;
@@ -246,7 +247,26 @@ int make_plan(const relattn_tensor* q, const relattn_tensor* k, const relattn_te
       return fail(RELATTN_ERR_INVALID_ARGUMENT, "bias: shape[1] must be 2*window+1 = %lld",
                   (long long)(2 * (int64_t)ob_window + 1));
   }
-  if (wK && (st = check_table(wK, "wK", q, clip_k))) return st;
+  const bool is_xl = xl_u != nullptr || xl_v != nullptr;
+  if (is_xl) {
+    // Transformer-XL: wK is the position table R (read by i - j), u and v the
+    // global biases; no value table, no scalar bias
+    if (!xl_u || !xl_v || !wK)
+      return fail(RELATTN_ERR_INVALID_ARGUMENT, "R, u and v must be given together");
+    if (wV || is_t5 || is_ob)
+      return fail(RELATTN_ERR_INVALID_ARGUMENT, "Transformer-XL logits exclude the other tables");
+    const relattn_tensor* uv[2] = {xl_u, xl_v};
+    const char* nm[2] = {"u", "v"};
+    for (int t = 0; t < 2; ++t) {
+      if ((st = check_view(uv[t], nm[t], 2, true))) return st;
+      if (uv[t]->dtype != q->dtype)
+        return fail(RELATTN_ERR_INVALID_ARGUMENT, "%s dtype differs from q", nm[t]);
+      if (!(uv[t]->shape[0] == q->shape[1] || uv[t]->shape[0] == 1) ||
+          uv[t]->shape[1] != q->shape[3])
+        return fail(RELATTN_ERR_INVALID_ARGUMENT, "%s must be [H or 1, d]", nm[t]);
+    }
+  }
+  if (wK && (st = check_table(wK, is_xl ? "R" : "wK", q, clip_k))) return st;
   if (wV && (st = check_table(wV, "wV", q, clip_k))) return st;
   T5Buckets tb = {};
   if (is_t5) {
@@ -392,6 +412,18 @@ int make_plan(const relattn_tensor* q, const relattn_tensor* k, const relattn_te
     p.wk = wK->data;
     p.wk_sh = wK->shape[0] == 1 ? 0 : wK->stride[0];
     p.wk_sr = wK->stride[1];
+  }
+  if (is_xl) {
+    // row r of the label window (offset j - i = r - clip) is R's row for
+    // distance i - j, 2*clip - r: start at the last row and step backwards
+    const int64_t esz = P.bf16 ? 2 : 4;
+    p.wk = static_cast<const char*>(wK->data) + 2 * (int64_t)clip_k * wK->stride[1] * esz;
+    p.wk_sr = -wK->stride[1];
+    p.xl = 1;
+    p.xl_u = xl_u->data;
+    p.xl_v = xl_v->data;
+    p.xl_u_sh = xl_u->shape[0] == 1 ? 0 : xl_u->stride[0];
+    p.xl_v_sh = xl_v->shape[0] == 1 ? 0 : xl_v->stride[0];
   }
   if (wV) {
     p.wv = wV->data;
@@ -959,6 +991,36 @@ int relattn_fwd_offset_bias(const relattn_tensor* q, const relattn_tensor* k,
   if (e != (int)hipSuccess)
     return fail(RELATTN_ERR_LAUNCH_FAILED, "launch failed: %s",
                 hipGetErrorString((hipError_t)e));
+  return RELATTN_OK;
+}
+
+int relattn_validate_xl(const relattn_tensor* q, const relattn_tensor* k, const relattn_tensor* v,
+                        const relattn_tensor* R, const relattn_tensor* u, const relattn_tensor* vb,
+                        int32_t window, float scale, const relattn_mask* mask,
+                        const relattn_tensor* out) {
+  g_last_error.clear();
+  if (!R || !u || !vb) return fail(RELATTN_ERR_INVALID_ARGUMENT, "R, u and v are required");
+  Plan plan;
+  return make_plan(q, k, v, R, nullptr, nullptr, nullptr, window, scale, mask, out, &plan, false,
+                   nullptr, 0, u, vb);
+}
+
+int relattn_fwd_xl(const relattn_tensor* q, const relattn_tensor* k, const relattn_tensor* v,
+                   const relattn_tensor* R, const relattn_tensor* u, const relattn_tensor* vb,
+                   int32_t window, float scale, const relattn_mask* mask, relattn_tensor* out,
+                   void* stream) {
+  g_last_error.clear();
+  if (!R || !u || !vb) return fail(RELATTN_ERR_INVALID_ARGUMENT, "R, u and v are required");
+  Plan plan;
+  int st = make_plan(q, k, v, R, nullptr, nullptr, nullptr, window, scale, mask, out, &plan, true,
+                     nullptr, 0, u, vb);
+  if (st) return st;
+  if ((st = check_device())) return st;
+  if (plan.empty) return RELATTN_OK;
+  const int e = relattn::launch_fwd(plan.bf16, plan.d, plan.cfg, plan.mode, plan.has_wk,
+                                    plan.has_wv, plan.p, stream);
+  if (e != (int)hipSuccess)
+    return fail(RELATTN_ERR_LAUNCH_FAILED, "launch failed: %s", hipGetErrorString((hipError_t)e));
   return RELATTN_OK;
 }
 

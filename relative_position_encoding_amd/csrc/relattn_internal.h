@@ -60,6 +60,13 @@ struct FwdParams {
   // natural-log log-sum-exp of row i's visible logits (-inf for none).
   float* lse;
   int64_t lse_sb, lse_sh;
+  // Transformer-XL (xl = 1, Shaw mode with the key table only): the key table
+  // is the position table R read by i - j, and the query is shifted by the
+  // head's global bias u for the content logit and v for the relative logit.
+  const void* xl_u;
+  const void* xl_v;
+  int64_t xl_u_sh, xl_v_sh;  // head strides (0 = one vector for all heads)
+  int32_t xl;
   T5Buckets t5;
 };
 

@@ -233,6 +233,26 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<D, NW, MODE, BF16, BC>()))) vo
   // DMA instructions issued after a register load and would wait for all of
   // them before the first use of Q.)  Query rows past n and key rows past the
   // key length read the last valid row (finite, never stored or masked).
+  // Transformer-XL: this lane's half of the head's global biases u (content
+  // logit) and v (relative logit), requested before any LDS-DMA so that the
+  // counted DMA waits below stay exact.
+  Op xu[NKS], xv[NKS];
+  if constexpr (SHAW && HAS_WK) {
+    if (p.xl) {
+      const T* up = reinterpret_cast<const T*>(p.xl_u) + h * p.xl_u_sh;
+      const T* vp = reinterpret_cast<const T*>(p.xl_v) + h * p.xl_v_sh;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        if constexpr (BF16) {
+          xu[ks] = *reinterpret_cast<const bf16x8*>(up + 16 * ks + 8 * hh);
+          xv[ks] = *reinterpret_cast<const bf16x8*>(vp + 16 * ks + 8 * hh);
+        } else {
+          xu[ks] = up[2 * ks + hh];
+          xv[ks] = vp[2 * ks + hh];
+        }
+      }
+    }
+  }
   compiler_fence();
   dma_tile<ROWB, NW>(smem_lds + lay.qs, qg, p.q_sn, i0, p.n - 1, G::BR, wave, lane);
   compiler_fence();
@@ -315,6 +335,10 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<D, NW, MODE, BF16, BC>()))) vo
   // T5: one shared vector holds log2e*bias[beta(delta), h] for delta in
   // [-dist, dist] at entries PADL + dist + delta, padded the same way.
   if constexpr (SHAW && HAS_WK) {
+    // the relative logit takes q + v under Transformer-XL
+    Op qpos[NKS];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) qpos[ks] = p.xl ? op_add(qop[ks], xv[ks]) : qop[ks];
     const unsigned char* wkt = smem + lay.wk;
     const int nlb = (p.nr + 31) / 32;
     float edge_lo = 0.f;
@@ -340,7 +364,7 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<D, NW, MODE, BF16, BC>()))) vo
       }
       f32x16 acc = {};
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) acc = mfma(a[ks], qop[ks], acc);
+      for (int ks = 0; ks < NKS; ++ks) acc = mfma(a[ks], qpos[ks], acc);
       if (PADL + nlb * 32 <= lay.lrs) {
         // the whole 32-label block fits the row: entries past the last label
         // land in the padding, which is written below
@@ -355,6 +379,11 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<D, NW, MODE, BF16, BC>()))) vo
         }
       }
       if (lb == 0) edge_lo = acc[0] * p.scale_log2;  // label 0 of this lane's query (hh = 0)
+    }
+    // the content logit takes q + u under Transformer-XL
+    if (p.xl) {
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) qop[ks] = op_add(qop[ks], xu[ks]);
     }
     compiler_fence();  // the row was written by both halves of this wave
     // Under the causal mask no offset above 0 is visible: the upper padding

@@ -248,6 +248,15 @@ __device__ __forceinline__ void frag_col_issue(uint32_t tile_lds, int row0, int 
   asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(lo) : "v"(a0));
   asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(hi) : "v"(a1));
 }
+// Elementwise sum of two MFMA operands, rounded once to the operand type.
+__device__ __forceinline__ bf16x8 op_add(bf16x8 a, bf16x8 b) {
+  bf16x8 r;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r[e] = (__bf16)((float)a[e] + (float)b[e]);
+  return r;
+}
+__device__ __forceinline__ float op_add(float a, float b) { return a + b; }
+
 __device__ __forceinline__ bf16x8 frag_join(bf16x4 lo, bf16x4 hi) {
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }

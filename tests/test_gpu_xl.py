@@ -1,0 +1,103 @@
+"""GPU parity of Transformer-XL relative logits (relattn_fwd_xl, through the C
+ABI) against the fp64 oracle (oracle.xl_attention).  Bars: max-abs 1e-5 (fp32)
+and 2e-2 (bf16; q + u and q + v are rounded once to bf16 like every operand)."""
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+TOL = {torch.float32: 1e-5, torch.bfloat16: 2e-2}
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module")
+def ra():
+    import relative_position_encoding_amd as ra
+    if not os.path.exists(ra.library_path):
+        from relative_position_encoding_amd import build
+        build.build()
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return ra
+
+
+@pytest.fixture(autouse=True)
+def _announce(request):
+    sys.stderr.write(f"\n[gpu-case] {request.node.nodeid}\n")
+    sys.stderr.flush()
+    yield
+
+
+def gen(shape, dtype, seed, std=1.0):
+    g = torch.Generator().manual_seed(seed)
+    return (torch.randn(*shape, generator=g) * std).to(dtype)
+
+
+def run(ra, q, k, v, R, u, vb, window, causal=False, lens=None, scale=None):
+    lens_d = None if lens is None else torch.tensor(lens, dtype=torch.int32, device=DEV)
+    out = ra.fwd_xl(*(x.to(DEV) for x in (q, k, v, R, u, vb)), window, causal=causal,
+                    key_lens=lens_d, scale=scale)
+    torch.cuda.synchronize()
+    return out.double().cpu().numpy()
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=str)
+@pytest.mark.parametrize("d", [32, 64, 128])
+@pytest.mark.parametrize("mask", ["none", "causal", "lens"])
+@pytest.mark.parametrize("window", ["full", 16])
+def test_xl_parity(ra, dtype, d, mask, window):
+    B, H, n = 2, 3, 150
+    W = n - 1 if window == "full" else window
+    q, k, v = (gen((B, H, n, d), dtype, 1300 + d + i) for i in range(3))
+    R = gen((H, 2 * W + 1, d), dtype, 1303, 0.5)
+    u, vb = gen((H, d), dtype, 1304, 0.5), gen((H, d), dtype, 1305, 0.5)
+    causal = mask == "causal"
+    lens = [n, 93] if mask == "lens" else None
+    got = run(ra, q, k, v, R, u, vb, W, causal, lens)
+    # the oracle takes q + u and q + v exactly; the kernel rounds each sum once
+    # to the input dtype, which the bf16 bar covers
+    want = oracle.xl_attention(q, k, v, R, u, vb, W, causal=causal, key_lens=lens)
+    err = float(np.max(np.abs(got - want)))
+    assert err <= TOL[dtype], err
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=str)
+def test_xl_shared_and_scale(ra, dtype):
+    """R, u and v shared by all heads; an explicit scale; a ragged small n."""
+    B, H, n, d, W = 2, 4, 37, 64, 40
+    q, k, v = (gen((B, H, n, d), dtype, 1400 + i) for i in range(3))
+    R = gen((1, 2 * W + 1, d), dtype, 1403, 0.5)
+    u, vb = gen((1, d), dtype, 1404, 0.5), gen((1, d), dtype, 1405, 0.5)
+    got = run(ra, q, k, v, R, u, vb, W, causal=True, scale=0.2)
+    want = oracle.xl_attention(q, k, v, R, u, vb, W, scale=0.2, causal=True)
+    assert float(np.max(np.abs(got - want))) <= TOL[dtype]
+
+
+def test_xl_zero_biases_match_shaw_with_reversed_table(ra):
+    """u = v = 0: bit-identical to relattn_fwd with the table reversed (the
+    same kernel reads the same rows in the same order)."""
+    B, H, n, d, W = 2, 2, 130, 64, 129
+    dtype = torch.bfloat16
+    q, k, v = (gen((B, H, n, d), dtype, 1500 + i).to(DEV) for i in range(3))
+    R = gen((H, 2 * W + 1, d), dtype, 1503, 0.5).to(DEV)
+    zero = torch.zeros(H, d, dtype=dtype, device=DEV)
+    a = ra.fwd_xl(q, k, v, R, zero, zero, W, causal=True)
+    b = ra.fwd(q, k, v, R.flip(1).contiguous(), None, clip=W, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_xl_rejects(ra):
+    q = gen((1, 2, 16, 64), torch.bfloat16, 1600).to(DEV)
+    R = gen((2, 9, 64), torch.bfloat16, 1601).to(DEV)
+    u = gen((2, 64), torch.bfloat16, 1602).to(DEV)
+    assert ra.validate_xl(q, q, q, R, u, u, 4) == ra.OK
+    assert ra.validate_xl(q, q, q, R, u.float(), u, 4) == ra.INVALID_ARGUMENT
+    assert ra.validate_xl(q, q, q, R, u[:, :32].contiguous(), u, 4) == ra.INVALID_ARGUMENT
+    assert ra.validate_xl(q, q, q, R, u, u, 5) == ra.INVALID_ARGUMENT  # R rows != 2W + 1
