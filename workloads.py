@@ -205,3 +205,63 @@ def make_decode_inputs(w: DecodeWorkload | str, *, batch=None, heads=None, cache
     lens = torch.randint(lo, hi + 1, (B,), generator=g, dtype=torch.int32)
     return {"q": q.to(w.dtype), "k": k.to(w.dtype), "v": v.to(w.dtype),
             "key_table": kt.to(w.dtype), "value_table": vt.to(w.dtype), "cache_lens": lens}
+
+
+# ---------------------------------------------------------------------------
+# Transformer-XL relative logits.  The pages give no sizes (the transformer-xl
+# page stops before its implementation); a language-model segment: B8 H16 n512
+# d64 causal, the position table over every distance (window n - 1), per-head
+# global biases.  R stands for the projected sinusoidal encodings W_R r.
+# ---------------------------------------------------------------------------
+
+@dataclass(frozen=True)
+class XLWorkload:
+    name: str
+    config_id: int
+    description: str
+    batch: int
+    heads: int
+    n: int
+    d: int
+    window: int
+    causal: bool = True
+    dtype: torch.dtype = torch.bfloat16
+    qkv_std: float = 1.0
+    table_std: float = 0.5
+
+    @property
+    def seed(self) -> int:
+        return SEED_BASE + self.config_id
+
+
+XL_WORKLOADS = {
+    "xl": XLWorkload(
+        name="xl", config_id=7,
+        description="Transformer-XL relative logits on a language-model segment: B8 H16 "
+                    "n512 d64 causal, position table over every distance (window 511), "
+                    "per-head u and v",
+        batch=8, heads=16, n=512, d=64, window=511),
+}
+
+
+def make_xl_inputs(w: XLWorkload | str, *, batch=None, heads=None, n=None, seed=None) -> dict:
+    """CPU tensors for an XL workload, drawn in this order: q, k, v [B, H, n, d],
+    the position table R [H, 2W+1, d], u and v biases [H, d] (fp32 draws cast
+    once to the workload dtype)."""
+    if isinstance(w, str):
+        w = XL_WORKLOADS[w]
+    B, H, N = batch or w.batch, heads or w.heads, n or w.n
+    W = min(w.window, N - 1)
+    g = torch.Generator().manual_seed(w.seed if seed is None else seed)
+
+    def normal(shape, std):
+        return torch.randn(shape, generator=g, dtype=torch.float32) * std
+
+    q = normal((B, H, N, w.d), w.qkv_std)
+    k = normal((B, H, N, w.d), w.qkv_std)
+    v = normal((B, H, N, w.d), w.qkv_std)
+    R = normal((H, 2 * W + 1, w.d), w.table_std)
+    u = normal((H, w.d), w.table_std)
+    vb = normal((H, w.d), w.table_std)
+    return {"q": q.to(w.dtype), "k": k.to(w.dtype), "v": v.to(w.dtype), "R": R.to(w.dtype),
+            "u": u.to(w.dtype), "vb": vb.to(w.dtype), "window": W}
