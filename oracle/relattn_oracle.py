@@ -41,6 +41,10 @@ Readings where the pages are silent or garbled (each is listed in the design doc):
   projected relative encodings, given as a table over i - j (clipped to +-W like
   the other tables; W >= n - 1 clips nothing); the attention scale (1/sqrt(d) by
   default) multiplies the whole score, as it does for the Shaw logit;
+* Swin 2-D bias (survey page, "Relative position embeddings", Swin paragraph):
+  the n = M*M tokens of a window are in raster order (token p at row p div M,
+  column p mod M); the table has (2M-1)^2 entries per head, entry
+  (dy + M - 1)(2M - 1) + (dx + M - 1) for the key-minus-query offset (dy, dx);
 * backward (no page prints it): the gradients of a scalar loss sum(dz * z) by
   the chain rule through the forward above; a table shared by all heads takes
   the sum over heads, and hidden pairs give no gradient.  Pinned by central
@@ -72,6 +76,7 @@ __all__ = [
     "t5_backward",
     "offset_bias_backward",
     "xl_attention",
+    "grid_bias_attention",
     "to_f64",
 ]
 
@@ -622,5 +627,34 @@ def xl_attention(q, k, v, R, u, vb, window: int, scale=None, causal: bool = Fals
             term_c = (k[b, h] @ uh)[None, :]
             term_d = np.einsum("d,ijd->ij", vh, Rh)
             e = s * (term_a + term_b + term_c + term_d)
+            z[b, h] = _masked_softmax_rows(e, ok) @ v[b, h]
+    return z
+
+
+def grid_bias_attention(q, k, v, bias, window: int, scale=None, key_lens=None):
+    """Swin-style relative position bias on an M x M window (survey page,
+    "Relative position embeddings": the T5 scalar bias ported to a grid, the
+    table indexed by the flattened 2-D offset):
+
+        A_ij = s q_i.k_j + bias[h', (y_j - y_i + M - 1)(2M - 1) + (x_j - x_i + M - 1)]
+
+    with token p at (y, x) = (p div M, p mod M), n = M * M.  bias: [Hb,
+    (2M-1)^2], Hb in {1, H}.  s defaults to 1/sqrt(d).
+    """
+    q, k, v = to_f64(q), to_f64(k), to_f64(v)
+    bias = to_f64(bias)
+    B, H, n, d = q.shape
+    M = int(window)
+    assert n == M * M
+    s = _default_scale(d, scale)
+    lens = _key_lengths(key_lens, B, n)
+    y, x = np.divmod(np.arange(n), M)
+    entry = (y[None, :] - y[:, None] + M - 1) * (2 * M - 1) + (x[None, :] - x[:, None] + M - 1)
+    z = np.zeros((B, H, n, v.shape[-1]))
+    for b in range(B):
+        ok = visible(n, False, lens[b])
+        for h in range(H):
+            row = bias[0 if bias.shape[0] == 1 else h]
+            e = s * (q[b, h] @ k[b, h].T) + row[entry]
             z[b, h] = _masked_softmax_rows(e, ok) @ v[b, h]
     return z

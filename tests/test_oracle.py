@@ -743,3 +743,56 @@ def test_xl_global_position_bias_is_an_offset_bias():
     bias = np.stack([0.5 * (R[h] @ vb[h])[::-1] for h in range(H)])  # entry W + (j - i)
     want = oracle.offset_bias_attention(q, k, v, bias, W, scale=0.5)
     np.testing.assert_allclose(got, want, rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# Swin 2-D window bias
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("M", [1, 3, 5])
+def test_grid_bias_of_a_1d_offset_function_is_an_offset_bias(M):
+    """A table whose entry (dy, dx) holds f(dy*M + dx) -- a function of the
+    raster offset j - i alone -- is the offset-bias attention with entry f(j -
+    i).  f is asymmetric, so a flipped sign or swapped dy/dx fails."""
+    n = M * M
+    B, H, d = 2, 2, 8
+    q, k, v = (rnd((B, H, n, d), 210 + i) for i in range(3))
+    W = n - 1
+    f = rnd((H, 2 * W + 1), 213)                     # f[h, W + delta]
+    dy, dx = np.meshgrid(np.arange(-(M - 1), M), np.arange(-(M - 1), M), indexing="ij")
+    table = np.stack([f[h][W + (dy * M + dx)].ravel() for h in range(H)])
+    got = oracle.grid_bias_attention(q, k, v, table, M, key_lens=[n, max(1, n - 2)])
+    want = oracle.offset_bias_attention(q, k, v, f, W, key_lens=[n, max(1, n - 2)])
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-12)
+
+
+def test_grid_bias_constant_table_is_textbook_attention():
+    M, B, H, d = 4, 1, 3, 8
+    n = M * M
+    q, k, v = (rnd((B, H, n, d), 220 + i) for i in range(3))
+    table = np.full((1, (2 * M - 1) ** 2), 0.7)
+    got = oracle.grid_bias_attention(q, k, v, table, M, scale=0.5)
+    want = torch.nn.functional.scaled_dot_product_attention(
+        *(torch.tensor(x) for x in (q, k, v)), scale=0.5).numpy()
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-12)
+
+
+def test_grid_bias_entry_layout_probe():
+    """A single large entry at (dy, dx) = (1, -2) with q = 0: each query's
+    weights pile on the key one row down and two columns left when it exists,
+    and are uniform otherwise."""
+    M = 4
+    n = M * M
+    q = np.zeros((1, 1, n, n))
+    k = rnd((1, 1, n, n), 231)
+    v = np.eye(n)[None, None]          # z_i = the weight row of query i
+    table = np.zeros((1, (2 * M - 1) ** 2))
+    table[0, (1 + M - 1) * (2 * M - 1) + (-2 + M - 1)] = 50.0
+    w = oracle.grid_bias_attention(q, k, v, table, M)[0, 0]
+    for i in range(n):
+        yi, xi = divmod(i, M)
+        if yi + 1 < M and xi - 2 >= 0:
+            j = (yi + 1) * M + (xi - 2)
+            assert w[i, j] > 0.999
+        else:
+            np.testing.assert_allclose(w[i], 1.0 / n, atol=1e-12)
