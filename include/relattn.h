@@ -182,6 +182,33 @@ int relattn_validate_xl(const relattn_tensor* q, const relattn_tensor* k, const 
                         int32_t window, float scale, const relattn_mask* mask,
                         const relattn_tensor* out);
 
+/*
+ * relattn_fwd_grid_bias: a relative position bias on an M x M window of
+ * tokens (survey page "Relative position embeddings", Swin paragraph: the T5
+ * scalar bias ported to a grid, the table indexed by the flattened 2-D offset):
+ *
+ *       e_ij = scale * q_i.k_j + bias[h', (y_j - y_i + M - 1)(2M - 1) + (x_j - x_i + M - 1)]
+ *
+ *   with token p at (y, x) = (p / M, p % M), raster order, n = M * M.
+ *   q, k, v, out : as for relattn_fwd; the batch dimension holds the windows.
+ *   bias         : [Hb, (2M-1)^2] F32, Hb in {H, 1}.
+ *   window_side  : M >= 1 (at most 2048).
+ *   scale        : <= 0 picks 1/sqrt(d).
+ *   mask         : key lengths only; a causal mask is INVALID_ARGUMENT.
+ * Errors as for relattn_fwd.  No value term.
+ */
+int relattn_fwd_grid_bias(const relattn_tensor* q, const relattn_tensor* k,
+                          const relattn_tensor* v, const relattn_tensor* bias,
+                          int32_t window_side, float scale, const relattn_mask* mask,
+                          relattn_tensor* out, void* stream);
+
+/* relattn_validate_grid_bias: the argument checks of relattn_fwd_grid_bias,
+ * host only. */
+int relattn_validate_grid_bias(const relattn_tensor* q, const relattn_tensor* k,
+                               const relattn_tensor* v, const relattn_tensor* bias,
+                               int32_t window_side, float scale, const relattn_mask* mask,
+                               const relattn_tensor* out);
+
 /* relattn_validate_offset_bias: the argument checks of relattn_fwd_offset_bias,
  * host only (no HIP call). */
 int relattn_validate_offset_bias(const relattn_tensor* q, const relattn_tensor* k,

@@ -13,7 +13,8 @@ import os
 __all__ = ["fwd", "validate", "fwd_offset_bias", "validate_offset_bias", "decode",
            "decode_workspace_size", "debug_indices", "fwd_lse", "fwd_offset_bias_lse",
            "bwd", "bwd_workspace_size", "bwd_offset_bias", "bwd_offset_bias_workspace_size",
-           "attention", "attention_offset_bias", "fwd_xl", "validate_xl",
+           "attention", "attention_offset_bias", "fwd_xl", "validate_xl", "fwd_grid_bias",
+           "validate_grid_bias",
            "RelattnError", "library_path",
            "OK", "INVALID_ARGUMENT", "UNSUPPORTED", "NO_DEVICE", "LAUNCH_FAILED"]
 
@@ -97,6 +98,10 @@ def _load():
     lib.relattn_fwd_xl.restype = ctypes.c_int
     lib.relattn_validate_xl.argtypes = xl
     lib.relattn_validate_xl.restype = ctypes.c_int
+    lib.relattn_fwd_grid_bias.argtypes = ob + [ctypes.c_void_p]
+    lib.relattn_fwd_grid_bias.restype = ctypes.c_int
+    lib.relattn_validate_grid_bias.argtypes = ob
+    lib.relattn_validate_grid_bias.restype = ctypes.c_int
     lib.relattn_debug_indices.argtypes = [ctypes.c_int32, ctypes.c_int32, P(_T5),
                                           ctypes.c_void_p, ctypes.c_void_p]
     lib.relattn_debug_indices.restype = ctypes.c_int
@@ -634,5 +639,38 @@ def validate_xl(q, k, v, R, u, vb, window, *, causal=False, key_lens=None, scale
     args, keep = _xl_args(q, k, v, R, u, vb, window, causal, key_lens, scale,
                           q if out is None else out)
     st = lib.relattn_validate_xl(*args)
+    del keep
+    return st
+
+
+# ---------------------------------------------------------------------------
+# 2-D window bias (Swin)
+# ---------------------------------------------------------------------------
+
+def fwd_grid_bias(q, k, v, bias, window_side, *, key_lens=None, scale=None, out=None,
+                  stream=None):
+    """Relative position bias on an M x M window (n = M*M raster tokens): bias
+    [H or 1, (2M-1)^2] float32, entry (dy + M - 1)(2M - 1) + (dx + M - 1) for the
+    key-minus-query offset (dy, dx).  Returns ``out``."""
+    import torch
+    lib = _load()
+    _check_lens(key_lens)
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    args, keep = _ob_args(q, k, v, bias, window_side, False, key_lens, scale, out)
+    st = lib.relattn_fwd_grid_bias(*args, ctypes.c_void_p(_stream_of(q, stream)))
+    del keep
+    if st != OK:
+        _raise(lib, st)
+    return out
+
+
+def validate_grid_bias(q, k, v, bias, window_side, *, causal=False, key_lens=None,
+                       scale=None, out=None):
+    """Host-only argument check of ``fwd_grid_bias``; returns the status code."""
+    lib = _load()
+    args, keep = _ob_args(q, k, v, bias, window_side, causal, key_lens, scale,
+                          q if out is None else out)
+    st = lib.relattn_validate_grid_bias(*args)
     del keep
     return st

@@ -198,7 +198,8 @@ int make_plan(const relattn_tensor* q, const relattn_tensor* k, const relattn_te
               const relattn_tensor* t5_bias, const relattn_t5_params* t5, int32_t clip_k,
               float scale, const relattn_mask* mask, const relattn_tensor* out, Plan* plan,
               bool want_t5_table, const relattn_tensor* ob = nullptr, int32_t ob_window = 0,
-              const relattn_tensor* xl_u = nullptr, const relattn_tensor* xl_v = nullptr) {
+              const relattn_tensor* xl_u = nullptr, const relattn_tensor* xl_v = nullptr,
+              int32_t grid_m = 0) {
   int st;
   if ((st = check_view(q, "q", 4, true))) return st;
   if ((st = check_view(k, "k", 4, true))) return st;
@@ -243,9 +244,22 @@ int make_plan(const relattn_tensor* q, const relattn_tensor* k, const relattn_te
     if (!(ob->shape[0] == q->shape[1] || ob->shape[0] == 1))
       return fail(RELATTN_ERR_INVALID_ARGUMENT, "bias: shape[0] must be H (%lld) or 1",
                   (long long)q->shape[1]);
-    if (ob->shape[1] != 2 * (int64_t)ob_window + 1)
+    if (grid_m > 0) {
+      // 2-D window of M x M raster tokens, table by flattened 2-D offset
+      if (grid_m > 2048)
+        return fail(RELATTN_ERR_UNSUPPORTED, "window side M = %d exceeds 2048", grid_m);
+      if (q->shape[2] != (int64_t)grid_m * grid_m)
+        return fail(RELATTN_ERR_INVALID_ARGUMENT, "n (%lld) must be M*M = %lld",
+                    (long long)q->shape[2], (long long)grid_m * grid_m);
+      if (ob->shape[1] != (int64_t)(2 * grid_m - 1) * (2 * grid_m - 1))
+        return fail(RELATTN_ERR_INVALID_ARGUMENT, "bias: shape[1] must be (2M-1)^2 = %lld",
+                    (long long)(2 * grid_m - 1) * (2 * grid_m - 1));
+      if (mask && mask->causal)
+        return fail(RELATTN_ERR_INVALID_ARGUMENT, "a 2-D window bias takes no causal mask");
+    } else if (ob->shape[1] != 2 * (int64_t)ob_window + 1) {
       return fail(RELATTN_ERR_INVALID_ARGUMENT, "bias: shape[1] must be 2*window+1 = %lld",
                   (long long)(2 * (int64_t)ob_window + 1));
+    }
   }
   const bool is_xl = xl_u != nullptr || xl_v != nullptr;
   if (is_xl) {
@@ -312,7 +326,16 @@ int make_plan(const relattn_tensor* q, const relattn_tensor* k, const relattn_te
   }
   p.t5_dist = is_t5 ? (int32_t)std::min<int64_t>(t5->max_distance, n - 1)
                     : (is_ob ? (int32_t)std::min<int64_t>(ob_window, n - 1) : 0);
-  if (is_ob) {
+  if (is_ob && grid_m > 0) {
+    // every offset is in the band (no end value); the (2M-1)^2 entries of the
+    // head's row are loaded and indexed per key from the 2-D offset
+    p.t5_dist = (int32_t)(n - 1);
+    tb.nb = (2 * grid_m - 1) * (2 * grid_m - 1);
+    p.ob = 1;
+    p.ob_lo = 0;
+    p.grid_m = grid_m;
+    p.grid_inv = 1.f / (float)grid_m;
+  } else if (is_ob) {
     // the table's entries for offsets -t5_dist .. t5_dist stand in for the
     // bucket column; offsets beyond them take the end entries, as buckets do
     tb.nb = 2 * p.t5_dist + 1;
@@ -329,7 +352,7 @@ int make_plan(const relattn_tensor* q, const relattn_tensor* k, const relattn_te
   // Among the shapes whose LDS fits, take the one that keeps the most waves
   // of this grid resident per compute unit (two per SIMD for d <= 64, one
   // for d = 128, as the kernels are compiled); ties go to the earlier one.
-  const int nb = is_t5 ? t5->num_buckets : (is_ob ? p.t5.nb : 0);
+  const int nb = is_t5 ? t5->num_buckets : (is_ob ? p.t5.nb : 0);  // entries staged
   auto lds_of = [&](const LaunchCfg& c) {
     return relattn::lds_bytes(P.bf16, P.d, c, P.mode, P.has_wk, P.has_wv, p.nr, p.t5_dist, nb);
   };
@@ -1014,6 +1037,38 @@ int relattn_fwd_xl(const relattn_tensor* q, const relattn_tensor* k, const relat
   Plan plan;
   int st = make_plan(q, k, v, R, nullptr, nullptr, nullptr, window, scale, mask, out, &plan, true,
                      nullptr, 0, u, vb);
+  if (st) return st;
+  if ((st = check_device())) return st;
+  if (plan.empty) return RELATTN_OK;
+  const int e = relattn::launch_fwd(plan.bf16, plan.d, plan.cfg, plan.mode, plan.has_wk,
+                                    plan.has_wv, plan.p, stream);
+  if (e != (int)hipSuccess)
+    return fail(RELATTN_ERR_LAUNCH_FAILED, "launch failed: %s", hipGetErrorString((hipError_t)e));
+  return RELATTN_OK;
+}
+
+int relattn_validate_grid_bias(const relattn_tensor* q, const relattn_tensor* k,
+                               const relattn_tensor* v, const relattn_tensor* bias,
+                               int32_t window_side, float scale, const relattn_mask* mask,
+                               const relattn_tensor* out) {
+  g_last_error.clear();
+  if (!bias) return fail(RELATTN_ERR_INVALID_ARGUMENT, "bias is NULL");
+  if (window_side < 1) return fail(RELATTN_ERR_INVALID_ARGUMENT, "window side M must be >= 1");
+  Plan plan;
+  return make_plan(q, k, v, nullptr, nullptr, nullptr, nullptr, 0, scale, mask, out, &plan, false,
+                   bias, 0, nullptr, nullptr, window_side);
+}
+
+int relattn_fwd_grid_bias(const relattn_tensor* q, const relattn_tensor* k,
+                          const relattn_tensor* v, const relattn_tensor* bias,
+                          int32_t window_side, float scale, const relattn_mask* mask,
+                          relattn_tensor* out, void* stream) {
+  g_last_error.clear();
+  if (!bias) return fail(RELATTN_ERR_INVALID_ARGUMENT, "bias is NULL");
+  if (window_side < 1) return fail(RELATTN_ERR_INVALID_ARGUMENT, "window side M must be >= 1");
+  Plan plan;
+  int st = make_plan(q, k, v, nullptr, nullptr, nullptr, nullptr, 0, scale, mask, out, &plan, true,
+                     bias, 0, nullptr, nullptr, window_side);
   if (st) return st;
   if ((st = check_device())) return st;
   if (plan.empty) return RELATTN_OK;

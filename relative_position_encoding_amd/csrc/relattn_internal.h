@@ -67,6 +67,11 @@ struct FwdParams {
   const void* xl_v;
   int64_t xl_u_sh, xl_v_sh;  // head strides (0 = one vector for all heads)
   int32_t xl;
+  // 2-D window bias (grid_m = M > 0, scalar-bias mode with ob = 1): tokens in
+  // raster order on an M x M grid; t5_bias points at the head's row of a
+  // [Hb, (2M-1)^2] table and t5.nb = (2M-1)^2 entries are loaded.
+  int32_t grid_m;
+  float grid_inv;  // 1 / M
   T5Buckets t5;
 };
 

@@ -419,6 +419,15 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<D, NW, MODE, BF16, BC>()))) vo
     Lhi = relrow[PADL + nwin - 1];
   }
   const int band = T5 ? p.t5_dist : c;  // |j - i| >= band: one end value for the tile
+  // 2-D window bias: this lane's query on the M x M grid
+  int gy = 0, gx = 0;
+  if constexpr (T5) {
+    if (p.grid_m) {
+      const int qc = min(qi, p.n - 1);
+      gy = qc / p.grid_m;
+      gx = qc - gy * p.grid_m;
+    }
+  }
   // offsets whose label holds a single key (1 <= r <= 2c - 1, reachable):
   // their logits are kept for the value term
   const int wb_lo = max(1, p.r_lo) - c, wb_hi = min(2 * c - 1, r_hi) - c;
@@ -523,6 +532,21 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<D, NW, MODE, BF16, BC>()))) vo
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
           for (int i = 0; i < 16; ++i) rv[kb][i] = rel;
+      } else if (T5 && p.grid_m) {
+        // 2-D window: the bias of the key's offset (dy, dx) from the query,
+        // tokens in raster order on an M x M grid; the row of key j is
+        // floor((j + 1/2) / M), exact in fp32 for j < 2^22
+        const int M = p.grid_m;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int j = j0 + hoff + 32 * kb + 16 * (i >> 3) + KSTR * (i & 7);
+            const int yj = (int)(((float)j + 0.5f) * p.grid_inv);
+            const int xj = j - yj * M;
+            const int e = (yj - gy + M - 1) * (2 * M - 1) + (xj - gx + M - 1);
+            rv[kb][i] = kLog2e * TBC[min(max(e, 0), p.t5.nb - 1)];
+          }
       } else {
         // band: every relative logit of the tile, 8 entries per group read
         // from one clamped base (the row padding makes the clamp exact)

@@ -1,0 +1,82 @@
+"""GPU parity of the 2-D window (Swin) relative position bias
+(relattn_fwd_grid_bias, through the C ABI) against the fp64 oracle
+(oracle.grid_bias_attention).  Bars: max-abs 1e-5 (fp32), 2e-2 (bf16)."""
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+TOL = {torch.float32: 1e-5, torch.bfloat16: 2e-2}
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module")
+def ra():
+    import relative_position_encoding_amd as ra
+    if not os.path.exists(ra.library_path):
+        from relative_position_encoding_amd import build
+        build.build()
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return ra
+
+
+@pytest.fixture(autouse=True)
+def _announce(request):
+    sys.stderr.write(f"\n[gpu-case] {request.node.nodeid}\n")
+    sys.stderr.flush()
+    yield
+
+
+def gen(shape, dtype, seed, std=1.0):
+    g = torch.Generator().manual_seed(seed)
+    return (torch.randn(*shape, generator=g) * std).to(dtype)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=str)
+@pytest.mark.parametrize("M", [1, 4, 7, 8, 12])
+@pytest.mark.parametrize("d", [32, 64])
+@pytest.mark.parametrize("shared", [False, True])
+def test_grid_bias_parity(ra, dtype, M, d, shared):
+    n = M * M
+    B, H = 5, 3
+    q, k, v = (gen((B, H, n, d), dtype, 1700 + M + d + i) for i in range(3))
+    bias = gen((1 if shared else H, (2 * M - 1) ** 2), torch.float32, 1703)
+    lens = [n, max(1, n - 3), n, 1, n]
+    lens_d = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    out = ra.fwd_grid_bias(q.to(DEV), k.to(DEV), v.to(DEV), bias.to(DEV), M, key_lens=lens_d)
+    torch.cuda.synchronize()
+    want = oracle.grid_bias_attention(q, k, v, bias, M, key_lens=lens)
+    err = float(np.max(np.abs(out.double().cpu().numpy() - want)))
+    assert err <= TOL[dtype], err
+
+
+def test_grid_bias_full_size_windows(ra):
+    """A stage of a windowed vision transformer: 2048 windows of 7 x 7 tokens,
+    3 heads, d = 32 (bf16), against the oracle on sampled windows."""
+    B, H, M, d = 2048, 3, 7, 32
+    n = M * M
+    q, k, v = (gen((B, H, n, d), torch.bfloat16, 1800 + i) for i in range(3))
+    bias = gen((H, (2 * M - 1) ** 2), torch.float32, 1803)
+    out = ra.fwd_grid_bias(q.to(DEV), k.to(DEV), v.to(DEV), bias.to(DEV), M)
+    torch.cuda.synchronize()
+    out = out.double().cpu().numpy()
+    for b in (0, 777, 2047):
+        want = oracle.grid_bias_attention(q[b:b + 1], k[b:b + 1], v[b:b + 1], bias, M)
+        assert float(np.max(np.abs(out[b:b + 1] - want))) <= TOL[torch.bfloat16]
+
+
+def test_grid_bias_rejects(ra):
+    q = gen((1, 2, 49, 32), torch.bfloat16, 1900).to(DEV)
+    bias = torch.zeros(2, 169, device=DEV)
+    assert ra.validate_grid_bias(q, q, q, bias, 7) == ra.OK
+    assert ra.validate_grid_bias(q, q, q, bias, 6) == ra.INVALID_ARGUMENT       # n != M*M
+    assert ra.validate_grid_bias(q, q, q, bias[:, :100], 7) == ra.INVALID_ARGUMENT
+    assert ra.validate_grid_bias(q, q, q, bias, 7, causal=True) == ra.INVALID_ARGUMENT
+    assert ra.validate_grid_bias(q, q, q, bias, 0) == ra.INVALID_ARGUMENT
