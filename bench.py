@@ -14,8 +14,8 @@ Prints ONE JSON line: TFLOP/s of the headline workload (Transformer-big
 decoder causal self-attention with key and value tables), its fraction of the
 bf16 MFMA peak, the HBM roofline of the kernel, the fp64 oracle timed on the
 host cores, the same figures for the other Transformer shapes, and those of
-incremental decoding, of the offset-bias (ALiBi) arm, of the backward and of
-Transformer-XL relative logits.
+incremental decoding, of the offset-bias (ALiBi) arm, of the backward, of
+Transformer-XL relative logits and of the 2-D window (Swin) bias.
 """
 from __future__ import annotations
 
@@ -543,6 +543,83 @@ def xl_report(ra, steps):
             "input_copies": cold["input_copies"], "steps_per_rep": steps}
 
 
+# ---------------------------------------------------------------------------
+# 2-D window bias (relattn_fwd_grid_bias)
+# ---------------------------------------------------------------------------
+
+def grid_work(w):
+    """(flops, bytes) of one call: 4*d per pair (every key of a window is
+    visible); bytes: q, k, v, out once and the table once."""
+    n = w.side * w.side
+    pairs = w.batch * w.heads * n * n
+    return 4.0 * w.d * pairs, 4.0 * w.batch * w.heads * n * w.d * w.dtype.itemsize + \
+        w.heads * (2 * w.side - 1) ** 2 * 4
+
+
+def time_grid(ra, steps, warmup, hot=False, reps=5):
+    import statistics
+    import torch
+    import workloads
+    lib = ra._load()
+    stream = torch.cuda.Stream()
+    w = workloads.GRID_WORKLOADS["swin"]
+    x = workloads.make_grid_inputs(w)
+    flops, nbytes = grid_work(w)
+    copies = 1 if hot else max(1, min(16, int(2 * LLC_BYTES // nbytes) + 1))
+    calls, keep = [], []
+    for _ in range(copies):
+        g = {k: t.to("cuda").clone() for k, t in x.items()}
+        out = torch.empty_like(g["q"])
+        args, kp = ra._ob_args(g["q"], g["k"], g["v"], g["bias"], w.side, False, None, None, out)
+        calls.append(args + [ctypes.c_void_p(stream.cuda_stream)])
+        keep += [g, out, kp]
+    fn = lib.relattn_fwd_grid_bias
+    times = []
+    with torch.cuda.stream(stream):
+        for s_ in range(warmup):
+            if fn(*calls[s_ % copies]) != 0:
+                raise RuntimeError(ra.last_error())
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        for _ in range(reps):
+            t0.record(stream)
+            for s_ in range(steps):
+                fn(*calls[s_ % copies])
+            t1.record(stream)
+            torch.cuda.synchronize()
+            times.append(t0.elapsed_time(t1) / steps)
+    del keep
+    ms = statistics.median(times)
+    sec = ms * 1e-3
+    return {"ms_per_step": ms, "tflops": flops / sec / 1e12, "hbm_gbs": nbytes / sec / 1e9,
+            "alg_gflop": flops / 1e9, "alg_mbytes": nbytes / 1e6, "input_copies": copies}
+
+
+def grid_report(ra, steps):
+    import workloads
+    w = workloads.GRID_WORKLOADS["swin"]
+    cold = time_grid(ra, steps, 10)
+    hot = time_grid(ra, steps, 10, hot=True)
+    flops, nbytes = cold["alg_gflop"] * 1e9, cold["alg_mbytes"] * 1e6
+    bound = bound_of(flops, nbytes, "bf16")
+    sec = cold["ms_per_step"] * 1e-3
+    if bound == "hbm":
+        ach, peak, unit = nbytes / sec / 1e9, PEAK_HBM_GBS, "GB/s"
+    else:
+        ach, peak, unit = flops / sec / 1e12, PEAK_TFLOPS["bf16"], "TFLOP/s"
+    tr = traffic_per_launch("swin")
+    return {"workload": w.description, "ms_per_step": round(cold["ms_per_step"], 5),
+            "tflops": round(cold["tflops"], 3),
+            "roofline": {"bound": bound, "achieved": round(ach, 2), "peak": peak, "unit": unit,
+                         "frac": round(ach / peak, 4),
+                         "traffic": None if tr is None else round(tr)},
+            "hbm_gbs": round(cold["hbm_gbs"], 1), "hot_ms_per_step": round(hot["ms_per_step"], 5),
+            "alg_gflop_per_step": round(cold["alg_gflop"], 4),
+            "alg_mbytes_per_step": round(cold["alg_mbytes"], 3),
+            "input_copies": cold["input_copies"], "steps_per_rep": steps}
+
+
 def bound_of(flops, nbytes, dt):
     ridge = PEAK_TFLOPS[dt] * 1e12 / (PEAK_HBM_GBS * 1e9)
     return "hbm" if flops / nbytes < ridge else "mfma"
@@ -754,6 +831,8 @@ def main():
                     help="time the backward on --workload only and print its figures")
     ap.add_argument("--xl-only", action="store_true",
                     help="time the Transformer-XL workload only and print its figures")
+    ap.add_argument("--grid-only", action="store_true",
+                    help="time the 2-D window (Swin) workload only and print its figures")
     a = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if a.gpus != 1 or world != 1:
@@ -782,6 +861,9 @@ def main():
         return
     if a.xl_only:
         print(json.dumps({"xl": xl_report(ra, max(50, a.steps // 5))}))
+        return
+    if a.grid_only:
+        print(json.dumps({"grid_bias": grid_report(ra, max(50, a.steps // 5))}))
         return
 
     if gpu is not None and not gpu.get("name"):
@@ -846,6 +928,7 @@ def main():
         line["offset_bias"] = alibi_report(ra, max(50, a.steps // 5))
         line["backward"] = bwd_report(ra, max(50, a.steps // 5))
         line["xl"] = xl_report(ra, max(50, a.steps // 5))
+        line["grid_bias"] = grid_report(ra, max(50, a.steps // 5))
     if not a.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w)
         if not a.only:

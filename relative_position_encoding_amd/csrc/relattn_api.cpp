@@ -376,6 +376,14 @@ int make_plan(const relattn_tensor* q, const relattn_tensor* k, const relattn_te
     if (d > 64) return 4 * ((P.bf16 && kblock == 32) ? 2 : 1);
     return 4 * ((P.bf16 && P.mode != relattn::kRelShaw && (d <= 32 || waves == 4)) ? 3 : 2);
   };
+  // a workgroup whose lower half of waves already covers every query row
+  // would leave the rest idle (short windows, e.g. 7 x 7 = 49 tokens)
+  {
+    std::vector<int> keep;
+    for (int w : waves)
+      if (w == 1 || 32 * (w / 2) < n) keep.push_back(w);
+    waves = keep;
+  }
   std::vector<LaunchCfg> order;
   for (int kb : kblocks)
     for (int w : waves)

@@ -265,3 +265,53 @@ def make_xl_inputs(w: XLWorkload | str, *, batch=None, heads=None, n=None, seed=
     vb = normal((H, w.d), w.table_std)
     return {"q": q.to(w.dtype), "k": k.to(w.dtype), "v": v.to(w.dtype), "R": R.to(w.dtype),
             "u": u.to(w.dtype), "vb": vb.to(w.dtype), "window": W}
+
+
+# ---------------------------------------------------------------------------
+# 2-D window bias (Swin).  The pages give no sizes; a first stage of a windowed
+# vision transformer: 7 x 7 windows (n = 49), 3 heads of d = 32, 2048 windows.
+# ---------------------------------------------------------------------------
+
+@dataclass(frozen=True)
+class GridWorkload:
+    name: str
+    config_id: int
+    description: str
+    batch: int          # windows
+    heads: int
+    side: int           # M: n = M * M tokens per window
+    d: int
+    dtype: torch.dtype = torch.bfloat16
+    qkv_std: float = 1.0
+    table_std: float = 1.0
+
+    @property
+    def seed(self) -> int:
+        return SEED_BASE + self.config_id
+
+
+GRID_WORKLOADS = {
+    "swin": GridWorkload(
+        name="swin", config_id=8,
+        description="2-D window relative position bias: 2048 windows of 7 x 7 tokens, "
+                    "H3 d32, bias table [3, 169]",
+        batch=2048, heads=3, side=7, d=32),
+}
+
+
+def make_grid_inputs(w: GridWorkload | str, *, batch=None, seed=None) -> dict:
+    """CPU tensors for a 2-D window workload, drawn in this order: q, k, v
+    [B, H, M*M, d] and the bias table [H, (2M-1)^2] fp32."""
+    if isinstance(w, str):
+        w = GRID_WORKLOADS[w]
+    B, H, n = batch or w.batch, w.heads, w.side * w.side
+    g = torch.Generator().manual_seed(w.seed if seed is None else seed)
+
+    def normal(shape, std):
+        return torch.randn(shape, generator=g, dtype=torch.float32) * std
+
+    q = normal((B, H, n, w.d), w.qkv_std)
+    k = normal((B, H, n, w.d), w.qkv_std)
+    v = normal((B, H, n, w.d), w.qkv_std)
+    bias = normal((H, (2 * w.side - 1) ** 2), w.table_std)
+    return {"q": q.to(w.dtype), "k": k.to(w.dtype), "v": v.to(w.dtype), "bias": bias}
