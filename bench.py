@@ -456,8 +456,8 @@ def bwd_report(ra, steps, name=HEADLINE):
             "alg_mbytes_per_step": round(cold["alg_mbytes"], 3),
             "workspace_mbytes": round(cold["workspace_mbytes"], 3),
             "input_copies": cold["input_copies"], "steps_per_rep": steps,
-            "kernels": "bwd_q_kernel (dq, label sums, table partials) + bwd_kv_kernel (dk, dv) "
-                       "+ bwd_reduce_kernel (table gradients)"}
+            "kernels": "bwd_q_kernel (dq, label sums, table partials) + bwd_kv_kernel (dk, dv, "
+                       "then the table-gradient sums)"}
 
 
 # ---------------------------------------------------------------------------

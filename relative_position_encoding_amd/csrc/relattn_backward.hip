@@ -28,8 +28,9 @@
 //    dV^T += dZ^T P and dK^T += Q^T dS with MFMA.  The relative rows of each
 //    query tile are recomputed there too (one small MFMA product against the
 //    table rows held in LDS) rather than read back from memory.
-//  * extra workgroups of the dk/dv launch sum the partial table and bias
-//    gradients over batches (and heads, for shared tables) in a fixed order.
+//  * after their own keys, the dk/dv workgroups (under the causal mask the
+//    lightest ones) sum the partial table and bias gradients over batches
+//    (and heads, for shared tables) in a fixed order.
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
@@ -788,7 +789,7 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd<D>()))) void bwd_q_kernel(
 
 // ---------------------------------------------------------------------------
 // Table and bias gradients: sums of the per-tile partials in a fixed order,
-// done by extra workgroups of the dk/dv launch.  Role ids: first one
+// done by the dk/dv workgroups after their keys.  Role ids: first one
 // workgroup per (table head, label) of d w^K, then of d w^V, then the bias
 // gradient's workgroups (nt entries each).
 // ---------------------------------------------------------------------------
@@ -903,13 +904,7 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd<D>()))) void bwd_kv_kernel
   constexpr bool SHAW = MODE == kRelShaw, T5 = MODE == kRelT5;
   constexpr bool ROWS = SHAW && (HAS_WK || HAS_WV);
 
-  // workgroups past the key tiles sum the table and bias gradients (the dq
-  // kernel, launched before on the same stream, has written the partials)
   const int n_kv = p.B * p.H * p.n_ktiles;
-  if ((int)blockIdx.x >= n_kv) {
-    reduce_role(p, (int)blockIdx.x - n_kv, NT);
-    return;
-  }
   const int lid = xcd_remap(blockIdx.x, n_kv);
   const int bh = lid / p.n_ktiles, kt = lid - bh * p.n_ktiles;
   const int b = bh / p.H, h = bh - b * p.H;
@@ -1011,7 +1006,6 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd<D>()))) void bwd_kv_kernel
     wait_vm<0>();
     block_sync();  // tile t (and the tables) landed everywhere; the other stage
                    // and the rows are free
-    if (t + 1 < t_end) issue(t + 1, stg ^ 1);
     const unsigned char* S0 = smem + stg * lay.stage;
     const unsigned char* Qt = S0 + lay.q;
     const unsigned char* Zt = S0 + lay.z;
@@ -1058,6 +1052,8 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd<D>()))) void bwd_kv_kernel
       }
       block_sync();
     }
+    // the next tile, requested once this tile's rows are in place
+    if (t + 1 < t_end) issue(t + 1, stg ^ 1);
     if (wk0 >= p.n || wk0 >= kv_len) continue;  // no live key in this wave
 
 #pragma unroll
@@ -1197,6 +1193,29 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd<D>()))) void bwd_kv_kernel
     store_row_block<T, D>(dkg + (int64_t)kj * p.dk_sn, dk, p.scale, hh, !k_ok);
     store_row_block<T, D>(dvg + (int64_t)kj * p.dv_sn, dv, 1.f, hh, !k_ok);
   }
+
+  // Then the table and bias gradients: sums of the partials the dq kernel
+  // (launched before on the same stream) wrote.  Under the causal mask the
+  // last key tiles of a head see the fewest queries and finish first; they
+  // take every reduction role.  Otherwise all workgroups share them.
+  const int n_roles = reduce_role_count(p, NT);
+  if (n_roles > 0) {
+    const int BH = p.B * p.H;
+    int first, stride;
+    if (p.causal && p.n_ktiles > 1) {
+      const int light = (p.n_ktiles + 1) / 2;  // key tiles kt >= n_ktiles - light
+      if (kt < p.n_ktiles - light) return;
+      first = (kt - (p.n_ktiles - light)) * BH + bh;
+      stride = light * BH;
+    } else {
+      first = lid;
+      stride = n_kv;
+    }
+    for (int role = first; role < n_roles; role += stride) {
+      block_sync();  // the LDS the role uses is free
+      reduce_role(p, role, NT);
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1311,7 +1330,7 @@ static int launch_kv(const BwdParams& p, hipStream_t s) {
                                              lay.total);
     if (e != hipSuccess) return (int)e;
   }
-  const dim3 grid((unsigned)((int64_t)p.B * p.H * p.n_ktiles + reduce_role_count(p, 64 * NW)));
+  const dim3 grid((unsigned)((int64_t)p.B * p.H * p.n_ktiles));
   hipLaunchKernelGGL(kern, grid, dim3(64 * NW), (size_t)max(lay.total, 64 * NW * 4), s, p);
   return (int)hipGetLastError();
 }
