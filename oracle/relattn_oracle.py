@@ -45,6 +45,13 @@ Readings where the pages are silent or garbled (each is listed in the design doc):
   the n = M*M tokens of a window are in raster order (token p at row p div M,
   column p mod M); the table has (2M-1)^2 entries per head, entry
   (dy + M - 1)(2M - 1) + (dx + M - 1) for the key-minus-query offset (dy, dx);
+* per-pair edge labels ("Self-Attention with Relative Position Representations"
+  summary page, the labeled-graph reading of section 3.1: any pairwise label
+  may index the relation; survey page, "Placement in the taxonomy": a scalar
+  bias table indexed per pair): labels are given per batch as an n x n integer
+  matrix E[b, i, j] for the edge from query i to key j, shared by the heads; the
+  bias table is [Hb, NL] with Hb in {1, H}; the attention scale (1/sqrt(d) by
+  default) multiplies the content logit only, as for the offset bias;
 * backward (no page prints it): the gradients of a scalar loss sum(dz * z) by
   the chain rule through the forward above; a table shared by all heads takes
   the sum over heads, and hidden pairs give no gradient.  Pinned by central
@@ -77,6 +84,7 @@ __all__ = [
     "offset_bias_backward",
     "xl_attention",
     "grid_bias_attention",
+    "edge_label_attention",
     "to_f64",
 ]
 
@@ -656,5 +664,40 @@ def grid_bias_attention(q, k, v, bias, window: int, scale=None, key_lens=None):
         for h in range(H):
             row = bias[0 if bias.shape[0] == 1 else h]
             e = s * (q[b, h] @ k[b, h].T) + row[entry]
+            z[b, h] = _masked_softmax_rows(e, ok) @ v[b, h]
+    return z
+
+
+# ---------------------------------------------------------------------------
+# Per-pair edge labels ("Self-Attention with Relative Position
+# Representations" summary page: the input as a labeled, directed, fully
+# connected graph whose edge labels need not be positions; survey page,
+# "Relative position embeddings", section "Placement in the taxonomy": the
+# scalar bias by a label of the pair)
+# ---------------------------------------------------------------------------
+
+def edge_label_attention(q, k, v, labels, bias, scale=None, causal: bool = False,
+                         key_lens=None):
+    """A_ij = scale * q_i.k_j + bias[h', E[b, i, j]], softmax, z_i = sum_j alpha_ij v_j.
+
+    labels: [B, n, n] integers in [0, NL), the label of the edge from query i
+    to key j, the same for every head of a batch entry.  bias: [Hb, NL] with
+    Hb in {1, H} (Hb == 1: one row for every head).  scale defaults to
+    1/sqrt(d).
+    """
+    q, k, v = to_f64(q), to_f64(k), to_f64(v)
+    bias = to_f64(bias)
+    E = np.asarray(labels).astype(np.int64)
+    B, H, n, d = q.shape
+    assert E.shape == (B, n, n)
+    assert E.min(initial=0) >= 0 and E.max(initial=0) < bias.shape[1]
+    s = _default_scale(d, scale)
+    lens = _key_lengths(key_lens, B, n)
+    z = np.zeros((B, H, n, v.shape[-1]))
+    for b in range(B):
+        ok = visible(n, causal, lens[b])
+        for h in range(H):
+            row = bias[0 if bias.shape[0] == 1 else h]
+            e = s * (q[b, h] @ k[b, h].T) + row[E[b]]
             z[b, h] = _masked_softmax_rows(e, ok) @ v[b, h]
     return z

@@ -796,3 +796,87 @@ def test_grid_bias_entry_layout_probe():
             assert w[i, j] > 0.999
         else:
             np.testing.assert_allclose(w[i], 1.0 / n, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# scalar bias by a per-pair edge label (summary page of "Self-Attention with
+# Relative Position Representations": any pairwise label may index the
+# relation; survey page, "Placement in the taxonomy")
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("bidir", [True, False])
+@pytest.mark.parametrize("causal,lens", [(False, None), (True, None), (False, [9, 30])])
+def test_edge_labels_from_t5_buckets_equal_t5(bidir, causal, lens):
+    """Labels E[i, j] = beta(j - i) with the T5 table as the bias rows give the
+    T5 attention (scale 1).  Bidirectional buckets are not symmetric in the
+    offset, so a transposed label matrix fails."""
+    B, H, n, d = 2, 3, 30, 8
+    q, k, v = rnd((B, H, n, d), 300), rnd((B, H, n, d), 301), rnd((B, H, n, d), 302)
+    t5b = rnd((32, H), 303)
+    E = np.array([[oracle.t5_bucket(j - i, 32, 16, bidir) for j in range(n)] for i in range(n)])
+    z = oracle.edge_label_attention(q, k, v, np.stack([E] * B), t5b.T, scale=1.0,
+                                    causal=causal, key_lens=lens)
+    want = oracle.t5_attention(q, k, v, t5b, 32, 16, bidir, causal=causal, key_lens=lens)
+    np.testing.assert_allclose(z, want, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("shared", [False, True])
+def test_edge_labels_from_clipped_offsets_equal_offset_bias(shared):
+    """Labels clip(j - i, W) + W reproduce the offset bias with the same table."""
+    B, H, n, d, W = 2, 3, 17, 8, 4
+    q, k, v = rnd((B, H, n, d), 310), rnd((B, H, n, d), 311), rnd((B, H, n, d), 312)
+    table = rnd((1 if shared else H, 2 * W + 1), 313)
+    E = oracle.relative_labels(n, W) + W
+    z = oracle.edge_label_attention(q, k, v, np.stack([E] * B), table, causal=True,
+                                    key_lens=[n, 11])
+    want = oracle.offset_bias_attention(q, k, v, table, W, causal=True, key_lens=[n, 11])
+    np.testing.assert_allclose(z, want, rtol=0, atol=1e-12)
+
+
+def test_edge_labels_constant_bias_is_textbook():
+    """One bias value for every label cancels in the softmax: textbook scaled
+    attention (library routine), whatever the labels."""
+    B, H, n, d = 2, 2, 13, 8
+    q, k, v = rnd((B, H, n, d), 320), rnd((B, H, n, d), 321), rnd((B, H, n, d), 322)
+    E = np.random.default_rng(323).integers(0, 5, (B, n, n))
+    z = oracle.edge_label_attention(q, k, v, E, np.full((1, 5), -1.3))
+    ok = np.ones((n, n), dtype=bool)
+    np.testing.assert_allclose(z, sdpa(q, k, v, ok, 1 / math.sqrt(d)), rtol=0, atol=1e-12)
+
+
+def test_edge_labels_probe_per_batch():
+    """A large bias on label 3 with q = 0 and v = I: query i of batch b spreads
+    its weight evenly over exactly the keys j with E[b, i, j] == 3 (uniformly
+    over all keys when there is none).  The two batch entries hold different
+    labels, so reading another entry's matrix or its transpose fails."""
+    B, n = 2, 12
+    rng = np.random.default_rng(330)
+    E = rng.integers(0, 6, (B, n, n))
+    E[0, 5, :] = 0                      # a row without label 3
+    q = np.zeros((B, 1, n, n))
+    k = rnd((B, 1, n, n), 331)
+    v = np.broadcast_to(np.eye(n), (B, 1, n, n)).copy()
+    bias = np.zeros((1, 6))
+    bias[0, 3] = 60.0
+    w = oracle.edge_label_attention(q, k, v, E, bias)
+    for b in range(B):
+        for i in range(n):
+            hit = E[b, i] == 3
+            want = hit / hit.sum() if hit.any() else np.full(n, 1.0 / n)
+            np.testing.assert_allclose(w[b, 0, i], want, rtol=0, atol=1e-12)
+
+
+def test_edge_labels_two_tokens_closed_form():
+    """n = 2: each row is a two-way softmax, alpha_i1 = 1 / (1 + exp(e_i0 - e_i1)),
+    with e_ij = s q_i k_j + b[E_ij], written out per element."""
+    rng = np.random.default_rng(340)
+    q, k, v = (rng.standard_normal((1, 1, 2, 3)) for _ in range(3))
+    E = np.array([[[2, 0], [1, 2]]])
+    bias = np.array([[0.4, -1.1, 0.9]])
+    s = 0.7
+    z = oracle.edge_label_attention(q, k, v, E, bias, scale=s)[0, 0]
+    for i in range(2):
+        e = [s * float(np.dot(q[0, 0, i], k[0, 0, j])) + bias[0, E[0, i, j]] for j in range(2)]
+        a1 = 1.0 / (1.0 + math.exp(e[0] - e[1]))
+        np.testing.assert_allclose(z[i], (1 - a1) * v[0, 0, 0] + a1 * v[0, 0, 1], rtol=0,
+                                   atol=1e-14)
