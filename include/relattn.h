@@ -57,7 +57,8 @@ typedef enum {
   RELATTN_ERR_LAUNCH_FAILED = -4     /* HIP reported an error at launch        */
 } relattn_status;
 
-typedef enum { RELATTN_F32 = 0, RELATTN_BF16 = 1 } relattn_dtype;
+/* RELATTN_U8 is taken only by the label matrix of relattn_fwd_edge_bias. */
+typedef enum { RELATTN_F32 = 0, RELATTN_BF16 = 1, RELATTN_U8 = 2 } relattn_dtype;
 
 /* A strided tensor view.  `stride` counts ELEMENTS, not bytes.  The last
  * dimension must be contiguous (stride 1).  Dimensions past `ndim` are ignored. */
@@ -208,6 +209,42 @@ int relattn_validate_grid_bias(const relattn_tensor* q, const relattn_tensor* k,
                                const relattn_tensor* v, const relattn_tensor* bias,
                                int32_t window_side, float scale, const relattn_mask* mask,
                                const relattn_tensor* out);
+
+/*
+ * relattn_fwd_edge_bias: a scalar bias indexed by a label given per (query,
+ * key) pair ("Self-Attention with Relative Position Representations", summary
+ * page: the input as a labeled, directed, fully connected graph whose edge
+ * labels need not be positions; survey page "Relative position embeddings",
+ * section "Placement in the taxonomy": the bias looked up per pair):
+ *
+ *       e_ij = scale * q_i.k_j + bias[h', labels[b, i, j]]
+ *
+ *   q, k, v, out : as for relattn_fwd.  No value term.
+ *   labels       : [B, n, n] U8 device matrix, the label of the edge from query
+ *                  i to key j, shared by the heads of a batch entry.  Rows are
+ *                  read in whole 16-byte chunks: the data pointer is 16-byte
+ *                  aligned, stride[0] and stride[1] are multiples of 16 (stride[0]
+ *                  may be 0: one matrix for all batch entries), stride[1] >= n
+ *                  rounded up to 16, stride[2] = 1, and every row is readable up to
+ *                  that rounded length (bytes past column n - 1 are read, never
+ *                  used).  A label >= NL is read as NL - 1.
+ *   bias         : [Hb, NL] F32, Hb in {H, 1}, 1 <= NL <= 256.
+ *   scale        : multiplies q.k only; <= 0 picks 1/sqrt(d).
+ *   mask, stream : as for relattn_fwd.
+ * Errors as for relattn_fwd; a layout of labels outside the rules above is
+ * UNSUPPORTED.
+ */
+int relattn_fwd_edge_bias(const relattn_tensor* q, const relattn_tensor* k,
+                          const relattn_tensor* v, const relattn_tensor* labels,
+                          const relattn_tensor* bias, float scale, const relattn_mask* mask,
+                          relattn_tensor* out, void* stream);
+
+/* relattn_validate_edge_bias: the argument checks of relattn_fwd_edge_bias,
+ * host only. */
+int relattn_validate_edge_bias(const relattn_tensor* q, const relattn_tensor* k,
+                               const relattn_tensor* v, const relattn_tensor* labels,
+                               const relattn_tensor* bias, float scale,
+                               const relattn_mask* mask, const relattn_tensor* out);
 
 /* relattn_validate_offset_bias: the argument checks of relattn_fwd_offset_bias,
  * host only (no HIP call). */

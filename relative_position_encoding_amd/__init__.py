@@ -14,12 +14,12 @@ __all__ = ["fwd", "validate", "fwd_offset_bias", "validate_offset_bias", "decode
            "decode_workspace_size", "debug_indices", "fwd_lse", "fwd_offset_bias_lse",
            "bwd", "bwd_workspace_size", "bwd_offset_bias", "bwd_offset_bias_workspace_size",
            "attention", "attention_offset_bias", "fwd_xl", "validate_xl", "fwd_grid_bias",
-           "validate_grid_bias",
+           "validate_grid_bias", "fwd_edge_bias", "validate_edge_bias", "edge_label_buffer",
            "RelattnError", "library_path",
            "OK", "INVALID_ARGUMENT", "UNSUPPORTED", "NO_DEVICE", "LAUNCH_FAILED"]
 
 OK, INVALID_ARGUMENT, UNSUPPORTED, NO_DEVICE, LAUNCH_FAILED = 0, -1, -2, -3, -4
-_F32, _BF16 = 0, 1
+_F32, _BF16, _U8 = 0, 1, 2
 
 library_path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "librelattn.so")
 
@@ -102,6 +102,11 @@ def _load():
     lib.relattn_fwd_grid_bias.restype = ctypes.c_int
     lib.relattn_validate_grid_bias.argtypes = ob
     lib.relattn_validate_grid_bias.restype = ctypes.c_int
+    edge = [P(_Tensor)] * 5 + [ctypes.c_float, P(_Mask), P(_Tensor)]
+    lib.relattn_fwd_edge_bias.argtypes = edge + [ctypes.c_void_p]
+    lib.relattn_fwd_edge_bias.restype = ctypes.c_int
+    lib.relattn_validate_edge_bias.argtypes = edge
+    lib.relattn_validate_edge_bias.restype = ctypes.c_int
     lib.relattn_debug_indices.argtypes = [ctypes.c_int32, ctypes.c_int32, P(_T5),
                                           ctypes.c_void_p, ctypes.c_void_p]
     lib.relattn_debug_indices.restype = ctypes.c_int
@@ -121,6 +126,8 @@ def _dtype_code(t):
         return _F32
     if t.dtype == torch.bfloat16:
         return _BF16
+    if t.dtype == torch.uint8:
+        return _U8
     return 99  # rejected by the library
 
 
@@ -672,5 +679,65 @@ def validate_grid_bias(q, k, v, bias, window_side, *, causal=False, key_lens=Non
     args, keep = _ob_args(q, k, v, bias, window_side, causal, key_lens, scale,
                           q if out is None else out)
     st = lib.relattn_validate_grid_bias(*args)
+    del keep
+    return st
+
+
+def edge_label_buffer(B, n, device=None):
+    """A zeroed uint8 [B, n, n] view whose rows are n rounded up to 16 bytes
+    apart, the layout ``fwd_edge_bias`` reads its labels in."""
+    import torch
+    n16 = (n + 15) // 16 * 16
+    return torch.zeros((B, n, n16), dtype=torch.uint8, device=device)[:, :, :n]
+
+
+def _edge_args(q, k, v, labels, bias, causal, key_lens, scale, out):
+    import torch
+    n = labels.shape[1] if labels.dim() == 3 else 0
+    if labels.dtype == torch.uint8 and labels.dim() == 3 and labels.numel() > 0:
+        # every row must be readable to n rounded up to 16 bytes
+        n16 = (n + 15) // 16 * 16
+        last = (labels.storage_offset() + (labels.shape[0] - 1) * labels.stride(0)
+                + (n - 1) * labels.stride(1) + n16)
+        if last > labels.untyped_storage().nbytes():
+            raise RelattnError(INVALID_ARGUMENT,
+                               "relattn: labels rows must be readable to n rounded up to 16 "
+                               "bytes (see edge_label_buffer)")
+    views = [_view(x) for x in (q, k, v, labels, bias)]
+    mask = None
+    if causal or key_lens is not None:
+        mask = _Mask(1 if causal else 0, key_lens.data_ptr() if key_lens is not None else None)
+    outv = _view(out)
+    args = [_ref(x) for x in views] + [float(0.0 if scale is None else scale), _ref(mask),
+                                        _ref(outv)]
+    return args, views + [mask, outv]
+
+
+def fwd_edge_bias(q, k, v, labels, bias, *, causal=False, key_lens=None, scale=None, out=None,
+                  stream=None):
+    """Attention with a scalar bias by a per-pair label: labels uint8 [B, n, n]
+    (rows padded to 16 bytes, e.g. from ``edge_label_buffer``), bias float32
+    [H or 1, NL]; e_ij = scale * q_i.k_j + bias[h, labels[b, i, j]].  Returns
+    ``out``."""
+    import torch
+    lib = _load()
+    _check_lens(key_lens)
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    args, keep = _edge_args(q, k, v, labels, bias, causal, key_lens, scale, out)
+    st = lib.relattn_fwd_edge_bias(*args, ctypes.c_void_p(_stream_of(q, stream)))
+    del keep
+    if st != OK:
+        _raise(lib, st)
+    return out
+
+
+def validate_edge_bias(q, k, v, labels, bias, *, causal=False, key_lens=None, scale=None,
+                       out=None):
+    """Host-only argument check of ``fwd_edge_bias``; returns the status code."""
+    lib = _load()
+    args, keep = _edge_args(q, k, v, labels, bias, causal, key_lens, scale,
+                            q if out is None else out)
+    st = lib.relattn_validate_edge_bias(*args)
     del keep
     return st

@@ -199,7 +199,7 @@ int make_plan(const relattn_tensor* q, const relattn_tensor* k, const relattn_te
               float scale, const relattn_mask* mask, const relattn_tensor* out, Plan* plan,
               bool want_t5_table, const relattn_tensor* ob = nullptr, int32_t ob_window = 0,
               const relattn_tensor* xl_u = nullptr, const relattn_tensor* xl_v = nullptr,
-              int32_t grid_m = 0) {
+              int32_t grid_m = 0, const relattn_tensor* labels = nullptr) {
   int st;
   if ((st = check_view(q, "q", 4, true))) return st;
   if ((st = check_view(k, "k", 4, true))) return st;
@@ -225,7 +225,10 @@ int make_plan(const relattn_tensor* q, const relattn_tensor* k, const relattn_te
     return fail(RELATTN_ERR_INVALID_ARGUMENT, "scale must be finite");
 
   const bool is_t5 = t5_bias != nullptr || t5 != nullptr;
-  const bool is_ob = ob != nullptr;  // scalar bias by clipped offset
+  const bool is_ob = ob != nullptr;  // scalar bias by clipped offset, 2-D offset or label
+  const bool is_lab = labels != nullptr;  // ... by a per-pair label
+  if (is_lab && (!is_ob || grid_m > 0))
+    return fail(RELATTN_ERR_INVALID_ARGUMENT, "edge labels take a bias table by label");
   if ((t5_bias == nullptr) != (t5 == nullptr))
     return fail(RELATTN_ERR_INVALID_ARGUMENT, "t5_bias and t5 params must be given together");
   if (is_t5 && (wK || wV))
@@ -256,6 +259,34 @@ int make_plan(const relattn_tensor* q, const relattn_tensor* k, const relattn_te
                     (long long)(2 * grid_m - 1) * (2 * grid_m - 1));
       if (mask && mask->causal)
         return fail(RELATTN_ERR_INVALID_ARGUMENT, "a 2-D window bias takes no causal mask");
+    } else if (is_lab) {
+      // [B, n, n] uint8 labels, rows read in whole 16-byte chunks
+      if (ob->shape[1] < 1 || ob->shape[1] > 256)
+        return fail(RELATTN_ERR_INVALID_ARGUMENT, "bias: shape[1] (labels) must be in [1, 256]");
+      if (labels->ndim != 3)
+        return fail(RELATTN_ERR_INVALID_ARGUMENT, "labels must have 3 dims, got %d", labels->ndim);
+      if (labels->dtype != RELATTN_U8)
+        return fail(RELATTN_ERR_INVALID_ARGUMENT, "labels must be U8");
+      if (labels->shape[0] != q->shape[0] || labels->shape[1] != q->shape[2] ||
+          labels->shape[2] != q->shape[2])
+        return fail(RELATTN_ERR_INVALID_ARGUMENT, "labels must be [B, n, n]");
+      for (int i = 0; i < 3; ++i)
+        if (labels->stride[i] < 0)
+          return fail(RELATTN_ERR_INVALID_ARGUMENT, "labels stride[%d] < 0", i);
+      if (numel(labels) > 0) {
+        const int64_t n16 = (q->shape[2] + 15) / 16 * 16;
+        if (!labels->data) return fail(RELATTN_ERR_INVALID_ARGUMENT, "labels data is NULL");
+        if (labels->stride[2] != 1)
+          return fail(RELATTN_ERR_UNSUPPORTED, "labels: innermost dimension must be contiguous");
+        if (!aligned16(labels->data))
+          return fail(RELATTN_ERR_UNSUPPORTED, "labels: data pointer is not 16-byte aligned");
+        if (labels->stride[1] % 16 != 0 || labels->stride[0] % 16 != 0)
+          return fail(RELATTN_ERR_UNSUPPORTED, "labels: strides must be multiples of 16 bytes");
+        if (labels->stride[1] < n16)
+          return fail(RELATTN_ERR_UNSUPPORTED,
+                      "labels: row stride %lld is below n rounded up to 16 (%lld)",
+                      (long long)labels->stride[1], (long long)n16);
+      }
     } else if (ob->shape[1] != 2 * (int64_t)ob_window + 1) {
       return fail(RELATTN_ERR_INVALID_ARGUMENT, "bias: shape[1] must be 2*window+1 = %lld",
                   (long long)(2 * (int64_t)ob_window + 1));
@@ -297,8 +328,9 @@ int make_plan(const relattn_tensor* q, const relattn_tensor* k, const relattn_te
   Plan& P = *plan;
   P.bf16 = q->dtype == RELATTN_BF16;
   P.d = (int)d;
-  P.mode = (is_t5 || is_ob) ? relattn::kRelT5
-                             : ((wK || wV) ? relattn::kRelShaw : relattn::kRelNone);
+  P.mode = is_lab ? relattn::kRelLabel
+                  : (is_t5 || is_ob) ? relattn::kRelT5
+                                     : ((wK || wV) ? relattn::kRelShaw : relattn::kRelNone);
   P.has_wk = wK != nullptr;
   P.has_wv = wV != nullptr;
   P.empty = (B == 0 || H == 0 || n == 0);
@@ -325,8 +357,16 @@ int make_plan(const relattn_tensor* q, const relattn_tensor* k, const relattn_te
     p.nr = 1;
   }
   p.t5_dist = is_t5 ? (int32_t)std::min<int64_t>(t5->max_distance, n - 1)
-                    : (is_ob ? (int32_t)std::min<int64_t>(ob_window, n - 1) : 0);
-  if (is_ob && grid_m > 0) {
+                    : ((is_ob && !is_lab) ? (int32_t)std::min<int64_t>(ob_window, n - 1) : 0);
+  if (is_lab) {
+    // the head's row of NL entries is loaded and indexed by each pair's label
+    tb.nb = (int32_t)ob->shape[1];
+    p.ob = 1;
+    p.ob_lo = 0;
+    p.lab = static_cast<const uint8_t*>(labels->data);
+    p.lab_sb = labels->stride[0];
+    p.lab_sn = labels->stride[1];
+  } else if (is_ob && grid_m > 0) {
     // every offset is in the band (no end value); the (2M-1)^2 entries of the
     // head's row are loaded and indexed per key from the 2-D offset
     p.t5_dist = (int32_t)(n - 1);
@@ -1077,6 +1117,38 @@ int relattn_fwd_grid_bias(const relattn_tensor* q, const relattn_tensor* k,
   Plan plan;
   int st = make_plan(q, k, v, nullptr, nullptr, nullptr, nullptr, 0, scale, mask, out, &plan, true,
                      bias, 0, nullptr, nullptr, window_side);
+  if (st) return st;
+  if ((st = check_device())) return st;
+  if (plan.empty) return RELATTN_OK;
+  const int e = relattn::launch_fwd(plan.bf16, plan.d, plan.cfg, plan.mode, plan.has_wk,
+                                    plan.has_wv, plan.p, stream);
+  if (e != (int)hipSuccess)
+    return fail(RELATTN_ERR_LAUNCH_FAILED, "launch failed: %s", hipGetErrorString((hipError_t)e));
+  return RELATTN_OK;
+}
+
+int relattn_validate_edge_bias(const relattn_tensor* q, const relattn_tensor* k,
+                               const relattn_tensor* v, const relattn_tensor* labels,
+                               const relattn_tensor* bias, float scale, const relattn_mask* mask,
+                               const relattn_tensor* out) {
+  g_last_error.clear();
+  if (!labels) return fail(RELATTN_ERR_INVALID_ARGUMENT, "labels is NULL");
+  if (!bias) return fail(RELATTN_ERR_INVALID_ARGUMENT, "bias is NULL");
+  Plan plan;
+  return make_plan(q, k, v, nullptr, nullptr, nullptr, nullptr, 0, scale, mask, out, &plan, false,
+                   bias, 0, nullptr, nullptr, 0, labels);
+}
+
+int relattn_fwd_edge_bias(const relattn_tensor* q, const relattn_tensor* k,
+                          const relattn_tensor* v, const relattn_tensor* labels,
+                          const relattn_tensor* bias, float scale, const relattn_mask* mask,
+                          relattn_tensor* out, void* stream) {
+  g_last_error.clear();
+  if (!labels) return fail(RELATTN_ERR_INVALID_ARGUMENT, "labels is NULL");
+  if (!bias) return fail(RELATTN_ERR_INVALID_ARGUMENT, "bias is NULL");
+  Plan plan;
+  int st = make_plan(q, k, v, nullptr, nullptr, nullptr, nullptr, 0, scale, mask, out, &plan, true,
+                     bias, 0, nullptr, nullptr, 0, labels);
   if (st) return st;
   if ((st = check_device())) return st;
   if (plan.empty) return RELATTN_OK;

@@ -72,10 +72,18 @@ struct FwdParams {
   // [Hb, (2M-1)^2] table and t5.nb = (2M-1)^2 entries are loaded.
   int32_t grid_m;
   float grid_inv;  // 1 / M
+  // Edge-label bias (label mode): lab[b * lab_sb + i * lab_sn + j] is the
+  // label of the edge from query i to key j; rows are read in whole 16-byte
+  // chunks (lab_sn a multiple of 16, at least n rounded up to 16); t5_bias
+  // points at the head's row of a [Hb, NL] table and t5.nb = NL.
+  const uint8_t* lab;
+  int64_t lab_sb, lab_sn;
   T5Buckets t5;
 };
 
-enum RelMode { kRelNone = 0, kRelShaw = 1, kRelT5 = 2 };
+// kRelT5: scalar bias by T5 bucket, clipped offset or 2-D offset; kRelLabel:
+// scalar bias by a per-pair label read from memory.
+enum RelMode { kRelNone = 0, kRelShaw = 1, kRelT5 = 2, kRelLabel = 3 };
 
 // Where the w^V rows wait for the epilogue: their own LDS region (loaded in
 // the prologue), the first K/V ring stage the loop frees, or the free ring

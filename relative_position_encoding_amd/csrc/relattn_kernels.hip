@@ -39,6 +39,11 @@
 // row per query and turned into weights in the epilogue once m_i is final.
 // The +c tail is a running sum (empty under the causal mask) and the -c tail
 // is what the row sum leaves.  The epilogue adds S W^V with MFMA.
+//
+// Edge labels (label mode): the scalar bias is indexed by a label given per
+// (query, key) pair instead of a function of the offset.  Each wave's 32 rows
+// of a tile's label matrix travel with the K/V stage by LDS-DMA, and every
+// logit gathers its bias from the head's row of the table in LDS.
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
@@ -88,7 +93,7 @@ struct Geo {
 };
 
 struct Layout {
-  int wk, wv, le, tbc, tb, qs, total;  // byte offsets / total bytes
+  int wk, wv, le, tbc, tb, qs, lab, total;  // byte offsets / total bytes
   int wk_rows, wv_rows, lrs;       // tile rows, relative-row stride (floats)
   int wk_chunk;                    // w^K rows staged at a time (multiple of 32)
   int wv_chunk;                    // w^V rows staged at a time (multiple of 16)
@@ -109,7 +114,7 @@ __host__ __device__ inline Layout make_layout(int mode, bool has_wk, bool has_wv
     off += (bytes + 15) & ~15;
     return at;
   };
-  const bool shaw = mode == kRelShaw, t5 = mode == kRelT5;
+  const bool shaw = mode == kRelShaw, t5 = mode == kRelT5, lab = mode == kRelLabel;
   L.wk_rows = dma_rows((nr + 31) & ~31, G::ROWB);
   L.wv_rows = dma_rows((nr + 15) & ~15, G::ROWB);
   // relative row: padding, nr labels, padding.  Dword LDS accesses are
@@ -146,8 +151,10 @@ __host__ __device__ inline Layout make_layout(int mode, bool has_wk, bool has_wv
     L.le = off;
     L.qs = q_bytes <= G::STAGEB ? (nstage - 1) * G::STAGEB : take(q_bytes);
   }
-  L.tbc = t5 ? take(((t5_nb + 63) & ~63) * 4) : off;
+  L.tbc = (t5 || lab) ? take(((t5_nb + 63) & ~63) * 4) : off;
   L.tb = t5 ? take((2 * t5_dist + 1 + G::PADL + G::PADU) * 4) : off;
+  // label mode: one BR x BC byte tile of labels per ring stage
+  L.lab = lab ? take(nstage * G::BR * BC) : off;
   L.total = off;
   return L;
 }
@@ -175,7 +182,13 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<D, NW, MODE, BF16, BC>()))) vo
   constexpr int KSTR = G::KSTR, SPAN = G::SPAN, PADL = G::PADL, PADU = G::PADU;
   constexpr bool SHAW = (MODE == kRelShaw);
   constexpr bool T5 = (MODE == kRelT5);
-  constexpr bool GATHER = (SHAW && HAS_WK) || T5;  // a gathered relative logit
+  constexpr bool LAB = (MODE == kRelLabel);
+  constexpr bool GATHER = (SHAW && HAS_WK) || T5 || LAB;  // a gathered relative logit
+  // label mode: each wave loads its 32 rows of a tile's labels (32 x BC bytes)
+  // with the stage, in 1 KB instructions
+  constexpr int LLPW = LAB ? BC / 32 : 0;
+  constexpr int SLPW = LPW + LLPW;  // DMA instructions per wave per stage
+  constexpr int LABB = G::BR * BC;  // label bytes per stage
 
   // One field of each 64-byte line of the parameter block (and the grid size),
   // so that all of them are requested together behind one wait instead of
@@ -227,6 +240,7 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<D, NW, MODE, BF16, BC>()))) vo
   const T* kg = reinterpret_cast<const T*>(p.k) + b * p.k_sb + h * p.k_sh;
   const T* vg = reinterpret_cast<const T*>(p.v) + b * p.v_sb + h * p.v_sh;
   T* og = reinterpret_cast<T*>(p.o) + b * p.o_sb + h * p.o_sh;
+  const uint8_t* labg = LAB ? p.lab + b * p.lab_sb : nullptr;
 
   // ---- LDS-DMA, oldest first: the Q tile, the relative tables, then the
   // first K/V stages.  (Q goes through LDS too: the compiler cannot count the
@@ -270,9 +284,10 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<D, NW, MODE, BF16, BC>()))) vo
       n_after_wk += dma_tile<ROWB, NW>(smem_lds + lay.wv, wvh, p.wv_sr, p.r_lo, r_hi,
                                        lay.wv_rows, wave, lane);
   }
-  if constexpr (T5) {
+  if constexpr (T5 || LAB) {
     // bias column of this head (or the window of its row of a table by
-    // offset), 4 bytes per lane, issued by wave 0
+    // offset, or its row of a table by label), 4 bytes per lane, issued by
+    // wave 0
     if (wave == 0) {
       for (int I = 0; I * 64 < p.t5.nb; ++I) {
         const int bucket = min(I * 64 + lane, p.t5.nb - 1) + p.ob_lo;
@@ -308,15 +323,32 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<D, NW, MODE, BF16, BC>()))) vo
       dma_stage<ROWB, NW, BC>(smem_lds + stage * G::STAGEB, kg, p.k_sn, vg, p.v_sn, tile * BC,
                               kv_last, wave, lane);
     }
+    if constexpr (LAB) {
+      // this wave's rows of the tile's labels, stored chunk-major: the 16-byte
+      // chunk c (keys 16c ..) of row r at slot 32 c + r, so that the 32 rows
+      // of one chunk are 512 contiguous bytes.  Rows past n read row n - 1;
+      // chunks past the last one holding a key read that chunk.
+      unsigned char RELATTN_LDS* dst = smem_lds + lay.lab + stage * LABB + wave * (32 * BC);
+      const int col_max = ((p.n - 1) >> 4) << 4;
+#pragma unroll
+      for (int I = 0; I < LLPW; ++I) {
+        const int slot = I * 64 + lane;
+        const int row = min(wq0 + (slot & 31), p.n - 1);
+        const int col = min(tile * BC + 16 * (slot >> 5), col_max);
+        __builtin_amdgcn_global_load_lds(
+            (const RELATTN_GLOBAL void*)(labg + (int64_t)row * p.lab_sn + col),
+            (RELATTN_LDS void*)(dst + I * 1024), 16, 0, 0);
+      }
+    }
     compiler_fence();
   };
   const int n_pre = min(nstage - 1, ntiles);
   for (int s = 0; s < n_pre; ++s) issue_stage(s, s);
-  n_after_wk += n_pre * LPW;
+  n_after_wk += n_pre * SLPW;
   n_after_q += n_after_wk;
 
   // ---- Q as the B operand of S^T = K Q^T, in registers for the whole kernel
-  wait_vm_dyn(SHAW && HAS_WK ? n_after_wk : (T5 ? n_pre * LPW : n_after_q));
+  wait_vm_dyn(SHAW && HAS_WK ? n_after_wk : ((T5 || LAB) ? n_pre * SLPW : n_after_q));
   block_sync();  // every wave's share of the Q tile (and of the tables) landed
   Op qop[NKS];
 #pragma unroll
@@ -406,6 +438,11 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<D, NW, MODE, BF16, BC>()))) vo
     }
     block_sync();
   }
+  if constexpr (LAB) {
+    // the head's bias row in log2 units, gathered by label in the loop
+    for (int x = tid; x < p.t5.nb; x += NT) TBC[x] *= kLog2e;
+    block_sync();
+  }
 
   // window of offsets delta = j - i covered by the relative row, and the
   // relative logit of its two ends (used for tiles entirely outside the band)
@@ -414,7 +451,7 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<D, NW, MODE, BF16, BC>()))) vo
   const int gtop = nwin + PADL + PADU - SPAN;     // highest gather base
   const float* relrow = T5 ? TB : myLE;
   float Llo = 0.f, Lhi = 0.f;
-  if constexpr (GATHER) {
+  if constexpr (GATHER && !LAB) {
     Llo = relrow[PADL];
     Lhi = relrow[PADL + nwin - 1];
   }
@@ -454,8 +491,8 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<D, NW, MODE, BF16, BC>()))) vo
     {
       // the steady state (one stage still in flight) and the drained state
       // take one compare each instead of the general switch's branch tree
-      const int pending = min(nstage - 2, ntiles - 1 - t) * LPW + wv_cnt;
-      if (pending == LPW) wait_vm<LPW>();
+      const int pending = min(nstage - 2, ntiles - 1 - t) * SLPW + wv_cnt;
+      if (pending == SLPW) wait_vm<SLPW>();
       else if (pending == 0) wait_vm<0>();
       else wait_vm_dyn(pending);
     }
@@ -502,9 +539,11 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<D, NW, MODE, BF16, BC>()))) vo
     const bool all_lo = dmax <= -band, all_hi = dmin >= band;  // wave-uniform
     const bool off_band = (SHAW || T5) && (all_lo || all_hi);
     // Per-element masking: key-length cuts, and causal cuts unless the
-    // gathered relative logits already carry them (-inf past offset 0).
+    // gathered relative logits already carry them (-inf past offset 0; not
+    // so for labels).
     const bool causal_cut = p.causal && j0 + BC - 1 > wq0;
-    const bool need_mask = (j0 + BC > kv_len) || (causal_cut && !(GATHER && !off_band));
+    const bool need_mask =
+        (j0 + BC > kv_len) || (causal_cut && (LAB || !(GATHER && !off_band)));
     // visible iff its key offset within the lane's keys is <= lim
     const int lim = min(kv_len - 1 - j0 - hoff, p.causal ? -kofs : 0x3fffffff);
 
@@ -532,6 +571,31 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<D, NW, MODE, BF16, BC>()))) vo
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
           for (int i = 0; i < 16; ++i) rv[kb][i] = rel;
+      } else if constexpr (LAB) {
+        // edge labels: the bias of each key's label, from the 16-byte label
+        // chunk of the lane's row that holds 16 consecutive keys of the tile
+        const unsigned char* labt = smem + lay.lab + st_cur * LABB + wave * (32 * BC);
+        const int nbm = p.t5.nb - 1;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int g = 0; g < 2; ++g) {
+            const uint4 w4 = *reinterpret_cast<const uint4*>(labt + ((2 * kb + g) * 32 + ql) * 16);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              uint32_t byte;
+              if constexpr (BF16) {
+                // keys 8 hh + e of the chunk
+                const uint32_t dw = (e < 4) ? (hh ? w4.z : w4.x) : (hh ? w4.w : w4.y);
+                byte = (dw >> (8 * (e & 3))) & 0xffu;
+              } else {
+                // keys hh + 2 e of the chunk
+                const uint32_t dw = (e < 2) ? w4.x : (e < 4) ? w4.y : (e < 6) ? w4.z : w4.w;
+                byte = (dw >> (8 * (hh + 2 * (e & 1)))) & 0xffu;
+              }
+              rv[kb][8 * g + e] = TBC[min((int)byte, nbm)];
+            }
+          }
       } else if (T5 && p.grid_m) {
         // 2-D window: the bias of the key's offset (dy, dx) from the query,
         // tokens in raster order on an M x M grid; the row of key j is
@@ -876,6 +940,7 @@ template <int D, int NW, int BC, bool BF16>
 static int launch_mode(RelMode mode, bool has_wk, bool has_wv, const FwdParams& p,
                        void* stream) {
   if (mode == kRelT5) return launch_t<D, NW, BC, BF16, kRelT5, false, false>(p, stream);
+  if (mode == kRelLabel) return launch_t<D, NW, BC, BF16, kRelLabel, false, false>(p, stream);
   if (mode == kRelShaw) {
     if (has_wk && has_wv) return launch_t<D, NW, BC, BF16, kRelShaw, true, true>(p, stream);
     if (has_wk) return launch_t<D, NW, BC, BF16, kRelShaw, true, false>(p, stream);

@@ -306,3 +306,47 @@ def test_bwd_offset_bias_window_checks(ra):
     small = T(2, 11, dtype=torch.float32)
     assert ra.bwd_offset_bias_workspace_size(q, k, v, small, 5, out=out, dout=dout,
                                              lse=lse) > 0
+
+
+def test_edge_bias_validation(ra):
+    """Label layout and bias-table checks of relattn_validate_edge_bias."""
+    B, H, n = 2, 3, 40
+    q, k, v = qkv(B, H, n)
+    bias = T(H, 7, dtype=torch.float32)
+    lab = ra.edge_label_buffer(B, n)
+    assert lab.stride(1) == 48
+    assert ra.validate_edge_bias(q, k, v, lab, bias) == ra.OK
+    assert ra.validate_edge_bias(q, k, v, lab, T(1, 7, dtype=torch.float32)) == ra.OK
+    kl = torch.zeros(B, dtype=torch.int32)
+    assert ra.validate_edge_bias(q, k, v, lab, bias, causal=True, key_lens=kl) == ra.OK
+    assert ra.validate_edge_bias(q, k, v, lab, T(H, 256, dtype=torch.float32)) == ra.OK
+    # one label matrix for every batch entry (batch stride 0)
+    shared = lab[:1].expand(B, n, n)
+    assert ra.validate_edge_bias(q, k, v, shared, bias) == ra.OK
+    # rows closer than n rounded up to 16, or not a multiple of 16 bytes apart
+    tight = torch.zeros(B * n * n + 16, dtype=torch.uint8).as_strided((B, n, n), (n * n, n, 1))
+    assert ra.validate_edge_bias(q, k, v, tight, bias) == ra.UNSUPPORTED
+    buf = torch.zeros(B * n * 64, dtype=torch.uint8)
+    assert ra.validate_edge_bias(q, k, v, buf.as_strided((B, n, n), (n * 32, 32, 1)),
+                                 bias) == ra.UNSUPPORTED
+    # a contiguous matrix whose n is a multiple of 16 needs no padding
+    q48, k48, v48 = qkv(B, H, 48)
+    assert ra.validate_edge_bias(q48, k48, v48, torch.zeros(B, 48, 48, dtype=torch.uint8),
+                                 bias) == ra.OK
+    # wrong label dtype or shape, bad bias tables
+    assert ra.validate_edge_bias(q, k, v, lab.to(torch.int32), bias) == ra.INVALID_ARGUMENT
+    assert ra.validate_edge_bias(q, k, v, ra.edge_label_buffer(B, n + 1)[:, :n, :n],
+                                 bias) == ra.OK
+    assert ra.validate_edge_bias(q, k, v, ra.edge_label_buffer(B + 1, n)[:, :, :],
+                                 bias) == ra.INVALID_ARGUMENT
+    assert ra.validate_edge_bias(q, k, v, lab, T(H, 0, dtype=torch.float32)) == ra.INVALID_ARGUMENT
+    assert ra.validate_edge_bias(q, k, v, lab, T(H, 257, dtype=torch.float32)) == ra.INVALID_ARGUMENT
+    assert ra.validate_edge_bias(q, k, v, lab, T(H, 7)) == ra.INVALID_ARGUMENT   # bf16 bias
+    assert ra.validate_edge_bias(q, k, v, lab, T(2, 7, dtype=torch.float32)) == ra.INVALID_ARGUMENT
+    # the last row must be readable to n rounded up to 16 (checked by the binding)
+    short = torch.zeros(B * n * 48 - 8, dtype=torch.uint8).as_strided((B, n, n), (n * 48, 48, 1))
+    with pytest.raises(ra.RelattnError):
+        ra.validate_edge_bias(q, k, v, short, bias)
+    # empty problems validate
+    q0, k0, v0 = qkv(0, H, n)
+    assert ra.validate_edge_bias(q0, k0, v0, ra.edge_label_buffer(0, n), bias) == ra.OK

@@ -1,0 +1,184 @@
+"""GPU parity of the scalar bias by per-pair edge label (relattn_fwd_edge_bias,
+through the C ABI) against the fp64 oracle (oracle.edge_label_attention).
+Bars: max-abs 1e-5 (fp32), 2e-2 (bf16), as for the other forward arms.  Labels
+that reproduce the offset and T5 arms must give those arms' outputs bit for bit
+(the same bias value enters the same logit arithmetic)."""
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+TOL = {torch.float32: 1e-5, torch.bfloat16: 2e-2}
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module")
+def ra():
+    import relative_position_encoding_amd as ra
+    if not os.path.exists(ra.library_path):
+        from relative_position_encoding_amd import build
+        build.build()
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return ra
+
+
+@pytest.fixture(autouse=True)
+def _announce(request):
+    sys.stderr.write(f"\n[gpu-case] {request.node.nodeid}\n")
+    sys.stderr.flush()
+    yield
+
+
+def gen(shape, dtype, seed, std=1.0):
+    g = torch.Generator().manual_seed(seed)
+    return (torch.randn(*shape, generator=g) * std).to(dtype)
+
+
+def labels_of(ra, E):
+    """Device copy of an integer [B, n, n] label matrix in the padded layout."""
+    B, n, _ = E.shape
+    lab = ra.edge_label_buffer(B, n, DEV)
+    lab.copy_(torch.as_tensor(E).to(torch.uint8))
+    return lab
+
+
+def run(ra, q, k, v, E, bias, **kw):
+    lens = kw.pop("key_lens", None)
+    lens_d = None if lens is None else torch.tensor(lens, dtype=torch.int32, device=DEV)
+    out = ra.fwd_edge_bias(q.to(DEV), k.to(DEV), v.to(DEV), labels_of(ra, E), bias.to(DEV),
+                           key_lens=lens_d, **kw)
+    torch.cuda.synchronize()
+    return out
+
+
+MASKS = [(False, None), (True, None), (False, "lens"), (True, "lens")]
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=str)
+@pytest.mark.parametrize("n", [1, 37, 100, 256])
+@pytest.mark.parametrize("d", [32, 64])
+@pytest.mark.parametrize("mask", range(len(MASKS)))
+def test_edge_bias_parity(ra, dtype, n, d, mask):
+    causal, lens_kind = MASKS[mask]
+    B, H, NL = 3, 2, 24
+    q, k, v = (gen((B, H, n, d), dtype, 2000 + n + d + i) for i in range(3))
+    bias = gen((H, NL), torch.float32, 2003, std=2.0)
+    E = np.random.default_rng(2004 + n).integers(0, NL, (B, n, n))
+    lens = [n, max(1, n // 2), max(1, n - 5)] if lens_kind else None
+    out = run(ra, q, k, v, E, bias, causal=causal, key_lens=lens)
+    want = oracle.edge_label_attention(q, k, v, E, bias, causal=causal, key_lens=lens)
+    err = float(np.max(np.abs(out.double().cpu().numpy() - want)))
+    assert err <= TOL[dtype], err
+
+
+@pytest.mark.parametrize("dtype,d", [(torch.bfloat16, 16), (torch.bfloat16, 128),
+                                     (torch.float32, 16), (torch.float32, 128)], ids=str)
+@pytest.mark.parametrize("NL,shared", [(1, False), (7, True), (256, False)])
+def test_edge_bias_head_sizes_and_vocabularies(ra, dtype, d, NL, shared):
+    B, H, n = 2, 3, 75
+    q, k, v = (gen((B, H, n, d), dtype, 2100 + d + NL + i) for i in range(3))
+    bias = gen((1 if shared else H, NL), torch.float32, 2103 + NL, std=2.0)
+    E = np.random.default_rng(2104 + NL).integers(0, NL, (B, n, n))
+    out = run(ra, q, k, v, E, bias, causal=True, key_lens=[n, 40])
+    want = oracle.edge_label_attention(q, k, v, E, bias, causal=True, key_lens=[n, 40])
+    assert float(np.max(np.abs(out.double().cpu().numpy() - want))) <= TOL[dtype]
+
+
+def test_edge_bias_labels_past_the_table_read_the_last_entry(ra):
+    """A label >= NL is read as NL - 1."""
+    B, H, n, d, NL = 2, 2, 50, 64, 5
+    q, k, v = (gen((B, H, n, d), torch.bfloat16, 2200 + i) for i in range(3))
+    bias = gen((H, NL), torch.float32, 2203, std=2.0)
+    E = np.random.default_rng(2204).integers(0, 256, (B, n, n))
+    out = run(ra, q, k, v, E, bias)
+    want = oracle.edge_label_attention(q, k, v, np.minimum(E, NL - 1), bias)
+    assert float(np.max(np.abs(out.double().cpu().numpy() - want))) <= TOL[torch.bfloat16]
+
+
+def test_edge_bias_one_matrix_for_the_batch(ra):
+    """Batch stride 0: every batch entry reads the same label matrix."""
+    B, H, n, d, NL = 3, 2, 70, 32, 9
+    q, k, v = (gen((B, H, n, d), torch.bfloat16, 2300 + i) for i in range(3))
+    bias = gen((H, NL), torch.float32, 2303, std=2.0)
+    E1 = np.random.default_rng(2304).integers(0, NL, (1, n, n))
+    lab = labels_of(ra, E1).expand(B, n, n)
+    out = ra.fwd_edge_bias(q.to(DEV), k.to(DEV), v.to(DEV), lab, bias.to(DEV))
+    torch.cuda.synchronize()
+    want = oracle.edge_label_attention(q, k, v, np.repeat(E1, B, axis=0), bias)
+    assert float(np.max(np.abs(out.double().cpu().numpy() - want))) <= TOL[torch.bfloat16]
+
+
+def test_edge_bias_unpadded_rows_when_n_is_a_multiple_of_16(ra):
+    B, H, n, d, NL = 2, 2, 64, 64, 12
+    q, k, v = (gen((B, H, n, d), torch.float32, 2400 + i) for i in range(3))
+    bias = gen((H, NL), torch.float32, 2403, std=2.0)
+    E = np.random.default_rng(2404).integers(0, NL, (B, n, n))
+    lab = torch.as_tensor(E).to(torch.uint8).contiguous().to(DEV)
+    out = ra.fwd_edge_bias(q.to(DEV), k.to(DEV), v.to(DEV), lab, bias.to(DEV), causal=True)
+    torch.cuda.synchronize()
+    want = oracle.edge_label_attention(q, k, v, E, bias, causal=True)
+    assert float(np.max(np.abs(out.double().cpu().numpy() - want))) <= TOL[torch.float32]
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=str)
+@pytest.mark.parametrize("causal", [False, True])
+def test_edge_labels_of_clipped_offsets_equal_the_offset_bias_bitwise(ra, dtype, causal):
+    B, H, n, d, W = 2, 4, 200, 64, 16
+    q, k, v = (gen((B, H, n, d), dtype, 2500 + i) for i in range(3))
+    table = gen((H, 2 * W + 1), torch.float32, 2503, std=2.0)
+    E = np.stack([oracle.relative_labels(n, W) + W] * B)
+    lens = torch.tensor([n, 130], dtype=torch.int32, device=DEV)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    got = ra.fwd_edge_bias(qd, kd, vd, labels_of(ra, E), table.to(DEV), causal=causal,
+                           key_lens=lens)
+    want = ra.fwd_offset_bias(qd, kd, vd, table.to(DEV), W, causal=causal, key_lens=lens)
+    torch.cuda.synchronize()
+    assert torch.equal(got, want)
+
+
+@pytest.mark.parametrize("bidir", [True, False])
+def test_edge_labels_of_t5_buckets_equal_the_t5_arm_bitwise(ra, bidir):
+    B, H, n, d = 2, 3, 150, 64
+    q, k, v = (gen((B, H, n, d), torch.bfloat16, 2600 + i) for i in range(3))
+    t5b = gen((32, H), torch.float32, 2603, std=2.0)
+    E = np.array([[oracle.t5_bucket(j - i, 32, 128, bidir) for j in range(n)] for i in range(n)])
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    got = ra.fwd_edge_bias(qd, kd, vd, labels_of(ra, np.stack([E] * B)),
+                           t5b.t().contiguous().to(DEV), scale=1.0)
+    want = ra.fwd(qd, kd, vd, t5_bias=t5b.to(DEV), num_buckets=32, max_distance=128,
+                  bidirectional=bidir)
+    torch.cuda.synchronize()
+    assert torch.equal(got, want)
+
+
+def test_edge_bias_full_size(ra):
+    """The benchmark shape (B16 H16 n256 d64, 64 labels uniform per pair), in the
+    launch configuration the benchmark times, against the oracle on sampled
+    (batch, head) slices."""
+    w = workloads.EDGE_WORKLOADS["edge"]
+    x = workloads.make_edge_inputs(w)
+    out = run(ra, x["q"], x["k"], x["v"], x["labels"].numpy(), x["bias"])
+    out = out.double().cpu().numpy()
+    E = x["labels"].numpy()
+    for b, h in ((0, 0), (7, 11), (15, 15)):
+        want = oracle.edge_label_attention(x["q"][b:b + 1, h:h + 1], x["k"][b:b + 1, h:h + 1],
+                                           x["v"][b:b + 1, h:h + 1], E[b:b + 1],
+                                           x["bias"][h:h + 1])
+        err = float(np.max(np.abs(out[b:b + 1, h:h + 1] - want)))
+        assert err <= TOL[torch.bfloat16], (b, h, err)
+
+
+def test_edge_bias_empty_problems(ra):
+    bias = torch.zeros(2, 4, device=DEV)
+    for B, n in ((0, 16), (2, 0)):
+        q = torch.zeros(B, 2, n, 32, dtype=torch.bfloat16, device=DEV)
+        out = ra.fwd_edge_bias(q, q, q, ra.edge_label_buffer(B, n, DEV), bias)
+        assert out.shape == q.shape

@@ -315,3 +315,60 @@ def make_grid_inputs(w: GridWorkload | str, *, batch=None, seed=None) -> dict:
     v = normal((B, H, n, w.d), w.qkv_std)
     bias = normal((H, (2 * w.side - 1) ** 2), w.table_std)
     return {"q": q.to(w.dtype), "k": k.to(w.dtype), "v": v.to(w.dtype), "bias": bias}
+
+
+# ---------------------------------------------------------------------------
+# Per-pair edge labels.  The pages give no sizes; the Transformer-big attention
+# shape (16 heads of d = 64) over 256-token inputs whose every (query, key)
+# edge carries one of 64 labels (a relation vocabulary the size of a set of
+# dependency or discourse types), drawn uniformly per pair.
+# ---------------------------------------------------------------------------
+
+@dataclass(frozen=True)
+class EdgeWorkload:
+    name: str
+    config_id: int
+    description: str
+    batch: int
+    heads: int
+    n: int
+    d: int
+    labels: int         # NL: label vocabulary
+    causal: bool = False
+    dtype: torch.dtype = torch.bfloat16
+    qkv_std: float = 1.0
+    table_std: float = 1.0
+
+    @property
+    def seed(self) -> int:
+        return SEED_BASE + self.config_id
+
+
+EDGE_WORKLOADS = {
+    "edge": EdgeWorkload(
+        name="edge", config_id=9,
+        description="per-pair edge labels: B16 H16 n256 d64, 64 labels uniform per pair, "
+                    "bias table [16, 64], no mask",
+        batch=16, heads=16, n=256, d=64, labels=64),
+}
+
+
+def make_edge_inputs(w: EdgeWorkload | str, *, batch=None, n=None, seed=None) -> dict:
+    """CPU tensors for an edge-label workload, drawn in this order: q, k, v
+    [B, H, n, d], the bias table [H, NL] fp32 and the labels [B, n, n] (int64,
+    uniform in [0, NL))."""
+    if isinstance(w, str):
+        w = EDGE_WORKLOADS[w]
+    B, H, n = batch or w.batch, w.heads, n or w.n
+    g = torch.Generator().manual_seed(w.seed if seed is None else seed)
+
+    def normal(shape, std):
+        return torch.randn(shape, generator=g, dtype=torch.float32) * std
+
+    q = normal((B, H, n, w.d), w.qkv_std)
+    k = normal((B, H, n, w.d), w.qkv_std)
+    v = normal((B, H, n, w.d), w.qkv_std)
+    bias = normal((H, w.labels), w.table_std)
+    labels = torch.randint(0, w.labels, (B, n, n), generator=g)
+    return {"q": q.to(w.dtype), "k": k.to(w.dtype), "v": v.to(w.dtype), "bias": bias,
+            "labels": labels}
