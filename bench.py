@@ -124,7 +124,7 @@ def time_gpu(ra, w, steps, warmup, hot=False, reps=1):
         for s in range(warmup):
             st = fwd(*calls[s % copies])
             if st != 0:
-                raise RuntimeError(ra.last_error())
+                raise RuntimeError(lib.relattn_last_error().decode())
         torch.cuda.synchronize()
         t0 = torch.cuda.Event(enable_timing=True)
         t1 = torch.cuda.Event(enable_timing=True)
@@ -212,7 +212,7 @@ def time_decode(ra, w, steps, warmup, hot=False, reps=1):
     with torch.cuda.stream(stream):
         for s_ in range(warmup):
             if fn(*calls[s_ % copies]) != 0:
-                raise RuntimeError(ra.last_error())
+                raise RuntimeError(lib.relattn_last_error().decode())
         torch.cuda.synchronize()
         t0 = torch.cuda.Event(enable_timing=True)
         t1 = torch.cuda.Event(enable_timing=True)
@@ -298,7 +298,7 @@ def time_alibi(ra, steps, warmup, hot=False, reps=5):
     with torch.cuda.stream(stream):
         for s_ in range(warmup):
             if fn(*calls[s_ % copies]) != 0:
-                raise RuntimeError(ra.last_error())
+                raise RuntimeError(lib.relattn_last_error().decode())
         torch.cuda.synchronize()
         t0 = torch.cuda.Event(enable_timing=True)
         t1 = torch.cuda.Event(enable_timing=True)
@@ -399,7 +399,7 @@ def time_bwd(ra, w, steps, warmup, hot=False, reps=5):
                                 t5.get("bidirectional", True), None, out, dz, lse, grads)
         need = ctypes.c_size_t(0)
         if lib.relattn_bwd_workspace_size(*args, ctypes.byref(need)) != 0:
-            raise RuntimeError(ra.last_error())
+            raise RuntimeError(lib.relattn_last_error().decode())
         ws = torch.empty(max(need.value, 1), dtype=torch.uint8, device="cuda")
         calls.append(args + [ctypes.c_void_p(ws.data_ptr()), ctypes.c_size_t(need.value),
                              ctypes.c_void_p(stream.cuda_stream)])
@@ -410,7 +410,7 @@ def time_bwd(ra, w, steps, warmup, hot=False, reps=5):
     with torch.cuda.stream(stream):
         for s_ in range(warmup):
             if fn(*calls[s_ % copies]) != 0:
-                raise RuntimeError(ra.last_error())
+                raise RuntimeError(lib.relattn_last_error().decode())
         torch.cuda.synchronize()
         t0 = torch.cuda.Event(enable_timing=True)
         t1 = torch.cuda.Event(enable_timing=True)
@@ -500,7 +500,7 @@ def time_xl(ra, steps, warmup, hot=False, reps=5):
     with torch.cuda.stream(stream):
         for s_ in range(warmup):
             if fn(*calls[s_ % copies]) != 0:
-                raise RuntimeError(ra.last_error())
+                raise RuntimeError(lib.relattn_last_error().decode())
         torch.cuda.synchronize()
         t0 = torch.cuda.Event(enable_timing=True)
         t1 = torch.cuda.Event(enable_timing=True)
@@ -578,7 +578,7 @@ def time_grid(ra, steps, warmup, hot=False, reps=5):
     with torch.cuda.stream(stream):
         for s_ in range(warmup):
             if fn(*calls[s_ % copies]) != 0:
-                raise RuntimeError(ra.last_error())
+                raise RuntimeError(lib.relattn_last_error().decode())
         torch.cuda.synchronize()
         t0 = torch.cuda.Event(enable_timing=True)
         t1 = torch.cuda.Event(enable_timing=True)
@@ -609,6 +609,86 @@ def grid_report(ra, steps):
     else:
         ach, peak, unit = flops / sec / 1e12, PEAK_TFLOPS["bf16"], "TFLOP/s"
     tr = traffic_per_launch("swin")
+    return {"workload": w.description, "ms_per_step": round(cold["ms_per_step"], 5),
+            "tflops": round(cold["tflops"], 3),
+            "roofline": {"bound": bound, "achieved": round(ach, 2), "peak": peak, "unit": unit,
+                         "frac": round(ach / peak, 4),
+                         "traffic": None if tr is None else round(tr)},
+            "hbm_gbs": round(cold["hbm_gbs"], 1), "hot_ms_per_step": round(hot["ms_per_step"], 5),
+            "alg_gflop_per_step": round(cold["alg_gflop"], 4),
+            "alg_mbytes_per_step": round(cold["alg_mbytes"], 3),
+            "input_copies": cold["input_copies"], "steps_per_rep": steps}
+
+
+# ---------------------------------------------------------------------------
+# Scalar bias by per-pair edge label (relattn_fwd_edge_bias)
+# ---------------------------------------------------------------------------
+
+def edge_work(w):
+    """(flops, bytes) of one call: 4*d per pair (no mask: every key visible);
+    bytes: q, k, v, out once, the table once and the label matrix once (one
+    byte per pair of a batch entry, shared by its heads)."""
+    pairs = w.batch * w.heads * w.n * w.n
+    return 4.0 * w.d * pairs, 4.0 * w.batch * w.heads * w.n * w.d * w.dtype.itemsize + \
+        w.heads * w.labels * 4 + w.batch * w.n * w.n
+
+
+def time_edge(ra, steps, warmup, hot=False, reps=5):
+    import statistics
+    import torch
+    import workloads
+    lib = ra._load()
+    stream = torch.cuda.Stream()
+    w = workloads.EDGE_WORKLOADS["edge"]
+    x = workloads.make_edge_inputs(w)
+    flops, nbytes = edge_work(w)
+    copies = 1 if hot else max(1, min(16, int(2 * LLC_BYTES // nbytes) + 1))
+    calls, keep = [], []
+    for _ in range(copies):
+        g = {k: t.to("cuda").clone() for k, t in x.items() if k != "labels"}
+        lab = ra.edge_label_buffer(w.batch, w.n, "cuda")
+        lab.copy_(x["labels"].to(torch.uint8))
+        out = torch.empty_like(g["q"])
+        args, kp = ra._edge_args(g["q"], g["k"], g["v"], lab, g["bias"], w.causal, None, None,
+                                 out)
+        calls.append(args + [ctypes.c_void_p(stream.cuda_stream)])
+        keep += [g, lab, out, kp]
+    fn = lib.relattn_fwd_edge_bias
+    times = []
+    with torch.cuda.stream(stream):
+        for s_ in range(warmup):
+            if fn(*calls[s_ % copies]) != 0:
+                raise RuntimeError(lib.relattn_last_error().decode())
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        for _ in range(reps):
+            t0.record(stream)
+            for s_ in range(steps):
+                fn(*calls[s_ % copies])
+            t1.record(stream)
+            torch.cuda.synchronize()
+            times.append(t0.elapsed_time(t1) / steps)
+    del keep
+    ms = statistics.median(times)
+    sec = ms * 1e-3
+    return {"ms_per_step": ms, "tflops": flops / sec / 1e12, "hbm_gbs": nbytes / sec / 1e9,
+            "alg_gflop": flops / 1e9, "alg_mbytes": nbytes / 1e6, "input_copies": copies}
+
+
+def edge_report(ra, steps):
+    import workloads
+    w = workloads.EDGE_WORKLOADS["edge"]
+    cold = time_edge(ra, steps, 10)
+    hot = time_edge(ra, steps, 10, hot=True)
+    flops, nbytes = cold["alg_gflop"] * 1e9, cold["alg_mbytes"] * 1e6
+    bound = bound_of(flops, nbytes, "bf16")
+    sec = cold["ms_per_step"] * 1e-3
+    if bound == "hbm":
+        ach, peak, unit = nbytes / sec / 1e9, PEAK_HBM_GBS, "GB/s"
+    else:
+        ach, peak, unit = flops / sec / 1e12, PEAK_TFLOPS["bf16"], "TFLOP/s"
+    tr = traffic_per_launch("edge")
     return {"workload": w.description, "ms_per_step": round(cold["ms_per_step"], 5),
             "tflops": round(cold["tflops"], 3),
             "roofline": {"bound": bound, "achieved": round(ach, 2), "peak": peak, "unit": unit,
@@ -833,6 +913,8 @@ def main():
                     help="time the Transformer-XL workload only and print its figures")
     ap.add_argument("--grid-only", action="store_true",
                     help="time the 2-D window (Swin) workload only and print its figures")
+    ap.add_argument("--edge-only", action="store_true",
+                    help="time the edge-label workload only and print its figures")
     a = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if a.gpus != 1 or world != 1:
@@ -864,6 +946,9 @@ def main():
         return
     if a.grid_only:
         print(json.dumps({"grid_bias": grid_report(ra, max(50, a.steps // 5))}))
+        return
+    if a.edge_only:
+        print(json.dumps({"edge_bias": edge_report(ra, max(50, a.steps // 5))}))
         return
 
     if gpu is not None and not gpu.get("name"):
@@ -929,6 +1014,7 @@ def main():
         line["backward"] = bwd_report(ra, max(50, a.steps // 5))
         line["xl"] = xl_report(ra, max(50, a.steps // 5))
         line["grid_bias"] = grid_report(ra, max(50, a.steps // 5))
+        line["edge_bias"] = edge_report(ra, max(50, a.steps // 5))
     if not a.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w)
         if not a.only:
