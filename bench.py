@@ -320,8 +320,19 @@ def alibi_report(ra, steps):
     cold = time_alibi(ra, steps, 10)
     hot = time_alibi(ra, steps, 10, hot=True)
     ceil = ceiling_tflops(cold["alg_gflop"] * 1e9, cold["alg_mbytes"] * 1e6, "bf16")
+    flops, nbytes = cold["alg_gflop"] * 1e9, cold["alg_mbytes"] * 1e6
+    bound = bound_of(flops, nbytes, "bf16")
+    sec = cold["ms_per_step"] * 1e-3
+    if bound == "hbm":
+        ach, peak, unit = nbytes / sec / 1e9, PEAK_HBM_GBS, "GB/s"
+    else:
+        ach, peak, unit = flops / sec / 1e12, PEAK_TFLOPS["bf16"], "TFLOP/s"
+    tr = traffic_per_launch("alibi")
     return {"workload": ALIBI["description"], "ms_per_step": round(cold["ms_per_step"], 5),
             "tflops": round(cold["tflops"], 3),
+            "roofline": {"bound": bound, "achieved": round(ach, 2), "peak": peak, "unit": unit,
+                         "frac": round(ach / peak, 4),
+                         "traffic": None if tr is None else round(tr)},
             "mfma_peak_frac": round(cold["tflops"] / PEAK_TFLOPS["bf16"], 4),
             "roofline_frac": round(cold["tflops"] / ceil, 4),
             "bound": bound_of(cold["alg_gflop"] * 1e9, cold["alg_mbytes"] * 1e6, "bf16"),
