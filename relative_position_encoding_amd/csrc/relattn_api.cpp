@@ -329,6 +329,7 @@ int make_plan(const relattn_tensor* q, const relattn_tensor* k, const relattn_te
   P.bf16 = q->dtype == RELATTN_BF16;
   P.d = (int)d;
   P.mode = is_lab ? relattn::kRelLabel
+                  : (is_ob && grid_m > 0) ? relattn::kRelGrid
                   : (is_t5 || is_ob) ? relattn::kRelT5
                                      : ((wK || wV) ? relattn::kRelShaw : relattn::kRelNone);
   P.has_wk = wK != nullptr;
@@ -447,7 +448,7 @@ int make_plan(const relattn_tensor* q, const relattn_tensor* k, const relattn_te
     }
   }
   if (!found) {
-    if (P.mode == relattn::kRelT5)
+    if (P.mode == relattn::kRelT5 || P.mode == relattn::kRelGrid)
       return fail(RELATTN_ERR_UNSUPPORTED,
                   "scalar-bias offset window 2*min(max_distance or window, n-1)+1 = %d "
                   "does not fit on chip",

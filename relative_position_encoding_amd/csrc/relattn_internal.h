@@ -67,7 +67,7 @@ struct FwdParams {
   const void* xl_v;
   int64_t xl_u_sh, xl_v_sh;  // head strides (0 = one vector for all heads)
   int32_t xl;
-  // 2-D window bias (grid_m = M > 0, scalar-bias mode with ob = 1): tokens in
+  // 2-D window bias (grid mode, grid_m = M > 0, ob = 1): tokens in
   // raster order on an M x M grid; t5_bias points at the head's row of a
   // [Hb, (2M-1)^2] table and t5.nb = (2M-1)^2 entries are loaded.
   int32_t grid_m;
@@ -81,9 +81,10 @@ struct FwdParams {
   T5Buckets t5;
 };
 
-// kRelT5: scalar bias by T5 bucket, clipped offset or 2-D offset; kRelLabel:
-// scalar bias by a per-pair label read from memory.
-enum RelMode { kRelNone = 0, kRelShaw = 1, kRelT5 = 2, kRelLabel = 3 };
+// kRelT5: scalar bias by T5 bucket or clipped offset; kRelLabel: scalar bias
+// by a per-pair label read from memory; kRelGrid: scalar bias by the 2-D
+// offset of raster tokens on an M x M window.
+enum RelMode { kRelNone = 0, kRelShaw = 1, kRelT5 = 2, kRelLabel = 3, kRelGrid = 4 };
 
 // Where the w^V rows wait for the epilogue: their own LDS region (loaded in
 // the prologue), the first K/V ring stage the loop frees, or the free ring

@@ -114,7 +114,8 @@ __host__ __device__ inline Layout make_layout(int mode, bool has_wk, bool has_wv
     off += (bytes + 15) & ~15;
     return at;
   };
-  const bool shaw = mode == kRelShaw, t5 = mode == kRelT5, lab = mode == kRelLabel;
+  const bool shaw = mode == kRelShaw, t5 = mode == kRelT5 || mode == kRelGrid;
+  const bool lab = mode == kRelLabel;
   L.wk_rows = dma_rows((nr + 31) & ~31, G::ROWB);
   L.wv_rows = dma_rows((nr + 15) & ~15, G::ROWB);
   // relative row: padding, nr labels, padding.  Dword LDS accesses are
@@ -181,7 +182,8 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<D, NW, MODE, BF16, BC>()))) vo
   constexpr int NKS = G::NKS, ROWB = G::ROWB, LPW = G::LPW;
   constexpr int KSTR = G::KSTR, SPAN = G::SPAN, PADL = G::PADL, PADU = G::PADU;
   constexpr bool SHAW = (MODE == kRelShaw);
-  constexpr bool T5 = (MODE == kRelT5);
+  constexpr bool GRID = (MODE == kRelGrid);  // the bias by 2-D offset
+  constexpr bool T5 = (MODE == kRelT5) || GRID;
   constexpr bool LAB = (MODE == kRelLabel);
   constexpr bool GATHER = (SHAW && HAS_WK) || T5 || LAB;  // a gathered relative logit
   // label mode: each wave loads its 32 rows of a tile's labels (32 x BC bytes)
@@ -458,12 +460,10 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<D, NW, MODE, BF16, BC>()))) vo
   const int band = T5 ? p.t5_dist : c;  // |j - i| >= band: one end value for the tile
   // 2-D window bias: this lane's query on the M x M grid
   int gy = 0, gx = 0;
-  if constexpr (T5) {
-    if (p.grid_m) {
-      const int qc = min(qi, p.n - 1);
-      gy = qc / p.grid_m;
-      gx = qc - gy * p.grid_m;
-    }
+  if constexpr (GRID) {
+    const int qc = min(qi, p.n - 1);
+    gy = qc / p.grid_m;
+    gx = qc - gy * p.grid_m;
   }
   // offsets whose label holds a single key (1 <= r <= 2c - 1, reachable):
   // their logits are kept for the value term
@@ -596,7 +596,7 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<D, NW, MODE, BF16, BC>()))) vo
               rv[kb][8 * g + e] = TBC[min((int)byte, nbm)];
             }
           }
-      } else if (T5 && p.grid_m) {
+      } else if constexpr (GRID) {
         // 2-D window: the bias of the key's offset (dy, dx) from the query,
         // tokens in raster order on an M x M grid; the row of key j is
         // floor((j + 1/2) / M), exact in fp32 for j < 2^22
@@ -940,6 +940,7 @@ template <int D, int NW, int BC, bool BF16>
 static int launch_mode(RelMode mode, bool has_wk, bool has_wv, const FwdParams& p,
                        void* stream) {
   if (mode == kRelT5) return launch_t<D, NW, BC, BF16, kRelT5, false, false>(p, stream);
+  if (mode == kRelGrid) return launch_t<D, NW, BC, BF16, kRelGrid, false, false>(p, stream);
   if (mode == kRelLabel) return launch_t<D, NW, BC, BF16, kRelLabel, false, false>(p, stream);
   if (mode == kRelShaw) {
     if (has_wk && has_wv) return launch_t<D, NW, BC, BF16, kRelShaw, true, true>(p, stream);
