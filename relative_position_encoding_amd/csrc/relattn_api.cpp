@@ -329,6 +329,7 @@ int make_plan(const relattn_tensor* q, const relattn_tensor* k, const relattn_te
   P.bf16 = q->dtype == RELATTN_BF16;
   P.d = (int)d;
   P.mode = is_lab ? relattn::kRelLabel
+                  : (is_xl && d <= 64) ? relattn::kRelXL
                   : (is_ob && grid_m > 0) ? relattn::kRelGrid
                   : (is_t5 || is_ob) ? relattn::kRelT5
                                      : ((wK || wV) ? relattn::kRelShaw : relattn::kRelNone);
@@ -415,7 +416,8 @@ int make_plan(const relattn_tensor* q, const relattn_tensor* k, const relattn_te
   // as the kernels')
   auto vgpr_waves_per_cu = [&](int kblock, int waves) {
     if (d > 64) return 4 * ((P.bf16 && kblock == 32) ? 2 : 1);
-    return 4 * ((P.bf16 && P.mode != relattn::kRelShaw && (d <= 32 || waves == 4)) ? 3 : 2);
+    return 4 * ((P.bf16 && P.mode != relattn::kRelShaw && P.mode != relattn::kRelXL &&
+                 (d <= 32 || waves == 4)) ? 3 : 2);
   };
   // a workgroup whose lower half of waves already covers every query row
   // would leave the rest idle (short windows, e.g. 7 x 7 = 49 tokens)
@@ -485,7 +487,18 @@ int make_plan(const relattn_tensor* q, const relattn_tensor* k, const relattn_te
     p.wk_sh = wK->shape[0] == 1 ? 0 : wK->stride[0];
     p.wk_sr = wK->stride[1];
   }
-  if (is_xl) {
+  if (is_xl && P.mode == relattn::kRelXL) {
+    // fused: the kernel reads R's row of distance i - j (clamped to +-clip)
+    // from the row of distance 0
+    const int64_t esz = P.bf16 ? 2 : 4;
+    p.wk = static_cast<const char*>(wK->data) + (int64_t)clip_k * wK->stride[1] * esz;
+    p.wk_sr = wK->stride[1];
+    p.xl = 1;
+    p.xl_u = xl_u->data;
+    p.xl_v = xl_v->data;
+    p.xl_u_sh = xl_u->shape[0] == 1 ? 0 : xl_u->stride[0];
+    p.xl_v_sh = xl_v->shape[0] == 1 ? 0 : xl_v->stride[0];
+  } else if (is_xl) {
     // row r of the label window (offset j - i = r - clip) is R's row for
     // distance i - j, 2*clip - r: start at the last row and step backwards
     const int64_t esz = P.bf16 ? 2 : 4;

@@ -83,8 +83,11 @@ struct FwdParams {
 
 // kRelT5: scalar bias by T5 bucket or clipped offset; kRelLabel: scalar bias
 // by a per-pair label read from memory; kRelGrid: scalar bias by the 2-D
-// offset of raster tokens on an M x M window.
-enum RelMode { kRelNone = 0, kRelShaw = 1, kRelT5 = 2, kRelLabel = 3, kRelGrid = 4 };
+// offset of raster tokens on an M x M window; kRelXL: Transformer-XL with the
+// relative logits formed per key tile (wk points at the position table's row of
+// distance 0, rows by distance i - j clamped to +-clip).
+enum RelMode { kRelNone = 0, kRelShaw = 1, kRelT5 = 2, kRelLabel = 3, kRelGrid = 4,
+               kRelXL = 5 };
 
 // Where the w^V rows wait for the epilogue: their own LDS region (loaded in
 // the prologue), the first K/V ring stage the loop frees, or the free ring

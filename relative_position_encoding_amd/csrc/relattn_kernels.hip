@@ -40,6 +40,14 @@
 // The +c tail is a running sum (empty under the causal mask) and the -c tail
 // is what the row sum leaves.  The epilogue adds S W^V with MFMA.
 //
+// Transformer-XL, fused (XL mode, d <= 64): the relative logit (q_i + v).R_{i-j}
+// is formed per key tile instead of once per query row: each wave multiplies
+// its 32 queries by the BC + 31 position-table rows of the distances they can
+// reach in the tile (rows read straight from L2 as MFMA operands), stores the
+// products position-major in a per-wave LDS block and gathers them like the
+// band.  No per-query window of every distance is kept, so long windows leave
+// room for four-wave workgroups.
+//
 // Edge labels (label mode): the scalar bias is indexed by a label given per
 // (query, key) pair instead of a function of the offset.  Each wave's 32 rows
 // of a tile's label matrix travel with the K/V stage by LDS-DMA, and every
@@ -88,6 +96,12 @@ struct Geo {
   static constexpr int SPAN = 7 * KSTR + 1;
   static constexpr int PADL = SPAN - 1;
   static constexpr int PADU = 2 * SPAN - 1;
+  // fused XL: 32-distance MFMA blocks per key tile (the BC + 31 offsets a
+  // wave's 32 queries reach in a tile), and the per-wave LDS block of their
+  // products (position-major, XRS floats per position)
+  static constexpr int NXB = (BC + 62) / 32;
+  static constexpr int XRS = 34;
+  static constexpr int XLB = NXB * 32 * XRS * 4;
   static_assert(STAGEB % (1024 * NW) == 0, "stage must split into whole 1 KB instructions");
   static_assert(BR * ROWB % 1024 == 0, "the Q tile must split into whole 1 KB instructions");
 };
@@ -115,7 +129,7 @@ __host__ __device__ inline Layout make_layout(int mode, bool has_wk, bool has_wv
     return at;
   };
   const bool shaw = mode == kRelShaw, t5 = mode == kRelT5 || mode == kRelGrid;
-  const bool lab = mode == kRelLabel;
+  const bool lab = mode == kRelLabel, xlf = mode == kRelXL;
   L.wk_rows = dma_rows((nr + 31) & ~31, G::ROWB);
   L.wv_rows = dma_rows((nr + 15) & ~15, G::ROWB);
   // relative row: padding, nr labels, padding.  Dword LDS accesses are
@@ -151,6 +165,9 @@ __host__ __device__ inline Layout make_layout(int mode, bool has_wk, bool has_wv
   } else {
     L.le = off;
     L.qs = q_bytes <= G::STAGEB ? (nstage - 1) * G::STAGEB : take(q_bytes);
+    // fused XL: per wave, the tile's relative logits position-major, 32 lanes
+    // (+2 floats) per position
+    if (xlf) L.le = take(NW * G::XLB);
   }
   L.tbc = (t5 || lab) ? take(((t5_nb + 63) & ~63) * 4) : off;
   L.tb = t5 ? take((2 * t5_dist + 1 + G::PADL + G::PADU) * 4) : off;
@@ -169,7 +186,7 @@ __host__ __device__ inline Layout make_layout(int mode, bool has_wk, bool has_wv
 template <int D, int NW, int MODE, bool BF16, int BC>
 __host__ __device__ constexpr int waves_per_simd() {
   return D > 64 ? ((BF16 && BC == 32) ? 2 : 1)
-                : ((BF16 && MODE != kRelShaw && (D <= 32 || NW == 4)) ? 3 : 2);
+                : ((BF16 && MODE != kRelShaw && MODE != kRelXL && (D <= 32 || NW == 4)) ? 3 : 2);
 }
 template <int D, int NW, int BC, bool BF16, int MODE, bool HAS_WK, bool HAS_WV>
 __global__ __launch_bounds__(64 * NW)
@@ -185,7 +202,9 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<D, NW, MODE, BF16, BC>()))) vo
   constexpr bool GRID = (MODE == kRelGrid);  // the bias by 2-D offset
   constexpr bool T5 = (MODE == kRelT5) || GRID;
   constexpr bool LAB = (MODE == kRelLabel);
-  constexpr bool GATHER = (SHAW && HAS_WK) || T5 || LAB;  // a gathered relative logit
+  constexpr bool XLF = (MODE == kRelXL);  // fused Transformer-XL
+  constexpr bool GATHER = (SHAW && HAS_WK) || T5 || LAB || XLF;  // a gathered relative logit
+  constexpr int NXB = G::NXB, XRS = G::XRS;
   // label mode: each wave loads its 32 rows of a tile's labels (32 x BC bytes)
   // with the stage, in 1 KB instructions
   constexpr int LLPW = LAB ? BC / 32 : 0;
@@ -253,8 +272,8 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<D, NW, MODE, BF16, BC>()))) vo
   // logit) and v (relative logit), requested before any LDS-DMA so that the
   // counted DMA waits below stay exact.
   Op xu[NKS], xv[NKS];
-  if constexpr (SHAW && HAS_WK) {
-    if (p.xl) {
+  if constexpr ((SHAW && HAS_WK) || XLF) {
+    if (XLF || p.xl) {
       const T* up = reinterpret_cast<const T*>(p.xl_u) + h * p.xl_u_sh;
       const T* vp = reinterpret_cast<const T*>(p.xl_v) + h * p.xl_v_sh;
 #pragma unroll
@@ -362,6 +381,16 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<D, NW, MODE, BF16, BC>()))) vo
     }
   }
   if constexpr (SHAW && (HAS_WK || HAS_WV)) block_sync();  // Q sits in the relative rows
+  // fused XL: q + v for the relative logit, q + u for the content logit
+  Op qpos_x[NKS];
+  if constexpr (XLF) {
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      qpos_x[ks] = op_add(qop[ks], xv[ks]);
+      qop[ks] = op_add(qop[ks], xu[ks]);
+    }
+  }
+  const T* xrh = XLF ? reinterpret_cast<const T*>(p.wk) + h * p.wk_sh : nullptr;
 
   // ---- relative logits in LDS.  Shaw: row qrow holds scale*log2e*q.w^K_r for
   // the reachable label rows r_lo..r_hi at entries PADL + (r - r_lo), with
@@ -453,7 +482,7 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<D, NW, MODE, BF16, BC>()))) vo
   const int gtop = nwin + PADL + PADU - SPAN;     // highest gather base
   const float* relrow = T5 ? TB : myLE;
   float Llo = 0.f, Lhi = 0.f;
-  if constexpr (GATHER && !LAB) {
+  if constexpr (GATHER && !LAB && !XLF) {
     Llo = relrow[PADL];
     Lhi = relrow[PADL + nwin - 1];
   }
@@ -497,6 +526,29 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<D, NW, MODE, BF16, BC>()))) vo
       else wait_vm_dyn(pending);
     }
     block_sync();  // ... and for every wave; stage (t - 1) % nstage is free
+    // fused XL: the position-table rows of the distances this wave reaches in
+    // the tile, as MFMA A operands (row = MFMA row ql of block b: offset j - i
+    // = omin + 32 b + ql, distance i - j clamped to the window), requested
+    // before the next stage so that one counted wait covers them
+    Op xr[XLF ? NXB : 1][NKS];
+    if constexpr (XLF) {
+      if (wq0 < p.n && !(p.causal && j0 > wq0 + 31)) {
+        const int omin = j0 - wq0 - 31;
+#pragma unroll
+        for (int bx = 0; bx < NXB; ++bx) {
+          const int dist = min(max(-(omin + 32 * bx + ql), -c), c);
+          const T* rp = xrh + (int64_t)dist * p.wk_sr;
+#pragma unroll
+          for (int ks = 0; ks < NKS; ++ks) {
+            if constexpr (BF16) {
+              xr[bx][ks] = *reinterpret_cast<const bf16x8*>(rp + 16 * ks + 8 * hh);
+            } else {
+              xr[bx][ks] = rp[2 * ks + hh];
+            }
+          }
+        }
+      }
+    }
     if (t + nstage - 1 < ntiles) {
       issue_stage(t + nstage - 1, st_next);
     } else if (wv_ring && wv_stage < 0) {
@@ -532,6 +584,25 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<D, NW, MODE, BF16, BC>()))) vo
       for (int ks = 0; ks < NKS; ++ks) s[kb] = mfma(a[ks], qop[ks], s[kb]);
     }
 
+    // fused XL: relative logits of the tile's distances, position p = offset
+    // - omin at xw[p * XRS + lane's query]
+    if constexpr (XLF) {
+      // the table rows are older than this iteration's stage requests
+      if (t + nstage - 1 < ntiles) wait_vm<SLPW>();
+      else wait_vm<0>();
+      float* xw = reinterpret_cast<float*>(smem + lay.le) + wave * (NXB * 32 * XRS) + ql;
+#pragma unroll
+      for (int bx = 0; bx < NXB; ++bx) {
+        f32x16 acc = {};
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) acc = mfma(xr[bx][ks], qpos_x[ks], acc);
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          xw[(32 * bx + 8 * (i >> 2) + 4 * hh + (i & 3)) * XRS] = acc[i] * p.scale_log2;
+      }
+      compiler_fence();  // both halves of the wave wrote each query's column
+    }
+
     // Register (kb, 8g + e) holds key j0 + hoff + 32kb + 16g + KSTR*e, i.e.
     // offset delta = kofs + 32kb + 16g + KSTR*e from this lane's query.
     const int kofs = j0 + hoff - qi;
@@ -543,7 +614,7 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<D, NW, MODE, BF16, BC>()))) vo
     // so for labels).
     const bool causal_cut = p.causal && j0 + BC - 1 > wq0;
     const bool need_mask =
-        (j0 + BC > kv_len) || (causal_cut && (LAB || !(GATHER && !off_band)));
+        (j0 + BC > kv_len) || (causal_cut && (LAB || XLF || !(GATHER && !off_band)));
     // visible iff its key offset within the lane's keys is <= lim
     const int lim = min(kv_len - 1 - j0 - hoff, p.causal ? -kofs : 0x3fffffff);
 
@@ -595,6 +666,19 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<D, NW, MODE, BF16, BC>()))) vo
               }
               rv[kb][8 * g + e] = TBC[min((int)byte, nbm)];
             }
+          }
+      } else if constexpr (XLF) {
+        // fused XL: key group (kb, g) starts at position hoff + 32 kb + 16 g
+        // + 31 - ql of the wave's block (offset kofs + 32 kb + 16 g - omin)
+        const float* xw =
+            reinterpret_cast<const float*>(smem + lay.le) + wave * (NXB * 32 * XRS) + ql;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int g = 0; g < 2; ++g) {
+            const int p0 = hoff + 32 * kb + 16 * g + 31 - ql;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) rv[kb][8 * g + e] = xw[(p0 + KSTR * e) * XRS];
           }
       } else if constexpr (GRID) {
         // 2-D window: the bias of the key's offset (dy, dx) from the query,
@@ -942,6 +1026,10 @@ static int launch_mode(RelMode mode, bool has_wk, bool has_wv, const FwdParams& 
   if (mode == kRelT5) return launch_t<D, NW, BC, BF16, kRelT5, false, false>(p, stream);
   if (mode == kRelGrid) return launch_t<D, NW, BC, BF16, kRelGrid, false, false>(p, stream);
   if (mode == kRelLabel) return launch_t<D, NW, BC, BF16, kRelLabel, false, false>(p, stream);
+  if (mode == kRelXL) {
+    if constexpr (D <= 64) return launch_t<D, NW, BC, BF16, kRelXL, false, false>(p, stream);
+    return (int)hipErrorInvalidValue;
+  }
   if (mode == kRelShaw) {
     if (has_wk && has_wv) return launch_t<D, NW, BC, BF16, kRelShaw, true, true>(p, stream);
     if (has_wk) return launch_t<D, NW, BC, BF16, kRelShaw, true, false>(p, stream);

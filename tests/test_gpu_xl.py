@@ -93,6 +93,40 @@ def test_xl_zero_biases_match_shaw_with_reversed_table(ra):
     assert torch.equal(a, b)
 
 
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=str)
+@pytest.mark.parametrize("n", [1, 33, 97])
+@pytest.mark.parametrize("causal", [False, True])
+def test_xl_small_rows_d16(ra, dtype, n, causal):
+    """Short and ragged segments at d = 16 (a single partial key tile, tiles
+    whose distance block reaches past both ends of the table)."""
+    B, H, d, W = 2, 2, 16, 20
+    q, k, v = (gen((B, H, n, d), dtype, 1700 + n + i) for i in range(3))
+    R = gen((H, 2 * W + 1, d), dtype, 1703, 0.5)
+    u, vb = gen((H, d), dtype, 1704, 0.5), gen((H, d), dtype, 1705, 0.5)
+    got = run(ra, q, k, v, R, u, vb, W, causal, [n, max(1, n - 7)])
+    want = oracle.xl_attention(q, k, v, R, u, vb, W, causal=causal, key_lens=[n, max(1, n - 7)])
+    assert float(np.max(np.abs(got - want))) <= TOL[dtype]
+
+
+def test_xl_full_size(ra):
+    """The benchmark segment (B8 H16 n512 d64, causal, every distance), in the
+    launch configuration the benchmark times, against the oracle on sampled
+    (batch, head) slices."""
+    import workloads
+    w = workloads.XL_WORKLOADS["xl"]
+    x = workloads.make_xl_inputs(w)
+    out = ra.fwd_xl(*(x[key].to(DEV) for key in ("q", "k", "v", "R", "u", "vb")), x["window"],
+                    causal=True)
+    torch.cuda.synchronize()
+    out = out.double().cpu().numpy()
+    for b, h in ((0, 0), (3, 9), (7, 15)):
+        sl = lambda t: t[b:b + 1, h:h + 1]
+        want = oracle.xl_attention(sl(x["q"]), sl(x["k"]), sl(x["v"]), x["R"][h:h + 1],
+                                   x["u"][h:h + 1], x["vb"][h:h + 1], x["window"], causal=True)
+        err = float(np.max(np.abs(out[b:b + 1, h:h + 1] - want)))
+        assert err <= TOL[torch.bfloat16], (b, h, err)
+
+
 def test_xl_rejects(ra):
     q = gen((1, 2, 16, 64), torch.bfloat16, 1600).to(DEV)
     R = gen((2, 9, 64), torch.bfloat16, 1601).to(DEV)
