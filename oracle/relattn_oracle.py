@@ -52,6 +52,10 @@ Readings where the pages are silent or garbled (each is listed in the design doc):
   matrix E[b, i, j] for the edge from query i to key j, shared by the heads; the
   bias table is [Hb, NL] with Hb in {1, H}; the attention scale (1/sqrt(d) by
   default) multiplies the content logit only, as for the offset bias;
+* per-pair edge labels with vector tables (the same labeled-graph reading of
+  Eq. 3 and Eq. 4): a^K_ij = w^K[h', E[b, i, j]] and a^V_ij = w^V[h', E[b, i, j]]
+  with tables [Ht, NL, d], Ht in {1, H}; the scale multiplies both terms of the
+  logit (as in Eq. 5) and a^V is unscaled, as for the clipped-offset tables;
 * backward (no page prints it): the gradients of a scalar loss sum(dz * z) by
   the chain rule through the forward above; a table shared by all heads takes
   the sum over heads, and hidden pairs give no gradient.  Pinned by central
@@ -85,6 +89,7 @@ __all__ = [
     "xl_attention",
     "grid_bias_attention",
     "edge_label_attention",
+    "edge_label_relattn",
     "to_f64",
 ]
 
@@ -700,4 +705,41 @@ def edge_label_attention(q, k, v, labels, bias, scale=None, causal: bool = False
             row = bias[0 if bias.shape[0] == 1 else h]
             e = s * (q[b, h] @ k[b, h].T) + row[E[b]]
             z[b, h] = _masked_softmax_rows(e, ok) @ v[b, h]
+    return z
+
+
+def edge_label_relattn(q, k, v, labels, aK=None, aV=None, scale=None, causal: bool = False,
+                       key_lens=None):
+    """Relation-aware self-attention (Eq. 4 and Eq. 3) over a labeled graph:
+    a^K_ij = aK[h', E[b, i, j]], a^V_ij = aV[h', E[b, i, j]], materialised.
+
+        e_ij = scale * q_i . (k_j + a^K_ij),   z_i = sum_j alpha_ij (v_j + a^V_ij)
+
+    labels: [B, n, n] integers in [0, NL), shared by the heads; aK, aV: [Ht, NL,
+    d] with Ht in {1, H}, either may be None (absent = zero).  scale defaults to
+    1/sqrt(d).
+    """
+    q, k, v = to_f64(q), to_f64(k), to_f64(v)
+    aK, aV = to_f64(aK), to_f64(aV)
+    E = np.asarray(labels).astype(np.int64)
+    B, H, n, d = q.shape
+    assert E.shape == (B, n, n)
+    for t in (aK, aV):
+        if t is not None:
+            assert E.min(initial=0) >= 0 and E.max(initial=0) < t.shape[1]
+    s = _default_scale(d, scale)
+    lens = _key_lengths(key_lens, B, n)
+    z = np.zeros((B, H, n, v.shape[-1]))
+    for b in range(B):
+        ok = visible(n, causal, lens[b])
+        for h in range(H):
+            kk = k[b, h][None, :, :]                                  # [1, n, d]
+            if aK is not None:
+                kk = kk + _table_for_head(aK, h)[E[b]]                # [n, n, d]
+            e = s * np.einsum("id,ijd->ij", q[b, h], np.broadcast_to(kk, (n, n, d)))
+            alpha = _masked_softmax_rows(e, ok)
+            vv = v[b, h][None, :, :]
+            if aV is not None:
+                vv = vv + _table_for_head(aV, h)[E[b]]
+            z[b, h] = np.einsum("ij,ijd->id", alpha, np.broadcast_to(vv, (n, n, v.shape[-1])))
     return z

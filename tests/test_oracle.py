@@ -880,3 +880,87 @@ def test_edge_labels_two_tokens_closed_form():
         a1 = 1.0 / (1.0 + math.exp(e[0] - e[1]))
         np.testing.assert_allclose(z[i], (1 - a1) * v[0, 0, 0] + a1 * v[0, 0, 1], rtol=0,
                                    atol=1e-14)
+
+
+# ---------------------------------------------------------------------------
+# relation-aware attention with per-pair labels and vector tables (Eq. 3 and
+# Eq. 4 over a labeled graph)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("tables", ["KV", "K", "V"])
+@pytest.mark.parametrize("causal,lens", [(False, None), (True, None), (False, [7, 15])])
+def test_edge_relattn_with_clipped_offset_labels_is_shaw(tables, causal, lens):
+    """Labels clip(j - i, k) + k with the 2k+1-row tables are Shaw's
+    relation-aware attention (the brute-force oracle)."""
+    B, H, n, d, kc = 2, 3, 15, 8, 3
+    q, k, v = rnd((B, H, n, d), 400), rnd((B, H, n, d), 401), rnd((B, H, n, d), 402)
+    aK = rnd((H, 2 * kc + 1, d), 403) if "K" in tables else None
+    aV = rnd((1, 2 * kc + 1, d), 404) if "V" in tables else None
+    E = np.stack([oracle.relative_labels(n, kc) + kc] * B)
+    z = oracle.edge_label_relattn(q, k, v, E, aK, aV, causal=causal, key_lens=lens)
+    want = oracle.relattn_bruteforce(q, k, v, aK, aV, kc, causal=causal, key_lens=lens)
+    np.testing.assert_allclose(z, want, rtol=0, atol=1e-12)
+
+
+def test_edge_relattn_single_label_is_textbook_on_shifted_keys_and_values():
+    """One label everywhere: a^K_ij = w^K, a^V_ij = w^V, i.e. attention over k_j + w^K
+    and v_j + w^V (library routine)."""
+    B, H, n, d = 2, 2, 11, 8
+    q, k, v = rnd((B, H, n, d), 410), rnd((B, H, n, d), 411), rnd((B, H, n, d), 412)
+    wK, wV = rnd((H, 1, d), 413), rnd((H, 1, d), 414)
+    E = np.zeros((B, n, n), dtype=np.int64)
+    z = oracle.edge_label_relattn(q, k, v, E, wK, wV, causal=True)
+    ok = np.tril(np.ones((n, n), dtype=bool))
+    want = sdpa(q, k + wK[None], v + wV[None], ok, 1 / math.sqrt(d))
+    np.testing.assert_allclose(z, want, rtol=0, atol=1e-12)
+
+
+def test_edge_relattn_value_histogram_probe():
+    """q = 0 (uniform weights over the visible keys), value table only:
+    z_i - mean_j v_j = sum_r (count of label r in row i of batch b / n) w^V_r.
+    The batch entries hold different label matrices and the rows are not
+    symmetric, so a transposed or another entry's matrix fails."""
+    B, H, n, d, NL = 2, 2, 9, 5, 6
+    rng = np.random.default_rng(420)
+    E = rng.integers(0, NL, (B, n, n))
+    q = np.zeros((B, H, n, d))
+    k, v = rnd((B, H, n, d), 421), rnd((B, H, n, d), 422)
+    aV = rnd((H, NL, d), 423)
+    z = oracle.edge_label_relattn(q, k, v, E, None, aV)
+    for b in range(B):
+        for h in range(H):
+            for i in range(n):
+                hist = np.bincount(E[b, i], minlength=NL) / n
+                np.testing.assert_allclose(z[b, h, i] - v[b, h].mean(axis=0), hist @ aV[h],
+                                           rtol=0, atol=1e-12)
+
+
+def test_edge_relattn_label_permutation_invariance():
+    """Renaming the labels and permuting the table rows alike changes nothing."""
+    B, H, n, d, NL = 2, 2, 10, 8, 7
+    q, k, v = rnd((B, H, n, d), 430), rnd((B, H, n, d), 431), rnd((B, H, n, d), 432)
+    aK, aV = rnd((H, NL, d), 433), rnd((H, NL, d), 434)
+    E = np.random.default_rng(435).integers(0, NL, (B, n, n))
+    perm = np.random.default_rng(436).permutation(NL)
+    inv = np.argsort(perm)
+    z1 = oracle.edge_label_relattn(q, k, v, E, aK, aV, causal=True)
+    z2 = oracle.edge_label_relattn(q, k, v, perm[E], aK[:, inv], aV[:, inv], causal=True)
+    np.testing.assert_allclose(z1, z2, rtol=0, atol=1e-12)
+
+
+def test_edge_relattn_two_tokens_closed_form():
+    """n = 2, d = 2, written out per element: e_ij = s q_i.(k_j + w^K_{E_ij}),
+    alpha_i1 = 1 / (1 + exp(e_i0 - e_i1)), z_i = sum_j alpha_ij (v_j + w^V_{E_ij})."""
+    rng = np.random.default_rng(440)
+    q, k, v = (rng.standard_normal((1, 1, 2, 2)) for _ in range(3))
+    E = np.array([[[1, 0], [2, 1]]])
+    wK, wV = rng.standard_normal((1, 3, 2)), rng.standard_normal((1, 3, 2))
+    s = 0.9
+    z = oracle.edge_label_relattn(q, k, v, E, wK, wV, scale=s)[0, 0]
+    for i in range(2):
+        e = [s * sum(q[0, 0, i, c] * (k[0, 0, j, c] + wK[0, E[0, i, j], c]) for c in range(2))
+             for j in range(2)]
+        a1 = 1.0 / (1.0 + math.exp(e[0] - e[1]))
+        want = [(1 - a1) * (v[0, 0, 0, c] + wV[0, E[0, i, 0], c])
+                + a1 * (v[0, 0, 1, c] + wV[0, E[0, i, 1], c]) for c in range(2)]
+        np.testing.assert_allclose(z[i], want, rtol=0, atol=1e-14)
