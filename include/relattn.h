@@ -246,6 +246,38 @@ int relattn_validate_edge_bias(const relattn_tensor* q, const relattn_tensor* k,
                                const relattn_tensor* bias, float scale,
                                const relattn_mask* mask, const relattn_tensor* out);
 
+/*
+ * relattn_fwd_edge_tables: relation-aware self-attention over a labeled graph
+ * ("Self-Attention with Relative Position Representations", summary page: Eq. 4
+ * and Eq. 3 with the edge representations a^K_ij, a^V_ij taken from the label
+ * of the pair, which need not be a clipped offset):
+ *
+ *       e_ij = scale * q_i.(k_j + wK[h', E_ij]),   z_i = sum_j alpha_ij (v_j + wV[h', E_ij])
+ *
+ *   with E_ij = labels[b, i, j].
+ *   q, k, v, out : as for relattn_fwd.
+ *   labels       : [B, n, n] U8, the layout rules of relattn_fwd_edge_bias; a
+ *                  label >= NL is read as NL - 1.
+ *   wK, wV       : [Ht, NL, d] in the dtype of q, Ht in {H, 1}, 1 <= NL <= 256
+ *                  (the same NL for both); either may be NULL (absent = zero),
+ *                  not both.  Rows 16-byte aligned as for relattn_fwd's tables.
+ *   scale        : multiplies both terms of the logit; <= 0 picks 1/sqrt(d).
+ *   mask, stream : as for relattn_fwd.
+ * Errors as for relattn_fwd; UNSUPPORTED when the NL-entry rows of a workgroup's
+ * queries do not fit on chip.
+ */
+int relattn_fwd_edge_tables(const relattn_tensor* q, const relattn_tensor* k,
+                            const relattn_tensor* v, const relattn_tensor* labels,
+                            const relattn_tensor* wK, const relattn_tensor* wV, float scale,
+                            const relattn_mask* mask, relattn_tensor* out, void* stream);
+
+/* relattn_validate_edge_tables: the argument checks of relattn_fwd_edge_tables,
+ * host only. */
+int relattn_validate_edge_tables(const relattn_tensor* q, const relattn_tensor* k,
+                                 const relattn_tensor* v, const relattn_tensor* labels,
+                                 const relattn_tensor* wK, const relattn_tensor* wV, float scale,
+                                 const relattn_mask* mask, const relattn_tensor* out);
+
 /* relattn_validate_offset_bias: the argument checks of relattn_fwd_offset_bias,
  * host only (no HIP call). */
 int relattn_validate_offset_bias(const relattn_tensor* q, const relattn_tensor* k,

@@ -15,6 +15,7 @@ __all__ = ["fwd", "validate", "fwd_offset_bias", "validate_offset_bias", "decode
            "bwd", "bwd_workspace_size", "bwd_offset_bias", "bwd_offset_bias_workspace_size",
            "attention", "attention_offset_bias", "fwd_xl", "validate_xl", "fwd_grid_bias",
            "validate_grid_bias", "fwd_edge_bias", "validate_edge_bias", "edge_label_buffer",
+           "fwd_edge_tables", "validate_edge_tables",
            "RelattnError", "library_path",
            "OK", "INVALID_ARGUMENT", "UNSUPPORTED", "NO_DEVICE", "LAUNCH_FAILED"]
 
@@ -107,6 +108,11 @@ def _load():
     lib.relattn_fwd_edge_bias.restype = ctypes.c_int
     lib.relattn_validate_edge_bias.argtypes = edge
     lib.relattn_validate_edge_bias.restype = ctypes.c_int
+    edget = [P(_Tensor)] * 6 + [ctypes.c_float, P(_Mask), P(_Tensor)]
+    lib.relattn_fwd_edge_tables.argtypes = edget + [ctypes.c_void_p]
+    lib.relattn_fwd_edge_tables.restype = ctypes.c_int
+    lib.relattn_validate_edge_tables.argtypes = edget
+    lib.relattn_validate_edge_tables.restype = ctypes.c_int
     lib.relattn_debug_indices.argtypes = [ctypes.c_int32, ctypes.c_int32, P(_T5),
                                           ctypes.c_void_p, ctypes.c_void_p]
     lib.relattn_debug_indices.restype = ctypes.c_int
@@ -691,7 +697,7 @@ def edge_label_buffer(B, n, device=None):
     return torch.zeros((B, n, n16), dtype=torch.uint8, device=device)[:, :, :n]
 
 
-def _edge_args(q, k, v, labels, bias, causal, key_lens, scale, out):
+def _edge_args(q, k, v, labels, bias, causal, key_lens, scale, out, tables=None):
     import torch
     n = labels.shape[1] if labels.dim() == 3 else 0
     if labels.dtype == torch.uint8 and labels.dim() == 3 and labels.numel() > 0:
@@ -703,7 +709,8 @@ def _edge_args(q, k, v, labels, bias, causal, key_lens, scale, out):
             raise RelattnError(INVALID_ARGUMENT,
                                "relattn: labels rows must be readable to n rounded up to 16 "
                                "bytes (see edge_label_buffer)")
-    views = [_view(x) for x in (q, k, v, labels, bias)]
+    views = [_view(x) for x in ((q, k, v, labels, bias) if tables is None
+                                 else (q, k, v, labels) + tuple(tables))]
     mask = None
     if causal or key_lens is not None:
         mask = _Mask(1 if causal else 0, key_lens.data_ptr() if key_lens is not None else None)
@@ -739,5 +746,35 @@ def validate_edge_bias(q, k, v, labels, bias, *, causal=False, key_lens=None, sc
     args, keep = _edge_args(q, k, v, labels, bias, causal, key_lens, scale,
                             q if out is None else out)
     st = lib.relattn_validate_edge_bias(*args)
+    del keep
+    return st
+
+
+def fwd_edge_tables(q, k, v, labels, wK=None, wV=None, *, causal=False, key_lens=None,
+                    scale=None, out=None, stream=None):
+    """Relation-aware attention over a labeled graph: labels uint8 [B, n, n]
+    (layout of ``fwd_edge_bias``), wK / wV [H or 1, NL, d] in the dtype of q;
+    e_ij = scale * q_i.(k_j + wK[E_ij]), z_i = sum_j alpha_ij (v_j + wV[E_ij]).
+    Returns ``out``."""
+    import torch
+    lib = _load()
+    _check_lens(key_lens)
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    args, keep = _edge_args(q, k, v, labels, None, causal, key_lens, scale, out, (wK, wV))
+    st = lib.relattn_fwd_edge_tables(*args, ctypes.c_void_p(_stream_of(q, stream)))
+    del keep
+    if st != OK:
+        _raise(lib, st)
+    return out
+
+
+def validate_edge_tables(q, k, v, labels, wK=None, wV=None, *, causal=False, key_lens=None,
+                         scale=None, out=None):
+    """Host-only argument check of ``fwd_edge_tables``; returns the status code."""
+    lib = _load()
+    args, keep = _edge_args(q, k, v, labels, None, causal, key_lens, scale,
+                            q if out is None else out, (wK, wV))
+    st = lib.relattn_validate_edge_tables(*args)
     del keep
     return st

@@ -226,9 +226,38 @@ int make_plan(const relattn_tensor* q, const relattn_tensor* k, const relattn_te
 
   const bool is_t5 = t5_bias != nullptr || t5 != nullptr;
   const bool is_ob = ob != nullptr;  // scalar bias by clipped offset, 2-D offset or label
-  const bool is_lab = labels != nullptr;  // ... by a per-pair label
-  if (is_lab && (!is_ob || grid_m > 0))
-    return fail(RELATTN_ERR_INVALID_ARGUMENT, "edge labels take a bias table by label");
+  const bool is_lab = labels != nullptr;  // ... by a per-pair label (or key/value tables)
+  if (is_lab && (grid_m > 0 || is_t5 || (!is_ob && !wK && !wV)))
+    return fail(RELATTN_ERR_INVALID_ARGUMENT,
+                "edge labels take a bias table or key/value tables by label");
+  if (is_lab) {
+    // [B, n, n] uint8 labels, rows read in whole 16-byte chunks
+    if (labels->ndim != 3)
+      return fail(RELATTN_ERR_INVALID_ARGUMENT, "labels must have 3 dims, got %d", labels->ndim);
+    if (labels->dtype != RELATTN_U8)
+      return fail(RELATTN_ERR_INVALID_ARGUMENT, "labels must be U8");
+    if (labels->shape[0] != q->shape[0] || labels->shape[1] != q->shape[2] ||
+        labels->shape[2] != q->shape[2])
+      return fail(RELATTN_ERR_INVALID_ARGUMENT, "labels must be [B, n, n]");
+    for (int i = 0; i < 3; ++i)
+      if (labels->stride[i] < 0)
+        return fail(RELATTN_ERR_INVALID_ARGUMENT, "labels stride[%d] < 0", i);
+    if (numel(labels) > 0) {
+      const int64_t n16 = (q->shape[2] + 15) / 16 * 16;
+      if (!labels->data) return fail(RELATTN_ERR_INVALID_ARGUMENT, "labels data is NULL");
+      if (labels->stride[2] != 1)
+        return fail(RELATTN_ERR_UNSUPPORTED, "labels: innermost dimension must be contiguous");
+      if (!aligned16(labels->data))
+        return fail(RELATTN_ERR_UNSUPPORTED, "labels: data pointer is not 16-byte aligned");
+      if (labels->stride[1] % 16 != 0 || labels->stride[0] % 16 != 0)
+        return fail(RELATTN_ERR_UNSUPPORTED, "labels: strides must be multiples of 16 bytes");
+      if (labels->stride[1] < n16)
+        return fail(RELATTN_ERR_UNSUPPORTED,
+                    "labels: row stride %lld is below n rounded up to 16 (%lld)",
+                    (long long)labels->stride[1], (long long)n16);
+    }
+  }
+  const bool is_graph = is_lab && !is_ob;  // Shaw tables indexed by label
   if ((t5_bias == nullptr) != (t5 == nullptr))
     return fail(RELATTN_ERR_INVALID_ARGUMENT, "t5_bias and t5 params must be given together");
   if (is_t5 && (wK || wV))
@@ -260,33 +289,8 @@ int make_plan(const relattn_tensor* q, const relattn_tensor* k, const relattn_te
       if (mask && mask->causal)
         return fail(RELATTN_ERR_INVALID_ARGUMENT, "a 2-D window bias takes no causal mask");
     } else if (is_lab) {
-      // [B, n, n] uint8 labels, rows read in whole 16-byte chunks
       if (ob->shape[1] < 1 || ob->shape[1] > 256)
         return fail(RELATTN_ERR_INVALID_ARGUMENT, "bias: shape[1] (labels) must be in [1, 256]");
-      if (labels->ndim != 3)
-        return fail(RELATTN_ERR_INVALID_ARGUMENT, "labels must have 3 dims, got %d", labels->ndim);
-      if (labels->dtype != RELATTN_U8)
-        return fail(RELATTN_ERR_INVALID_ARGUMENT, "labels must be U8");
-      if (labels->shape[0] != q->shape[0] || labels->shape[1] != q->shape[2] ||
-          labels->shape[2] != q->shape[2])
-        return fail(RELATTN_ERR_INVALID_ARGUMENT, "labels must be [B, n, n]");
-      for (int i = 0; i < 3; ++i)
-        if (labels->stride[i] < 0)
-          return fail(RELATTN_ERR_INVALID_ARGUMENT, "labels stride[%d] < 0", i);
-      if (numel(labels) > 0) {
-        const int64_t n16 = (q->shape[2] + 15) / 16 * 16;
-        if (!labels->data) return fail(RELATTN_ERR_INVALID_ARGUMENT, "labels data is NULL");
-        if (labels->stride[2] != 1)
-          return fail(RELATTN_ERR_UNSUPPORTED, "labels: innermost dimension must be contiguous");
-        if (!aligned16(labels->data))
-          return fail(RELATTN_ERR_UNSUPPORTED, "labels: data pointer is not 16-byte aligned");
-        if (labels->stride[1] % 16 != 0 || labels->stride[0] % 16 != 0)
-          return fail(RELATTN_ERR_UNSUPPORTED, "labels: strides must be multiples of 16 bytes");
-        if (labels->stride[1] < n16)
-          return fail(RELATTN_ERR_UNSUPPORTED,
-                      "labels: row stride %lld is below n rounded up to 16 (%lld)",
-                      (long long)labels->stride[1], (long long)n16);
-      }
     } else if (ob->shape[1] != 2 * (int64_t)ob_window + 1) {
       return fail(RELATTN_ERR_INVALID_ARGUMENT, "bias: shape[1] must be 2*window+1 = %lld",
                   (long long)(2 * (int64_t)ob_window + 1));
@@ -311,8 +315,27 @@ int make_plan(const relattn_tensor* q, const relattn_tensor* k, const relattn_te
         return fail(RELATTN_ERR_INVALID_ARGUMENT, "%s must be [H or 1, d]", nm[t]);
     }
   }
-  if (wK && (st = check_table(wK, is_xl ? "R" : "wK", q, clip_k))) return st;
-  if (wV && (st = check_table(wV, "wV", q, clip_k))) return st;
+  int64_t n_labels = 0;  // graph mode: rows of the key/value tables
+  if (is_graph) {
+    const relattn_tensor* tabs[2] = {wK, wV};
+    const char* nm[2] = {"wK", "wV"};
+    for (int t = 0; t < 2; ++t) {
+      if (!tabs[t]) continue;
+      if ((st = check_view(tabs[t], nm[t], 3, true))) return st;
+      if (tabs[t]->dtype != q->dtype)
+        return fail(RELATTN_ERR_INVALID_ARGUMENT, "%s dtype differs from q", nm[t]);
+      if (!(tabs[t]->shape[0] == H || tabs[t]->shape[0] == 1) || tabs[t]->shape[2] != d)
+        return fail(RELATTN_ERR_INVALID_ARGUMENT, "%s must be [H or 1, NL, d]", nm[t]);
+      if (tabs[t]->shape[1] < 1 || tabs[t]->shape[1] > 256)
+        return fail(RELATTN_ERR_INVALID_ARGUMENT, "%s: NL = shape[1] must be in [1, 256]", nm[t]);
+      if (n_labels && tabs[t]->shape[1] != n_labels)
+        return fail(RELATTN_ERR_INVALID_ARGUMENT, "wK and wV must have the same NL");
+      n_labels = tabs[t]->shape[1];
+    }
+  } else {
+    if (wK && (st = check_table(wK, is_xl ? "R" : "wK", q, clip_k))) return st;
+    if (wV && (st = check_table(wV, "wV", q, clip_k))) return st;
+  }
   T5Buckets tb = {};
   if (is_t5) {
     if ((st = check_view(t5_bias, "t5_bias", 2, false))) return st;
@@ -328,7 +351,8 @@ int make_plan(const relattn_tensor* q, const relattn_tensor* k, const relattn_te
   Plan& P = *plan;
   P.bf16 = q->dtype == RELATTN_BF16;
   P.d = (int)d;
-  P.mode = is_lab ? relattn::kRelLabel
+  P.mode = is_graph ? relattn::kRelGraph
+          : is_lab ? relattn::kRelLabel
                   : (is_xl && d <= 64) ? relattn::kRelXL
                   : (is_ob && grid_m > 0) ? relattn::kRelGrid
                   : (is_t5 || is_ob) ? relattn::kRelT5
@@ -348,7 +372,10 @@ int make_plan(const relattn_tensor* q, const relattn_tensor* k, const relattn_te
   const bool causal = p.causal != 0;
   // Label rows any query can reach: offsets j - i lie in [-(n-1), n-1], or in
   // [-(n-1), 0] under the causal mask.
-  if (P.mode == relattn::kRelShaw) {
+  if (P.mode == relattn::kRelGraph) {
+    p.r_lo = 0;
+    p.nr = (int32_t)n_labels;
+  } else if (P.mode == relattn::kRelShaw) {
     const int64_t c = clip_k;
     const int64_t r_lo = std::max<int64_t>(0, c - (n - 1));
     const int64_t r_hi = causal ? c : std::min<int64_t>(2 * c, c + n - 1);
@@ -360,7 +387,11 @@ int make_plan(const relattn_tensor* q, const relattn_tensor* k, const relattn_te
   }
   p.t5_dist = is_t5 ? (int32_t)std::min<int64_t>(t5->max_distance, n - 1)
                     : ((is_ob && !is_lab) ? (int32_t)std::min<int64_t>(ob_window, n - 1) : 0);
-  if (is_lab) {
+  if (is_graph) {
+    p.lab = static_cast<const uint8_t*>(labels->data);
+    p.lab_sb = labels->stride[0];
+    p.lab_sn = labels->stride[1];
+  } else if (is_lab) {
     // the head's row of NL entries is loaded and indexed by each pair's label
     tb.nb = (int32_t)ob->shape[1];
     p.ob = 1;
@@ -421,7 +452,7 @@ int make_plan(const relattn_tensor* q, const relattn_tensor* k, const relattn_te
   auto vgpr_waves_per_cu = [&](int kblock, int waves) {
     if (d > 64) return 4 * ((P.bf16 && kblock == 32) ? 2 : 1);
     return 4 * ((P.bf16 && P.mode != relattn::kRelShaw && P.mode != relattn::kRelXL &&
-                 (d <= 32 || waves == 4)) ? 3 : 2);
+                 P.mode != relattn::kRelGraph && (d <= 32 || waves == 4)) ? 3 : 2);
   };
   // a workgroup whose lower half of waves already covers every query row
   // would leave the rest idle (short windows, e.g. 7 x 7 = 49 tokens)
@@ -1167,6 +1198,36 @@ int relattn_fwd_edge_bias(const relattn_tensor* q, const relattn_tensor* k,
   Plan plan;
   int st = make_plan(q, k, v, nullptr, nullptr, nullptr, nullptr, 0, scale, mask, out, &plan, true,
                      bias, 0, nullptr, nullptr, 0, labels);
+  if (st) return st;
+  if ((st = check_device())) return st;
+  if (plan.empty) return RELATTN_OK;
+  const int e = relattn::launch_fwd(plan.bf16, plan.d, plan.cfg, plan.mode, plan.has_wk,
+                                    plan.has_wv, plan.p, stream);
+  if (e != (int)hipSuccess)
+    return fail(RELATTN_ERR_LAUNCH_FAILED, "launch failed: %s", hipGetErrorString((hipError_t)e));
+  return RELATTN_OK;
+}
+
+int relattn_validate_edge_tables(const relattn_tensor* q, const relattn_tensor* k,
+                                 const relattn_tensor* v, const relattn_tensor* labels,
+                                 const relattn_tensor* wK, const relattn_tensor* wV, float scale,
+                                 const relattn_mask* mask, const relattn_tensor* out) {
+  g_last_error.clear();
+  if (!labels) return fail(RELATTN_ERR_INVALID_ARGUMENT, "labels is NULL");
+  Plan plan;
+  return make_plan(q, k, v, wK, wV, nullptr, nullptr, 0, scale, mask, out, &plan, false, nullptr,
+                   0, nullptr, nullptr, 0, labels);
+}
+
+int relattn_fwd_edge_tables(const relattn_tensor* q, const relattn_tensor* k,
+                            const relattn_tensor* v, const relattn_tensor* labels,
+                            const relattn_tensor* wK, const relattn_tensor* wV, float scale,
+                            const relattn_mask* mask, relattn_tensor* out, void* stream) {
+  g_last_error.clear();
+  if (!labels) return fail(RELATTN_ERR_INVALID_ARGUMENT, "labels is NULL");
+  Plan plan;
+  int st = make_plan(q, k, v, wK, wV, nullptr, nullptr, 0, scale, mask, out, &plan, true, nullptr,
+                     0, nullptr, nullptr, 0, labels);
   if (st) return st;
   if ((st = check_device())) return st;
   if (plan.empty) return RELATTN_OK;

@@ -86,8 +86,10 @@ struct FwdParams {
 // offset of raster tokens on an M x M window; kRelXL: Transformer-XL with the
 // relative logits formed per key tile (wk points at the position table's row of
 // distance 0, rows by distance i - j clamped to +-clip).
+// kRelGraph: the Shaw key/value tables indexed by a per-pair label (lab as for
+// kRelLabel; r_lo = 0, nr = NL table rows).
 enum RelMode { kRelNone = 0, kRelShaw = 1, kRelT5 = 2, kRelLabel = 3, kRelGrid = 4,
-               kRelXL = 5 };
+               kRelXL = 5, kRelGraph = 6 };
 
 // Where the w^V rows wait for the epilogue: their own LDS region (loaded in
 // the prologue), the first K/V ring stage the loop frees, or the free ring

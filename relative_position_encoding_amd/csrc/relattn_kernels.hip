@@ -52,6 +52,14 @@
 // (query, key) pair instead of a function of the offset.  Each wave's 32 rows
 // of a tile's label matrix travel with the K/V stage by LDS-DMA, and every
 // logit gathers its bias from the head's row of the table in LDS.
+//
+// Edge labels with key and value tables (graph mode): Eq. 4 and Eq. 3 with
+// a^K_ij = w^K[label], a^V_ij = w^V[label].  The relative logits are the Shaw
+// rows over the NL labels; the label tiles travel as in label mode.  A label
+// may hold any number of a row's keys, so the value term keeps a second LDS row
+// per query, S[i, r] = sum of p_ij over the keys of label r, accumulated with
+// LDS float atomics (both halves of a wave hold keys of the same query) and
+// rescaled with the row when the running max grows; the epilogue adds S W^V.
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
@@ -111,6 +119,7 @@ struct Layout {
   int wk_rows, wv_rows, lrs;       // tile rows, relative-row stride (floats)
   int wk_chunk;                    // w^K rows staged at a time (multiple of 32)
   int wv_chunk;                    // w^V rows staged at a time (multiple of 16)
+  int se, ses;                     // graph mode: weight-sum rows, their stride (floats)
 };
 
 // w^V staging (wv_mode): kWvResident gives the tile its own region, loaded
@@ -128,7 +137,8 @@ __host__ __device__ inline Layout make_layout(int mode, bool has_wk, bool has_wv
     off += (bytes + 15) & ~15;
     return at;
   };
-  const bool shaw = mode == kRelShaw, t5 = mode == kRelT5 || mode == kRelGrid;
+  const bool graph = mode == kRelGraph;
+  const bool shaw = mode == kRelShaw || graph, t5 = mode == kRelT5 || mode == kRelGrid;
   const bool lab = mode == kRelLabel, xlf = mode == kRelXL;
   L.wk_rows = dma_rows((nr + 31) & ~31, G::ROWB);
   L.wv_rows = dma_rows((nr + 15) & ~15, G::ROWB);
@@ -171,8 +181,12 @@ __host__ __device__ inline Layout make_layout(int mode, bool has_wk, bool has_wv
   }
   L.tbc = (t5 || lab) ? take(((t5_nb + 63) & ~63) * 4) : off;
   L.tb = t5 ? take((2 * t5_dist + 1 + G::PADL + G::PADU) * 4) : off;
-  // label mode: one BR x BC byte tile of labels per ring stage
-  L.lab = lab ? take(nstage * G::BR * BC) : off;
+  // label and graph modes: one BR x BC byte tile of labels per ring stage
+  L.lab = (lab || graph) ? take(nstage * G::BR * BC) : off;
+  // graph mode: per query, the weight sum of each label (odd stride: the lanes'
+  // rows start in different banks)
+  L.ses = nr | 1;
+  L.se = (graph && has_wv) ? take(G::BR * L.ses * 4) : off;
   L.total = off;
   return L;
 }
@@ -186,7 +200,8 @@ __host__ __device__ inline Layout make_layout(int mode, bool has_wk, bool has_wv
 template <int D, int NW, int MODE, bool BF16, int BC>
 __host__ __device__ constexpr int waves_per_simd() {
   return D > 64 ? ((BF16 && BC == 32) ? 2 : 1)
-                : ((BF16 && MODE != kRelShaw && MODE != kRelXL && (D <= 32 || NW == 4)) ? 3 : 2);
+                : ((BF16 && MODE != kRelShaw && MODE != kRelXL && MODE != kRelGraph &&
+                    (D <= 32 || NW == 4)) ? 3 : 2);
 }
 template <int D, int NW, int BC, bool BF16, int MODE, bool HAS_WK, bool HAS_WV>
 __global__ __launch_bounds__(64 * NW)
@@ -198,7 +213,8 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<D, NW, MODE, BF16, BC>()))) vo
   constexpr int NT = G::NT, NKB = G::NKB, DVB = G::DVB;
   constexpr int NKS = G::NKS, ROWB = G::ROWB, LPW = G::LPW;
   constexpr int KSTR = G::KSTR, SPAN = G::SPAN, PADL = G::PADL, PADU = G::PADU;
-  constexpr bool SHAW = (MODE == kRelShaw);
+  constexpr bool GRAPH = (MODE == kRelGraph);  // Shaw tables indexed by per-pair labels
+  constexpr bool SHAW = (MODE == kRelShaw) || GRAPH;
   constexpr bool GRID = (MODE == kRelGrid);  // the bias by 2-D offset
   constexpr bool T5 = (MODE == kRelT5) || GRID;
   constexpr bool LAB = (MODE == kRelLabel);
@@ -207,7 +223,7 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<D, NW, MODE, BF16, BC>()))) vo
   constexpr int NXB = G::NXB, XRS = G::XRS;
   // label mode: each wave loads its 32 rows of a tile's labels (32 x BC bytes)
   // with the stage, in 1 KB instructions
-  constexpr int LLPW = LAB ? BC / 32 : 0;
+  constexpr int LLPW = (LAB || GRAPH) ? BC / 32 : 0;
   constexpr int SLPW = LPW + LLPW;  // DMA instructions per wave per stage
   constexpr int LABB = G::BR * BC;  // label bytes per stage
 
@@ -261,7 +277,7 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<D, NW, MODE, BF16, BC>()))) vo
   const T* kg = reinterpret_cast<const T*>(p.k) + b * p.k_sb + h * p.k_sh;
   const T* vg = reinterpret_cast<const T*>(p.v) + b * p.v_sb + h * p.v_sh;
   T* og = reinterpret_cast<T*>(p.o) + b * p.o_sb + h * p.o_sh;
-  const uint8_t* labg = LAB ? p.lab + b * p.lab_sb : nullptr;
+  const uint8_t* labg = (LAB || GRAPH) ? p.lab + b * p.lab_sb : nullptr;
 
   // ---- LDS-DMA, oldest first: the Q tile, the relative tables, then the
   // first K/V stages.  (Q goes through LDS too: the compiler cannot count the
@@ -344,7 +360,7 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<D, NW, MODE, BF16, BC>()))) vo
       dma_stage<ROWB, NW, BC>(smem_lds + stage * G::STAGEB, kg, p.k_sn, vg, p.v_sn, tile * BC,
                               kv_last, wave, lane);
     }
-    if constexpr (LAB) {
+    if constexpr (LAB || GRAPH) {
       // this wave's rows of the tile's labels, stored chunk-major: the 16-byte
       // chunk c (keys 16c ..) of row r at slot 32 c + r, so that the 32 rows
       // of one chunk are 512 contiguous bytes.  Rows past n read row n - 1;
@@ -473,6 +489,12 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<D, NW, MODE, BF16, BC>()))) vo
     // the head's bias row in log2 units, gathered by label in the loop
     for (int x = tid; x < p.t5.nb; x += NT) TBC[x] *= kLog2e;
     block_sync();
+  }
+
+  // graph mode: this lane's half of its query's weight-sum row starts at zero
+  float* myS = reinterpret_cast<float*>(smem + lay.se) + qrow * lay.ses;
+  if constexpr (GRAPH && HAS_WV) {
+    for (int r = hh; r < p.nr; r += 2) myS[r] = 0.f;
   }
 
   // window of offsets delta = j - i covered by the relative row, and the
@@ -608,15 +630,41 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<D, NW, MODE, BF16, BC>()))) vo
     const int kofs = j0 + hoff - qi;
     const int dmin = j0 - (wq0 + 31), dmax = j0 + BC - 1 - wq0;
     const bool all_lo = dmax <= -band, all_hi = dmin >= band;  // wave-uniform
-    const bool off_band = (SHAW || T5) && (all_lo || all_hi);
+    const bool off_band = ((SHAW && !GRAPH) || T5) && (all_lo || all_hi);
     // Per-element masking: key-length cuts, and causal cuts unless the
     // gathered relative logits already carry them (-inf past offset 0; not
     // so for labels).
     const bool causal_cut = p.causal && j0 + BC - 1 > wq0;
     const bool need_mask =
-        (j0 + BC > kv_len) || (causal_cut && (LAB || XLF || !(GATHER && !off_band)));
+        (j0 + BC > kv_len) ||
+        (causal_cut && (LAB || XLF || GRAPH || !(GATHER && !off_band)));
     // visible iff its key offset within the lane's keys is <= lim
     const int lim = min(kv_len - 1 - j0 - hoff, p.causal ? -kofs : 0x3fffffff);
+
+    // graph mode: the lane's label chunks of the tile (two 16-key chunks per
+    // 32-key block), for the key-table gather and the value-term sums
+    uint4 glw[GRAPH ? NKB : 1][2];
+    if constexpr (GRAPH) {
+      const unsigned char* labt = smem + lay.lab + st_cur * LABB + wave * (32 * BC);
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int g = 0; g < 2; ++g)
+          glw[kb][g] = *reinterpret_cast<const uint4*>(labt + ((2 * kb + g) * 32 + ql) * 16);
+    }
+    // label of register (kb, 8g + e), clamped to the table
+    auto glabel = [&](int kb, int g, int e) __attribute__((always_inline)) {
+      const uint4 w4 = glw[GRAPH ? kb : 0][g];
+      uint32_t byte;
+      if constexpr (BF16) {
+        const uint32_t dw = (e < 4) ? (hh ? w4.z : w4.x) : (hh ? w4.w : w4.y);
+        byte = (dw >> (8 * (e & 3))) & 0xffu;
+      } else {
+        const uint32_t dw = (e < 2) ? w4.x : (e < 4) ? w4.y : (e < 6) ? w4.z : w4.w;
+        byte = (dw >> (8 * (hh + 2 * (e & 1)))) & 0xffu;
+      }
+      return min((int)byte, p.nr - 1);
+    };
 
     // logits (log2 units) of the tile, masked to -inf where invisible
     float tmax = kNegInf;
@@ -667,6 +715,14 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<D, NW, MODE, BF16, BC>()))) vo
               rv[kb][8 * g + e] = TBC[min((int)byte, nbm)];
             }
           }
+      } else if constexpr (GRAPH) {
+        // graph mode: the relative logit of each key's label
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int g = 0; g < 2; ++g)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) rv[kb][8 * g + e] = myLE[PADL + glabel(kb, g, e)];
       } else if constexpr (XLF) {
         // fused XL: key group (kb, g) starts at position hoff + 32 kb + 16 g
         // + 31 - ql of the wave's block (offset kofs + 32 kb + 16 g - omin)
@@ -715,7 +771,7 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<D, NW, MODE, BF16, BC>()))) vo
         finish(rv, std::false_type{});
       }
     }
-    if constexpr (SHAW && HAS_WV) {
+    if constexpr (SHAW && HAS_WV && !GRAPH) {
       // The value term needs the final logit of every key whose label holds
       // that key alone.  Each group of 8 that touches such an offset is stored
       // whole at its own label entries (PADL + delta - dlo onwards).  A lane's
@@ -750,6 +806,11 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<D, NW, MODE, BF16, BC>()))) vo
       if constexpr (SHAW && HAS_WV) thi *= alpha;
 #pragma unroll
       for (int mb = 0; mb < DVB; ++mb) oacc[mb] *= alpha;
+      if constexpr (GRAPH && HAS_WV) {
+        // the weight sums follow the row's scale (this lane's half of the row)
+        if (grow)
+          for (int r = hh; r < p.nr; r += 2) myS[r] *= alpha;
+      }
     }
     const float m_use = (m_run == kNegInf) ? 0.f : m_run;
 
@@ -764,7 +825,19 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<D, NW, MODE, BF16, BC>()))) vo
       }
     }
     l_part += psum;
-    if constexpr (SHAW && HAS_WV) {
+    if constexpr (GRAPH && HAS_WV) {
+      // each key's weight into its label's sum (both halves of the wave add to
+      // the same row: LDS atomics)
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int g = 0; g < 2; ++g)
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            __hip_atomic_fetch_add(myS + glabel(kb, g, e), s[kb][8 * g + e], __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+    if constexpr (SHAW && HAS_WV && !GRAPH) {
       // +c bucket (keys at offset >= c); empty under the causal mask
       if (!p.causal && !all_lo) {
         if (dmin >= hi_from) {
@@ -877,26 +950,35 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<D, NW, MODE, BF16, BC>()))) vo
         wv_off = wv_stage * G::STAGEB;
       }
       float w[8];
+      if constexpr (GRAPH) {
+        // graph mode: the weight sums, already at the row's final scale
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int idx = label_of(ls, e);
-        const float x = myLE[PADL + idx];  // inside the row for every step
-        const bool ok = any_in && (unsigned)(idx - i_in_lo) <= i_in_w;
-        w[e] = ok ? fast_exp2(x - m_fin) : 0.f;
-        isum += w[e];
-      }
-      if (it + 1 == nls) {
-        // every single-key weight is in isum now
-        tlo_all = fmaxf(l - halves_sum(isum) - thi_all, 0.f);
-        if (p.r_lo == 0 && hh == 0) w[0] += tlo_all;  // label index 0 is -c
-      }
-      if (!p.causal) {
+        for (int e = 0; e < 8; ++e) {
+          const int idx = label_of(ls, e);
+          w[e] = (q_ok && idx < p.nr) ? myS[idx] : 0.f;
+        }
+      } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) w[e] += (label_of(ls, e) == i_thi) ? thi_all : 0.f;
-      }
-      if (!q_ok) {
+        for (int e = 0; e < 8; ++e) {
+          const int idx = label_of(ls, e);
+          const float x = myLE[PADL + idx];  // inside the row for every step
+          const bool ok = any_in && (unsigned)(idx - i_in_lo) <= i_in_w;
+          w[e] = ok ? fast_exp2(x - m_fin) : 0.f;
+          isum += w[e];
+        }
+        if (it + 1 == nls) {
+          // every single-key weight is in isum now
+          tlo_all = fmaxf(l - halves_sum(isum) - thi_all, 0.f);
+          if (p.r_lo == 0 && hh == 0) w[0] += tlo_all;  // label index 0 is -c
+        }
+        if (!p.causal) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) w[e] = 0.f;
+          for (int e = 0; e < 8; ++e) w[e] += (label_of(ls, e) == i_thi) ? thi_all : 0.f;
+        }
+        if (!q_ok) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) w[e] = 0.f;
+        }
       }
       const unsigned char* wvt = smem + wv_off;
       if constexpr (BF16) {
@@ -971,7 +1053,8 @@ static size_t lds_bytes_t(RelMode mode, bool has_wk, bool has_wv, int nr, int ns
   using G = Geo<BF16, D, NW, BC>;
   const Layout L = make_layout<BF16, D, NW, BC>(mode, has_wk, has_wv, nr, nstage, t5_dist, t5_nb,
                                                 wv_mode);
-  if (mode == kRelShaw && has_wv && wv_mode == kWvRing && L.wv_rows * G::ROWB > G::STAGEB)
+  if ((mode == kRelShaw || mode == kRelGraph) && has_wv && wv_mode == kWvRing &&
+      L.wv_rows * G::ROWB > G::STAGEB)
     return ~(size_t)0;  // the w^V tile does not fit one ring stage
   return (size_t)L.total;
 }
@@ -1028,6 +1111,12 @@ static int launch_mode(RelMode mode, bool has_wk, bool has_wv, const FwdParams& 
   if (mode == kRelLabel) return launch_t<D, NW, BC, BF16, kRelLabel, false, false>(p, stream);
   if (mode == kRelXL) {
     if constexpr (D <= 64) return launch_t<D, NW, BC, BF16, kRelXL, false, false>(p, stream);
+    return (int)hipErrorInvalidValue;
+  }
+  if (mode == kRelGraph) {
+    if (has_wk && has_wv) return launch_t<D, NW, BC, BF16, kRelGraph, true, true>(p, stream);
+    if (has_wk) return launch_t<D, NW, BC, BF16, kRelGraph, true, false>(p, stream);
+    if (has_wv) return launch_t<D, NW, BC, BF16, kRelGraph, false, true>(p, stream);
     return (int)hipErrorInvalidValue;
   }
   if (mode == kRelShaw) {

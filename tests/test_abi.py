@@ -350,3 +350,26 @@ def test_edge_bias_validation(ra):
     # empty problems validate
     q0, k0, v0 = qkv(0, H, n)
     assert ra.validate_edge_bias(q0, k0, v0, ra.edge_label_buffer(0, n), bias) == ra.OK
+
+
+def test_edge_tables_validation(ra):
+    """Table checks of relattn_validate_edge_tables (label layout as for the bias)."""
+    B, H, n, d = 2, 3, 40, 64
+    q, k, v = qkv(B, H, n, d)
+    lab = ra.edge_label_buffer(B, n)
+    wK, wV = T(H, 9, d), T(1, 9, d)
+    assert ra.validate_edge_tables(q, k, v, lab, wK, wV) == ra.OK
+    assert ra.validate_edge_tables(q, k, v, lab, wK, None, causal=True) == ra.OK
+    assert ra.validate_edge_tables(q, k, v, lab, None, wV) == ra.OK
+    assert ra.validate_edge_tables(q, k, v, lab, T(H, 256, d), None) == ra.OK
+    assert ra.validate_edge_tables(q, k, v, lab, None, None) == ra.INVALID_ARGUMENT
+    assert ra.validate_edge_tables(q, k, v, lab, wK, T(H, 8, d)) == ra.INVALID_ARGUMENT
+    assert ra.validate_edge_tables(q, k, v, lab, T(H, 257, d), None) == ra.INVALID_ARGUMENT
+    assert ra.validate_edge_tables(q, k, v, lab, T(H, 0, d), None) == ra.INVALID_ARGUMENT
+    assert ra.validate_edge_tables(q, k, v, lab, T(2, 9, d), None) == ra.INVALID_ARGUMENT
+    assert ra.validate_edge_tables(q, k, v, lab, T(H, 9, 32), None) == ra.INVALID_ARGUMENT
+    assert ra.validate_edge_tables(q, k, v, lab, T(H, 9, d, dtype=torch.float32),
+                                   None) == ra.INVALID_ARGUMENT
+    assert ra.validate_edge_tables(q, k, v, lab.to(torch.int32), wK, None) == ra.INVALID_ARGUMENT
+    tight = torch.zeros(B * n * n + 16, dtype=torch.uint8).as_strided((B, n, n), (n * n, n, 1))
+    assert ra.validate_edge_tables(q, k, v, tight, wK, None) == ra.UNSUPPORTED

@@ -334,6 +334,7 @@ class EdgeWorkload:
     n: int
     d: int
     labels: int         # NL: label vocabulary
+    tables: bool = False  # key and value tables [H, NL, d] instead of a bias table
     causal: bool = False
     dtype: torch.dtype = torch.bfloat16
     qkv_std: float = 1.0
@@ -350,13 +351,19 @@ EDGE_WORKLOADS = {
         description="per-pair edge labels: B16 H16 n256 d64, 64 labels uniform per pair, "
                     "bias table [16, 64], no mask",
         batch=16, heads=16, n=256, d=64, labels=64),
+    "edge_kv": EdgeWorkload(
+        name="edge_kv", config_id=10,
+        description="relation-aware attention over a labeled graph: B16 H16 n256 d64, 64 "
+                    "labels uniform per pair, key+value tables [16, 64, 64], no mask",
+        batch=16, heads=16, n=256, d=64, labels=64, tables=True, table_std=0.02),
 }
 
 
 def make_edge_inputs(w: EdgeWorkload | str, *, batch=None, n=None, seed=None) -> dict:
     """CPU tensors for an edge-label workload, drawn in this order: q, k, v
-    [B, H, n, d], the bias table [H, NL] fp32 and the labels [B, n, n] (int64,
-    uniform in [0, NL))."""
+    [B, H, n, d], the bias table [H, NL] fp32 (or the key and value tables [H,
+    NL, d] in the workload dtype) and the labels [B, n, n] (int64, uniform in
+    [0, NL))."""
     if isinstance(w, str):
         w = EDGE_WORKLOADS[w]
     B, H, n = batch or w.batch, w.heads, n or w.n
@@ -368,6 +375,12 @@ def make_edge_inputs(w: EdgeWorkload | str, *, batch=None, n=None, seed=None) ->
     q = normal((B, H, n, w.d), w.qkv_std)
     k = normal((B, H, n, w.d), w.qkv_std)
     v = normal((B, H, n, w.d), w.qkv_std)
+    if w.tables:
+        wK = normal((H, w.labels, w.d), w.table_std)
+        wV = normal((H, w.labels, w.d), w.table_std)
+        labels = torch.randint(0, w.labels, (B, n, n), generator=g)
+        return {"q": q.to(w.dtype), "k": k.to(w.dtype), "v": v.to(w.dtype),
+                "wK": wK.to(w.dtype), "wV": wV.to(w.dtype), "labels": labels}
     bias = normal((H, w.labels), w.table_std)
     labels = torch.randint(0, w.labels, (B, n, n), generator=g)
     return {"q": q.to(w.dtype), "k": k.to(w.dtype), "v": v.to(w.dtype), "bias": bias,
