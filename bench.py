@@ -636,21 +636,29 @@ def grid_report(ra, steps):
 # ---------------------------------------------------------------------------
 
 def edge_work(w):
-    """(flops, bytes) of one call: 4*d per pair (no mask: every key visible);
-    bytes: q, k, v, out once, the table once and the label matrix once (one
-    byte per pair of a batch entry, shared by its heads)."""
+    """(flops, bytes) of one call: 4*d per pair (no mask: every key visible),
+    plus with key and value tables 2*d per (query, label) for q.w^K and for the
+    weight sums times W^V; bytes: q, k, v, out once, the table(s) once and the
+    label matrix once (one byte per pair of a batch entry, shared by its
+    heads)."""
     pairs = w.batch * w.heads * w.n * w.n
-    return 4.0 * w.d * pairs, 4.0 * w.batch * w.heads * w.n * w.d * w.dtype.itemsize + \
-        w.heads * w.labels * 4 + w.batch * w.n * w.n
+    flops = 4.0 * w.d * pairs
+    nbytes = 4.0 * w.batch * w.heads * w.n * w.d * w.dtype.itemsize + w.batch * w.n * w.n
+    if w.tables:
+        flops += 2 * 2.0 * w.d * w.batch * w.heads * w.n * w.labels
+        nbytes += 2 * w.heads * w.labels * w.d * w.dtype.itemsize
+    else:
+        nbytes += w.heads * w.labels * 4
+    return flops, nbytes
 
 
-def time_edge(ra, steps, warmup, hot=False, reps=5):
+def time_edge(ra, steps, warmup, hot=False, reps=5, name="edge"):
     import statistics
     import torch
     import workloads
     lib = ra._load()
     stream = torch.cuda.Stream()
-    w = workloads.EDGE_WORKLOADS["edge"]
+    w = workloads.EDGE_WORKLOADS[name]
     x = workloads.make_edge_inputs(w)
     flops, nbytes = edge_work(w)
     copies = 1 if hot else max(1, min(16, int(2 * LLC_BYTES // nbytes) + 1))
@@ -660,11 +668,15 @@ def time_edge(ra, steps, warmup, hot=False, reps=5):
         lab = ra.edge_label_buffer(w.batch, w.n, "cuda")
         lab.copy_(x["labels"].to(torch.uint8))
         out = torch.empty_like(g["q"])
-        args, kp = ra._edge_args(g["q"], g["k"], g["v"], lab, g["bias"], w.causal, None, None,
-                                 out)
+        if w.tables:
+            args, kp = ra._edge_args(g["q"], g["k"], g["v"], lab, None, w.causal, None, None,
+                                     out, (g["wK"], g["wV"]))
+        else:
+            args, kp = ra._edge_args(g["q"], g["k"], g["v"], lab, g["bias"], w.causal, None,
+                                     None, out)
         calls.append(args + [ctypes.c_void_p(stream.cuda_stream)])
         keep += [g, lab, out, kp]
-    fn = lib.relattn_fwd_edge_bias
+    fn = lib.relattn_fwd_edge_tables if w.tables else lib.relattn_fwd_edge_bias
     times = []
     with torch.cuda.stream(stream):
         for s_ in range(warmup):
@@ -687,11 +699,11 @@ def time_edge(ra, steps, warmup, hot=False, reps=5):
             "alg_gflop": flops / 1e9, "alg_mbytes": nbytes / 1e6, "input_copies": copies}
 
 
-def edge_report(ra, steps):
+def edge_report(ra, steps, name="edge"):
     import workloads
-    w = workloads.EDGE_WORKLOADS["edge"]
-    cold = time_edge(ra, steps, 10)
-    hot = time_edge(ra, steps, 10, hot=True)
+    w = workloads.EDGE_WORKLOADS[name]
+    cold = time_edge(ra, steps, 10, name=name)
+    hot = time_edge(ra, steps, 10, hot=True, name=name)
     flops, nbytes = cold["alg_gflop"] * 1e9, cold["alg_mbytes"] * 1e6
     bound = bound_of(flops, nbytes, "bf16")
     sec = cold["ms_per_step"] * 1e-3
@@ -699,7 +711,7 @@ def edge_report(ra, steps):
         ach, peak, unit = nbytes / sec / 1e9, PEAK_HBM_GBS, "GB/s"
     else:
         ach, peak, unit = flops / sec / 1e12, PEAK_TFLOPS["bf16"], "TFLOP/s"
-    tr = traffic_per_launch("edge")
+    tr = traffic_per_launch(name)
     return {"workload": w.description, "ms_per_step": round(cold["ms_per_step"], 5),
             "tflops": round(cold["tflops"], 3),
             "roofline": {"bound": bound, "achieved": round(ach, 2), "peak": peak, "unit": unit,
@@ -926,6 +938,8 @@ def main():
                     help="time the 2-D window (Swin) workload only and print its figures")
     ap.add_argument("--edge-only", action="store_true",
                     help="time the edge-label workload only and print its figures")
+    ap.add_argument("--edge-tables-only", action="store_true",
+                    help="time the edge-label workload with key and value tables only")
     a = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if a.gpus != 1 or world != 1:
@@ -960,6 +974,9 @@ def main():
         return
     if a.edge_only:
         print(json.dumps({"edge_bias": edge_report(ra, max(50, a.steps // 5))}))
+        return
+    if a.edge_tables_only:
+        print(json.dumps({"edge_tables": edge_report(ra, max(50, a.steps // 5), "edge_kv")}))
         return
 
     if gpu is not None and not gpu.get("name"):
@@ -1026,6 +1043,7 @@ def main():
         line["xl"] = xl_report(ra, max(50, a.steps // 5))
         line["grid_bias"] = grid_report(ra, max(50, a.steps // 5))
         line["edge_bias"] = edge_report(ra, max(50, a.steps // 5))
+        line["edge_tables"] = edge_report(ra, max(50, a.steps // 5), "edge_kv")
     if not a.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w)
         if not a.only:

@@ -57,9 +57,10 @@
 // a^K_ij = w^K[label], a^V_ij = w^V[label].  The relative logits are the Shaw
 // rows over the NL labels; the label tiles travel as in label mode.  A label
 // may hold any number of a row's keys, so the value term keeps a second LDS row
-// per query, S[i, r] = sum of p_ij over the keys of label r, accumulated with
-// LDS float atomics (both halves of a wave hold keys of the same query) and
-// rescaled with the row when the running max grows; the epilogue adds S W^V.
+// per query and wave half, S[i, r] = sum of p_ij over the half's keys of label r
+// (each half owns its row, so plain LDS read-modify-writes suffice: LDS float
+// atomics measured about three times slower per call here), rescaled with the
+// row when the running max grows; the epilogue adds (S_0 + S_1) W^V.
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
@@ -183,10 +184,10 @@ __host__ __device__ inline Layout make_layout(int mode, bool has_wk, bool has_wv
   L.tb = t5 ? take((2 * t5_dist + 1 + G::PADL + G::PADU) * 4) : off;
   // label and graph modes: one BR x BC byte tile of labels per ring stage
   L.lab = (lab || graph) ? take(nstage * G::BR * BC) : off;
-  // graph mode: per query, the weight sum of each label (odd stride: the lanes'
-  // rows start in different banks)
+  // graph mode: per query and wave half, the weight sum of each label (odd
+  // stride: the lanes' rows start in different banks)
   L.ses = nr | 1;
-  L.se = (graph && has_wv) ? take(G::BR * L.ses * 4) : off;
+  L.se = (graph && has_wv) ? take(2 * G::BR * L.ses * 4) : off;
   L.total = off;
   return L;
 }
@@ -491,10 +492,10 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<D, NW, MODE, BF16, BC>()))) vo
     block_sync();
   }
 
-  // graph mode: this lane's half of its query's weight-sum row starts at zero
-  float* myS = reinterpret_cast<float*>(smem + lay.se) + qrow * lay.ses;
+  // graph mode: this lane's weight-sum row (row 2 qrow + hh) starts at zero
+  float* myS = reinterpret_cast<float*>(smem + lay.se) + (2 * qrow + hh) * lay.ses;
   if constexpr (GRAPH && HAS_WV) {
-    for (int r = hh; r < p.nr; r += 2) myS[r] = 0.f;
+    for (int r = 0; r < p.nr; ++r) myS[r] = 0.f;
   }
 
   // window of offsets delta = j - i covered by the relative row, and the
@@ -807,9 +808,9 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<D, NW, MODE, BF16, BC>()))) vo
 #pragma unroll
       for (int mb = 0; mb < DVB; ++mb) oacc[mb] *= alpha;
       if constexpr (GRAPH && HAS_WV) {
-        // the weight sums follow the row's scale (this lane's half of the row)
+        // the weight sums follow the row's scale
         if (grow)
-          for (int r = hh; r < p.nr; r += 2) myS[r] *= alpha;
+          for (int r = 0; r < p.nr; ++r) myS[r] *= alpha;
       }
     }
     const float m_use = (m_run == kNegInf) ? 0.f : m_run;
@@ -826,16 +827,13 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<D, NW, MODE, BF16, BC>()))) vo
     }
     l_part += psum;
     if constexpr (GRAPH && HAS_WV) {
-      // each key's weight into its label's sum (both halves of the wave add to
-      // the same row: LDS atomics)
+      // each key's weight into its label's sum, in this lane's own row
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int g = 0; g < 2; ++g)
 #pragma unroll
-          for (int e = 0; e < 8; ++e)
-            __hip_atomic_fetch_add(myS + glabel(kb, g, e), s[kb][8 * g + e], __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_WORKGROUP);
+          for (int e = 0; e < 8; ++e) myS[glabel(kb, g, e)] += s[kb][8 * g + e];
     }
     if constexpr (SHAW && HAS_WV && !GRAPH) {
       // +c bucket (keys at offset >= c); empty under the causal mask
@@ -951,11 +949,13 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<D, NW, MODE, BF16, BC>()))) vo
       }
       float w[8];
       if constexpr (GRAPH) {
-        // graph mode: the weight sums, already at the row's final scale
+        // graph mode: the two halves' weight sums, already at the row's final
+        // scale
+        const float* rowS = reinterpret_cast<const float*>(smem + lay.se) + 2 * qrow * lay.ses;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int idx = label_of(ls, e);
-          w[e] = (q_ok && idx < p.nr) ? myS[idx] : 0.f;
+          w[e] = (q_ok && idx < p.nr) ? rowS[idx] + rowS[lay.ses + idx] : 0.f;
         }
       } else {
 #pragma unroll
