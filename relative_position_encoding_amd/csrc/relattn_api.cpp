@@ -490,6 +490,9 @@ int make_plan(const relattn_tensor* q, const relattn_tensor* k, const relattn_te
                   "scalar-bias offset window 2*min(max_distance or window, n-1)+1 = %d "
                   "does not fit on chip",
                   2 * p.t5_dist + 1);
+    if (P.mode == relattn::kRelGraph)
+      return fail(RELATTN_ERR_UNSUPPORTED, "rows of %d labels per query do not fit on chip",
+                  p.nr);
     return fail(RELATTN_ERR_UNSUPPORTED,
                 "label window of %d rows (2*clip_k+1 clipped to 2n-1) does not fit on chip",
                 p.nr);
