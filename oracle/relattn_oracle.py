@@ -83,6 +83,7 @@ __all__ = [
     "relattn_decode",
     "t5_decode",
     "offset_bias_attention",
+    "offset_bias_decode",
     "relattn_backward",
     "t5_backward",
     "offset_bias_backward",
@@ -492,6 +493,33 @@ def offset_bias_attention(q, k, v, bias, window: int, scale=None, causal: bool =
             row = bias[0 if bias.shape[0] == 1 else h]
             e = s * (q[b, h] @ k[b, h].T) + row[R]
             z[b, h] = _masked_softmax_rows(e, ok) @ v[b, h]
+    return z
+
+
+def offset_bias_decode(q, k, v, bias, window: int, scale=None, cache_lens=None):
+    """The offset-bias attention (ALiBi as a table) for the newest Tq positions
+    over a cache: query t of batch b sits at position len_b - Tq + t and sees
+    keys 0 .. that position; e_j = scale * q.k_j + bias[h', clip(j - i, W) + W].
+    scale defaults to 1/sqrt(d); positions and visibility as in
+    ``relattn_decode``."""
+    q, k, v = to_f64(q), to_f64(k), to_f64(v)
+    bias = to_f64(bias)
+    B, H, Tq, d = q.shape
+    L = k.shape[2]
+    s = _default_scale(d, scale)
+    pos = _decode_positions(Tq, L, cache_lens, B)
+    z = np.zeros((B, H, Tq, v.shape[-1]))
+    for b in range(B):
+        for h in range(H):
+            row = bias[0 if bias.shape[0] == 1 else h]
+            for t in range(Tq):
+                i = pos[b][t]
+                if i < 0:
+                    continue
+                e = np.array([s * float(q[b, h, t] @ k[b, h, j]) + row[clip(j - i, window) + window]
+                              for j in range(i + 1)])
+                w = np.exp(e - e.max())
+                z[b, h, t] = (w / w.sum()) @ v[b, h, :i + 1]
     return z
 
 

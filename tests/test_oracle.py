@@ -964,3 +964,28 @@ def test_edge_relattn_two_tokens_closed_form():
         want = [(1 - a1) * (v[0, 0, 0, c] + wV[0, E[0, i, 0], c])
                 + a1 * (v[0, 0, 1, c] + wV[0, E[0, i, 1], c]) for c in range(2)]
         np.testing.assert_allclose(z[i], want, rtol=0, atol=1e-14)
+
+
+@pytest.mark.parametrize("window,shared", [(3, False), (40, True)])
+def test_offset_bias_decode_matches_forward_rows(window, shared):
+    """Decoding with an offset table reproduces the causal offset-bias
+    attention's rows at the decoded positions (per-head and shared rows, a window
+    that clips and one that does not)."""
+    q_full, k, v, lens, Tq = _decode_case(70, L=40)
+    B, H, L, d = q_full.shape
+    bias = rnd((1 if shared else H, 2 * window + 1), 71)
+    q = np.zeros((B, H, Tq, d))
+    for b in range(B):
+        for t in range(Tq):
+            i = lens[b] - Tq + t
+            if i >= 0:
+                q[b, :, t] = q_full[b, :, i]
+    z = oracle.offset_bias_decode(q, k, v, bias, window, cache_lens=lens)
+    full = oracle.offset_bias_attention(q_full, k, v, bias, window, causal=True, key_lens=lens)
+    for b in range(B):
+        for t in range(Tq):
+            i = lens[b] - Tq + t
+            if i >= 0:
+                np.testing.assert_allclose(z[b, :, t], full[b, :, i], rtol=0, atol=1e-12)
+            else:
+                assert np.all(z[b, :, t] == 0.0)
