@@ -320,6 +320,33 @@ int relattn_decode(const relattn_tensor* q, const relattn_tensor* k,
                    const int32_t* cache_lens, relattn_tensor* out,
                    void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * relattn_decode_offset_bias: incremental decoding with a scalar bias by clipped
+ * offset (survey page "Relative position embeddings", section "Placement in
+ * the taxonomy": ALiBi is the bias -m_h |delta| written as such a table):
+ *
+ *       e_j = scale * q.k_j + bias[h', clip(j - i, window) + window],  j <= i
+ *
+ *   q, k, v, out, cache_lens, workspace, stream : as for relattn_decode (query t
+ *                  of batch b at position len_b - Tq + t over keys 0 .. that
+ *                  position).
+ *   bias         : [Hb, 2*window + 1] F32, Hb in {H, 1}; window >= 0.
+ *   scale        : multiplies q.k only; <= 0 picks 1/sqrt(d).
+ * relattn_decode_offset_bias_workspace_size gives the workspace bytes.  Errors
+ * as for relattn_decode.  No value term.
+ */
+int relattn_decode_offset_bias(const relattn_tensor* q, const relattn_tensor* k,
+                               const relattn_tensor* v, const relattn_tensor* bias, int32_t window,
+                               float scale, const int32_t* cache_lens, relattn_tensor* out,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/* relattn_decode_offset_bias_workspace_size: host only; *bytes receives the
+ * workspace relattn_decode_offset_bias needs for these shapes (0 when none). */
+int relattn_decode_offset_bias_workspace_size(const relattn_tensor* q, const relattn_tensor* k,
+                                              const relattn_tensor* v, const relattn_tensor* bias,
+                                              int32_t window, float scale,
+                                              const relattn_tensor* out, size_t* bytes);
+
 /* relattn_decode_workspace_size: the argument checks of relattn_decode (host
  * only: no HIP call, works without a GPU) and the workspace it needs, written
  * to *bytes.  The size depends only on the shapes, dtype and tables. */

@@ -584,7 +584,8 @@ size_t align16(size_t x) { return (x + 15) & ~size_t(15); }
 int make_dec_plan(const relattn_tensor* q, const relattn_tensor* k, const relattn_tensor* v,
                   const relattn_tensor* wK, const relattn_tensor* wV,
                   const relattn_tensor* t5_bias, const relattn_t5_params* t5, int32_t clip_k,
-                  float scale, const relattn_tensor* out, DecPlan* plan, bool want_t5_table) {
+                  float scale, const relattn_tensor* out, DecPlan* plan, bool want_t5_table,
+                  const relattn_tensor* ob = nullptr, int32_t ob_window = 0) {
   int st;
   if ((st = check_view(q, "q", 4, true))) return st;
   if ((st = check_view(k, "k", 4, true))) return st;
@@ -637,7 +638,23 @@ int make_dec_plan(const relattn_tensor* q, const relattn_tensor* k, const relatt
   DecPlan& P = *plan;
   P.bf16 = q->dtype == RELATTN_BF16;
   P.d = (int)d;
-  P.mode = is_t5 ? relattn::kRelT5 : ((wK || wV) ? relattn::kRelShaw : relattn::kRelNone);
+  const bool is_ob = ob != nullptr;  // scalar bias by clipped offset
+  if (is_ob) {
+    if (wK || wV || is_t5)
+      return fail(RELATTN_ERR_INVALID_ARGUMENT, "an offset bias excludes the other tables");
+    if ((st = check_view(ob, "bias", 2, false))) return st;
+    if (ob->dtype != RELATTN_F32) return fail(RELATTN_ERR_INVALID_ARGUMENT, "bias must be F32");
+    if (ob_window < 0) return fail(RELATTN_ERR_INVALID_ARGUMENT, "window must be >= 0");
+    if ((int64_t)ob_window > kMaxSeq) return fail(RELATTN_ERR_UNSUPPORTED, "window exceeds 2^30");
+    if (!(ob->shape[0] == q->shape[1] || ob->shape[0] == 1))
+      return fail(RELATTN_ERR_INVALID_ARGUMENT, "bias: shape[0] must be H (%lld) or 1",
+                  (long long)q->shape[1]);
+    if (ob->shape[1] != 2 * (int64_t)ob_window + 1)
+      return fail(RELATTN_ERR_INVALID_ARGUMENT, "bias: shape[1] must be 2*window+1 = %lld",
+                  (long long)(2 * (int64_t)ob_window + 1));
+  }
+  P.mode = (is_t5 || is_ob) ? relattn::kRelT5
+                            : ((wK || wV) ? relattn::kRelShaw : relattn::kRelNone);
   P.has_wk = wK != nullptr;
   P.has_wv = wV != nullptr;
   P.empty = (B == 0 || H == 0 || Tq == 0);
@@ -670,7 +687,7 @@ int make_dec_plan(const relattn_tensor* q, const relattn_tensor* k, const relatt
   p.H = (int32_t)H;
   p.Tq = (int32_t)Tq;
   p.L = (int32_t)L;
-  p.clip = is_t5 ? 0 : clip_k;
+  p.clip = (is_t5 || is_ob) ? 0 : clip_k;
   p.nband = (int32_t)nband;
   p.nch = (int32_t)nch;
   p.cps = (int32_t)cps;
@@ -679,6 +696,14 @@ int make_dec_plan(const relattn_tensor* q, const relattn_tensor* k, const relatt
   p.t5 = tb;
   const float s = scale > 0.f ? scale : (is_t5 ? 1.f : 1.f / std::sqrt((float)d));
   p.scale_log2 = s * 1.4426950408889634f;
+  if (is_ob) {
+    // the bias of offset delta is entry clip(delta, W) + W of the head's row
+    p.ob = 1;
+    p.ob_w = ob_window;
+    p.t5_bias = static_cast<const float*>(ob->data);
+    p.tb_sb = ob->stride[1];
+    p.tb_sh = ob->shape[0] == 1 ? 0 : ob->stride[0];
+  }
   p.q = q->data;
   p.k = k->data;
   p.v = v->data;
@@ -1282,6 +1307,55 @@ int relattn_decode(const relattn_tensor* q, const relattn_tensor* k, const relat
   g_last_error.clear();
   DecPlan plan;
   int st = make_dec_plan(q, k, v, wK, wV, t5_bias, t5, clip_k, scale, out, &plan, true);
+  if (st) return st;
+  if (cache_lens && (reinterpret_cast<uintptr_t>(cache_lens) & 3u))
+    return fail(RELATTN_ERR_INVALID_ARGUMENT, "cache_lens is not 4-byte aligned");
+  if (!plan.empty && plan.ws_bytes > 0) {
+    if (workspace_bytes < plan.ws_bytes)
+      return fail(RELATTN_ERR_INVALID_ARGUMENT, "workspace of %zu bytes, %zu needed",
+                  workspace_bytes, plan.ws_bytes);
+    if (!workspace || !aligned16(workspace))
+      return fail(RELATTN_ERR_INVALID_ARGUMENT, "workspace is NULL or not 16-byte aligned");
+  }
+  if ((st = check_device())) return st;
+  if (plan.empty) return RELATTN_OK;
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  plan.p.cache_lens = cache_lens;
+  plan.p.ws_ml = reinterpret_cast<float*>(ws);
+  plan.p.ws_o = reinterpret_cast<float*>(ws + plan.ws_o_off);
+  plan.p.ws_band = reinterpret_cast<float*>(ws + plan.ws_band_off);
+  const int e = relattn::launch_decode(plan.bf16, plan.d, plan.mode, plan.has_wk, plan.has_wv,
+                                       plan.p, stream);
+  if (e != (int)hipSuccess)
+    return fail(RELATTN_ERR_LAUNCH_FAILED, "launch failed: %s",
+                hipGetErrorString((hipError_t)e));
+  return RELATTN_OK;
+}
+
+int relattn_decode_offset_bias_workspace_size(const relattn_tensor* q, const relattn_tensor* k,
+                                              const relattn_tensor* v, const relattn_tensor* bias,
+                                              int32_t window, float scale,
+                                              const relattn_tensor* out, size_t* bytes) {
+  g_last_error.clear();
+  if (!bytes) return fail(RELATTN_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  if (!bias) return fail(RELATTN_ERR_INVALID_ARGUMENT, "bias is NULL");
+  DecPlan plan;
+  const int st = make_dec_plan(q, k, v, nullptr, nullptr, nullptr, nullptr, 0, scale, out, &plan,
+                               false, bias, window);
+  if (st) return st;
+  *bytes = plan.empty ? 0 : plan.ws_bytes;
+  return RELATTN_OK;
+}
+
+int relattn_decode_offset_bias(const relattn_tensor* q, const relattn_tensor* k,
+                               const relattn_tensor* v, const relattn_tensor* bias, int32_t window,
+                               float scale, const int32_t* cache_lens, relattn_tensor* out,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  if (!bias) return fail(RELATTN_ERR_INVALID_ARGUMENT, "bias is NULL");
+  DecPlan plan;
+  int st = make_dec_plan(q, k, v, nullptr, nullptr, nullptr, nullptr, 0, scale, out, &plan, true,
+                         bias, window);
   if (st) return st;
   if (cache_lens && (reinterpret_cast<uintptr_t>(cache_lens) & 3u))
     return fail(RELATTN_ERR_INVALID_ARGUMENT, "cache_lens is not 4-byte aligned");

@@ -9,7 +9,8 @@
 // parallel:
 //   decode_partial_kernel  one workgroup per (query row, chunk of keys): the
 //       chunk's logits e_j = scale * q . (k_j + a^K_ij) in log2 units (T5: the
-//       bucketed bias instead of a^K), its max m_c, the sum l_c of 2^(e_j - m_c)
+//       bucketed bias instead of a^K; or the entry of a table by clipped
+//       offset, e.g. ALiBi), its max m_c, the sum l_c of 2^(e_j - m_c)
 //       and the partial output O_c = sum_j 2^(e_j - m_c) v_j.  Each K and V row
 //       is read by LPR lanes with 16-byte loads (coalesced rows, every load of
 //       a lane issued before the first use); a dot product is summed over the
@@ -189,7 +190,11 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(4))
           rel = far;
         }
       }
-      if constexpr (T5) rel = kLog2e * p.t5_bias[t5_bucket(delta, p.t5) * p.tb_sb + h * p.tb_sh];
+      if constexpr (T5) {
+        // T5 bucket, or the entry of a table by clipped offset
+        const int entry = p.ob ? min(max(delta, -p.ob_w), p.ob_w) + p.ob_w : t5_bucket(delta, p.t5);
+        rel = kLog2e * p.t5_bias[entry * p.tb_sb + h * p.tb_sh];
+      }
       float dot = 0.f;
 #pragma unroll
       for (int e = 0; e < EPL; ++e) dot = fmaf(qf[e], x[e], dot);

@@ -239,6 +239,10 @@ struct DecParams {
   int32_t direct;       // nsp == 1 and the row's single-key labels fit in LDS:
                         // one workgroup per row writes the output itself
   float scale_log2;
+  // scalar-bias mode with ob = 1: t5_bias points at a [Hb, 2W + 1] table by
+  // clipped offset (entry clip(delta, W) + W, W = ob_w) instead of T5 buckets
+  int32_t ob;
+  int32_t ob_w;
   T5Buckets t5;
 };
 

@@ -373,3 +373,20 @@ def test_edge_tables_validation(ra):
     assert ra.validate_edge_tables(q, k, v, lab.to(torch.int32), wK, None) == ra.INVALID_ARGUMENT
     tight = torch.zeros(B * n * n + 16, dtype=torch.uint8).as_strided((B, n, n), (n * n, n, 1))
     assert ra.validate_edge_tables(q, k, v, tight, wK, None) == ra.UNSUPPORTED
+
+
+def test_decode_offset_bias_checks(ra):
+    """Workspace size and argument checks of the offset-bias decode (host only)."""
+    B, H, L, d = 2, 3, 64, 64
+    q = T(B, H, 1, d)
+    k, v = T(B, H, L, d), T(B, H, L, d)
+    bias = T(H, 2 * 10 + 1, dtype=torch.float32)
+    n1 = ra.decode_offset_bias_workspace_size(q, k, v, bias, 10)
+    n0 = ra.decode_workspace_size(q, k, v, t5_bias=T(32, H, dtype=torch.float32))
+    assert n1 == n0     # the same plan as the T5 bias: no value term
+    assert ra.decode_offset_bias_workspace_size(q, k, v, T(1, 21, dtype=torch.float32), 10) == n1
+    for bad, win in ((T(H, 20, dtype=torch.float32), 10), (T(2, 21, dtype=torch.float32), 10),
+                     (T(H, 21), 10), (bias, -1)):
+        with pytest.raises(ra.RelattnError) as e:
+            ra.decode_offset_bias_workspace_size(q, k, v, bad, win)
+        assert e.value.status == ra.INVALID_ARGUMENT

@@ -238,3 +238,46 @@ def test_decode_splits_of_several_chunks(ra):
             want = oracle.relattn_decode(sl(q), sl(k), sl(v), wK[h:h + 1], wV[h:h + 1], c,
                                          cache_lens=[lens[b]])
             assert maxerr(got[b, h], want[0, 0]) <= 2e-2, (b, h)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=str)
+@pytest.mark.parametrize("d", [32, 64, 128])
+@pytest.mark.parametrize("window,shared", [(8, False), (700, True), (0, False)])
+def test_decode_offset_bias_parity(ra, dtype, d, window, shared):
+    """Decoding with a table by clipped offset (ALiBi slopes on the per-head rows)
+    against the oracle: windows that clip, one wider than the cache, and 0."""
+    B, H, Tq, L = 4, 3, 2, 600
+    g = torch.Generator().manual_seed(700 + d + window)
+    q = (torch.randn(B, H, Tq, d, generator=g) / 8).to(dtype)
+    k = (torch.randn(B, H, L, d, generator=g) / 8).to(dtype)
+    v = torch.randn(B, H, L, d, generator=g).to(dtype)
+    slopes = torch.tensor([2.0 ** (-8 * (h + 1) / H) for h in range(H)])
+    dist = torch.arange(-window, window + 1).abs().float()
+    bias = -(slopes[:, None] * dist[None, :])
+    if shared:
+        bias = bias[:1]
+    lens = [L, 333, 1, 0]
+    lens_d = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    out = ra.decode_offset_bias(dev(q), dev(k), dev(v), dev(bias), window, cache_lens=lens_d)
+    torch.cuda.synchronize()
+    want = oracle.offset_bias_decode(q, k, v, bias, window, cache_lens=lens)
+    assert maxerr(out.float().cpu().numpy(), want) <= TOL[dtype]
+
+
+def test_decode_offset_bias_matches_forward_rows(ra):
+    """The newest position decoded with an offset table equals the causal
+    offset-bias forward's row at that position (two HIP paths, same inputs)."""
+    B, H, L, d, W = 2, 4, 300, 64, 40
+    g = torch.Generator().manual_seed(800)
+    q_full = torch.randn(B, H, L, d, generator=g)
+    k, v = torch.randn(B, H, L, d, generator=g), torch.randn(B, H, L, d, generator=g)
+    bias = torch.randn(H, 2 * W + 1, generator=g)
+    lens = [L, 211]
+    lens_d = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    fwd = ra.fwd_offset_bias(dev(q_full), dev(k), dev(v), dev(bias), W, causal=True)
+    q = torch.stack([q_full[b, :, lens[b] - 1] for b in range(B)])[:, :, None]
+    dec = ra.decode_offset_bias(dev(q), dev(k), dev(v), dev(bias), W, cache_lens=lens_d)
+    torch.cuda.synchronize()
+    for b in range(B):
+        want = fwd[b, :, lens[b] - 1].cpu()
+        assert float((dec[b, :, 0].cpu() - want).abs().max()) <= 1e-5
