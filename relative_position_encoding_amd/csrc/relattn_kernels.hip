@@ -802,14 +802,16 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<D, NW, MODE, BF16, BC>()))) vo
     if (__any(grow)) {  // wave-uniform
       const float m_next = grow ? tmax : m_run;
       const float alpha = fast_exp2(m_run - m_next);  // 0 when m_run is -inf
+      [[maybe_unused]] const bool had_max = m_run != kNegInf;
       m_run = m_next;
       l_part *= alpha;
       if constexpr (SHAW && HAS_WV) thi *= alpha;
 #pragma unroll
       for (int mb = 0; mb < DVB; ++mb) oacc[mb] *= alpha;
       if constexpr (GRAPH && HAS_WV) {
-        // the weight sums follow the row's scale
-        if (grow)
+        // the weight sums follow the row's scale (still all zero while the row
+        // had no visible key)
+        if (grow && had_max)
           for (int r = 0; r < p.nr; ++r) myS[r] *= alpha;
       }
     }
