@@ -182,3 +182,15 @@ def test_edge_bias_empty_problems(ra):
         q = torch.zeros(B, 2, n, 32, dtype=torch.bfloat16, device=DEV)
         out = ra.fwd_edge_bias(q, q, q, ra.edge_label_buffer(B, n, DEV), bias)
         assert out.shape == q.shape
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_edge_bias_long_rows(ra, causal):
+    """n = 2000: 32 key tiles per row through the label ring, 200 labels."""
+    B, H, n, d, NL = 1, 2, 2000, 64, 200
+    q, k, v = (gen((B, H, n, d), torch.bfloat16, 2700 + i) for i in range(3))
+    bias = gen((H, NL), torch.float32, 2703, std=2.0)
+    E = np.random.default_rng(2704).integers(0, NL, (B, n, n))
+    out = run(ra, q, k, v, E, bias, causal=causal, key_lens=[1900])
+    want = oracle.edge_label_attention(q, k, v, E, bias, causal=causal, key_lens=[1900])
+    assert float(np.max(np.abs(out.double().cpu().numpy() - want))) <= TOL[torch.bfloat16]

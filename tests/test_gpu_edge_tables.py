@@ -170,3 +170,15 @@ def test_edge_tables_empty_problems(ra):
         q = torch.zeros(B, 2, n, 32, dtype=torch.bfloat16, device=DEV)
         out = ra.fwd_edge_tables(q, q, q, ra.edge_label_buffer(B, n, DEV), wK, wK)
         assert out.shape == q.shape
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_edge_tables_long_rows(ra, causal):
+    """n = 600 (ten key tiles per row, several weight-sum rescales), 48 labels."""
+    B, H, n, d, NL = 1, 2, 600, 32, 48
+    q, k, v = (gen((B, H, n, d), torch.bfloat16, 3600 + i) for i in range(3))
+    wK, wV = gen((H, NL, d), torch.bfloat16, 3603, 0.5), gen((H, NL, d), torch.bfloat16, 3604, 0.5)
+    E = np.random.default_rng(3605).integers(0, NL, (B, n, n))
+    got = run(ra, q, k, v, E, wK, wV, causal=causal, lens=[555])
+    want = oracle.edge_label_relattn(q, k, v, E, wK, wV, causal=causal, key_lens=[555])
+    assert float(np.max(np.abs(got - want))) <= TOL[torch.bfloat16]

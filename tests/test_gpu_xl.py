@@ -127,6 +127,20 @@ def test_xl_full_size(ra):
         assert err <= TOL[torch.bfloat16], (b, h, err)
 
 
+@pytest.mark.parametrize("d", [32, 64])
+def test_xl_long_segment(ra, d):
+    """n = 2048 with every distance (fused mode: 32 key tiles per row, table
+    rows read across the whole window)."""
+    B, H, n = 1, 2, 2048
+    W = n - 1
+    q, k, v = (gen((B, H, n, d), torch.bfloat16, 1800 + d + i) for i in range(3))
+    R = gen((H, 2 * W + 1, d), torch.bfloat16, 1803, 0.5)
+    u, vb = gen((H, d), torch.bfloat16, 1804, 0.5), gen((H, d), torch.bfloat16, 1805, 0.5)
+    got = run(ra, q, k, v, R, u, vb, W, causal=True, lens=[2000])
+    want = oracle.xl_attention(q, k, v, R, u, vb, W, causal=True, key_lens=[2000])
+    assert float(np.max(np.abs(got - want))) <= TOL[torch.bfloat16]
+
+
 def test_xl_rejects(ra):
     q = gen((1, 2, 16, 64), torch.bfloat16, 1600).to(DEV)
     R = gen((2, 9, 64), torch.bfloat16, 1601).to(DEV)
