@@ -390,3 +390,28 @@ def test_decode_offset_bias_checks(ra):
         with pytest.raises(ra.RelattnError) as e:
             ra.decode_offset_bias_workspace_size(q, k, v, bad, win)
         assert e.value.status == ra.INVALID_ARGUMENT
+
+
+def test_missing_library_fails_loudly():
+    """Without the built library every entry point raises: there is no CPU
+    fallback behind the binding."""
+    code = r"""
+import sys, torch
+sys.path.insert(0, %r)
+import relative_position_encoding_amd as ra
+ra.library_path = "/nonexistent/librelattn.so"
+q = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
+for call in (lambda: ra.fwd(q, q, q), lambda: ra.validate(q, q, q),
+             lambda: ra.fwd_edge_bias(q, q, q, ra.edge_label_buffer(1, 8), torch.zeros(1, 4)),
+             lambda: ra.decode(q, q, q)):
+    try:
+        call()
+    except RuntimeError as e:
+        assert "not built" in str(e), e
+    else:
+        raise SystemExit("no error")
+print("ok")
+""" % ROOT
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stderr
+    assert r.stdout.strip().splitlines()[-1] == "ok"
