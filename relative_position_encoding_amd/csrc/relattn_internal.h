@@ -60,9 +60,11 @@ struct FwdParams {
   // natural-log log-sum-exp of row i's visible logits (-inf for none).
   float* lse;
   int64_t lse_sb, lse_sh;
-  // Transformer-XL (xl = 1, Shaw mode with the key table only): the key table
-  // is the position table R read by i - j, and the query is shifted by the
-  // head's global bias u for the content logit and v for the relative logit.
+  // Transformer-XL (xl = 1): the key table is the position table R read by
+  // i - j, and the query is shifted by the head's global bias u for the content
+  // logit and v for the relative logit.  Shaw mode with the key table only
+  // (d = 128): wk starts at R's last row with a negative row stride; XL mode
+  // (d <= 64): wk points at R's row of distance 0.
   const void* xl_u;
   const void* xl_v;
   int64_t xl_u_sh, xl_v_sh;  // head strides (0 = one vector for all heads)
@@ -72,10 +74,11 @@ struct FwdParams {
   // [Hb, (2M-1)^2] table and t5.nb = (2M-1)^2 entries are loaded.
   int32_t grid_m;
   float grid_inv;  // 1 / M
-  // Edge-label bias (label mode): lab[b * lab_sb + i * lab_sn + j] is the
-  // label of the edge from query i to key j; rows are read in whole 16-byte
-  // chunks (lab_sn a multiple of 16, at least n rounded up to 16); t5_bias
-  // points at the head's row of a [Hb, NL] table and t5.nb = NL.
+  // Edge labels (label and graph modes): lab[b * lab_sb + i * lab_sn + j] is
+  // the label of the edge from query i to key j; rows are read in whole
+  // 16-byte chunks (lab_sn a multiple of 16, at least n rounded up to 16).
+  // Label mode: t5_bias points at the head's row of a [Hb, NL] table and
+  // t5.nb = NL.  Graph mode: wk / wv are [Ht, NL, d] tables, r_lo = 0, nr = NL.
   const uint8_t* lab;
   int64_t lab_sb, lab_sn;
   T5Buckets t5;
