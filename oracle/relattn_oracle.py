@@ -88,6 +88,7 @@ __all__ = [
     "t5_backward",
     "offset_bias_backward",
     "xl_attention",
+    "xl_decode",
     "grid_bias_attention",
     "edge_label_attention",
     "edge_label_relattn",
@@ -669,6 +670,39 @@ def xl_attention(q, k, v, R, u, vb, window: int, scale=None, causal: bool = Fals
             term_d = np.einsum("d,ijd->ij", vh, Rh)
             e = s * (term_a + term_b + term_c + term_d)
             z[b, h] = _masked_softmax_rows(e, ok) @ v[b, h]
+    return z
+
+
+def xl_decode(q, k, v, R, u, vb, window: int, scale=None, cache_lens=None):
+    """Transformer-XL logits for the newest Tq positions over a cache (the
+    evaluation setting of the transformer-xl page: each new token attends over
+    everything before it): query t of batch b at position i = len_b - Tq + t
+    sees keys 0 .. i, e_j = s [q.k_j + q.R_{i-j} + u.k_j + v.R_{i-j}] with R's
+    row window + (i - j), distances beyond the window taking the end row.
+    Positions and visibility as in ``relattn_decode``."""
+    q, k, v = to_f64(q), to_f64(k), to_f64(v)
+    R, u, vb = to_f64(R), to_f64(u), to_f64(vb)
+    B, H, Tq, d = q.shape
+    L = k.shape[2]
+    s = _default_scale(d, scale)
+    pos = _decode_positions(Tq, L, cache_lens, B)
+    z = np.zeros((B, H, Tq, v.shape[-1]))
+    for b in range(B):
+        for h in range(H):
+            Rh = R[0 if R.shape[0] == 1 else h]
+            uh = u[0 if u.shape[0] == 1 else h]
+            vh = vb[0 if vb.shape[0] == 1 else h]
+            for t in range(Tq):
+                i = pos[b][t]
+                if i < 0:
+                    continue
+                e = np.array([s * (float(q[b, h, t] @ k[b, h, j])
+                                   + float(q[b, h, t] @ Rh[clip(i - j, window) + window])
+                                   + float(uh @ k[b, h, j])
+                                   + float(vh @ Rh[clip(i - j, window) + window]))
+                              for j in range(i + 1)])
+                w = np.exp(e - e.max())
+                z[b, h, t] = (w / w.sum()) @ v[b, h, :i + 1]
     return z
 
 

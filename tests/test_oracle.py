@@ -989,3 +989,30 @@ def test_offset_bias_decode_matches_forward_rows(window, shared):
                 np.testing.assert_allclose(z[b, :, t], full[b, :, i], rtol=0, atol=1e-12)
             else:
                 assert np.all(z[b, :, t] == 0.0)
+
+
+@pytest.mark.parametrize("window,shared", [(3, False), (40, True)])
+def test_xl_decode_matches_forward_rows(window, shared):
+    """Transformer-XL decoding reproduces the causal XL attention's rows at the
+    decoded positions (per-head and shared R, u, v; a window that clips and one
+    that does not)."""
+    q_full, k, v, lens, Tq = _decode_case(80, L=40)
+    B, H, L, d = q_full.shape
+    Hr = 1 if shared else H
+    R = rnd((Hr, 2 * window + 1, d), 81, 0.5)
+    u, vb = rnd((Hr, d), 82, 0.5), rnd((Hr, d), 83, 0.5)
+    q = np.zeros((B, H, Tq, d))
+    for b in range(B):
+        for t in range(Tq):
+            i = lens[b] - Tq + t
+            if i >= 0:
+                q[b, :, t] = q_full[b, :, i]
+    z = oracle.xl_decode(q, k, v, R, u, vb, window, cache_lens=lens)
+    full = oracle.xl_attention(q_full, k, v, R, u, vb, window, causal=True, key_lens=lens)
+    for b in range(B):
+        for t in range(Tq):
+            i = lens[b] - Tq + t
+            if i >= 0:
+                np.testing.assert_allclose(z[b, :, t], full[b, :, i], rtol=0, atol=1e-12)
+            else:
+                assert np.all(z[b, :, t] == 0.0)
