@@ -321,6 +321,34 @@ int relattn_decode(const relattn_tensor* q, const relattn_tensor* k,
                    void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * relattn_decode_xl: incremental decoding with Transformer-XL relative logits
+ * (the transformer-xl page's four-term score; the newest positions attend over
+ * everything before them):
+ *
+ *       e_j = scale * [ (q + u).k_j + (q + vb).R_{i-j} ],  j <= i
+ *
+ *   q, k, v, out, cache_lens, workspace, stream : as for relattn_decode.
+ *   R, u, vb, window : as for relattn_fwd_xl (R [Hr, 2*window + 1, d], row
+ *                  window + (i - j); u, vb [Hu, d]; q + u and q + vb rounded
+ *                  once to the input dtype).
+ *   scale        : multiplies the whole score; <= 0 picks 1/sqrt(d).
+ * relattn_decode_xl_workspace_size gives the workspace bytes.  Errors as for
+ * relattn_decode.  No value term; the segment memory is the cache itself.
+ */
+int relattn_decode_xl(const relattn_tensor* q, const relattn_tensor* k, const relattn_tensor* v,
+                      const relattn_tensor* R, const relattn_tensor* u, const relattn_tensor* vb,
+                      int32_t window, float scale, const int32_t* cache_lens, relattn_tensor* out,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* relattn_decode_xl_workspace_size: host only; *bytes receives the workspace
+ * relattn_decode_xl needs for these shapes (0 when none). */
+int relattn_decode_xl_workspace_size(const relattn_tensor* q, const relattn_tensor* k,
+                                     const relattn_tensor* v, const relattn_tensor* R,
+                                     const relattn_tensor* u, const relattn_tensor* vb,
+                                     int32_t window, float scale, const relattn_tensor* out,
+                                     size_t* bytes);
+
+/*
  * relattn_decode_offset_bias: incremental decoding with a scalar bias by clipped
  * offset (survey page "Relative position embeddings", section "Placement in
  * the taxonomy": ALiBi is the bias -m_h |delta| written as such a table):

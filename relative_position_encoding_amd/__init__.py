@@ -16,7 +16,7 @@ __all__ = ["fwd", "validate", "fwd_offset_bias", "validate_offset_bias", "decode
            "attention", "attention_offset_bias", "fwd_xl", "validate_xl", "fwd_grid_bias",
            "validate_grid_bias", "fwd_edge_bias", "validate_edge_bias", "edge_label_buffer",
            "fwd_edge_tables", "validate_edge_tables", "decode_offset_bias",
-           "decode_offset_bias_workspace_size",
+           "decode_offset_bias_workspace_size", "decode_xl", "decode_xl_workspace_size",
            "RelattnError", "library_path",
            "OK", "INVALID_ARGUMENT", "UNSUPPORTED", "NO_DEVICE", "LAUNCH_FAILED"]
 
@@ -80,6 +80,12 @@ def _load():
     lib.relattn_decode_offset_bias_workspace_size.argtypes = decob + [P(_Tensor),
                                                                       P(ctypes.c_size_t)]
     lib.relattn_decode_offset_bias_workspace_size.restype = ctypes.c_int
+    decxl = [P(_Tensor)] * 6 + [ctypes.c_int32, ctypes.c_float]
+    lib.relattn_decode_xl.argtypes = decxl + [ctypes.c_void_p, P(_Tensor), ctypes.c_void_p,
+                                              ctypes.c_size_t, ctypes.c_void_p]
+    lib.relattn_decode_xl.restype = ctypes.c_int
+    lib.relattn_decode_xl_workspace_size.argtypes = decxl + [P(_Tensor), P(ctypes.c_size_t)]
+    lib.relattn_decode_xl_workspace_size.restype = ctypes.c_int
     ob = [P(_Tensor), P(_Tensor), P(_Tensor), P(_Tensor), ctypes.c_int32, ctypes.c_float,
           P(_Mask), P(_Tensor)]
     lib.relattn_fwd_offset_bias.argtypes = ob + [ctypes.c_void_p]
@@ -820,6 +826,48 @@ def decode_offset_bias(q, k, v, bias, window, *, cache_lens=None, scale=None, ou
     views = [_view(x) for x in (q, k, v, bias)]
     outv = _view(out)
     st = lib.relattn_decode_offset_bias(
+        *[_ref(x) for x in views], int(window), float(0.0 if scale is None else scale),
+        ctypes.c_void_p(cache_lens.data_ptr() if cache_lens is not None else None),
+        ctypes.byref(outv), ctypes.c_void_p(workspace.data_ptr()),
+        ctypes.c_size_t(workspace.numel() * workspace.element_size()),
+        ctypes.c_void_p(_stream_of(q, stream)))
+    del views, outv
+    if st != OK:
+        _raise(lib, st)
+    return out
+
+
+def decode_xl_workspace_size(q, k, v, R, u, vb, window, *, scale=None, out=None):
+    """Workspace bytes ``decode_xl`` needs for these shapes (host only)."""
+    lib = _load()
+    views = [_view(x) for x in (q, k, v, R, u, vb)]
+    outv = _view(q if out is None else out)
+    nbytes = ctypes.c_size_t(0)
+    st = lib.relattn_decode_xl_workspace_size(
+        *[_ref(x) for x in views], int(window), float(0.0 if scale is None else scale),
+        ctypes.byref(outv), ctypes.byref(nbytes))
+    if st != OK:
+        _raise(lib, st)
+    return nbytes.value
+
+
+def decode_xl(q, k, v, R, u, vb, window, *, cache_lens=None, scale=None, out=None,
+              workspace=None, stream=None):
+    """Incremental decoding (positions as for ``decode``) with Transformer-XL
+    relative logits: R [H or 1, 2*window+1, d] by distance i - j, u and vb
+    [H or 1, d] (arguments of ``fwd_xl``).  Returns ``out``."""
+    import torch
+    lib = _load()
+    if cache_lens is not None and cache_lens.dtype != torch.int32:
+        raise RelattnError(INVALID_ARGUMENT, "relattn: cache_lens must be int32")
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    need = decode_xl_workspace_size(q, k, v, R, u, vb, window, scale=scale, out=out)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    views = [_view(x) for x in (q, k, v, R, u, vb)]
+    outv = _view(out)
+    st = lib.relattn_decode_xl(
         *[_ref(x) for x in views], int(window), float(0.0 if scale is None else scale),
         ctypes.c_void_p(cache_lens.data_ptr() if cache_lens is not None else None),
         ctypes.byref(outv), ctypes.c_void_p(workspace.data_ptr()),

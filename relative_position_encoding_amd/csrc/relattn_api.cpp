@@ -588,7 +588,8 @@ int make_dec_plan(const relattn_tensor* q, const relattn_tensor* k, const relatt
                   const relattn_tensor* wK, const relattn_tensor* wV,
                   const relattn_tensor* t5_bias, const relattn_t5_params* t5, int32_t clip_k,
                   float scale, const relattn_tensor* out, DecPlan* plan, bool want_t5_table,
-                  const relattn_tensor* ob = nullptr, int32_t ob_window = 0) {
+                  const relattn_tensor* ob = nullptr, int32_t ob_window = 0,
+                  const relattn_tensor* xl_u = nullptr, const relattn_tensor* xl_v = nullptr) {
   int st;
   if ((st = check_view(q, "q", 4, true))) return st;
   if ((st = check_view(k, "k", 4, true))) return st;
@@ -626,7 +627,25 @@ int make_dec_plan(const relattn_tensor* q, const relattn_tensor* k, const relatt
   if (!is_t5 && clip_k < 0) return fail(RELATTN_ERR_INVALID_ARGUMENT, "clip_k must be >= 0");
   if (!is_t5 && (int64_t)clip_k > kMaxSeq)
     return fail(RELATTN_ERR_UNSUPPORTED, "clip_k exceeds 2^30");
-  if (wK && (st = check_table(wK, "wK", q, clip_k))) return st;
+  const bool is_xl = xl_u != nullptr || xl_v != nullptr;
+  if (is_xl) {
+    // Transformer-XL: wK is the position table R (by distance i - j), u and v
+    // the global biases; no value table, no scalar bias
+    if (!xl_u || !xl_v || !wK)
+      return fail(RELATTN_ERR_INVALID_ARGUMENT, "R, u and v must be given together");
+    if (wV || is_t5 || ob)
+      return fail(RELATTN_ERR_INVALID_ARGUMENT, "Transformer-XL logits exclude the other tables");
+    const relattn_tensor* uv[2] = {xl_u, xl_v};
+    const char* nm[2] = {"u", "v"};
+    for (int t = 0; t < 2; ++t) {
+      if ((st = check_view(uv[t], nm[t], 2, true))) return st;
+      if (uv[t]->dtype != q->dtype)
+        return fail(RELATTN_ERR_INVALID_ARGUMENT, "%s dtype differs from q", nm[t]);
+      if (!(uv[t]->shape[0] == H || uv[t]->shape[0] == 1) || uv[t]->shape[1] != d)
+        return fail(RELATTN_ERR_INVALID_ARGUMENT, "%s must be [H or 1, d]", nm[t]);
+    }
+  }
+  if (wK && (st = check_table(wK, is_xl ? "R" : "wK", q, clip_k))) return st;
   if (wV && (st = check_table(wV, "wV", q, clip_k))) return st;
   T5Buckets tb = {};
   if (is_t5) {
@@ -656,8 +675,9 @@ int make_dec_plan(const relattn_tensor* q, const relattn_tensor* k, const relatt
       return fail(RELATTN_ERR_INVALID_ARGUMENT, "bias: shape[1] must be 2*window+1 = %lld",
                   (long long)(2 * (int64_t)ob_window + 1));
   }
-  P.mode = (is_t5 || is_ob) ? relattn::kRelT5
-                            : ((wK || wV) ? relattn::kRelShaw : relattn::kRelNone);
+  P.mode = is_xl ? relattn::kRelXL
+                 : (is_t5 || is_ob) ? relattn::kRelT5
+                                    : ((wK || wV) ? relattn::kRelShaw : relattn::kRelNone);
   P.has_wk = wK != nullptr;
   P.has_wv = wV != nullptr;
   P.empty = (B == 0 || H == 0 || Tq == 0);
@@ -699,6 +719,12 @@ int make_dec_plan(const relattn_tensor* q, const relattn_tensor* k, const relatt
   p.t5 = tb;
   const float s = scale > 0.f ? scale : (is_t5 ? 1.f : 1.f / std::sqrt((float)d));
   p.scale_log2 = s * 1.4426950408889634f;
+  if (is_xl) {
+    p.xl_u = xl_u->data;
+    p.xl_v = xl_v->data;
+    p.xl_u_sh = xl_u->shape[0] == 1 ? 0 : xl_u->stride[0];
+    p.xl_v_sh = xl_v->shape[0] == 1 ? 0 : xl_v->stride[0];
+  }
   if (is_ob) {
     // the bias of offset delta is entry clip(delta, W) + W of the head's row
     p.ob = 1;
@@ -1310,6 +1336,56 @@ int relattn_decode(const relattn_tensor* q, const relattn_tensor* k, const relat
   g_last_error.clear();
   DecPlan plan;
   int st = make_dec_plan(q, k, v, wK, wV, t5_bias, t5, clip_k, scale, out, &plan, true);
+  if (st) return st;
+  if (cache_lens && (reinterpret_cast<uintptr_t>(cache_lens) & 3u))
+    return fail(RELATTN_ERR_INVALID_ARGUMENT, "cache_lens is not 4-byte aligned");
+  if (!plan.empty && plan.ws_bytes > 0) {
+    if (workspace_bytes < plan.ws_bytes)
+      return fail(RELATTN_ERR_INVALID_ARGUMENT, "workspace of %zu bytes, %zu needed",
+                  workspace_bytes, plan.ws_bytes);
+    if (!workspace || !aligned16(workspace))
+      return fail(RELATTN_ERR_INVALID_ARGUMENT, "workspace is NULL or not 16-byte aligned");
+  }
+  if ((st = check_device())) return st;
+  if (plan.empty) return RELATTN_OK;
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  plan.p.cache_lens = cache_lens;
+  plan.p.ws_ml = reinterpret_cast<float*>(ws);
+  plan.p.ws_o = reinterpret_cast<float*>(ws + plan.ws_o_off);
+  plan.p.ws_band = reinterpret_cast<float*>(ws + plan.ws_band_off);
+  const int e = relattn::launch_decode(plan.bf16, plan.d, plan.mode, plan.has_wk, plan.has_wv,
+                                       plan.p, stream);
+  if (e != (int)hipSuccess)
+    return fail(RELATTN_ERR_LAUNCH_FAILED, "launch failed: %s",
+                hipGetErrorString((hipError_t)e));
+  return RELATTN_OK;
+}
+
+int relattn_decode_xl_workspace_size(const relattn_tensor* q, const relattn_tensor* k,
+                                     const relattn_tensor* v, const relattn_tensor* R,
+                                     const relattn_tensor* u, const relattn_tensor* vb,
+                                     int32_t window, float scale, const relattn_tensor* out,
+                                     size_t* bytes) {
+  g_last_error.clear();
+  if (!bytes) return fail(RELATTN_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  if (!R || !u || !vb) return fail(RELATTN_ERR_INVALID_ARGUMENT, "R, u and v must be given");
+  DecPlan plan;
+  const int st = make_dec_plan(q, k, v, R, nullptr, nullptr, nullptr, window, scale, out, &plan,
+                               false, nullptr, 0, u, vb);
+  if (st) return st;
+  *bytes = plan.empty ? 0 : plan.ws_bytes;
+  return RELATTN_OK;
+}
+
+int relattn_decode_xl(const relattn_tensor* q, const relattn_tensor* k, const relattn_tensor* v,
+                      const relattn_tensor* R, const relattn_tensor* u, const relattn_tensor* vb,
+                      int32_t window, float scale, const int32_t* cache_lens, relattn_tensor* out,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  if (!R || !u || !vb) return fail(RELATTN_ERR_INVALID_ARGUMENT, "R, u and v must be given");
+  DecPlan plan;
+  int st = make_dec_plan(q, k, v, R, nullptr, nullptr, nullptr, window, scale, out, &plan, true,
+                         nullptr, 0, u, vb);
   if (st) return st;
   if (cache_lens && (reinterpret_cast<uintptr_t>(cache_lens) & 3u))
     return fail(RELATTN_ERR_INVALID_ARGUMENT, "cache_lens is not 4-byte aligned");

@@ -10,7 +10,9 @@
 //   decode_partial_kernel  one workgroup per (query row, chunk of keys): the
 //       chunk's logits e_j = scale * q . (k_j + a^K_ij) in log2 units (T5: the
 //       bucketed bias instead of a^K; or the entry of a table by clipped
-//       offset, e.g. ALiBi), its max m_c, the sum l_c of 2^(e_j - m_c)
+//       offset, e.g. ALiBi; Transformer-XL: (q + u).k_j + (q + v).R_{i-j} with the
+//       position table's row of each key requested with its K row), its max
+//       m_c, the sum l_c of 2^(e_j - m_c)
 //       and the partial output O_c = sum_j 2^(e_j - m_c) v_j.  Each K and V row
 //       is read by LPR lanes with 16-byte loads (coalesced rows, every load of
 //       a lane issued before the first use); a dot product is summed over the
@@ -95,8 +97,16 @@ __device__ __forceinline__ RowPos row_pos(const DecParams& p, int row) {
   return r;
 }
 
+// Waves per SIMD the register budget is sized for: four, except Transformer-XL,
+// whose position-table rows (requested with the K rows) would spill there.
+template <int MODE>
+constexpr int dec_waves_per_eu() {
+  return MODE == kRelXL ? 2 : 4;
+}
+
 template <int D, bool BF16, int MODE, bool HAS_WK, bool HAS_WV, bool DIRECT>
-__global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(4))) void decode_kernel(
+__global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(
+    dec_waves_per_eu<MODE>()))) void decode_kernel(
     const DecParams p) {
   using V = typename Frag<BF16>::V;
   using T = std::conditional_t<BF16, __bf16, float>;
@@ -109,6 +119,7 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(4))
   static_assert(LPR >= 1 && LPR <= 64 && NP * RPP == CH, "chunk geometry");
   constexpr bool SHAW = MODE == kRelShaw;
   constexpr bool T5 = MODE == kRelT5;
+  constexpr bool XLD = MODE == kRelXL;  // Transformer-XL: wk is the position table R
   constexpr bool VT = SHAW && HAS_WV;
   __shared__ float s_e[CH];
   __shared__ float s_red[8];
@@ -135,6 +146,18 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(4))
     const V x = load_frag<BF16>(p.q, b * p.q_sb + h * p.q_sh + rp.t * p.q_st + c0);
 #pragma unroll
     for (int e = 0; e < EPL; ++e) qf[e] = (float)x[e];
+  }
+  // Transformer-XL: q + v for the position term, q + u for the content term,
+  // each rounded once to the input dtype (as the forward does)
+  float qv[XLD ? EPL : 1];
+  if constexpr (XLD) {
+    const V xu = load_frag<BF16>(p.xl_u, h * p.xl_u_sh + c0);
+    const V xv = load_frag<BF16>(p.xl_v, h * p.xl_v_sh + c0);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      qv[e] = (float)(T)(qf[e] + (float)xv[e]);
+      qf[e] = (float)(T)(qf[e] + (float)xu[e]);
+    }
   }
   const int64_t kb = b * p.k_sb + h * p.k_sh, vb = b * p.v_sb + h * p.v_sh;
 
@@ -169,6 +192,17 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(4))
       const int j = min(j0 + rs + it * RPP, j1 - 1);
       vf[it] = load_frag<BF16>(p.v, vb + j * p.v_sn + c0);
     }
+    // Transformer-XL: each key's position-table row, distance i - j clamped to
+    // the window (row clip + distance)
+    V rf[XLD ? NP : 1];
+    if constexpr (XLD) {
+#pragma unroll
+      for (int it = 0; it < NP; ++it) {
+        const int j = min(j0 + rs + it * RPP, j1 - 1);
+        const int dist = min(i - j, p.clip);
+        rf[it] = load_frag<BF16>(p.wk, h * p.wk_sh + (p.clip + dist) * p.wk_sr + c0);
+      }
+    }
     // logits, log2 units
 #pragma unroll
     for (int it = 0; it < NP; ++it) {
@@ -196,6 +230,10 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(4))
         rel = kLog2e * p.t5_bias[entry * p.tb_sb + h * p.tb_sh];
       }
       float dot = 0.f;
+      if constexpr (XLD) {
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) dot = fmaf(qv[e], (float)rf[it][e], dot);
+      }
 #pragma unroll
       for (int e = 0; e < EPL; ++e) dot = fmaf(qf[e], x[e], dot);
       dot = group_sum<LPR>(dot);
@@ -487,6 +525,7 @@ int launch_dec_t(const DecParams& p, hipStream_t s) {
 template <int D, bool BF16>
 int launch_dec_mode(RelMode mode, bool has_wk, bool has_wv, const DecParams& p, hipStream_t s) {
   if (mode == kRelT5) return launch_dec_t<D, BF16, kRelT5, false, false>(p, s);
+  if (mode == kRelXL) return launch_dec_t<D, BF16, kRelXL, true, false>(p, s);
   if (mode == kRelShaw) {
     if (has_wk && has_wv) return launch_dec_t<D, BF16, kRelShaw, true, true>(p, s);
     if (has_wk) return launch_dec_t<D, BF16, kRelShaw, true, false>(p, s);

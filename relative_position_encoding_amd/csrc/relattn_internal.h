@@ -246,6 +246,12 @@ struct DecParams {
   // clipped offset (entry clip(delta, W) + W, W = ob_w) instead of T5 buckets
   int32_t ob;
   int32_t ob_w;
+  // Transformer-XL (XL mode): wk is the position table R [Hr, 2 clip + 1, d]
+  // (row clip + (i - j)); u and v shift the query for the content and the
+  // position term (head strides 0 = shared)
+  const void* xl_u;
+  const void* xl_v;
+  int64_t xl_u_sh, xl_v_sh;
   T5Buckets t5;
 };
 

@@ -423,3 +423,18 @@ def test_bench_refuses_more_than_one_gpu():
                        capture_output=True, text=True, timeout=300)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_decode_xl_checks(ra):
+    """Workspace size and argument checks of the Transformer-XL decode (host only)."""
+    B, H, L, d, W = 2, 3, 64, 64, 70
+    q = T(B, H, 1, d)
+    k, v = T(B, H, L, d), T(B, H, L, d)
+    R, u = T(H, 2 * W + 1, d), T(H, d)
+    n1 = ra.decode_xl_workspace_size(q, k, v, R, u, u, W)
+    assert n1 == ra.decode_workspace_size(q, k, v, R, None, clip=W)
+    for args in ((R, u.float(), u, W), (R, u, T(H, 32), W), (R[:, :-1], u, u, W),
+                 (R, T(2, d), u, W)):
+        with pytest.raises(ra.RelattnError) as e:
+            ra.decode_xl_workspace_size(q, k, v, *args)
+        assert e.value.status == ra.INVALID_ARGUMENT
