@@ -252,6 +252,93 @@ def decode_report(ra, steps):
     }
 
 
+XL_DECODE_SEED = 20260011
+
+
+def time_decode_xl(ra, w, steps, warmup, hot=False, reps=1):
+    """The decode workload's caches and queries with Transformer-XL logits: a
+    position table over every distance of the cache (window L - 1) and per-head
+    u and v, seeded.  flops: 4*d per visible key (q.k, p.v) + 2*d ((q + v).R);
+    bytes: every visible cache row of k and v once, q and out once, the table
+    rows the longest row reaches once, u and v."""
+    import statistics
+    import torch
+    import workloads
+    lib = ra._load()
+    stream = torch.cuda.Stream()  # default priority
+    x = workloads.make_decode_inputs(w)
+    lens = x["cache_lens"].tolist()
+    W = w.cache - 1
+    g0 = torch.Generator().manual_seed(XL_DECODE_SEED)
+    R = (torch.randn(w.heads, 2 * W + 1, w.d, generator=g0) * 0.5).to(w.dtype)
+    u = (torch.randn(w.heads, w.d, generator=g0) * 0.5).to(w.dtype)
+    vb = (torch.randn(w.heads, w.d, generator=g0) * 0.5).to(w.dtype)
+    esz = w.dtype.itemsize
+    keys = sum(int(n) for n in lens) * w.heads * w.tq
+    flops = 6.0 * w.d * keys
+    nbytes = (2.0 * sum(int(n) for n in lens) * w.heads * w.d * esz
+              + 2.0 * w.batch * w.heads * w.tq * w.d * esz
+              + w.heads * max(int(n) for n in lens) * w.d * esz + 2 * w.heads * w.d * esz)
+    copies = 1 if hot else max(1, min(16, int(2 * LLC_BYTES // nbytes) + 1))
+    calls, keep = [], []
+    for _ in range(copies):
+        g = {k: t.to("cuda").clone() for k, t in x.items()}
+        t5 = [R.to("cuda"), u.to("cuda"), vb.to("cuda")]
+        out = torch.empty_like(g["q"])
+        need = ra.decode_xl_workspace_size(g["q"], g["k"], g["v"], *t5, W, out=out)
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
+        views = [ra._view(t) for t in (g["q"], g["k"], g["v"], *t5)]
+        outv = ra._view(out)
+        calls.append([ctypes.byref(vw) for vw in views] +
+                     [ctypes.c_int32(W), ctypes.c_float(0.0),
+                      ctypes.c_void_p(g["cache_lens"].data_ptr()), ctypes.byref(outv),
+                      ctypes.c_void_p(ws.data_ptr()), ctypes.c_size_t(max(need, 16)),
+                      ctypes.c_void_p(stream.cuda_stream)])
+        keep += [g, t5, out, ws, views, outv]
+    fn = lib.relattn_decode_xl
+    times = []
+    with torch.cuda.stream(stream):
+        for s_ in range(warmup):
+            if fn(*calls[s_ % copies]) != 0:
+                raise RuntimeError(lib.relattn_last_error().decode())
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        for _ in range(reps):
+            t0.record(stream)
+            for s_ in range(steps):
+                fn(*calls[s_ % copies])
+            t1.record(stream)
+            torch.cuda.synchronize()
+            times.append(t0.elapsed_time(t1) / steps)
+    del keep
+    ms = statistics.median(times)
+    return {"ms_per_step": ms, "gbs": nbytes / (ms * 1e-3) / 1e9,
+            "tflops": flops / (ms * 1e-3) / 1e12, "alg_mbytes": nbytes / 1e6,
+            "input_copies": copies, "tokens_per_s": w.batch * w.tq / (ms * 1e-3)}
+
+
+def decode_xl_report(ra, steps):
+    import workloads
+    w = workloads.DECODE_WORKLOADS["decode"]
+    cold = time_decode_xl(ra, w, steps, 20, reps=5)
+    hot = time_decode_xl(ra, w, steps, 20, hot=True, reps=5)
+    tr = traffic_per_launch("decode_xl")
+    return {
+        "workload": w.description.replace("clip 16, key+value tables",
+                                          "Transformer-XL logits, position table over every "
+                                          "distance (window 1023), per-head u and v"),
+        "ms_per_step": round(cold["ms_per_step"], 5),
+        "tokens_per_s": round(cold["tokens_per_s"], 1),
+        "roofline": {"bound": "hbm", "achieved": round(cold["gbs"], 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(cold["gbs"] / PEAK_HBM_GBS, 4),
+                     "traffic": None if tr is None else round(tr)},
+        "tflops": round(cold["tflops"], 3), "alg_mbytes_per_step": round(cold["alg_mbytes"], 3),
+        "hot_ms_per_step": round(hot["ms_per_step"], 5), "input_copies": cold["input_copies"],
+        "steps_per_rep": steps,
+    }
+
+
 # ---------------------------------------------------------------------------
 # scalar bias by clipped offset: causal ALiBi on the T5 shape
 # ---------------------------------------------------------------------------
@@ -745,7 +832,8 @@ def traffic_per_launch(name):
         return None
     with open(path) as f:
         t = json.load(f)
-    src = DECODE_SRC if name == "decode" else (BWD_SRC if name.startswith("bwd_") else KERNEL_SRC)
+    src = DECODE_SRC if name.startswith("decode") else (BWD_SRC if name.startswith("bwd_")
+                                                        else KERNEL_SRC)
     if t.get("kernel_sha256") != kernel_sha(src):
         return None
     return t["fetch_kib"] * 1024 * t["fetch_scale"] + t["write_kib"] * 1024 * t["write_scale"]
@@ -938,6 +1026,8 @@ def main():
                     help="time the 2-D window (Swin) workload only and print its figures")
     ap.add_argument("--edge-only", action="store_true",
                     help="time the edge-label workload only and print its figures")
+    ap.add_argument("--decode-xl-only", action="store_true",
+                    help="time the Transformer-XL decode workload only and print its figures")
     ap.add_argument("--edge-tables-only", action="store_true",
                     help="time the edge-label workload with key and value tables only")
     a = ap.parse_args()
@@ -974,6 +1064,9 @@ def main():
         return
     if a.edge_only:
         print(json.dumps({"edge_bias": edge_report(ra, max(50, a.steps // 5))}))
+        return
+    if a.decode_xl_only:
+        print(json.dumps({"decode_xl": decode_xl_report(ra, max(50, a.steps // 5))}))
         return
     if a.edge_tables_only:
         print(json.dumps({"edge_tables": edge_report(ra, max(50, a.steps // 5), "edge_kv")}))
@@ -1038,6 +1131,7 @@ def main():
             per[name] = e
         line["workloads"] = per
         line["decode"] = decode_report(ra, max(50, a.steps // 5))
+        line["decode_xl"] = decode_xl_report(ra, max(50, a.steps // 5))
         line["offset_bias"] = alibi_report(ra, max(50, a.steps // 5))
         line["backward"] = bwd_report(ra, max(50, a.steps // 5))
         line["xl"] = xl_report(ra, max(50, a.steps // 5))
