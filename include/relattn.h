@@ -1,6 +1,7 @@
 /*
  * librelattn: fused forward of relation-aware self-attention on AMD MI355X
- * (gfx950), plus the T5 bucketed scalar-bias variant.
+ * (gfx950), plus the T5 bucketed scalar-bias variant and the related
+ * operators listed below.
  *
  * What is computed (one head; q_i, k_j, v_j are rows of q, k, v):
  *
@@ -20,6 +21,15 @@
  *     = num_buckets/2 buckets per sign, keys after the query (j > i) use the
  *     upper half; unidirectional: all buckets for j <= i, bucket 0 for j > i.
  *     B_exact = half/2; the floor in beta is taken of the exact real value.
+ *
+ *   Around these, each declared below with its own formula: incremental
+ *   decoding against a key/value cache (relattn_decode, _offset_bias, _xl), a
+ *   scalar bias by clipped offset such as ALiBi (relattn_fwd_offset_bias), the
+ *   backward with the table and bias gradients (relattn_bwd, _offset_bias),
+ *   Transformer-XL relative logits (relattn_fwd_xl), the 2-D window bias of
+ *   windowed vision models (relattn_fwd_grid_bias), and per-pair edge labels as a
+ *   scalar bias (relattn_fwd_edge_bias) or with key and value tables
+ *   (relattn_fwd_edge_tables).
  *
  *   Masks (no page defines them): causal hides keys j > i; key_lens[b] hides
  *   keys j >= key_lens[b] (clamped to [0, n]) of batch b.  A hidden key adds
