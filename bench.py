@@ -167,6 +167,31 @@ def ceiling_tflops(flops, nbytes, dt):
 # incremental decoding (the newest position of each sequence over its cache)
 # ---------------------------------------------------------------------------
 
+def time_calls(lib, fn, calls, steps, warmup, reps, stream):
+    """Median over ``reps`` timed regions of the time per call (ms) of ``steps``
+    back-to-back calls of the C entry point ``fn``, cycling through the argument
+    lists ``calls``, on ``stream`` between two HIP events, after ``warmup``
+    untimed calls."""
+    import statistics
+    import torch
+    times = []
+    with torch.cuda.stream(stream):
+        for s_ in range(warmup):
+            if fn(*calls[s_ % len(calls)]) != 0:
+                raise RuntimeError(lib.relattn_last_error().decode())
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        for _ in range(reps):
+            t0.record(stream)
+            for s_ in range(steps):
+                fn(*calls[s_ % len(calls)])
+            t1.record(stream)
+            torch.cuda.synchronize()
+            times.append(t0.elapsed_time(t1) / steps)
+    return statistics.median(times)
+
+
 def decode_work(w, cache_lens):
     """(flops, bytes) one decoding step must do: q.k and p.v for every visible
     key (4*d per key), the relative key term for the labels (2*d*(k+1)) and
@@ -185,7 +210,6 @@ def time_decode(ra, w, steps, warmup, hot=False, reps=1):
     """Time ``steps`` back-to-back decoding steps (median of ``reps`` timed
     regions).  Cold: the steps cycle through enough cache copies to exceed
     twice the last-level cache; hot: one cache, reused by every step."""
-    import statistics
     import torch
     import workloads
     lib = ra._load()
@@ -208,23 +232,8 @@ def time_decode(ra, w, steps, warmup, hot=False, reps=1):
                              ctypes.c_void_p(stream.cuda_stream)])
         keep += [g, out, ws, kp, outv]
     fn = lib.relattn_decode
-    times = []
-    with torch.cuda.stream(stream):
-        for s_ in range(warmup):
-            if fn(*calls[s_ % copies]) != 0:
-                raise RuntimeError(lib.relattn_last_error().decode())
-        torch.cuda.synchronize()
-        t0 = torch.cuda.Event(enable_timing=True)
-        t1 = torch.cuda.Event(enable_timing=True)
-        for _ in range(reps):
-            t0.record(stream)
-            for s_ in range(steps):
-                fn(*calls[s_ % copies])
-            t1.record(stream)
-            torch.cuda.synchronize()
-            times.append(t0.elapsed_time(t1) / steps)
+    ms = time_calls(lib, fn, calls, steps, warmup, reps, stream)
     del keep
-    ms = statistics.median(times)
     return {"ms_per_step": ms, "gbs": nbytes / (ms * 1e-3) / 1e9,
             "tflops": flops / (ms * 1e-3) / 1e12, "alg_mbytes": nbytes / 1e6,
             "alg_gflop": flops / 1e9, "input_copies": copies,
@@ -261,7 +270,6 @@ def time_decode_xl(ra, w, steps, warmup, hot=False, reps=1):
     u and v, seeded.  flops: 4*d per visible key (q.k, p.v) + 2*d ((q + v).R);
     bytes: every visible cache row of k and v once, q and out once, the table
     rows the longest row reaches once, u and v."""
-    import statistics
     import torch
     import workloads
     lib = ra._load()
@@ -296,23 +304,8 @@ def time_decode_xl(ra, w, steps, warmup, hot=False, reps=1):
                       ctypes.c_void_p(stream.cuda_stream)])
         keep += [g, t5, out, ws, views, outv]
     fn = lib.relattn_decode_xl
-    times = []
-    with torch.cuda.stream(stream):
-        for s_ in range(warmup):
-            if fn(*calls[s_ % copies]) != 0:
-                raise RuntimeError(lib.relattn_last_error().decode())
-        torch.cuda.synchronize()
-        t0 = torch.cuda.Event(enable_timing=True)
-        t1 = torch.cuda.Event(enable_timing=True)
-        for _ in range(reps):
-            t0.record(stream)
-            for s_ in range(steps):
-                fn(*calls[s_ % copies])
-            t1.record(stream)
-            torch.cuda.synchronize()
-            times.append(t0.elapsed_time(t1) / steps)
+    ms = time_calls(lib, fn, calls, steps, warmup, reps, stream)
     del keep
-    ms = statistics.median(times)
     return {"ms_per_step": ms, "gbs": nbytes / (ms * 1e-3) / 1e9,
             "tflops": flops / (ms * 1e-3) / 1e12, "alg_mbytes": nbytes / 1e6,
             "input_copies": copies, "tokens_per_s": w.batch * w.tq / (ms * 1e-3)}
@@ -362,7 +355,6 @@ def alibi_inputs():
 
 
 def time_alibi(ra, steps, warmup, hot=False, reps=5):
-    import statistics
     import torch
     lib = ra._load()
     stream = torch.cuda.Stream()
@@ -381,23 +373,8 @@ def time_alibi(ra, steps, warmup, hot=False, reps=5):
         calls.append(args + [ctypes.c_void_p(stream.cuda_stream)])
         keep += [g, out, kp]
     fn = lib.relattn_fwd_offset_bias
-    times = []
-    with torch.cuda.stream(stream):
-        for s_ in range(warmup):
-            if fn(*calls[s_ % copies]) != 0:
-                raise RuntimeError(lib.relattn_last_error().decode())
-        torch.cuda.synchronize()
-        t0 = torch.cuda.Event(enable_timing=True)
-        t1 = torch.cuda.Event(enable_timing=True)
-        for _ in range(reps):
-            t0.record(stream)
-            for s_ in range(steps):
-                fn(*calls[s_ % copies])
-            t1.record(stream)
-            torch.cuda.synchronize()
-            times.append(t0.elapsed_time(t1) / steps)
+    ms = time_calls(lib, fn, calls, steps, warmup, reps, stream)
     del keep
-    ms = statistics.median(times)
     sec = ms * 1e-3
     return {"ms_per_step": ms, "tflops": flops / sec / 1e12, "hbm_gbs": nbytes / sec / 1e9,
             "alg_gflop": flops / 1e9, "alg_mbytes": nbytes / 1e6, "input_copies": copies}
@@ -470,7 +447,6 @@ def time_bwd(ra, w, steps, warmup, hot=False, reps=5):
     """Time ``steps`` back-to-back relattn_bwd calls (median of ``reps``
     timed regions); cold: the calls cycle through enough input copies to
     exceed twice the last-level cache; hot: one input set."""
-    import statistics
     import torch
     import workloads
     lib = ra._load()
@@ -504,23 +480,8 @@ def time_bwd(ra, w, steps, warmup, hot=False, reps=5):
         keep += [g, dz, out, lse, grads, kp, ws]
     torch.cuda.synchronize()
     fn = lib.relattn_bwd
-    times = []
-    with torch.cuda.stream(stream):
-        for s_ in range(warmup):
-            if fn(*calls[s_ % copies]) != 0:
-                raise RuntimeError(lib.relattn_last_error().decode())
-        torch.cuda.synchronize()
-        t0 = torch.cuda.Event(enable_timing=True)
-        t1 = torch.cuda.Event(enable_timing=True)
-        for _ in range(reps):
-            t0.record(stream)
-            for s_ in range(steps):
-                fn(*calls[s_ % copies])
-            t1.record(stream)
-            torch.cuda.synchronize()
-            times.append(t0.elapsed_time(t1) / steps)
+    ms = time_calls(lib, fn, calls, steps, warmup, reps, stream)
     del keep
-    ms = statistics.median(times)
     sec = ms * 1e-3
     return {"ms_per_step": ms, "tflops": flops / sec / 1e12, "hbm_gbs": nbytes / sec / 1e9,
             "alg_gflop": flops / 1e9, "alg_mbytes": nbytes / 1e6, "input_copies": copies,
@@ -576,7 +537,6 @@ def xl_work(w):
 
 
 def time_xl(ra, steps, warmup, hot=False, reps=5):
-    import statistics
     import torch
     import workloads
     lib = ra._load()
@@ -594,23 +554,8 @@ def time_xl(ra, steps, warmup, hot=False, reps=5):
         calls.append(args + [ctypes.c_void_p(stream.cuda_stream)])
         keep += [g, out, kp]
     fn = lib.relattn_fwd_xl
-    times = []
-    with torch.cuda.stream(stream):
-        for s_ in range(warmup):
-            if fn(*calls[s_ % copies]) != 0:
-                raise RuntimeError(lib.relattn_last_error().decode())
-        torch.cuda.synchronize()
-        t0 = torch.cuda.Event(enable_timing=True)
-        t1 = torch.cuda.Event(enable_timing=True)
-        for _ in range(reps):
-            t0.record(stream)
-            for s_ in range(steps):
-                fn(*calls[s_ % copies])
-            t1.record(stream)
-            torch.cuda.synchronize()
-            times.append(t0.elapsed_time(t1) / steps)
+    ms = time_calls(lib, fn, calls, steps, warmup, reps, stream)
     del keep
-    ms = statistics.median(times)
     sec = ms * 1e-3
     return {"ms_per_step": ms, "tflops": flops / sec / 1e12, "hbm_gbs": nbytes / sec / 1e9,
             "alg_gflop": flops / 1e9, "alg_mbytes": nbytes / 1e6, "input_copies": copies}
@@ -655,7 +600,6 @@ def grid_work(w):
 
 
 def time_grid(ra, steps, warmup, hot=False, reps=5):
-    import statistics
     import torch
     import workloads
     lib = ra._load()
@@ -672,23 +616,8 @@ def time_grid(ra, steps, warmup, hot=False, reps=5):
         calls.append(args + [ctypes.c_void_p(stream.cuda_stream)])
         keep += [g, out, kp]
     fn = lib.relattn_fwd_grid_bias
-    times = []
-    with torch.cuda.stream(stream):
-        for s_ in range(warmup):
-            if fn(*calls[s_ % copies]) != 0:
-                raise RuntimeError(lib.relattn_last_error().decode())
-        torch.cuda.synchronize()
-        t0 = torch.cuda.Event(enable_timing=True)
-        t1 = torch.cuda.Event(enable_timing=True)
-        for _ in range(reps):
-            t0.record(stream)
-            for s_ in range(steps):
-                fn(*calls[s_ % copies])
-            t1.record(stream)
-            torch.cuda.synchronize()
-            times.append(t0.elapsed_time(t1) / steps)
+    ms = time_calls(lib, fn, calls, steps, warmup, reps, stream)
     del keep
-    ms = statistics.median(times)
     sec = ms * 1e-3
     return {"ms_per_step": ms, "tflops": flops / sec / 1e12, "hbm_gbs": nbytes / sec / 1e9,
             "alg_gflop": flops / 1e9, "alg_mbytes": nbytes / 1e6, "input_copies": copies}
@@ -740,7 +669,6 @@ def edge_work(w):
 
 
 def time_edge(ra, steps, warmup, hot=False, reps=5, name="edge"):
-    import statistics
     import torch
     import workloads
     lib = ra._load()
@@ -764,23 +692,8 @@ def time_edge(ra, steps, warmup, hot=False, reps=5, name="edge"):
         calls.append(args + [ctypes.c_void_p(stream.cuda_stream)])
         keep += [g, lab, out, kp]
     fn = lib.relattn_fwd_edge_tables if w.tables else lib.relattn_fwd_edge_bias
-    times = []
-    with torch.cuda.stream(stream):
-        for s_ in range(warmup):
-            if fn(*calls[s_ % copies]) != 0:
-                raise RuntimeError(lib.relattn_last_error().decode())
-        torch.cuda.synchronize()
-        t0 = torch.cuda.Event(enable_timing=True)
-        t1 = torch.cuda.Event(enable_timing=True)
-        for _ in range(reps):
-            t0.record(stream)
-            for s_ in range(steps):
-                fn(*calls[s_ % copies])
-            t1.record(stream)
-            torch.cuda.synchronize()
-            times.append(t0.elapsed_time(t1) / steps)
+    ms = time_calls(lib, fn, calls, steps, warmup, reps, stream)
     del keep
-    ms = statistics.median(times)
     sec = ms * 1e-3
     return {"ms_per_step": ms, "tflops": flops / sec / 1e12, "hbm_gbs": nbytes / sec / 1e9,
             "alg_gflop": flops / 1e9, "alg_mbytes": nbytes / 1e6, "input_copies": copies}
