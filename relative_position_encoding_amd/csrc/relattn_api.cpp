@@ -992,20 +992,54 @@ int run_bwd(BwdPlan& plan, const relattn_tensor* wK, const relattn_tensor* wV, b
   return RELATTN_OK;
 }
 
-int run_fwd_lse(Plan& plan, const relattn_tensor* lse, void* stream) {
-  if (plan.empty) return RELATTN_OK;
-  if (lse->stride[2] != 1)
-    return fail(RELATTN_ERR_UNSUPPORTED, "lse: innermost dimension must be contiguous");
+// Enqueue the forward launch of a made plan (nothing for an empty problem).
+int run_fwd(const Plan& plan, void* stream) {
   int st;
   if ((st = check_device())) return st;
-  plan.p.lse = static_cast<float*>(lse->data);
-  plan.p.lse_sb = lse->stride[0];
-  plan.p.lse_sh = lse->stride[1];
+  if (plan.empty) return RELATTN_OK;
   const int e = relattn::launch_fwd(plan.bf16, plan.d, plan.cfg, plan.mode, plan.has_wk,
                                     plan.has_wv, plan.p, stream);
   if (e != (int)hipSuccess)
     return fail(RELATTN_ERR_LAUNCH_FAILED, "launch failed: %s", hipGetErrorString((hipError_t)e));
   return RELATTN_OK;
+}
+
+// Check the cache lengths and workspace of a made decode plan, then enqueue it.
+int run_decode(DecPlan& plan, const int32_t* cache_lens, void* workspace,
+               size_t workspace_bytes, void* stream) {
+  if (cache_lens && (reinterpret_cast<uintptr_t>(cache_lens) & 3u))
+    return fail(RELATTN_ERR_INVALID_ARGUMENT, "cache_lens is not 4-byte aligned");
+  if (!plan.empty && plan.ws_bytes > 0) {
+    if (workspace_bytes < plan.ws_bytes)
+      return fail(RELATTN_ERR_INVALID_ARGUMENT, "workspace of %zu bytes, %zu needed",
+                  workspace_bytes, plan.ws_bytes);
+    if (!workspace || !aligned16(workspace))
+      return fail(RELATTN_ERR_INVALID_ARGUMENT, "workspace is NULL or not 16-byte aligned");
+  }
+  int st;
+  if ((st = check_device())) return st;
+  if (plan.empty) return RELATTN_OK;
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  plan.p.cache_lens = cache_lens;
+  plan.p.ws_ml = reinterpret_cast<float*>(ws);
+  plan.p.ws_o = reinterpret_cast<float*>(ws + plan.ws_o_off);
+  plan.p.ws_band = reinterpret_cast<float*>(ws + plan.ws_band_off);
+  const int e = relattn::launch_decode(plan.bf16, plan.d, plan.mode, plan.has_wk, plan.has_wv,
+                                       plan.p, stream);
+  if (e != (int)hipSuccess)
+    return fail(RELATTN_ERR_LAUNCH_FAILED, "launch failed: %s",
+                hipGetErrorString((hipError_t)e));
+  return RELATTN_OK;
+}
+
+int run_fwd_lse(Plan& plan, const relattn_tensor* lse, void* stream) {
+  if (plan.empty) return RELATTN_OK;
+  if (lse->stride[2] != 1)
+    return fail(RELATTN_ERR_UNSUPPORTED, "lse: innermost dimension must be contiguous");
+  plan.p.lse = static_cast<float*>(lse->data);
+  plan.p.lse_sb = lse->stride[0];
+  plan.p.lse_sh = lse->stride[1];
+  return run_fwd(plan, stream);
 }
 
 }  // namespace
@@ -1130,14 +1164,7 @@ int relattn_fwd(const relattn_tensor* q, const relattn_tensor* k, const relattn_
   Plan plan;
   int st = make_plan(q, k, v, wK, wV, t5_bias, t5, clip_k, scale, mask, out, &plan, true);
   if (st) return st;
-  if ((st = check_device())) return st;
-  if (plan.empty) return RELATTN_OK;
-  const int e = relattn::launch_fwd(plan.bf16, plan.d, plan.cfg, plan.mode, plan.has_wk,
-                                    plan.has_wv, plan.p, stream);
-  if (e != (int)hipSuccess)
-    return fail(RELATTN_ERR_LAUNCH_FAILED, "launch failed: %s",
-                hipGetErrorString((hipError_t)e));
-  return RELATTN_OK;
+  return run_fwd(plan, stream);
 }
 
 int relattn_validate_offset_bias(const relattn_tensor* q, const relattn_tensor* k,
@@ -1161,14 +1188,7 @@ int relattn_fwd_offset_bias(const relattn_tensor* q, const relattn_tensor* k,
   int st = make_plan(q, k, v, nullptr, nullptr, nullptr, nullptr, 0, scale, mask, out, &plan, true,
                      bias, window);
   if (st) return st;
-  if ((st = check_device())) return st;
-  if (plan.empty) return RELATTN_OK;
-  const int e = relattn::launch_fwd(plan.bf16, plan.d, plan.cfg, plan.mode, plan.has_wk,
-                                    plan.has_wv, plan.p, stream);
-  if (e != (int)hipSuccess)
-    return fail(RELATTN_ERR_LAUNCH_FAILED, "launch failed: %s",
-                hipGetErrorString((hipError_t)e));
-  return RELATTN_OK;
+  return run_fwd(plan, stream);
 }
 
 int relattn_validate_xl(const relattn_tensor* q, const relattn_tensor* k, const relattn_tensor* v,
@@ -1192,13 +1212,7 @@ int relattn_fwd_xl(const relattn_tensor* q, const relattn_tensor* k, const relat
   int st = make_plan(q, k, v, R, nullptr, nullptr, nullptr, window, scale, mask, out, &plan, true,
                      nullptr, 0, u, vb);
   if (st) return st;
-  if ((st = check_device())) return st;
-  if (plan.empty) return RELATTN_OK;
-  const int e = relattn::launch_fwd(plan.bf16, plan.d, plan.cfg, plan.mode, plan.has_wk,
-                                    plan.has_wv, plan.p, stream);
-  if (e != (int)hipSuccess)
-    return fail(RELATTN_ERR_LAUNCH_FAILED, "launch failed: %s", hipGetErrorString((hipError_t)e));
-  return RELATTN_OK;
+  return run_fwd(plan, stream);
 }
 
 int relattn_validate_grid_bias(const relattn_tensor* q, const relattn_tensor* k,
@@ -1224,13 +1238,7 @@ int relattn_fwd_grid_bias(const relattn_tensor* q, const relattn_tensor* k,
   int st = make_plan(q, k, v, nullptr, nullptr, nullptr, nullptr, 0, scale, mask, out, &plan, true,
                      bias, 0, nullptr, nullptr, window_side);
   if (st) return st;
-  if ((st = check_device())) return st;
-  if (plan.empty) return RELATTN_OK;
-  const int e = relattn::launch_fwd(plan.bf16, plan.d, plan.cfg, plan.mode, plan.has_wk,
-                                    plan.has_wv, plan.p, stream);
-  if (e != (int)hipSuccess)
-    return fail(RELATTN_ERR_LAUNCH_FAILED, "launch failed: %s", hipGetErrorString((hipError_t)e));
-  return RELATTN_OK;
+  return run_fwd(plan, stream);
 }
 
 int relattn_validate_edge_bias(const relattn_tensor* q, const relattn_tensor* k,
@@ -1256,13 +1264,7 @@ int relattn_fwd_edge_bias(const relattn_tensor* q, const relattn_tensor* k,
   int st = make_plan(q, k, v, nullptr, nullptr, nullptr, nullptr, 0, scale, mask, out, &plan, true,
                      bias, 0, nullptr, nullptr, 0, labels);
   if (st) return st;
-  if ((st = check_device())) return st;
-  if (plan.empty) return RELATTN_OK;
-  const int e = relattn::launch_fwd(plan.bf16, plan.d, plan.cfg, plan.mode, plan.has_wk,
-                                    plan.has_wv, plan.p, stream);
-  if (e != (int)hipSuccess)
-    return fail(RELATTN_ERR_LAUNCH_FAILED, "launch failed: %s", hipGetErrorString((hipError_t)e));
-  return RELATTN_OK;
+  return run_fwd(plan, stream);
 }
 
 int relattn_validate_edge_tables(const relattn_tensor* q, const relattn_tensor* k,
@@ -1286,13 +1288,7 @@ int relattn_fwd_edge_tables(const relattn_tensor* q, const relattn_tensor* k,
   int st = make_plan(q, k, v, wK, wV, nullptr, nullptr, 0, scale, mask, out, &plan, true, nullptr,
                      0, nullptr, nullptr, 0, labels);
   if (st) return st;
-  if ((st = check_device())) return st;
-  if (plan.empty) return RELATTN_OK;
-  const int e = relattn::launch_fwd(plan.bf16, plan.d, plan.cfg, plan.mode, plan.has_wk,
-                                    plan.has_wv, plan.p, stream);
-  if (e != (int)hipSuccess)
-    return fail(RELATTN_ERR_LAUNCH_FAILED, "launch failed: %s", hipGetErrorString((hipError_t)e));
-  return RELATTN_OK;
+  return run_fwd(plan, stream);
 }
 
 int relattn_debug_indices(int32_t n, int32_t clip_k, const relattn_t5_params* t5,
@@ -1337,28 +1333,7 @@ int relattn_decode(const relattn_tensor* q, const relattn_tensor* k, const relat
   DecPlan plan;
   int st = make_dec_plan(q, k, v, wK, wV, t5_bias, t5, clip_k, scale, out, &plan, true);
   if (st) return st;
-  if (cache_lens && (reinterpret_cast<uintptr_t>(cache_lens) & 3u))
-    return fail(RELATTN_ERR_INVALID_ARGUMENT, "cache_lens is not 4-byte aligned");
-  if (!plan.empty && plan.ws_bytes > 0) {
-    if (workspace_bytes < plan.ws_bytes)
-      return fail(RELATTN_ERR_INVALID_ARGUMENT, "workspace of %zu bytes, %zu needed",
-                  workspace_bytes, plan.ws_bytes);
-    if (!workspace || !aligned16(workspace))
-      return fail(RELATTN_ERR_INVALID_ARGUMENT, "workspace is NULL or not 16-byte aligned");
-  }
-  if ((st = check_device())) return st;
-  if (plan.empty) return RELATTN_OK;
-  unsigned char* ws = static_cast<unsigned char*>(workspace);
-  plan.p.cache_lens = cache_lens;
-  plan.p.ws_ml = reinterpret_cast<float*>(ws);
-  plan.p.ws_o = reinterpret_cast<float*>(ws + plan.ws_o_off);
-  plan.p.ws_band = reinterpret_cast<float*>(ws + plan.ws_band_off);
-  const int e = relattn::launch_decode(plan.bf16, plan.d, plan.mode, plan.has_wk, plan.has_wv,
-                                       plan.p, stream);
-  if (e != (int)hipSuccess)
-    return fail(RELATTN_ERR_LAUNCH_FAILED, "launch failed: %s",
-                hipGetErrorString((hipError_t)e));
-  return RELATTN_OK;
+  return run_decode(plan, cache_lens, workspace, workspace_bytes, stream);
 }
 
 int relattn_decode_xl_workspace_size(const relattn_tensor* q, const relattn_tensor* k,
@@ -1387,28 +1362,7 @@ int relattn_decode_xl(const relattn_tensor* q, const relattn_tensor* k, const re
   int st = make_dec_plan(q, k, v, R, nullptr, nullptr, nullptr, window, scale, out, &plan, true,
                          nullptr, 0, u, vb);
   if (st) return st;
-  if (cache_lens && (reinterpret_cast<uintptr_t>(cache_lens) & 3u))
-    return fail(RELATTN_ERR_INVALID_ARGUMENT, "cache_lens is not 4-byte aligned");
-  if (!plan.empty && plan.ws_bytes > 0) {
-    if (workspace_bytes < plan.ws_bytes)
-      return fail(RELATTN_ERR_INVALID_ARGUMENT, "workspace of %zu bytes, %zu needed",
-                  workspace_bytes, plan.ws_bytes);
-    if (!workspace || !aligned16(workspace))
-      return fail(RELATTN_ERR_INVALID_ARGUMENT, "workspace is NULL or not 16-byte aligned");
-  }
-  if ((st = check_device())) return st;
-  if (plan.empty) return RELATTN_OK;
-  unsigned char* ws = static_cast<unsigned char*>(workspace);
-  plan.p.cache_lens = cache_lens;
-  plan.p.ws_ml = reinterpret_cast<float*>(ws);
-  plan.p.ws_o = reinterpret_cast<float*>(ws + plan.ws_o_off);
-  plan.p.ws_band = reinterpret_cast<float*>(ws + plan.ws_band_off);
-  const int e = relattn::launch_decode(plan.bf16, plan.d, plan.mode, plan.has_wk, plan.has_wv,
-                                       plan.p, stream);
-  if (e != (int)hipSuccess)
-    return fail(RELATTN_ERR_LAUNCH_FAILED, "launch failed: %s",
-                hipGetErrorString((hipError_t)e));
-  return RELATTN_OK;
+  return run_decode(plan, cache_lens, workspace, workspace_bytes, stream);
 }
 
 int relattn_decode_offset_bias_workspace_size(const relattn_tensor* q, const relattn_tensor* k,
@@ -1436,28 +1390,7 @@ int relattn_decode_offset_bias(const relattn_tensor* q, const relattn_tensor* k,
   int st = make_dec_plan(q, k, v, nullptr, nullptr, nullptr, nullptr, 0, scale, out, &plan, true,
                          bias, window);
   if (st) return st;
-  if (cache_lens && (reinterpret_cast<uintptr_t>(cache_lens) & 3u))
-    return fail(RELATTN_ERR_INVALID_ARGUMENT, "cache_lens is not 4-byte aligned");
-  if (!plan.empty && plan.ws_bytes > 0) {
-    if (workspace_bytes < plan.ws_bytes)
-      return fail(RELATTN_ERR_INVALID_ARGUMENT, "workspace of %zu bytes, %zu needed",
-                  workspace_bytes, plan.ws_bytes);
-    if (!workspace || !aligned16(workspace))
-      return fail(RELATTN_ERR_INVALID_ARGUMENT, "workspace is NULL or not 16-byte aligned");
-  }
-  if ((st = check_device())) return st;
-  if (plan.empty) return RELATTN_OK;
-  unsigned char* ws = static_cast<unsigned char*>(workspace);
-  plan.p.cache_lens = cache_lens;
-  plan.p.ws_ml = reinterpret_cast<float*>(ws);
-  plan.p.ws_o = reinterpret_cast<float*>(ws + plan.ws_o_off);
-  plan.p.ws_band = reinterpret_cast<float*>(ws + plan.ws_band_off);
-  const int e = relattn::launch_decode(plan.bf16, plan.d, plan.mode, plan.has_wk, plan.has_wv,
-                                       plan.p, stream);
-  if (e != (int)hipSuccess)
-    return fail(RELATTN_ERR_LAUNCH_FAILED, "launch failed: %s",
-                hipGetErrorString((hipError_t)e));
-  return RELATTN_OK;
+  return run_decode(plan, cache_lens, workspace, workspace_bytes, stream);
 }
 
 const char* relattn_strerror(int status) {
