@@ -194,3 +194,36 @@ def test_edge_bias_long_rows(ra, causal):
     out = run(ra, q, k, v, E, bias, causal=causal, key_lens=[1900])
     want = oracle.edge_label_attention(q, k, v, E, bias, causal=causal, key_lens=[1900])
     assert float(np.max(np.abs(out.double().cpu().numpy() - want))) <= TOL[torch.bfloat16]
+
+
+def test_edge_modes_rows_without_visible_keys_output_zeros(ra):
+    """A batch entry with key length 0: every row of it outputs zeros, in the
+    label mode, the graph mode and the fused Transformer-XL mode (the other
+    entry is checked against its oracle)."""
+    B, H, n, d, NL = 2, 2, 90, 64, 10
+    q, k, v = (gen((B, H, n, d), torch.bfloat16, 2800 + i) for i in range(3))
+    E = np.random.default_rng(2803).integers(0, NL, (B, n, n))
+    lens = torch.tensor([0, 70], dtype=torch.int32, device=DEV)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    bias = gen((H, NL), torch.float32, 2804)
+    wK, wV = gen((H, NL, d), torch.bfloat16, 2805, 0.5), gen((H, NL, d), torch.bfloat16, 2806, 0.5)
+    R = gen((H, 2 * n - 1, d), torch.bfloat16, 2807, 0.5)
+    u, vb = gen((H, d), torch.bfloat16, 2808, 0.5), gen((H, d), torch.bfloat16, 2809, 0.5)
+    outs = {
+        "label": ra.fwd_edge_bias(qd, kd, vd, labels_of(ra, E), bias.to(DEV), key_lens=lens),
+        "graph": ra.fwd_edge_tables(qd, kd, vd, labels_of(ra, E), wK.to(DEV), wV.to(DEV),
+                                    key_lens=lens),
+        "xl": ra.fwd_xl(qd, kd, vd, R.to(DEV), u.to(DEV), vb.to(DEV), n - 1, causal=True,
+                        key_lens=lens),
+    }
+    torch.cuda.synchronize()
+    wants = {
+        "label": oracle.edge_label_attention(q[1:], k[1:], v[1:], E[1:], bias, key_lens=[70]),
+        "graph": oracle.edge_label_relattn(q[1:], k[1:], v[1:], E[1:], wK, wV, key_lens=[70]),
+        "xl": oracle.xl_attention(q[1:], k[1:], v[1:], R, u, vb, n - 1, causal=True,
+                                  key_lens=[70]),
+    }
+    for name, out in outs.items():
+        assert torch.count_nonzero(out[0]) == 0, name
+        err = float(np.max(np.abs(out[1:].double().cpu().numpy() - wants[name])))
+        assert err <= TOL[torch.bfloat16], (name, err)
