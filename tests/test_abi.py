@@ -438,3 +438,13 @@ def test_decode_xl_checks(ra):
         with pytest.raises(ra.RelattnError) as e:
             ra.decode_xl_workspace_size(q, k, v, *args)
         assert e.value.status == ra.INVALID_ARGUMENT
+
+
+def test_edge_tables_vocabulary_too_wide_for_chip(ra):
+    """At d = 128 the rows of 256 labels (label logits and two weight sums per
+    query) do not fit beside the K/V ring: UNSUPPORTED from the host plan."""
+    B, H, n = 1, 2, 64
+    q = T(B, H, n, 128)
+    lab = ra.edge_label_buffer(B, n)
+    assert ra.validate_edge_tables(q, q, q, lab, T(H, 200, 128), T(H, 200, 128)) == ra.OK
+    assert ra.validate_edge_tables(q, q, q, lab, T(H, 256, 128), T(H, 256, 128)) == ra.UNSUPPORTED

@@ -182,3 +182,18 @@ def test_edge_tables_long_rows(ra, causal):
     got = run(ra, q, k, v, E, wK, wV, causal=causal, lens=[555])
     want = oracle.edge_label_relattn(q, k, v, E, wK, wV, causal=causal, key_lens=[555])
     assert float(np.max(np.abs(got - want))) <= TOL[torch.bfloat16]
+
+
+@pytest.mark.parametrize("d,NL", [(64, 256), (128, 200)])
+def test_edge_tables_largest_vocabulary(ra, d, NL):
+    """The largest vocabularies that fit (256 labels, all the uint8 labels
+    address, at d = 64; 200 at d = 128): the per-query label rows and weight
+    sums take most of the LDS, the plan falls back to smaller workgroups and
+    staged value tables."""
+    B, H, n = 2, 2, 150
+    q, k, v = (gen((B, H, n, d), torch.bfloat16, 3700 + d + i) for i in range(3))
+    wK, wV = gen((H, NL, d), torch.bfloat16, 3703, 0.5), gen((H, NL, d), torch.bfloat16, 3704, 0.5)
+    E = np.random.default_rng(3705).integers(0, NL, (B, n, n))
+    got = run(ra, q, k, v, E, wK, wV, causal=True, lens=[n, 120])
+    want = oracle.edge_label_relattn(q, k, v, E, wK, wV, causal=True, key_lens=[n, 120])
+    assert float(np.max(np.abs(got - want))) <= TOL[torch.bfloat16]
