@@ -22,7 +22,7 @@ Sources (page titles, then section / equation):
 * "Relative position embeddings" (survey page), section "T5": the scalar bias
   A_ij = q_i.k_j + b^(h)_beta(j-i), the bucket function beta, no 1/sqrt(d).
 
-Readings where the pages are silent or garbled (each is listed in the design doc):
+Readings where the pages are silent or garbled:
 
 * offset sign is j - i, table row 0 holds offset -k;
 * tables are [Ht, 2k+1, d] with Ht in {1, H} (Ht == 1: shared by all heads);
