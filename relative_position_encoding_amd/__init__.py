@@ -8,6 +8,7 @@ if the library is missing, every call raises.
 from __future__ import annotations
 
 import ctypes
+import functools
 import os
 
 __all__ = ["fwd", "validate", "fwd_offset_bias", "validate_offset_bias", "decode",
@@ -193,6 +194,26 @@ def _raise(lib, status):
     raise RelattnError(status, f"relattn: {lib.relattn_strerror(status).decode()}: {msg}")
 
 
+def _on_stream(fn):
+    """Run a binding call with the stream it enqueues on as torch's current
+    stream.  Every tensor the binding allocates for the call (outputs,
+    workspace) then comes from the caching allocator's pool of that stream, so
+    a workspace dropped when the call returns is handed out again only to work
+    ordered after the kernels that use it, whichever stream the caller names.
+    A raw hipStream_t handle is wrapped as an external torch stream."""
+    @functools.wraps(fn)
+    def call(*args, stream=None, **kw):
+        if stream is None:
+            return fn(*args, **kw)
+        import torch
+        if not hasattr(stream, "cuda_stream"):
+            stream = torch.cuda.ExternalStream(int(stream))
+        with torch.cuda.stream(stream):
+            return fn(*args, **kw)
+    return call
+
+
+@_on_stream
 def fwd(q, k, v, wK=None, wV=None, *, clip=0, causal=False, key_lens=None,
         t5_bias=None, num_buckets=32, max_distance=128, bidirectional=True,
         scale=None, out=None, stream=None):
@@ -240,6 +261,7 @@ def last_error() -> str:
     return _load().relattn_last_error().decode()
 
 
+@_on_stream
 def debug_indices(n, clip=0, *, t5=False, num_buckets=32, max_distance=128,
                   bidirectional=True, device="cuda", stream=None):
     """Per-offset integer indices computed on the GPU by the kernels' own index
@@ -288,6 +310,7 @@ def decode_workspace_size(q, k, v, wK=None, wV=None, *, clip=0, t5_bias=None,
     return int(nbytes.value)
 
 
+@_on_stream
 def decode(q, k, v, wK=None, wV=None, *, clip=0, cache_lens=None, t5_bias=None,
            num_buckets=32, max_distance=128, bidirectional=True, scale=None, out=None,
            workspace=None, stream=None):
@@ -338,6 +361,7 @@ def _ob_args(q, k, v, bias, window, causal, key_lens, scale, out):
     return args, views + [mask, outv]
 
 
+@_on_stream
 def fwd_offset_bias(q, k, v, bias, window, *, causal=False, key_lens=None, scale=None,
                     out=None, stream=None):
     """Attention with a scalar bias by clipped offset: bias [H or 1, 2*window+1]
@@ -393,6 +417,7 @@ def _new_lse(q):
     return torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
 
 
+@_on_stream
 def fwd_lse(q, k, v, wK=None, wV=None, *, clip=0, causal=False, key_lens=None,
             t5_bias=None, num_buckets=32, max_distance=128, bidirectional=True,
             scale=None, out=None, lse=None, stream=None):
@@ -416,6 +441,7 @@ def fwd_lse(q, k, v, wK=None, wV=None, *, clip=0, causal=False, key_lens=None,
     return out, lse
 
 
+@_on_stream
 def fwd_offset_bias_lse(q, k, v, bias, window, *, causal=False, key_lens=None, scale=None,
                         out=None, lse=None, stream=None):
     """``fwd_offset_bias`` with the row log-sum-exp; returns (out, lse)."""
@@ -477,6 +503,7 @@ def bwd_workspace_size(q, k, v, wK=None, wV=None, *, out, dout, lse, clip=0, cau
     return int(n.value)
 
 
+@_on_stream
 def bwd(q, k, v, wK=None, wV=None, *, out, dout, lse, clip=0, causal=False, key_lens=None,
         t5_bias=None, num_buckets=32, max_distance=128, bidirectional=True, scale=None,
         dq=None, dk=None, dv=None, dwK=None, dwV=None, dbias=None, want_dwk=True,
@@ -532,6 +559,7 @@ def bwd_offset_bias_workspace_size(q, k, v, bias, window, *, out, dout, lse, cau
     return int(n.value)
 
 
+@_on_stream
 def bwd_offset_bias(q, k, v, bias, window, *, out, dout, lse, causal=False, key_lens=None,
                     scale=None, dq=None, dk=None, dv=None, dbias=None, want_dbias=True,
                     workspace=None, stream=None):
@@ -641,6 +669,7 @@ def _xl_args(q, k, v, R, u, vb, window, causal, key_lens, scale, out):
     return args, views + [mask, outv]
 
 
+@_on_stream
 def fwd_xl(q, k, v, R, u, vb, window, *, causal=False, key_lens=None, scale=None, out=None,
            stream=None):
     """Transformer-XL relative logits: e_ij = s[(q_i + u).k_j + (q_i + vb).R_{i-j}].
@@ -675,6 +704,7 @@ def validate_xl(q, k, v, R, u, vb, window, *, causal=False, key_lens=None, scale
 # 2-D window bias (Swin)
 # ---------------------------------------------------------------------------
 
+@_on_stream
 def fwd_grid_bias(q, k, v, bias, window_side, *, key_lens=None, scale=None, out=None,
                   stream=None):
     """Relative position bias on an M x M window (n = M*M raster tokens): bias
@@ -735,6 +765,7 @@ def _edge_args(q, k, v, labels, bias, causal, key_lens, scale, out, tables=None)
     return args, views + [mask, outv]
 
 
+@_on_stream
 def fwd_edge_bias(q, k, v, labels, bias, *, causal=False, key_lens=None, scale=None, out=None,
                   stream=None):
     """Attention with a scalar bias by a per-pair label: labels uint8 [B, n, n]
@@ -765,6 +796,7 @@ def validate_edge_bias(q, k, v, labels, bias, *, causal=False, key_lens=None, sc
     return st
 
 
+@_on_stream
 def fwd_edge_tables(q, k, v, labels, wK=None, wV=None, *, causal=False, key_lens=None,
                     scale=None, out=None, stream=None):
     """Relation-aware attention over a labeled graph: labels uint8 [B, n, n]
@@ -809,6 +841,7 @@ def decode_offset_bias_workspace_size(q, k, v, bias, window, *, scale=None, out=
     return nbytes.value
 
 
+@_on_stream
 def decode_offset_bias(q, k, v, bias, window, *, cache_lens=None, scale=None, out=None,
                        workspace=None, stream=None):
     """Incremental decoding (positions as for ``decode``) with a scalar bias by
@@ -851,6 +884,7 @@ def decode_xl_workspace_size(q, k, v, R, u, vb, window, *, scale=None, out=None)
     return nbytes.value
 
 
+@_on_stream
 def decode_xl(q, k, v, R, u, vb, window, *, cache_lens=None, scale=None, out=None,
               workspace=None, stream=None):
     """Incremental decoding (positions as for ``decode``) with Transformer-XL

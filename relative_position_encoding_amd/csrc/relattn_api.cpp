@@ -10,6 +10,7 @@
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <cstring>
 #include <string>
 #include <vector>
 
@@ -426,6 +427,20 @@ int make_plan(const relattn_tensor* q, const relattn_tensor* k, const relattn_te
   // of this grid resident per compute unit (two per SIMD for d <= 64, one
   // for d = 128, as the kernels are compiled); ties go to the earlier one.
   const int nb = is_t5 ? t5->num_buckets : (is_ob ? p.t5.nb : 0);  // entries staged
+  // A window whose per-query rows (or per-head vector) alone exceed a
+  // workgroup's LDS can never fit.  Rejecting it before any layout is sized
+  // also keeps the layouts' 32-bit byte arithmetic far from overflow (rows of
+  // 2^22 labels times 128 query rows would wrap).
+  {
+    constexpr int64_t kMaxEntries = (int64_t)(kMaxLdsBytes / 4);  // fp32 entries
+    const int64_t win = (P.mode == relattn::kRelShaw || P.mode == relattn::kRelGraph)
+                            ? (int64_t)p.nr
+                            : 2 * (int64_t)p.t5_dist + 1;
+    if (win > kMaxEntries || (int64_t)nb > kMaxEntries)
+      return fail(RELATTN_ERR_UNSUPPORTED,
+                  "a window of %lld offsets (%d staged entries) does not fit on chip",
+                  (long long)win, nb);
+  }
   auto lds_of = [&](const LaunchCfg& c) {
     return relattn::lds_bytes(P.bf16, P.d, c, P.mode, P.has_wk, P.has_wv, p.nr, p.t5_dist, nb);
   };
@@ -1042,6 +1057,121 @@ int run_fwd_lse(Plan& plan, const relattn_tensor* lse, void* stream) {
   return run_fwd(plan, stream);
 }
 
+// ---- plan cache of the forward -------------------------------------------
+// A forward plan depends on the arguments' dtypes, shapes, strides and scalars,
+// and on the data pointers only through their nullness and 16-byte alignment.
+// Each thread keeps its last few plans keyed on exactly those facts: a hit
+// copies the cached plan and substitutes the call's pointers, so a repeated
+// call costs a key comparison instead of the validation and the search over
+// launch shapes.  The cache is thread-local (no locks) and a fixed array (no
+// allocation); only plans that passed every check are stored.
+struct TensorKey {
+  int64_t shape[4], stride[4];
+  int32_t dtype, ndim;
+  uint32_t ptr_bits;  // 0: NULL view; else 1 + (data & 15), or 32 for a non-NULL view without data
+};
+struct FwdKey {
+  TensorKey t[7];  // q, k, v, wK, wV, t5_bias, out
+  relattn_t5_params t5;
+  int32_t has_t5, clip, causal, has_mask;
+  uint32_t lens_bits;  // 0: no key lengths; else 1 + (pointer & 3)
+  float scale;
+};
+
+bool make_tensor_key(const relattn_tensor* t, TensorKey* k) {
+  if (!t) return true;  // stays all zero
+  if (t->ndim < 0 || t->ndim > 4) return false;
+  k->dtype = t->dtype;
+  k->ndim = t->ndim;
+  for (int i = 0; i < t->ndim; ++i) {
+    k->shape[i] = t->shape[i];
+    k->stride[i] = t->stride[i];
+  }
+  const uintptr_t a = reinterpret_cast<uintptr_t>(t->data);
+  k->ptr_bits = a ? 1u + (uint32_t)(a & 15u) : 32u;
+  return true;
+}
+
+bool make_fwd_key(const relattn_tensor* q, const relattn_tensor* k, const relattn_tensor* v,
+                  const relattn_tensor* wK, const relattn_tensor* wV,
+                  const relattn_tensor* t5_bias, const relattn_t5_params* t5, int32_t clip_k,
+                  float scale, const relattn_mask* mask, const relattn_tensor* out,
+                  FwdKey* key) {
+  // cleared whole, padding included, so that keys compare with memcmp
+  std::memset(key, 0, sizeof *key);
+  const relattn_tensor* ts[7] = {q, k, v, wK, wV, t5_bias, out};
+  for (int i = 0; i < 7; ++i)
+    if (!make_tensor_key(ts[i], &key->t[i])) return false;
+  if (t5) {
+    key->t5 = *t5;
+    key->has_t5 = 1;
+  }
+  key->clip = clip_k;
+  key->scale = scale;
+  if (mask) {
+    key->has_mask = 1;
+    key->causal = mask->causal;
+    const uintptr_t a = reinterpret_cast<uintptr_t>(mask->key_lens);
+    key->lens_bits = a ? 1u + (uint32_t)(a & 3u) : 0u;
+  }
+  return !std::isnan(scale);  // NaN never compares equal: not cached (and rejected anyway)
+}
+
+constexpr int kPlanCacheSize = 8;
+struct PlanCacheEntry {
+  bool used;
+  FwdKey key;
+  Plan plan;
+};
+thread_local PlanCacheEntry g_plan_cache[kPlanCacheSize];
+thread_local int g_plan_cache_next = 0;
+
+// The call's pointers into a plan made for other pointers with the same key.
+void rebind_plan(Plan* P, const relattn_tensor* q, const relattn_tensor* k,
+                 const relattn_tensor* v, const relattn_tensor* wK, const relattn_tensor* wV,
+                 const relattn_tensor* t5_bias, const relattn_mask* mask,
+                 const relattn_tensor* out) {
+  FwdParams& p = P->p;
+  p.q = q->data;
+  p.k = k->data;
+  p.v = v->data;
+  p.o = out->data;
+  p.wk = wK ? wK->data : nullptr;
+  p.wv = wV ? wV->data : nullptr;
+  p.t5_bias = t5_bias ? static_cast<const float*>(t5_bias->data) : nullptr;
+  p.key_lens = mask ? mask->key_lens : nullptr;
+  p.lse = nullptr;
+}
+
+// make_plan (with the T5 thresholds) through the cache.
+int cached_fwd_plan(const relattn_tensor* q, const relattn_tensor* k, const relattn_tensor* v,
+                    const relattn_tensor* wK, const relattn_tensor* wV,
+                    const relattn_tensor* t5_bias, const relattn_t5_params* t5, int32_t clip_k,
+                    float scale, const relattn_mask* mask, const relattn_tensor* out,
+                    Plan* plan) {
+  FwdKey key;
+  const bool keyed = q && k && v && out &&
+                     make_fwd_key(q, k, v, wK, wV, t5_bias, t5, clip_k, scale, mask, out, &key);
+  if (keyed) {
+    for (int i = 0; i < kPlanCacheSize; ++i) {
+      const PlanCacheEntry& e = g_plan_cache[i];
+      if (e.used && std::memcmp(&e.key, &key, sizeof key) == 0) {
+        *plan = e.plan;
+        if (!plan->empty) rebind_plan(plan, q, k, v, wK, wV, t5_bias, mask, out);
+        return RELATTN_OK;
+      }
+    }
+  }
+  const int st = make_plan(q, k, v, wK, wV, t5_bias, t5, clip_k, scale, mask, out, plan, true);
+  if (st || !keyed) return st;
+  PlanCacheEntry& e = g_plan_cache[g_plan_cache_next];
+  g_plan_cache_next = (g_plan_cache_next + 1) % kPlanCacheSize;
+  e.used = true;
+  e.key = key;
+  e.plan = *plan;
+  return RELATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -1053,7 +1183,7 @@ int relattn_fwd_lse(const relattn_tensor* q, const relattn_tensor* k, const rela
                     relattn_tensor* lse, void* stream) {
   g_last_error.clear();
   Plan plan;
-  int st = make_plan(q, k, v, wK, wV, t5_bias, t5, clip_k, scale, mask, out, &plan, true);
+  int st = cached_fwd_plan(q, k, v, wK, wV, t5_bias, t5, clip_k, scale, mask, out, &plan);
   if (st) return st;
   if ((st = check_lse(lse, q))) return st;
   return run_fwd_lse(plan, lse, stream);
@@ -1162,7 +1292,7 @@ int relattn_fwd(const relattn_tensor* q, const relattn_tensor* k, const relattn_
                 float scale, const relattn_mask* mask, relattn_tensor* out, void* stream) {
   g_last_error.clear();
   Plan plan;
-  int st = make_plan(q, k, v, wK, wV, t5_bias, t5, clip_k, scale, mask, out, &plan, true);
+  const int st = cached_fwd_plan(q, k, v, wK, wV, t5_bias, t5, clip_k, scale, mask, out, &plan);
   if (st) return st;
   return run_fwd(plan, stream);
 }

@@ -1309,12 +1309,9 @@ static int launch_q(const BwdParams& p, hipStream_t s) {
   const bool want_db = MODE == kRelT5 && p.ws_pb != nullptr;
   const LayQ lay = make_lay_q<BF16, D, NW, BC>(MODE, WK, WV, p.nr, p.t5_dist, p.t5.nb, want_db);
   auto kern = bwd_q_kernel<D, NW, BC, BF16, MODE, WK, WV>;
-  if (lay.total > 64 * 1024) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize,
-                                             lay.total);
-    if (e != hipSuccess) return (int)e;
-  }
+  static std::atomic<int> lds_set[64];
+  const hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(kern), lay.total, lds_set);
+  if (e != hipSuccess) return (int)e;
   const dim3 grid((unsigned)((int64_t)p.B * p.H * p.n_qtiles));
   hipLaunchKernelGGL(kern, grid, dim3(64 * NW), (size_t)lay.total, s, p);
   return (int)hipGetLastError();
@@ -1324,12 +1321,9 @@ template <int D, int NW, int BQ, bool BF16, int MODE, bool WK, bool WV>
 static int launch_kv(const BwdParams& p, hipStream_t s) {
   const LayKV lay = make_lay_kv<BF16, D, NW, BQ>(MODE, WK, WV, p.nr, p.t5_dist);
   auto kern = bwd_kv_kernel<D, NW, BQ, BF16, MODE, WK, WV>;
-  if (lay.total > 64 * 1024) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize,
-                                             lay.total);
-    if (e != hipSuccess) return (int)e;
-  }
+  static std::atomic<int> lds_set[64];
+  const hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(kern), lay.total, lds_set);
+  if (e != hipSuccess) return (int)e;
   const dim3 grid((unsigned)((int64_t)p.B * p.H * p.n_ktiles));
   hipLaunchKernelGGL(kern, grid, dim3(64 * NW), (size_t)max(lay.total, 64 * NW * 4), s, p);
   return (int)hipGetLastError();

@@ -1093,12 +1093,9 @@ static int launch_t(const FwdParams& p, void* stream) {
   auto kern = fwd_kernel<D, NW, BC, BF16, MODE, HAS_WK, HAS_WV>;
   const size_t lds = lds_bytes_t<BF16, D, NW, BC>((RelMode)MODE, HAS_WK, HAS_WV, p.nr,
                                                   p.nstage, p.t5_dist, p.t5.nb, p.wv_mode);
-  if (lds > 64 * 1024) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)lds);
-    if (e != hipSuccess) return (int)e;
-  }
+  static std::atomic<int> lds_set[64];
+  const hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(kern), lds, lds_set);
+  if (e != hipSuccess) return (int)e;
   const long long grid = (long long)p.B * p.H * p.n_qtiles;
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * NW), lds,
                      reinterpret_cast<hipStream_t>(stream), p);

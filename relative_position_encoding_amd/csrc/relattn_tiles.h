@@ -4,6 +4,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+
 #include "relattn_device.h"
 
 namespace relattn {
@@ -289,6 +291,24 @@ __device__ __forceinline__ float halves_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
                                                   false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// Host: allow a kernel `lds` bytes of dynamic LDS (needed above 64 KB), at most
+// once per kernel, device and size: `done` (one per kernel) remembers the
+// largest size set on each device, so repeated launches skip the runtime call.
+inline hipError_t allow_dynamic_lds(const void* kern, size_t lds, std::atomic<int> (&done)[64]) {
+  if (lds <= 64 * 1024) return hipSuccess;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = -1;
+  if (dev >= 0 && done[dev].load(std::memory_order_relaxed) >= (int)lds) return hipSuccess;
+  const hipError_t e =
+      hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e == hipSuccess && dev >= 0) {
+    int seen = done[dev].load(std::memory_order_relaxed);
+    while (seen < (int)lds && !done[dev].compare_exchange_weak(seen, (int)lds)) {
+    }
+  }
+  return e;
 }
 
 }  // namespace relattn

@@ -101,6 +101,19 @@ def test_invalid_arguments(ra, case):
     assert ra.last_error()
 
 
+@pytest.mark.parametrize("n,causal", [(2 ** 21 + 5, False), (2 ** 22, True), (2 ** 22, False)])
+def test_window_past_32bit_layout_is_unsupported(ra, n, causal):
+    """Label windows of millions of rows (n and clip of order 2^21-2^22, given
+    as expanded stride-0 views so nothing large is allocated): the plan rejects
+    them before sizing any LDS layout, whose byte offsets are 32-bit."""
+    x = torch.zeros(1, 1, 1, 64, dtype=torch.bfloat16).expand(1, 1, n, 64)
+    tab = torch.zeros(1, 1, 64, dtype=torch.bfloat16).expand(1, 2 * n + 1, 64)
+    assert ra.validate(x, x, x, tab, tab, clip=n, causal=causal) == ra.UNSUPPORTED
+    assert "fit" in ra.last_error()
+    bias = torch.zeros(1, 2 * n + 1)
+    assert ra.validate_offset_bias(x, x, x, bias, n, causal=causal) == ra.UNSUPPORTED
+
+
 @pytest.mark.parametrize("case", ["head_size", "noncontig_d", "misaligned_stride",
                                   "huge_label_window", "fp16"])
 def test_unsupported_arguments(ra, case):
@@ -150,6 +163,42 @@ print(st)
                        env=env, timeout=300)
     assert r.returncode == 0, r.stderr
     assert int(r.stdout.strip().splitlines()[-1]) == -3
+
+
+def test_plan_cache_keeps_every_check():
+    """relattn_fwd keeps recent plans per thread, keyed on shapes, strides,
+    dtypes, scalars and pointer alignment.  After a valid call is cached, calls
+    that differ only in a misaligned pointer, a dtype, a table shape, the key
+    lengths' alignment or the clip still fail their checks, and the valid call
+    still reaches the device check (no device is visible to the child)."""
+    code = r"""
+import sys, torch
+sys.path.insert(0, %r)
+import relative_position_encoding_amd as ra
+lib = ra._load()
+bf = torch.bfloat16
+q = torch.zeros(2, 3, 40, 64, dtype=bf)
+tab = torch.zeros(3, 9, 64, dtype=bf)
+lens = torch.zeros(4, dtype=torch.int32)
+def call(q=q, k=q, v=q, wK=tab, wV=tab, clip=4, causal=True, key_lens=None, out=q):
+    args, keep = ra._args(q, k, v, wK, wV, None, clip, causal, key_lens, 32, 128, True, None,
+                          out)
+    return lib.relattn_fwd(*args, None)
+mis = torch.zeros(2 * 3 * 40 * 64 + 8, dtype=bf)[1:1 + 2 * 3 * 40 * 64].view(2, 3, 40, 64)
+class Mis:  # key lengths at an address that is not 4-byte aligned (never read)
+    def data_ptr(self):
+        return lens.data_ptr() + 2
+res = [call(), call(), call(q=mis), call(out=q.float()), call(wK=torch.zeros(3, 8, 64, dtype=bf)),
+       call(key_lens=Mis()), call(clip=-1), call(), call(key_lens=lens[:2])]
+print(" ".join(map(str, res)))
+""" % ROOT
+    env = dict(os.environ, HIP_VISIBLE_DEVICES="-1", ROCR_VISIBLE_DEVICES="-1",
+               CUDA_VISIBLE_DEVICES="-1")
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True,
+                       env=env, timeout=300)
+    assert r.returncode == 0, r.stderr
+    got = [int(x) for x in r.stdout.strip().splitlines()[-1].split()]
+    assert got == [-3, -3, -2, -1, -1, -1, -1, -3, -3], got
 
 
 # ---------------------------------------------------------------------------

@@ -255,6 +255,39 @@ def test_backward_full_size_sampled(ra, shape):
     assert np.max(np.abs(dwv.sum(axis=1) - zsum)) <= 0.02 * np.abs(zsum).max()
 
 
+@pytest.mark.parametrize("shape", ["big_causal_kv", "base"])
+def test_backward_full_size_table_gradients(ra, shape):
+    """The workload shapes at full size in one call; for two sampled heads h,
+    the table gradients dw^K[h] and dw^V[h] element by element against the
+    oracle summed over every batch entry of that head (the tables are per head,
+    so their gradient is the sum over the batch of Eq. 3 and Eq. 4's bucketed
+    terms), and dq, dk, dv of every batch entry of those heads."""
+    import workloads
+    w = workloads.WORKLOADS[shape]
+    x = workloads.make_inputs(w)
+    dtype = x["q"].dtype
+    B, H, n, d = x["q"].shape
+    assert x["key_table"].shape[0] == H and x["value_table"].shape[0] == H
+    dz = gen((B, H, n, d), dtype, 900)
+    lens = x["key_lens"]
+    lens_l = None if lens is None else lens.tolist()
+    g = run_shaw(ra, x["q"], x["k"], x["v"], x["key_table"], x["value_table"], dz, w.clip,
+                 w.causal, lens_l)
+    rng = np.random.default_rng(902)
+    heads = [int(h) for h in rng.choice(H, size=2, replace=False)]
+    for h in heads:
+        hs = slice(h, h + 1)
+        want = oracle.relattn_backward(x["q"][:, hs], x["k"][:, hs], x["v"][:, hs],
+                                       x["key_table"][hs], x["value_table"][hs], w.clip,
+                                       dz[:, hs], causal=w.causal, key_lens=lens_l)
+        got = [t[:, hs] for t in g[:3]] + [g[3][hs], g[4][hs]]
+        errs = {name: nerr(a, b) for name, a, b in
+                zip(("dq", "dk", "dv", "dwK", "dwV"), got, want)}
+        print(f"{shape} head {h}: normalised errors " +
+              ", ".join(f"{k} {v:.3g}" for k, v in errs.items()))
+        check(got, want, dtype)
+
+
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=str)
 @pytest.mark.parametrize("mask", ["none", "causal", "lens"])
 @pytest.mark.parametrize("window,shared", [(0, False), (5, True), (20, False)])

@@ -265,9 +265,23 @@ def test_workload_t5_full_oracle(ra):
     assert err <= TOL[w.dtype]
 
 
+def test_workload_long_full_oracle(ra):
+    """n = 4096, clip 64, causal: every output row against the factored fp64
+    oracle (Eq. 5 form, itself pinned to brute force), so every query tile, the
+    heaviest-first tile order and the chunked table staging are all compared."""
+    w, x, got = _run_workload(ra, "long")
+    want = oracle.relattn_factored(x["q"], x["k"], x["v"], x["key_table"], x["value_table"],
+                                   w.clip, causal=w.causal, key_lens=x["key_lens"])
+    assert want.shape == got.shape
+    err = maxerr(got, want)
+    print(f"long: max abs err over all {got.shape[0] * got.shape[1] * got.shape[2]} rows {err:.3g}")
+    assert err <= TOL[w.dtype]
+
+
 def test_workload_long_sampled_rows(ra):
-    """n = 4096: 64 sampled rows against the brute-force row oracle, including
-    rows at the clip boundary and the last row."""
+    """n = 4096: 64 sampled rows against the brute-force row oracle (the
+    materialised n x n x d form of Eq. 3 and Eq. 4, row by row), including rows
+    at the clip boundary and the last row."""
     w, x, got = _run_workload(ra, "long")
     rng = np.random.default_rng(4)
     c, n = w.clip, w.n

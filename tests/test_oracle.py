@@ -966,6 +966,102 @@ def test_edge_relattn_two_tokens_closed_form():
         np.testing.assert_allclose(z[i], want, rtol=0, atol=1e-14)
 
 
+# ---------------------------------------------------------------------------
+# the edge-label pins bite: plant a mistake in either edge-label oracle and
+# watch the named pin fail
+# ---------------------------------------------------------------------------
+
+def _plant(monkeypatch, name, wrong):
+    monkeypatch.setattr(orc, name, wrong)
+    monkeypatch.setattr(oracle, name, wrong)
+
+
+@pytest.mark.parametrize("fault", ["transposed", "wrong_batch", "dropped_scale", "head0_row"])
+def test_planted_edge_bias_mistakes_are_caught(monkeypatch, fault):
+    """Scalar bias by edge label: a transposed label matrix, every batch entry
+    reading entry 0's labels, the 1/sqrt(d) (or explicit) scale dropped from
+    q.k, and head 0's bias row used for every head each fail a pin."""
+    real = orc.edge_label_attention
+
+    def wrong(q, k, v, labels, bias, scale=None, causal=False, key_lens=None):
+        E = np.asarray(labels)
+        b = orc.to_f64(bias)
+        if fault == "transposed":
+            E = np.swapaxes(E, 1, 2)
+        elif fault == "wrong_batch":
+            E = np.broadcast_to(E[:1], E.shape)
+        elif fault == "dropped_scale":
+            scale = 1.0
+        elif fault == "head0_row":
+            b = b[:1]
+        return real(q, k, v, E, b, scale=scale, causal=causal, key_lens=key_lens)
+
+    _plant(monkeypatch, "edge_label_attention", wrong)
+    pin = {
+        "transposed": lambda: test_edge_labels_from_t5_buckets_equal_t5(True, False, None),
+        "wrong_batch": test_edge_labels_probe_per_batch,
+        "dropped_scale": test_edge_labels_two_tokens_closed_form,
+        "head0_row": lambda: test_edge_labels_from_clipped_offsets_equal_offset_bias(False),
+    }[fault]
+    with pytest.raises(AssertionError):
+        pin()
+
+
+def _edge_relattn_with(fault):
+    """edge_label_relattn written out again with one planted mistake."""
+    def f(q, k, v, labels, aK=None, aV=None, scale=None, causal=False, key_lens=None):
+        q, k, v = orc.to_f64(q), orc.to_f64(k), orc.to_f64(v)
+        aK, aV = orc.to_f64(aK), orc.to_f64(aV)
+        E = np.asarray(labels).astype(np.int64)
+        B, H, n, d = q.shape
+        s = 1.0 / np.sqrt(d) if (scale is None or scale <= 0) else float(scale)
+        EK = np.swapaxes(E, 1, 2) if fault == "key_transposed" else E
+        EV = np.swapaxes(E, 1, 2) if fault == "value_transposed" else E
+        if fault == "wrong_batch":
+            EK = EV = np.broadcast_to(E[:1], E.shape)
+        lens = [n] * B if key_lens is None else [max(0, min(n, int(x))) for x in key_lens]
+        z = np.zeros((B, H, n, v.shape[-1]))
+        for b in range(B):
+            ok = orc.visible(n, causal, lens[b])
+            for h in range(H):
+                hh = 0 if fault == "head0_tables" else h
+                kk = np.broadcast_to(k[b, h][None], (n, n, d))
+                if aK is not None:
+                    kk = kk + aK[0 if aK.shape[0] == 1 else hh][EK[b]]
+                alpha = orc._masked_softmax_rows(np.einsum("id,ijd->ij", s * q[b, h], kk), ok)
+                vv = np.broadcast_to(v[b, h][None], (n, n, v.shape[-1]))
+                if aV is not None:
+                    tv = aV[0 if aV.shape[0] == 1 else hh][EV[b]]
+                    vv = vv + (s * tv if fault == "scaled_value" else tv)
+                z[b, h] = np.einsum("ij,ijd->id", alpha, vv)
+        return z
+    return f
+
+
+@pytest.mark.parametrize("fault", ["key_transposed", "value_transposed", "wrong_batch",
+                                   "head0_tables", "scaled_value"])
+def test_planted_edge_relattn_mistakes_are_caught(monkeypatch, fault):
+    """Edge labels with key and value tables: a transposed label matrix on the
+    key side or on the value side, every batch entry reading entry 0's labels,
+    head 0's tables used for every head, and the 1/sqrt(d) scale applied to the
+    value term each fail a pin.  The unplanted rewrite passes the same pins, so
+    each failure is the planted mistake's."""
+    pin = {
+        "key_transposed": lambda: test_edge_relattn_with_clipped_offset_labels_is_shaw(
+            "K", False, None),
+        "value_transposed": test_edge_relattn_value_histogram_probe,
+        "wrong_batch": test_edge_relattn_value_histogram_probe,
+        "head0_tables": lambda: test_edge_relattn_with_clipped_offset_labels_is_shaw(
+            "K", False, None),
+        "scaled_value": test_edge_relattn_two_tokens_closed_form,
+    }[fault]
+    _plant(monkeypatch, "edge_label_relattn", _edge_relattn_with(None))
+    pin()
+    _plant(monkeypatch, "edge_label_relattn", _edge_relattn_with(fault))
+    with pytest.raises(AssertionError):
+        pin()
+
+
 @pytest.mark.parametrize("window,shared", [(3, False), (40, True)])
 def test_offset_bias_decode_matches_forward_rows(window, shared):
     """Decoding with an offset table reproduces the causal offset-bias
