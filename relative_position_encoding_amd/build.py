@@ -20,7 +20,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "librelattn.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["relattn_kernels.hip", "relattn_decode.hip", "relattn_backward.hip", "relattn_api.cpp"]
+SOURCES = ["relattn_kernels.hip", "relattn_fwd_bf16.hip", "relattn_decode.hip",
+           "relattn_backward.hip", "relattn_api.cpp"]
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

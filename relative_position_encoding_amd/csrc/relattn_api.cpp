@@ -477,6 +477,42 @@ int make_plan(const relattn_tensor* q, const relattn_tensor* k, const relattn_te
       if (w == 1 || 32 * (w / 2) < n) keep.push_back(w);
     waves = keep;
   }
+  bool found_lean = false;
+  // The lean bf16 kernel serves the Shaw tables and plain attention at d = 64
+  // whenever its resident tables and relative rows fit.  Among its shapes take
+  // the one that keeps the most waves of this grid resident per compute unit
+  // (two per SIMD); on a tie the four-wave shape (two workgroups per compute
+  // unit drift apart in phase, so one's exponentials overlap the other's
+  // products: measured 14.1 us against 16.3 us for one eight-wave workgroup on
+  // the Transformer-big causal shape), then the deepest ring (a ring that
+  // holds every tile of a workgroup requests them all at entry).
+  if (relattn::lean_mode_ok(P.bf16, P.d, P.mode) && !is_xl) {
+    const int kb = P.d == 64 ? 64 : 32;
+    int64_t best_res = -1;
+    int best_st = -1, best_w = -1;
+    for (int w : {4, 8}) {
+      if (w == 8 && n <= 128) continue;  // half the waves would hold no query row
+      const int64_t wgs = B * H * ((n + 32 * w - 1) / (32 * w));
+      const int64_t need = (wgs + kNumCUs - 1) / kNumCUs;
+      const int64_t max_tiles = (n + kb - 1) / kb;  // tiles of the heaviest workgroup
+      for (int st = (int)std::min<int64_t>(max_tiles, 8); st >= 1; --st) {
+        if (st == 1 && max_tiles > 1) break;  // a ring needs two stages
+        const LaunchCfg c{w, kb, st, relattn::kWvResident, 1};
+        const size_t lds = relattn::lean_lds_bytes(P.d, c, P.mode, P.has_wk, P.has_wv, p.nr,
+                                                   p.t5_dist, nb);
+        if (lds > kMaxLdsBytes) continue;
+        const int64_t fit = std::min<int64_t>(8 / w, (int64_t)(kMaxLdsBytes / lds));
+        const int64_t resident = std::min(fit, need) * w;
+        if (resident > best_res || (resident == best_res && w == best_w && st > best_st)) {
+          best_res = resident;
+          best_st = st;
+          best_w = w;
+          P.cfg = c;
+        }
+      }
+    }
+    if (best_res > 0) found_lean = true;
+  }
   std::vector<LaunchCfg> order;
   for (int kb : kblocks)
     for (int w : waves)
@@ -486,9 +522,10 @@ int make_plan(const relattn_tensor* q, const relattn_tensor* k, const relattn_te
       for (int st : {2, 3})
         for (int wm : {relattn::kWvResident, relattn::kWvRing, relattn::kWvChunked})
           order.push_back({w, kb, st, wm});
-  bool found = false;
+  bool found = found_lean;
   int64_t best = -1;
   for (const auto& c : order) {
+    if (found_lean) break;
     const size_t lds = lds_of(c);
     if (lds > kMaxLdsBytes) continue;
     const int64_t wgs = B * H * ((n + 32 * c.waves - 1) / (32 * c.waves));
@@ -529,6 +566,22 @@ int make_plan(const relattn_tensor* q, const relattn_tensor* k, const relattn_te
   }
   if (B * H * (int64_t)p.n_qtiles > INT32_MAX)
     return fail(RELATTN_ERR_UNSUPPORTED, "too many workgroups (B*H*ceil(n/%d))", br);
+  {
+    // x / d as (umulhi(x, m) + x) >> s for every x < 2^31: s = ceil(log2 d),
+    // m = floor(2^32 (2^s - d) / d) + 1
+    auto divisor = [](int64_t d, uint32_t* m, int32_t* sh) {
+      if (d < 1) d = 1;
+      int e = 0;
+      while ((int64_t(1) << e) < d) ++e;
+      *m = (uint32_t)((((uint64_t)1 << 32) * (((uint64_t)1 << e) - (uint64_t)d)) / (uint64_t)d + 1);
+      *sh = e;
+    };
+    const int64_t grid = B * H * p.n_qtiles;
+    const int64_t hpx = (grid % 8 == 0) ? (grid / 8) / p.n_qtiles : 1;
+    divisor(H, &p.dv_h_m, &p.dv_h_s);
+    divisor(p.n_qtiles, &p.dv_qt_m, &p.dv_qt_s);
+    divisor(hpx, &p.dv_hpx_m, &p.dv_hpx_s);
+  }
 
   p.q = q->data;
   p.k = k->data;
@@ -1012,8 +1065,11 @@ int run_fwd(const Plan& plan, void* stream) {
   int st;
   if ((st = check_device())) return st;
   if (plan.empty) return RELATTN_OK;
-  const int e = relattn::launch_fwd(plan.bf16, plan.d, plan.cfg, plan.mode, plan.has_wk,
-                                    plan.has_wv, plan.p, stream);
+  const int e = plan.cfg.lean
+                    ? relattn::launch_fwd_lean(plan.d, plan.cfg, plan.mode, plan.has_wk,
+                                               plan.has_wv, plan.p, stream)
+                    : relattn::launch_fwd(plan.bf16, plan.d, plan.cfg, plan.mode, plan.has_wk,
+                                          plan.has_wv, plan.p, stream);
   if (e != (int)hipSuccess)
     return fail(RELATTN_ERR_LAUNCH_FAILED, "launch failed: %s", hipGetErrorString((hipError_t)e));
   return RELATTN_OK;

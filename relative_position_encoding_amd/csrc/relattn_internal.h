@@ -50,6 +50,11 @@ struct FwdParams {
   int32_t nstage;          // K/V tiles in the LDS ring (2 or 3)
   int32_t wv_mode;         // WvMode: where the w^V tile is staged
   int32_t dma32;           // K/V tile rows fit 32-bit byte offsets (fast stage loads)
+  // Divisions of workgroup ids (< 2^31) by H, by the query tiles per head and by
+  // the heads per XCD, as x / d == (umulhi(x, m) + x) >> s (host-computed; the
+  // lean kernel's tile mapping uses them instead of a division sequence).
+  uint32_t dv_h_m, dv_qt_m, dv_hpx_m;
+  int32_t dv_h_s, dv_qt_s, dv_hpx_s;
   // The scalar-bias arm takes either T5 buckets (ob = 0: t5_bias is [NB, H])
   // or a table by clipped offset (ob = 1: t5_bias points at the head's row of
   // a [Hb, 2W + 1] table; t5.nb = 2 * t5_dist + 1 entries starting at ob_lo
@@ -104,13 +109,24 @@ struct LaunchCfg {
   int waves;   // 32 query rows per wave
   int kblock;  // keys per tile
   int nstage;  // K/V tiles in the LDS ring
-  int wv_mode;  // WvMode
+  int wv_mode;  // WvMode (general kernel)
+  int lean = 0;  // 1: the lean bf16 kernel (relattn_fwd_bf16.hip)
 };
 
 // Dynamic LDS bytes of one workgroup (same layout function as the kernel);
 // SIZE_MAX when the configuration cannot hold the tables.
 size_t lds_bytes(bool bf16, int d, const LaunchCfg& cfg, RelMode mode, bool has_wk,
                  bool has_wv, int nr, int t5_dist, int t5_nb);
+
+// The lean bf16 kernel (relattn_fwd_bf16.hip): bf16, d = 64, 64-key tiles, 4 or
+// 8 waves, the Shaw tables, the T5 / clipped-offset
+// scalar bias or no relative term.  Its tables and relative rows stay resident
+// in LDS; the ring prefetches every tile of a workgroup when nstage covers them.
+bool lean_mode_ok(bool bf16, int d, RelMode mode);
+size_t lean_lds_bytes(int d, const LaunchCfg& cfg, RelMode mode, bool has_wk, bool has_wv,
+                      int nr, int t5_dist, int t5_nb);
+int launch_fwd_lean(int d, const LaunchCfg& cfg, RelMode mode, bool has_wk, bool has_wv,
+                    const FwdParams& p, void* stream);
 
 // Launchers (relattn_kernels.hip).  Return a hipError_t value.
 int launch_fwd(bool bf16, int d, const LaunchCfg& cfg, RelMode mode, bool has_wk,
