@@ -331,6 +331,26 @@ int relattn_decode(const relattn_tensor* q, const relattn_tensor* k,
                    void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * relattn_decode_noalloc: relattn_decode for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Same arguments, results, dtypes and errors as
+ * relattn_decode, without workspace: the split rows' partial results go to a
+ * static scratch array of 4 MiB that the library holds on each device it runs
+ * on until the process ends.  Shapes whose relattn_decode_workspace_size
+ * exceeds 4 MiB return RELATTN_ERR_UNSUPPORTED.  The call allocates nothing
+ * (no hipMalloc, no hipFree).  Every call on a device shares that device's
+ * scratch, whose contents on entry do not matter: calls on one device that
+ * overlap in time (different streams, or different host threads without
+ * ordering) race and must be serialised by the caller.  The first call on a
+ * device resolves that device's copy of the array (hipGetSymbolAddress).
+ */
+int relattn_decode_noalloc(const relattn_tensor* q, const relattn_tensor* k,
+                           const relattn_tensor* v, const relattn_tensor* wK,
+                           const relattn_tensor* wV, const relattn_tensor* t5_bias,
+                           const relattn_t5_params* t5, int32_t clip_k, float scale,
+                           const int32_t* cache_lens, relattn_tensor* out, void* stream);
+
+/*
  * relattn_decode_xl: incremental decoding with Transformer-XL relative logits
  * (the transformer-xl page's four-term score; the newest positions attend over
  * everything before them):

@@ -12,7 +12,7 @@ import functools
 import os
 
 __all__ = ["fwd", "validate", "fwd_offset_bias", "validate_offset_bias", "decode",
-           "decode_workspace_size", "debug_indices", "fwd_lse", "fwd_offset_bias_lse",
+           "decode_workspace_size", "decode_noalloc", "debug_indices", "fwd_lse", "fwd_offset_bias_lse",
            "bwd", "bwd_workspace_size", "bwd_offset_bias", "bwd_offset_bias_workspace_size",
            "attention", "attention_offset_bias", "fwd_xl", "validate_xl", "fwd_grid_bias",
            "validate_grid_bias", "fwd_edge_bias", "validate_edge_bias", "edge_label_buffer",
@@ -73,6 +73,8 @@ def _load():
     lib.relattn_decode.restype = ctypes.c_int
     lib.relattn_decode_workspace_size.argtypes = dec + [P(_Tensor), P(ctypes.c_size_t)]
     lib.relattn_decode_workspace_size.restype = ctypes.c_int
+    lib.relattn_decode_noalloc.argtypes = dec + [ctypes.c_void_p, P(_Tensor), ctypes.c_void_p]
+    lib.relattn_decode_noalloc.restype = ctypes.c_int
     decob = [P(_Tensor)] * 4 + [ctypes.c_int32, ctypes.c_float]
     lib.relattn_decode_offset_bias.argtypes = decob + [ctypes.c_void_p, P(_Tensor),
                                                        ctypes.c_void_p, ctypes.c_size_t,
@@ -344,6 +346,35 @@ def decode(q, k, v, wK=None, wV=None, *, clip=0, cache_lens=None, t5_bias=None,
                             ctypes.byref(outv), ctypes.c_void_p(workspace.data_ptr()),
                             ctypes.c_size_t(workspace.numel() * workspace.element_size()),
                             ctypes.c_void_p(stream))
+    del keep
+    if st != OK:
+        _raise(lib, st)
+    return out
+
+
+def decode_noalloc(q, k, v, wK=None, wV=None, *, clip=0, cache_lens=None, t5_bias=None,
+                   num_buckets=32, max_distance=128, bidirectional=True, scale=None, out,
+                   stream=None):
+    """``decode`` through the entry point that allocates nothing on the device:
+    the library's static per-device scratch stands in for the workspace (at
+    most 4 MiB of it; larger shapes raise UNSUPPORTED).  ``out`` must be given
+    (the caller owns every buffer).  Calls on one device share the scratch:
+    calls that overlap in time race.  Returns ``out``."""
+    import torch
+    lib = _load()
+    if cache_lens is not None and cache_lens.dtype != torch.int32:
+        raise RelattnError(INVALID_ARGUMENT, "relattn: cache_lens must be int32")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    elif hasattr(stream, "cuda_stream"):
+        stream = stream.cuda_stream
+    args, keep = _dec_args(q, k, v, wK, wV, t5_bias, clip, num_buckets, max_distance,
+                           bidirectional, scale)
+    outv = _view(out)
+    st = lib.relattn_decode_noalloc(*args,
+                                    ctypes.c_void_p(cache_lens.data_ptr() if cache_lens is not None
+                                                    else None),
+                                    ctypes.byref(outv), ctypes.c_void_p(stream))
     del keep
     if st != OK:
         _raise(lib, st)

@@ -11,6 +11,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -1076,6 +1077,51 @@ int run_fwd(const Plan& plan, void* stream) {
 }
 
 // Check the cache lengths and workspace of a made decode plan, then enqueue it.
+// ---- scratch of the entry points that allocate nothing ----------------------
+// One file-scope array per device (each GPU the library runs on holds its own
+// copy until the process ends).  Host code never uses the array's name as an
+// address: hipGetSymbolAddress resolves this device's copy once, with that
+// device current, and the pointer is kept per device.
+constexpr size_t kScratchBytes = size_t(4) << 20;
+}  // namespace
+namespace relattn {
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+}  // namespace relattn
+namespace {
+
+constexpr int kMaxScratchDevices = 64;
+std::atomic<void*> g_scratch_addr[kMaxScratchDevices];
+std::mutex g_scratch_mu;
+
+int scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    (void)hipGetLastError();
+    return fail(RELATTN_ERR_NO_DEVICE, "no HIP device available");
+  }
+  if (dev >= kMaxScratchDevices)
+    return fail(RELATTN_ERR_UNSUPPORTED, "device ordinal %d exceeds %d", dev,
+                kMaxScratchDevices - 1);
+  void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_addr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      void* a = nullptr;
+      const hipError_t e = hipGetSymbolAddress(&a, HIP_SYMBOL(relattn::scratch));
+      if (e != hipSuccess || !a) {
+        (void)hipGetLastError();
+        return fail(RELATTN_ERR_LAUNCH_FAILED, "cannot resolve the scratch array on device %d: %s",
+                    dev, hipGetErrorString(e));
+      }
+      g_scratch_addr[dev].store(a, std::memory_order_release);
+      p = a;
+    }
+  }
+  *out = p;
+  return RELATTN_OK;
+}
+
 int run_decode(DecPlan& plan, const int32_t* cache_lens, void* workspace,
                size_t workspace_bytes, void* stream) {
   if (cache_lens && (reinterpret_cast<uintptr_t>(cache_lens) & 3u))
@@ -1520,6 +1566,25 @@ int relattn_decode(const relattn_tensor* q, const relattn_tensor* k, const relat
   int st = make_dec_plan(q, k, v, wK, wV, t5_bias, t5, clip_k, scale, out, &plan, true);
   if (st) return st;
   return run_decode(plan, cache_lens, workspace, workspace_bytes, stream);
+}
+
+int relattn_decode_noalloc(const relattn_tensor* q, const relattn_tensor* k,
+                           const relattn_tensor* v, const relattn_tensor* wK,
+                           const relattn_tensor* wV, const relattn_tensor* t5_bias,
+                           const relattn_t5_params* t5, int32_t clip_k, float scale,
+                           const int32_t* cache_lens, relattn_tensor* out, void* stream) {
+  g_last_error.clear();
+  DecPlan plan;
+  int st = make_dec_plan(q, k, v, wK, wV, t5_bias, t5, clip_k, scale, out, &plan, true);
+  if (st) return st;
+  if (!plan.empty && plan.ws_bytes > kScratchBytes)
+    return fail(RELATTN_ERR_UNSUPPORTED,
+                "these shapes need %zu bytes of workspace; the static scratch holds %zu",
+                plan.ws_bytes, kScratchBytes);
+  if ((st = check_device())) return st;
+  void* ws = nullptr;
+  if ((st = scratch_address(&ws))) return st;
+  return run_decode(plan, cache_lens, ws, kScratchBytes, stream);
 }
 
 int relattn_decode_xl_workspace_size(const relattn_tensor* q, const relattn_tensor* k,
