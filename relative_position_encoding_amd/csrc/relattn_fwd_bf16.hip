@@ -33,6 +33,8 @@ namespace {
 
 constexpr float kSlack = 8.f;  // log2 units a row max may run ahead of the one in use
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
 // One 16-byte K fragment read from LDS (32-key block kb of the tile at the
 // lane's byte address ad), as inline assembly so that all of a tile's reads
 // are in flight together; the caller waits with lgkmcnt(0).
@@ -483,7 +485,10 @@ void fwd_bf16_kernel(const FwdParams p) {
       // online softmax: one cross-lane max per tile, everything else per lane
       tmax = halves_max3(tmax);
       const bool grow = tmax > m_run + kSlack;  // -inf + slack is -inf
-      if (__any(grow)) {
+      {
+        // rescaled every tile (alpha is exactly 1 while the max in use holds):
+        // a branch taken only on growth would make the compiler keep a second
+        // copy of the accumulators for the path around it
         const float m_next = grow ? tmax : m_run;
         const float alpha = fast_exp2(m_run - m_next);  // 0 when m_run is -inf
         m_run = m_next;
@@ -505,19 +510,35 @@ void fwd_bf16_kernel(const FwdParams p) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) s[kb][i] = fast_exp2(s[kb][i] - m_use);
       }
-      // row sum, as a tree (short dependency chains)
-      float ps[NKB][2];
+      // the weights as the bf16 operands of the P.V product, and the row sum
+      // of those same operands by pairwise dot products with (1, 1): the
+      // normaliser then sums exactly the weights the product used
+      bf16x8 pb[NKB][2];
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int g = 0; g < 2; ++g) {
-          const int o = 8 * g;
-          ps[kb][g] = ((s[kb][o] + s[kb][o + 1]) + (s[kb][o + 2] + s[kb][o + 3])) +
-                      ((s[kb][o + 4] + s[kb][o + 5]) + (s[kb][o + 6] + s[kb][o + 7]));
-        }
-      float psum = 0.f;
+        for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) psum += ps[kb][0] + ps[kb][1];
+          for (int e = 0; e < 8; ++e) pb[kb][t2][e] = (__bf16)s[kb][8 * t2 + e];
+      float psum = 0.f;
+      {
+        bf16x2 one;
+        one[0] = (__bf16)1.f;
+        one[1] = (__bf16)1.f;
+        float acc2[2] = {0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+            for (int e = 0; e < 8; e += 2) {
+              bf16x2 pr;
+              pr[0] = pb[kb][t2][e];
+              pr[1] = pb[kb][t2][e + 1];
+              acc2[t2] = __builtin_amdgcn_fdot2_f32_bf16(pr, one, acc2[t2], false);
+            }
+        psum = acc2[0] + acc2[1];
+      }
       l_part += psum;
       if constexpr (SHAW && HAS_WV) {
         // +c label (keys at offset >= c); empty under the causal mask
@@ -550,17 +571,13 @@ void fwd_bf16_kernel(const FwdParams p) {
           for (int mb = 0; mb < DVB; ++mb)
             frag_col_issue_blk<ROWB>(2 * kb + t2, vt_lds + trb_lo[mb], vt_lds + trb_hi[mb],
                                      vlo[t2 * DVB + mb], vhi[t2 * DVB + mb]);
-        bf16x8 pb[2];
-#pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) pb[t2][e] = (__bf16)s[kb][8 * t2 + e];
         frag_col_wait(vlo, vhi);
 #pragma unroll
         for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
           for (int mb = 0; mb < DVB; ++mb)
-            oacc[mb] = mfma(frag_join(vlo[t2 * DVB + mb], vhi[t2 * DVB + mb]), pb[t2], oacc[mb]);
+            oacc[mb] = mfma(frag_join(vlo[t2 * DVB + mb], vhi[t2 * DVB + mb]), pb[kb][t2],
+                            oacc[mb]);
       }
     };
     using Yes = std::true_type;
