@@ -24,7 +24,9 @@ __all__ = ["fwd", "validate", "fwd_offset_bias", "validate_offset_bias", "decode
 OK, INVALID_ARGUMENT, UNSUPPORTED, NO_DEVICE, LAUNCH_FAILED = 0, -1, -2, -3, -4
 _F32, _BF16, _U8 = 0, 1, 2
 
-library_path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "librelattn.so")
+# RELATTN_LIBRARY names another build of the same library (e.g. the host-sanitized one)
+library_path = os.environ.get("RELATTN_LIBRARY") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "librelattn.so")
 
 
 class RelattnError(RuntimeError):

@@ -41,6 +41,43 @@ def _compile(src: str) -> str:
     return obj
 
 
+# Host sanitizers for the C-ABI code (argument checks, plans, the caches): the
+# host pass of relattn_api.cpp is built with AddressSanitizer and
+# UndefinedBehaviorSanitizer (-Xarch_host: the device code is not
+# instrumented), the kernels as usual, into _build/librelattn_san.so.  Run the
+# CPU tests against it with
+#   RELATTN_LIBRARY=_build/librelattn_san.so ASAN_OPTIONS=detect_leaks=0 \
+#   LD_PRELOAD=$(hipcc -print-file-name=libclang_rt.asan-x86_64.so) \
+#   python -m pytest tests/test_abi.py -m "not gpu"
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-fno-sanitize-recover=all"]
+
+
+def build_sanitized(verbose: bool = True) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    src = "relattn_api.cpp"
+    obj = os.path.join(BUILD, "relattn_api_san.o")
+    cmd = [HIPCC] + FLAGS + SAN_FLAGS + ["-O1", "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout + r.stderr)
+        raise RuntimeError("hipcc failed on the sanitized host build")
+    objs = [os.path.join(BUILD, os.path.splitext(x)[0] + ".o") for x in SOURCES if x != src]
+    for o in objs:
+        if not os.path.exists(o):
+            raise RuntimeError(f"{o} missing: run the normal build first")
+    out = os.path.join(BUILD, "librelattn_san.so")
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-fsanitize=address",
+           "-fsanitize=undefined", "-shared-libsan", "-o", out] + objs + [obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout + r.stderr)
+        raise RuntimeError("linking librelattn_san.so failed")
+    if verbose:
+        print(f"built {out}")
+    return out
+
+
 def build(verbose: bool = True) -> str:
     os.makedirs(BUILD, exist_ok=True)
     with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
@@ -58,4 +95,7 @@ def build(verbose: bool = True) -> str:
 
 
 if __name__ == "__main__":
-    build()
+    if "--sanitize" in sys.argv[1:]:
+        build_sanitized()
+    else:
+        build()
