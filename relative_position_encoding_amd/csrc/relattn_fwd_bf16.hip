@@ -34,6 +34,7 @@ namespace {
 constexpr float kSlack = 8.f;  // log2 units a row max may run ahead of the one in use
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 // One 16-byte K fragment read from LDS (32-key block kb of the tile at the
 // lane's byte address ad), as inline assembly so that all of a tile's reads
@@ -103,9 +104,11 @@ __host__ __device__ inline LLayout lean_layout(int mode, bool has_wk, bool has_w
   L.wk = (shaw && has_wk) ? take(L.wk_rows * G::ROWB) : off;
   L.wv = (shaw && has_wv) ? take(L.wv_rows * G::ROWB) : off;
   // relative row: PADL copies of the first label, the labels, PADU copies of
-  // the last; a stride of 2 mod 4 keeps the lanes' diagonal and column reads
-  // nearly free of bank conflicts
-  const int m = nr + G::PADL + G::PADU;
+  // the last (and room for whole 32-label blocks of the relative-key product,
+  // whose entries past the last label the padding then overwrites); a stride
+  // of 2 mod 4 keeps the lanes' diagonal and column reads nearly free of bank
+  // conflicts
+  const int m = max(nr + G::PADL + G::PADU, G::PADL + ((nr + 31) & ~31));
   L.lrs = m + ((2 - m) & 3);
   L.le = (shaw && (has_wk || has_wv)) ? take(G::BR * L.lrs * 4) : off;
   L.tbc = t5 ? take(((t5_nb + 63) & ~63) * 4) : off;
@@ -270,26 +273,38 @@ void fwd_bf16_kernel(const FwdParams p) {
   // of log2e*bias by offset in [-dist, dist], padded the same way.
   float Llo = 0.f, Lhi = 0.f;
   if constexpr (SHAW && HAS_WK) {
-    const unsigned char* wkt = smem + lay.wk;
     const int nlb = (p.nr + 31) / 32;
-    for (int lb = 0; lb < nlb; ++lb) {
-      bf16x8 a[NKS];
+    // lane's fragment of label row ql, chunk 2ks + hh, in the first 32-label
+    // block; later blocks lie 32 rows on, which the swizzle does not see
+    uint32_t wfo[NKS];
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) a[ks] = frag_row<ROWB>(wkt, lb * 32 + ql, 2 * ks + hh);
-      f32x16 acc = {};
+    for (int ks = 0; ks < NKS; ++ks)
+      wfo[ks] = smem_addr + (uint32_t)lay.wk + (uint32_t)tile_offset<ROWB>(ql, (2 * ks + hh) * 16);
+    // two label blocks per round: every fragment read of the round is in
+    // flight before the first product (the row holds whole blocks, so the
+    // stores need no per-label test)
+    for (int lb = 0; lb < nlb; lb += 2) {
+      const bool two = lb + 1 < nlb;  // wave-uniform
+      bf16x8 a[2][NKS];
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) acc = mfma(a[ks], qop[ks], acc);
-      // register i of lane half hh holds label lb*32 + 8(i>>2) + 4hh + (i&3)
-      if (PADL + nlb * 32 <= lay.lrs) {
+      for (int ks = 0; ks < NKS; ++ks) {
+        const uint32_t ad = wfo[ks] + (uint32_t)(lb * 32 * ROWB);
+        asm volatile("ds_read_b128 %0, %1" : "=v"(a[0][ks]) : "v"(ad));
+        if (two) asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(a[1][ks]) : "v"(ad), "n"(32 * ROWB));
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) asm volatile("" : "+v"(a[0][ks]), "+v"(a[1][ks]));
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        if (u == 1 && !two) break;
+        f32x16 acc = {};
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) acc = mfma(a[u][ks], qop[ks], acc);
+        // register i of lane half hh holds label (lb+u)*32 + 8(i>>2) + 4hh + (i&3)
 #pragma unroll
         for (int i = 0; i < 16; ++i)
-          myLE[PADL + lb * 32 + 8 * (i >> 2) + 4 * hh + (i & 3)] = acc[i] * p.scale_log2;
-      } else {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int idx = lb * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
-          if (idx < p.nr) myLE[PADL + idx] = acc[i] * p.scale_log2;
-        }
+          myLE[PADL + (lb + u) * 32 + 8 * (i >> 2) + 4 * hh + (i & 3)] = acc[i] * p.scale_log2;
       }
     }
     compiler_fence();  // the row was written by both halves of the wave
@@ -319,7 +334,8 @@ void fwd_bf16_kernel(const FwdParams p) {
   const int dlo = T5 ? -p.t5_dist : p.r_lo - c;  // offset of entry PADL
   const int nwin = T5 ? 2 * p.t5_dist + 1 : p.nr;
   const int gtop = nwin + PADL + PADU - SPAN;      // highest gather base
-  const float* relrow = T5 ? TB : myLE;
+  const uint32_t relrow_lds =
+      smem_addr + (uint32_t)(T5 ? lay.tb : lay.le + qrow * lay.lrs * 4);
   const int band = T5 ? p.t5_dist : c;             // |j - i| >= band: one end value per tile
   // offsets whose label holds a single key (1 <= r <= 2c - 1, reachable)
   const int wb_lo = max(1, p.r_lo) - c, wb_hi = min(2 * c - 1, r_hi) - c;
@@ -441,17 +457,37 @@ void fwd_bf16_kernel(const FwdParams p) {
         tmax = fmaf(mr, sl2, cadd);  // -inf stays -inf
       } else {
         // band: every relative logit of the tile, 8 entries per group read
-        // from one clamped base (the row padding makes the clamp exact)
+        // from one clamped base (the row padding makes the clamp exact); all
+        // of the tile's reads are in flight before the first use
+        f32x2 gv[NKB][2][4];
+        if constexpr (GATHER) {
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int g = 0; g < 2; ++g) {
+              const int d0 = kofs + 32 * kb + 16 * g;
+              const uint32_t ad = relrow_lds + 4u * (uint32_t)min(max(d0 - dlo + PADL, 0), gtop);
+              asm volatile("ds_read2_b32 %0, %1 offset1:1" : "=v"(gv[kb][g][0]) : "v"(ad));
+              asm volatile("ds_read2_b32 %0, %1 offset0:2 offset1:3" : "=v"(gv[kb][g][1]) : "v"(ad));
+              asm volatile("ds_read2_b32 %0, %1 offset0:4 offset1:5" : "=v"(gv[kb][g][2]) : "v"(ad));
+              asm volatile("ds_read2_b32 %0, %1 offset0:6 offset1:7" : "=v"(gv[kb][g][3]) : "v"(ad));
+            }
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int g = 0; g < 2; ++g)
+#pragma unroll
+              for (int e2 = 0; e2 < 4; ++e2) asm volatile("" : "+v"(gv[kb][g][e2]));
+        }
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
           for (int g = 0; g < 2; ++g) {
-            const int d0 = kofs + 32 * kb + 16 * g;
-            const int bidx = min(max(d0 - dlo + PADL, 0), gtop);
-            const float* grp = relrow + bidx;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-              float x = GATHER ? fmaf(s[kb][8 * g + e], sl2, grp[e]) : s[kb][8 * g + e] * sl2;
+              float x = GATHER ? fmaf(s[kb][8 * g + e], sl2, gv[kb][g][e >> 1][e & 1])
+                               : s[kb][8 * g + e] * sl2;
               if constexpr (MASK) x = (32 * kb + 16 * g + e <= lim) ? x : kNegInf;
               s[kb][8 * g + e] = x;
             }
@@ -605,50 +641,84 @@ void fwd_bf16_kernel(const FwdParams p) {
     // alone: r in [1, 2c-1], key j = qi + r - c in [0, kv_len), j <= qi if causal
     int r_in_hi = min(2 * c - 1, c - qi + kv_len - 1);
     if (p.causal) r_in_hi = min(r_in_hi, c);
-    const int i_in_lo = max(1, c - qi) - p.r_lo;
-    const int i_in_hi = q_ok ? r_in_hi - p.r_lo : i_in_lo - 1;
-    const bool any_in = i_in_hi >= i_in_lo;
+    int i_in_lo = max(1, c - qi) - p.r_lo;
+    int i_in_hi = q_ok ? r_in_hi - p.r_lo : i_in_lo - 1;
+    // Label +c (its weight is the tail summed in the loop) joins the range as
+    // the log of its weight: it is nonzero only when the row has keys at every
+    // offset up to c, so its index 2c - r_lo then directly follows the range.
+    if (thi_all > 0.f && q_ok) {
+      myLE[PADL + 2 * c - p.r_lo] = __builtin_amdgcn_logf(thi_all) + m_fin;
+      i_in_hi = 2 * c - p.r_lo;
+    }
+    if (i_in_hi < i_in_lo) i_in_lo = 1 << 30, i_in_hi = 1 << 30;  // no index passes
     const unsigned i_in_w = (unsigned)(i_in_hi - i_in_lo);
-    const int i_thi = 2 * c - p.r_lo;  // label +c (index past nr when unreachable)
     const int nls = (p.nr + 15) / 16;
     float isum = 0.f;
     const uint32_t wv_lds = smem_addr + (uint32_t)lay.wv;
-    // label -c, whose weight is what the row sum leaves after all others,
-    // sits in step 0: do that step last
-    for (int it = 0; it < nls; ++it) {
-      const int ls = (it + 1 < nls) ? it + 1 : 0;
-      float w[8];
+    // 16 labels per step.  Label -c, whose weight is what the row sum leaves
+    // after all others, sits in step 0: that step is taken last.  The steps
+    // go up to four at a time (NP of them from it0, all present) with every
+    // LDS read of the group in flight before the first exponential.
+    auto steps = [&](auto np_tag, int it0) __attribute__((always_inline)) {
+      constexpr int NP = decltype(np_tag)::value;
+      float x[NP][8];
+      bf16x4 wlo[NP][DVB], whi[NP][DVB];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int idx = ls * 16 + 8 * hh + e;
-        const float x = myLE[PADL + idx];  // inside the row for every step
-        const bool ok = any_in && (unsigned)(idx - i_in_lo) <= i_in_w;
-        w[e] = ok ? fast_exp2(x - m_fin) : 0.f;
-        isum += w[e];
+      for (int u = 0; u < NP; ++u) {
+        const int it = it0 + u;
+        const int ls = (it + 1 < nls) ? it + 1 : 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[u][e] = myLE[PADL + ls * 16 + 8 * hh + e];  // in the row
+#pragma unroll
+        for (int mb = 0; mb < DVB; ++mb)
+          frag_col_issue<ROWB, D>(wv_lds, ls * 16, 32 * mb, lane, wlo[u][mb], whi[u][mb]);
       }
-      if (it + 1 == nls) {
-        // every single-key weight is in isum now
-        const float tlo_all = fmaxf(l - halves_sum(isum) - thi_all, 0.f);
-        if (p.r_lo == 0 && hh == 0) w[0] += tlo_all;  // label index 0 is -c
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+      for (int u = 0; u < NP; ++u)
+#pragma unroll
+        for (int mb = 0; mb < DVB; ++mb) asm volatile("" : "+v"(wlo[u][mb]), "+v"(whi[u][mb]));
+      float w[NP][8];
+#pragma unroll
+      for (int u = 0; u < NP; ++u) {
+        const int it = it0 + u;
+        const int ls = (it + 1 < nls) ? it + 1 : 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int idx = ls * 16 + 8 * hh + e;
+          const bool ok = (unsigned)(idx - i_in_lo) <= i_in_w;
+          // the exponential for every lane, then a select (a conditional
+          // exponential becomes a branch per element)
+          float ex = fast_exp2(x[u][e] - m_fin);
+          asm volatile("" : "+v"(ex));
+          w[u][e] = ok ? ex : 0.f;
+          isum += w[u][e];
+        }
       }
-      if (!p.causal) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) w[e] += (ls * 16 + 8 * hh + e == i_thi) ? thi_all : 0.f;
+      for (int u = 0; u < NP; ++u) {
+        const int it = it0 + u;
+        const int ls = (it + 1 < nls) ? it + 1 : 0;
+        if (it + 1 == nls) {
+          // every other label's weight is in isum now
+          const float tlo_all = fmaxf(l - halves_sum(isum), 0.f);
+          if (p.r_lo == 0 && hh == 0 && q_ok) w[u][0] += tlo_all;  // label index 0 is -c
+        }
+        bf16x8 bw;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) bw[e] = (__bf16)w[u][e];  // all 0 past the last query
+#pragma unroll
+        for (int mb = 0; mb < DVB; ++mb)
+          oacc[mb] = mfma(frag_join(wlo[u][mb], whi[u][mb]), bw, oacc[mb]);
       }
-      if (!q_ok) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) w[e] = 0.f;
-      }
-      bf16x8 bw;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) bw[e] = (__bf16)w[e];
-      bf16x4 wlo[DVB], whi[DVB];
-#pragma unroll
-      for (int mb = 0; mb < DVB; ++mb)
-        frag_col_issue<ROWB, D>(wv_lds, ls * 16, 32 * mb, lane, wlo[mb], whi[mb]);
-      frag_col_wait(wlo, whi);
-#pragma unroll
-      for (int mb = 0; mb < DVB; ++mb) oacc[mb] = mfma(frag_join(wlo[mb], whi[mb]), bw, oacc[mb]);
+    };
+    int it0 = 0;
+    for (; it0 + 4 <= nls; it0 += 4) steps(std::integral_constant<int, 4>{}, it0);
+    switch (nls - it0) {
+      case 1: steps(std::integral_constant<int, 1>{}, it0); break;
+      case 2: steps(std::integral_constant<int, 2>{}, it0); break;
+      case 3: steps(std::integral_constant<int, 3>{}, it0); break;
+      default: break;
     }
   }
 
