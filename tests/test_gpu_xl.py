@@ -80,17 +80,25 @@ def test_xl_shared_and_scale(ra, dtype):
 
 
 def test_xl_zero_biases_match_shaw_with_reversed_table(ra):
-    """u = v = 0: bit-identical to relattn_fwd with the table reversed (the
-    same kernel reads the same rows in the same order)."""
+    """u = v = 0: relattn_fwd with the table reversed computes the same
+    attention.  At bf16 and d = 64 the two calls run different kernels (the
+    Shaw call takes the lean kernel, whose normaliser sums the bf16-rounded
+    weights), so they agree to the output rounding: one bf16 step (2^-8
+    relative) either way, 2^-7 of the largest output; both meet the oracle."""
     B, H, n, d, W = 2, 2, 130, 64, 129
     dtype = torch.bfloat16
-    q, k, v = (gen((B, H, n, d), dtype, 1500 + i).to(DEV) for i in range(3))
-    R = gen((H, 2 * W + 1, d), dtype, 1503, 0.5).to(DEV)
+    qc, kc, vc = (gen((B, H, n, d), dtype, 1500 + i) for i in range(3))
+    Rc = gen((H, 2 * W + 1, d), dtype, 1503, 0.5)
+    q, k, v, R = (t.to(DEV) for t in (qc, kc, vc, Rc))
     zero = torch.zeros(H, d, dtype=dtype, device=DEV)
     a = ra.fwd_xl(q, k, v, R, zero, zero, W, causal=True)
     b = ra.fwd(q, k, v, R.flip(1).contiguous(), None, clip=W, causal=True)
     torch.cuda.synchronize()
-    assert torch.equal(a, b)
+    a, b = a.float().cpu().numpy(), b.float().cpu().numpy()
+    assert float(np.max(np.abs(a - b))) <= 2.0 ** -7 * max(float(np.abs(b).max()), 1.0)
+    want = oracle.relattn_factored(qc, kc, vc, Rc.flip(1).contiguous(), None, W, causal=True)
+    assert float(np.max(np.abs(a - want))) <= TOL[dtype]
+    assert float(np.max(np.abs(b - want))) <= TOL[dtype]
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=str)
