@@ -432,6 +432,7 @@ void fwd_bf16_kernel(const FwdParams p) {
     // band (one relative logit for the whole tile) or in it, and with or
     // without per-key masking.  Each case is its own straight-line code, so no
     // value has to be carried across a join of the four.
+    bf16x8 pb[NKB][2];  // the weights as the bf16 operands of P.V
     auto tile_rest = [&](auto off_tag, auto mask_tag) __attribute__((always_inline)) {
       constexpr bool OFF = decltype(off_tag)::value;
       constexpr bool MASK = decltype(mask_tag)::value;
@@ -523,8 +524,9 @@ void fwd_bf16_kernel(const FwdParams p) {
       const bool grow = tmax > m_run + kSlack;  // -inf + slack is -inf
       {
         // rescaled every tile (alpha is exactly 1 while the max in use holds):
-        // a branch taken only on growth would make the compiler keep a second
-        // copy of the accumulators for the path around it
+        // the multiply is also the move the register allocator wants for the
+        // loop-carried accumulators, where a branch taken only on growth costs
+        // a copy of all of them on the common path
         const float m_next = grow ? tmax : m_run;
         const float alpha = fast_exp2(m_run - m_next);  // 0 when m_run is -inf
         m_run = m_next;
@@ -549,7 +551,6 @@ void fwd_bf16_kernel(const FwdParams p) {
       // the weights as the bf16 operands of the P.V product, and the row sum
       // of those same operands by pairwise dot products with (1, 1): the
       // normaliser then sums exactly the weights the product used
-      bf16x8 pb[NKB][2];
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
@@ -596,25 +597,6 @@ void fwd_bf16_kernel(const FwdParams p) {
         }
       }
 
-      // O^T += V^T P^T
-      const uint32_t vt_lds = smem_addr + (uint32_t)(Vt - smem);
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        bf16x4 vlo[2 * DVB], vhi[2 * DVB];
-#pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2)
-#pragma unroll
-          for (int mb = 0; mb < DVB; ++mb)
-            frag_col_issue_blk<ROWB>(2 * kb + t2, vt_lds + trb_lo[mb], vt_lds + trb_hi[mb],
-                                     vlo[t2 * DVB + mb], vhi[t2 * DVB + mb]);
-        frag_col_wait(vlo, vhi);
-#pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2)
-#pragma unroll
-          for (int mb = 0; mb < DVB; ++mb)
-            oacc[mb] = mfma(frag_join(vlo[t2 * DVB + mb], vhi[t2 * DVB + mb]), pb[kb][t2],
-                            oacc[mb]);
-      }
     };
     using Yes = std::true_type;
     using No = std::false_type;
@@ -624,6 +606,27 @@ void fwd_bf16_kernel(const FwdParams p) {
     } else {
       if (need_mask) tile_rest(No{}, Yes{});
       else tile_rest(No{}, No{});
+    }
+
+    // O^T += V^T P^T (one copy of this code for the four cases above, so the
+    // accumulators keep one set of registers through the loop)
+    const uint32_t vt_lds = smem_addr + (uint32_t)(Vt - smem);
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      bf16x4 vlo[2 * DVB], vhi[2 * DVB];
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+        for (int mb = 0; mb < DVB; ++mb)
+          frag_col_issue_blk<ROWB>(2 * kb + t2, vt_lds + trb_lo[mb], vt_lds + trb_hi[mb],
+                                   vlo[t2 * DVB + mb], vhi[t2 * DVB + mb]);
+      frag_col_wait(vlo, vhi);
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+        for (int mb = 0; mb < DVB; ++mb)
+          oacc[mb] = mfma(frag_join(vlo[t2 * DVB + mb], vhi[t2 * DVB + mb]), pb[kb][t2],
+                          oacc[mb]);
     }
   }
 
