@@ -36,8 +36,20 @@ OTHER = ["base", "big_causal_k", "long", "t5"]
 PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # dense MFMA, MI355X
 PEAK_HBM_GBS = 8000.0
 LLC_BYTES = 256 << 20
-KERNEL_SRC = os.path.join(ROOT, "relative_position_encoding_amd", "csrc", "relattn_kernels.hip")
-DECODE_SRC = os.path.join(ROOT, "relative_position_encoding_amd", "csrc", "relattn_decode.hip")
+CSRC = os.path.join(ROOT, "relative_position_encoding_amd", "csrc")
+KERNEL_SRC = os.path.join(CSRC, "relattn_kernels.hip")
+LEAN_SRC = os.path.join(CSRC, "relattn_fwd_bf16.hip")
+DECODE_SRC = os.path.join(CSRC, "relattn_decode.hip")
+BWD_SRC = os.path.join(CSRC, "relattn_backward.hip")
+# headers every kernel source includes (tile layout, device helpers, parameters)
+SHARED_HEADERS = [os.path.join(CSRC, h) for h in
+                  ("relattn_device.h", "relattn_internal.h", "relattn_tiles.h")]
+# the kernel source each measured arm runs: the lean bf16 kernel serves the Shaw
+# tables at d = 64, the general kernel the other forward arms
+TRAFFIC_SRC = {"base": LEAN_SRC, "big_causal_k": LEAN_SRC, "big_causal_kv": LEAN_SRC,
+               "long": KERNEL_SRC, "t5": KERNEL_SRC, "alibi": KERNEL_SRC, "xl": KERNEL_SRC,
+               "swin": KERNEL_SRC, "edge": KERNEL_SRC, "edge_kv": KERNEL_SRC,
+               "decode": DECODE_SRC, "decode_xl": DECODE_SRC}
 
 
 # ---------------------------------------------------------------------------
@@ -408,7 +420,6 @@ def alibi_report(ra, steps):
 # backward (relattn_bwd: dq/dk/dv kernels and the table-gradient reduction)
 # ---------------------------------------------------------------------------
 
-BWD_SRC = os.path.join(ROOT, "relative_position_encoding_amd", "csrc", "relattn_backward.hip")
 
 
 def bwd_work(w, key_lens):
@@ -733,8 +744,16 @@ def bound_of(flops, nbytes, dt):
 # ---------------------------------------------------------------------------
 
 def kernel_sha(path=KERNEL_SRC):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    """sha256 over a kernel source and the headers it shares with the others."""
+    h = hashlib.sha256()
+    for fn in [path] + SHARED_HEADERS:
+        with open(fn, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def traffic_source(name):
+    return BWD_SRC if name.startswith("bwd_") else TRAFFIC_SRC[name]
 
 
 def traffic_per_launch(name):
@@ -745,9 +764,7 @@ def traffic_per_launch(name):
         return None
     with open(path) as f:
         t = json.load(f)
-    src = DECODE_SRC if name.startswith("decode") else (BWD_SRC if name.startswith("bwd_")
-                                                        else KERNEL_SRC)
-    if t.get("kernel_sha256") != kernel_sha(src):
+    if t.get("kernel_sha256") != kernel_sha(traffic_source(name)):
         return None
     return t["fetch_kib"] * 1024 * t["fetch_scale"] + t["write_kib"] * 1024 * t["write_scale"]
 
@@ -774,12 +791,27 @@ def cpu_baseline(w, min_seconds=12.0):
         el = time.perf_counter() - t0
         if el >= min_seconds:
             break
+    import torch
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     return {"value": flops * reps / el / 1e12, "unit": "TFLOP/s", "cores": threads,
             "kind": "oracle",
-            "sample": f"whole {w.name} workload, fp64 factored oracle (Eq. 5 form), "
-                      f"{reps} run(s) in {el:.1f} s, {len(os.sched_getaffinity(0))} host "
-                      f"cores visible"}
+            "cpu": host_cpu_model(), "blas_threads": threads,
+            "torch_threads": torch.get_num_threads(),
+            "sample": f"whole {w.name} workload, fp64 factored oracle (Eq. 5 form, numpy with "
+                      f"{threads} BLAS thread(s)), {reps} run(s) in {el:.1f} s, "
+                      f"{len(os.sched_getaffinity(0))} host cores visible"}
+
+
+def host_cpu_model():
+    """Model name of the host CPU (first entry of /proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def oracle_report(per_workload_s=2.0):
