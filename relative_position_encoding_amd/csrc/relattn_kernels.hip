@@ -234,7 +234,19 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<D, NW, MODE, BF16, BC>()))) vo
   asm volatile("" ::"s"(p.q), "s"(p.q_sb), "s"(p.v_sn), "s"(p.tb_sb), "s"(p.dma32), "s"(gridDim.x));
   // ---- which tile
   int bh, qt;
-  if (p.causal && (gridDim.x & 7) == 0 && (gridDim.x >> 3) % p.n_qtiles == 0) {
+  constexpr int kCusPerXcd = 32;
+  if (p.causal && (gridDim.x & 7) == 0 && p.n_qtiles == kCusPerXcd &&
+      (gridDim.x >> 3) % (2 * kCusPerXcd) == 0) {
+    // A head has one causal tile per CU of its XCD: the XCD takes its heads two
+    // at a time and deals the pair's tiles heaviest first, alternating between
+    // the two heads, so only two heads' K and V are in use at a time (they fit
+    // the XCD's L2 where every head of the XCD at once did not).
+    const int x = blockIdx.x & 7, loc = blockIdx.x >> 3;
+    const int pair = loc / (2 * kCusPerXcd), k = loc % (2 * kCusPerXcd);
+    const int hpx = (gridDim.x >> 3) / p.n_qtiles;  // heads per XCD
+    bh = x * hpx + 2 * pair + (k & 1);
+    qt = p.n_qtiles - 1 - (k >> 1);
+  } else if (p.causal && (gridDim.x & 7) == 0 && (gridDim.x >> 3) % p.n_qtiles == 0) {
     // Causal tiles differ in work.  Each XCD holds whole heads; it is dealt the
     // heaviest tile of each of its heads first, then the next heaviest, and so
     // on, so that the workgroups that share a CU in one round differ in work
