@@ -170,6 +170,50 @@ def time_gpu(ra, w, steps, warmup, hot=False, reps=1):
     return res
 
 
+def time_gpu_graph(ra, w, steps, warmup, reps=5):
+    """The same K back-to-back calls captured once into a HIP graph and replayed:
+    the kernels and their inputs are those of time_gpu (cold input copies); the
+    host submits one graph launch instead of K kernel launches.  Returns ms per
+    call (median over the replays) and the host time per call of a replay."""
+    import statistics
+    import torch
+    lib = ra._load()
+    stream = torch.cuda.Stream()  # default priority
+    flops, nbytes, dense = work(w, None)
+    copies = max(1, min(16, int(2 * LLC_BYTES // max(nbytes, 1)) + 1))
+    x, calls, keep = _prepare(ra, w, copies, stream.cuda_stream)
+    fwd = lib.relattn_fwd
+    with torch.cuda.stream(stream):
+        for s in range(warmup):
+            if fwd(*calls[s % copies]) != 0:
+                raise RuntimeError(lib.relattn_last_error().decode())
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for s in range(steps):
+            if fwd(*calls[s % copies]) != 0:
+                raise RuntimeError(lib.relattn_last_error().decode())
+    torch.cuda.synchronize()
+    times, submit = [], []
+    with torch.cuda.stream(stream):
+        for _ in range(2):
+            g.replay()
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        for r in range(reps):
+            t0.record(stream)
+            w0 = time.perf_counter()
+            g.replay()
+            submit.append((time.perf_counter() - w0) / steps * 1e6)
+            t1.record(stream)
+            torch.cuda.synchronize()
+            times.append(t0.elapsed_time(t1) / steps)
+    del g, keep
+    return {"ms_per_step": statistics.median(times), "host_submit_us_per_step":
+            statistics.median(submit), "steps": steps, "reps": reps, "input_copies": copies}
+
+
 def ceiling_tflops(flops, nbytes, dt):
     """Roofline ceiling min(MFMA peak, arithmetic intensity x HBM peak), TFLOP/s."""
     return min(PEAK_TFLOPS[dt], flops / nbytes * PEAK_HBM_GBS / 1e3)
@@ -1054,6 +1098,12 @@ def main():
         "host_submit_us_per_step": round(head["host_submit_us_per_step"], 2),
         "gpu": gpu,
     }
+    # the same calls captured in one HIP graph and replayed (launch-bound loops)
+    gr = time_gpu_graph(ra, w, a.steps, a.warmup)
+    line["graph"] = {"ms_per_step": round(gr["ms_per_step"], 5),
+                     "host_submit_us_per_step": round(gr["host_submit_us_per_step"], 3),
+                     "steps": gr["steps"], "replays": gr["reps"],
+                     "note": "the timed calls captured once into a HIP graph, replayed whole"}
     if not a.only:
         # every workload, the headline included: median of 5 timed regions with
         # inputs streamed from HBM (cold) and with one cache-resident input set (hot)
