@@ -49,6 +49,7 @@ SHARED_HEADERS = [os.path.join(CSRC, h) for h in
 TRAFFIC_SRC = {"base": LEAN_SRC, "big_causal_k": LEAN_SRC, "big_causal_kv": LEAN_SRC,
                "long": KERNEL_SRC, "t5": KERNEL_SRC, "alibi": KERNEL_SRC, "xl": KERNEL_SRC,
                "swin": KERNEL_SRC, "edge": KERNEL_SRC, "edge_kv": KERNEL_SRC,
+               "xl128": KERNEL_SRC,
                "decode": DECODE_SRC, "decode_xl": DECODE_SRC}
 
 
@@ -591,12 +592,12 @@ def xl_work(w):
     return flops, nbytes
 
 
-def time_xl(ra, steps, warmup, hot=False, reps=5):
+def time_xl(ra, steps, warmup, hot=False, reps=5, name="xl"):
     import torch
     import workloads
     lib = ra._load()
     stream = torch.cuda.Stream()
-    w = workloads.XL_WORKLOADS["xl"]
+    w = workloads.XL_WORKLOADS[name]
     x = workloads.make_xl_inputs(w)
     flops, nbytes = xl_work(w)
     copies = 1 if hot else max(1, min(16, int(2 * LLC_BYTES // nbytes) + 1))
@@ -616,11 +617,11 @@ def time_xl(ra, steps, warmup, hot=False, reps=5):
             "alg_gflop": flops / 1e9, "alg_mbytes": nbytes / 1e6, "input_copies": copies}
 
 
-def xl_report(ra, steps):
+def xl_report(ra, steps, name="xl"):
     import workloads
-    w = workloads.XL_WORKLOADS["xl"]
-    cold = time_xl(ra, steps, 10)
-    hot = time_xl(ra, steps, 10, hot=True)
+    w = workloads.XL_WORKLOADS[name]
+    cold = time_xl(ra, steps, 10, name=name)
+    hot = time_xl(ra, steps, 10, hot=True, name=name)
     flops, nbytes = cold["alg_gflop"] * 1e9, cold["alg_mbytes"] * 1e6
     bound = bound_of(flops, nbytes, "bf16")
     sec = cold["ms_per_step"] * 1e-3
@@ -628,7 +629,7 @@ def xl_report(ra, steps):
         ach, peak, unit = nbytes / sec / 1e9, PEAK_HBM_GBS, "GB/s"
     else:
         ach, peak, unit = flops / sec / 1e12, PEAK_TFLOPS["bf16"], "TFLOP/s"
-    tr = traffic_per_launch("xl")
+    tr = traffic_per_launch(name)
     return {"workload": w.description, "ms_per_step": round(cold["ms_per_step"], 5),
             "tflops": round(cold["tflops"], 3),
             "mfma_peak_frac": round(cold["tflops"] / PEAK_TFLOPS["bf16"], 4),
@@ -1011,6 +1012,8 @@ def main():
                     help="time the backward on --workload only and print its figures")
     ap.add_argument("--xl-only", action="store_true",
                     help="time the Transformer-XL workload only and print its figures")
+    ap.add_argument("--xl128-only", action="store_true",
+                    help="time the Transformer-XL workload with 128-wide heads only")
     ap.add_argument("--grid-only", action="store_true",
                     help="time the 2-D window (Swin) workload only and print its figures")
     ap.add_argument("--edge-only", action="store_true",
@@ -1047,6 +1050,9 @@ def main():
         return
     if a.xl_only:
         print(json.dumps({"xl": xl_report(ra, max(50, a.steps // 5))}))
+        return
+    if a.xl128_only:
+        print(json.dumps({"xl128": xl_report(ra, max(50, a.steps // 5), "xl128")}))
         return
     if a.grid_only:
         print(json.dumps({"grid_bias": grid_report(ra, max(50, a.steps // 5))}))
@@ -1130,6 +1136,7 @@ def main():
         line["offset_bias"] = alibi_report(ra, max(50, a.steps // 5))
         line["backward"] = bwd_report(ra, max(50, a.steps // 5))
         line["xl"] = xl_report(ra, max(50, a.steps // 5))
+        line["xl128"] = xl_report(ra, max(50, a.steps // 5), "xl128")
         line["grid_bias"] = grid_report(ra, max(50, a.steps // 5))
         line["edge_bias"] = edge_report(ra, max(50, a.steps // 5))
         line["edge_tables"] = edge_report(ra, max(50, a.steps // 5), "edge_kv")

@@ -355,7 +355,7 @@ int make_plan(const relattn_tensor* q, const relattn_tensor* k, const relattn_te
   P.d = (int)d;
   P.mode = is_graph ? relattn::kRelGraph
           : is_lab ? relattn::kRelLabel
-                  : (is_xl && d <= 64) ? relattn::kRelXL
+                  : (is_xl && (d <= 64 || (q->dtype == RELATTN_BF16 && d == 128))) ? relattn::kRelXL
                   : (is_ob && grid_m > 0) ? relattn::kRelGrid
                   : (is_t5 || is_ob) ? relattn::kRelT5
                                      : ((wK || wV) ? relattn::kRelShaw : relattn::kRelNone);
@@ -457,7 +457,10 @@ int make_plan(const relattn_tensor* q, const relattn_tensor* k, const relattn_te
     // one four-wave workgroup (measured 33.8 vs 37.0 us on B8 H16 n512 d64)
     if (P.mode == relattn::kRelXL) waves = {2, 4, 1};
     kblocks = {64};
-    if (d == 128) kblocks.push_back(32);  // two waves per SIMD at d = 128
+    // two waves per SIMD at d = 128 with 32-key tiles, except for the fused
+    // Transformer-XL mode, whose table fragments spill there (it runs one wave
+    // per SIMD with 64-key tiles)
+    if (d == 128 && P.mode != relattn::kRelXL) kblocks.push_back(32);
   } else {
     kblocks = {32};
     if (n <= 32) waves = {1, 2};

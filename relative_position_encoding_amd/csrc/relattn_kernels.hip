@@ -1121,7 +1121,7 @@ static int launch_mode(RelMode mode, bool has_wk, bool has_wv, const FwdParams& 
   if (mode == kRelGrid) return launch_t<D, NW, BC, BF16, kRelGrid, false, false>(p, stream);
   if (mode == kRelLabel) return launch_t<D, NW, BC, BF16, kRelLabel, false, false>(p, stream);
   if (mode == kRelXL) {
-    if constexpr (D <= 64) return launch_t<D, NW, BC, BF16, kRelXL, false, false>(p, stream);
+    if constexpr (D <= 64 || BF16) return launch_t<D, NW, BC, BF16, kRelXL, false, false>(p, stream);
     return (int)hipErrorInvalidValue;
   }
   if (mode == kRelGraph) {

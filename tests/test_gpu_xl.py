@@ -116,18 +116,20 @@ def test_xl_small_rows_d16(ra, dtype, n, causal):
     assert float(np.max(np.abs(got - want))) <= TOL[dtype]
 
 
-def test_xl_full_size(ra):
-    """The benchmark segment (B8 H16 n512 d64, causal, every distance), in the
-    launch configuration the benchmark times, against the oracle on sampled
-    (batch, head) slices."""
+@pytest.mark.parametrize("name,slices", [("xl", ((0, 0), (3, 9), (7, 15))),
+                                         ("xl128", ((0, 0), (4, 3), (7, 7)))])
+def test_xl_full_size(ra, name, slices):
+    """The benchmark segments (B8 H16 n512 d64 and B8 H8 n512 d128, causal, every
+    distance), in the launch configuration the benchmark times, against the
+    oracle on sampled (batch, head) slices."""
     import workloads
-    w = workloads.XL_WORKLOADS["xl"]
+    w = workloads.XL_WORKLOADS[name]
     x = workloads.make_xl_inputs(w)
     out = ra.fwd_xl(*(x[key].to(DEV) for key in ("q", "k", "v", "R", "u", "vb")), x["window"],
                     causal=True)
     torch.cuda.synchronize()
     out = out.double().cpu().numpy()
-    for b, h in ((0, 0), (3, 9), (7, 15)):
+    for b, h in slices:
         sl = lambda t: t[b:b + 1, h:h + 1]
         want = oracle.xl_attention(sl(x["q"]), sl(x["k"]), sl(x["v"]), x["R"][h:h + 1],
                                    x["u"][h:h + 1], x["vb"][h:h + 1], x["window"], causal=True)
@@ -135,7 +137,7 @@ def test_xl_full_size(ra):
         assert err <= TOL[torch.bfloat16], (b, h, err)
 
 
-@pytest.mark.parametrize("d", [32, 64])
+@pytest.mark.parametrize("d", [32, 64, 128])
 def test_xl_long_segment(ra, d):
     """n = 2048 with every distance (fused mode: 32 key tiles per row, table
     rows read across the whole window)."""

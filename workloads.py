@@ -241,6 +241,12 @@ XL_WORKLOADS = {
                     "n512 d64 causal, position table over every distance (window 511), "
                     "per-head u and v",
         batch=8, heads=16, n=512, d=64, window=511),
+    "xl128": XLWorkload(
+        name="xl128", config_id=7,
+        description="Transformer-XL relative logits with 128-wide heads: B8 H8 n512 d128 "
+                    "causal, position table over every distance (window 511), per-head u "
+                    "and v",
+        batch=8, heads=8, n=512, d=128, window=511),
 }
 
 
