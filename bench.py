@@ -41,14 +41,16 @@ KERNEL_SRC = os.path.join(CSRC, "relattn_kernels.hip")
 LEAN_SRC = os.path.join(CSRC, "relattn_fwd_bf16.hip")
 DECODE_SRC = os.path.join(CSRC, "relattn_decode.hip")
 BWD_SRC = os.path.join(CSRC, "relattn_backward.hip")
+WINDOW_SRC = os.path.join(CSRC, "relattn_window.hip")
 # headers every kernel source includes (tile layout, device helpers, parameters)
 SHARED_HEADERS = [os.path.join(CSRC, h) for h in
                   ("relattn_device.h", "relattn_internal.h", "relattn_tiles.h")]
 # the kernel source each measured arm runs: the lean bf16 kernel serves the Shaw
-# tables at d = 64, the general kernel the other forward arms
+# tables at d = 64, the small-window kernel the 7 x 7 windows, the general
+# kernel the other forward arms
 TRAFFIC_SRC = {"base": LEAN_SRC, "big_causal_k": LEAN_SRC, "big_causal_kv": LEAN_SRC,
                "long": KERNEL_SRC, "t5": KERNEL_SRC, "alibi": KERNEL_SRC, "xl": KERNEL_SRC,
-               "swin": KERNEL_SRC, "edge": KERNEL_SRC, "edge_kv": KERNEL_SRC,
+               "swin": WINDOW_SRC, "edge": KERNEL_SRC, "edge_kv": KERNEL_SRC,
                "xl128": KERNEL_SRC,
                "decode": DECODE_SRC, "decode_xl": DECODE_SRC}
 

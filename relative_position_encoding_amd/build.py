@@ -20,7 +20,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "librelattn.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["relattn_kernels.hip", "relattn_fwd_bf16.hip", "relattn_decode.hip",
+SOURCES = ["relattn_kernels.hip", "relattn_fwd_bf16.hip", "relattn_window.hip", "relattn_decode.hip",
            "relattn_backward.hip", "relattn_api.cpp"]
 
 FLAGS = [

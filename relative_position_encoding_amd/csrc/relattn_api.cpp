@@ -482,6 +482,14 @@ int make_plan(const relattn_tensor* q, const relattn_tensor* k, const relattn_te
     waves = keep;
   }
   bool found_lean = false;
+  // Small windows of the 2-D window bias: the persistent window kernel
+  // (a whole window is one key tile; items stream through two LDS slots)
+  if (P.mode == relattn::kRelGrid &&
+      relattn::window_grid_ok(P.bf16, P.d, (int)n, grid_m,
+                              std::max({q->stride[2], k->stride[2], v->stride[2]}))) {
+    P.cfg = LaunchCfg{2, 64, 1, relattn::kWvResident, 3};
+    found_lean = true;
+  }
   // The lean bf16 kernel serves the Shaw tables and plain attention at d = 64
   // whenever its resident tables and relative rows fit.  Among its shapes take
   // the one that keeps the most waves of this grid resident per compute unit
@@ -490,7 +498,7 @@ int make_plan(const relattn_tensor* q, const relattn_tensor* k, const relattn_te
   // products: measured 14.1 us against 16.3 us for one eight-wave workgroup on
   // the Transformer-big causal shape), then the deepest ring (a ring that
   // holds every tile of a workgroup requests them all at entry).
-  if (relattn::lean_mode_ok(P.bf16, P.d, P.mode) && !is_xl) {
+  if (!found_lean && relattn::lean_mode_ok(P.bf16, P.d, P.mode) && !is_xl) {
     const int kb = P.d == 64 ? 64 : 32;
     int64_t best_res = -1;
     int best_st = -1, best_w = -1;
@@ -1069,7 +1077,9 @@ int run_fwd(const Plan& plan, void* stream) {
   int st;
   if ((st = check_device())) return st;
   if (plan.empty) return RELATTN_OK;
-  const int e = plan.cfg.lean
+  const int e = plan.cfg.lean == 3
+                    ? relattn::launch_window_grid(plan.d, plan.p, stream)
+                : plan.cfg.lean
                     ? relattn::launch_fwd_lean(plan.d, plan.cfg, plan.mode, plan.has_wk,
                                                plan.has_wv, plan.p, stream)
                     : relattn::launch_fwd(plan.bf16, plan.d, plan.cfg, plan.mode, plan.has_wk,

@@ -33,7 +33,6 @@ namespace {
 
 constexpr float kSlack = 8.f;  // log2 units a row max may run ahead of the one in use
 
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 // One 16-byte K fragment read from LDS (32-key block kb of the tile at the

@@ -110,7 +110,7 @@ struct LaunchCfg {
   int kblock;  // keys per tile
   int nstage;  // K/V tiles in the LDS ring
   int wv_mode;  // WvMode (general kernel)
-  int lean = 0;  // 1: the lean bf16 kernel (relattn_fwd_bf16.hip)
+  int lean = 0;  // 1: the lean bf16 kernel (relattn_fwd_bf16.hip); 3: the small-window kernel
 };
 
 // Dynamic LDS bytes of one workgroup (same layout function as the kernel);
@@ -127,6 +127,14 @@ size_t lean_lds_bytes(int d, const LaunchCfg& cfg, RelMode mode, bool has_wk, bo
                       int nr, int t5_dist, int t5_nb);
 int launch_fwd_lean(int d, const LaunchCfg& cfg, RelMode mode, bool has_wk, bool has_wv,
                     const FwdParams& p, void* stream);
+
+// The persistent small-window kernel of the 2-D window bias
+// (relattn_window.hip): bf16, d = 32 or 64, windows of at most 64 tokens
+// (M <= 8), row strides below 2^24 elements; each workgroup walks a run of
+// (window, head) items through a ring of LDS slots, the next items' rows
+// requested during the current one.
+bool window_grid_ok(bool bf16, int d, int n, int grid_m, int64_t max_row_stride);
+int launch_window_grid(int d, const FwdParams& p, void* stream);
 
 // Launchers (relattn_kernels.hip).  Return a hipError_t value.
 int launch_fwd(bool bf16, int d, const LaunchCfg& cfg, RelMode mode, bool has_wk,

@@ -72,6 +72,29 @@ def test_grid_bias_full_size_windows(ra):
         assert float(np.max(np.abs(out[b:b + 1] - want))) <= TOL[torch.bfloat16]
 
 
+@pytest.mark.parametrize("B,H,M,d", [(2045, 3, 7, 32), (49200, 3, 7, 32), (16387, 2, 8, 64),
+                                     (3001, 4, 5, 64)])
+def test_grid_bias_long_runs(ra, B, H, M, d):
+    """Many windows per launch (bf16): each workgroup walks a run of
+    (window, head) items that crosses head boundaries, and runs of more than 64
+    items restage their key lengths; sampled windows (every head) against the
+    oracle, with ragged key lengths."""
+    n = M * M
+    g = torch.Generator(device=DEV).manual_seed(2100 + B)
+    q, k, v = (torch.randn(B, H, n, d, generator=g, device=DEV).to(torch.bfloat16)
+               for _ in range(3))
+    bias = gen((H, (2 * M - 1) ** 2), torch.float32, 2104)
+    lens = torch.randint(1, n + 1, (B,), generator=g, device=DEV, dtype=torch.int32)
+    out = ra.fwd_grid_bias(q, k, v, bias.to(DEV), M, key_lens=lens)
+    torch.cuda.synchronize()
+    lens_h = lens.cpu().tolist()
+    for b in sorted({0, 1, 63, 64, 65, B // 3, B // 2 + 7, B - 65, B - 2, B - 1}):
+        want = oracle.grid_bias_attention(q[b:b + 1].cpu(), k[b:b + 1].cpu(), v[b:b + 1].cpu(),
+                                          bias, M, key_lens=[lens_h[b]])
+        err = float(np.max(np.abs(out[b:b + 1].double().cpu().numpy() - want)))
+        assert err <= TOL[torch.bfloat16], (b, err)
+
+
 def test_grid_bias_rejects(ra):
     q = gen((1, 2, 49, 32), torch.bfloat16, 1900).to(DEV)
     bias = torch.zeros(2, 169, device=DEV)
