@@ -547,11 +547,12 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<D, NW, MODE, BF16, BC>()))) vo
   const int hoff = BF16 ? 8 * hh : hh;  // key offset of this lane half
   int wv_stage = -1, wv_cnt = 0;        // ring stage and DMA count of the w^V tile
 
-  int st_cur = 0, st_next = nstage - 1;  // ring stages of tiles t and t + nstage - 1
-  for (int t = 0; t < ntiles; ++t, st_cur = (st_cur + 1 == nstage) ? 0 : st_cur + 1,
-           st_next = (st_next + 1 == nstage) ? 0 : st_next + 1) {
+  // Start of tile t: the tile landed for this wave (later stages and w^V may
+  // still be in flight), then for every wave, which frees stage (t - 1) %
+  // nstage for the next request.  `act`: the wave computes the tile.
+  using XrOps = Op[XLF ? NXB : 1][NKS];
+  auto tile_head = [&](int t, int st_next, bool act, XrOps& xr) __attribute__((always_inline)) {
     const int j0 = t * BC;
-    // tile t landed for this wave (later stages and w^V may still be in flight) ...
     {
       // the steady state (one stage still in flight) and the drained state
       // take one compare each instead of the general switch's branch tree
@@ -560,14 +561,13 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<D, NW, MODE, BF16, BC>()))) vo
       else if (pending == 0) wait_vm<0>();
       else wait_vm_dyn(pending);
     }
-    block_sync();  // ... and for every wave; stage (t - 1) % nstage is free
+    block_sync();
     // fused XL: the position-table rows of the distances this wave reaches in
     // the tile, as MFMA A operands (row = MFMA row ql of block b: offset j - i
     // = omin + 32 b + ql, distance i - j clamped to the window), requested
     // before the next stage so that one counted wait covers them
-    Op xr[XLF ? NXB : 1][NKS];
     if constexpr (XLF) {
-      if (wq0 < p.n && !(p.causal && j0 > wq0 + 31)) {
+      if (act) {
         const int omin = j0 - wq0 - 31;
 #pragma unroll
         for (int bx = 0; bx < NXB; ++bx) {
@@ -593,9 +593,20 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<D, NW, MODE, BF16, BC>()))) vo
                                   lay.wv_rows, wave, lane);
       compiler_fence();
     }
-
-    if (wq0 >= p.n) continue;                  // no live query in this wave
-    if (p.causal && j0 > wq0 + 31) continue;   // tile entirely in the future
+  };
+  // The tiles this wave computes are a prefix: none when it holds no live
+  // query, under the causal mask those up to its last row.  The rest only
+  // keep the workgroup's waits, barriers and requests in step.  (Two loops
+  // rather than a skip inside one: a path around the tile's work made the
+  // compiler copy every accumulator at the loop's back edge.)
+  const int t_act = (wq0 >= p.n) ? 0 : (p.causal ? min(ntiles, (wq0 + 31) / BC + 1) : ntiles);
+  int st_cur = 0, st_next = nstage - 1;  // ring stages of tiles t and t + nstage - 1
+  int t = 0;
+  for (; t < t_act; ++t, st_cur = (st_cur + 1 == nstage) ? 0 : st_cur + 1,
+                    st_next = (st_next + 1 == nstage) ? 0 : st_next + 1) {
+    const int j0 = t * BC;
+    XrOps xr;
+    tile_head(t, st_next, true, xr);
 
     const unsigned char* Kt = smem + st_cur * G::STAGEB;
     const unsigned char* Vt = Kt + G::TILEB;
@@ -694,16 +705,31 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<D, NW, MODE, BF16, BC>()))) vo
           tmax = fmaxf(tmax, x);
         }
     };
-    {
+    // one relative logit for every key of the tile (the lane's end value)
+    auto finish_const = [&](float rel, auto mask_tag) __attribute__((always_inline)) {
+      constexpr bool MASK = decltype(mask_tag)::value;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int ko = 32 * kb + 16 * (i >> 3) + KSTR * (i & 7);
+          float x = fmaf(s[kb][i], p.scale_log2, rel);
+          if constexpr (MASK) x = (ko <= lim) ? x : kNegInf;
+          s[kb][i] = x;
+          tmax = fmaxf(tmax, x);
+        }
+    };
+    if (!GATHER || off_band) {
+      // no gathered term: nothing relative, or the tile's end value
+      const float rel = GATHER ? (all_lo ? Llo : Lhi) : 0.f;
+      if (need_mask) {
+        finish_const(rel, std::true_type{});
+      } else {
+        finish_const(rel, std::false_type{});
+      }
+    } else {
       float rv[NKB][16];
-      if (!GATHER || off_band) {
-        // no gathered term: nothing relative, or the tile's end value
-        const float rel = GATHER ? (all_lo ? Llo : Lhi) : 0.f;
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) rv[kb][i] = rel;
-      } else if constexpr (LAB) {
+      if constexpr (LAB) {
         // edge labels: the bias of each key's label, from the 16-byte label
         // chunk of the lane's row that holds 16 consecutive keys of the tile
         const unsigned char* labt = smem + lay.lab + st_cur * LABB + wave * (32 * BC);
@@ -829,15 +855,38 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<D, NW, MODE, BF16, BC>()))) vo
     }
     const float m_use = (m_run == kNegInf) ? 0.f : m_run;
 
+    // the weights; in bf16 also as the operands of the P.V product, whose
+    // row sum is taken from those same operands by pairwise dot products with
+    // (1, 1), so that the normaliser sums exactly the weights the product uses
     float psum = 0.f;
+    [[maybe_unused]] bf16x8 pbw[BF16 ? NKB : 1][2];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const float pv = fast_exp2(s[kb][i] - m_use);
         s[kb][i] = pv;
-        psum += pv;
+        if constexpr (BF16) pbw[kb][i >> 3][i & 7] = (__bf16)pv;
+        else psum += pv;
       }
+    }
+    if constexpr (BF16) {
+      bf16x2 one;
+      one[0] = (__bf16)1.f;
+      one[1] = (__bf16)1.f;
+      float acc2[2] = {0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+          for (int e = 0; e < 8; e += 2) {
+            bf16x2 pr;
+            pr[0] = pbw[kb][t2][e];
+            pr[1] = pbw[kb][t2][e + 1];
+            acc2[t2] = __builtin_amdgcn_fdot2_f32_bf16(pr, one, acc2[t2], false);
+          }
+      psum = acc2[0] + acc2[1];
     }
     l_part += psum;
     if constexpr (GRAPH && HAS_WV) {
@@ -881,17 +930,13 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<D, NW, MODE, BF16, BC>()))) vo
           for (int mb = 0; mb < DVB; ++mb)
             frag_col_issue_blk<ROWB>(2 * kb + t2, vt_lds + trb_lo[mb], vt_lds + trb_hi[mb],
                                      vlo[t2 * DVB + mb], vhi[t2 * DVB + mb]);
-        bf16x8 pb[2];
-#pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) pb[t2][e] = (__bf16)s[kb][8 * t2 + e];
         frag_col_wait(vlo, vhi);
 #pragma unroll
         for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
           for (int mb = 0; mb < DVB; ++mb)
-            oacc[mb] = mfma(frag_join(vlo[t2 * DVB + mb], vhi[t2 * DVB + mb]), pb[t2], oacc[mb]);
+            oacc[mb] = mfma(frag_join(vlo[t2 * DVB + mb], vhi[t2 * DVB + mb]), pbw[kb][t2],
+                            oacc[mb]);
       } else {
 #pragma unroll
         for (int s2 = 0; s2 < 16; ++s2) {
@@ -903,6 +948,11 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<D, NW, MODE, BF16, BC>()))) vo
         }
       }
     }
+  }
+  for (; t < ntiles; ++t, st_cur = (st_cur + 1 == nstage) ? 0 : st_cur + 1,
+                    st_next = (st_next + 1 == nstage) ? 0 : st_next + 1) {
+    XrOps xr;
+    tile_head(t, st_next, false, xr);
   }
   if (wv_ring && wv_stage < 0) {
     // no tile ran: any stage is free
