@@ -1139,7 +1139,12 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd<D>()))) void bwd_kv_kernel
             rl = TB[min(max(delta, -dist), dist) + dist];
           }
           const bool vis = qq < p.n && (!p.causal || delta <= 0);
-          const float pv = vis ? fast_exp2(fmaf(s[i], p.scale_log2, rl) - lsv[i]) : 0.f;
+          // the exponential for every lane, then a select (a conditional
+          // exponential becomes a branch per element, each waiting for its
+          // own row reads)
+          float ex = fast_exp2(fmaf(s[i], p.scale_log2, rl) - lsv[i]);
+          asm volatile("" : "+v"(ex));
+          const float pv = vis ? ex : 0.f;
           pw[i] = pv;
           ds[i] = vis ? pv * (dp[i] + rv - ddv[i]) : 0.f;
         }
