@@ -95,6 +95,38 @@ def test_grid_bias_long_runs(ra, B, H, M, d):
         assert err <= TOL[torch.bfloat16], (b, err)
 
 
+@pytest.mark.parametrize("d", [32, 64])
+def test_grid_bias_window_layouts(ra, d):
+    """Small windows (bf16) from strided operands: q a head-interleaved
+    [B, n, H, d] buffer seen as [B, H, n, d], k and v slices of wider rows, the
+    table rows of a wider table, the output written into a strided view;
+    windows with no visible key (length 0) give zero rows, like the oracle's."""
+    B, H, M = 37, 3, 7
+    n = M * M
+    g = torch.Generator(device=DEV).manual_seed(2200 + d)
+    qb = torch.randn(B, n, H, d, generator=g, device=DEV).to(torch.bfloat16)
+    q = qb.permute(0, 2, 1, 3)
+    kb = torch.randn(B, H, n, 2 * d, generator=g, device=DEV).to(torch.bfloat16)
+    vb = torch.randn(B, H, n, d + 16, generator=g, device=DEV).to(torch.bfloat16)
+    k, v = kb[..., d:], vb[..., 8:8 + d]
+    nb = (2 * M - 1) ** 2
+    bias_w = gen((H, nb + 12), torch.float32, 2204).to(DEV)
+    bias = bias_w[:, 4:4 + nb]  # rows of a wider table
+    lens = torch.randint(0, n + 1, (B,), generator=g, device=DEV, dtype=torch.int32)
+    lens[0], lens[1], lens[2] = 0, n, 1
+    ob = torch.full((B, H, n, d + 16), float("nan"), device=DEV, dtype=torch.bfloat16)
+    out = ob[..., 8:8 + d]  # (operands start on 16-byte boundaries)
+    ra.fwd_grid_bias(q, k, v, bias, M, key_lens=lens, out=out)
+    torch.cuda.synchronize()
+    assert torch.isnan(ob[..., :8]).all() and torch.isnan(ob[..., 8 + d:]).all()
+    want = oracle.grid_bias_attention(q.cpu(), k.cpu(), v.cpu(), bias.cpu(), M,
+                                      key_lens=lens.cpu().tolist())
+    err = float(np.max(np.abs(out.double().cpu().numpy() - want)))
+    assert err <= TOL[torch.bfloat16], err
+    assert not torch.isnan(out).any()
+    assert float(out[0].abs().max()) == 0.0
+
+
 def test_grid_bias_rejects(ra):
     q = gen((1, 2, 49, 32), torch.bfloat16, 1900).to(DEV)
     bias = torch.zeros(2, 169, device=DEV)
