@@ -262,7 +262,17 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<D, NW, MODE, BF16, BC>()))) vo
     qt = lid - bh * p.n_qtiles;
     if (p.causal) qt = p.n_qtiles - 1 - qt;  // longest causal rows first
   }
-  const int b = bh / p.H, h = bh - b * p.H;
+  // (b, h) of the tile: batch entry major; in the XL mode head major instead,
+  // so that the heads' position tables, shared by every batch entry, are read
+  // by one XCD each (an XCD holds consecutive ids) rather than by all of them
+  int b, h;
+  if constexpr (XLF) {
+    h = bh / p.B;
+    b = bh - h * p.B;
+  } else {
+    b = bh / p.H;
+    h = bh - b * p.H;
+  }
   const int i0 = qt * (32 * NW);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar loops
