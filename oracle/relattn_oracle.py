@@ -90,6 +90,7 @@ __all__ = [
     "xl_attention",
     "xl_decode",
     "grid_bias_attention",
+    "grid_bias_backward",
     "edge_label_attention",
     "edge_label_relattn",
     "to_f64",
@@ -733,6 +734,41 @@ def grid_bias_attention(q, k, v, bias, window: int, scale=None, key_lens=None):
             e = s * (q[b, h] @ k[b, h].T) + row[entry]
             z[b, h] = _masked_softmax_rows(e, ok) @ v[b, h]
     return z
+
+
+def grid_bias_backward(q, k, v, bias, window: int, dz=None, scale=None, key_lens=None):
+    """Gradients (dq, dk, dv, dbias) of sum(dz * z) for grid_bias_attention, the
+    2-D window bias as a function of its table (survey page, "Relative position
+    embeddings", Swin paragraph): de_ij = alpha_ij (dalpha_ij - sum_j' alpha_ij'
+    dalpha_ij') with dalpha_ij = dz_i . v_j, dq = s de k, dk = s de^T q,
+    dv = alpha^T dz, and dbias[h', e] = the sum of de_ij over the pairs whose
+    flattened 2-D offset is entry e (summed over the heads when one row serves
+    every head)."""
+    q, k, v, dz = to_f64(q), to_f64(k), to_f64(v), to_f64(dz)
+    bias = to_f64(bias)
+    B, H, n, d = q.shape
+    M = int(window)
+    assert n == M * M
+    s = _default_scale(d, scale)
+    lens = _key_lengths(key_lens, B, n)
+    y, x = np.divmod(np.arange(n), M)
+    entry = (y[None, :] - y[:, None] + M - 1) * (2 * M - 1) + (x[None, :] - x[:, None] + M - 1)
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    db = np.zeros_like(bias)
+    for b in range(B):
+        ok = visible(n, False, lens[b])
+        for h in range(H):
+            hb = 0 if bias.shape[0] == 1 else h
+            e = s * (q[b, h] @ k[b, h].T) + bias[hb][entry]
+            alpha = _masked_softmax_rows(e, ok)
+            dalpha = dz[b, h] @ v[b, h].T
+            de = alpha * (dalpha - (alpha * dalpha).sum(axis=1, keepdims=True))
+            dq[b, h] = s * de @ k[b, h]
+            dk[b, h] = s * de.T @ q[b, h]
+            dv[b, h] = alpha.T @ dz[b, h]
+            db[hb] += np.bincount(entry.ravel(), weights=de.ravel(),
+                                  minlength=(2 * M - 1) ** 2)
+    return dq, dk, dv, db
 
 
 # ---------------------------------------------------------------------------

@@ -777,6 +777,47 @@ def test_grid_bias_constant_table_is_textbook_attention():
     np.testing.assert_allclose(got, want, rtol=0, atol=1e-12)
 
 
+@pytest.mark.parametrize("shared", [False, True])
+def test_grid_bias_backward_matches_finite_differences(shared):
+    M, B, H, d = 3, 2, 2, 4
+    n = M * M
+    q, k, v, dz = (rnd((B, H, n, d), 240 + i) for i in range(4))
+    bias = rnd((1 if shared else H, (2 * M - 1) ** 2), 244)
+    lens = [n, 5]
+    grads = oracle.grid_bias_backward(q, k, v, bias, M, dz, key_lens=lens)
+    loss = lambda: float((dz * oracle.grid_bias_attention(q, k, v, bias, M,
+                                                          key_lens=lens)).sum())
+    rng = np.random.default_rng(245)
+    for x, g in zip((q, k, v, bias), grads):
+        idx = [tuple(int(rng.integers(s)) for s in x.shape) for _ in range(6)]
+        _fd_check(loss, x, g, idx)
+
+
+@pytest.mark.parametrize("M", [2, 4])
+def test_grid_bias_backward_of_a_1d_offset_function_is_the_offset_bias_backward(M):
+    """With a table holding f(dy*M + dx), q, k and v get the offset-bias
+    gradients, and the table's gradient summed over the entries of each raster
+    offset is the offset table's gradient (an entry swap or a sign slip in the
+    entry fails); each head's table gradient sums to zero (softmax rows)."""
+    n = M * M
+    B, H, d = 2, 2, 8
+    q, k, v, dz = (rnd((B, H, n, d), 250 + i) for i in range(4))
+    W = n - 1
+    f = rnd((H, 2 * W + 1), 254)
+    dy, dx = np.meshgrid(np.arange(-(M - 1), M), np.arange(-(M - 1), M), indexing="ij")
+    delta = (dy * M + dx).ravel()
+    table = np.stack([f[h][W + delta] for h in range(H)])
+    lens = [n, max(1, n - 3)]
+    gq, gk, gv, gdb = oracle.grid_bias_backward(q, k, v, table, M, dz, key_lens=lens)
+    oq, ok_, ov, odb = oracle.offset_bias_backward(q, k, v, f, W, dz, key_lens=lens)
+    for a, b_ in ((gq, oq), (gk, ok_), (gv, ov)):
+        np.testing.assert_allclose(a, b_, rtol=0, atol=1e-12)
+    for h in range(H):
+        folded = np.bincount(W + delta, weights=gdb[h], minlength=2 * W + 1)
+        np.testing.assert_allclose(folded, odb[h], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(gdb.sum(axis=1), 0.0, atol=1e-12)
+
+
 def test_grid_bias_entry_layout_probe():
     """A single large entry at (dy, dx) = (1, -2) with q = 0: each query's
     weights pile on the key one row down and two columns left when it exists,
