@@ -511,6 +511,35 @@ int relattn_bwd_offset_bias_workspace_size(const relattn_tensor* q, const relatt
                                            const relattn_tensor* dk, const relattn_tensor* dv,
                                            const relattn_tensor* dbias, size_t* bytes);
 
+/* relattn_fwd_grid_bias_lse, relattn_bwd_grid_bias and its workspace size: the
+ * same for the 2-D window bias of relattn_fwd_grid_bias (survey page "Relative
+ * position embeddings", Swin paragraph), differentiated by the chain rule:
+ *     dbias[h', e] = sum over the heads h' covers, the windows and the pairs
+ *                    (i, j) whose 2-D offset is entry e of dS_ij
+ * lse as for relattn_fwd_lse; dbias is [Hb, (2M-1)^2] F32 or NULL.  The
+ * backward holds the head's (2M-1)^2 entries on chip, and with dbias a
+ * per-wave sum over them: large windows give UNSUPPORTED (head size 64 in
+ * BF16: M up to 40 with dbias, 74 without). */
+int relattn_fwd_grid_bias_lse(const relattn_tensor* q, const relattn_tensor* k,
+                              const relattn_tensor* v, const relattn_tensor* bias,
+                              int32_t window_side, float scale, const relattn_mask* mask,
+                              relattn_tensor* out, relattn_tensor* lse, void* stream);
+int relattn_bwd_grid_bias(const relattn_tensor* q, const relattn_tensor* k,
+                          const relattn_tensor* v, const relattn_tensor* bias,
+                          int32_t window_side, float scale, const relattn_mask* mask,
+                          const relattn_tensor* out, const relattn_tensor* dout,
+                          const relattn_tensor* lse, relattn_tensor* dq, relattn_tensor* dk,
+                          relattn_tensor* dv, relattn_tensor* dbias, void* workspace,
+                          size_t workspace_bytes, void* stream);
+int relattn_bwd_grid_bias_workspace_size(const relattn_tensor* q, const relattn_tensor* k,
+                                         const relattn_tensor* v, const relattn_tensor* bias,
+                                         int32_t window_side, float scale,
+                                         const relattn_mask* mask, const relattn_tensor* out,
+                                         const relattn_tensor* dout,
+                                         const relattn_tensor* lse, const relattn_tensor* dq,
+                                         const relattn_tensor* dk, const relattn_tensor* dv,
+                                         const relattn_tensor* dbias, size_t* bytes);
+
 /* Static text for a status code. */
 const char* relattn_strerror(int status);
 

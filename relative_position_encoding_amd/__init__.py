@@ -15,7 +15,8 @@ __all__ = ["fwd", "validate", "fwd_offset_bias", "validate_offset_bias", "decode
            "decode_workspace_size", "decode_noalloc", "debug_indices", "fwd_lse", "fwd_offset_bias_lse",
            "bwd", "bwd_workspace_size", "bwd_offset_bias", "bwd_offset_bias_workspace_size",
            "attention", "attention_offset_bias", "fwd_xl", "validate_xl", "fwd_grid_bias",
-           "validate_grid_bias", "fwd_edge_bias", "validate_edge_bias", "edge_label_buffer",
+           "validate_grid_bias", "fwd_grid_bias_lse", "bwd_grid_bias",
+           "bwd_grid_bias_workspace_size", "attention_grid_bias", "fwd_edge_bias", "validate_edge_bias", "edge_label_buffer",
            "fwd_edge_tables", "validate_edge_tables", "decode_offset_bias",
            "decode_offset_bias_workspace_size", "decode_xl", "decode_xl_workspace_size",
            "RelattnError", "library_path",
@@ -123,6 +124,13 @@ def _load():
     lib.relattn_fwd_grid_bias.restype = ctypes.c_int
     lib.relattn_validate_grid_bias.argtypes = ob
     lib.relattn_validate_grid_bias.restype = ctypes.c_int
+    lib.relattn_fwd_grid_bias_lse.argtypes = ob + [P(_Tensor), ctypes.c_void_p]
+    lib.relattn_fwd_grid_bias_lse.restype = ctypes.c_int
+    lib.relattn_bwd_grid_bias.argtypes = obw + [ctypes.c_void_p, ctypes.c_size_t,
+                                                ctypes.c_void_p]
+    lib.relattn_bwd_grid_bias.restype = ctypes.c_int
+    lib.relattn_bwd_grid_bias_workspace_size.argtypes = obw + [P(ctypes.c_size_t)]
+    lib.relattn_bwd_grid_bias_workspace_size.restype = ctypes.c_int
     edge = [P(_Tensor)] * 5 + [ctypes.c_float, P(_Mask), P(_Tensor)]
     lib.relattn_fwd_edge_bias.argtypes = edge + [ctypes.c_void_p]
     lib.relattn_fwd_edge_bias.restype = ctypes.c_int
@@ -765,6 +773,100 @@ def validate_grid_bias(q, k, v, bias, window_side, *, causal=False, key_lens=Non
     st = lib.relattn_validate_grid_bias(*args)
     del keep
     return st
+
+
+@_on_stream
+def fwd_grid_bias_lse(q, k, v, bias, window_side, *, key_lens=None, scale=None, out=None,
+                      lse=None, stream=None):
+    """``fwd_grid_bias`` with the row log-sum-exp; returns (out, lse)."""
+    import torch
+    lib = _load()
+    _check_lens(key_lens)
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    if lse is None:
+        lse = _new_lse(q)
+    args, keep = _ob_args(q, k, v, bias, window_side, False, key_lens, scale, out)
+    lv = _view(lse)
+    st = lib.relattn_fwd_grid_bias_lse(*args, _ref(lv), ctypes.c_void_p(_stream_of(q, stream)))
+    del keep, lv
+    if st != OK:
+        _raise(lib, st)
+    return out, lse
+
+
+def bwd_grid_bias_workspace_size(q, k, v, bias, window_side, *, out, dout, lse, key_lens=None,
+                                 scale=None, want_dbias=True):
+    """Workspace bytes ``bwd_grid_bias`` needs (host only)."""
+    lib = _load()
+    db = _bwd_outputs(q, None, None, bias, q, q, q, None, None, None, False, False,
+                      want_dbias)[5]
+    args, keep = _bwd_ob_args(q, k, v, bias, window_side, False, key_lens, scale, out, dout,
+                              lse, (q, q, q, db))
+    n = ctypes.c_size_t(0)
+    st = lib.relattn_bwd_grid_bias_workspace_size(*args, ctypes.byref(n))
+    del keep
+    if st != OK:
+        _raise(lib, st)
+    return int(n.value)
+
+
+@_on_stream
+def bwd_grid_bias(q, k, v, bias, window_side, *, out, dout, lse, key_lens=None, scale=None,
+                  dq=None, dk=None, dv=None, dbias=None, want_dbias=True, workspace=None,
+                  stream=None):
+    """Gradients for ``fwd_grid_bias_lse``: returns (dq, dk, dv, dbias); dbias
+    float32 like ``bias`` (None when not wanted)."""
+    import torch
+    lib = _load()
+    _check_lens(key_lens)
+    dq, dk, dv, _, _, db = _bwd_outputs(q, None, None, bias, dq, dk, dv, None, None, dbias,
+                                        False, False, want_dbias)
+    args, keep = _bwd_ob_args(q, k, v, bias, window_side, False, key_lens, scale, out, dout,
+                              lse, (dq, dk, dv, db))
+    n = ctypes.c_size_t(0)
+    st = lib.relattn_bwd_grid_bias_workspace_size(*args, ctypes.byref(n))
+    if st != OK:
+        _raise(lib, st)
+    if workspace is None:
+        workspace = torch.empty(max(int(n.value), 1), dtype=torch.uint8, device=q.device)
+    st = lib.relattn_bwd_grid_bias(*args, ctypes.c_void_p(workspace.data_ptr()),
+                                   ctypes.c_size_t(workspace.numel()),
+                                   ctypes.c_void_p(_stream_of(q, stream)))
+    del keep
+    if st != OK:
+        _raise(lib, st)
+    return dq, dk, dv, db
+
+
+_grid_fn = None
+
+
+def attention_grid_bias(q, k, v, bias, window_side, *, key_lens=None, scale=None):
+    """Differentiable ``fwd_grid_bias``: the forward runs ``fwd_grid_bias_lse``,
+    the backward ``bwd_grid_bias``."""
+    global _grid_fn
+    if _grid_fn is None:
+        import torch
+
+        class _AttentionGrid(torch.autograd.Function):
+            @staticmethod
+            def forward(ctx, q, k, v, bias, window_side, opts):
+                out, lse = fwd_grid_bias_lse(q, k, v, bias, window_side, **opts)
+                ctx.save_for_backward(q, k, v, bias, out, lse)
+                ctx.window_side, ctx.opts = window_side, opts
+                return out
+
+            @staticmethod
+            def backward(ctx, dout):
+                q, k, v, bias, out, lse = ctx.saved_tensors
+                dq, dk, dv, db = bwd_grid_bias(q, k, v, bias, ctx.window_side, out=out,
+                                               dout=dout.contiguous(), lse=lse,
+                                               want_dbias=ctx.needs_input_grad[3], **ctx.opts)
+                return dq, dk, dv, db, None, None
+
+        _grid_fn = _AttentionGrid
+    return _grid_fn.apply(q, k, v, bias, window_side, dict(key_lens=key_lens, scale=scale))
 
 
 def edge_label_buffer(B, n, device=None):

@@ -118,6 +118,10 @@ __host__ __device__ inline LayQ make_lay_q(int mode, bool has_wk, bool has_wv, i
     L.tb = take((2 * t5_dist + 1) * 4);
     L.tbi = take((2 * t5_dist + 1) * 4);
     if (want_db) L.gb = take(2 * G::BR * L.gbs * 4);
+  } else if (mode == kRelGrid) {
+    // the head's table, and one bias-gradient row per wave and lane half
+    L.tb = take(nb * 4);
+    if (want_db) L.gb = take(2 * NW * L.gbs * 4);
   }
   L.total = off;
   return L;
@@ -152,7 +156,7 @@ struct LayKV {
 
 template <bool BF16, int D, int NW, int BQ>
 __host__ __device__ inline LayKV make_lay_kv(int mode, bool has_wk, bool has_wv, int nr,
-                                             int t5_dist) {
+                                             int t5_dist, int nb) {
   using G = BGeo<BF16, D, NW, BQ>;
   LayKV L{};
   int off = 0;
@@ -182,6 +186,7 @@ __host__ __device__ inline LayKV make_lay_kv(int mode, bool has_wk, bool has_wv,
     L.tail = take(4 * BQ * 4);
   }
   if (mode == kRelT5) L.tb = take((2 * t5_dist + 1) * 4);
+  if (mode == kRelGrid) L.tb = take(nb * 4);  // the head's 2-D window table
   L.total = off;
   return L;
 }
@@ -272,7 +277,7 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd<D>()))) void bwd_q_kernel(
   using Op = std::conditional_t<BF16, bf16x8, float>;
   constexpr int NT = G::NT, NKB = G::NKB, DVB = G::DVB, NKS = G::NKS, ROWB = G::ROWB;
   constexpr int KSTR = G::KSTR, BR = G::BR;
-  constexpr bool SHAW = MODE == kRelShaw, T5 = MODE == kRelT5;
+  constexpr bool SHAW = MODE == kRelShaw, T5 = MODE == kRelT5, GRID = MODE == kRelGrid;
   constexpr bool ROWS = SHAW && (HAS_WK || HAS_WV);
   static_assert(2 * BR * ROWB <= 4 * G::TILEB, "Q and dZ tiles must fit the ring");
   constexpr int SPAN = G::SPAN, PADL = G::PADL;
@@ -290,7 +295,7 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd<D>()))) void bwd_q_kernel(
   const int wq0 = i0 + wave * 32;
   const int c = p.clip;
   const int r_hi = p.r_lo + p.nr - 1;
-  const bool want_db = T5 && p.ws_pb != nullptr;
+  const bool want_db = (T5 || GRID) && p.ws_pb != nullptr;
   const int dist = p.t5_dist;
 
   const LayQ lay = make_lay_q<BF16, D, NW, BC>(MODE, HAS_WK, HAS_WV, p.nr, dist, p.t5.nb, want_db);
@@ -304,7 +309,11 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd<D>()))) void bwd_q_kernel(
   float* RV = RVp + PADL;
   float* TB = reinterpret_cast<float*>(smem + lay.tb);
   int* TBI = reinterpret_cast<int*>(smem + lay.tbi);
-  float* GB = reinterpret_cast<float*>(smem + lay.gb) + (2 * qrow + hh) * lay.gbs;
+  // T5: a bias-gradient row per query and lane half; 2-D window: per wave and
+  // lane half (within one register, the 32 lanes of a half hold one key and 32
+  // queries, whose 2-D offsets are all different, so their updates never meet)
+  float* GB = reinterpret_cast<float*>(smem + lay.gb) +
+              (GRID ? 2 * wave + hh : 2 * qrow + hh) * lay.gbs;
 
   const T* qg = reinterpret_cast<const T*>(p.q) + b * p.q_sb + h * p.q_sh;
   const T* kg = reinterpret_cast<const T*>(p.k) + b * p.k_sb + h * p.k_sh;
@@ -341,6 +350,15 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd<D>()))) void bwd_q_kernel(
     if (want_db) {
       float* gb0 = reinterpret_cast<float*>(smem + lay.gb);
       for (int x = tid; x < 2 * BR * lay.gbs; x += NT) gb0[x] = 0.f;
+    }
+  }
+  if constexpr (GRID) {
+    // log2(e) * the head's (2M - 1)^2 entries
+    for (int x = tid; x < p.t5.nb; x += NT)
+      TB[x] = kLog2e * p.t5_bias[x * p.tb_sb + h * p.tb_sh];
+    if (want_db) {
+      float* gb0 = reinterpret_cast<float*>(smem + lay.gb);
+      for (int x = tid; x < 2 * NW * lay.gbs; x += NT) gb0[x] = 0.f;
     }
   }
   compiler_fence();
@@ -406,7 +424,9 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd<D>()))) void bwd_q_kernel(
   }
 
   // ---- key loop (tile 0 is in stage 0)
-  const int band = T5 ? dist : c;          // |delta| >= band: an end label
+  // |delta| >= band: an end label (none in the 2-D window: every pair has its
+  // own entry)
+  const int band = T5 ? dist : (GRID ? (1 << 30) : c);
   const int hi_from = max(band, 1 - band);  // delta >= hi_from: the upper end
   const float rl_lo = (SHAW && HAS_WK) ? RG[0] : (T5 ? TB[0] : 0.f);
   const float rl_hi = (SHAW && HAS_WK) ? RG[p.nr - 1] : (T5 ? TB[2 * dist] : 0.f);
@@ -564,6 +584,36 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd<D>()))) void bwd_q_kernel(
               if constexpr (HAS_WV) RV[base + KSTR * e] = pw[8 * g + e];
             }
           }
+        }
+      } else if constexpr (GRID) {
+        // 2-D window: each pair's entry of the head's table, from the (dy, dx)
+        // of key minus query (token t at row t div M, taken in fp32 as
+        // (t + 1/2) / M, exact for t < 2^22, and column t mod M); keys and rows
+        // past n read a clamped entry and weigh 0
+        const int M = p.grid_m;
+        const int qc = min(qi, p.n - 1);
+        const int yq = (int)(((float)qc + 0.5f) * p.grid_inv), xq = qc - yq * M;
+        int ent[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int ko = 16 * (i >> 3) + KSTR * (i & 7);
+          const int j = min(jb + hoff + ko, p.n - 1);
+          const int yj = (int)(((float)j + 0.5f) * p.grid_inv), xj = j - yj * M;
+          ent[i] = (yj - yq + M - 1) * (2 * M - 1) + (xj - xq + M - 1);
+          const bool vis = ko <= lim;
+          // the exponential for every lane, then a select
+          float ex = fast_exp2(fmaf(s[i], p.scale_log2, TB[ent[i]]) - lse2);
+          asm volatile("" : "+v"(ex));
+          const float pv = vis ? ex : 0.f;
+          pw[i] = pv;
+          ds[i] = vis ? pv * (dp[i] - dd) : 0.f;
+        }
+        // each register's 32 lanes of a half hold distinct entries (rows past
+        // n, which share the clamped row's entries, add nothing); the
+        // registers follow one another in program order
+        if (want_db && q_ok) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) GB[ent[i]] += ds[i];
         }
       } else {
         // T5 in the band: the bias of each key's bucket
@@ -771,6 +821,18 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd<D>()))) void bwd_q_kernel(
   }
 
   // ---- partial bias gradient of this tile (sum over its rows, fixed order)
+  if constexpr (GRID) {
+    if (want_db) {
+      block_sync();
+      const float* gb0 = reinterpret_cast<const float*>(smem + lay.gb);
+      const int64_t tile_id = (int64_t)bh * p.n_qtiles + qt;
+      for (int e = tid; e < p.t5.nb; e += NT) {
+        float acc = 0.f;
+        for (int slot = 0; slot < 2 * NW; ++slot) acc += gb0[slot * lay.gbs + e];
+        p.ws_pb[tile_id * p.t5.nb + e] = acc;
+      }
+    }
+  }
   if constexpr (T5) {
     if (want_db) {
       GB[TBI[0]] += g_lo;
@@ -901,7 +963,7 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd<D>()))) void bwd_kv_kernel
   using Op = std::conditional_t<BF16, bf16x8, float>;
   constexpr int NT = G::NT, NQB = G::NKB, DVB = G::DVB, NKS = G::NKS, ROWB = G::ROWB;
   constexpr int KSTR = G::KSTR, BR = G::BR;
-  constexpr bool SHAW = MODE == kRelShaw, T5 = MODE == kRelT5;
+  constexpr bool SHAW = MODE == kRelShaw, T5 = MODE == kRelT5, GRID = MODE == kRelGrid;
   constexpr bool ROWS = SHAW && (HAS_WK || HAS_WV);
 
   const int n_kv = p.B * p.H * p.n_ktiles;
@@ -918,7 +980,7 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd<D>()))) void bwd_kv_kernel
   const int dist = p.t5_dist;
   const int r_hi = p.r_lo + p.nr - 1;
 
-  const LayKV lay = make_lay_kv<BF16, D, NW, BQ>(MODE, HAS_WK, HAS_WV, p.nr, dist);
+  const LayKV lay = make_lay_kv<BF16, D, NW, BQ>(MODE, HAS_WK, HAS_WV, p.nr, dist, p.t5.nb);
   extern __shared__ __align__(16) unsigned char smem[];
   unsigned char RELATTN_LDS* smem_lds = (unsigned char RELATTN_LDS*)smem;
   const uint32_t smem_addr = (uint32_t)(uintptr_t)smem_lds;
@@ -953,6 +1015,9 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd<D>()))) void bwd_kv_kernel
       TB[x] = kLog2e * p.t5_bias[(entry + p.ob_lo) * p.tb_sb + h * p.tb_sh];
     }
   }
+  if constexpr (GRID) {
+    for (int x = tid; x < p.t5.nb; x += NT) TB[x] = kLog2e * p.t5_bias[x * p.tb_sb + h * p.tb_sh];
+  }
   compiler_fence();
   if constexpr (SHAW && HAS_WK)
     dma_tile<ROWB, NW>(smem_lds + lay.tk, reinterpret_cast<const T*>(p.wk) + h * p.wk_sh,
@@ -980,8 +1045,17 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd<D>()))) void bwd_kv_kernel
   for (int mb = 0; mb < DVB; ++mb) frag_col_base<ROWB, D>(32 * mb, lane, trb_lo[mb], trb_hi[mb]);
   const int hoff = BF16 ? 8 * hh : hh;
   const bool k_ok = kj < kv_len;
-  const int band = T5 ? dist : c;          // |delta| >= band: an end label
+  // |delta| >= band: an end label (none in the 2-D window)
+  const int band = T5 ? dist : (GRID ? (1 << 30) : c);
   const int hi_from = max(band, 1 - band);  // delta >= hi_from: the upper end
+  // 2-D window: this lane's key on the M x M grid (row (t + 1/2) / M in fp32,
+  // exact for t < 2^22)
+  [[maybe_unused]] int yk = 0, xk = 0;
+  if constexpr (GRID) {
+    const int kc = min(kj, p.n - 1);
+    yk = (int)(((float)kc + 0.5f) * p.grid_inv);
+    xk = kc - yk * p.grid_m;
+  }
 
   // 16 per-query values of this lane's registers: vector reads of 4
   // consecutive queries (bf16 register order), else one by one
@@ -1137,6 +1211,11 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd<D>()))) void bwd_kv_kernel
             if constexpr (HAS_WV) rv = RVt[lq * lay.lrs + x];
           } else if constexpr (T5) {
             rl = TB[min(max(delta, -dist), dist) + dist];
+          } else if constexpr (GRID) {
+            const int M = p.grid_m;
+            const int qc = min(qq, p.n - 1);
+            const int yq = (int)(((float)qc + 0.5f) * p.grid_inv), xq = qc - yq * M;
+            rl = TB[(yk - yq + M - 1) * (2 * M - 1) + (xk - xq + M - 1)];
           }
           const bool vis = qq < p.n && (!p.causal || delta <= 0);
           // the exponential for every lane, then a select (a conditional
@@ -1254,12 +1333,12 @@ static size_t lds_q_t(int qwaves, RelMode mode, bool has_wk, bool has_wv, int nr
 }
 template <bool BF16, int D>
 static size_t lds_kv_t(int kqblock, RelMode mode, bool has_wk, bool has_wv, int nr,
-                       int t5_dist) {
+                       int t5_dist, int nb) {
   using S = BwdShape<BF16, D>;
   if (kqblock == S::KBQ_WIDE)
-    return (size_t)make_lay_kv<BF16, D, S::KW, S::KBQ_WIDE>(mode, has_wk, has_wv, nr, t5_dist)
+    return (size_t)make_lay_kv<BF16, D, S::KW, S::KBQ_WIDE>(mode, has_wk, has_wv, nr, t5_dist, nb)
         .total;
-  return (size_t)make_lay_kv<BF16, D, S::KW, S::KBQ_NARROW>(mode, has_wk, has_wv, nr, t5_dist)
+  return (size_t)make_lay_kv<BF16, D, S::KW, S::KBQ_NARROW>(mode, has_wk, has_wv, nr, t5_dist, nb)
       .total;
 }
 
@@ -1289,12 +1368,12 @@ static size_t lds_q_d(int d, int qw, RelMode mode, bool wk, bool wv, int nr, int
   }
 }
 template <bool BF16>
-static size_t lds_kv_d(int d, int bq, RelMode mode, bool wk, bool wv, int nr, int dist) {
+static size_t lds_kv_d(int d, int bq, RelMode mode, bool wk, bool wv, int nr, int dist, int nb) {
   switch (d) {
-    case 16: return lds_kv_t<BF16, 16>(bq, mode, wk, wv, nr, dist);
-    case 32: return lds_kv_t<BF16, 32>(bq, mode, wk, wv, nr, dist);
-    case 64: return lds_kv_t<BF16, 64>(bq, mode, wk, wv, nr, dist);
-    default: return lds_kv_t<BF16, 128>(bq, mode, wk, wv, nr, dist);
+    case 16: return lds_kv_t<BF16, 16>(bq, mode, wk, wv, nr, dist, nb);
+    case 32: return lds_kv_t<BF16, 32>(bq, mode, wk, wv, nr, dist, nb);
+    case 64: return lds_kv_t<BF16, 64>(bq, mode, wk, wv, nr, dist, nb);
+    default: return lds_kv_t<BF16, 128>(bq, mode, wk, wv, nr, dist, nb);
   }
 }
 
@@ -1304,14 +1383,14 @@ size_t bwd_lds_q(bool bf16, int d, const BwdCfg& cfg, RelMode mode, bool has_wk,
               : lds_q_d<false>(d, cfg.qwaves, mode, has_wk, has_wv, nr, t5_dist, nb, want_db);
 }
 size_t bwd_lds_kv(bool bf16, int d, const BwdCfg& cfg, RelMode mode, bool has_wk, bool has_wv,
-                  int nr, int t5_dist) {
-  return bf16 ? lds_kv_d<true>(d, cfg.kqblock, mode, has_wk, has_wv, nr, t5_dist)
-              : lds_kv_d<false>(d, cfg.kqblock, mode, has_wk, has_wv, nr, t5_dist);
+                  int nr, int t5_dist, int nb) {
+  return bf16 ? lds_kv_d<true>(d, cfg.kqblock, mode, has_wk, has_wv, nr, t5_dist, nb)
+              : lds_kv_d<false>(d, cfg.kqblock, mode, has_wk, has_wv, nr, t5_dist, nb);
 }
 
 template <int D, int NW, int BC, bool BF16, int MODE, bool WK, bool WV>
 static int launch_q(const BwdParams& p, hipStream_t s) {
-  const bool want_db = MODE == kRelT5 && p.ws_pb != nullptr;
+  const bool want_db = (MODE == kRelT5 || MODE == kRelGrid) && p.ws_pb != nullptr;
   const LayQ lay = make_lay_q<BF16, D, NW, BC>(MODE, WK, WV, p.nr, p.t5_dist, p.t5.nb, want_db);
   auto kern = bwd_q_kernel<D, NW, BC, BF16, MODE, WK, WV>;
   static std::atomic<int> lds_set[64];
@@ -1324,7 +1403,7 @@ static int launch_q(const BwdParams& p, hipStream_t s) {
 
 template <int D, int NW, int BQ, bool BF16, int MODE, bool WK, bool WV>
 static int launch_kv(const BwdParams& p, hipStream_t s) {
-  const LayKV lay = make_lay_kv<BF16, D, NW, BQ>(MODE, WK, WV, p.nr, p.t5_dist);
+  const LayKV lay = make_lay_kv<BF16, D, NW, BQ>(MODE, WK, WV, p.nr, p.t5_dist, p.t5.nb);
   auto kern = bwd_kv_kernel<D, NW, BQ, BF16, MODE, WK, WV>;
   static std::atomic<int> lds_set[64];
   const hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(kern), lay.total, lds_set);
@@ -1352,12 +1431,14 @@ template <bool BF16, int D>
 static int launch_bwd_mode(const BwdCfg& c, RelMode mode, bool wk, bool wv, const BwdParams& p,
                            void* stream) {
   if (mode == kRelT5) return launch_bwd_t<BF16, D, kRelT5, false, false>(c, p, stream);
+  if (mode == kRelGrid) return launch_bwd_t<BF16, D, kRelGrid, false, false>(c, p, stream);
   if (mode == kRelShaw) {
     if (wk && wv) return launch_bwd_t<BF16, D, kRelShaw, true, true>(c, p, stream);
     if (wk) return launch_bwd_t<BF16, D, kRelShaw, true, false>(c, p, stream);
     return launch_bwd_t<BF16, D, kRelShaw, false, true>(c, p, stream);
   }
-  return launch_bwd_t<BF16, D, kRelNone, false, false>(c, p, stream);
+  if (mode == kRelNone) return launch_bwd_t<BF16, D, kRelNone, false, false>(c, p, stream);
+  return (int)hipErrorInvalidValue;
 }
 
 template <bool BF16>

@@ -166,7 +166,7 @@ struct BwdParams {
   void* dv;
   float* dwk;               // [Htk, 2c+1, d] or null
   float* dwv;
-  float* db;                // T5: [NB, H]; offset bias: [Hb, 2W+1]; or null
+  float* db;                // T5: [NB, H]; offset bias: [Hb, 2W+1]; 2-D window: [Hb, (2M-1)^2]; or null
   float* ws_stat;
   float* ws_pk;
   float* ws_pv;
@@ -199,6 +199,8 @@ struct BwdParams {
   float scale_log2;         // s * log2(e)
   int32_t t5_dist;
   int32_t ob, ob_lo, ob_w;  // offset bias: window W of the table
+  int32_t grid_m;           // 2-D window: side M (n = M * M); its table has (2M-1)^2 entries
+  float grid_inv;           // 1 / M
   int32_t n_qtiles;         // query tiles per (b, h) of the dq kernel
   int32_t n_ktiles;         // key tiles per (b, h) of the dk/dv kernel
   T5Buckets t5;
@@ -216,7 +218,7 @@ BwdCfg bwd_cfg(bool bf16, int d, bool narrow_q, bool narrow_kv);
 size_t bwd_lds_q(bool bf16, int d, const BwdCfg& cfg, RelMode mode, bool has_wk, bool has_wv,
                  int nr, int t5_dist, int nb, bool want_db);
 size_t bwd_lds_kv(bool bf16, int d, const BwdCfg& cfg, RelMode mode, bool has_wk, bool has_wv,
-                  int nr, int t5_dist);
+                  int nr, int t5_dist, int nb);
 int launch_bwd(bool bf16, int d, const BwdCfg& cfg, RelMode mode, bool has_wk, bool has_wv,
                const BwdParams& p, void* stream);
 

@@ -348,6 +348,9 @@ void window_grid_kernel(const FwdParams p, int items_per_wg) {
           for (int e = 0; e < 4; ++e) o4[e] = (__bf16)(oacc[mb][4 * g + e] * inv_l);
           *reinterpret_cast<bf16x4*>(orow + 32 * mb + 8 * g + 4 * hh) = o4;
         }
+      // row statistic for the backward pass, natural log
+      if (p.lse && hh == 0)
+        p.lse[b * p.lse_sb + h * p.lse_sh + qrow] = l > 0.f ? (m_use + log2f(l)) * kLn2 : kNegInf;
     }
   }
 }

@@ -497,3 +497,24 @@ def test_edge_tables_vocabulary_too_wide_for_chip(ra):
     lab = ra.edge_label_buffer(B, n)
     assert ra.validate_edge_tables(q, q, q, lab, T(H, 200, 128), T(H, 200, 128)) == ra.OK
     assert ra.validate_edge_tables(q, q, q, lab, T(H, 256, 128), T(H, 256, 128)) == ra.UNSUPPORTED
+
+
+def test_bwd_grid_bias_window_checks(ra):
+    """The grid backward holds the head's (2M-1)^2 entries on chip, and with a
+    bias gradient a sum over them per wave: head size 64 in bf16 reaches M = 40
+    with the gradient and M = 74 without; one more is UNSUPPORTED."""
+    def ws(M, want):
+        q = T(1, 2, M * M, 64)
+        bias = T(2, (2 * M - 1) ** 2, dtype=torch.float32)
+        lse = T(1, 2, M * M, dtype=torch.float32)
+        return ra.bwd_grid_bias_workspace_size(q, q, q, bias, M, out=q, dout=q, lse=lse,
+                                               want_dbias=want)
+    assert ws(40, True) > 0 and ws(74, False) > 0
+    for M, want in ((41, True), (75, False)):
+        with pytest.raises(ra.RelattnError) as e:
+            ws(M, want)
+        assert e.value.status == ra.UNSUPPORTED
+    # the bias gradient's partial sums: one row of (2M-1)^2 per query tile
+    M = 7
+    assert ws(M, True) == _ws_expected(1, 2, M * M, 64, 1, 0, nb=(2 * M - 1) ** 2)
+    assert ws(M, False) == _ws_expected(1, 2, M * M, 64, 1, 0)
