@@ -92,6 +92,7 @@ __all__ = [
     "grid_bias_attention",
     "grid_bias_backward",
     "edge_label_attention",
+    "edge_label_backward",
     "edge_label_relattn",
     "to_f64",
 ]
@@ -804,6 +805,38 @@ def edge_label_attention(q, k, v, labels, bias, scale=None, causal: bool = False
             e = s * (q[b, h] @ k[b, h].T) + row[E[b]]
             z[b, h] = _masked_softmax_rows(e, ok) @ v[b, h]
     return z
+
+
+def edge_label_backward(q, k, v, labels, bias, dz=None, scale=None, causal: bool = False,
+                        key_lens=None):
+    """Gradients (dq, dk, dv, dbias) of sum(dz * z) for edge_label_attention, the
+    scalar bias looked up by each pair's label, by the chain rule: de_ij =
+    alpha_ij (dalpha_ij - sum_j' alpha_ij' dalpha_ij') with dalpha_ij = dz_i . v_j,
+    dq = s de k, dk = s de^T q, dv = alpha^T dz, and dbias[h', l] = the sum of
+    de_ij over the pairs labelled l (over the heads h' covers and the batch)."""
+    q, k, v, dz = to_f64(q), to_f64(k), to_f64(v), to_f64(dz)
+    bias = to_f64(bias)
+    E = np.asarray(labels).astype(np.int64)
+    B, H, n, d = q.shape
+    assert E.shape == (B, n, n)
+    assert E.min(initial=0) >= 0 and E.max(initial=0) < bias.shape[1]
+    s = _default_scale(d, scale)
+    lens = _key_lengths(key_lens, B, n)
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    db = np.zeros_like(bias)
+    for b in range(B):
+        ok = visible(n, causal, lens[b])
+        for h in range(H):
+            hb = 0 if bias.shape[0] == 1 else h
+            e = s * (q[b, h] @ k[b, h].T) + bias[hb][E[b]]
+            alpha = _masked_softmax_rows(e, ok)
+            dalpha = dz[b, h] @ v[b, h].T
+            de = alpha * (dalpha - (alpha * dalpha).sum(axis=1, keepdims=True))
+            dq[b, h] = s * de @ k[b, h]
+            dk[b, h] = s * de.T @ q[b, h]
+            dv[b, h] = alpha.T @ dz[b, h]
+            db[hb] += np.bincount(E[b].ravel(), weights=de.ravel(), minlength=bias.shape[1])
+    return dq, dk, dv, db
 
 
 def edge_label_relattn(q, k, v, labels, aK=None, aV=None, scale=None, causal: bool = False,

@@ -923,6 +923,62 @@ def test_edge_labels_two_tokens_closed_form():
                                    atol=1e-14)
 
 
+
+@pytest.mark.parametrize("causal,lens,shared", [(False, None, False), (True, None, True),
+                                               (False, [6, 3], False)])
+def test_edge_label_backward_matches_finite_differences(causal, lens, shared):
+    B, H, n, d, NL = 2, 2, 6, 4, 5
+    q, k, v, dz = (rnd((B, H, n, d), 350 + i) for i in range(4))
+    bias = rnd((1 if shared else H, NL), 354)
+    E = np.random.default_rng(355).integers(0, NL, size=(B, n, n))
+    grads = oracle.edge_label_backward(q, k, v, E, bias, dz, causal=causal, key_lens=lens)
+    loss = lambda: float((dz * oracle.edge_label_attention(q, k, v, E, bias, causal=causal,
+                                                           key_lens=lens)).sum())
+    rng = np.random.default_rng(356)
+    for x, g in zip((q, k, v, bias), grads):
+        idx = [tuple(int(rng.integers(s)) for s in x.shape) for _ in range(6)]
+        _fd_check(loss, x, g, idx)
+
+
+@pytest.mark.parametrize("bidir", [True, False])
+@pytest.mark.parametrize("causal,lens", [(False, None), (True, None), (False, [9, 30])])
+def test_edge_label_backward_from_t5_buckets_is_t5_backward(bidir, causal, lens):
+    """Labels E[i, j] = beta(j - i) with the T5 table as bias rows give the T5
+    gradients, the bias gradient transposed ([H, NL] against [NL, H]); the
+    buckets are not symmetric in the offset, so transposed labels fail."""
+    B, H, n, d = 2, 3, 30, 8
+    q, k, v, dz = (rnd((B, H, n, d), 360 + i) for i in range(4))
+    t5b = rnd((32, H), 364)
+    E = np.array([[oracle.t5_bucket(j - i, 32, 16, bidir) for j in range(n)] for i in range(n)])
+    got = oracle.edge_label_backward(q, k, v, np.stack([E] * B), t5b.T, dz, scale=1.0,
+                                     causal=causal, key_lens=lens)
+    want = oracle.t5_backward(q, k, v, t5b, 32, 16, bidir, dz, scale=1.0, causal=causal,
+                              key_lens=lens)
+    for a, b_ in zip(got[:3], want[:3]):
+        np.testing.assert_allclose(a, b_, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(got[3], want[3].T, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("shared", [False, True])
+def test_edge_label_backward_from_clipped_offsets_is_offset_bias_backward(shared):
+    """Labels clip(j - i, W) + W: the offset-bias gradients, table included; a
+    table row that no pair reaches gets exactly 0, and each head's bias
+    gradient sums to 0 (every softmax row's dS does)."""
+    B, H, n, d, W = 2, 3, 17, 8, 4
+    q, k, v, dz = (rnd((B, H, n, d), 370 + i) for i in range(4))
+    table = rnd((1 if shared else H, 2 * W + 2), 374)  # one label more than any pair carries
+    E = oracle.relative_labels(n, W) + W
+    got = oracle.edge_label_backward(q, k, v, np.stack([E] * B), table, dz, causal=True,
+                                     key_lens=[n, 11])
+    want = oracle.offset_bias_backward(q, k, v, table[:, :2 * W + 1], W, dz, causal=True,
+                                       key_lens=[n, 11])
+    for a, b_ in zip(got[:3], want[:3]):
+        np.testing.assert_allclose(a, b_, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(got[3][:, :2 * W + 1], want[3], rtol=0, atol=1e-12)
+    assert np.all(got[3][:, 2 * W + 1] == 0.0)
+    np.testing.assert_allclose(got[3].sum(axis=1), 0.0, atol=1e-12)
+
+
 # ---------------------------------------------------------------------------
 # relation-aware attention with per-pair labels and vector tables (Eq. 3 and
 # Eq. 4 over a labeled graph)
