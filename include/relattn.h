@@ -540,6 +540,40 @@ int relattn_bwd_grid_bias_workspace_size(const relattn_tensor* q, const relattn_
                                          const relattn_tensor* dk, const relattn_tensor* dv,
                                          const relattn_tensor* dbias, size_t* bytes);
 
+/* relattn_fwd_edge_bias_lse, relattn_bwd_edge_bias and its workspace size: the
+ * same for the scalar bias by per-pair edge label of relattn_fwd_edge_bias
+ * (summary page of "Self-Attention with Relative Position Representations",
+ * the labeled-graph reading; survey page, "Placement in the taxonomy"),
+ * differentiated by the chain rule:
+ *     dbias[h', l] = sum over the heads h' covers, the batch and the pairs
+ *                    (i, j) labelled l of dS_ij
+ * labels and their layout rules as for relattn_fwd_edge_bias (a label >= NL
+ * counts as NL - 1 here too); lse as for relattn_fwd_lse; dbias is [Hb, NL]
+ * F32 or NULL, and a label no visible pair carries gets 0.  The backward
+ * holds the head's NL entries on chip, and with dbias one sum over them per
+ * query and lane half: tables too long for on-chip memory give UNSUPPORTED
+ * (every NL up to 256 fits, except BF16 at head size 64 with dbias: NL up to
+ * 253). */
+int relattn_fwd_edge_bias_lse(const relattn_tensor* q, const relattn_tensor* k,
+                              const relattn_tensor* v, const relattn_tensor* labels,
+                              const relattn_tensor* bias, float scale, const relattn_mask* mask,
+                              relattn_tensor* out, relattn_tensor* lse, void* stream);
+int relattn_bwd_edge_bias(const relattn_tensor* q, const relattn_tensor* k,
+                          const relattn_tensor* v, const relattn_tensor* labels,
+                          const relattn_tensor* bias, float scale, const relattn_mask* mask,
+                          const relattn_tensor* out, const relattn_tensor* dout,
+                          const relattn_tensor* lse, relattn_tensor* dq, relattn_tensor* dk,
+                          relattn_tensor* dv, relattn_tensor* dbias, void* workspace,
+                          size_t workspace_bytes, void* stream);
+int relattn_bwd_edge_bias_workspace_size(const relattn_tensor* q, const relattn_tensor* k,
+                                         const relattn_tensor* v, const relattn_tensor* labels,
+                                         const relattn_tensor* bias, float scale,
+                                         const relattn_mask* mask, const relattn_tensor* out,
+                                         const relattn_tensor* dout,
+                                         const relattn_tensor* lse, const relattn_tensor* dq,
+                                         const relattn_tensor* dk, const relattn_tensor* dv,
+                                         const relattn_tensor* dbias, size_t* bytes);
+
 /* Static text for a status code. */
 const char* relattn_strerror(int status);
 

@@ -16,7 +16,9 @@ __all__ = ["fwd", "validate", "fwd_offset_bias", "validate_offset_bias", "decode
            "bwd", "bwd_workspace_size", "bwd_offset_bias", "bwd_offset_bias_workspace_size",
            "attention", "attention_offset_bias", "fwd_xl", "validate_xl", "fwd_grid_bias",
            "validate_grid_bias", "fwd_grid_bias_lse", "bwd_grid_bias",
-           "bwd_grid_bias_workspace_size", "attention_grid_bias", "fwd_edge_bias", "validate_edge_bias", "edge_label_buffer",
+           "bwd_grid_bias_workspace_size", "attention_grid_bias", "fwd_edge_bias",
+           "fwd_edge_bias_lse", "bwd_edge_bias", "bwd_edge_bias_workspace_size",
+           "attention_edge_bias", "validate_edge_bias", "edge_label_buffer",
            "fwd_edge_tables", "validate_edge_tables", "decode_offset_bias",
            "decode_offset_bias_workspace_size", "decode_xl", "decode_xl_workspace_size",
            "RelattnError", "library_path",
@@ -136,6 +138,15 @@ def _load():
     lib.relattn_fwd_edge_bias.restype = ctypes.c_int
     lib.relattn_validate_edge_bias.argtypes = edge
     lib.relattn_validate_edge_bias.restype = ctypes.c_int
+    lib.relattn_fwd_edge_bias_lse.argtypes = edge + [P(_Tensor), ctypes.c_void_p]
+    lib.relattn_fwd_edge_bias_lse.restype = ctypes.c_int
+    # q k v labels bias scale mask out dout lse dq dk dv dbias
+    edgew = edge + [P(_Tensor)] * 6
+    lib.relattn_bwd_edge_bias.argtypes = edgew + [ctypes.c_void_p, ctypes.c_size_t,
+                                                  ctypes.c_void_p]
+    lib.relattn_bwd_edge_bias.restype = ctypes.c_int
+    lib.relattn_bwd_edge_bias_workspace_size.argtypes = edgew + [P(ctypes.c_size_t)]
+    lib.relattn_bwd_edge_bias_workspace_size.restype = ctypes.c_int
     edget = [P(_Tensor)] * 6 + [ctypes.c_float, P(_Mask), P(_Tensor)]
     lib.relattn_fwd_edge_tables.argtypes = edget + [ctypes.c_void_p]
     lib.relattn_fwd_edge_tables.restype = ctypes.c_int
@@ -918,6 +929,107 @@ def fwd_edge_bias(q, k, v, labels, bias, *, causal=False, key_lens=None, scale=N
     if st != OK:
         _raise(lib, st)
     return out
+
+
+@_on_stream
+def fwd_edge_bias_lse(q, k, v, labels, bias, *, causal=False, key_lens=None, scale=None,
+                      out=None, lse=None, stream=None):
+    """``fwd_edge_bias`` with the row log-sum-exp; returns (out, lse)."""
+    import torch
+    lib = _load()
+    _check_lens(key_lens)
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    if lse is None:
+        lse = _new_lse(q)
+    args, keep = _edge_args(q, k, v, labels, bias, causal, key_lens, scale, out)
+    lv = _view(lse)
+    st = lib.relattn_fwd_edge_bias_lse(*args, _ref(lv), ctypes.c_void_p(_stream_of(q, stream)))
+    del keep, lv
+    if st != OK:
+        _raise(lib, st)
+    return out, lse
+
+
+def _bwd_edge_args(q, k, v, labels, bias, causal, key_lens, scale, out, dout, lse, grads):
+    args, keep = _edge_args(q, k, v, labels, bias, causal, key_lens, scale, out)
+    extra = [_view(x) for x in (dout, lse) + tuple(grads)]
+    return args + [_ref(x) for x in extra], keep + extra
+
+
+def bwd_edge_bias_workspace_size(q, k, v, labels, bias, *, out, dout, lse, causal=False,
+                                 key_lens=None, scale=None, want_dbias=True):
+    """Workspace bytes ``bwd_edge_bias`` needs (host only)."""
+    lib = _load()
+    db = _bwd_outputs(q, None, None, bias, q, q, q, None, None, None, False, False,
+                      want_dbias)[5]
+    args, keep = _bwd_edge_args(q, k, v, labels, bias, causal, key_lens, scale, out, dout, lse,
+                                (q, q, q, db))
+    n = ctypes.c_size_t(0)
+    st = lib.relattn_bwd_edge_bias_workspace_size(*args, ctypes.byref(n))
+    del keep
+    if st != OK:
+        _raise(lib, st)
+    return int(n.value)
+
+
+@_on_stream
+def bwd_edge_bias(q, k, v, labels, bias, *, out, dout, lse, causal=False, key_lens=None,
+                  scale=None, dq=None, dk=None, dv=None, dbias=None, want_dbias=True,
+                  workspace=None, stream=None):
+    """Gradients for ``fwd_edge_bias_lse``: returns (dq, dk, dv, dbias); dbias
+    float32 like ``bias`` (None when not wanted)."""
+    import torch
+    lib = _load()
+    _check_lens(key_lens)
+    dq, dk, dv, _, _, db = _bwd_outputs(q, None, None, bias, dq, dk, dv, None, None, dbias,
+                                        False, False, want_dbias)
+    args, keep = _bwd_edge_args(q, k, v, labels, bias, causal, key_lens, scale, out, dout, lse,
+                                (dq, dk, dv, db))
+    n = ctypes.c_size_t(0)
+    st = lib.relattn_bwd_edge_bias_workspace_size(*args, ctypes.byref(n))
+    if st != OK:
+        _raise(lib, st)
+    if workspace is None:
+        workspace = torch.empty(max(int(n.value), 1), dtype=torch.uint8, device=q.device)
+    st = lib.relattn_bwd_edge_bias(*args, ctypes.c_void_p(workspace.data_ptr()),
+                                   ctypes.c_size_t(workspace.numel()),
+                                   ctypes.c_void_p(_stream_of(q, stream)))
+    del keep
+    if st != OK:
+        _raise(lib, st)
+    return dq, dk, dv, db
+
+
+_edge_fn = None
+
+
+def attention_edge_bias(q, k, v, labels, bias, *, causal=False, key_lens=None, scale=None):
+    """Differentiable ``fwd_edge_bias`` (gradients to q, k, v and bias; the
+    labels are integers)."""
+    global _edge_fn
+    if _edge_fn is None:
+        import torch
+
+        class _AttentionEdge(torch.autograd.Function):
+            @staticmethod
+            def forward(ctx, q, k, v, labels, bias, opts):
+                out, lse = fwd_edge_bias_lse(q, k, v, labels, bias, **opts)
+                ctx.save_for_backward(q, k, v, labels, bias, out, lse)
+                ctx.opts = opts
+                return out
+
+            @staticmethod
+            def backward(ctx, dout):
+                q, k, v, labels, bias, out, lse = ctx.saved_tensors
+                dq, dk, dv, db = bwd_edge_bias(q, k, v, labels, bias, out=out,
+                                               dout=dout.contiguous(), lse=lse,
+                                               want_dbias=ctx.needs_input_grad[4], **ctx.opts)
+                return dq, dk, dv, None, db, None
+
+        _edge_fn = _AttentionEdge
+    return _edge_fn.apply(q, k, v, labels, bias,
+                          dict(causal=causal, key_lens=key_lens, scale=scale))
 
 
 def validate_edge_bias(q, k, v, labels, bias, *, causal=False, key_lens=None, scale=None,

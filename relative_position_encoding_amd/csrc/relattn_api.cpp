@@ -909,10 +909,10 @@ int make_bwd_plan(const relattn_tensor* q, const relattn_tensor* k, const relatt
                   const relattn_tensor* dwK, const relattn_tensor* dwV,
                   const relattn_tensor* dbias, BwdPlan* plan, bool want_t5_table,
                   const relattn_tensor* ob = nullptr, int32_t ob_window = 0,
-                  int32_t grid_m = 0) {
+                  int32_t grid_m = 0, const relattn_tensor* labels = nullptr) {
   Plan& F = plan->fwd;
   int st = make_plan(q, k, v, wK, wV, t5_bias, t5, clip_k, scale, mask, out, &F, want_t5_table,
-                     ob, ob_window, nullptr, nullptr, grid_m);
+                     ob, ob_window, nullptr, nullptr, grid_m, labels);
   if (st) return st;
   if ((st = check_like_q(dout, "dout", q))) return st;
   if ((st = check_like_q(dq, "dq", q))) return st;
@@ -962,13 +962,20 @@ int make_bwd_plan(const relattn_tensor* q, const relattn_tensor* k, const relatt
   p.t5_dist = f.t5_dist;
   p.ob = f.ob;
   p.ob_lo = f.ob_lo;
-  p.ob_w = ob ? ob_window : 0;
-  const bool grid = F.mode == relattn::kRelGrid;
+  p.ob_n = ob ? 2 * ob_window + 1 : 0;
+  const bool grid = F.mode == relattn::kRelGrid, lab = F.mode == relattn::kRelLabel;
   if (grid) {
     // the table's (2M - 1)^2 entries, summed like an offset table of that many
-    p.ob_w = (f.t5.nb - 1) / 2;
+    p.ob_n = f.t5.nb;
     p.grid_m = f.grid_m;
     p.grid_inv = f.grid_inv;
+  }
+  if (lab) {
+    // the table's NL entries, one per label
+    p.ob_n = f.t5.nb;
+    p.lab = f.lab;
+    p.lab_sb = f.lab_sb;
+    p.lab_sn = f.lab_sn;
   }
   p.t5 = f.t5;
   p.t5_bias = f.t5_bias;
@@ -1017,7 +1024,7 @@ int make_bwd_plan(const relattn_tensor* q, const relattn_tensor* k, const relatt
     p.db_s1 = dbias->stride[1];
   }
   const bool shaw = F.mode == relattn::kRelShaw, t5m = F.mode == relattn::kRelT5;
-  const bool want_db = (t5m || grid) && dbias != nullptr;
+  const bool want_db = (t5m || grid || lab) && dbias != nullptr;
   // the wide workgroup shapes unless their LDS does not fit
   size_t lq = relattn::bwd_lds_q(F.bf16, F.d, cfg, F.mode, F.has_wk, F.has_wv, p.nr, p.t5_dist,
                                  p.t5.nb, want_db);
@@ -1574,6 +1581,60 @@ int relattn_fwd_edge_bias(const relattn_tensor* q, const relattn_tensor* k,
                      bias, 0, nullptr, nullptr, 0, labels);
   if (st) return st;
   return run_fwd(plan, stream);
+}
+
+int relattn_fwd_edge_bias_lse(const relattn_tensor* q, const relattn_tensor* k,
+                              const relattn_tensor* v, const relattn_tensor* labels,
+                              const relattn_tensor* bias, float scale, const relattn_mask* mask,
+                              relattn_tensor* out, relattn_tensor* lse, void* stream) {
+  g_last_error.clear();
+  if (!labels) return fail(RELATTN_ERR_INVALID_ARGUMENT, "labels is NULL");
+  if (!bias) return fail(RELATTN_ERR_INVALID_ARGUMENT, "bias is NULL");
+  Plan plan;
+  int st = make_plan(q, k, v, nullptr, nullptr, nullptr, nullptr, 0, scale, mask, out, &plan, true,
+                     bias, 0, nullptr, nullptr, 0, labels);
+  if (st) return st;
+  if ((st = check_lse(lse, q))) return st;
+  return run_fwd_lse(plan, lse, stream);
+}
+
+int relattn_bwd_edge_bias_workspace_size(const relattn_tensor* q, const relattn_tensor* k,
+                                         const relattn_tensor* v, const relattn_tensor* labels,
+                                         const relattn_tensor* bias, float scale,
+                                         const relattn_mask* mask, const relattn_tensor* out,
+                                         const relattn_tensor* dout, const relattn_tensor* lse,
+                                         const relattn_tensor* dq, const relattn_tensor* dk,
+                                         const relattn_tensor* dv, const relattn_tensor* dbias,
+                                         size_t* bytes) {
+  g_last_error.clear();
+  if (!bytes) return fail(RELATTN_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  if (!labels) return fail(RELATTN_ERR_INVALID_ARGUMENT, "labels is NULL");
+  if (!bias) return fail(RELATTN_ERR_INVALID_ARGUMENT, "bias is NULL");
+  BwdPlan plan;
+  const int st = make_bwd_plan(q, k, v, nullptr, nullptr, nullptr, nullptr, 0, scale, mask, out,
+                               dout, lse, dq, dk, dv, nullptr, nullptr, dbias, &plan, true, bias,
+                               0, 0, labels);
+  if (st) return st;
+  *bytes = plan.fwd.empty ? 0 : plan.ws_bytes;
+  return RELATTN_OK;
+}
+
+int relattn_bwd_edge_bias(const relattn_tensor* q, const relattn_tensor* k,
+                          const relattn_tensor* v, const relattn_tensor* labels,
+                          const relattn_tensor* bias, float scale, const relattn_mask* mask,
+                          const relattn_tensor* out, const relattn_tensor* dout,
+                          const relattn_tensor* lse, relattn_tensor* dq, relattn_tensor* dk,
+                          relattn_tensor* dv, relattn_tensor* dbias, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  if (!labels) return fail(RELATTN_ERR_INVALID_ARGUMENT, "labels is NULL");
+  if (!bias) return fail(RELATTN_ERR_INVALID_ARGUMENT, "bias is NULL");
+  BwdPlan plan;
+  const int st = make_bwd_plan(q, k, v, nullptr, nullptr, nullptr, nullptr, 0, scale, mask, out,
+                               dout, lse, dq, dk, dv, nullptr, nullptr, dbias, &plan, true, bias,
+                               0, 0, labels);
+  if (st) return st;
+  return run_bwd(plan, nullptr, nullptr, dbias != nullptr, workspace, workspace_bytes, stream);
 }
 
 int relattn_validate_edge_tables(const relattn_tensor* q, const relattn_tensor* k,

@@ -122,6 +122,10 @@ __host__ __device__ inline LayQ make_lay_q(int mode, bool has_wk, bool has_wv, i
     // the head's table, and one bias-gradient row per wave and lane half
     L.tb = take(nb * 4);
     if (want_db) L.gb = take(2 * NW * L.gbs * 4);
+  } else if (mode == kRelLabel) {
+    // the head's table, and one bias-gradient row per query and lane half
+    L.tb = take(nb * 4);
+    if (want_db) L.gb = take(2 * G::BR * L.gbs * 4);
   }
   L.total = off;
   return L;
@@ -186,7 +190,7 @@ __host__ __device__ inline LayKV make_lay_kv(int mode, bool has_wk, bool has_wv,
     L.tail = take(4 * BQ * 4);
   }
   if (mode == kRelT5) L.tb = take((2 * t5_dist + 1) * 4);
-  if (mode == kRelGrid) L.tb = take(nb * 4);  // the head's 2-D window table
+  if (mode == kRelGrid || mode == kRelLabel) L.tb = take(nb * 4);  // the head's table
   L.total = off;
   return L;
 }
@@ -278,6 +282,7 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd<D>()))) void bwd_q_kernel(
   constexpr int NT = G::NT, NKB = G::NKB, DVB = G::DVB, NKS = G::NKS, ROWB = G::ROWB;
   constexpr int KSTR = G::KSTR, BR = G::BR;
   constexpr bool SHAW = MODE == kRelShaw, T5 = MODE == kRelT5, GRID = MODE == kRelGrid;
+  constexpr bool LAB = MODE == kRelLabel;
   constexpr bool ROWS = SHAW && (HAS_WK || HAS_WV);
   static_assert(2 * BR * ROWB <= 4 * G::TILEB, "Q and dZ tiles must fit the ring");
   constexpr int SPAN = G::SPAN, PADL = G::PADL;
@@ -295,7 +300,7 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd<D>()))) void bwd_q_kernel(
   const int wq0 = i0 + wave * 32;
   const int c = p.clip;
   const int r_hi = p.r_lo + p.nr - 1;
-  const bool want_db = (T5 || GRID) && p.ws_pb != nullptr;
+  const bool want_db = (T5 || GRID || LAB) && p.ws_pb != nullptr;
   const int dist = p.t5_dist;
 
   const LayQ lay = make_lay_q<BF16, D, NW, BC>(MODE, HAS_WK, HAS_WV, p.nr, dist, p.t5.nb, want_db);
@@ -323,6 +328,7 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd<D>()))) void bwd_q_kernel(
   T* dqg = reinterpret_cast<T*>(p.dq) + b * p.dq_sb + h * p.dq_sh;
   const T* wkh = reinterpret_cast<const T*>(p.wk) + h * p.wk_sh;
   const T* wvh = reinterpret_cast<const T*>(p.wv) + h * p.wv_sh;
+  [[maybe_unused]] const uint8_t* labg = LAB ? p.lab + b * p.lab_sb : nullptr;
 
   // ---- everything the loop needs, requested at once: this lane's q and dz
   // row (B operands, straight from memory), the lse, z for D, the table rows
@@ -352,13 +358,13 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd<D>()))) void bwd_q_kernel(
       for (int x = tid; x < 2 * BR * lay.gbs; x += NT) gb0[x] = 0.f;
     }
   }
-  if constexpr (GRID) {
-    // log2(e) * the head's (2M - 1)^2 entries
+  if constexpr (GRID || LAB) {
+    // log2(e) * the head's (2M - 1)^2 or NL entries
     for (int x = tid; x < p.t5.nb; x += NT)
       TB[x] = kLog2e * p.t5_bias[x * p.tb_sb + h * p.tb_sh];
     if (want_db) {
       float* gb0 = reinterpret_cast<float*>(smem + lay.gb);
-      for (int x = tid; x < 2 * NW * lay.gbs; x += NT) gb0[x] = 0.f;
+      for (int x = tid; x < (GRID ? 2 * NW : 2 * BR) * lay.gbs; x += NT) gb0[x] = 0.f;
     }
   }
   compiler_fence();
@@ -424,9 +430,9 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd<D>()))) void bwd_q_kernel(
   }
 
   // ---- key loop (tile 0 is in stage 0)
-  // |delta| >= band: an end label (none in the 2-D window: every pair has its
-  // own entry)
-  const int band = T5 ? dist : (GRID ? (1 << 30) : c);
+  // |delta| >= band: an end label (none in the 2-D window or by edge label:
+  // every pair has its own entry)
+  const int band = T5 ? dist : ((GRID || LAB) ? (1 << 30) : c);
   const int hi_from = max(band, 1 - band);  // delta >= hi_from: the upper end
   const float rl_lo = (SHAW && HAS_WK) ? RG[0] : (T5 ? TB[0] : 0.f);
   const float rl_hi = (SHAW && HAS_WK) ? RG[p.nr - 1] : (T5 ? TB[2 * dist] : 0.f);
@@ -612,6 +618,47 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd<D>()))) void bwd_q_kernel(
         // n, which share the clamped row's entries, add nothing); the
         // registers follow one another in program order
         if (want_db && q_ok) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) GB[ent[i]] += ds[i];
+        }
+      } else if constexpr (LAB) {
+        // edge labels: the 32 keys of the block lie in two 16-byte chunks of
+        // the query's label row; this lane's keys are bytes hoff + KSTR e of
+        // each.  Chunks past the row's readable length (keys past n, which
+        // weigh 0) re-read its last chunk; rows past n read row n - 1.
+        const uint8_t* lrow = labg + (int64_t)min(qi, p.n - 1) * p.lab_sn;
+        const int cmax = ((p.n + 15) & ~15) - 16;
+        uint4 ch[2];
+#pragma unroll
+        for (int g = 0; g < 2; ++g)
+          ch[g] = *reinterpret_cast<const uint4*>(lrow + min(jb + 16 * g, cmax));
+        int ent[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const uint4 c4 = ch[i >> 3];
+          const int e = i & 7;
+          uint32_t lb;
+          if constexpr (BF16) {
+            // bytes 8 hh + e: word (e >> 2) of the lane's 8-byte half
+            const uint32_t w = (e >> 2) ? (hh ? c4.w : c4.y) : (hh ? c4.z : c4.x);
+            lb = (w >> (8 * (e & 3))) & 0xffu;
+          } else {
+            // bytes hh + 2 e: word e >> 1, byte 2 (e & 1) + hh
+            const uint32_t w = (e >> 1) == 0 ? c4.x : (e >> 1) == 1 ? c4.y
+                             : (e >> 1) == 2 ? c4.z : c4.w;
+            lb = (w >> (8 * (2 * (e & 1) + hh))) & 0xffu;
+          }
+          ent[i] = min((int)lb, p.t5.nb - 1);  // a label past the table reads its last entry
+          const int ko = 16 * (i >> 3) + KSTR * (i & 7);
+          const bool vis = ko <= lim;
+          float ex = fast_exp2(fmaf(s[i], p.scale_log2, TB[ent[i]]) - lse2);
+          asm volatile("" : "+v"(ex));
+          const float pv = vis ? ex : 0.f;
+          pw[i] = pv;
+          ds[i] = vis ? pv * (dp[i] - dd) : 0.f;
+        }
+        // one row per query and lane half: a single writer
+        if (want_db) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) GB[ent[i]] += ds[i];
         }
@@ -821,14 +868,14 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd<D>()))) void bwd_q_kernel(
   }
 
   // ---- partial bias gradient of this tile (sum over its rows, fixed order)
-  if constexpr (GRID) {
+  if constexpr (GRID || LAB) {
     if (want_db) {
       block_sync();
       const float* gb0 = reinterpret_cast<const float*>(smem + lay.gb);
       const int64_t tile_id = (int64_t)bh * p.n_qtiles + qt;
       for (int e = tid; e < p.t5.nb; e += NT) {
         float acc = 0.f;
-        for (int slot = 0; slot < 2 * NW; ++slot) acc += gb0[slot * lay.gbs + e];
+        for (int slot = 0; slot < (GRID ? 2 * NW : 2 * BR); ++slot) acc += gb0[slot * lay.gbs + e];
         p.ws_pb[tile_id * p.t5.nb + e] = acc;
       }
     }
@@ -862,7 +909,7 @@ __host__ __device__ inline int reduce_tables_rows(const BwdParams& p, int which)
 __host__ __device__ inline int reduce_role_count(const BwdParams& p, int nt) {
   int n = reduce_tables_rows(p, 0) + reduce_tables_rows(p, 1);
   if (p.db) {
-    const int64_t total = p.ob ? (int64_t)p.hb * (2 * p.ob_w + 1) : (int64_t)p.t5.nb * p.H;
+    const int64_t total = p.ob ? (int64_t)p.hb * p.ob_n : (int64_t)p.t5.nb * p.H;
     n += (int)((total + nt - 1) / nt);
   }
   return n;
@@ -911,9 +958,9 @@ __device__ void reduce_bias(const BwdParams& p, int blk, int nt) {
   const int nq = p.n_qtiles;
   const int nbt = p.t5.nb;  // entries per head in the partials
   if (p.ob) {
-    // offset-bias table [hb, 2W + 1]: entries outside the loaded window
+    // scalar-bias table [hb, ob_n]: entries outside the loaded window
     // (offsets no pair reaches) get zero
-    const int nw = 2 * p.ob_w + 1;
+    const int nw = p.ob_n;
     if (idx >= (int64_t)p.hb * nw) return;
     const int w = (int)(idx % nw), hq = (int)(idx / nw);
     const int e = w - p.ob_lo;
@@ -964,6 +1011,7 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd<D>()))) void bwd_kv_kernel
   constexpr int NT = G::NT, NQB = G::NKB, DVB = G::DVB, NKS = G::NKS, ROWB = G::ROWB;
   constexpr int KSTR = G::KSTR, BR = G::BR;
   constexpr bool SHAW = MODE == kRelShaw, T5 = MODE == kRelT5, GRID = MODE == kRelGrid;
+  constexpr bool LAB = MODE == kRelLabel;
   constexpr bool ROWS = SHAW && (HAS_WK || HAS_WV);
 
   const int n_kv = p.B * p.H * p.n_ktiles;
@@ -1015,7 +1063,7 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd<D>()))) void bwd_kv_kernel
       TB[x] = kLog2e * p.t5_bias[(entry + p.ob_lo) * p.tb_sb + h * p.tb_sh];
     }
   }
-  if constexpr (GRID) {
+  if constexpr (GRID || LAB) {
     for (int x = tid; x < p.t5.nb; x += NT) TB[x] = kLog2e * p.t5_bias[x * p.tb_sb + h * p.tb_sh];
   }
   compiler_fence();
@@ -1045,8 +1093,8 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd<D>()))) void bwd_kv_kernel
   for (int mb = 0; mb < DVB; ++mb) frag_col_base<ROWB, D>(32 * mb, lane, trb_lo[mb], trb_hi[mb]);
   const int hoff = BF16 ? 8 * hh : hh;
   const bool k_ok = kj < kv_len;
-  // |delta| >= band: an end label (none in the 2-D window)
-  const int band = T5 ? dist : (GRID ? (1 << 30) : c);
+  // |delta| >= band: an end label (none in the 2-D window or by edge label)
+  const int band = T5 ? dist : ((GRID || LAB) ? (1 << 30) : c);
   const int hi_from = max(band, 1 - band);  // delta >= hi_from: the upper end
   // 2-D window: this lane's key on the M x M grid (row (t + 1/2) / M in fp32,
   // exact for t < 2^22)
@@ -1056,6 +1104,10 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd<D>()))) void bwd_kv_kernel
     yk = (int)(((float)kc + 0.5f) * p.grid_inv);
     xk = kc - yk * p.grid_m;
   }
+  // edge labels: this lane's key column of the batch entry's label matrix
+  // (keys past n read column n - 1; they are stored as zeros)
+  [[maybe_unused]] const uint8_t* labk =
+      LAB ? p.lab + b * p.lab_sb + min(kj, p.n - 1) : nullptr;
 
   // 16 per-query values of this lane's registers: vector reads of 4
   // consecutive queries (bf16 register order), else one by one
@@ -1216,6 +1268,9 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd<D>()))) void bwd_kv_kernel
             const int qc = min(qq, p.n - 1);
             const int yq = (int)(((float)qc + 0.5f) * p.grid_inv), xq = qc - yq * M;
             rl = TB[(yk - yq + M - 1) * (2 * M - 1) + (xk - xq + M - 1)];
+          } else if constexpr (LAB) {
+            const int lb = labk[(int64_t)min(qq, p.n - 1) * p.lab_sn];
+            rl = TB[min(lb, p.t5.nb - 1)];
           }
           const bool vis = qq < p.n && (!p.causal || delta <= 0);
           // the exponential for every lane, then a select (a conditional
@@ -1390,7 +1445,8 @@ size_t bwd_lds_kv(bool bf16, int d, const BwdCfg& cfg, RelMode mode, bool has_wk
 
 template <int D, int NW, int BC, bool BF16, int MODE, bool WK, bool WV>
 static int launch_q(const BwdParams& p, hipStream_t s) {
-  const bool want_db = (MODE == kRelT5 || MODE == kRelGrid) && p.ws_pb != nullptr;
+  const bool want_db = (MODE == kRelT5 || MODE == kRelGrid || MODE == kRelLabel) &&
+                       p.ws_pb != nullptr;
   const LayQ lay = make_lay_q<BF16, D, NW, BC>(MODE, WK, WV, p.nr, p.t5_dist, p.t5.nb, want_db);
   auto kern = bwd_q_kernel<D, NW, BC, BF16, MODE, WK, WV>;
   static std::atomic<int> lds_set[64];
@@ -1432,6 +1488,7 @@ static int launch_bwd_mode(const BwdCfg& c, RelMode mode, bool wk, bool wv, cons
                            void* stream) {
   if (mode == kRelT5) return launch_bwd_t<BF16, D, kRelT5, false, false>(c, p, stream);
   if (mode == kRelGrid) return launch_bwd_t<BF16, D, kRelGrid, false, false>(c, p, stream);
+  if (mode == kRelLabel) return launch_bwd_t<BF16, D, kRelLabel, false, false>(c, p, stream);
   if (mode == kRelShaw) {
     if (wk && wv) return launch_bwd_t<BF16, D, kRelShaw, true, true>(c, p, stream);
     if (wk) return launch_bwd_t<BF16, D, kRelShaw, true, false>(c, p, stream);

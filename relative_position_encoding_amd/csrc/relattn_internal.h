@@ -198,9 +198,15 @@ struct BwdParams {
   float scale;              // logit scale s
   float scale_log2;         // s * log2(e)
   int32_t t5_dist;
-  int32_t ob, ob_lo, ob_w;  // offset bias: window W of the table
+  int32_t ob, ob_lo;        // scalar bias from a [hb, ob_n] table (ob = 1)
+  int32_t ob_n;             // its entries per row: 2W + 1 by clipped offset, (2M-1)^2 by
+                            // 2-D offset, NL by edge label
   int32_t grid_m;           // 2-D window: side M (n = M * M); its table has (2M-1)^2 entries
   float grid_inv;           // 1 / M
+  // edge labels: lab[b * lab_sb + i * lab_sn + j] labels the pair (query i,
+  // key j); rows are readable in whole 16-byte chunks up to n rounded up to 16
+  const uint8_t* lab;
+  int64_t lab_sb, lab_sn;
   int32_t n_qtiles;         // query tiles per (b, h) of the dq kernel
   int32_t n_ktiles;         // key tiles per (b, h) of the dk/dv kernel
   T5Buckets t5;

@@ -227,3 +227,109 @@ def test_edge_modes_rows_without_visible_keys_output_zeros(ra):
         assert torch.count_nonzero(out[0]) == 0, name
         err = float(np.max(np.abs(out[1:].double().cpu().numpy() - wants[name])))
         assert err <= TOL[torch.bfloat16], (name, err)
+
+
+# ---------------------------------------------------------------------------
+# backward: relattn_fwd_edge_bias_lse + relattn_bwd_edge_bias against the
+# oracle's chain-rule gradients (oracle.edge_label_backward).  Bar as for the
+# other backward passes: max|gpu - oracle| <= BTOL * max(max|oracle|, 1), with
+# BTOL = 1e-4 (fp32) and 3e-2 (bf16: operands of the weight and dS products
+# rounded to bf16, 2^-9 relative each, and dq, dk, dv rounded to bf16).
+# ---------------------------------------------------------------------------
+
+BTOL = {torch.float32: 1e-4, torch.bfloat16: 3e-2}
+
+
+def bcheck(got, want, dtype, names=("dq", "dk", "dv", "dbias")):
+    for name, g, w in zip(names, got, want):
+        w = np.asarray(w, np.float64)
+        e = float(np.max(np.abs(g.double().cpu().numpy() - w))) / max(float(np.abs(w).max()), 1.0)
+        assert e <= BTOL[dtype], f"{name}: normalised error {e:.3g} > {BTOL[dtype]}"
+
+
+def edge_grads(ra, q, k, v, E, bias, dz, causal=False, lens=None, want_dbias=True):
+    lens_d = None if lens is None else torch.tensor(lens, dtype=torch.int32, device=DEV)
+    qd, kd, vd, bd, dzd = (x.to(DEV) for x in (q, k, v, bias, dz))
+    lab = labels_of(ra, E)
+    out, lse = ra.fwd_edge_bias_lse(qd, kd, vd, lab, bd, causal=causal, key_lens=lens_d)
+    g = ra.bwd_edge_bias(qd, kd, vd, lab, bd, out=out, dout=dzd, lse=lse, causal=causal,
+                         key_lens=lens_d, want_dbias=want_dbias)
+    torch.cuda.synchronize()
+    return out, lse, g
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=str)
+@pytest.mark.parametrize("n", [1, 37, 100, 200])
+@pytest.mark.parametrize("d", [32, 64])
+@pytest.mark.parametrize("mask", range(len(MASKS)))
+def test_edge_bias_backward_parity(ra, dtype, n, d, mask):
+    """dq, dk, dv and the table gradient under every mask, with ragged tails;
+    some labels lie past the table (read as its last entry, as the oracle is
+    given them)."""
+    causal, lens_kind = MASKS[mask]
+    B, H, NL = 3, 2, 24
+    q, k, v, dz = (gen((B, H, n, d), dtype, 2900 + n + d + i) for i in range(4))
+    bias = gen((H, NL), torch.float32, 2904, std=2.0)
+    E = np.random.default_rng(2905 + n).integers(0, NL + 6, (B, n, n))
+    lens = [n, max(1, n // 2), max(1, n - 5)] if lens_kind else None
+    _, _, got = edge_grads(ra, q, k, v, E, bias, dz, causal, lens)
+    want = oracle.edge_label_backward(q, k, v, np.minimum(E, NL - 1), bias, dz, causal=causal,
+                                      key_lens=lens)
+    bcheck(got, want, dtype)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=str)
+@pytest.mark.parametrize("d,NL", [(16, 1), (16, 7), (128, 100), (64, 253), (32, 256)])
+def test_edge_bias_backward_shapes(ra, dtype, d, NL):
+    """Head sizes 16 and 128, one label, and the longest tables that fit, with a
+    shared bias row (its gradient summed over the heads) and an empty
+    sequence (key length 0: every gradient through it is 0)."""
+    B, H, n = 3, 3, 70
+    q, k, v, dz = (gen((B, H, n, d), dtype, 3000 + d + NL + i) for i in range(4))
+    bias = gen((1, NL), torch.float32, 3004)
+    E = np.random.default_rng(3005 + NL).integers(0, NL, (B, n, n))
+    lens = [n, 0, 33]
+    _, _, got = edge_grads(ra, q, k, v, E, bias, dz, True, lens)
+    want = oracle.edge_label_backward(q, k, v, E, bias, dz, causal=True, key_lens=lens)
+    bcheck(got, want, dtype)
+    for g in got[:3]:
+        assert torch.count_nonzero(g[1]).item() == 0
+
+
+def test_edge_bias_backward_without_bias_gradient(ra):
+    B, H, n, d, NL = 2, 2, 90, 64, 16
+    q, k, v, dz = (gen((B, H, n, d), torch.bfloat16, 3100 + i) for i in range(4))
+    bias = gen((H, NL), torch.float32, 3104)
+    E = np.random.default_rng(3105).integers(0, NL, (B, n, n))
+    _, _, got = edge_grads(ra, q, k, v, E, bias, dz, want_dbias=False)
+    assert got[3] is None
+    want = oracle.edge_label_backward(q, k, v, E, bias, dz)
+    bcheck(got[:3], want[:3], torch.bfloat16, names=("dq", "dk", "dv"))
+
+
+def test_edge_bias_autograd(ra):
+    """torch.autograd through attention_edge_bias matches the oracle (fp32)."""
+    B, H, n, d, NL = 2, 2, 40, 32, 9
+    q, k, v, dz = (gen((B, H, n, d), torch.float32, 3200 + i) for i in range(4))
+    bias = gen((H, NL), torch.float32, 3204)
+    E = np.random.default_rng(3205).integers(0, NL, (B, n, n))
+    leaves = [x.to(DEV).requires_grad_(True) for x in (q, k, v, bias)]
+    out = ra.attention_edge_bias(leaves[0], leaves[1], leaves[2], labels_of(ra, E), leaves[3],
+                                 causal=True)
+    out.backward(dz.to(DEV))
+    want = oracle.edge_label_backward(q, k, v, E, bias, dz, causal=True)
+    bcheck([x.grad for x in leaves], want, torch.float32)
+
+
+def test_edge_bias_backward_full_size(ra):
+    """The edge-label workload at full size in one call (B16 H16 n256 d64,
+    64 labels uniform per pair, bf16): every gradient element by element
+    against the oracle over the whole batch."""
+    x = workloads.make_edge_inputs("edge")
+    dtype = workloads.EDGE_WORKLOADS["edge"].dtype
+    q, k, v = (x[t].to(dtype) for t in ("q", "k", "v"))
+    bias, E = x["bias"], x["labels"].numpy()
+    dz = gen(q.shape, dtype, 3300)
+    _, _, got = edge_grads(ra, q, k, v, E, bias, dz)
+    want = oracle.edge_label_backward(q, k, v, E, bias, dz)
+    bcheck(got, want, dtype)
