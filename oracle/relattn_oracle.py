@@ -93,6 +93,7 @@ __all__ = [
     "grid_bias_backward",
     "edge_label_attention",
     "edge_label_backward",
+    "xl_backward",
     "edge_label_relattn",
     "to_f64",
 ]
@@ -673,6 +674,55 @@ def xl_attention(q, k, v, R, u, vb, window: int, scale=None, causal: bool = Fals
             e = s * (term_a + term_b + term_c + term_d)
             z[b, h] = _masked_softmax_rows(e, ok) @ v[b, h]
     return z
+
+
+def xl_backward(q, k, v, R, u, vb, window: int, dz=None, scale=None, causal: bool = False,
+                key_lens=None):
+    """Gradients (dq, dk, dv, dR, du, dvb) of sum(dz * z) for xl_attention, by
+    the chain rule through the four-term score written as
+    e_ij = s [(q_i + u).k_j + (q_i + v).R_{i-j}]:
+    de_ij = alpha_ij (dalpha_ij - sum_j' alpha_ij' dalpha_ij') with dalpha_ij =
+    dz_i . v_j, and
+        dq_i = s sum_j de_ij (k_j + R_{i-j})      dk_j = s sum_i de_ij (q_i + u)
+        dv_j = sum_i alpha_ij dz_i
+        dR_r = s sum over pairs with row r of de_ij (q_i + v)
+        du = s sum_ij de_ij k_j                   dv_bias = s sum_ij de_ij R_{i-j}
+    Tables shared by the heads (leading dimension 1) get the sum over heads."""
+    q, k, v, dz = to_f64(q), to_f64(k), to_f64(v), to_f64(dz)
+    R, u, vb = to_f64(R), to_f64(u), to_f64(vb)
+    B, H, n, d = q.shape
+    s = _default_scale(d, scale)
+    lens = _key_lengths(key_lens, B, n)
+    i = np.arange(n)[:, None]
+    j = np.arange(n)[None, :]
+    dist = np.clip(i - j, -window, window) + window
+    nrow = 2 * window + 1
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    dR, du, dvb = np.zeros_like(R), np.zeros_like(u), np.zeros_like(vb)
+    for b in range(B):
+        ok = visible(n, causal, lens[b])
+        for h in range(H):
+            hr = 0 if R.shape[0] == 1 else h
+            hu = 0 if u.shape[0] == 1 else h
+            hv = 0 if vb.shape[0] == 1 else h
+            Rh = R[hr][dist]                                    # [n, n, d]
+            a = q[b, h] + u[hu]                                 # content query
+            c = q[b, h] + vb[hv]                                # position query
+            e = s * (a @ k[b, h].T + np.einsum("id,ijd->ij", c, Rh))
+            alpha = _masked_softmax_rows(e, ok)
+            dalpha = dz[b, h] @ v[b, h].T
+            de = alpha * (dalpha - (alpha * dalpha).sum(axis=1, keepdims=True))
+            dq[b, h] = s * (de @ k[b, h] + np.einsum("ij,ijd->id", de, Rh))
+            dk[b, h] = s * de.T @ a
+            dv[b, h] = alpha.T @ dz[b, h]
+            # per query, the sum of de over the pairs of each row of R
+            G = np.zeros((n, nrow))
+            for t in range(n):
+                G[t] = np.bincount(dist[t], weights=de[t], minlength=nrow)
+            dR[hr] += s * G.T @ c
+            du[hu] += s * de.sum(axis=0) @ k[b, h]
+            dvb[hv] += s * G.sum(axis=0) @ R[hr]
+    return dq, dk, dv, dR, du, dvb
 
 
 def xl_decode(q, k, v, R, u, vb, window: int, scale=None, cache_lens=None):

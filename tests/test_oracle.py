@@ -745,6 +745,58 @@ def test_xl_global_position_bias_is_an_offset_bias():
     np.testing.assert_allclose(got, want, rtol=0, atol=1e-12)
 
 
+
+@pytest.mark.parametrize("causal,lens,window,shared", [(False, None, 2, False),
+                                                       (True, None, 9, True),
+                                                       (False, [6, 4], 3, False)])
+def test_xl_backward_matches_finite_differences(causal, lens, window, shared):
+    B, H, n, d = 2, 2, 6, 4
+    q, k, v, dz = (rnd((B, H, n, d), 380 + i) for i in range(4))
+    Hs = 1 if shared else H
+    R, u, vb = rnd((Hs, 2 * window + 1, d), 384, 0.5), rnd((Hs, d), 385), rnd((Hs, d), 386)
+    grads = oracle.xl_backward(q, k, v, R, u, vb, window, dz, causal=causal, key_lens=lens)
+    loss = lambda: float((dz * oracle.xl_attention(q, k, v, R, u, vb, window, causal=causal,
+                                                   key_lens=lens)).sum())
+    rng = np.random.default_rng(387)
+    for x, g in zip((q, k, v, R, u, vb), grads):
+        idx = [tuple(int(rng.integers(s)) for s in x.shape) for _ in range(6)]
+        _fd_check(loss, x, g, idx)
+
+
+@pytest.mark.parametrize("causal,window,shared", [(False, 20, False), (True, 4, True)])
+def test_xl_backward_without_global_biases_is_shaw_backward(causal, window, shared):
+    """u = v = 0: dq, dk, dv are the Shaw key-table gradients with the table
+    read by i - j (w^K[r] = R[2W - r]), and dR is that table's gradient
+    reversed."""
+    B, H, n, d = 2, 2, 11, 8
+    q, k, v, dz = (rnd((B, H, n, d), 390 + i) for i in range(4))
+    R = rnd((1 if shared else H, 2 * window + 1, d), 394)
+    zero = np.zeros((1, d))
+    got = oracle.xl_backward(q, k, v, R, zero, zero, window, dz, causal=causal, key_lens=[n, 7])
+    want = oracle.relattn_backward(q, k, v, R[:, ::-1].copy(), None, window, dz, causal=causal,
+                                   key_lens=[n, 7])
+    for a, b_ in zip(got[:3], want[:3]):
+        np.testing.assert_allclose(a, b_, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(got[3], want[3][:, ::-1], rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("shared", [False, True])
+def test_xl_backward_global_bias_gradients_sum_to_the_query_gradients(shared):
+    """q enters every logit through q + u and q + v, so du + dv_bias equals the
+    query gradients summed over the batch and the positions (and over the heads
+    for one shared pair), and the key gradients of each row sum to zero
+    (softmax rows)."""
+    B, H, n, d, W = 2, 3, 9, 8, 3
+    q, k, v, dz = (rnd((B, H, n, d), 400 + i) for i in range(4))
+    Hs = 1 if shared else H
+    R, u, vb = rnd((Hs, 2 * W + 1, d), 404), rnd((Hs, d), 405), rnd((Hs, d), 406)
+    dq, dk, dv, dR, du, dvb = oracle.xl_backward(q, k, v, R, u, vb, W, dz, causal=True,
+                                                 key_lens=[n, 5])
+    per_head = dq.sum(axis=(0, 2))
+    want = per_head.sum(axis=0, keepdims=True) if shared else per_head
+    np.testing.assert_allclose(du + dvb, want, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dk.sum(axis=2), 0.0, atol=1e-12)
+
 # ---------------------------------------------------------------------------
 # Swin 2-D window bias
 # ---------------------------------------------------------------------------
