@@ -574,6 +574,45 @@ int relattn_bwd_edge_bias_workspace_size(const relattn_tensor* q, const relattn_
                                          const relattn_tensor* dk, const relattn_tensor* dv,
                                          const relattn_tensor* dbias, size_t* bytes);
 
+/* relattn_fwd_xl_lse, relattn_bwd_xl and its workspace size: the same for the
+ * Transformer-XL logits of relattn_fwd_xl ("Relative Position Encoding in
+ * Transformer-XL", the four-term score), differentiated by the chain rule with
+ * the score written as s [(q_i + u).k_j + (q_i + v).R_{i-j}]:
+ *     dq_i = s sum_j dS_ij (k_j + R_{i-j})     dk_j = s sum_i dS_ij (q_i + u)
+ *     dR_r = s sum over pairs at row r of dS_ij (q_i + v)
+ *     du = s sum_ij dS_ij k_j                  dv = s sum_ij dS_ij R_{i-j}
+ * (dv here is the gradient of the position bias v; the value gradient is the
+ * argument dv of relattn_bwd's list, named dv as there).
+ *   q .. mask      : exactly the arguments of the forward call.
+ *   dR             : [Hr, 2*window + 1, d] F32 (innermost contiguous), or NULL.
+ *   du, dvb        : [Hu, d] and [Hv, d] F32 (innermost contiguous), or NULL.
+ * A shared R, u or v (leading dimension 1) gets the sum over the heads; rows
+ * of distances no pair reaches are set to zero.  The backward holds one row
+ * of relative logits per query over the reachable distances on chip:
+ * distances past what fits give UNSUPPORTED (bf16 at d = 64: every distance
+ * of a 512-token causal segment fits, with one wave per query tile).
+ * Errors, workspace and reproducibility as for relattn_bwd. */
+int relattn_fwd_xl_lse(const relattn_tensor* q, const relattn_tensor* k, const relattn_tensor* v,
+                       const relattn_tensor* R, const relattn_tensor* u, const relattn_tensor* vb,
+                       int32_t window, float scale, const relattn_mask* mask, relattn_tensor* out,
+                       relattn_tensor* lse, void* stream);
+int relattn_bwd_xl(const relattn_tensor* q, const relattn_tensor* k, const relattn_tensor* v,
+                   const relattn_tensor* R, const relattn_tensor* u, const relattn_tensor* vb,
+                   int32_t window, float scale, const relattn_mask* mask,
+                   const relattn_tensor* out, const relattn_tensor* dout,
+                   const relattn_tensor* lse, relattn_tensor* dq, relattn_tensor* dk,
+                   relattn_tensor* dv, relattn_tensor* dR, relattn_tensor* du,
+                   relattn_tensor* dvb, void* workspace, size_t workspace_bytes, void* stream);
+int relattn_bwd_xl_workspace_size(const relattn_tensor* q, const relattn_tensor* k,
+                                  const relattn_tensor* v, const relattn_tensor* R,
+                                  const relattn_tensor* u, const relattn_tensor* vb,
+                                  int32_t window, float scale, const relattn_mask* mask,
+                                  const relattn_tensor* out, const relattn_tensor* dout,
+                                  const relattn_tensor* lse, const relattn_tensor* dq,
+                                  const relattn_tensor* dk, const relattn_tensor* dv,
+                                  const relattn_tensor* dR, const relattn_tensor* du,
+                                  const relattn_tensor* dvb, size_t* bytes);
+
 /* Static text for a status code. */
 const char* relattn_strerror(int status);
 

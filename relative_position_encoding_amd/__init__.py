@@ -18,7 +18,7 @@ __all__ = ["fwd", "validate", "fwd_offset_bias", "validate_offset_bias", "decode
            "validate_grid_bias", "fwd_grid_bias_lse", "bwd_grid_bias",
            "bwd_grid_bias_workspace_size", "attention_grid_bias", "fwd_edge_bias",
            "fwd_edge_bias_lse", "bwd_edge_bias", "bwd_edge_bias_workspace_size",
-           "attention_edge_bias", "validate_edge_bias", "edge_label_buffer",
+           "attention_edge_bias", "fwd_xl_lse", "bwd_xl", "bwd_xl_workspace_size", "attention_xl", "validate_edge_bias", "edge_label_buffer",
            "fwd_edge_tables", "validate_edge_tables", "decode_offset_bias",
            "decode_offset_bias_workspace_size", "decode_xl", "decode_xl_workspace_size",
            "RelattnError", "library_path",
@@ -122,6 +122,14 @@ def _load():
     lib.relattn_fwd_xl.restype = ctypes.c_int
     lib.relattn_validate_xl.argtypes = xl
     lib.relattn_validate_xl.restype = ctypes.c_int
+    lib.relattn_fwd_xl_lse.argtypes = xl + [P(_Tensor), ctypes.c_void_p]
+    lib.relattn_fwd_xl_lse.restype = ctypes.c_int
+    # q k v R u v window scale mask out dout lse dq dk dv dR du dv_bias
+    xlw = xl + [P(_Tensor)] * 8
+    lib.relattn_bwd_xl.argtypes = xlw + [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    lib.relattn_bwd_xl.restype = ctypes.c_int
+    lib.relattn_bwd_xl_workspace_size.argtypes = xlw + [P(ctypes.c_size_t)]
+    lib.relattn_bwd_xl_workspace_size.restype = ctypes.c_int
     lib.relattn_fwd_grid_bias.argtypes = ob + [ctypes.c_void_p]
     lib.relattn_fwd_grid_bias.restype = ctypes.c_int
     lib.relattn_validate_grid_bias.argtypes = ob
@@ -750,6 +758,118 @@ def validate_xl(q, k, v, R, u, vb, window, *, causal=False, key_lens=None, scale
     st = lib.relattn_validate_xl(*args)
     del keep
     return st
+
+
+@_on_stream
+def fwd_xl_lse(q, k, v, R, u, vb, window, *, causal=False, key_lens=None, scale=None,
+               out=None, lse=None, stream=None):
+    """``fwd_xl`` with the row log-sum-exp; returns (out, lse)."""
+    import torch
+    lib = _load()
+    _check_lens(key_lens)
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    if lse is None:
+        lse = _new_lse(q)
+    args, keep = _xl_args(q, k, v, R, u, vb, window, causal, key_lens, scale, out)
+    lv = _view(lse)
+    st = lib.relattn_fwd_xl_lse(*args, _ref(lv), ctypes.c_void_p(_stream_of(q, stream)))
+    del keep, lv
+    if st != OK:
+        _raise(lib, st)
+    return out, lse
+
+
+def _xl_grads(q, R, u, vb, dq, dk, dv, dR, du, dvb, want_dR, want_du, want_dvb):
+    import torch
+
+    def f32(x, ref, want):
+        if x is not None or not want:
+            return x
+        return torch.empty(ref.shape, dtype=torch.float32, device=q.device)
+    base = _bwd_outputs(q, None, None, None, dq, dk, dv, None, None, None, False, False, False)
+    return base[:3] + (f32(dR, R, want_dR), f32(du, u, want_du), f32(dvb, vb, want_dvb))
+
+
+def _bwd_xl_args(q, k, v, R, u, vb, window, causal, key_lens, scale, out, dout, lse, grads):
+    args, keep = _xl_args(q, k, v, R, u, vb, window, causal, key_lens, scale, out)
+    extra = [_view(x) for x in (dout, lse) + tuple(grads)]
+    return args + [_ref(x) for x in extra], keep + extra
+
+
+def bwd_xl_workspace_size(q, k, v, R, u, vb, window, *, out, dout, lse, causal=False,
+                          key_lens=None, scale=None, want_dR=True, want_du=True, want_dvb=True):
+    """Workspace bytes ``bwd_xl`` needs (host only)."""
+    lib = _load()
+    g = _xl_grads(q, R, u, vb, q, q, q, None, None, None, want_dR, want_du, want_dvb)
+    args, keep = _bwd_xl_args(q, k, v, R, u, vb, window, causal, key_lens, scale, out, dout,
+                              lse, g)
+    n = ctypes.c_size_t(0)
+    st = lib.relattn_bwd_xl_workspace_size(*args, ctypes.byref(n))
+    del keep
+    if st != OK:
+        _raise(lib, st)
+    return int(n.value)
+
+
+@_on_stream
+def bwd_xl(q, k, v, R, u, vb, window, *, out, dout, lse, causal=False, key_lens=None,
+           scale=None, dq=None, dk=None, dv=None, dR=None, du=None, dvb=None, want_dR=True,
+           want_du=True, want_dvb=True, workspace=None, stream=None):
+    """Gradients for ``fwd_xl_lse``: returns (dq, dk, dv, dR, du, dvb), the
+    last three float32 like R, u and vb (None when not wanted)."""
+    import torch
+    lib = _load()
+    _check_lens(key_lens)
+    g = _xl_grads(q, R, u, vb, dq, dk, dv, dR, du, dvb, want_dR, want_du, want_dvb)
+    args, keep = _bwd_xl_args(q, k, v, R, u, vb, window, causal, key_lens, scale, out, dout,
+                              lse, g)
+    n = ctypes.c_size_t(0)
+    st = lib.relattn_bwd_xl_workspace_size(*args, ctypes.byref(n))
+    if st != OK:
+        _raise(lib, st)
+    if workspace is None:
+        workspace = torch.empty(max(int(n.value), 1), dtype=torch.uint8, device=q.device)
+    st = lib.relattn_bwd_xl(*args, ctypes.c_void_p(workspace.data_ptr()),
+                            ctypes.c_size_t(workspace.numel()),
+                            ctypes.c_void_p(_stream_of(q, stream)))
+    del keep
+    if st != OK:
+        _raise(lib, st)
+    return g
+
+
+_xl_fn = None
+
+
+def attention_xl(q, k, v, R, u, vb, window, *, causal=False, key_lens=None, scale=None):
+    """Differentiable ``fwd_xl``: gradients to q, k, v, R, u and vb."""
+    global _xl_fn
+    if _xl_fn is None:
+        import torch
+
+        class _AttentionXL(torch.autograd.Function):
+            @staticmethod
+            def forward(ctx, q, k, v, R, u, vb, window, opts):
+                out, lse = fwd_xl_lse(q, k, v, R, u, vb, window, **opts)
+                ctx.save_for_backward(q, k, v, R, u, vb, out, lse)
+                ctx.window, ctx.opts = window, opts
+                return out
+
+            @staticmethod
+            def backward(ctx, dout):
+                q, k, v, R, u, vb, out, lse = ctx.saved_tensors
+                need = ctx.needs_input_grad
+                dq, dk, dv, dR, du, dvb = bwd_xl(q, k, v, R, u, vb, ctx.window, out=out,
+                                                 dout=dout.contiguous(), lse=lse,
+                                                 want_dR=need[3], want_du=need[4],
+                                                 want_dvb=need[5], **ctx.opts)
+                cast = lambda x, ref: None if x is None else x.to(ref.dtype)
+                return dq, dk, dv, cast(dR, R), cast(du, u), cast(dvb, vb), None, None
+
+        _xl_fn = _AttentionXL
+    return _xl_fn.apply(q, k, v, R, u, vb, window,
+                        dict(causal=causal, key_lens=key_lens, scale=scale))
 
 
 # ---------------------------------------------------------------------------

@@ -897,7 +897,7 @@ struct BwdPlan {
   relattn::BwdCfg cfg{};
   relattn::BwdParams p{};
   size_t ws_bytes = 0;
-  size_t off_stat = 0, off_pk = 0, off_pv = 0, off_pb = 0;
+  size_t off_stat = 0, off_pk = 0, off_pv = 0, off_pb = 0, off_pu = 0;
 };
 
 int make_bwd_plan(const relattn_tensor* q, const relattn_tensor* k, const relattn_tensor* v,
@@ -909,11 +909,37 @@ int make_bwd_plan(const relattn_tensor* q, const relattn_tensor* k, const relatt
                   const relattn_tensor* dwK, const relattn_tensor* dwV,
                   const relattn_tensor* dbias, BwdPlan* plan, bool want_t5_table,
                   const relattn_tensor* ob = nullptr, int32_t ob_window = 0,
-                  int32_t grid_m = 0, const relattn_tensor* labels = nullptr) {
+                  int32_t grid_m = 0, const relattn_tensor* labels = nullptr,
+                  const relattn_tensor* xl_u = nullptr, const relattn_tensor* xl_v = nullptr,
+                  const relattn_tensor* du = nullptr, const relattn_tensor* dvb = nullptr) {
   Plan& F = plan->fwd;
   int st = make_plan(q, k, v, wK, wV, t5_bias, t5, clip_k, scale, mask, out, &F, want_t5_table,
-                     ob, ob_window, nullptr, nullptr, grid_m, labels);
+                     ob, ob_window, xl_u, xl_v, grid_m, labels);
   if (st) return st;
+  // Transformer-XL: the backward runs the key-table path with R as the table
+  const bool xl = xl_u != nullptr;
+  if (xl) {
+    F.mode = relattn::kRelXL;
+    F.has_wk = true;
+    F.has_wv = false;
+  }
+  {
+    const int64_t d0 = q->shape[3];
+    if ((du || dvb) && !xl)
+      return fail(RELATTN_ERR_INVALID_ARGUMENT, "du / dv given without Transformer-XL biases");
+    if (du) {
+      const int64_t shp[2] = {xl_u->shape[0], d0};
+      if ((st = check_f32(du, "du", 2, shp))) return st;
+      if (numel(du) > 0 && du->stride[1] != 1)
+        return fail(RELATTN_ERR_UNSUPPORTED, "du: innermost dimension must be contiguous");
+    }
+    if (dvb) {
+      const int64_t shp[2] = {xl_v->shape[0], d0};
+      if ((st = check_f32(dvb, "dv", 2, shp))) return st;
+      if (numel(dvb) > 0 && dvb->stride[1] != 1)
+        return fail(RELATTN_ERR_UNSUPPORTED, "dv: innermost dimension must be contiguous");
+    }
+  }
   if ((st = check_like_q(dout, "dout", q))) return st;
   if ((st = check_like_q(dq, "dq", q))) return st;
   if ((st = check_like_q(dk, "dk", q))) return st;
@@ -1023,7 +1049,41 @@ int make_bwd_plan(const relattn_tensor* q, const relattn_tensor* k, const relatt
     p.db_s0 = dbias->stride[0];
     p.db_s1 = dbias->stride[1];
   }
-  const bool shaw = F.mode == relattn::kRelShaw, t5m = F.mode == relattn::kRelT5;
+  if (xl) {
+    // the table row of label r (offset j - i = r - c) is R's row of distance
+    // i - j, 2c - r: start at R's last row and step backwards (the gradient
+    // table the same way)
+    const int64_t c = clip_k;
+    const int64_t r_lo = std::max<int64_t>(0, c - (n - 1));
+    const int64_t r_hi = f.causal ? c : std::min<int64_t>(2 * c, c + n - 1);
+    p.clip = (int32_t)c;
+    p.r_lo = (int32_t)r_lo;
+    p.nr = (int32_t)(r_hi - r_lo + 1);
+    const int64_t esz = F.bf16 ? 2 : 4;
+    p.wk = static_cast<const char*>(wK->data) + 2 * c * wK->stride[1] * esz;
+    p.wk_sr = -wK->stride[1];
+    p.wk_sh = wK->shape[0] == 1 ? 0 : wK->stride[0];
+    p.htk = (int32_t)wK->shape[0];
+    p.xl_u = xl_u->data;
+    p.xl_v = xl_v->data;
+    p.xl_u_sh = xl_u->shape[0] == 1 ? 0 : xl_u->stride[0];
+    p.xl_v_sh = xl_v->shape[0] == 1 ? 0 : xl_v->stride[0];
+    if (dwK) {
+      p.dwk = static_cast<float*>(dwK->data) + 2 * c * dwK->stride[1];
+      p.dwk_sr = -dwK->stride[1];
+    }
+    if (du) {
+      p.du = static_cast<float*>(du->data);
+      p.du_sh = du->stride[0];
+      p.hu = (int32_t)xl_u->shape[0];
+    }
+    if (dvb) {
+      p.dvb = static_cast<float*>(dvb->data);
+      p.dvb_sh = dvb->stride[0];
+      p.hv = (int32_t)xl_v->shape[0];
+    }
+  }
+  const bool shaw = F.mode == relattn::kRelShaw || xl, t5m = F.mode == relattn::kRelT5;
   const bool want_db = (t5m || grid || lab) && dbias != nullptr;
   // the wide workgroup shapes unless their LDS does not fit
   size_t lq = relattn::bwd_lds_q(F.bf16, F.d, cfg, F.mode, F.has_wk, F.has_wv, p.nr, p.t5_dist,
@@ -1036,6 +1096,12 @@ int make_bwd_plan(const relattn_tensor* q, const relattn_tensor* k, const relatt
                             p.t5.nb, want_db);
     lkv = relattn::bwd_lds_kv(F.bf16, F.d, cfg, F.mode, F.has_wk, F.has_wv, p.nr, p.t5_dist,
                               p.t5.nb);
+    // the key table alone in bf16 at d <= 64: one wave and 32-key tiles
+    if (lq > kMaxLdsBytes && F.bf16 && F.d <= 64 && shaw && F.has_wk && !F.has_wv) {
+      cfg = relattn::bwd_cfg(F.bf16, F.d, true, lkv > kMaxLdsBytes || cfg.kqblock != 64, true);
+      lq = relattn::bwd_lds_q(F.bf16, F.d, cfg, F.mode, F.has_wk, F.has_wv, p.nr, p.t5_dist,
+                              p.t5.nb, want_db);
+    }
   }
   const int64_t brq = 32 * cfg.qwaves, brk = 32 * cfg.kwaves;
   p.n_qtiles = (int32_t)((n + brq - 1) / brq);
@@ -1060,6 +1126,7 @@ int make_bwd_plan(const relattn_tensor* q, const relattn_tensor* k, const relatt
   plan->off_pk = (shaw && F.has_wk) ? take(BH * p.n_qtiles * p.nr * d) : 0;
   plan->off_pv = (shaw && F.has_wv) ? take(BH * p.n_qtiles * p.nr * d) : 0;
   plan->off_pb = want_db ? take(BH * p.n_qtiles * p.t5.nb) : 0;
+  plan->off_pu = (xl && (du || dvb)) ? take(BH * p.n_qtiles * 2 * d) : 0;
   plan->ws_bytes = off;
   return RELATTN_OK;
 }
@@ -1076,9 +1143,11 @@ int run_bwd(BwdPlan& plan, const relattn_tensor* wK, const relattn_tensor* wV, b
   if ((st = check_device())) return st;
   unsigned char* ws = static_cast<unsigned char*>(workspace);
   relattn::BwdParams& p = plan.p;
-  const bool shaw = plan.fwd.mode == relattn::kRelShaw;
+  const bool xl = plan.fwd.mode == relattn::kRelXL;
+  const bool shaw = plan.fwd.mode == relattn::kRelShaw || xl;
   p.ws_stat = reinterpret_cast<float*>(ws + plan.off_stat);
   p.ws_pk = (shaw && wK) ? reinterpret_cast<float*>(ws + plan.off_pk) : nullptr;
+  p.ws_pu = (xl && (p.du || p.dvb)) ? reinterpret_cast<float*>(ws + plan.off_pu) : nullptr;
   p.ws_pv = (shaw && wV) ? reinterpret_cast<float*>(ws + plan.off_pv) : nullptr;
   p.ws_pb = want_db ? reinterpret_cast<float*>(ws + plan.off_pb) : nullptr;
   const int e = relattn::launch_bwd(plan.fwd.bf16, plan.fwd.d, plan.cfg, plan.fwd.mode,
@@ -1474,6 +1543,58 @@ int relattn_fwd_xl(const relattn_tensor* q, const relattn_tensor* k, const relat
                      nullptr, 0, u, vb);
   if (st) return st;
   return run_fwd(plan, stream);
+}
+
+int relattn_fwd_xl_lse(const relattn_tensor* q, const relattn_tensor* k, const relattn_tensor* v,
+                       const relattn_tensor* R, const relattn_tensor* u, const relattn_tensor* vb,
+                       int32_t window, float scale, const relattn_mask* mask, relattn_tensor* out,
+                       relattn_tensor* lse, void* stream) {
+  g_last_error.clear();
+  if (!R || !u || !vb) return fail(RELATTN_ERR_INVALID_ARGUMENT, "R, u and v are required");
+  Plan plan;
+  int st = make_plan(q, k, v, R, nullptr, nullptr, nullptr, window, scale, mask, out, &plan, true,
+                     nullptr, 0, u, vb);
+  if (st) return st;
+  if ((st = check_lse(lse, q))) return st;
+  return run_fwd_lse(plan, lse, stream);
+}
+
+int relattn_bwd_xl_workspace_size(const relattn_tensor* q, const relattn_tensor* k,
+                                  const relattn_tensor* v, const relattn_tensor* R,
+                                  const relattn_tensor* u, const relattn_tensor* vb,
+                                  int32_t window, float scale, const relattn_mask* mask,
+                                  const relattn_tensor* out, const relattn_tensor* dout,
+                                  const relattn_tensor* lse, const relattn_tensor* dq,
+                                  const relattn_tensor* dk, const relattn_tensor* dv,
+                                  const relattn_tensor* dR, const relattn_tensor* du,
+                                  const relattn_tensor* dvb, size_t* bytes) {
+  g_last_error.clear();
+  if (!bytes) return fail(RELATTN_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  if (!R || !u || !vb) return fail(RELATTN_ERR_INVALID_ARGUMENT, "R, u and v are required");
+  BwdPlan plan;
+  const int st = make_bwd_plan(q, k, v, R, nullptr, nullptr, nullptr, window, scale, mask, out,
+                               dout, lse, dq, dk, dv, dR, nullptr, nullptr, &plan, true, nullptr,
+                               0, 0, nullptr, u, vb, du, dvb);
+  if (st) return st;
+  *bytes = plan.fwd.empty ? 0 : plan.ws_bytes;
+  return RELATTN_OK;
+}
+
+int relattn_bwd_xl(const relattn_tensor* q, const relattn_tensor* k, const relattn_tensor* v,
+                   const relattn_tensor* R, const relattn_tensor* u, const relattn_tensor* vb,
+                   int32_t window, float scale, const relattn_mask* mask,
+                   const relattn_tensor* out, const relattn_tensor* dout,
+                   const relattn_tensor* lse, relattn_tensor* dq, relattn_tensor* dk,
+                   relattn_tensor* dv, relattn_tensor* dR, relattn_tensor* du,
+                   relattn_tensor* dvb, void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  if (!R || !u || !vb) return fail(RELATTN_ERR_INVALID_ARGUMENT, "R, u and v are required");
+  BwdPlan plan;
+  const int st = make_bwd_plan(q, k, v, R, nullptr, nullptr, nullptr, window, scale, mask, out,
+                               dout, lse, dq, dk, dv, dR, nullptr, nullptr, &plan, true, nullptr,
+                               0, 0, nullptr, u, vb, du, dvb);
+  if (st) return st;
+  return run_bwd(plan, R, nullptr, false, workspace, workspace_bytes, stream);
 }
 
 int relattn_fwd_grid_bias_lse(const relattn_tensor* q, const relattn_tensor* k,

@@ -78,7 +78,7 @@ __host__ __device__ constexpr int bwd_waves_per_simd() {
 // tiles), the table rows of the reachable labels (resident), then the
 // per-query rows (Shaw) or the offset vector and bucket rows (T5).
 struct LayQ {
-  int ring, tk, tv, rg, rv, tb, tbi, gb, total;
+  int ring, tk, tv, rg, rv, tb, tbi, gb, xs, total;
   int lrs;       // relative row stride (floats)
   int gbs;       // bucket row stride (floats)
   int tab_rows;  // table rows held (labels rounded up to 32)
@@ -103,9 +103,9 @@ __host__ __device__ inline LayQ make_lay_q(int mode, bool has_wk, bool has_wv, i
     L.lrs = m + ((2 - m) & 3);
   }
   L.tab_rows = (nr + 31) / 32 * 32;
-  L.tk = L.tv = L.rg = L.rv = L.tb = L.tbi = L.gb = off;
+  L.tk = L.tv = L.rg = L.rv = L.tb = L.tbi = L.gb = L.xs = off;
   L.gbs = nb | 1;
-  if (mode == kRelShaw) {
+  if (mode == kRelShaw || mode == kRelXL) {
     if (has_wk) {
       L.tk = take(L.tab_rows * G::ROWB);
       L.rg = take(G::BR * L.lrs * 4);
@@ -127,6 +127,8 @@ __host__ __device__ inline LayQ make_lay_q(int mode, bool has_wk, bool has_wv, i
     L.tb = take(nb * 4);
     if (want_db) L.gb = take(2 * G::BR * L.gbs * 4);
   }
+  // Transformer-XL: per wave, its rows' sums of a dq-shaped accumulator
+  if (mode == kRelXL) L.xs = take(NW * D * 4);
   L.total = off;
   return L;
 }
@@ -153,7 +155,7 @@ __device__ __forceinline__ void load_row_frags(const T* row, int hh, Op (&op)[BF
 // s*log2(e)*q.w^K_r and dz.w^V_r, computed per tile) and, per query, the two
 // end labels' values less lse and D.
 struct LayKV {
-  int q, z, lse, dd, stage, rl, rv, tail, tk, tv, tb, total;
+  int q, z, lse, dd, stage, rl, rv, tail, tk, tv, tb, xb, total;
   int lrs;       // relative row stride (floats)
   int tab_rows;  // table rows held (labels rounded up to 32)
 };
@@ -177,8 +179,8 @@ __host__ __device__ inline LayKV make_lay_kv(int mode, bool has_wk, bool has_wv,
   off = 2 * L.stage;
   L.lrs = nr + ((2 - nr) & 3);
   L.tab_rows = (nr + 31) / 32 * 32;
-  L.rl = L.rv = L.tail = L.tk = L.tv = L.tb = off;
-  if (mode == kRelShaw && (has_wk || has_wv)) {
+  L.rl = L.rv = L.tail = L.tk = L.tv = L.tb = L.xb = off;
+  if ((mode == kRelShaw || mode == kRelXL) && (has_wk || has_wv)) {
     if (has_wk) {
       L.tk = take(L.tab_rows * G::ROWB);
       L.rl = take(BQ * L.lrs * 4);
@@ -191,6 +193,8 @@ __host__ __device__ inline LayKV make_lay_kv(int mode, bool has_wk, bool has_wv,
   }
   if (mode == kRelT5) L.tb = take((2 * t5_dist + 1) * 4);
   if (mode == kRelGrid || mode == kRelLabel) L.tb = take(nb * 4);  // the head's table
+  // Transformer-XL: v . R_r of every table row
+  if (mode == kRelXL) L.xb = take(L.tab_rows * 4);
   L.total = off;
   return L;
 }
@@ -281,7 +285,9 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd<D>()))) void bwd_q_kernel(
   using Op = std::conditional_t<BF16, bf16x8, float>;
   constexpr int NT = G::NT, NKB = G::NKB, DVB = G::DVB, NKS = G::NKS, ROWB = G::ROWB;
   constexpr int KSTR = G::KSTR, BR = G::BR;
-  constexpr bool SHAW = MODE == kRelShaw, T5 = MODE == kRelT5, GRID = MODE == kRelGrid;
+  // Transformer-XL runs the key-table path with R as the table
+  constexpr bool XL = MODE == kRelXL;
+  constexpr bool SHAW = MODE == kRelShaw || XL, T5 = MODE == kRelT5, GRID = MODE == kRelGrid;
   constexpr bool LAB = MODE == kRelLabel;
   constexpr bool ROWS = SHAW && (HAS_WK || HAS_WV);
   static_assert(2 * BR * ROWB <= 4 * G::TILEB, "Q and dZ tiles must fit the ring");
@@ -344,6 +350,13 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd<D>()))) void bwd_q_kernel(
   load_row_frags<BF16, D>(zg + (int64_t)qr * p.do_sn, hh, zop);
   Op oop[NKS];
   load_row_frags<BF16, D>(og + (int64_t)qr * p.o_sn, hh, oop);
+  // Transformer-XL: the head's global biases u (content logit) and v
+  // (relative logit), in the layout of the q fragments
+  [[maybe_unused]] Op xu[NKS], xv[NKS];
+  if constexpr (XL) {
+    load_row_frags<BF16, D>(reinterpret_cast<const T*>(p.xl_u) + h * p.xl_u_sh, hh, xu);
+    load_row_frags<BF16, D>(reinterpret_cast<const T*>(p.xl_v) + h * p.xl_v_sh, hh, xv);
+  }
   float lse2 = kPosInf;  // rows past n: every weight comes out 0
   if (q_ok) lse2 = p.lse[b * p.lse_sb + h * p.lse_sh + qi] * kLog2e;
   if constexpr (T5) {
@@ -399,6 +412,10 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd<D>()))) void bwd_q_kernel(
   // ---- relative rows: Shaw row qrow holds s*log2(e)*q.w^K_r (then dS sums)
   // and dz.w^V_r (then weight sums) for labels r_lo + x, x < nr
   if constexpr (ROWS) {
+    // the key table's product takes q + v under Transformer-XL
+    Op qrel[NKS];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) qrel[ks] = XL ? op_add(qop[ks], xv[ks]) : qop[ks];
     const int nlb = lay.tab_rows / 32;
     for (int lb = 0; lb < nlb; ++lb) {
 #pragma unroll
@@ -410,10 +427,10 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd<D>()))) void bwd_q_kernel(
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
           if constexpr (BF16) {
-            acc = mfma(frag_row<ROWB>(tile, lb * 32 + ql, 2 * ks + hh), which ? zop[ks] : qop[ks],
+            acc = mfma(frag_row<ROWB>(tile, lb * 32 + ql, 2 * ks + hh), which ? zop[ks] : qrel[ks],
                        acc);
           } else {
-            acc = mfma(elem_f32<ROWB>(tile, lb * 32 + ql, 2 * ks + hh), which ? zop[ks] : qop[ks],
+            acc = mfma(elem_f32<ROWB>(tile, lb * 32 + ql, 2 * ks + hh), which ? zop[ks] : qrel[ks],
                        acc);
           }
         }
@@ -427,6 +444,11 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd<D>()))) void bwd_q_kernel(
       }
     }
     compiler_fence();  // each row is read back by the lanes of its own wave only
+  }
+  // Transformer-XL: the content logits take q + u
+  if constexpr (XL) {
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) qop[ks] = op_add(qop[ks], xu[ks]);
   }
 
   // ---- key loop (tile 0 is in stage 0)
@@ -726,6 +748,15 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd<D>()))) void bwd_q_kernel(
   // the Q and dZ tiles for the partial table gradients, rebuilt in the ring
   // from the row fragments each lane holds (same layout as a DMA'd tile)
   if constexpr (ROWS) {
+    if constexpr (XL) {
+      // the table gradient takes q + v: the row and v again (the lane's q
+      // fragments hold q + u by now)
+      Op qq[NKS];
+      load_row_frags<BF16, D>(qg + (int64_t)qr * p.q_sn, hh, qq);
+      load_row_frags<BF16, D>(reinterpret_cast<const T*>(p.xl_v) + h * p.xl_v_sh, hh, xv);
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) qop[ks] = op_add(qq[ks], xv[ks]);
+    }
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
       if constexpr (BF16) {
@@ -781,8 +812,16 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd<D>()))) void bwd_q_kernel(
     compiler_fence();  // the other half of this wave wrote the rest of the row
   }
 
-  // ---- dQ^T += (w^K)^T G^T with the resident w^K rows
-  if constexpr (SHAW && HAS_WK) {
+  // ---- dQ^T += (w^K)^T G^T with the resident w^K rows (Transformer-XL: into
+  // an accumulator of its own first, so that the tile's sums over its rows of
+  // the content part, s sum dS k (-> du), and of this part, s sum G R (-> dv),
+  // can be taken apart)
+  [[maybe_unused]] f32x16 gw[DVB];
+  if constexpr (XL) {
+#pragma unroll
+    for (int mb = 0; mb < DVB; ++mb) gw[mb] = f32x16{};
+  }
+  auto add_table_part = [&](f32x16 (&acc)[DVB]) __attribute__((always_inline)) {
     const int nls = (p.nr + 15) / 16;
     const uint32_t tk_lds = smem_addr + (uint32_t)lay.tk;
     for (int ls = 0; ls < nls; ++ls) {
@@ -799,7 +838,7 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd<D>()))) void bwd_q_kernel(
           frag_col_issue<ROWB, D>(tk_lds, ls * 16, 32 * mb, lane, wlo[mb], whi[mb]);
         frag_col_wait(wlo, whi);
 #pragma unroll
-        for (int mb = 0; mb < DVB; ++mb) dq[mb] = mfma(frag_join(wlo[mb], whi[mb]), bw, dq[mb]);
+        for (int mb = 0; mb < DVB; ++mb) acc[mb] = mfma(frag_join(wlo[mb], whi[mb]), bw, acc[mb]);
       } else {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -808,11 +847,46 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd<D>()))) void bwd_q_kernel(
 #pragma unroll
           for (int mb = 0; mb < DVB; ++mb) {
             const int dcol = min(32 * mb + ql, D - 1);
-            dq[mb] = mfma(elem_f32<ROWB>(smem + lay.tk, ls * 16 + 2 * e + hh, dcol), w, dq[mb]);
+            acc[mb] = mfma(elem_f32<ROWB>(smem + lay.tk, ls * 16 + 2 * e + hh, dcol), w, acc[mb]);
           }
         }
       }
     }
+  };
+  if constexpr (XL) {
+    add_table_part(gw);
+    if (p.ws_pu) {
+      // this tile's sums over its rows: the content part, then the table part
+      const int64_t tile_id = (int64_t)bh * p.n_qtiles + qt;
+      float* xs = reinterpret_cast<float*>(smem + lay.xs);
+      float* dst = p.ws_pu + tile_id * 2 * D;
+      auto rows_sum = [&](const f32x16 (&acc)[DVB], float* out) __attribute__((always_inline)) {
+#pragma unroll
+        for (int mb = 0; mb < DVB; ++mb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            // the 32 lanes of a half hold the same d and 32 queries
+            float v = acc[mb][i];
+#pragma unroll
+            for (int m = 16; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+            const int dd = 32 * mb + 8 * (i >> 2) + 4 * hh + (i & 3);
+            if (ql == 0 && dd < D) xs[wave * D + dd] = v;
+          }
+        block_sync();
+        for (int dd = tid; dd < D; dd += NT) {
+          float sum = 0.f;
+          for (int w = 0; w < NW; ++w) sum += xs[w * D + dd];
+          out[dd] = sum;
+        }
+        block_sync();
+      };
+      rows_sum(dq, dst);
+      rows_sum(gw, dst + D);
+    }
+#pragma unroll
+    for (int mb = 0; mb < DVB; ++mb) dq[mb] += gw[mb];
+  } else if constexpr (SHAW && HAS_WK) {
+    add_table_part(dq);
   }
   if (q_ok) store_row_block<T, D>(dqg + (int64_t)qi * p.dq_sn, dq, p.scale, hh);
 
@@ -906,8 +980,16 @@ __host__ __device__ inline int reduce_tables_rows(const BwdParams& p, int which)
   const int ht = which ? (p.dwv ? p.htv : 0) : (p.dwk ? p.htk : 0);
   return ht * (2 * p.clip + 1);
 }
+// (Transformer-XL's du and dv rows only in that mode's kernels: read in the
+// others, their fields would hold registers through the whole kernel)
+template <bool XL>
+__host__ __device__ inline int reduce_xl_rows(const BwdParams& p) {
+  if constexpr (XL) return (p.du ? p.hu : 0) + (p.dvb ? p.hv : 0);
+  return 0;
+}
+template <bool XL>
 __host__ __device__ inline int reduce_role_count(const BwdParams& p, int nt) {
-  int n = reduce_tables_rows(p, 0) + reduce_tables_rows(p, 1);
+  int n = reduce_tables_rows(p, 0) + reduce_tables_rows(p, 1) + reduce_xl_rows<XL>(p);
   if (p.db) {
     const int64_t total = p.ob ? (int64_t)p.hb * p.ob_n : (int64_t)p.t5.nb * p.H;
     n += (int)((total + nt - 1) / nt);
@@ -987,14 +1069,52 @@ __device__ void reduce_bias(const BwdParams& p, int blk, int nt) {
   }
 }
 
+// Transformer-XL: one head row of du (which = 0) or dv (which = 1), s times
+// the sum of the query tiles' partials over the batch (and over the heads
+// for one shared vector); the nt threads form nt/d groups of d columns, added
+// in order as for the tables.
+__device__ void reduce_xl_row(const BwdParams& p, int which, int hq, int nt) {
+  const int hx = which ? p.hv : p.hu;
+  const int d = p.d, G = nt / d;
+  const int tid = threadIdx.x;
+  const int dd = tid % d, g = tid / d;
+  const int h_lo = hx == 1 ? 0 : hq, hn = hx == 1 ? p.H : 1;
+  const int nq = p.n_qtiles;
+  const int U = p.B * hn * nq;  // term u: (b, head, query tile)
+  float acc = 0.f;
+  if (g < G) {
+    for (int u = g; u < U; u += G) {
+      const int tq = u % nq, bh2 = u / nq;
+      const int b = bh2 / hn, hh = h_lo + (bh2 - b * hn);
+      acc += p.ws_pu[(((int64_t)(b * p.H + hh) * nq + tq) * 2 + which) * d + dd];
+    }
+  }
+  extern __shared__ __align__(16) unsigned char smem[];
+  float* red = reinterpret_cast<float*>(smem);
+  red[tid] = acc;
+  __syncthreads();
+  if (g == 0) {
+    float sum = 0.f;
+    for (int k = 0; k < G; ++k) sum += red[k * d + dd];
+    if (which) p.dvb[hq * p.dvb_sh + dd] = sum * p.scale;
+    else p.du[hq * p.du_sh + dd] = sum * p.scale;
+  }
+}
+
+template <bool XL>
 __device__ void reduce_role(const BwdParams& p, int role, int nt) {
   const int rk = reduce_tables_rows(p, 0), rv = reduce_tables_rows(p, 1);
+  const int ru = XL ? (p.du ? p.hu : 0) : 0, rx = reduce_xl_rows<XL>(p);
   if (role < rk) {
     reduce_table_row(p, 0, role, nt);
   } else if (role < rk + rv) {
     reduce_table_row(p, 1, role - rk, nt);
+  } else if (XL && role < rk + rv + rx) {
+    const int r = role - rk - rv;
+    if (r < ru) reduce_xl_row(p, 0, r, nt);
+    else reduce_xl_row(p, 1, r - ru, nt);
   } else {
-    reduce_bias(p, role - rk - rv, nt);
+    reduce_bias(p, role - rk - rv - rx, nt);
   }
 }
 
@@ -1010,7 +1130,9 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd<D>()))) void bwd_kv_kernel
   using Op = std::conditional_t<BF16, bf16x8, float>;
   constexpr int NT = G::NT, NQB = G::NKB, DVB = G::DVB, NKS = G::NKS, ROWB = G::ROWB;
   constexpr int KSTR = G::KSTR, BR = G::BR;
-  constexpr bool SHAW = MODE == kRelShaw, T5 = MODE == kRelT5, GRID = MODE == kRelGrid;
+  // Transformer-XL runs the key-table path with R as the table
+  constexpr bool XL = MODE == kRelXL;
+  constexpr bool SHAW = MODE == kRelShaw || XL, T5 = MODE == kRelT5, GRID = MODE == kRelGrid;
   constexpr bool LAB = MODE == kRelLabel;
   constexpr bool ROWS = SHAW && (HAS_WK || HAS_WV);
 
@@ -1036,6 +1158,7 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd<D>()))) void bwd_kv_kernel
   float* RLt = reinterpret_cast<float*>(smem + lay.rl);
   float* RVt = reinterpret_cast<float*>(smem + lay.rv);
   float* TAIL = reinterpret_cast<float*>(smem + lay.tail);  // [a_lo | a_hi | b_lo | b_hi][BQ]
+  float* XB = reinterpret_cast<float*>(smem + lay.xb);
 
   const T* qg = reinterpret_cast<const T*>(p.q) + b * p.q_sb + h * p.q_sh;
   const T* kg = reinterpret_cast<const T*>(p.k) + b * p.k_sb + h * p.k_sh;
@@ -1057,6 +1180,24 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd<D>()))) void bwd_kv_kernel
   Op kop[NKS], vop[NKS];
   load_row_frags<BF16, D>(kg + (int64_t)kr * p.k_sn, hh, kop);
   load_row_frags<BF16, D>(vg + (int64_t)kr * p.v_sn, hh, vop);
+  // Transformer-XL: the content logit's term u . k_j of this lane's key (log2
+  // units), and its running sum of dS for dk's share s u sum_i dS_ij
+  [[maybe_unused]] float ukl2 = 0.f, cs = 0.f;
+  if constexpr (XL) {
+    Op xu[NKS];
+    load_row_frags<BF16, D>(reinterpret_cast<const T*>(p.xl_u) + h * p.xl_u_sh, hh, xu);
+    float part = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      if constexpr (BF16) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) part = fmaf((float)xu[ks][e], (float)kop[ks][e], part);
+      } else {
+        part = fmaf(xu[ks], kop[ks], part);
+      }
+    }
+    ukl2 = halves_sum(part) * p.scale_log2;
+  }
   if constexpr (T5) {
     for (int x = tid; x <= 2 * dist; x += NT) {
       const int entry = p.ob ? x : t5_bucket(x - dist, p.t5);
@@ -1139,6 +1280,22 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd<D>()))) void bwd_kv_kernel
     const float* DD = reinterpret_cast<const float*>(S0 + lay.dd);
     const int q0 = t * BQ;
 
+    if constexpr (XL) {
+      if (t == t_lo) {
+        // v . R_r for every resident table row (landed with the first tile)
+        const T* vbp = reinterpret_cast<const T*>(p.xl_v) + h * p.xl_v_sh;
+        const unsigned char* tk = smem + lay.tk;
+        for (int x = tid; x < lay.tab_rows; x += NT) {
+          float acc = 0.f;
+          for (int dd = 0; dd < D; ++dd)
+            acc = fmaf((float)vbp[dd],
+                       (float)*reinterpret_cast<const T*>(tk + tile_offset<ROWB>(x, dd * G::ESZ)),
+                       acc);
+          XB[x] = acc;
+        }
+        block_sync();
+      }
+    }
     if constexpr (ROWS) {
       // relative rows of the tile's queries: C[label, query] = w_r . x_q with
       // x = q (key table, scaled to log2 units) or dz (value table), and the
@@ -1170,7 +1327,8 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd<D>()))) void bwd_kv_kernel
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int x = lb * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
-          const float v = acc[i] * mul;
+          // Transformer-XL: (q + v) . R_r = q . R_r + v . R_r
+          const float v = (XL ? acc[i] + XB[x] : acc[i]) * mul;
           if (x < p.nr) row[x] = v;
           if (x == 0) tl[lq] = v - sub;
           if (x == p.nr - 1) tl[BQ + lq] = v - sub;
@@ -1233,7 +1391,7 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd<D>()))) void bwd_kv_kernel
           constexpr bool MASK = decltype(mask_tag)::value;
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            float pv = fast_exp2(fmaf(s[i], p.scale_log2, av[i]));
+            float pv = fast_exp2(fmaf(s[i], p.scale_log2, XL ? av[i] + ukl2 : av[i]));
             if constexpr (MASK) {
               const int qq = qb0 + hoff + 16 * (i >> 3) + KSTR * (i & 7);
               pv = (qq < p.n && (!p.causal || kj <= qq)) ? pv : 0.f;
@@ -1276,12 +1434,16 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd<D>()))) void bwd_kv_kernel
           // the exponential for every lane, then a select (a conditional
           // exponential becomes a branch per element, each waiting for its
           // own row reads)
-          float ex = fast_exp2(fmaf(s[i], p.scale_log2, rl) - lsv[i]);
+          float ex = fast_exp2(fmaf(s[i], p.scale_log2, XL ? rl + ukl2 : rl) - lsv[i]);
           asm volatile("" : "+v"(ex));
           const float pv = vis ? ex : 0.f;
           pw[i] = pv;
           ds[i] = vis ? pv * (dp[i] + rv - ddv[i]) : 0.f;
         }
+      }
+      if constexpr (XL) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) cs += ds[i];
       }
       // dV^T += dZ^T P and dK^T += Q^T dS
       if constexpr (BF16) {
@@ -1327,6 +1489,18 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd<D>()))) void bwd_kv_kernel
     }
   }
   wait_vm<0>();
+  if constexpr (XL) {
+    // dk_j = s sum_i dS_ij (q_i + u): add u times the key's sum of dS
+    const float cst = halves_sum(cs);
+    const T* up = reinterpret_cast<const T*>(p.xl_u) + h * p.xl_u_sh;
+#pragma unroll
+    for (int mb = 0; mb < DVB; ++mb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int dd = 32 * mb + 8 * (i >> 2) + 4 * hh + (i & 3);
+        if (dd < D) dk[mb][i] = fmaf((float)up[dd], cst, dk[mb][i]);
+      }
+  }
   if (kj < p.n) {
     // a key past the key length is seen by no query: its gradients are zero
     store_row_block<T, D>(dkg + (int64_t)kj * p.dk_sn, dk, p.scale, hh, !k_ok);
@@ -1337,7 +1511,7 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd<D>()))) void bwd_kv_kernel
   // (launched before on the same stream) wrote.  Under the causal mask the
   // last key tiles of a head see the fewest queries and finish first; they
   // take every reduction role.  Otherwise all workgroups share them.
-  const int n_roles = reduce_role_count(p, NT);
+  const int n_roles = reduce_role_count<XL>(p, NT);
   if (n_roles > 0) {
     const int BH = p.B * p.H;
     int first, stride;
@@ -1352,7 +1526,7 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd<D>()))) void bwd_kv_kernel
     }
     for (int role = first; role < n_roles; role += stride) {
       block_sync();  // the LDS the role uses is free
-      reduce_role(p, role, NT);
+      reduce_role<XL>(p, role, NT);
     }
   }
 }
@@ -1372,6 +1546,10 @@ struct BwdShape {
   static constexpr int KW = BF16 ? 4 : 2;
   static constexpr int KBQ_WIDE = BIG ? 64 : 32;
   static constexpr int KBQ_NARROW = 32;
+  // the tiny dq shape of the key-table modes (bf16, d <= 64): one wave,
+  // 32-key tiles
+  static constexpr int QW_TINY = 1;
+  static constexpr int QBC_TINY = 32;
 };
 
 template <bool BF16, int D>
@@ -1381,6 +1559,10 @@ static size_t lds_q_t(int qwaves, RelMode mode, bool has_wk, bool has_wv, int nr
   if (qwaves == S::QW_WIDE)
     return (size_t)make_lay_q<BF16, D, S::QW_WIDE, S::QBC>(mode, has_wk, has_wv, nr, t5_dist, nb,
                                                            want_db)
+        .total;
+  if (S::BIG && qwaves == S::QW_TINY)
+    return (size_t)make_lay_q<BF16, D, S::QW_TINY, S::QBC_TINY>(mode, has_wk, has_wv, nr, t5_dist,
+                                                                nb, want_db)
         .total;
   return (size_t)make_lay_q<BF16, D, S::QW_NARROW, S::QBC>(mode, has_wk, has_wv, nr, t5_dist, nb,
                                                            want_db)
@@ -1398,18 +1580,20 @@ static size_t lds_kv_t(int kqblock, RelMode mode, bool has_wk, bool has_wv, int 
 }
 
 template <bool BF16, int D>
-static BwdCfg cfg_t(bool narrow_q, bool narrow_kv) {
+static BwdCfg cfg_t(bool narrow_q, bool narrow_kv, bool tiny_q) {
   using S = BwdShape<BF16, D>;
+  if (S::BIG && tiny_q)
+    return BwdCfg{S::QW_TINY, S::QBC_TINY, S::KW, narrow_kv ? S::KBQ_NARROW : S::KBQ_WIDE};
   return BwdCfg{narrow_q ? S::QW_NARROW : S::QW_WIDE, S::QBC, S::KW,
                 narrow_kv ? S::KBQ_NARROW : S::KBQ_WIDE};
 }
 
-BwdCfg bwd_cfg(bool bf16, int d, bool narrow_q, bool narrow_kv) {
+BwdCfg bwd_cfg(bool bf16, int d, bool narrow_q, bool narrow_kv, bool tiny_q) {
   if (bf16) {
-    if (d > 64) return cfg_t<true, 128>(narrow_q, narrow_kv);
-    return cfg_t<true, 64>(narrow_q, narrow_kv);
+    if (d > 64) return cfg_t<true, 128>(narrow_q, narrow_kv, false);
+    return cfg_t<true, 64>(narrow_q, narrow_kv, tiny_q);
   }
-  return cfg_t<false, 64>(narrow_q, narrow_kv);
+  return cfg_t<false, 64>(narrow_q, narrow_kv, false);
 }
 
 template <bool BF16>
@@ -1473,9 +1657,18 @@ template <bool BF16, int D, int MODE, bool WK, bool WV>
 static int launch_bwd_t(const BwdCfg& cfg, const BwdParams& p, void* stream) {
   using S = BwdShape<BF16, D>;
   const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  int e = cfg.qwaves == S::QW_WIDE
-              ? launch_q<D, S::QW_WIDE, S::QBC, BF16, MODE, WK, WV>(p, s)
-              : launch_q<D, S::QW_NARROW, S::QBC, BF16, MODE, WK, WV>(p, s);
+  int e;
+  if constexpr (S::BIG && (MODE == kRelShaw || MODE == kRelXL) && WK && !WV) {
+    if (cfg.qwaves == S::QW_TINY && cfg.qkblock == S::QBC_TINY) {
+      e = launch_q<D, S::QW_TINY, S::QBC_TINY, BF16, MODE, WK, WV>(p, s);
+      if (e != (int)hipSuccess) return e;
+      return cfg.kqblock == S::KBQ_WIDE ? launch_kv<D, S::KW, S::KBQ_WIDE, BF16, MODE, WK, WV>(p, s)
+                                        : launch_kv<D, S::KW, S::KBQ_NARROW, BF16, MODE, WK, WV>(p, s);
+    }
+  }
+  if (cfg.qwaves != S::QW_WIDE && cfg.qwaves != S::QW_NARROW) return (int)hipErrorInvalidValue;
+  e = cfg.qwaves == S::QW_WIDE ? launch_q<D, S::QW_WIDE, S::QBC, BF16, MODE, WK, WV>(p, s)
+                               : launch_q<D, S::QW_NARROW, S::QBC, BF16, MODE, WK, WV>(p, s);
   if (e != (int)hipSuccess) return e;
   e = cfg.kqblock == S::KBQ_WIDE ? launch_kv<D, S::KW, S::KBQ_WIDE, BF16, MODE, WK, WV>(p, s)
                                  : launch_kv<D, S::KW, S::KBQ_NARROW, BF16, MODE, WK, WV>(p, s);
@@ -1489,6 +1682,7 @@ static int launch_bwd_mode(const BwdCfg& c, RelMode mode, bool wk, bool wv, cons
   if (mode == kRelT5) return launch_bwd_t<BF16, D, kRelT5, false, false>(c, p, stream);
   if (mode == kRelGrid) return launch_bwd_t<BF16, D, kRelGrid, false, false>(c, p, stream);
   if (mode == kRelLabel) return launch_bwd_t<BF16, D, kRelLabel, false, false>(c, p, stream);
+  if (mode == kRelXL) return launch_bwd_t<BF16, D, kRelXL, true, false>(c, p, stream);
   if (mode == kRelShaw) {
     if (wk && wv) return launch_bwd_t<BF16, D, kRelShaw, true, true>(c, p, stream);
     if (wk) return launch_bwd_t<BF16, D, kRelShaw, true, false>(c, p, stream);

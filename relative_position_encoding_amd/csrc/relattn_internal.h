@@ -150,6 +150,9 @@ int launch_debug_indices(int n, int clip, const T5Buckets* t5, int32_t* out,
 //   ws_pk   [B*H][n_qtiles][nr][d], ws_pv the same : per query-tile partial
 //                                  table gradients (ws_pk already scaled)
 //   ws_pb   [B*H][n_qtiles][nb]  : per query-tile partial bias gradients
+//   ws_pu   [B*H][n_qtiles][2][d]: Transformer-XL, per query tile, its rows'
+//                                  sums of the content and the relative part
+//                                  of dq (unscaled)
 struct BwdParams {
   const void* q;
   const void* k;
@@ -201,15 +204,28 @@ struct BwdParams {
   int32_t ob, ob_lo;        // scalar bias from a [hb, ob_n] table (ob = 1)
   int32_t ob_n;             // its entries per row: 2W + 1 by clipped offset, (2M-1)^2 by
                             // 2-D offset, NL by edge label
+  int32_t n_qtiles;         // query tiles per (b, h) of the dq kernel
+  int32_t n_ktiles;         // key tiles per (b, h) of the dk/dv kernel
+  T5Buckets t5;
+  // (the modes below read fields of their own, kept after the common ones)
   int32_t grid_m;           // 2-D window: side M (n = M * M); its table has (2M-1)^2 entries
   float grid_inv;           // 1 / M
   // edge labels: lab[b * lab_sb + i * lab_sn + j] labels the pair (query i,
   // key j); rows are readable in whole 16-byte chunks up to n rounded up to 16
   const uint8_t* lab;
   int64_t lab_sb, lab_sn;
-  int32_t n_qtiles;         // query tiles per (b, h) of the dq kernel
-  int32_t n_ktiles;         // key tiles per (b, h) of the dk/dv kernel
-  T5Buckets t5;
+  // Transformer-XL (mode kRelXL, the Shaw key-table path): wk is R read by
+  // i - j (its last row, negative row stride); the content logit takes q + u
+  // and the relative logit q + v.  du, dvb: [hu, d] and [hv, d] fp32 outputs
+  // (NULL to skip).
+  const void* xl_u;
+  const void* xl_v;
+  int64_t xl_u_sh, xl_v_sh;
+  float* du;
+  float* dvb;
+  int64_t du_sh, dvb_sh;
+  int32_t hu, hv;
+  float* ws_pu;
 };
 
 struct BwdCfg {
@@ -219,8 +235,10 @@ struct BwdCfg {
 
 // Workgroup shapes the backward kernels are built with: the wide ones, or the
 // narrow ones (half the query rows of the dq kernel, or half the queries per
-// tile of the dk/dv kernel) that fit larger label windows on chip.
-BwdCfg bwd_cfg(bool bf16, int d, bool narrow_q, bool narrow_kv);
+// tile of the dk/dv kernel) that fit larger label windows on chip; for the
+// widest windows of the key-table modes in bf16 at d <= 64, a tiny dq shape
+// (one wave, 32-key tiles).
+BwdCfg bwd_cfg(bool bf16, int d, bool narrow_q, bool narrow_kv, bool tiny_q = false);
 size_t bwd_lds_q(bool bf16, int d, const BwdCfg& cfg, RelMode mode, bool has_wk, bool has_wv,
                  int nr, int t5_dist, int nb, bool want_db);
 size_t bwd_lds_kv(bool bf16, int d, const BwdCfg& cfg, RelMode mode, bool has_wk, bool has_wv,

@@ -518,3 +518,29 @@ def test_bwd_grid_bias_window_checks(ra):
     M = 7
     assert ws(M, True) == _ws_expected(1, 2, M * M, 64, 1, 0, nb=(2 * M - 1) ** 2)
     assert ws(M, False) == _ws_expected(1, 2, M * M, 64, 1, 0)
+
+
+def test_bwd_xl_window_checks(ra):
+    """The Transformer-XL backward holds one row of relative logits per query
+    over the reachable distances on chip: every distance of a 512-token causal
+    segment fits in bf16 at d = 64 (one-wave query tiles); at d = 128 or over
+    1024 tokens it is UNSUPPORTED, before any launch; the gradient buffers of
+    u and v need the biases they belong to."""
+    def ws(n, d, W, dtype=torch.bfloat16):
+        q = T(1, 2, n, d, dtype=dtype)
+        R, u = T(2, 2 * W + 1, d, dtype=dtype), T(2, d, dtype=dtype)
+        lse = T(1, 2, n, dtype=torch.float32)
+        return ra.bwd_xl_workspace_size(q, q, q, R, u, u, W, out=q, dout=q, lse=lse, causal=True)
+    assert ws(512, 64, 511) > 0
+    for n, d in ((512, 128), (1024, 64)):
+        with pytest.raises(ra.RelattnError) as e:
+            ws(n, d, n - 1)
+        assert e.value.status == ra.UNSUPPORTED
+    # partials of du and dv: 2 d floats per one-wave query tile of each head
+    n, d, W = 512, 64, 511
+    no_biases = ra.bwd_xl_workspace_size(
+        T(1, 2, n, d), T(1, 2, n, d), T(1, 2, n, d), T(2, 2 * W + 1, d), T(2, d), T(2, d), W,
+        out=T(1, 2, n, d), dout=T(1, 2, n, d), lse=T(1, 2, n, dtype=torch.float32),
+        causal=True, want_du=False, want_dvb=False)
+    up = lambda floats: (floats * 4 + 255) // 256 * 256
+    assert ws(n, d, W) - no_biases == up(1 * 2 * (n // 32) * 2 * d)

@@ -159,3 +159,132 @@ def test_xl_rejects(ra):
     assert ra.validate_xl(q, q, q, R, u.float(), u, 4) == ra.INVALID_ARGUMENT
     assert ra.validate_xl(q, q, q, R, u[:, :32].contiguous(), u, 4) == ra.INVALID_ARGUMENT
     assert ra.validate_xl(q, q, q, R, u, u, 5) == ra.INVALID_ARGUMENT  # R rows != 2W + 1
+
+
+# ---------------------------------------------------------------------------
+# backward: relattn_fwd_xl_lse + relattn_bwd_xl against the oracle's
+# chain-rule gradients (oracle.xl_backward).  Bar as for the other backward
+# passes: max|gpu - oracle| <= BTOL * max(max|oracle|, 1), BTOL = 1e-4 (fp32)
+# and 3e-2 (bf16: the product operands rounded to bf16, 2^-9 relative each,
+# q + u and q + v rounded once like every operand, and dq, dk, dv rounded to
+# bf16).
+# ---------------------------------------------------------------------------
+
+BTOL = {torch.float32: 1e-4, torch.bfloat16: 3e-2}
+XL_GRADS = ("dq", "dk", "dv", "dR", "du", "dv_bias")
+
+
+def bcheck(got, want, dtype, names=XL_GRADS):
+    for name, g, w in zip(names, got, want):
+        w = np.asarray(w, np.float64)
+        e = float(np.max(np.abs(g.double().cpu().numpy() - w))) / max(float(np.abs(w).max()), 1.0)
+        assert e <= BTOL[dtype], f"{name}: normalised error {e:.3g} > {BTOL[dtype]}"
+
+
+def xl_grads(ra, q, k, v, R, u, vb, W, dz, causal=False, lens=None):
+    lens_d = None if lens is None else torch.tensor(lens, dtype=torch.int32, device=DEV)
+    qd, kd, vd, Rd, ud, vbd, dzd = (x.to(DEV) for x in (q, k, v, R, u, vb, dz))
+    out, lse = ra.fwd_xl_lse(qd, kd, vd, Rd, ud, vbd, W, causal=causal, key_lens=lens_d)
+    g = ra.bwd_xl(qd, kd, vd, Rd, ud, vbd, W, out=out, dout=dzd, lse=lse, causal=causal,
+                  key_lens=lens_d)
+    torch.cuda.synchronize()
+    return g
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=str)
+@pytest.mark.parametrize("d", [32, 64, 128])
+@pytest.mark.parametrize("mask", ["none", "causal", "lens"])
+@pytest.mark.parametrize("window", ["full", 9])
+def test_xl_backward_parity(ra, dtype, d, mask, window):
+    """Every gradient, per-head R, u and v, the full distance range and a
+    clipped one (end rows shared by the far pairs), under every mask (fp32 at
+    d = 128 over 64 tokens: the 199 rows of 100 would not fit on chip)."""
+    B, H = 2, 2
+    n = 64 if (dtype == torch.float32 and d == 128) else 100
+    W = n - 1 if window == "full" else window
+    q, k, v, dz = (gen((B, H, n, d), dtype, 3400 + d + i) for i in range(4))
+    R = gen((H, 2 * W + 1, d), dtype, 3404, 0.5)
+    u, vb = gen((H, d), dtype, 3405, 0.5), gen((H, d), dtype, 3406, 0.5)
+    causal = mask == "causal"
+    lens = [n, 61] if mask == "lens" else None
+    got = xl_grads(ra, q, k, v, R, u, vb, W, dz, causal, lens)
+    want = oracle.xl_backward(q, k, v, R, u, vb, W, dz, causal=causal, key_lens=lens)
+    bcheck(got, want, dtype)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=str)
+def test_xl_backward_shared_and_empty(ra, dtype):
+    """One R, u and v for every head (gradients summed over the heads), an
+    explicit scale, and a sequence with no visible key (its gradients 0)."""
+    B, H, n, d, W = 3, 3, 70, 64, 20
+    q, k, v, dz = (gen((B, H, n, d), dtype, 3500 + i) for i in range(4))
+    R = gen((1, 2 * W + 1, d), dtype, 3504, 0.5)
+    u, vb = gen((1, d), dtype, 3505, 0.5), gen((1, d), dtype, 3506, 0.5)
+    lens = [n, 0, 33]
+    lens_d = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    qd, kd, vd, Rd, ud, vbd, dzd = (x.to(DEV) for x in (q, k, v, R, u, vb, dz))
+    out, lse = ra.fwd_xl_lse(qd, kd, vd, Rd, ud, vbd, W, causal=True, key_lens=lens_d,
+                             scale=0.3)
+    got = ra.bwd_xl(qd, kd, vd, Rd, ud, vbd, W, out=out, dout=dzd, lse=lse, causal=True,
+                    key_lens=lens_d, scale=0.3)
+    torch.cuda.synchronize()
+    want = oracle.xl_backward(q, k, v, R, u, vb, W, dz, scale=0.3, causal=True, key_lens=lens)
+    bcheck(got, want, dtype)
+    for g in got[:3]:
+        assert torch.count_nonzero(g[1]).item() == 0
+
+
+def test_xl_backward_autograd(ra):
+    """torch.autograd through attention_xl matches the oracle (fp32)."""
+    B, H, n, d, W = 2, 2, 40, 32, 12
+    q, k, v, dz = (gen((B, H, n, d), torch.float32, 3600 + i) for i in range(4))
+    R = gen((H, 2 * W + 1, d), torch.float32, 3604, 0.5)
+    u, vb = gen((H, d), torch.float32, 3605, 0.5), gen((H, d), torch.float32, 3606, 0.5)
+    leaves = [x.to(DEV).requires_grad_(True) for x in (q, k, v, R, u, vb)]
+    out = ra.attention_xl(*leaves, W, causal=True)
+    out.backward(dz.to(DEV))
+    want = oracle.xl_backward(q, k, v, R, u, vb, W, dz, causal=True)
+    bcheck([x.grad for x in leaves], want, torch.float32)
+
+
+def test_xl_backward_full_segment(ra):
+    """The language-model segment at full size (B8 H16 n512 d64, every
+    distance, causal, bf16): one row of relative logits per query over 512
+    distances takes the one-wave query tiles.  dq, dk, dv of sampled (batch,
+    head) pairs against the oracle on those heads; dR, du and dv of two sampled
+    heads element by element against the oracle summed over the batch."""
+    import workloads
+    x = workloads.make_xl_inputs("xl")
+    q, k, v, R, u, vb, W = (x[t] for t in ("q", "k", "v", "R", "u", "vb", "window"))
+    B, H, n, d = q.shape
+    dz = gen(q.shape, q.dtype, 3700)
+    got = xl_grads(ra, q, k, v, R, u, vb, W, dz, causal=True)
+    rng = np.random.default_rng(3701)
+    for h in (int(z) for z in rng.choice(H, size=2, replace=False)):
+        hs = slice(h, h + 1)
+        want = oracle.xl_backward(q[:, hs], k[:, hs], v[:, hs], R[hs], u[hs], vb[hs], W,
+                                  dz[:, hs], causal=True)
+        bcheck([got[3][hs], got[4][hs], got[5][hs]], want[3:], torch.bfloat16,
+               names=("dR", "du", "dv_bias"))
+        for b in (int(z) for z in rng.choice(B, size=2, replace=False)):
+            bcheck([t[b:b + 1, hs] for t in got[:3]], [w[b:b + 1] for w in want[:3]],
+                   torch.bfloat16, names=("dq", "dk", "dv"))
+
+
+def test_shaw_backward_widest_window(ra):
+    """The key table alone over every offset of a 512-token causal sequence
+    (bf16, d = 64): the one-wave query tiles, against the oracle on sampled
+    heads."""
+    B, H, n, d, c = 2, 4, 512, 64, 511
+    q, k, v, dz = (gen((B, H, n, d), torch.bfloat16, 3800 + i) for i in range(4))
+    wK = gen((H, 2 * c + 1, d), torch.bfloat16, 3804, 0.5)
+    qd, kd, vd, wkd, dzd = (x.to(DEV) for x in (q, k, v, wK, dz))
+    out, lse = ra.fwd_lse(qd, kd, vd, wkd, None, clip=c, causal=True)
+    got = ra.bwd(qd, kd, vd, wkd, None, out=out, dout=dzd, lse=lse, clip=c, causal=True)
+    torch.cuda.synchronize()
+    for h in (0, 3):
+        hs = slice(h, h + 1)
+        want = oracle.relattn_backward(q[:, hs], k[:, hs], v[:, hs], wK[hs], None, c, dz[:, hs],
+                                       causal=True)
+        bcheck([got[0][:, hs], got[1][:, hs], got[2][:, hs], got[3][hs]], want[:4],
+               torch.bfloat16, names=("dq", "dk", "dv", "dwK"))
