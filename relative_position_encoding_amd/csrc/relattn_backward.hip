@@ -980,6 +980,14 @@ __host__ __device__ inline int reduce_tables_rows(const BwdParams& p, int which)
   const int ht = which ? (p.dwv ? p.htv : 0) : (p.dwk ? p.htk : 0);
   return ht * (2 * p.clip + 1);
 }
+// Groups of threads that share one bias-gradient entry: enough for about 16
+// partials each (a power of two up to the workgroup).
+__host__ __device__ inline int bias_groups(const BwdParams& p, int nt) {
+  const int64_t U = (int64_t)p.B * ((p.ob && p.hb == 1) ? p.H : 1) * p.n_qtiles;
+  int G = 1;
+  while (G < nt && (int64_t)G * 16 < U) G *= 2;
+  return G;
+}
 // (Transformer-XL's du and dv rows only in that mode's kernels: read in the
 // others, their fields would hold registers through the whole kernel)
 template <bool XL>
@@ -992,7 +1000,8 @@ __host__ __device__ inline int reduce_role_count(const BwdParams& p, int nt) {
   int n = reduce_tables_rows(p, 0) + reduce_tables_rows(p, 1) + reduce_xl_rows<XL>(p);
   if (p.db) {
     const int64_t total = p.ob ? (int64_t)p.hb * p.ob_n : (int64_t)p.t5.nb * p.H;
-    n += (int)((total + nt - 1) / nt);
+    const int epr = nt / bias_groups(p, nt);
+    n += (int)((total + epr - 1) / epr);
   }
   return n;
 }
@@ -1036,36 +1045,51 @@ __device__ void reduce_table_row(const BwdParams& p, int which, int row, int nt)
 
 // Bias gradient entries [blk * nt, blk * nt + nt): one thread each.
 __device__ void reduce_bias(const BwdParams& p, int blk, int nt) {
-  const int64_t idx = (int64_t)blk * nt + threadIdx.x;
+  // G groups of EPR threads: thread (g, el) sums terms g, g + G, ... of entry
+  // blk * EPR + el, and the groups are added in order
+  const int G = bias_groups(p, nt), EPR = nt / G;
+  const int tid = threadIdx.x, g = tid / EPR, el = tid - g * EPR;
+  const int64_t idx = (int64_t)blk * EPR + el;
   const int nq = p.n_qtiles;
   const int nbt = p.t5.nb;  // entries per head in the partials
-  if (p.ob) {
-    // scalar-bias table [hb, ob_n]: entries outside the loaded window
-    // (offsets no pair reaches) get zero
-    const int nw = p.ob_n;
-    if (idx >= (int64_t)p.hb * nw) return;
-    const int w = (int)(idx % nw), hq = (int)(idx / nw);
-    const int e = w - p.ob_lo;
-    float acc = 0.f;
-    if (e >= 0 && e < nbt) {
-      const int h_lo = p.hb == 1 ? 0 : hq, h_hi = p.hb == 1 ? p.H : hq + 1;
-      for (int b = 0; b < p.B; ++b)
-        for (int hh = h_lo; hh < h_hi; ++hh) {
-          const float* src = p.ws_pb + (int64_t)(b * p.H + hh) * nq * nbt + e;
-          for (int t = 0; t < nq; ++t) acc += src[(int64_t)t * nbt];
-        }
+  const bool ob = p.ob != 0;
+  const int nw = p.ob_n;
+  const int64_t total = ob ? (int64_t)p.hb * nw : (int64_t)nbt * p.H;
+  const bool live = idx < total;
+  // scalar-bias table [hb, ob_n] (entries outside the loaded window, offsets
+  // no pair reaches, get zero) or T5 table [nb, H]
+  int hq = 0, w = 0, e = -1;
+  if (live) {
+    if (ob) {
+      w = (int)(idx % nw);
+      hq = (int)(idx / nw);
+      e = w - p.ob_lo;
+      if (e >= nbt) e = -1;
+    } else {
+      hq = (int)(idx % p.H);
+      e = (int)(idx / p.H);
     }
-    p.db[hq * p.db_s0 + w * p.db_s1] = acc;
-  } else {
-    // T5 table [nb, H]
-    if (idx >= (int64_t)nbt * p.H) return;
-    const int hq = (int)(idx % p.H), e = (int)(idx / p.H);
-    float acc = 0.f;
-    for (int b = 0; b < p.B; ++b) {
-      const float* src = p.ws_pb + (int64_t)(b * p.H + hq) * nq * nbt + e;
-      for (int t = 0; t < nq; ++t) acc += src[(int64_t)t * nbt];
+  }
+  const int hn = (ob && p.hb == 1) ? p.H : 1, h_lo = hn == 1 ? hq : 0;
+  float acc = 0.f;
+  if (live && e >= 0) {
+    const int64_t U = (int64_t)p.B * hn * nq;  // term u: (b, head, query tile)
+    for (int64_t u = g; u < U; u += G) {
+      const int t = (int)(u % nq);
+      const int bh2 = (int)(u / nq);
+      const int b = bh2 / hn, hh = h_lo + (bh2 - b * hn);
+      acc += p.ws_pb[((int64_t)(b * p.H + hh) * nq + t) * nbt + e];
     }
-    p.db[e * p.db_s0 + hq * p.db_s1] = acc;
+  }
+  extern __shared__ __align__(16) unsigned char smem[];
+  float* red = reinterpret_cast<float*>(smem);
+  red[tid] = acc;
+  __syncthreads();
+  if (g == 0 && live) {
+    float sum = 0.f;
+    for (int k = 0; k < G; ++k) sum += red[k * EPR + el];
+    if (ob) p.db[hq * p.db_s0 + w * p.db_s1] = sum;
+    else p.db[e * p.db_s0 + hq * p.db_s1] = sum;
   }
 }
 
