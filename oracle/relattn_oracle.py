@@ -94,6 +94,7 @@ __all__ = [
     "edge_label_attention",
     "edge_label_backward",
     "xl_backward",
+    "edge_label_relattn_backward",
     "edge_label_relattn",
     "to_f64",
 ]
@@ -924,3 +925,50 @@ def edge_label_relattn(q, k, v, labels, aK=None, aV=None, scale=None, causal: bo
                 vv = vv + _table_for_head(aV, h)[E[b]]
             z[b, h] = np.einsum("ij,ijd->id", alpha, np.broadcast_to(vv, (n, n, v.shape[-1])))
     return z
+
+
+def edge_label_relattn_backward(q, k, v, labels, aK=None, aV=None, dz=None, scale=None,
+                                causal: bool = False, key_lens=None):
+    """Gradients (dq, dk, dv, daK, daV) of sum(dz * z) for edge_label_relattn,
+    by the chain rule through Eq. 4 and Eq. 3 with each pair's tables read by
+    its label: dalpha_ij = dz_i . (v_j + a^V_ij), de_ij = alpha_ij (dalpha_ij -
+    sum_j' alpha_ij' dalpha_ij'), and
+        dq_i = s sum_j de_ij (k_j + a^K_ij)     dk_j = s sum_i de_ij q_i
+        dv_j = sum_i alpha_ij dz_i
+        daK[l] = s sum over the pairs labelled l of de_ij q_i
+        daV[l] = sum over the pairs labelled l of alpha_ij dz_i
+    (summed over the heads for a shared table; None for an absent table)."""
+    q, k, v, dz = to_f64(q), to_f64(k), to_f64(v), to_f64(dz)
+    aK, aV = to_f64(aK), to_f64(aV)
+    E = np.asarray(labels).astype(np.int64)
+    B, H, n, d = q.shape
+    assert E.shape == (B, n, n)
+    s = _default_scale(d, scale)
+    lens = _key_lengths(key_lens, B, n)
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    daK = None if aK is None else np.zeros_like(aK)
+    daV = None if aV is None else np.zeros_like(aV)
+    for b in range(B):
+        ok = visible(n, causal, lens[b])
+        for h in range(H):
+            kk = np.broadcast_to(k[b, h][None, :, :], (n, n, d))
+            if aK is not None:
+                kk = kk + _table_for_head(aK, h)[E[b]]
+            vv = np.broadcast_to(v[b, h][None, :, :], (n, n, d))
+            if aV is not None:
+                vv = vv + _table_for_head(aV, h)[E[b]]
+            e = s * np.einsum("id,ijd->ij", q[b, h], kk)
+            alpha = _masked_softmax_rows(e, ok)
+            dalpha = np.einsum("id,ijd->ij", dz[b, h], vv)
+            de = alpha * (dalpha - (alpha * dalpha).sum(axis=1, keepdims=True))
+            dq[b, h] = s * np.einsum("ij,ijd->id", de, kk)
+            dk[b, h] = s * de.T @ q[b, h]
+            dv[b, h] = alpha.T @ dz[b, h]
+            for i in range(n):
+                if aK is not None:
+                    gk = np.bincount(E[b, i], weights=de[i], minlength=aK.shape[1])
+                    daK[0 if aK.shape[0] == 1 else h] += s * gk[:, None] * q[b, h, i][None, :]
+                if aV is not None:
+                    gv = np.bincount(E[b, i], weights=alpha[i], minlength=aV.shape[1])
+                    daV[0 if aV.shape[0] == 1 else h] += gv[:, None] * dz[b, h, i][None, :]
+    return dq, dk, dv, daK, daV

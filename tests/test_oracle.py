@@ -1051,6 +1051,44 @@ def test_edge_relattn_with_clipped_offset_labels_is_shaw(tables, causal, lens):
     np.testing.assert_allclose(z, want, rtol=0, atol=1e-12)
 
 
+@pytest.mark.parametrize("tables", ["KV", "K", "V"])
+@pytest.mark.parametrize("causal,lens,shared", [(False, None, False), (True, None, True),
+                                               (False, [6, 3], False)])
+def test_edge_relattn_backward_matches_finite_differences(tables, causal, lens, shared):
+    B, H, n, d, NL = 2, 2, 6, 4, 5
+    q, k, v, dz = (rnd((B, H, n, d), 410 + i) for i in range(4))
+    Ht = 1 if shared else H
+    aK = rnd((Ht, NL, d), 414, 0.5) if "K" in tables else None
+    aV = rnd((Ht, NL, d), 415, 0.5) if "V" in tables else None
+    E = np.random.default_rng(416).integers(0, NL, size=(B, n, n))
+    grads = oracle.edge_label_relattn_backward(q, k, v, E, aK, aV, dz, causal=causal,
+                                               key_lens=lens)
+    loss = lambda: float((dz * oracle.edge_label_relattn(q, k, v, E, aK, aV, causal=causal,
+                                                         key_lens=lens)).sum())
+    rng = np.random.default_rng(417)
+    for x, g in zip((q, k, v, aK, aV), grads):
+        if x is None:
+            assert g is None
+            continue
+        idx = [tuple(int(rng.integers(s)) for s in x.shape) for _ in range(6)]
+        _fd_check(loss, x, g, idx)
+
+
+@pytest.mark.parametrize("causal,lens", [(False, None), (True, [11, 7])])
+def test_edge_relattn_backward_with_clipped_offset_labels_is_shaw_backward(causal, lens):
+    """Labels clip(j - i, k) + k: Shaw's backward, tables included (a
+    transposed label matrix or a swapped table gradient fails)."""
+    B, H, n, d, c = 2, 2, 11, 8, 3
+    q, k, v, dz = (rnd((B, H, n, d), 420 + i) for i in range(4))
+    aK, aV = rnd((H, 2 * c + 1, d), 424, 0.5), rnd((H, 2 * c + 1, d), 425, 0.5)
+    E = np.stack([oracle.relative_labels(n, c) + c] * B)
+    got = oracle.edge_label_relattn_backward(q, k, v, E, aK, aV, dz, causal=causal,
+                                             key_lens=lens)
+    want = oracle.relattn_backward(q, k, v, aK, aV, c, dz, causal=causal, key_lens=lens)
+    for a, b_ in zip(got, want):
+        np.testing.assert_allclose(a, b_, rtol=0, atol=1e-12)
+
+
 def test_edge_relattn_single_label_is_textbook_on_shifted_keys_and_values():
     """One label everywhere: a^K_ij = w^K, a^V_ij = w^V, i.e. attention over k_j + w^K
     and v_j + w^V (library routine)."""
