@@ -613,6 +613,41 @@ int relattn_bwd_xl_workspace_size(const relattn_tensor* q, const relattn_tensor*
                                   const relattn_tensor* dR, const relattn_tensor* du,
                                   const relattn_tensor* dvb, size_t* bytes);
 
+/* relattn_fwd_edge_tables_lse, relattn_bwd_edge_tables and its workspace size:
+ * the same for relation-aware attention over a labeled graph,
+ * relattn_fwd_edge_tables (summary page of "Self-Attention with Relative
+ * Position Representations", Eq. 3 and Eq. 4 with each pair's table rows read
+ * by its label), differentiated by the chain rule as relattn_bwd does for the
+ * clipped offset:
+ *     dwK[l] = s sum over the pairs labelled l of dS_ij q_i
+ *     dwV[l] = sum over the pairs labelled l of P_ij dout_i
+ * labels and tables as for relattn_fwd_edge_tables (a label >= NL counts as
+ * NL - 1); dwK, dwV: [Ht, NL, d] F32 (innermost contiguous) or NULL, a NULL
+ * one needing no table.  The dq workgroup keeps, per query row, the label sums
+ * of dS and of P on chip: tables too long give UNSUPPORTED (key and value
+ * tables in bf16 at d = 64: NL up to 64).  Errors, workspace and
+ * reproducibility as for relattn_bwd. */
+int relattn_fwd_edge_tables_lse(const relattn_tensor* q, const relattn_tensor* k,
+                                const relattn_tensor* v, const relattn_tensor* labels,
+                                const relattn_tensor* wK, const relattn_tensor* wV, float scale,
+                                const relattn_mask* mask, relattn_tensor* out,
+                                relattn_tensor* lse, void* stream);
+int relattn_bwd_edge_tables(const relattn_tensor* q, const relattn_tensor* k,
+                            const relattn_tensor* v, const relattn_tensor* labels,
+                            const relattn_tensor* wK, const relattn_tensor* wV, float scale,
+                            const relattn_mask* mask, const relattn_tensor* out,
+                            const relattn_tensor* dout, const relattn_tensor* lse,
+                            relattn_tensor* dq, relattn_tensor* dk, relattn_tensor* dv,
+                            relattn_tensor* dwK, relattn_tensor* dwV, void* workspace,
+                            size_t workspace_bytes, void* stream);
+int relattn_bwd_edge_tables_workspace_size(
+    const relattn_tensor* q, const relattn_tensor* k, const relattn_tensor* v,
+    const relattn_tensor* labels, const relattn_tensor* wK, const relattn_tensor* wV, float scale,
+    const relattn_mask* mask, const relattn_tensor* out, const relattn_tensor* dout,
+    const relattn_tensor* lse, const relattn_tensor* dq, const relattn_tensor* dk,
+    const relattn_tensor* dv, const relattn_tensor* dwK, const relattn_tensor* dwV,
+    size_t* bytes);
+
 /* Static text for a status code. */
 const char* relattn_strerror(int status);
 

@@ -18,7 +18,9 @@ __all__ = ["fwd", "validate", "fwd_offset_bias", "validate_offset_bias", "decode
            "validate_grid_bias", "fwd_grid_bias_lse", "bwd_grid_bias",
            "bwd_grid_bias_workspace_size", "attention_grid_bias", "fwd_edge_bias",
            "fwd_edge_bias_lse", "bwd_edge_bias", "bwd_edge_bias_workspace_size",
-           "attention_edge_bias", "fwd_xl_lse", "bwd_xl", "bwd_xl_workspace_size", "attention_xl", "validate_edge_bias", "edge_label_buffer",
+           "attention_edge_bias", "fwd_xl_lse", "bwd_xl", "bwd_xl_workspace_size", "attention_xl",
+           "fwd_edge_tables_lse", "bwd_edge_tables", "bwd_edge_tables_workspace_size",
+           "attention_edge_tables", "validate_edge_bias", "edge_label_buffer",
            "fwd_edge_tables", "validate_edge_tables", "decode_offset_bias",
            "decode_offset_bias_workspace_size", "decode_xl", "decode_xl_workspace_size",
            "RelattnError", "library_path",
@@ -160,6 +162,15 @@ def _load():
     lib.relattn_fwd_edge_tables.restype = ctypes.c_int
     lib.relattn_validate_edge_tables.argtypes = edget
     lib.relattn_validate_edge_tables.restype = ctypes.c_int
+    lib.relattn_fwd_edge_tables_lse.argtypes = edget + [P(_Tensor), ctypes.c_void_p]
+    lib.relattn_fwd_edge_tables_lse.restype = ctypes.c_int
+    # q k v labels wK wV scale mask out dout lse dq dk dv dwK dwV
+    edgetw = edget + [P(_Tensor)] * 7
+    lib.relattn_bwd_edge_tables.argtypes = edgetw + [ctypes.c_void_p, ctypes.c_size_t,
+                                                     ctypes.c_void_p]
+    lib.relattn_bwd_edge_tables.restype = ctypes.c_int
+    lib.relattn_bwd_edge_tables_workspace_size.argtypes = edgetw + [P(ctypes.c_size_t)]
+    lib.relattn_bwd_edge_tables_workspace_size.restype = ctypes.c_int
     lib.relattn_debug_indices.argtypes = [ctypes.c_int32, ctypes.c_int32, P(_T5),
                                           ctypes.c_void_p, ctypes.c_void_p]
     lib.relattn_debug_indices.restype = ctypes.c_int
@@ -1181,6 +1192,108 @@ def fwd_edge_tables(q, k, v, labels, wK=None, wV=None, *, causal=False, key_lens
     if st != OK:
         _raise(lib, st)
     return out
+
+
+@_on_stream
+def fwd_edge_tables_lse(q, k, v, labels, wK=None, wV=None, *, causal=False, key_lens=None,
+                        scale=None, out=None, lse=None, stream=None):
+    """``fwd_edge_tables`` with the row log-sum-exp; returns (out, lse)."""
+    import torch
+    lib = _load()
+    _check_lens(key_lens)
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    if lse is None:
+        lse = _new_lse(q)
+    args, keep = _edge_args(q, k, v, labels, None, causal, key_lens, scale, out, (wK, wV))
+    lv = _view(lse)
+    st = lib.relattn_fwd_edge_tables_lse(*args, _ref(lv), ctypes.c_void_p(_stream_of(q, stream)))
+    del keep, lv
+    if st != OK:
+        _raise(lib, st)
+    return out, lse
+
+
+def _bwd_edget_args(q, k, v, labels, wK, wV, causal, key_lens, scale, out, dout, lse, grads):
+    args, keep = _edge_args(q, k, v, labels, None, causal, key_lens, scale, out, (wK, wV))
+    extra = [_view(x) for x in (dout, lse) + tuple(grads)]
+    return args + [_ref(x) for x in extra], keep + extra
+
+
+def bwd_edge_tables_workspace_size(q, k, v, labels, wK=None, wV=None, *, out, dout, lse,
+                                   causal=False, key_lens=None, scale=None, want_dwk=True,
+                                   want_dwv=True):
+    """Workspace bytes ``bwd_edge_tables`` needs (host only)."""
+    lib = _load()
+    g = _bwd_outputs(q, wK, wV, None, q, q, q, None, None, None, want_dwk, want_dwv, False)
+    args, keep = _bwd_edget_args(q, k, v, labels, wK, wV, causal, key_lens, scale, out, dout,
+                                 lse, g[:5])
+    n = ctypes.c_size_t(0)
+    st = lib.relattn_bwd_edge_tables_workspace_size(*args, ctypes.byref(n))
+    del keep
+    if st != OK:
+        _raise(lib, st)
+    return int(n.value)
+
+
+@_on_stream
+def bwd_edge_tables(q, k, v, labels, wK=None, wV=None, *, out, dout, lse, causal=False,
+                    key_lens=None, scale=None, dq=None, dk=None, dv=None, dwK=None, dwV=None,
+                    want_dwk=True, want_dwv=True, workspace=None, stream=None):
+    """Gradients for ``fwd_edge_tables_lse``: returns (dq, dk, dv, dwK, dwV), the
+    table gradients float32 like the tables (None when absent or not wanted)."""
+    import torch
+    lib = _load()
+    _check_lens(key_lens)
+    g = _bwd_outputs(q, wK, wV, None, dq, dk, dv, dwK, dwV, None, want_dwk, want_dwv, False)
+    args, keep = _bwd_edget_args(q, k, v, labels, wK, wV, causal, key_lens, scale, out, dout,
+                                 lse, g[:5])
+    n = ctypes.c_size_t(0)
+    st = lib.relattn_bwd_edge_tables_workspace_size(*args, ctypes.byref(n))
+    if st != OK:
+        _raise(lib, st)
+    if workspace is None:
+        workspace = torch.empty(max(int(n.value), 1), dtype=torch.uint8, device=q.device)
+    st = lib.relattn_bwd_edge_tables(*args, ctypes.c_void_p(workspace.data_ptr()),
+                                     ctypes.c_size_t(workspace.numel()),
+                                     ctypes.c_void_p(_stream_of(q, stream)))
+    del keep
+    if st != OK:
+        _raise(lib, st)
+    return g[:5]
+
+
+_edget_fn = None
+
+
+def attention_edge_tables(q, k, v, labels, wK=None, wV=None, *, causal=False, key_lens=None,
+                          scale=None):
+    """Differentiable ``fwd_edge_tables``: gradients to q, k, v and the tables."""
+    global _edget_fn
+    if _edget_fn is None:
+        import torch
+
+        class _AttentionEdgeTables(torch.autograd.Function):
+            @staticmethod
+            def forward(ctx, q, k, v, labels, wK, wV, opts):
+                out, lse = fwd_edge_tables_lse(q, k, v, labels, wK, wV, **opts)
+                ctx.save_for_backward(q, k, v, labels, wK, wV, out, lse)
+                ctx.opts = opts
+                return out
+
+            @staticmethod
+            def backward(ctx, dout):
+                q, k, v, labels, wK, wV, out, lse = ctx.saved_tensors
+                need = ctx.needs_input_grad
+                dq, dk, dv, dwK, dwV = bwd_edge_tables(
+                    q, k, v, labels, wK, wV, out=out, dout=dout.contiguous(), lse=lse,
+                    want_dwk=need[4], want_dwv=need[5], **ctx.opts)
+                cast = lambda x, ref: None if x is None else x.to(ref.dtype)
+                return dq, dk, dv, None, cast(dwK, wK), cast(dwV, wV), None
+
+        _edget_fn = _AttentionEdgeTables
+    return _edget_fn.apply(q, k, v, labels, wK, wV,
+                           dict(causal=causal, key_lens=key_lens, scale=scale))
 
 
 def validate_edge_tables(q, k, v, labels, wK=None, wV=None, *, causal=False, key_lens=None,

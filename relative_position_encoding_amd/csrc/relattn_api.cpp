@@ -946,14 +946,16 @@ int make_bwd_plan(const relattn_tensor* q, const relattn_tensor* k, const relatt
   if ((st = check_like_q(dv, "dv", q))) return st;
   if ((st = check_lse(lse, q))) return st;
   const int64_t B = q->shape[0], H = q->shape[1], n = q->shape[2], d = q->shape[3];
+  // table rows: 2 clip + 1 labels by clipped offset, NL by edge label
+  const bool graph = F.mode == relattn::kRelGraph;
   if (dwK) {
     if (!wK) return fail(RELATTN_ERR_INVALID_ARGUMENT, "dwK given without wK");
-    const int64_t shp[3] = {wK->shape[0], 2 * (int64_t)clip_k + 1, d};
+    const int64_t shp[3] = {wK->shape[0], graph ? wK->shape[1] : 2 * (int64_t)clip_k + 1, d};
     if ((st = check_f32(dwK, "dwK", 3, shp))) return st;
   }
   if (dwV) {
     if (!wV) return fail(RELATTN_ERR_INVALID_ARGUMENT, "dwV given without wV");
-    const int64_t shp[3] = {wV->shape[0], 2 * (int64_t)clip_k + 1, d};
+    const int64_t shp[3] = {wV->shape[0], graph ? wV->shape[1] : 2 * (int64_t)clip_k + 1, d};
     if ((st = check_f32(dwV, "dwV", 3, shp))) return st;
   }
   if (dbias) {
@@ -999,6 +1001,13 @@ int make_bwd_plan(const relattn_tensor* q, const relattn_tensor* k, const relatt
   if (lab) {
     // the table's NL entries, one per label
     p.ob_n = f.t5.nb;
+    p.lab = f.lab;
+    p.lab_sb = f.lab_sb;
+    p.lab_sn = f.lab_sn;
+  }
+  if (graph) {
+    // the tables' NL rows, one per label
+    p.nlab = f.nr;
     p.lab = f.lab;
     p.lab_sb = f.lab_sb;
     p.lab_sn = f.lab_sn;
@@ -1083,7 +1092,7 @@ int make_bwd_plan(const relattn_tensor* q, const relattn_tensor* k, const relatt
       p.hv = (int32_t)xl_v->shape[0];
     }
   }
-  const bool shaw = F.mode == relattn::kRelShaw || xl, t5m = F.mode == relattn::kRelT5;
+  const bool shaw = F.mode == relattn::kRelShaw || xl || graph, t5m = F.mode == relattn::kRelT5;
   const bool want_db = (t5m || grid || lab) && dbias != nullptr;
   // the wide workgroup shapes unless their LDS does not fit
   size_t lq = relattn::bwd_lds_q(F.bf16, F.d, cfg, F.mode, F.has_wk, F.has_wv, p.nr, p.t5_dist,
@@ -1144,7 +1153,8 @@ int run_bwd(BwdPlan& plan, const relattn_tensor* wK, const relattn_tensor* wV, b
   unsigned char* ws = static_cast<unsigned char*>(workspace);
   relattn::BwdParams& p = plan.p;
   const bool xl = plan.fwd.mode == relattn::kRelXL;
-  const bool shaw = plan.fwd.mode == relattn::kRelShaw || xl;
+  const bool shaw = plan.fwd.mode == relattn::kRelShaw || xl ||
+                    plan.fwd.mode == relattn::kRelGraph;
   p.ws_stat = reinterpret_cast<float*>(ws + plan.off_stat);
   p.ws_pk = (shaw && wK) ? reinterpret_cast<float*>(ws + plan.off_pk) : nullptr;
   p.ws_pu = (xl && (p.du || p.dvb)) ? reinterpret_cast<float*>(ws + plan.off_pu) : nullptr;
@@ -1756,6 +1766,56 @@ int relattn_bwd_edge_bias(const relattn_tensor* q, const relattn_tensor* k,
                                0, 0, labels);
   if (st) return st;
   return run_bwd(plan, nullptr, nullptr, dbias != nullptr, workspace, workspace_bytes, stream);
+}
+
+int relattn_fwd_edge_tables_lse(const relattn_tensor* q, const relattn_tensor* k,
+                                const relattn_tensor* v, const relattn_tensor* labels,
+                                const relattn_tensor* wK, const relattn_tensor* wV, float scale,
+                                const relattn_mask* mask, relattn_tensor* out,
+                                relattn_tensor* lse, void* stream) {
+  g_last_error.clear();
+  if (!labels) return fail(RELATTN_ERR_INVALID_ARGUMENT, "labels is NULL");
+  Plan plan;
+  int st = make_plan(q, k, v, wK, wV, nullptr, nullptr, 0, scale, mask, out, &plan, true, nullptr,
+                     0, nullptr, nullptr, 0, labels);
+  if (st) return st;
+  if ((st = check_lse(lse, q))) return st;
+  return run_fwd_lse(plan, lse, stream);
+}
+
+int relattn_bwd_edge_tables_workspace_size(
+    const relattn_tensor* q, const relattn_tensor* k, const relattn_tensor* v,
+    const relattn_tensor* labels, const relattn_tensor* wK, const relattn_tensor* wV, float scale,
+    const relattn_mask* mask, const relattn_tensor* out, const relattn_tensor* dout,
+    const relattn_tensor* lse, const relattn_tensor* dq, const relattn_tensor* dk,
+    const relattn_tensor* dv, const relattn_tensor* dwK, const relattn_tensor* dwV,
+    size_t* bytes) {
+  g_last_error.clear();
+  if (!bytes) return fail(RELATTN_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  if (!labels) return fail(RELATTN_ERR_INVALID_ARGUMENT, "labels is NULL");
+  BwdPlan plan;
+  const int st = make_bwd_plan(q, k, v, wK, wV, nullptr, nullptr, 0, scale, mask, out, dout, lse,
+                               dq, dk, dv, dwK, dwV, nullptr, &plan, true, nullptr, 0, 0, labels);
+  if (st) return st;
+  *bytes = plan.fwd.empty ? 0 : plan.ws_bytes;
+  return RELATTN_OK;
+}
+
+int relattn_bwd_edge_tables(const relattn_tensor* q, const relattn_tensor* k,
+                            const relattn_tensor* v, const relattn_tensor* labels,
+                            const relattn_tensor* wK, const relattn_tensor* wV, float scale,
+                            const relattn_mask* mask, const relattn_tensor* out,
+                            const relattn_tensor* dout, const relattn_tensor* lse,
+                            relattn_tensor* dq, relattn_tensor* dk, relattn_tensor* dv,
+                            relattn_tensor* dwK, relattn_tensor* dwV, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  if (!labels) return fail(RELATTN_ERR_INVALID_ARGUMENT, "labels is NULL");
+  BwdPlan plan;
+  const int st = make_bwd_plan(q, k, v, wK, wV, nullptr, nullptr, 0, scale, mask, out, dout, lse,
+                               dq, dk, dv, dwK, dwV, nullptr, &plan, true, nullptr, 0, 0, labels);
+  if (st) return st;
+  return run_bwd(plan, wK, wV, false, workspace, workspace_bytes, stream);
 }
 
 int relattn_validate_edge_tables(const relattn_tensor* q, const relattn_tensor* k,

@@ -78,7 +78,7 @@ __host__ __device__ constexpr int bwd_waves_per_simd() {
 // tiles), the table rows of the reachable labels (resident), then the
 // per-query rows (Shaw) or the offset vector and bucket rows (T5).
 struct LayQ {
-  int ring, tk, tv, rg, rv, tb, tbi, gb, xs, total;
+  int ring, tk, tv, rg, rv, tb, tbi, gb, gw, xs, total;
   int lrs;       // relative row stride (floats)
   int gbs;       // bucket row stride (floats)
   int tab_rows;  // table rows held (labels rounded up to 32)
@@ -103,9 +103,9 @@ __host__ __device__ inline LayQ make_lay_q(int mode, bool has_wk, bool has_wv, i
     L.lrs = m + ((2 - m) & 3);
   }
   L.tab_rows = (nr + 31) / 32 * 32;
-  L.tk = L.tv = L.rg = L.rv = L.tb = L.tbi = L.gb = L.xs = off;
-  L.gbs = nb | 1;
-  if (mode == kRelShaw || mode == kRelXL) {
+  L.tk = L.tv = L.rg = L.rv = L.tb = L.tbi = L.gb = L.gw = L.xs = off;
+  L.gbs = (mode == kRelGraph ? nr : nb) | 1;
+  if (mode == kRelShaw || mode == kRelXL || mode == kRelGraph) {
     if (has_wk) {
       L.tk = take(L.tab_rows * G::ROWB);
       L.rg = take(G::BR * L.lrs * 4);
@@ -113,6 +113,12 @@ __host__ __device__ inline LayQ make_lay_q(int mode, bool has_wk, bool has_wv, i
     if (has_wv) {
       L.tv = take(L.tab_rows * G::ROWB);
       L.rv = take(G::BR * L.lrs * 4);
+    }
+    if (mode == kRelGraph) {
+      // edge labels repeat along a row: per query and lane half, the sums of
+      // dS (key table) and of P (value table) by label
+      if (has_wk) L.gb = take(2 * G::BR * L.gbs * 4);
+      if (has_wv) L.gw = take(2 * G::BR * L.gbs * 4);
     }
   } else if (mode == kRelT5) {
     L.tb = take((2 * t5_dist + 1) * 4);
@@ -180,7 +186,7 @@ __host__ __device__ inline LayKV make_lay_kv(int mode, bool has_wk, bool has_wv,
   L.lrs = nr + ((2 - nr) & 3);
   L.tab_rows = (nr + 31) / 32 * 32;
   L.rl = L.rv = L.tail = L.tk = L.tv = L.tb = L.xb = off;
-  if ((mode == kRelShaw || mode == kRelXL) && (has_wk || has_wv)) {
+  if ((mode == kRelShaw || mode == kRelXL || mode == kRelGraph) && (has_wk || has_wv)) {
     if (has_wk) {
       L.tk = take(L.tab_rows * G::ROWB);
       L.rl = take(BQ * L.lrs * 4);
@@ -285,10 +291,11 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd<D>()))) void bwd_q_kernel(
   using Op = std::conditional_t<BF16, bf16x8, float>;
   constexpr int NT = G::NT, NKB = G::NKB, DVB = G::DVB, NKS = G::NKS, ROWB = G::ROWB;
   constexpr int KSTR = G::KSTR, BR = G::BR;
-  // Transformer-XL runs the key-table path with R as the table
-  constexpr bool XL = MODE == kRelXL;
-  constexpr bool SHAW = MODE == kRelShaw || XL, T5 = MODE == kRelT5, GRID = MODE == kRelGrid;
-  constexpr bool LAB = MODE == kRelLabel;
+  // Transformer-XL runs the key-table path with R as the table; the tables
+  // by edge label (GRAPH) run it with each pair's label as its table row
+  constexpr bool XL = MODE == kRelXL, GRAPH = MODE == kRelGraph;
+  constexpr bool SHAW = MODE == kRelShaw || XL || GRAPH, T5 = MODE == kRelT5;
+  constexpr bool GRID = MODE == kRelGrid, LAB = MODE == kRelLabel;
   constexpr bool ROWS = SHAW && (HAS_WK || HAS_WV);
   static_assert(2 * BR * ROWB <= 4 * G::TILEB, "Q and dZ tiles must fit the ring");
   constexpr int SPAN = G::SPAN, PADL = G::PADL;
@@ -334,7 +341,10 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd<D>()))) void bwd_q_kernel(
   T* dqg = reinterpret_cast<T*>(p.dq) + b * p.dq_sb + h * p.dq_sh;
   const T* wkh = reinterpret_cast<const T*>(p.wk) + h * p.wk_sh;
   const T* wvh = reinterpret_cast<const T*>(p.wv) + h * p.wv_sh;
-  [[maybe_unused]] const uint8_t* labg = LAB ? p.lab + b * p.lab_sb : nullptr;
+  [[maybe_unused]] const uint8_t* labg = (LAB || GRAPH) ? p.lab + b * p.lab_sb : nullptr;
+  // edge-label tables: this lane's rows of label sums (dS, P)
+  [[maybe_unused]] float* GSr = reinterpret_cast<float*>(smem + lay.gb) + (2 * qrow + hh) * lay.gbs;
+  [[maybe_unused]] float* GWr = reinterpret_cast<float*>(smem + lay.gw) + (2 * qrow + hh) * lay.gbs;
 
   // ---- everything the loop needs, requested at once: this lane's q and dz
   // row (B operands, straight from memory), the lse, z for D, the table rows
@@ -369,6 +379,12 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd<D>()))) void bwd_q_kernel(
     if (want_db) {
       float* gb0 = reinterpret_cast<float*>(smem + lay.gb);
       for (int x = tid; x < 2 * BR * lay.gbs; x += NT) gb0[x] = 0.f;
+    }
+  }
+  if constexpr (GRAPH) {
+    for (int x = tid; x < 2 * BR * lay.gbs; x += NT) {
+      if constexpr (HAS_WK) reinterpret_cast<float*>(smem + lay.gb)[x] = 0.f;
+      if constexpr (HAS_WV) reinterpret_cast<float*>(smem + lay.gw)[x] = 0.f;
     }
   }
   if constexpr (GRID || LAB) {
@@ -454,7 +470,7 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd<D>()))) void bwd_q_kernel(
   // ---- key loop (tile 0 is in stage 0)
   // |delta| >= band: an end label (none in the 2-D window or by edge label:
   // every pair has its own entry)
-  const int band = T5 ? dist : ((GRID || LAB) ? (1 << 30) : c);
+  const int band = T5 ? dist : ((GRID || LAB || GRAPH) ? (1 << 30) : c);
   const int hi_from = max(band, 1 - band);  // delta >= hi_from: the upper end
   const float rl_lo = (SHAW && HAS_WK) ? RG[0] : (T5 ? TB[0] : 0.f);
   const float rl_hi = (SHAW && HAS_WK) ? RG[p.nr - 1] : (T5 ? TB[2 * dist] : 0.f);
@@ -554,6 +570,48 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd<D>()))) void bwd_q_kernel(
             w_hi += ws;
           } else if constexpr (T5) {
             g_lo += gs;
+          }
+        }
+      } else if constexpr (GRAPH) {
+        // tables by edge label: each key's relative logit and value term from
+        // its label's entries of this query's rows; the key's dS and P go to
+        // the label's sums in this lane's own rows (labels repeat along a row)
+        const uint8_t* lrow = labg + (int64_t)min(qi, p.n - 1) * p.lab_sn;
+        const int cmax = ((p.n + 15) & ~15) - 16;
+        uint4 ch[2];
+#pragma unroll
+        for (int g = 0; g < 2; ++g)
+          ch[g] = *reinterpret_cast<const uint4*>(lrow + min(jb + 16 * g, cmax));
+        int ent[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const uint4 c4 = ch[i >> 3];
+          const int e = i & 7;
+          uint32_t lb;
+          if constexpr (BF16) {
+            const uint32_t w = (e >> 2) ? (hh ? c4.w : c4.y) : (hh ? c4.z : c4.x);
+            lb = (w >> (8 * (e & 3))) & 0xffu;
+          } else {
+            const uint32_t w = (e >> 1) == 0 ? c4.x : (e >> 1) == 1 ? c4.y
+                             : (e >> 1) == 2 ? c4.z : c4.w;
+            lb = (w >> (8 * (2 * (e & 1) + hh))) & 0xffu;
+          }
+          ent[i] = min((int)lb, p.nr - 1);  // a label past the tables reads their last row
+          const int ko = 16 * (i >> 3) + KSTR * (i & 7);
+          const bool vis = ko <= lim;
+          const float rl = HAS_WK ? RG[ent[i]] : 0.f;
+          const float rv = HAS_WV ? RV[ent[i]] : 0.f;
+          float ex = fast_exp2(fmaf(s[i], p.scale_log2, rl) - lse2);
+          asm volatile("" : "+v"(ex));
+          const float pv = vis ? ex : 0.f;
+          pw[i] = pv;
+          ds[i] = vis ? pv * (dp[i] + rv - dd) : 0.f;
+        }
+        if (q_ok) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            if constexpr (HAS_WK) GSr[ent[i]] += ds[i];
+            if constexpr (HAS_WV) GWr[ent[i]] += pw[i];
           }
         }
       } else if constexpr (SHAW) {
@@ -774,7 +832,17 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd<D>()))) void bwd_q_kernel(
   // ---- epilogue: final label sums of this row.  In-band labels hold their
   // key's dS (and P) where the pair is visible, zero elsewhere; the lower end
   // label takes what the row's total leaves after the in-band and upper sums.
-  if constexpr (ROWS) {
+  // Tables by edge label: the two lane halves' sums of each label, added.
+  if constexpr (GRAPH) {
+    compiler_fence();
+    const float* g0 = reinterpret_cast<const float*>(smem + lay.gb) + 2 * qrow * lay.gbs;
+    const float* w0 = reinterpret_cast<const float*>(smem + lay.gw) + 2 * qrow * lay.gbs;
+    for (int x = hh; x < p.nr; x += 2) {
+      if constexpr (HAS_WK) RG[x] = q_ok ? g0[x] + g0[lay.gbs + x] : 0.f;
+      if constexpr (HAS_WV) RV[x] = q_ok ? w0[x] + w0[lay.gbs + x] : 0.f;
+    }
+    compiler_fence();  // the other half of this wave wrote the rest of the row
+  } else if constexpr (ROWS) {
     const float gall = halves_sum(g_all), wall = halves_sum(w_all);
     const float gh = halves_sum(g_hi), wh = halves_sum(w_hi);
     const int x_lo = -p.r_lo;         // label -c (present when r_lo == 0)
@@ -976,9 +1044,13 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd<D>()))) void bwd_q_kernel(
 // workgroup per (table head, label) of d w^K, then of d w^V, then the bias
 // gradient's workgroups (nt entries each).
 // ---------------------------------------------------------------------------
+// table rows per head: 2 clip + 1 labels by clipped offset, NL by edge label
+__host__ __device__ inline int table_labels(const BwdParams& p) {
+  return p.nlab ? p.nlab : 2 * p.clip + 1;
+}
 __host__ __device__ inline int reduce_tables_rows(const BwdParams& p, int which) {
   const int ht = which ? (p.dwv ? p.htv : 0) : (p.dwk ? p.htk : 0);
-  return ht * (2 * p.clip + 1);
+  return ht * table_labels(p);
 }
 // Groups of threads that share one bias-gradient entry: enough for about 16
 // partials each (a power of two up to the workgroup).
@@ -1012,7 +1084,7 @@ __host__ __device__ inline int reduce_role_count(const BwdParams& p, int nt) {
 __device__ void reduce_table_row(const BwdParams& p, int which, int row, int nt) {
   float* out = which ? p.dwv : p.dwk;
   const int ht = which ? p.htv : p.htk;
-  const int nlab = 2 * p.clip + 1;
+  const int nlab = table_labels(p);
   const int hq = row / nlab, r = row - hq * nlab;
   const int d = p.d, G = nt / d;
   const int tid = threadIdx.x;
@@ -1154,10 +1226,11 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd<D>()))) void bwd_kv_kernel
   using Op = std::conditional_t<BF16, bf16x8, float>;
   constexpr int NT = G::NT, NQB = G::NKB, DVB = G::DVB, NKS = G::NKS, ROWB = G::ROWB;
   constexpr int KSTR = G::KSTR, BR = G::BR;
-  // Transformer-XL runs the key-table path with R as the table
-  constexpr bool XL = MODE == kRelXL;
-  constexpr bool SHAW = MODE == kRelShaw || XL, T5 = MODE == kRelT5, GRID = MODE == kRelGrid;
-  constexpr bool LAB = MODE == kRelLabel;
+  // Transformer-XL runs the key-table path with R as the table; the tables
+  // by edge label (GRAPH) run it with each pair's label as its table row
+  constexpr bool XL = MODE == kRelXL, GRAPH = MODE == kRelGraph;
+  constexpr bool SHAW = MODE == kRelShaw || XL || GRAPH, T5 = MODE == kRelT5;
+  constexpr bool GRID = MODE == kRelGrid, LAB = MODE == kRelLabel;
   constexpr bool ROWS = SHAW && (HAS_WK || HAS_WV);
 
   const int n_kv = p.B * p.H * p.n_ktiles;
@@ -1259,7 +1332,7 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd<D>()))) void bwd_kv_kernel
   const int hoff = BF16 ? 8 * hh : hh;
   const bool k_ok = kj < kv_len;
   // |delta| >= band: an end label (none in the 2-D window or by edge label)
-  const int band = T5 ? dist : ((GRID || LAB) ? (1 << 30) : c);
+  const int band = T5 ? dist : ((GRID || LAB || GRAPH) ? (1 << 30) : c);
   const int hi_from = max(band, 1 - band);  // delta >= hi_from: the upper end
   // 2-D window: this lane's key on the M x M grid (row (t + 1/2) / M in fp32,
   // exact for t < 2^22)
@@ -1272,7 +1345,7 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd<D>()))) void bwd_kv_kernel
   // edge labels: this lane's key column of the batch entry's label matrix
   // (keys past n read column n - 1; they are stored as zeros)
   [[maybe_unused]] const uint8_t* labk =
-      LAB ? p.lab + b * p.lab_sb + min(kj, p.n - 1) : nullptr;
+      (LAB || GRAPH) ? p.lab + b * p.lab_sb + min(kj, p.n - 1) : nullptr;
 
   // 16 per-query values of this lane's registers: vector reads of 4
   // consecutive queries (bf16 register order), else one by one
@@ -1440,7 +1513,9 @@ __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd<D>()))) void bwd_kv_kernel
           const int delta = kj - qq;
           float rl = 0.f, rv = 0.f;
           if constexpr (SHAW) {
-            const int x = min(max(delta + c - p.r_lo, 0), p.nr - 1);
+            // the pair's table row: its clipped offset, or its edge label
+            const int x = GRAPH ? min((int)labk[(int64_t)min(qq, p.n - 1) * p.lab_sn], p.nr - 1)
+                                : min(max(delta + c - p.r_lo, 0), p.nr - 1);
             if constexpr (HAS_WK) rl = RLt[lq * lay.lrs + x];
             if constexpr (HAS_WV) rv = RVt[lq * lay.lrs + x];
           } else if constexpr (T5) {
@@ -1682,7 +1757,8 @@ static int launch_bwd_t(const BwdCfg& cfg, const BwdParams& p, void* stream) {
   using S = BwdShape<BF16, D>;
   const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   int e;
-  if constexpr (S::BIG && (MODE == kRelShaw || MODE == kRelXL) && WK && !WV) {
+  if constexpr (S::BIG && (MODE == kRelShaw || MODE == kRelXL || MODE == kRelGraph) && WK &&
+                !WV) {
     if (cfg.qwaves == S::QW_TINY && cfg.qkblock == S::QBC_TINY) {
       e = launch_q<D, S::QW_TINY, S::QBC_TINY, BF16, MODE, WK, WV>(p, s);
       if (e != (int)hipSuccess) return e;
@@ -1707,6 +1783,11 @@ static int launch_bwd_mode(const BwdCfg& c, RelMode mode, bool wk, bool wv, cons
   if (mode == kRelGrid) return launch_bwd_t<BF16, D, kRelGrid, false, false>(c, p, stream);
   if (mode == kRelLabel) return launch_bwd_t<BF16, D, kRelLabel, false, false>(c, p, stream);
   if (mode == kRelXL) return launch_bwd_t<BF16, D, kRelXL, true, false>(c, p, stream);
+  if (mode == kRelGraph) {
+    if (wk && wv) return launch_bwd_t<BF16, D, kRelGraph, true, true>(c, p, stream);
+    if (wk) return launch_bwd_t<BF16, D, kRelGraph, true, false>(c, p, stream);
+    return launch_bwd_t<BF16, D, kRelGraph, false, true>(c, p, stream);
+  }
   if (mode == kRelShaw) {
     if (wk && wv) return launch_bwd_t<BF16, D, kRelShaw, true, true>(c, p, stream);
     if (wk) return launch_bwd_t<BF16, D, kRelShaw, true, false>(c, p, stream);

@@ -226,6 +226,8 @@ struct BwdParams {
   int64_t du_sh, dvb_sh;
   int32_t hu, hv;
   float* ws_pu;
+  // tables by edge label: rows per head of each table (0: 2 clip + 1)
+  int32_t nlab;
 };
 
 struct BwdCfg {

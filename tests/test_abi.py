@@ -544,3 +544,27 @@ def test_bwd_xl_window_checks(ra):
         causal=True, want_du=False, want_dvb=False)
     up = lambda floats: (floats * 4 + 255) // 256 * 256
     assert ws(n, d, W) - no_biases == up(1 * 2 * (n // 32) * 2 * d)
+
+
+def test_bwd_edge_tables_checks(ra):
+    """The edge-table backward keeps per query row the label sums of dS and P on
+    chip: key and value tables of 64 labels fit in bf16 at d = 64, 128 do not
+    (UNSUPPORTED before any launch); a key table alone reaches 256 labels; the
+    table gradients have the tables' NL rows."""
+    B, H, n, d = 1, 2, 100, 64
+    q = T(B, H, n, d)
+    lab = ra.edge_label_buffer(B, n)
+    lse = T(B, H, n, dtype=torch.float32)
+
+    def ws(wK, wV, **kw):
+        return ra.bwd_edge_tables_workspace_size(q, q, q, lab, wK, wV, out=q, dout=q, lse=lse,
+                                                 **kw)
+    assert ws(T(H, 64, d), T(H, 64, d)) > 0
+    assert ws(T(H, 256, d), None) > 0
+    with pytest.raises(ra.RelattnError) as e:
+        ws(T(H, 128, d), T(H, 128, d))
+    assert e.value.status == ra.UNSUPPORTED
+    with pytest.raises(ra.RelattnError) as e:
+        ra.bwd_edge_tables(q, q, q, lab, T(H, 16, d), None, out=q, dout=q, lse=lse,
+                           dwK=T(H, 17, d, dtype=torch.float32))
+    assert e.value.status == ra.INVALID_ARGUMENT
