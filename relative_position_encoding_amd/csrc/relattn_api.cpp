@@ -1112,6 +1112,17 @@ int make_bwd_plan(const relattn_tensor* q, const relattn_tensor* k, const relatt
                               p.t5.nb, want_db);
     }
   }
+  // short sequences: no dq workgroup wider than the rows there are
+  if (n <= 64 && cfg.qwaves == 4 && lq <= kMaxLdsBytes) {
+    const relattn::BwdCfg narrow = relattn::bwd_cfg(F.bf16, F.d, true, cfg.kqblock == 32);
+    const size_t ln = relattn::bwd_lds_q(F.bf16, F.d, narrow, F.mode, F.has_wk, F.has_wv, p.nr,
+                                         p.t5_dist, p.t5.nb, want_db);
+    if (narrow.qwaves == 2 && ln <= kMaxLdsBytes) {
+      cfg.qwaves = narrow.qwaves;
+      cfg.qkblock = narrow.qkblock;
+      lq = ln;
+    }
+  }
   const int64_t brq = 32 * cfg.qwaves, brk = 32 * cfg.kwaves;
   p.n_qtiles = (int32_t)((n + brq - 1) / brq);
   p.n_ktiles = (int32_t)((n + brk - 1) / brk);
