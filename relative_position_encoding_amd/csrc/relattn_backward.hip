@@ -1096,12 +1096,21 @@ __device__ void reduce_table_row(const BwdParams& p, int which, int row, int nt)
     const int h_lo = ht == 1 ? 0 : hq, hn = ht == 1 ? p.H : 1;
     const int nq = p.n_qtiles;
     const int U = p.B * hn * nq;  // term u: (b, head, query tile)
-#pragma unroll 4
-    for (int u = g; u < U; u += G) {
+    auto term = [&](int u) __attribute__((always_inline)) {
       const int tq = u % nq, bh2 = u / nq;
       const int b = bh2 / hn, hh = h_lo + (bh2 - b * hn);
-      acc += part[(((int64_t)(b * p.H + hh) * nq + tq) * p.nr + x) * d + dd];
+      return part[(((int64_t)(b * p.H + hh) * nq + tq) * p.nr + x) * d + dd];
+    };
+    // eight loads in flight, then added in order
+    int u = g;
+    for (; u + 7 * G < U; u += 8 * G) {
+      float t8[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) t8[k] = term(u + k * G);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) acc += t8[k];
     }
+    for (; u < U; u += G) acc += term(u);
   }
   extern __shared__ __align__(16) unsigned char smem[];
   float* red = reinterpret_cast<float*>(smem);
@@ -1146,12 +1155,21 @@ __device__ void reduce_bias(const BwdParams& p, int blk, int nt) {
   float acc = 0.f;
   if (live && e >= 0) {
     const int64_t U = (int64_t)p.B * hn * nq;  // term u: (b, head, query tile)
-    for (int64_t u = g; u < U; u += G) {
+    auto term = [&](int64_t u) __attribute__((always_inline)) {
       const int t = (int)(u % nq);
       const int bh2 = (int)(u / nq);
       const int b = bh2 / hn, hh = h_lo + (bh2 - b * hn);
-      acc += p.ws_pb[((int64_t)(b * p.H + hh) * nq + t) * nbt + e];
+      return p.ws_pb[((int64_t)(b * p.H + hh) * nq + t) * nbt + e];
+    };
+    int64_t u = g;
+    for (; u + 7 * G < U; u += 8 * G) {
+      float t8[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) t8[k] = term(u + k * G);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) acc += t8[k];
     }
+    for (; u < U; u += G) acc += term(u);
   }
   extern __shared__ __align__(16) unsigned char smem[];
   float* red = reinterpret_cast<float*>(smem);
@@ -1179,11 +1197,20 @@ __device__ void reduce_xl_row(const BwdParams& p, int which, int hq, int nt) {
   const int U = p.B * hn * nq;  // term u: (b, head, query tile)
   float acc = 0.f;
   if (g < G) {
-    for (int u = g; u < U; u += G) {
+    auto term = [&](int u) __attribute__((always_inline)) {
       const int tq = u % nq, bh2 = u / nq;
       const int b = bh2 / hn, hh = h_lo + (bh2 - b * hn);
-      acc += p.ws_pu[(((int64_t)(b * p.H + hh) * nq + tq) * 2 + which) * d + dd];
+      return p.ws_pu[(((int64_t)(b * p.H + hh) * nq + tq) * 2 + which) * d + dd];
+    };
+    int u = g;
+    for (; u + 7 * G < U; u += 8 * G) {
+      float t8[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) t8[k] = term(u + k * G);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) acc += t8[k];
     }
+    for (; u < U; u += G) acc += term(u);
   }
   extern __shared__ __align__(16) unsigned char smem[];
   float* red = reinterpret_cast<float*>(smem);
