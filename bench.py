@@ -577,6 +577,73 @@ def bwd_report(ra, steps, name=HEADLINE):
                        "then the table-gradient sums)"}
 
 
+
+def bwd_arms_report(ra, steps):
+    """The backward passes of the other arms on their workloads: ms per call
+    (HIP events over back-to-back calls after a warm-up, one input set, so the
+    operands may sit in the last-level cache), beside the forward-with-lse call
+    that produces their lse.  No roofline: these passes are built for coverage
+    (one workgroup shape per mode, per-pair label and entry gathers)."""
+    import torch
+    import workloads
+    torch.manual_seed(20260011)
+    dev = "cuda"
+
+    def ms(fn, n):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(n):
+            fn()
+        t1.record()
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / n
+
+    out = {}
+    x = workloads.make_grid_inputs("swin")
+    q, k, v, bias = (x[t].to(dev) for t in ("q", "k", "v", "bias"))
+    M = workloads.GRID_WORKLOADS["swin"].side
+    dz = torch.randn_like(q)
+    o, lse = ra.fwd_grid_bias_lse(q, k, v, bias, M)
+    out["grid_bias"] = {
+        "workload": workloads.GRID_WORKLOADS["swin"].description,
+        "fwd_lse_ms": round(ms(lambda: ra.fwd_grid_bias_lse(q, k, v, bias, M, out=o, lse=lse), steps), 5),
+        "bwd_ms": round(ms(lambda: ra.bwd_grid_bias(q, k, v, bias, M, out=o, dout=dz, lse=lse), steps), 5)}
+    for name, key in (("edge", "edge_bias"), ("edge_kv", "edge_tables")):
+        w = workloads.EDGE_WORKLOADS[name]
+        x = workloads.make_edge_inputs(name)
+        q, k, v = (x[t].to(dev) for t in ("q", "k", "v"))
+        lab = ra.edge_label_buffer(q.shape[0], q.shape[2], dev)
+        lab.copy_(x["labels"].to(torch.uint8))
+        dz = torch.randn_like(q)
+        if w.tables:
+            wK, wV = x["wK"].to(dev), x["wV"].to(dev)
+            o, lse = ra.fwd_edge_tables_lse(q, k, v, lab, wK, wV)
+            f = lambda: ra.fwd_edge_tables_lse(q, k, v, lab, wK, wV, out=o, lse=lse)
+            b = lambda: ra.bwd_edge_tables(q, k, v, lab, wK, wV, out=o, dout=dz, lse=lse)
+        else:
+            bias = x["bias"].to(dev)
+            o, lse = ra.fwd_edge_bias_lse(q, k, v, lab, bias)
+            f = lambda: ra.fwd_edge_bias_lse(q, k, v, lab, bias, out=o, lse=lse)
+            b = lambda: ra.bwd_edge_bias(q, k, v, lab, bias, out=o, dout=dz, lse=lse)
+        out[key] = {"workload": w.description, "fwd_lse_ms": round(ms(f, steps), 5),
+                    "bwd_ms": round(ms(b, steps), 5)}
+    x = workloads.make_xl_inputs("xl")
+    q, k, v, R, u, vb = (x[t].to(dev) for t in ("q", "k", "v", "R", "u", "vb"))
+    W = x["window"]
+    dz = torch.randn_like(q)
+    o, lse = ra.fwd_xl_lse(q, k, v, R, u, vb, W, causal=True)
+    out["xl"] = {
+        "workload": workloads.XL_WORKLOADS["xl"].description,
+        "fwd_lse_ms": round(ms(lambda: ra.fwd_xl_lse(q, k, v, R, u, vb, W, causal=True, out=o,
+                                                      lse=lse), steps), 5),
+        "bwd_ms": round(ms(lambda: ra.bwd_xl(q, k, v, R, u, vb, W, out=o, dout=dz, lse=lse,
+                                              causal=True), max(5, steps // 10)), 5)}
+    return out
+
 # ---------------------------------------------------------------------------
 # Transformer-XL relative logits (relattn_fwd_xl)
 # ---------------------------------------------------------------------------
@@ -1142,6 +1209,7 @@ def main():
         line["grid_bias"] = grid_report(ra, max(50, a.steps // 5))
         line["edge_bias"] = edge_report(ra, max(50, a.steps // 5))
         line["edge_tables"] = edge_report(ra, max(50, a.steps // 5), "edge_kv")
+        line["backward_arms"] = bwd_arms_report(ra, max(20, a.steps // 10))
     if not a.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w)
         if not a.only:
