@@ -29,7 +29,8 @@
  *   Transformer-XL relative logits (relattn_fwd_xl), the 2-D window bias of
  *   windowed vision models (relattn_fwd_grid_bias), and per-pair edge labels as a
  *   scalar bias (relattn_fwd_edge_bias) or with key and value tables
- *   (relattn_fwd_edge_tables).
+ *   (relattn_fwd_edge_tables); each of these forwards has an _lse variant and a
+ *   backward (relattn_bwd_xl, _grid_bias, _edge_bias, _edge_tables).
  *
  *   Masks (no page defines them): causal hides keys j > i; key_lens[b] hides
  *   keys j >= key_lens[b] (clamped to [0, n]) of batch b.  A hidden key adds
