@@ -261,3 +261,18 @@ def test_grid_bias_backward_full_size(ra, shared):
         sl = slice(b, b + 1)
         bcheck([t[sl] for t in got[:3]], [w[sl] for w in want[:3]], torch.bfloat16,
                names=("dq", "dk", "dv"))
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=str)
+@pytest.mark.parametrize("d", [16, 128])
+def test_grid_bias_backward_head_sizes(ra, dtype, d):
+    """Head sizes 16 and 128 (the general kernel's other register layouts),
+    per-head table, ragged key lengths."""
+    M, B, H = 6, 4, 2
+    n = M * M
+    q, k, v, dz = (gen((B, H, n, d), dtype, 2800 + d + i) for i in range(4))
+    bias = gen((H, (2 * M - 1) ** 2), torch.float32, 2804)
+    lens = [n, 20, 1, n - 1]
+    _, _, got = grid_grads(ra, q, k, v, bias, M, dz, lens)
+    want = oracle.grid_bias_backward(q, k, v, bias, M, dz, key_lens=lens)
+    bcheck(got, want, dtype)
