@@ -288,3 +288,17 @@ def test_shaw_backward_widest_window(ra):
                                        causal=True)
         bcheck([got[0][:, hs], got[1][:, hs], got[2][:, hs], got[3][hs]], want[:4],
                torch.bfloat16, names=("dq", "dk", "dv", "dwK"))
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=str)
+@pytest.mark.parametrize("n,causal", [(1, True), (33, True), (97, False)])
+def test_xl_backward_d16(ra, dtype, n, causal):
+    """Head size 16, short segments (one row, a ragged tail), every distance."""
+    B, H, d = 2, 2, 16
+    W = max(n - 1, 0)
+    q, k, v, dz = (gen((B, H, n, d), dtype, 3900 + n + i) for i in range(4))
+    R = gen((H, 2 * W + 1, d), dtype, 3904, 0.5)
+    u, vb = gen((H, d), dtype, 3905, 0.5), gen((H, d), dtype, 3906, 0.5)
+    got = xl_grads(ra, q, k, v, R, u, vb, W, dz, causal)
+    want = oracle.xl_backward(q, k, v, R, u, vb, W, dz, causal=causal)
+    bcheck(got, want, dtype)
